@@ -1,0 +1,200 @@
+/*
+ * CPU oracle for the dense GEMM path -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * load this library.  The GPU library never links, includes or calls it, and
+ * it includes nothing from the GPU library.
+ *
+ * What it computes (plain definitions, accumulated in IEEE double):
+ *
+ *   fp32 row-major SGEMM   C = alpha * A * B + beta * C
+ *     The operation of the cp.async SGEMM example on the page "异步拷贝与
+ *     Hopper/Blackwell 新特性" (section "cp.async 与多级流水", file
+ *     gemm_cp_async.cu): each output is alpha times the K-long dot product of
+ *     row i of A[M][K] with column j of B[K][N], plus beta times the old C.
+ *     The plain triple loop of page 1 ("第 6 章 Shared Memory & Tile",
+ *     section 6.1) fixes the row-major indexing A[row*K+k], B[k*N+col].
+ *     beta == 0 is read as BLAS does: C is then write-only and its old value
+ *     (NaN included) never reaches the result.
+ *
+ *   fp16 "NT" GEMM         C = A * B^T,  A[M][K], B[N][K] row-major binary16
+ *     The definition in section "0. Naive Implementation" of the page
+ *     "从零开始的 AI Infra: 算子基础与GPU架构": C[m][n] is the sum over k of
+ *     A[m*K+k] * B[n*K+k], and the result is rounded to half.  Section "19.
+ *     去掉转置" confirms that B[n][k] lives at n*K+k.  The page accumulates in
+ *     float; this oracle accumulates in double and rounds the double sum to
+ *     binary16 once, round-to-nearest-even, subnormals kept, overflow to inf.
+ *
+ * Loop order: i-k-j with a double row accumulator for the NN product, i-j-k
+ * for the NT product.  Rows are shared out over OpenMP threads; every output
+ * is still one sequential sum, so the thread count never changes a result.
+ * Build with -O2 -fopenmp -ffp-contract=off and without -ffast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- IEEE 754 binary16, written out from the format's definition ---------
+ * 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits.
+ *   exponent 0      : subnormal, value = fraction * 2^-24
+ *   exponent 1..30  : normal,    value = (1024 + fraction) * 2^(exponent-25)
+ *   exponent 31     : inf (fraction 0) or NaN                                */
+
+double oracle_half_to_double(uint16_t h) {
+  const int sign = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1f;
+  const int f = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)f, -24);
+  } else if (e == 31) {
+    v = (f == 0) ? INFINITY : NAN;
+  } else {
+    v = ldexp((double)(1024 + f), e - 25);
+  }
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16, ties to even. */
+uint16_t oracle_half_from_double(double x) {
+  if (isnan(x)) return 0x7e00;
+  const uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return (uint16_t)(sign | 0x7c00);
+  /* a = m * 2^e with m in [0.5, 1): floor(log2 a) = e - 1. */
+  int e;
+  frexp(a, &e);
+  int E = e - 1;
+  if (E < -14) E = -14;            /* below the normal range: subnormal ulp */
+  const int q = E - 10;            /* the ulp of binary16 at this magnitude is 2^q */
+  const double s = ldexp(a, -q);   /* exact: a power-of-two scaling */
+  double r = floor(s);
+  const double frac = s - r;       /* exact: s < 2^12 */
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  /* value = r * 2^q; r in [0, 2048]; renormalise when rounding carried. */
+  int qq = q;
+  long ri = (long)r;
+  if (ri == 0) return sign;
+  if (ri < 1024) {                 /* only reachable when q == -24: subnormal */
+    return (uint16_t)(sign | ri);
+  }
+  while (ri >= 2048) { ri >>= 1; ++qq; }
+  const int field = qq + 25;       /* (1024 + f) * 2^(field-25) */
+  if (field >= 31) return (uint16_t)(sign | 0x7c00);
+  return (uint16_t)(sign | (field << 10) | (ri - 1024));
+}
+
+void oracle_half_round_array(long n, const double* x, uint16_t* out) {
+  for (long i = 0; i < n; ++i) out[i] = oracle_half_from_double(x[i]);
+}
+
+void oracle_half_decode_array(long n, const uint16_t* h, double* out) {
+  for (long i = 0; i < n; ++i) out[i] = oracle_half_to_double(h[i]);
+}
+
+/* ---- fp32 row-major C = alpha*A*B + beta*C -------------------------------
+ * Cref[i*ldr + j] = alpha * sum_k A[i*lda+k]*B[k*ldb+j]  (+ beta*Cin[i*ldc+j]
+ * when beta != 0), all in double.  Cin may be NULL when beta == 0. */
+void oracle_gemm_f32(int M, int N, int K, double alpha,
+                     const float* A, long lda, const float* B, long ldb,
+                     double beta, const float* Cin, long ldc,
+                     double* Cref, long ldr) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < M; ++i) {
+    double* acc = Cref + (long)i * ldr;
+    for (int j = 0; j < N; ++j) acc[j] = 0.0;
+    for (int k = 0; k < K; ++k) {
+      const double a = (double)A[(long)i * lda + k];
+      const float* brow = B + (long)k * ldb;
+      for (int j = 0; j < N; ++j) acc[j] += a * (double)brow[j];
+    }
+    for (int j = 0; j < N; ++j) {
+      double c = alpha * acc[j];
+      if (beta != 0.0) c += beta * (double)Cin[(long)i * ldc + j];
+      acc[j] = c;
+    }
+  }
+}
+
+/* The same definition, evaluated one output at a time at the given
+ * (rows[t], cols[t]) coordinates.  For sampling products too large to
+ * evaluate in full. */
+void oracle_gemm_f32_points(int K, double alpha,
+                            const float* A, long lda, const float* B, long ldb,
+                            double beta, const float* Cin, long ldc,
+                            long count, const int* rows, const int* cols,
+                            double* out) {
+#pragma omp parallel for schedule(static)
+  for (long t = 0; t < count; ++t) {
+    const long i = rows[t], j = cols[t];
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k)
+      acc += (double)A[i * lda + k] * (double)B[(long)k * ldb + j];
+    double c = alpha * acc;
+    if (beta != 0.0) c += beta * (double)Cin[i * ldc + j];
+    out[t] = c;
+  }
+}
+
+/* ---- fp16 C = A * B^T ------------------------------------------------------
+ * Cref[i*ldr + j] = sum_k A[i*lda+k] * B[j*ldb+k] in double (the value before
+ * the final rounding).  A and B are binary16 bit patterns. */
+void oracle_gemm_f16_nt(int M, int N, int K,
+                        const uint16_t* A, long lda, const uint16_t* B, long ldb,
+                        double* Cref, long ldr) {
+  /* Decode B once; A is decoded one row at a time. */
+  double* Bd = (double*)malloc(sizeof(double) * (size_t)N * (size_t)(K > 0 ? K : 1));
+  for (long j = 0; j < N; ++j)
+    for (int k = 0; k < K; ++k) Bd[j * K + k] = oracle_half_to_double(B[j * ldb + k]);
+#pragma omp parallel
+  {
+    double* arow = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int i = 0; i < M; ++i) {
+      for (int k = 0; k < K; ++k) arow[k] = oracle_half_to_double(A[(long)i * lda + k]);
+      for (int j = 0; j < N; ++j) {
+        const double* brow = Bd + (long)j * K;
+        double acc = 0.0;
+        for (int k = 0; k < K; ++k) acc += arow[k] * brow[k];
+        Cref[(long)i * ldr + j] = acc;
+      }
+    }
+    free(arow);
+  }
+  free(Bd);
+}
+
+void oracle_gemm_f16_nt_points(int K,
+                               const uint16_t* A, long lda, const uint16_t* B, long ldb,
+                               long count, const int* rows, const int* cols,
+                               double* out) {
+#pragma omp parallel for schedule(static)
+  for (long t = 0; t < count; ++t) {
+    const long i = rows[t], j = cols[t];
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k)
+      acc += oracle_half_to_double(A[i * lda + k]) * oracle_half_to_double(B[j * ldb + k]);
+    out[t] = acc;
+  }
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

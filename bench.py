@@ -1,0 +1,195 @@
+"""Benchmark of the dense GEMM hot path on one MI355X.
+
+One step = one fp16 C = A*B^T GEMM at 5376 x 5376 x 2048 (fp32 accumulate,
+fp16 out) followed by one fp32 SGEMM C = A*B at 4096^3 (alpha = 1, beta = 0),
+both through the library's C ABI on torch's current stream, on seeded
+synthetic inputs that are resident in HBM before timing starts.
+
+Prints one JSON line.  ``value`` is the step's throughput, 2MNK summed over
+both products divided by the step time (TFLOP/s).  ``kernels`` breaks it down
+per product; ``roofline`` describes the product that takes most of the step
+time, timed with HIP events recorded on the stream the kernels run on;
+``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of the same
+two products (whole output rows), scaled to TFLOP/s of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s fp16 A·Bᵀ 5376×5376×2048 + fp32 4096³ SGEMM; % of MI355X peak"
+# MI355X dense peaks: 256 CUs x 2.4 GHz x (4096 fp16 | 256 fp32) FLOP per clock per CU.
+PEAK_TFLOPS = {"f16": 2516.58, "f32": 157.29}
+HBM_PEAK_GBS = 8000.0
+
+H_NAME, F_NAME = "hgemm_nt_5376x5376x2048", "sgemm_4096"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", choices=["both", "hgemm", "sgemm"], default="both",
+                    help="time only one of the two products (for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="approximate oracle seconds per product for the CPU baseline")
+    return ap.parse_args()
+
+
+def flops(w) -> float:
+    return 2.0 * w["M"] * w["N"] * w["K"]
+
+
+def cpu_baseline(seconds: float) -> dict:
+    """Times the fp64 oracle on whole output rows of both products."""
+    import oracle
+    from dense_gemm_sgemm_amd import inputs
+
+    def rate(run, n_rows_total, flop_per_row, budget):
+        rows = 2
+        while True:                                  # calibrate on a few rows first
+            t0 = time.perf_counter()
+            run(rows)
+            dt = time.perf_counter() - t0
+            if dt > 0.5 or rows >= n_rows_total:
+                break
+            rows = min(n_rows_total, rows * 4)
+        target = int(min(n_rows_total, max(rows, rows * budget / max(dt, 1e-6))))
+        t0 = time.perf_counter()
+        run(target)
+        dt = time.perf_counter() - t0
+        return target, dt, target * flop_per_row / dt
+
+    hw, fw = inputs.WORKLOADS[H_NAME], inputs.WORKLOADS[F_NAME]
+    Ah, Bh = inputs.workload_operands(H_NAME)
+    Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
+    h_rows, h_dt, h_rate = rate(lambda r: oracle.gemm_f16_nt_exact(Ah[:r], Bh), hw["M"],
+                                2.0 * hw["N"] * hw["K"], seconds)
+    f_rows, f_dt, f_rate = rate(lambda r: oracle.gemm_f32(Af[:r], Bf), fw["M"],
+                                2.0 * fw["N"] * fw["K"], seconds)
+    step_s = flops(hw) / h_rate + flops(fw) / f_rate
+    return {
+        "value": (flops(hw) + flops(fw)) / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": ("fp64 oracle on rows 0..%d of the 5376x5376x2048 fp16 A*B^T (%.1f s) and rows "
+                   "0..%d of the 4096^3 fp32 SGEMM (%.1f s); step time extrapolated from the "
+                   "per-row rates" % (h_rows - 1, h_dt, f_rows - 1, f_dt)),
+        "per_product_gflops": {H_NAME: h_rate / 1e9, F_NAME: f_rate / 1e9},
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (the GEMM "
+              "would shard by output panels with no exchange; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import dense_gemm_sgemm_amd as dg
+    from dense_gemm_sgemm_amd import inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dg.load_library()
+
+    hw, fw = inputs.WORKLOADS[H_NAME], inputs.WORKLOADS[F_NAME]
+    parts = []
+    if args.only in ("both", "hgemm"):
+        Ah, Bh = inputs.workload_operands(H_NAME)
+        dAh, dBh = torch.from_numpy(Ah).to(dev), torch.from_numpy(Bh).to(dev)
+        dCh = torch.empty(hw["M"], hw["N"], device=dev, dtype=torch.float16)
+        assert dg.f16_nt_path(dAh, dBh, dCh) == "f16_mfma"
+        parts.append((H_NAME, "f16", "hgemm_nt_mfma_kernel", flops(hw),
+                      lambda: dg.gemm_f16_nt(dAh, dBh, dCh)))
+    if args.only in ("both", "sgemm"):
+        Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
+        dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
+        dCf = torch.empty(fw["M"], fw["N"], device=dev, dtype=torch.float32)
+        assert dg.f32_path(dAf, dBf, dCf) == "f32_mfma"
+        parts.append((F_NAME, "f32", "sgemm_mfma_kernel", flops(fw),
+                      lambda: dg.gemm_f32(dAf, dBf, dCf, 1.0, 0.0)))
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for p in parts:
+            p[4]()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in parts] for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for s in range(args.steps):
+        for i, p in enumerate(parts):
+            ev[s][i][0].record(stream)
+            p[4]()
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    ms_step = t_begin.elapsed_time(t_end) / args.steps
+    total_flop = sum(p[3] for p in parts)
+    kernels = {}
+    for i, (name, dt, kname, fl, _) in enumerate(parts):
+        times = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)])
+        avg = float(times.mean())
+        kernels[name] = {
+            "kernel": kname, "dtype": dt, "avg_ms": avg, "median_ms": float(np.median(times)),
+            "min_ms": float(times.min()), "tflops": fl / (avg * 1e-3) / 1e12,
+            "peak_tflops": PEAK_TFLOPS[dt], "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_TFLOPS[dt],
+        }
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
+    kd = kernels[dom]
+    roofline = {"bound": "mfma", "achieved": kd["tflops"], "peak": kd["peak_tflops"],
+                "unit": "TFLOP/s", "frac": kd["frac_of_peak"], "traffic": None,
+                "kernel": kd["kernel"], "workload": dom}
+
+    out = {
+        "metric": METRIC,
+        "value": total_flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "wall_ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (fp32 acc) + f32" if len(parts) == 2 else parts[0][1],
+        "data": "synthetic (seeded uniform[-1,1); inputs resident in HBM)",
+        "config": {"workload": " + ".join(p[0] for p in parts),
+                   "shapes": {p[0]: [inputs.WORKLOADS[p[0]][k] for k in ("M", "N", "K")]
+                              for p in parts},
+                   "parallelism": "single GPU"},
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline and args.only == "both":
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,147 @@
-"""MI355X (gfx950) dense GEMM library: Python binding over the C ABI."""
+"""MI355X (gfx950) dense GEMM library: a thin Python binding over the C ABI.
+
+Every step of the computation runs in the HIP kernels of ``libmi355gemm.so``;
+this module only marshals torch tensors (device pointers, leading dimensions,
+the current HIP stream) into the C calls declared in ``include/mi355gemm.h``
+and turns a nonzero status into an exception.  There is no fallback: if the
+library is missing the calls raise.
+
+    gemm_f32(A, B, C, alpha=1.0, beta=0.0)   # C = alpha*A@B + beta*C, fp32
+    gemm_f16_nt(A, B, C)                     # C = A@B.T, fp16 in/out, fp32 acc
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmi355gemm.so")
+
+# Status and path codes, mirroring include/mi355gemm.h.
+GEMM_OK = 0
+PATHS = {0: "noop", 1: "f32_scale", 2: "f32_general", 3: "f32_mfma", 4: "f16_zero",
+         5: "f16_general", 6: "f16_mfma"}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s (status %d)" % (message, status))
+        self.status = status
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the C-ABI library; raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("%s is missing: build it with `python -m dense_gemm_sgemm_amd.build` "
+                              "(or __graft_entry__.build())" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        lib.gemm_f32.argtypes = [i, i, i, f, p, i, p, i, f, p, i, p]
+        lib.gemm_f32.restype = i
+        lib.gemm_f16_nt.argtypes = [i, i, i, p, i, p, i, p, i, p]
+        lib.gemm_f16_nt.restype = i
+        lib.gemm_f32_path.argtypes = [i, i, i, f, p, i, p, i, f, p, i]
+        lib.gemm_f32_path.restype = i
+        lib.gemm_f16_nt_path.argtypes = [i, i, i, p, i, p, i, p, i]
+        lib.gemm_f16_nt_path.restype = i
+        lib.gemm_status_string.argtypes = [i]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_path_name.argtypes = [i]
+        lib.gemm_path_name.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().gemm_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != GEMM_OK:
+        raise GemmError(status, status_string(status))
+
+
+def _matrix(t, name: str, dtype):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise TypeError("%s must be a 2-D torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise TypeError("%s must live on the GPU" % name)
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit stride along its rows (row-major)" % name)
+    ld = t.stride(0) if rows > 1 else max(1, cols)
+    return rows, cols, ld, (t.data_ptr() if t.numel() else None)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def gemm_f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
+    """In place ``C = alpha * A @ B + beta * C`` for float32 A[M,K], B[K,N], C[M,N].
+
+    Enqueued on ``stream`` (default: torch's current stream); returns C."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float32)
+    K2, N, ldb, pb = _matrix(B, "B", torch.float32)
+    M2, N2, ldc, pc = _matrix(C, "C", torch.float32)
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    _check(load_library().gemm_f32(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc, ldc,
+                                   _stream(stream)))
+    return C
+
+
+def gemm_f16_nt(A, B, C, stream=None):
+    """``C = A @ B.T`` for float16 A[M,K], B[N,K]; fp32 accumulation, result in C[M,N].
+
+    Enqueued on ``stream`` (default: torch's current stream); returns C."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float16)
+    N, K2, ldb, pb = _matrix(B, "B", torch.float16)
+    M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    _check(load_library().gemm_f16_nt(M, N, K, pa, lda, pb, ldb, pc, ldc, _stream(stream)))
+    return C
+
+
+def f32_path(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> str:
+    """Name of the kernel ``gemm_f32`` would launch for these tensors (host only)."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float32)
+    _, N, ldb, pb = _matrix(B, "B", torch.float32)
+    _, _, ldc, pc = _matrix(C, "C", torch.float32)
+    code = load_library().gemm_f32_path(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc,
+                                        ldc)
+    return PATHS.get(code, "error %d" % code)
+
+
+def f16_nt_path(A, B, C) -> str:
+    """Name of the kernel ``gemm_f16_nt`` would launch for these tensors (host only)."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float16)
+    N, _, ldb, pb = _matrix(B, "B", torch.float16)
+    _, _, ldc, pc = _matrix(C, "C", torch.float16)
+    code = load_library().gemm_f16_nt_path(M, N, K, pa, lda, pb, ldb, pc, ldc)
+    return PATHS.get(code, "error %d" % code)

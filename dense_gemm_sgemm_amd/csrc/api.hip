@@ -1,0 +1,140 @@
+// C ABI: argument validation, kernel selection and launch.
+#define MI355GEMM_BUILDING 1
+#include "mi355gemm.h"
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "internal.h"
+
+using namespace mi355gemm;
+
+namespace {
+
+bool force_general() {
+  const char* v = std::getenv("MI355GEMM_FORCE_PATH");
+  return v != nullptr && std::strcmp(v, "general") == 0;
+}
+
+// Per-device verdict of the gfx950 check: 0 unknown, 1 supported, 2 not.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
+  if (dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED_DEVICE;
+  int s = g_device_state[dev].load(std::memory_order_acquire);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+              std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    s = ok ? 1 : 2;
+    g_device_state[dev].store(s, std::memory_order_release);
+  }
+  return s == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+}
+
+int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
+               float beta, const float* C, int ldc) {
+  (void)beta;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
+  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    return GEMM_ERR_BAD_LD;
+  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (K == 0 || alpha == 0.f) return GEMM_PATH_F32_SCALE;
+  if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (!force_general() && f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc))
+    return GEMM_PATH_F32_MFMA;
+  return GEMM_PATH_F32_GENERAL;
+}
+
+int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb, const void* C,
+               int ldc) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
+  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
+  if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1))
+    return GEMM_ERR_BAD_LD;
+  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (K == 0) return GEMM_PATH_F16_ZERO;
+  if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (!force_general() && f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc))
+    return GEMM_PATH_F16_MFMA;
+  return GEMM_PATH_F16_GENERAL;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
+                           const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
+  const int path = f32_select(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const int dev = check_device();
+  if (dev != GEMM_OK) return dev;
+  const F32Args a{A, B, C, lda, ldb, ldc, M, N, K, alpha, beta};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (path) {
+    case GEMM_PATH_F32_SCALE: return to_status(launch_f32_scale(a, s));
+    case GEMM_PATH_F32_MFMA: return to_status(launch_f32_mfma(a, s));
+    default: return to_status(launch_f32_general(a, s));
+  }
+}
+
+MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                              void* C, int ldc, void* stream) {
+  const int path = f16_select(M, N, K, A, lda, B, ldb, C, ldc);
+  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const int dev = check_device();
+  if (dev != GEMM_OK) return dev;
+  const F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+                  static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (path) {
+    case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
+    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, s));
+    default: return to_status(launch_f16_general(a, s));
+  }
+}
+
+MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha, const float* A, int lda,
+                                const float* B, int ldb, float beta, const float* C, int ldc) {
+  return f32_select(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+}
+
+MI355GEMM_API int gemm_f16_nt_path(int M, int N, int K, const void* A, int lda, const void* B,
+                                   int ldb, const void* C, int ldc) {
+  return f16_select(M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+MI355GEMM_API const char* gemm_status_string(int status) {
+  switch (status) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_NEGATIVE_DIM: return "a matrix dimension (M, N or K) is negative";
+    case GEMM_ERR_BAD_LD: return "a leading dimension is smaller than its row length";
+    case GEMM_ERR_NULL_POINTER: return "a matrix pointer that would be accessed is NULL";
+    case GEMM_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not gfx950";
+    case GEMM_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    default: return "unknown status code";
+  }
+}
+
+MI355GEMM_API const char* gemm_path_name(int path) {
+  switch (path) {
+    case GEMM_PATH_NOOP: return "noop";
+    case GEMM_PATH_F32_SCALE: return "f32_scale";
+    case GEMM_PATH_F32_GENERAL: return "f32_general";
+    case GEMM_PATH_F32_MFMA: return "f32_mfma";
+    case GEMM_PATH_F16_ZERO: return "f16_zero";
+    case GEMM_PATH_F16_GENERAL: return "f16_general";
+    case GEMM_PATH_F16_MFMA: return "f16_mfma";
+    default: return "?";
+  }
+}
+
+}  // extern "C"

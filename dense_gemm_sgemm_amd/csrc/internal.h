@@ -1,0 +1,67 @@
+// Internal declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355gemm {
+
+typedef _Float16 half_t;
+
+// Arguments of one fp32 call, as validated by the C-ABI layer.
+struct F32Args {
+  const float* A;
+  const float* B;
+  float* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  float alpha, beta;
+};
+
+// Arguments of one fp16 A*B^T call.
+struct F16Args {
+  const half_t* A;
+  const half_t* B;
+  half_t* C;
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+};
+
+// Launchers.  Each enqueues its kernel(s) on `stream` and returns the HIP
+// runtime's verdict on the launch.
+hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream);
+hipError_t launch_f32_general(const F32Args& a, hipStream_t stream);
+hipError_t launch_f32_mfma(const F32Args& a, hipStream_t stream);
+hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
+hipError_t launch_f16_general(const F16Args& a, hipStream_t stream);
+hipError_t launch_f16_mfma(const F16Args& a, hipStream_t stream);
+
+// Shape and alignment conditions of the fast kernels (checked on the host).
+bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   const void* C, int64_t ldc);
+bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   const void* C, int64_t ldc);
+
+// Launches `kernel(args, tile_base)` over `tiles` workgroups, split into
+// launches of at most 2^20 workgroups so that no grid exceeds the 32-bit
+// work-item count of a dispatch.  Workgroup b of a launch handles tile
+// tile_base + b.
+template <typename Args>
+hipError_t launch_tiles(const void* kernel, const Args& a, int64_t tiles, int threads,
+                        unsigned lds_bytes, hipStream_t stream) {
+  constexpr int64_t kMaxBlocks = int64_t(1) << 20;
+  for (int64_t base = 0; base < tiles; base += kMaxBlocks) {
+    const int64_t n = (tiles - base < kMaxBlocks) ? tiles - base : kMaxBlocks;
+    Args p = a;
+    int64_t b = base;
+    void* args[] = {&p, &b};
+    const hipError_t e =
+        hipLaunchKernel(kernel, dim3((unsigned)n), dim3(threads), args, lds_bytes, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace mi355gemm

@@ -1,0 +1,135 @@
+/*
+ * mi355gemm -- dense matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ * Public C ABI.  Plain pointers and sizes only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All matrices are row-major.  Element (i, j) of X with leading dimension
+ *    ldx sits at X[i*ldx + j].  Dimensions and leading dimensions are int;
+ *    offsets are computed in 64 bits.
+ *  - A, B and C are DEVICE pointers, allocated and owned by the caller.  The
+ *    library never allocates, frees or keeps a pointer after the call returns,
+ *    and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Work is enqueued on it and the call returns without synchronising; a
+ *    fault during execution surfaces at the caller's next synchronisation.
+ *  - C must not overlap A or B (undefined otherwise).  A and B may alias.
+ *  - Misaligned pointers or leading dimensions are never an error: they only
+ *    select a slower kernel.
+ *  - Calls are thread-safe.  The first call on a device checks, once, that
+ *    the device is a gfx950.
+ *
+ * Return value: GEMM_OK (0) or one of the negative GEMM_ERR_* codes below.
+ * On an error no work is enqueued and C is untouched.
+ */
+#ifndef MI355GEMM_H
+#define MI355GEMM_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(MI355GEMM_BUILDING)
+#define MI355GEMM_API __attribute__((visibility("default")))
+#else
+#define MI355GEMM_API
+#endif
+
+enum {
+  GEMM_OK = 0,
+  GEMM_ERR_NEGATIVE_DIM = -1,      /* M, N or K < 0                                  */
+  GEMM_ERR_BAD_LD = -2,            /* a leading dimension is too small               */
+  GEMM_ERR_NULL_POINTER = -3,      /* NULL for an operand that would be read/written */
+  GEMM_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or the current one is not gfx950 */
+  GEMM_ERR_LAUNCH = -5             /* the HIP runtime refused the kernel launch      */
+};
+
+/*
+ * fp32 SGEMM:  C = alpha * A * B + beta * C
+ *
+ * The operation of the cp.async SGEMM example on the page "异步拷贝与
+ * Hopper/Blackwell 新特性" (section "cp.async 与多级流水"): every C[i][j]
+ * becomes alpha times the dot product of row i of A with column j of B, plus
+ * beta times its old value.  Page 1 ("第 6 章 Shared Memory & Tile", section
+ * 6.1) fixes the row-major indexing.
+ *
+ *   A : float[M][lda], lda >= max(1, K)   (read)
+ *   B : float[K][ldb], ldb >= max(1, N)   (read)
+ *   C : float[M][ldc], ldc >= max(1, N)   (read if beta != 0, written)
+ *
+ * beta == 0 follows BLAS: C is then write-only and its old contents (NaN
+ * included) never reach the result.  K == 0 or alpha == 0 gives C = beta * C
+ * (C = 0 when beta == 0 too).  M == 0 or N == 0 is a no-op that accepts NULL
+ * pointers.  The fp32 products are accumulated in fp32.
+ */
+MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha,
+                           const float* A, int lda,
+                           const float* B, int ldb,
+                           float beta, float* C, int ldc,
+                           void* stream);
+
+/*
+ * fp16 "NT" GEMM:  C = A * B^T, fp32 accumulation, fp16 output.
+ *
+ * The product that the page "从零开始的 AI Infra: 算子基础与GPU架构" tunes,
+ * as defined in its section "0. Naive Implementation": C[m][n] is the sum
+ * over k of A[m][k] * B[n][k] accumulated in fp32 and rounded to half
+ * (round to nearest, ties to even).  Section "19. 去掉转置" is the layout:
+ * B is stored [N][K], so B[n][k] sits at n*ldb + k.
+ *
+ *   A : IEEE binary16 [M][lda], lda >= max(1, K)   (read)
+ *   B : IEEE binary16 [N][ldb], ldb >= max(1, K)   (read)
+ *   C : IEEE binary16 [M][ldc], ldc >= max(1, N)   (written only)
+ *
+ * K == 0 gives C = 0.  M == 0 or N == 0 is a no-op that accepts NULL
+ * pointers.  Results overflow to +-inf like any fp32 -> fp16 conversion.
+ */
+MI355GEMM_API int gemm_f16_nt(int M, int N, int K,
+                              const void* A, int lda,
+                              const void* B, int ldb,
+                              void* C, int ldc,
+                              void* stream);
+
+/* A static, human-readable message for a GEMM_* status code. */
+MI355GEMM_API const char* gemm_status_string(int status);
+
+/*
+ * Kernel selection, exposed for inspection and testing.  These are pure host
+ * functions: they make no HIP call and never touch the pointed-to memory
+ * (the pointers are only checked for alignment).  They return the GEMM_PATH_*
+ * value that gemm_f32 / gemm_f16_nt would launch for the same arguments, or a
+ * negative GEMM_ERR_* code for arguments those calls would reject (a device
+ * check excepted).
+ *
+ * The environment variable MI355GEMM_FORCE_PATH=general, read at every call,
+ * forces the general kernels even where a fast path applies.
+ */
+enum {
+  GEMM_PATH_NOOP = 0,           /* M == 0 or N == 0: nothing is launched          */
+  GEMM_PATH_F32_SCALE = 1,      /* K == 0 or alpha == 0: C = beta * C             */
+  GEMM_PATH_F32_GENERAL = 2,    /* LDS-tiled, any shape / leading dim / alignment */
+  GEMM_PATH_F32_MFMA = 3,       /* v_mfma f32 tiles; full tiles, 16-byte aligned  */
+  GEMM_PATH_F16_ZERO = 4,       /* K == 0: C = 0                                  */
+  GEMM_PATH_F16_GENERAL = 5,    /* LDS-tiled, any shape / leading dim / alignment */
+  GEMM_PATH_F16_MFMA = 6        /* v_mfma f16 tiles; 16-byte aligned rows         */
+};
+
+MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,
+                                const float* A, int lda,
+                                const float* B, int ldb,
+                                float beta, const float* C, int ldc);
+
+MI355GEMM_API int gemm_f16_nt_path(int M, int N, int K,
+                                   const void* A, int lda,
+                                   const void* B, int ldb,
+                                   const void* C, int ldc);
+
+/* A static name for a GEMM_PATH_* value ("f32_mfma", ...); "?" if unknown. */
+MI355GEMM_API const char* gemm_path_name(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355GEMM_H */

@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: exported symbols, argument validation and
+kernel selection.  None of these calls reaches the HIP runtime (validation
+returns before the device check; the *_path functions are pure host code)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_gemm_sgemm_amd as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
+
+F32_MFMA, F32_GENERAL, F32_SCALE = 3, 2, 1
+F16_MFMA, F16_GENERAL, F16_ZERO = 6, 5, 4
+ALIGNED = 0x100000          # fake device addresses: only their alignment is looked at
+p = ctypes.c_void_p
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dg.LIB_PATH):
+        from dense_gemm_sgemm_amd import build
+        build.build()
+    return dg.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MI355GEMM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted(["gemm_f32", "gemm_f16_nt", "gemm_status_string",
+                                         "gemm_f32_path", "gemm_f16_nt_path", "gemm_path_name"])
+
+
+def test_library_exports_exactly_the_header(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", dg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(l.split()[-1] for l in out.splitlines() if " T " in l)
+    assert exported == declared_symbols()
+    for name in declared_symbols():
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = dg.status_string(code)
+        assert s and s != "unknown status code"
+    assert dg.status_string(17) == "unknown status code"
+    assert lib.gemm_path_name(3) == b"f32_mfma" and lib.gemm_path_name(99) == b"?"
+
+
+def f32(lib, M, N, K, alpha=1.0, A=ALIGNED, lda=None, B=ALIGNED, ldb=None, beta=0.0, C=ALIGNED,
+        ldc=None):
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, N) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return lib.gemm_f32_path(M, N, K, alpha, p(A) if A else None, lda, p(B) if B else None, ldb,
+                             beta, p(C) if C else None, ldc)
+
+
+def f16(lib, M, N, K, A=ALIGNED, lda=None, B=ALIGNED, ldb=None, C=ALIGNED, ldc=None):
+    lda = max(1, K) if lda is None else lda
+    ldb = max(1, K) if ldb is None else ldb
+    ldc = max(1, N) if ldc is None else ldc
+    return lib.gemm_f16_nt_path(M, N, K, p(A) if A else None, lda, p(B) if B else None, ldb,
+                                p(C) if C else None, ldc)
+
+
+def test_validation_codes(lib):
+    assert f32(lib, -1, 4, 4) == -1 and f32(lib, 4, 4, -2) == -1 and f16(lib, 4, -1, 4) == -1
+    assert f32(lib, 8, 8, 8, lda=7) == -2 and f32(lib, 8, 8, 8, ldb=7) == -2
+    assert f32(lib, 8, 8, 8, ldc=7) == -2
+    assert f16(lib, 8, 8, 8, lda=7) == -2 and f16(lib, 8, 8, 8, ldb=7) == -2
+    assert f16(lib, 8, 8, 8, ldc=7) == -2
+    assert f32(lib, 8, 8, 8, C=0) == -3 and f32(lib, 8, 8, 8, A=0) == -3
+    assert f16(lib, 8, 8, 8, B=0) == -3 and f16(lib, 8, 8, 8, C=0) == -3
+    # operands that are never read may be NULL
+    assert f32(lib, 8, 8, 0, A=0, B=0) == F32_SCALE
+    assert f32(lib, 8, 8, 8, alpha=0.0, A=0, B=0) == F32_SCALE
+    assert f16(lib, 8, 8, 0, A=0, B=0) == F16_ZERO
+    assert f32(lib, 0, 8, 8, A=0, B=0, C=0) == 0 and f16(lib, 8, 0, 8, A=0, B=0, C=0) == 0
+
+
+def test_entry_points_reject_bad_arguments_before_any_device_call(lib):
+    null = None
+    assert lib.gemm_f32(-1, 1, 1, 1.0, null, 1, null, 1, 0.0, null, 1, null) == -1
+    assert lib.gemm_f32(4, 4, 4, 1.0, p(ALIGNED), 4, p(ALIGNED), 3, 0.0, p(ALIGNED), 4, null) == -2
+    assert lib.gemm_f16_nt(4, 4, 4, null, 4, p(ALIGNED), 4, p(ALIGNED), 4, null) == -3
+    assert lib.gemm_f32(0, 5, 5, 1.0, null, 5, null, 5, 0.0, null, 5, null) == 0
+    assert lib.gemm_f16_nt(5, 0, 5, null, 5, null, 5, null, 1, null) == 0
+
+
+def test_path_selection(lib, monkeypatch):
+    monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
+    assert f32(lib, 4096, 4096, 4096) == F32_MFMA
+    assert f32(lib, 256, 256, 256) == F32_MFMA and f32(lib, 1024, 1024, 1024) == F32_MFMA
+    assert f32(lib, 4096, 4096, 4096, beta=0.5) == F32_MFMA
+    assert f32(lib, 4000, 4096, 4096) == F32_GENERAL                # ragged M
+    assert f32(lib, 4096, 4096, 4096, A=ALIGNED + 4) == F32_GENERAL  # 4-byte aligned only
+    assert f32(lib, 256, 256, 256, lda=258) == F32_GENERAL
+    assert f16(lib, 5376, 5376, 2048) == F16_MFMA
+    assert f16(lib, 5000, 3001, 1537) == F16_GENERAL
+    assert f16(lib, 5376, 5376, 2048, ldb=2052) == F16_GENERAL
+    assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_GENERAL
+    monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
+    assert f32(lib, 4096, 4096, 4096) == F32_GENERAL
+    assert f16(lib, 5376, 5376, 2048) == F16_GENERAL
+    assert f32(lib, 8, 8, 0) == F32_SCALE
+
+
+def test_python_binding_validates_tensors(lib):
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 4)
+    with pytest.raises(TypeError):
+        dg.gemm_f32(a, a, a)                       # CPU tensors are refused
+    with pytest.raises(TypeError):
+        dg.gemm_f16_nt(a, a, a)

@@ -1,0 +1,350 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Small and medium shapes are compared element by element with the full oracle
+result; the full-size workloads (4096^3 fp32, 5376x5376x2048 and
+5000x3001x1537 fp16) are compared on sampled outputs that the oracle computes
+one by one: whole rows, whole columns, whole output tiles (first, last and one
+in the middle) and random points.  Tolerances are in ``tolerance.py``.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_sgemm_amd import inputs
+from tolerance import f16_check, f32_check, f32_tolerance
+
+torch = pytest.importorskip("torch")
+import dense_gemm_sgemm_amd as dg  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say("\n[gpu case] %s" % request.node.nodeid)
+    yield
+
+
+@pytest.fixture(params=["auto", "general"])
+def path_mode(request, monkeypatch):
+    if request.param == "general":
+        monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
+    else:
+        monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
+    return request.param
+
+
+def dev(x: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def gpu_f32(A, B, alpha=1.0, beta=0.0, C=None, expect=None):
+    dA, dB = dev(A), dev(B)
+    M, N = A.shape[0], B.shape[1]
+    dC = dev(C) if C is not None else torch.full((M, N), float("nan"), device=DEV)
+    if expect is not None:
+        assert dg.f32_path(dA, dB, dC, alpha, beta) == expect
+    dg.gemm_f32(dA, dB, dC, alpha, beta)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()
+
+
+def gpu_f16(A, B, expect=None):
+    dA, dB = dev(A), dev(B)
+    dC = torch.full((A.shape[0], B.shape[0]), float("nan"), device=DEV, dtype=torch.float16)
+    if expect is not None:
+        assert dg.f16_nt_path(dA, dB, dC) == expect
+    dg.gemm_f16_nt(dA, dB, dC)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()
+
+
+def abs16(x: np.ndarray) -> np.ndarray:
+    return (x.view(np.uint16) & np.uint16(0x7FFF)).view(np.float16)
+
+
+def expected_f32_path(mode, M, N, K):
+    if mode == "general":
+        return "f32_general"
+    return "f32_mfma" if (M % 128 == 0 and N % 128 == 0 and K % 16 == 0) else "f32_general"
+
+
+def expected_f16_path(mode, M, N, K):
+    if mode == "general":
+        return "f16_general"
+    return "f16_mfma" if (M % 256 == 0 and N % 256 == 0 and K % 64 == 0) else "f16_general"
+
+
+# ----------------------------------------------------------------- fp32 -----
+F32_SHAPES = [(1, 1, 1), (3, 5, 7), (17, 33, 9), (64, 64, 16), (65, 63, 17), (128, 128, 16),
+              (128, 256, 32), (256, 128, 48), (129, 127, 31), (256, 384, 160), (200, 300, 1),
+              (384, 256, 512)]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_shapes(shape, path_mode):
+    M, N, K = shape
+    A, B, _ = inputs.sgemm_operands(M, N, K)
+    got = gpu_f32(A, B, expect=expected_f32_path(path_mode, M, N, K))
+    f32_check(got, oracle.gemm_f32(A, B), f32_tolerance(K, 1.0, 1.0))
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, -1.25])
+@pytest.mark.parametrize("alpha", [1.0, 2.0, -0.5])
+def test_f32_alpha_beta(alpha, beta, path_mode):
+    M, N, K = 256, 256, 64
+    A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
+    got = gpu_f32(A, B, alpha, beta, C.copy())
+    ref = oracle.gemm_f32(A, B, alpha, beta, C)
+    f32_check(got, ref, f32_tolerance(K, 1.0, 1.0, alpha, beta, 1.0))
+
+
+def test_f32_beta_zero_ignores_nan_and_alpha_scales_exactly(path_mode):
+    M, N, K = 256, 128, 96
+    A, B, _ = inputs.sgemm_operands(M, N, K)
+    one = gpu_f32(A, B, 1.0, 0.0)                       # C prefilled with NaN
+    assert np.all(np.isfinite(one))
+    two = gpu_f32(A, B, 2.0, 0.0)
+    assert np.array_equal(two, 2.0 * one)
+
+
+def test_f32_quick_returns():
+    M, N = 64, 96
+    A, B, C = inputs.sgemm_operands(M, N, 16, with_c=True)
+    got = gpu_f32(A, B, 0.0, 0.5, C.copy(), expect="f32_scale")
+    assert np.array_equal(got, (np.float32(0.5) * C))
+    got = gpu_f32(A[:, :0], B[:0, :], 1.0, 0.0, None, expect="f32_scale")
+    assert np.array_equal(got, np.zeros((M, N), np.float32))
+    dA = torch.zeros(0, 5, device=DEV)
+    dB = torch.zeros(5, 7, device=DEV)
+    dC = torch.zeros(0, 7, device=DEV)
+    dg.gemm_f32(dA, dB, dC)                             # M == 0: no-op
+    torch.cuda.synchronize()
+
+
+def test_f32_small_integers_are_exact(path_mode):
+    for (M, N, K) in [(128, 128, 512), (77, 65, 300)]:
+        A = inputs.small_ints((M, K), 1, -3, 3, np.float32)
+        B = inputs.small_ints((K, N), 2, -3, 3, np.float32)
+        got = gpu_f32(A, B)
+        assert np.array_equal(got.astype(np.float64), oracle.gemm_f32(A, B))
+
+
+def test_f32_padded_leading_dimensions(path_mode):
+    M, N, K = 256, 256, 64
+    for pad in (3, 8):
+        Abig, Bbig, Cbig = inputs.sgemm_operands(M, N + pad, K + pad, with_c=True)
+        A, B = Abig[:, :K], Bbig[:K, :N]
+        dA, dB, dC = dev(Abig)[:, :K], dev(Bbig)[:K, :N], dev(Cbig)
+        dCv = dC[:, :N]
+        dg.gemm_f32(dA, dB, dCv, 1.0, 0.5)
+        torch.cuda.synchronize()
+        got = dC.cpu().numpy()
+        ref = oracle.gemm_f32(A, B, 1.0, 0.5, Cbig[:, :N])
+        f32_check(got[:, :N], ref, f32_tolerance(K, 1.0, 1.0, 1.0, 0.5, 1.0))
+        assert np.array_equal(got[:, N:], Cbig[:, N:])   # the padding is not written
+
+
+def test_f32_deterministic():
+    A, B, _ = inputs.sgemm_operands(512, 512, 256)
+    assert np.array_equal(gpu_f32(A, B), gpu_f32(A, B))
+
+
+def test_f32_on_a_side_stream():
+    A, B, _ = inputs.sgemm_operands(256, 256, 128)
+    s = torch.cuda.Stream()
+    dA, dB = dev(A), dev(B)
+    dC = torch.empty(256, 256, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dg.gemm_f32(dA, dB, dC)
+    s.synchronize()
+    f32_check(dC.cpu().numpy(), oracle.gemm_f32(A, B), f32_tolerance(128, 1.0, 1.0))
+
+
+# ----------------------------------------------------------------- fp16 -----
+F16_SHAPES = [(1, 1, 1), (3, 5, 7), (17, 33, 9), (64, 64, 32), (65, 63, 33), (256, 256, 64),
+              (256, 512, 128), (512, 256, 192), (257, 255, 65), (300, 200, 1), (512, 768, 320),
+              (129, 130, 1537)]
+
+
+@pytest.mark.parametrize("shape", F16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_shapes(shape, path_mode):
+    M, N, K = shape
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    got = gpu_f16(A, B, expect=expected_f16_path(path_mode, M, N, K))
+    ref = oracle.gemm_f16_nt_exact(A, B)
+    sab = oracle.gemm_f16_nt_exact(abs16(A), abs16(B))
+    f16_check(got, ref, sab)
+
+
+def test_f16_small_integers_are_exact_and_ties_go_even(path_mode):
+    A = inputs.small_ints((256, 512), 1, -2, 2, np.float16)
+    B = inputs.small_ints((256, 512), 2, -2, 2, np.float16)
+    got = gpu_f16(A, B)
+    exact = A.astype(np.int64) @ B.astype(np.int64).T
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
+    # sums past 2048: ties go to the even neighbour, as in the oracle's pins
+    K = 2112
+    A = np.zeros((256, K), np.float16)
+    B = np.zeros((256, K), np.float16)
+    B[:, :] = 1.0
+    for row, total in enumerate([2049, 2050, 2051, 2053, 2047, 4097]):
+        A[row, :min(total, K)] = 1.0
+        if total > K:
+            A[row, 0] = total - (K - 1)
+    got = gpu_f16(A, B)
+    _, want = oracle.gemm_f16_nt(A, B)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+    assert list(got[:6, 0].astype(np.float64)) == [2048.0, 2050.0, 2052.0, 2052.0, 2047.0, 4096.0]
+
+
+def test_f16_outer_product_rounding(path_mode):
+    """Only k = 0 is nonzero: fp32 holds a*b exactly, so C must equal half(a*b)."""
+    rng = np.random.default_rng(21)
+    M, N, K = 256, 256, 64
+    A = np.zeros((M, K), np.float16)
+    B = np.zeros((N, K), np.float16)
+    A[:, 0] = rng.normal(0, 20, M).astype(np.float16)
+    B[:, 0] = rng.normal(0, 0.05, N).astype(np.float16)
+    got = gpu_f16(A, B)
+    _, want = oracle.gemm_f16_nt(A, B)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_f16_quick_returns():
+    dA = torch.zeros(64, 0, device=DEV, dtype=torch.float16)
+    dB = torch.zeros(32, 0, device=DEV, dtype=torch.float16)
+    dC = torch.full((64, 32), 7.0, device=DEV, dtype=torch.float16)
+    assert dg.f16_nt_path(dA, dB, dC) == "f16_zero"
+    dg.gemm_f16_nt(dA, dB, dC)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dC).item() == 0
+
+
+def test_f16_padded_leading_dimensions(path_mode):
+    M, N, K = 256, 256, 128
+    for pad in (1, 8):
+        Abig, Bbig = inputs.hgemm_nt_operands(M, N, K + pad)
+        dA, dB = dev(Abig)[:, :K], dev(Bbig)[:, :K]
+        dC = torch.full((M, N + pad), 3.0, device=DEV, dtype=torch.float16)
+        dg.gemm_f16_nt(dA, dB, dC[:, :N])
+        torch.cuda.synchronize()
+        got = dC.cpu().numpy()
+        A, B = Abig[:, :K], Bbig[:, :K]
+        f16_check(got[:, :N], oracle.gemm_f16_nt_exact(A, B),
+                  oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+        assert np.all(got[:, N:] == 3.0)
+
+
+def test_f16_transpose_relation_and_determinism():
+    """C(B, A) is C(A, B) transposed: both match the oracle, and runs repeat bitwise."""
+    A, B = inputs.hgemm_nt_operands(512, 256, 256)
+    c1 = gpu_f16(A, B)
+    assert np.array_equal(c1.view(np.uint16), gpu_f16(A, B).view(np.uint16))
+    ct = gpu_f16(B, A)
+    ref = oracle.gemm_f16_nt_exact(A, B)
+    sab = oracle.gemm_f16_nt_exact(abs16(A), abs16(B))
+    f16_check(c1, ref, sab)
+    f16_check(ct.T, ref, sab)
+
+
+# ------------------------------------------------------ 64-bit offsets -------
+def test_offsets_beyond_4_gib():
+    """Leading dimensions large enough that row offsets exceed 2^32 bytes."""
+    M, N, K = 256, 256, 64
+    lda = (1 << 24) + 8                                     # 256 rows * 32 MiB = 8 GiB
+    A, B = inputs.hgemm_nt_operands(M, N, K)
+    big = torch.empty(M, lda, device=DEV, dtype=torch.float16)
+    big[:, :K].copy_(dev(A))
+    dB = dev(B)
+    dC = torch.empty(M, N, device=DEV, dtype=torch.float16)
+    assert dg.f16_nt_path(big[:, :K], dB, dC) == "f16_mfma"
+    dg.gemm_f16_nt(big[:, :K], dB, dC)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_f16_nt_exact(A, B)
+    sab = oracle.gemm_f16_nt_exact(abs16(A), abs16(B))
+    f16_check(dC.cpu().numpy(), ref, sab)
+    del big
+    lda32 = (1 << 23) + 4
+    A32, B32, _ = inputs.sgemm_operands(M, N, K)
+    big = torch.empty(M, lda32, device=DEV)
+    big[:, :K].copy_(dev(A32))
+    dC = torch.empty(M, N, device=DEV)
+    dg.gemm_f32(big[:, :K], dev(B32), dC)
+    torch.cuda.synchronize()
+    f32_check(dC.cpu().numpy(), oracle.gemm_f32(A32, B32), f32_tolerance(K, 1.0, 1.0))
+    del big
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ full-size workloads ---
+def sample_points(M, N, tiles, seed=0, n_random=20000):
+    """Whole rows, whole columns, whole tiles and random points of an M x N output."""
+    rng = np.random.default_rng(seed)
+    rows, cols = [], []
+    for i in sorted({0, 1, M // 2 + 3, M - 1}):
+        rows.append(np.full(N, i))
+        cols.append(np.arange(N))
+    for j in sorted({0, N // 3, N - 1}):
+        rows.append(np.arange(M))
+        cols.append(np.full(M, j))
+    for (r0, r1, c0, c1) in tiles:
+        rr, cc = np.meshgrid(np.arange(r0, r1), np.arange(c0, c1), indexing="ij")
+        rows.append(rr.ravel())
+        cols.append(cc.ravel())
+    rows.append(rng.integers(0, M, n_random))
+    cols.append(rng.integers(0, N, n_random))
+    return np.concatenate(rows).astype(np.int32), np.concatenate(cols).astype(np.int32)
+
+
+def tile_windows(M, N, tm, tn):
+    last_m, last_n = ((M - 1) // tm) * tm, ((N - 1) // tn) * tn
+    mid_m, mid_n = ((M // 2) // tm) * tm, ((N // 3) // tn) * tn
+    return [(0, min(tm, M), 0, min(tn, N)), (last_m, M, last_n, N),
+            (mid_m, min(mid_m + tm, M), mid_n, min(mid_n + tn, N))]
+
+
+@pytest.mark.parametrize("name", ["sgemm_256", "sgemm_1024"])
+def test_workload_sgemm_small_full(name):
+    w = inputs.WORKLOADS[name]
+    A, B, _ = inputs.workload_operands(name)
+    got = gpu_f32(A, B, w["alpha"], 0.0, expect="f32_mfma")
+    f32_check(got, oracle.gemm_f32(A, B), f32_tolerance(w["K"], np.abs(A).max(), np.abs(B).max()))
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_workload_sgemm_4096(beta):
+    M = N = K = 4096
+    A, B, C = inputs.workload_operands("sgemm_4096")
+    got = gpu_f32(A, B, 1.0, beta, C.copy() if beta else None, expect="f32_mfma")
+    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128))
+    ref = oracle.gemm_f32_points(A, B, rows, cols, 1.0, beta, C)
+    tol = f32_tolerance(K, np.abs(A).max(), np.abs(B).max(), 1.0, beta, np.abs(C).max())
+    f32_check(got[rows, cols], ref, tol)
+
+
+@pytest.mark.parametrize("name,path", [("hgemm_nt_5376x5376x2048", "f16_mfma"),
+                                       ("hgemm_nt_5000x3001x1537", "f16_general")])
+def test_workload_hgemm(name, path):
+    w = inputs.WORKLOADS[name]
+    M, N = w["M"], w["N"]
+    A, B = inputs.workload_operands(name)
+    got = gpu_f16(A, B, expect=path)
+    rows, cols = sample_points(M, N, tile_windows(M, N, 256, 256))
+    ref = oracle.gemm_f16_nt_points(A, B, rows, cols)
+    sab = oracle.gemm_f16_nt_points(abs16(A), abs16(B), rows, cols)
+    res = f16_check(got[rows, cols], ref, sab)
+    say("[%s] checked %d outputs, max %.2f ulp, literal-2ulp violations %d"
+        % (name, res["count"], res["max_ulps"], res["literal_2ulp_violations"]))

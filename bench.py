@@ -44,7 +44,53 @@ def parse_args():
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="approximate oracle seconds per product for the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device-to-device copy of a known size (the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+# Kernel sources whose measured HBM traffic (profiles/traffic.json) stays valid
+# only while they are unchanged.
+KERNEL_SOURCES = {
+    H_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_mfma.hip"],
+    F_NAME: ["dense_gemm_sgemm_amd/csrc/sgemm_mfma.hip"],
+}
+COPY_BYTES = 1 << 30
+
+
+def source_sha(name: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch from profiles/traffic.json, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(name):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def copy_calibration():
+    """A plain copy of COPY_BYTES: reads and writes exactly that many bytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def flops(w) -> float:
@@ -57,42 +103,51 @@ def cpu_baseline(seconds: float) -> dict:
     from dense_gemm_sgemm_amd import inputs
 
     def rate(run, n_rows_total, flop_per_row, budget):
+        """Rows-per-second of the oracle: a first pass on a few rows sizes a
+        sample of about `budget` seconds (whole products repeated if the
+        full product is faster than that)."""
         rows = 2
-        while True:                                  # calibrate on a few rows first
+        while True:
             t0 = time.perf_counter()
             run(rows)
             dt = time.perf_counter() - t0
             if dt > 0.5 or rows >= n_rows_total:
                 break
             rows = min(n_rows_total, rows * 4)
-        target = int(min(n_rows_total, max(rows, rows * budget / max(dt, 1e-6))))
+        want = rows * budget / max(dt, 1e-6)
+        target = int(min(n_rows_total, max(rows, want)))
+        reps = max(1, int(round(want / target))) if target == n_rows_total else 1
         t0 = time.perf_counter()
-        run(target)
+        for _ in range(reps):
+            run(target)
         dt = time.perf_counter() - t0
-        return target, dt, target * flop_per_row / dt
+        return target, reps, dt, reps * target * flop_per_row / dt
 
     hw, fw = inputs.WORKLOADS[H_NAME], inputs.WORKLOADS[F_NAME]
     Ah, Bh = inputs.workload_operands(H_NAME)
     Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
-    h_rows, h_dt, h_rate = rate(lambda r: oracle.gemm_f16_nt_exact(Ah[:r], Bh), hw["M"],
-                                2.0 * hw["N"] * hw["K"], seconds)
-    f_rows, f_dt, f_rate = rate(lambda r: oracle.gemm_f32(Af[:r], Bf), fw["M"],
-                                2.0 * fw["N"] * fw["K"], seconds)
+    h_rows, h_reps, h_dt, h_rate = rate(lambda r: oracle.gemm_f16_nt_exact(Ah[:r], Bh), hw["M"],
+                                        2.0 * hw["N"] * hw["K"], seconds)
+    f_rows, f_reps, f_dt, f_rate = rate(lambda r: oracle.gemm_f32(Af[:r], Bf), fw["M"],
+                                        2.0 * fw["N"] * fw["K"], seconds)
     step_s = flops(hw) / h_rate + flops(fw) / f_rate
     return {
         "value": (flops(hw) + flops(fw)) / step_s / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": ("fp64 oracle on rows 0..%d of the 5376x5376x2048 fp16 A*B^T (%.1f s) and rows "
-                   "0..%d of the 4096^3 fp32 SGEMM (%.1f s); step time extrapolated from the "
-                   "per-row rates" % (h_rows - 1, h_dt, f_rows - 1, f_dt)),
+        "sample": ("fp64 oracle on rows 0..%d of the 5376x5376x2048 fp16 A*B^T x%d (%.1f s) and "
+                   "rows 0..%d of the 4096^3 fp32 SGEMM x%d (%.1f s); step time from the per-row "
+                   "rates" % (h_rows - 1, h_reps, h_dt, f_rows - 1, f_reps, f_dt)),
         "per_product_gflops": {H_NAME: h_rate / 1e9, F_NAME: f_rate / 1e9},
     }
 
 
 def main():
     args = parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path (the GEMM "
               "would shard by output panels with no exchange; see DESIGN.md). Run with --gpus 1.",
@@ -115,7 +170,7 @@ def main():
         dAh, dBh = torch.from_numpy(Ah).to(dev), torch.from_numpy(Bh).to(dev)
         dCh = torch.empty(hw["M"], hw["N"], device=dev, dtype=torch.float16)
         assert dg.f16_nt_path(dAh, dBh, dCh) == "f16_mfma"
-        parts.append((H_NAME, "f16", "hgemm_nt_mfma_kernel", flops(hw),
+        parts.append((H_NAME, "f16", "hgemm_nt_kernel", flops(hw),
                       lambda: dg.gemm_f16_nt(dAh, dBh, dCh)))
     if args.only in ("both", "sgemm"):
         Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
@@ -159,11 +214,14 @@ def main():
             "min_ms": float(times.min()), "tflops": fl / (avg * 1e-3) / 1e12,
             "peak_tflops": PEAK_TFLOPS[dt], "frac_of_peak": fl / (avg * 1e-3) / 1e12 / PEAK_TFLOPS[dt],
         }
+    rooflines = {}
+    for name, kd in kernels.items():
+        rooflines[name] = {"bound": "mfma", "achieved": kd["tflops"], "peak": kd["peak_tflops"],
+                           "unit": "TFLOP/s", "frac": kd["frac_of_peak"],
+                           "traffic": measured_traffic(name), "kernel": kd["kernel"],
+                           "workload": name}
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"])
-    kd = kernels[dom]
-    roofline = {"bound": "mfma", "achieved": kd["tflops"], "peak": kd["peak_tflops"],
-                "unit": "TFLOP/s", "frac": kd["frac_of_peak"], "traffic": None,
-                "kernel": kd["kernel"], "workload": dom}
+    roofline = rooflines[dom]
 
     out = {
         "metric": METRIC,
@@ -185,6 +243,7 @@ def main():
                    "parallelism": "single GPU"},
         "kernels": kernels,
         "roofline": roofline,
+        "roofline_by_kernel": rooflines,
     }
     if not args.no_cpu_baseline and args.only == "both":
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -17,10 +17,12 @@ bool force_general() {
   return v != nullptr && std::strcmp(v, "general") == 0;
 }
 
-// Per-device verdict of the gfx950 check: 0 unknown, 1 supported, 2 not.
+// Per-device verdict of the gfx950 check: 0 unknown, -1 not supported, else
+// the device's compute-unit count.
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_device_state[kMaxDevices];
 
+// Returns the current device's CU count, or GEMM_ERR_UNSUPPORTED_DEVICE.
 int check_device() {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMM_ERR_UNSUPPORTED_DEVICE;
@@ -28,12 +30,13 @@ int check_device() {
   int s = g_device_state[dev].load(std::memory_order_acquire);
   if (s == 0) {
     hipDeviceProp_t prop;
-    bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
-              std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    s = ok ? 1 : 2;
+    const bool ok = hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                    std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                    prop.multiProcessorCount > 0;
+    s = ok ? prop.multiProcessorCount : -1;
     g_device_state[dev].store(s, std::memory_order_release);
   }
-  return s == 1 ? GEMM_OK : GEMM_ERR_UNSUPPORTED_DEVICE;
+  return s > 0 ? s : GEMM_ERR_UNSUPPORTED_DEVICE;
 }
 
 int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
@@ -75,8 +78,8 @@ MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int
                            const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
   const int path = f32_select(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
-  const int dev = check_device();
-  if (dev != GEMM_OK) return dev;
+  const int cus = check_device();
+  if (cus < 0) return cus;
   const F32Args a{A, B, C, lda, ldb, ldc, M, N, K, alpha, beta};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (path) {
@@ -90,14 +93,14 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const
                               void* C, int ldc, void* stream) {
   const int path = f16_select(M, N, K, A, lda, B, ldb, C, ldc);
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
-  const int dev = check_device();
-  if (dev != GEMM_OK) return dev;
+  const int cus = check_device();
+  if (cus < 0) return cus;
   const F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
                   static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (path) {
     case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
-    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, s));
+    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, cus, s));
     default: return to_status(launch_f16_general(a, s));
   }
 }

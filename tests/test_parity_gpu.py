@@ -83,7 +83,8 @@ def expected_f32_path(mode, M, N, K):
 def expected_f16_path(mode, M, N, K):
     if mode == "general":
         return "f16_general"
-    return "f16_mfma" if (M % 256 == 0 and N % 256 == 0 and K % 64 == 0) else "f16_general"
+    fast = M % 256 == 0 and (N % 256 == 0 or N % 224 == 0) and K % 64 == 0
+    return "f16_mfma" if fast else "f16_general"
 
 
 # ----------------------------------------------------------------- fp32 -----
@@ -174,9 +175,11 @@ def test_f32_on_a_side_stream():
 
 
 # ----------------------------------------------------------------- fp16 -----
+# Includes shapes for both fast-path tile widths (N % 256 == 0 and N % 224 == 0),
+# a single K slab, and several tiles in each direction.
 F16_SHAPES = [(1, 1, 1), (3, 5, 7), (17, 33, 9), (64, 64, 32), (65, 63, 33), (256, 256, 64),
               (256, 512, 128), (512, 256, 192), (257, 255, 65), (300, 200, 1), (512, 768, 320),
-              (129, 130, 1537)]
+              (129, 130, 1537), (256, 224, 64), (512, 448, 128), (768, 672, 256), (256, 1792, 576)]
 
 
 @pytest.mark.parametrize("shape", F16_SHAPES, ids=lambda s: "x".join(map(str, s)))

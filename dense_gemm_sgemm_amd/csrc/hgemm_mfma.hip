@@ -6,7 +6,8 @@ namespace mi355gemm {
 
 namespace {
 // Tiles are 256 rows of C by 256 or 224 columns, K slabs of 64, 8 waves in a
-// 4 x 2 grid; tiles are grouped 8 tile-rows at a time per XCD.
+// 4 x 2 grid of which waves 0-3 (one per SIMD) issue the slab copies; tiles
+// are grouped 8 tile-rows at a time per XCD; one persistent workgroup per CU.
 constexpr int BM = 256, BK = 64, GM = 8;
 }  // namespace
 
@@ -31,8 +32,8 @@ int f16_mfma_tile_n(int M, int N, int cus) {
 
 hipError_t launch_f16_mfma(const F16Args& a, int cus, hipStream_t stream) {
   if (f16_mfma_tile_n(a.M, a.N, cus) == 224)
-    return hgemm::launch<BM, 224, BK, 4, 2, GM>(a, stream);
-  return hgemm::launch<BM, 256, BK, 4, 2, GM>(a, stream);
+    return hgemm::launch<BM, 224, BK, 4, 2, GM, 1>(a, cus, stream);
+  return hgemm::launch<BM, 256, BK, 4, 2, GM, 1>(a, cus, stream);
 }
 
 }  // namespace mi355gemm

@@ -71,28 +71,27 @@ __device__ __forceinline__ void map_tile(int64_t b, int tiles_m, int tiles_n, in
   tn = (int)(w / rows);
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int COPY_SEL = 0>
 struct Config {
   static constexpr int kWaves = WAVES_M * WAVES_N;
+  // Waves that issue the slab copies: all of them (COPY_SEL 0), or half of
+  // them -- waves 0 .. kWaves/2 - 1 (COPY_SEL 1) or the even waves (COPY_SEL 2).
+  static constexpr int kCopyWaves = COPY_SEL == 0 ? kWaves : kWaves / 2;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int kChunks = BK / 8;                    // 16-byte chunks per slab row
   static constexpr int kRowsPerCopy = 64 / kChunks;         // rows one copy instruction fills
   static constexpr int kCopiesA = BM / kRowsPerCopy;        // copy instructions per slab of A
   static constexpr int kCopiesB = BN / kRowsPerCopy;
-  static constexpr int kPerWaveA = (kCopiesA + kWaves - 1) / kWaves;
-  static constexpr int kPerWaveB = (kCopiesB + kWaves - 1) / kWaves;
+  static constexpr int kPerWaveA = (kCopiesA + kCopyWaves - 1) / kCopyWaves;
+  static constexpr int kPerWaveB = (kCopiesB + kCopyWaves - 1) / kCopyWaves;
   static constexpr int kBlocksM = WM / 16, kBlocksN = WN / 16;
   static constexpr int kSteps = BK / 32;                    // MFMA k-steps per slab
   static constexpr int kStageBytes = (BM + BN) * BK * 2;
   static constexpr int kOutRowBytes = 256;                  // staging row: 16 slots of 16 bytes
-  static constexpr int kStageBytesOut = kWaves * WM * kOutRowBytes;
-  static constexpr int kLdsBytes =
-      2 * kStageBytes > kStageBytesOut ? 2 * kStageBytes : kStageBytesOut;
   static_assert(BK == 64, "the slab swizzle and the two-step pipeline assume 128-byte rows");
   static_assert(WN % 16 == 0 && WN * 2 <= kOutRowBytes, "wave tile columns");
   static_assert(WM % 16 == 0 && BM % kRowsPerCopy == 0 && BN % kRowsPerCopy == 0, "tile rows");
-  static_assert(kLdsBytes <= 160 * 1024, "LDS");
 };
 
 __device__ __forceinline__ int slab_swz(int row) { return (row >> 1) & 7; }
@@ -102,61 +101,87 @@ __device__ __forceinline__ int slab_swz(int row) { return (row >> 1) & 7; }
 constexpr int kWaitVmLgkm0 = 0x0070;   // vmcnt(0) lgkmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;     // lgkmcnt(0)
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Args p,
-                                                                       int64_t tile_base) {
-  typedef Config<BM, BN, BK, WAVES_M, WAVES_N> C;
+// Kernel arguments: the product, and the tiles this launch covers.  The
+// launch has `grid` workgroups; workgroup b handles tiles b, b + grid, ...
+// (< tiles), one after another, as one continuous stream of K slabs.
+struct TileArgs {
+  F16Args p;
+  int64_t tiles;
+};
+
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileArgs ta) {
+  typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLdsBytes];
+  const F16Args& p = ta.p;
+  // Two slab stages, then the epilogue staging area (16 rows of 256 bytes per
+  // wave, see below).
+  constexpr int kOutRows = 16;
+  constexpr int kOutBytes = C::kWaves * kOutRows * C::kOutRowBytes;
+  constexpr int kLds = 2 * C::kStageBytes + kOutBytes;
+  static_assert(kLds <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wm = (wave / WAVES_N) * C::WM, wn = (wave % WAVES_N) * C::WN;
-  int tm, tn;
-  map_tile<GM>(tile_base + blockIdx.x, p.M / BM, p.N / BN, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+  const int64_t stride = gridDim.x;
+  const int ntiles = (int)((ta.tiles - blockIdx.x + stride - 1) / stride);
+  auto tile_origin = [&](int j, int& m0, int& n0) __attribute__((always_inline)) {
+    int tm, tn;
+    map_tile<GM>(blockIdx.x + j * stride, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+  };
 
   // Copy assignment: copy instruction c of a slab fills rows [8 c, 8 c + 8);
-  // wave w issues copies w, w + kWaves, ...  Lane l writes row 8 c + l / 8 at
-  // position l % 8, so it loads logical chunk (l % 8) ^ swz(row).
-  const half_t* srcA[C::kPerWaveA];
-  const half_t* srcB[C::kPerWaveB];
-  int dstA[C::kPerWaveA], dstB[C::kPerWaveB];   // byte offset of the copy's first row
-#pragma unroll
-  for (int i = 0; i < C::kPerWaveA; ++i) {
-    const int cp = i * C::kWaves + wave;
-    const int row0 = (cp < C::kCopiesA ? cp : 0) * C::kRowsPerCopy;
-    const int row = row0 + lane / kChunks, c = (lane % kChunks) ^ slab_swz(row);
-    srcA[i] = p.A + (int64_t)(m0 + row) * p.lda + 8 * c;
-    dstA[i] = row0 * BK * 2;
-  }
-#pragma unroll
-  for (int i = 0; i < C::kPerWaveB; ++i) {
-    const int cp = i * C::kWaves + wave;
-    const int row0 = (cp < C::kCopiesB ? cp : 0) * C::kRowsPerCopy;
-    const int row = row0 + lane / kChunks, c = (lane % kChunks) ^ slab_swz(row);
-    srcB[i] = p.B + (int64_t)(n0 + row) * p.ldb + 8 * c;
-    dstB[i] = BM * BK * 2 + row0 * BK * 2;
-  }
-  auto copy_slab = [&](int stage, int k0) {
+  // copying wave cw issues copies cw, cw + kCopyWaves, ...  Lane l writes row
+  // 8 c + l / 8 at position l % 8, so it loads logical chunk
+  // (l % 8) ^ swz(row), swz(row) = ((8 c + l / 8) >> 1) & 7
+  // = (4 (c & 1) + l / 16) & 7.  A wave's copies all have c & 1 == cw & 1
+  // (kCopyWaves is even), so one 32-bit offset per lane serves every copy;
+  // the row base of a copy is wave-uniform.
+  static_assert(C::kCopyWaves % 2 == 0 && C::kRowsPerCopy == 8, "copy addressing");
+  const int cw = COPY_SEL == 0 ? wave
+               : COPY_SEL == 1 ? (wave < C::kCopyWaves ? wave : -1)
+                               : ((wave & 1) == 0 ? wave / 2 : -1);
+  const bool copier = cw >= 0;
+  const int cwp = copier ? cw : 0;
+  const int lane_row = lane / kChunks;
+  const int lane_chunk = (lane % kChunks) ^ ((4 * (cwp & 1) + (lane >> 4)) & 7);
+  const uint32_t offA = (uint32_t)(lane_row * p.lda + 8 * lane_chunk) * 2;   // bytes
+  const uint32_t offB = (uint32_t)(lane_row * p.ldb + 8 * lane_chunk) * 2;
+  const int64_t copy_strideA = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.lda * 2;
+  const int64_t copy_strideB = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.ldb * 2;
+  const int64_t firstA = (int64_t)cwp * C::kRowsPerCopy * p.lda * 2;
+  const int64_t firstB = (int64_t)cwp * C::kRowsPerCopy * p.ldb * 2;
+
+  // Issues this wave's copies of K slab `t` of the tile with origin (m0, n0)
+  // into `stage`.
+  auto copy_slab = [&](int stage, int m0, int n0, int t) __attribute__((always_inline)) {
     unsigned char* base = lds + stage * C::kStageBytes;
+    const char* srcA = (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
+    const char* srcB = (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
 #pragma unroll
     for (int i = 0; i < C::kPerWaveA; ++i)
-      if (C::kCopiesA % C::kWaves == 0 || i * C::kWaves + wave < C::kCopiesA)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(srcA[i] + k0),
-                                         (lds_void_t*)(base + dstA[i]), 16, 0, 0);
+      if (C::kCopiesA % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesA)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(srcA + i * copy_strideA + offA),
+                                         (lds_void_t*)(base + (i * C::kCopyWaves + cw) * 1024),
+                                         16, 0, 0);
 #pragma unroll
     for (int i = 0; i < C::kPerWaveB; ++i)
-      if (C::kCopiesB % C::kWaves == 0 || i * C::kWaves + wave < C::kCopiesB)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(srcB[i] + k0),
-                                         (lds_void_t*)(base + dstB[i]), 16, 0, 0);
+      if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB)
+        __builtin_amdgcn_global_load_lds(
+            (gbl_void_t*)(srcB + i * copy_strideB + offB),
+            (lds_void_t*)(base + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024), 16, 0, 0);
   };
   // All of this wave's copies have landed in LDS, and all of its LDS reads
   // have returned; then every wave of the workgroup meets.  The waits use the
   // builtin (which the compiler's own wait insertion understands); the
   // barrier is an asm statement with a memory clobber so that no memory
   // access is moved across it.
-  auto wait_and_sync = [&]() {
+  auto wait_and_sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
     asm volatile("s_barrier" ::: "memory");
   };
@@ -167,14 +192,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Arg
   const int a_off = (wm + r) * kChunks, b_off = (BM + wn + r) * kChunks;   // in 16-byte units
 
   f4 acc[C::kBlocksM][C::kBlocksN];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < C::kBlocksM; ++i)
+    for (int i = 0; i < C::kBlocksM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::kBlocksN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < C::kBlocksN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+  };
 
   // Two register sets of operand fragments: set s holds k-step s of a slab.
   h8 fa[2][C::kBlocksM], fb[2][C::kBlocksN];
-  auto load_frags = [&](int set, int stage, int s) {
+  auto load_frags = [&](int set, int stage, int s) __attribute__((always_inline)) {
     const h8* st = (const h8*)(lds + stage * C::kStageBytes);
     const int pc = (4 * s + g) ^ fr;
 #pragma unroll
@@ -182,7 +209,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Arg
 #pragma unroll
     for (int j = 0; j < C::kBlocksN; ++j) fb[set][j] = st[b_off + 16 * kChunks * j + pc];
   };
-  auto mfma_step = [&](int set) {
+  auto mfma_step = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::kBlocksM; ++i)
 #pragma unroll
@@ -190,13 +217,52 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Arg
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
   };
 
-  // Software pipeline over k-steps (two per slab).  The one barrier per slab
-  // sits between the slab's two steps: before it, every wave has landed its
-  // copy of slab t + 1 and has finished reading slab t (its step-1
-  // fragments are in registers); after it, slab t's stage is refilled with
-  // slab t + 2 and slab t + 1's first fragments are loaded while slab t's
-  // second step runs.  Every fragment load overlaps the previous step's MFMAs
-  // and every copy has one slab of MFMAs to land.
+  // Epilogue of the tile with origin (m0, n0): acc[i][j][v] is
+  // C[m0 + wm + 16 i + r][n0 + wn + 16 j + 4 g + v].  Row block i at a time,
+  // the quads are rounded to half and written (8 bytes per lane) to this
+  // wave's 16-row staging area, chunk c (8 columns) of staging row R in slot
+  // c ^ R (conflict-free for the writes and for the row reads), then whole
+  // row segments are stored to C with 16 bytes per lane.
+  unsigned char* stage_out = lds + 2 * C::kStageBytes + wave * (kOutRows * C::kOutRowBytes);
+  auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
+    const int cc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < C::kBlocksM; ++i) {
+#pragma unroll
+      for (int j = 0; j < C::kBlocksN; ++j) {
+        h4 o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+        const int c = 2 * j + (g >> 1);
+        *(h4*)(stage_out + r * C::kOutRowBytes + 16 * (c ^ r) + 8 * (g & 1)) = o;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < kOutRows / 4; ++q) {
+        const int R = 4 * q + (lane >> 4);
+        const h8 v = *(const h8*)(stage_out + R * C::kOutRowBytes + 16 * (cc ^ R));
+        if (C::WN == 128 || cc < C::WN / 8) {
+          h8* dst = (h8*)(p.C + (int64_t)(m0 + wm + 16 * i + R) * p.ldc + n0 + wn + 8 * cc);
+          if (OPT & 1) {
+            __builtin_nontemporal_store(v, dst);   // OPT bit 0: streaming stores of C
+          } else {
+            *dst = v;
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  };
+
+  // Software pipeline over the workgroup's slab stream (ntiles x nk slabs,
+  // two k-steps each).  The one barrier per slab sits between the slab's two
+  // steps: before it, every wave has landed its copy of the next slab and has
+  // finished reading this one (its step-1 fragments are in registers); after
+  // it, this slab's stage is refilled with the slab after next (which may
+  // belong to the next tile) and the next slab's first fragments are loaded
+  // while this slab's second step runs.  Every fragment load overlaps the
+  // previous step's MFMAs and every copy has one slab of MFMAs to land; the
+  // next tile's first two slabs land while this tile finishes and stores.
   //
   // Within each half the copies and LDS reads are interleaved one by one with
   // the MFMAs (sched_group_barrier), so that the two waves sharing a SIMD's
@@ -207,10 +273,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Arg
   constexpr int kReads = C::kBlocksM + C::kBlocksN;
   constexpr int kCopies = C::kPerWaveA + C::kPerWaveB;
   static_assert(kReads + kCopies <= kMfma, "interleave pattern");
-  auto slab = [&](int t, auto copy, auto next) {
-    // First half: step 0 of slab t, with the loads of step 1.
+  const int nk = p.K / BK;
+  const int total = ntiles * nk;
+  // The copy target runs two slabs ahead of the compute: slab tc of the tile
+  // `ahead` tiles after the current one (origins o[0..2] are refreshed once
+  // per tile, outside the MFMA loop).  Past the end of the stream it stays on
+  // the last slab of the last tile.
+  int tc = 0, ahead = 0, cur = 0;
+  int om[3], on[3];
+  auto refresh_origins = [&](int j) __attribute__((always_inline)) {
+    cur = j;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) tile_origin(j + d < ntiles ? j + d : ntiles - 1, om[d], on[d]);
+  };
+  refresh_origins(0);
+  auto advance_copy = [&]() __attribute__((always_inline)) {
+    if (++tc == nk) {
+      tc = 0;
+      ++ahead;
+    }
+  };
+  auto copy_next = [&](int stage) __attribute__((always_inline)) {
+    const bool past = cur + ahead >= ntiles;
+    const int d = ahead < 2 ? ahead : 2;
+    const int m0 = d == 0 ? om[0] : d == 1 ? om[1] : om[2];
+    const int n0 = d == 0 ? on[0] : d == 1 ? on[1] : on[2];
+    copy_slab(stage, m0, n0, past ? nk - 1 : tc);
+  };
+  auto slab = [&](int gs, auto copy, auto next, auto is_copier) __attribute__((always_inline)) {
+    constexpr bool kCp = decltype(is_copier)::value && decltype(copy)::value;
+    // First half: step 0 of slab gs, with the loads of step 1.
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    load_frags(1, t & 1, 1);
+    load_frags(1, gs & 1, 1);
     mfma_step(0);
 #pragma unroll
     for (int q = 0; q < kReads; ++q) {
@@ -221,13 +315,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Arg
     __builtin_amdgcn_sched_barrier(0);
     wait_and_sync();
     __builtin_amdgcn_sched_barrier(0);
-    // Second half: step 1 of slab t, with the copy of slab t + 2 and the
-    // loads of slab t + 1's step 0.
-    if constexpr (decltype(copy)::value) copy_slab(t & 1, (t + 2) * BK);
-    if constexpr (decltype(next)::value) load_frags(0, (t + 1) & 1, 0);
+    // Second half: step 1 of slab gs, with the copy of slab gs + 2 and the
+    // loads of slab gs + 1's step 0.
+    if constexpr (kCp) copy_next(gs & 1);
+    if constexpr (decltype(next)::value) load_frags(0, (gs + 1) & 1, 0);
     mfma_step(1);
     constexpr int kR = decltype(next)::value ? kReads : 0;
-    constexpr int kV = decltype(copy)::value ? kCopies : 0;
+    constexpr int kV = kCp ? kCopies : 0;
 #pragma unroll
     for (int q = 0; q < (kR > kV ? kR : kV); ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -236,61 +330,79 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(F16Arg
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma - (kR > kV ? kR : kV), 0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(copy)::value) advance_copy();
   };
   typedef std::integral_constant<bool, true> yes;
   typedef std::integral_constant<bool, false> no;
 
-  const int nk = p.K / BK;
-  copy_slab(0, 0);
+  // Prologue: slab 0 (tile 0), then slab 1 in flight.
+  if (copier) copy_next(0);
+  advance_copy();
   wait_and_sync();
-  if (nk > 1) copy_slab(1, BK);
+  if (copier) copy_next(1);
+  advance_copy();
+  // (jc, tc) now names slab 2 of the stream.
   load_frags(0, 0, 0);
-  for (int t = 0; t + 2 < nk; ++t) slab(t, yes(), yes());
-  if (nk >= 2) slab(nk - 2, no(), yes());
-  slab(nk - 1, no(), no());
+  zero_acc();
 
-  // Epilogue.  acc[i][j][v] = C[m0 + wm + 16 i + r][n0 + wn + 16 j + 4 g + v].
-  // Staging row R (= 16 i + r) of this wave: 16 slots of 16 bytes, chunk c
-  // (8 columns) stored in slot c ^ (R & 15).
-  unsigned char* stage_out = lds + wave * (C::WM * C::kOutRowBytes);
-#pragma unroll
-  for (int i = 0; i < C::kBlocksM; ++i) {
-    const int R = 16 * i + r;
-#pragma unroll
-    for (int j = 0; j < C::kBlocksN; ++j) {
-      h4 o;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
-      const int c = 2 * j + (g >> 1);
-      *(h4*)(stage_out + R * C::kOutRowBytes + 16 * (c ^ (R & 15)) + 8 * (g & 1)) = o;
+  // The stream, once for waves that issue copies and once for waves that do
+  // not (a wave-uniform branch outside the loop keeps each body
+  // straight-line; both execute the same sequence of barriers).  A tile's
+  // last slab loads no fragments: the next tile's first ones are loaded after
+  // the epilogue, which keeps the epilogue's registers free.  Past the end of
+  // the stream the copies repeat the last slab into a stage nothing reads
+  // any more (harmless; drained before the kernel ends), so every slab has
+  // the same shape.
+  auto stream = [&](auto cp) __attribute__((always_inline)) {
+    int gs = 0;
+    for (int j = 0; j < ntiles; ++j) {
+      const int m0 = om[0], n0 = on[0];
+      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), yes(), cp);
+      slab(gs, yes(), no(), cp);
+      ++gs;
+      epilogue(m0, n0);
+      zero_acc();
+      --ahead;
+      refresh_origins(j + 1);
+      load_frags(0, gs & 1, 0);
     }
+  };
+  if (C::kCopyWaves == C::kWaves || copier) {
+    // OPT bit 1: copying waves take issue priority over their SIMD partner.
+    if ((OPT & 2) && C::kCopyWaves != C::kWaves) __builtin_amdgcn_s_setprio(2);
+    stream(yes());
+    if ((OPT & 2) && C::kCopyWaves != C::kWaves) __builtin_amdgcn_s_setprio(0);
+  } else {
+    stream(no());
   }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  // Lanes 16 q' .. 16 q' + 15 store staging row R, 16 bytes each, for the WN / 8
-  // chunks the row holds.
-  const int cc = lane & 15;
-#pragma unroll
-  for (int q = 0; q < C::WM / 4; ++q) {
-    const int R = 4 * q + (lane >> 4);
-    const h8 v = *(const h8*)(stage_out + R * C::kOutRowBytes + 16 * (cc ^ (R & 15)));
-    if (C::WN == 128 || cc < C::WN / 8)
-      *(h8*)(p.C + (int64_t)(m0 + wm + R) * p.ldc + n0 + wn + 8 * cc) = v;
-  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);   // drain the copies past the end of the stream
 }
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM>
-hipError_t launch(const F16Args& a, hipStream_t stream) {
-  typedef Config<BM, BN, BK, WAVES_M, WAVES_N> C;
+// PERSISTENT: one workgroup per CU (at most) walking tiles; otherwise one
+// workgroup per tile.
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
+          bool PERSISTENT = true>
+hipError_t launch(const F16Args& a, int cus, hipStream_t stream) {
+  typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN);
-  return launch_tiles((const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM>, a, tiles,
-                      C::kThreads, 0, stream);
+  const int64_t max_grid = int64_t(1) << 20;
+  int64_t grid = PERSISTENT ? (tiles < cus ? tiles : cus) : (tiles < max_grid ? tiles : max_grid);
+  if (grid < 1) grid = 1;
+  TileArgs ta{a, tiles};
+  void* args[] = {&ta};
+  return hipLaunchKernel((const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT>,
+                         dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 
+// Leading dimensions must also keep a lane's 32-bit copy offset (up to 8 rows
+// into a copy) in range: ld < 2^28 elements.
 template <int BM, int BN, int BK>
 bool fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
           const void* Cp, int64_t ldc) {
+  constexpr int64_t kMaxLd = int64_t(1) << 28;
   return M % BM == 0 && N % BN == 0 && K % BK == 0 && aligned16(A) && aligned16(B) &&
-         aligned16(Cp) && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0;
+         aligned16(Cp) && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0 && lda < kMaxLd &&
+         ldb < kMaxLd;
 }
 
 }  // namespace hgemm

@@ -44,6 +44,9 @@ def parse_args():
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="approximate oracle seconds per product for the CPU baseline")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the timing of the remaining workloads (256^3, 1024^3, 4096^3 with "
+                         "beta 0.5, ragged 5000x3001x1537)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of a known size (the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -141,6 +144,45 @@ def cpu_baseline(seconds: float) -> dict:
                    "rates" % (h_rows - 1, h_reps, h_dt, f_rows - 1, f_reps, f_dt)),
         "per_product_gflops": {H_NAME: h_rate / 1e9, F_NAME: f_rate / 1e9},
     }
+
+
+def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
+    """Per-launch times of the workloads that are not part of the step: the
+    small SGEMMs, the 4096^3 SGEMM with beta = 0.5 and the ragged fp16 product.
+    Reported next to the step for context; not part of ``value``."""
+    res = {}
+    cases = [("sgemm_256", 0.0), ("sgemm_1024", 0.0), ("sgemm_4096", 0.5),
+             ("hgemm_nt_5000x3001x1537", None)]
+    for name, beta in cases:
+        w = inputs.WORKLOADS[name]
+        if w["kind"] == "f32":
+            A, B, C = inputs.sgemm_operands(w["M"], w["N"], w["K"], with_c=True)
+            dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
+            run = lambda: dg.gemm_f32(dA, dB, dC, 1.0, beta)
+            path = dg.f32_path(dA, dB, dC, 1.0, beta)
+            dt = "f32"
+        else:
+            A, B = inputs.workload_operands(name)
+            dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+            dC = torch.empty(w["M"], w["N"], device=dev, dtype=torch.float16)
+            run = lambda: dg.gemm_f16_nt(dA, dB, dC)
+            path = dg.f16_nt_path(dA, dB, dC)
+            dt = "f16"
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flops(w) / (ms * 1e-3) / 1e12
+        key = name if beta is None or beta == 0.0 else "%s_beta%g" % (name, beta)
+        res[key] = {"path": path, "avg_ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_TFLOPS[dt]}
+    return res
 
 
 def main():
@@ -245,6 +287,8 @@ def main():
         "roofline": roofline,
         "roofline_by_kernel": rooflines,
     }
+    if not args.no_other_configs and args.only == "both":
+        out["other_configs"] = other_configs(dg, inputs, torch, dev)
     if not args.no_cpu_baseline and args.only == "both":
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

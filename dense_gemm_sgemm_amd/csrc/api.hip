@@ -101,7 +101,7 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const
   switch (path) {
     case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
     case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, cus, s));
-    default: return to_status(launch_f16_general(a, s));
+    default: return to_status(launch_f16_edge(a, s));
   }
 }
 

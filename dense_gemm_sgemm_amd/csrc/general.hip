@@ -88,61 +88,6 @@ __global__ __launch_bounds__(kThreads) void sgemm_scale_kernel(F32Args p) {
 }
 
 // ---------------------------------------------------------------- fp16 -------
-constexpr int kF16Bk = 32;
-
-__global__ __launch_bounds__(kThreads) void hgemm_nt_general_kernel(F16Args p, int64_t tile_base) {
-  // Both operands are staged k-major in fp32 (the half -> float conversion is
-  // exact), padded by one column so the transposing stores spread over banks.
-  __shared__ float As[kF16Bk][kTile + 1];
-  __shared__ float Bs[kF16Bk][kTile + 1];
-  const int tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;
-  const int64_t tile = tile_base + blockIdx.x, tiles_n = (p.N + kTile - 1) / kTile;
-  const int m0 = (int)(tile / tiles_n) * kTile, n0 = (int)(tile % tiles_n) * kTile;
-
-  float acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-
-  for (int k0 = 0; k0 < p.K; k0 += kF16Bk) {
-#pragma unroll
-    for (int r = 0; r < (kTile * kF16Bk) / kThreads; ++r) {
-      const int e = tid + kThreads * r;
-      const int row = e / kF16Bk, kk = e % kF16Bk, k = k0 + kk;
-      const int m = m0 + row, n = n0 + row;
-      As[kk][row] = (m < p.M && k < p.K) ? (float)p.A[(int64_t)m * p.lda + k] : 0.f;
-      Bs[kk][row] = (n < p.N && k < p.K) ? (float)p.B[(int64_t)n * p.ldb + k] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kF16Bk; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
-    }
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty + 16 * i;
-    if (m >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx + 16 * j;
-      if (n < p.N) p.C[(int64_t)m * p.ldc + n] = (half_t)acc[i][j];  // round to nearest even
-    }
-  }
-}
-
 __global__ __launch_bounds__(kThreads) void hgemm_zero_kernel(F16Args p) {
   const int64_t total = (int64_t)p.M * p.N;
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
@@ -173,11 +118,6 @@ hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream) {
   void* args[] = {&p};
   return hipLaunchKernel((const void*)sgemm_scale_kernel, dim3(fill_blocks(a.M, a.N)),
                          dim3(kThreads), args, 0, stream);
-}
-
-hipError_t launch_f16_general(const F16Args& a, hipStream_t stream) {
-  return launch_tiles((const void*)hgemm_nt_general_kernel, a, tile_count(a.M, a.N), kThreads, 0,
-                      stream);
 }
 
 hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream) {

@@ -1,0 +1,181 @@
+// fp16 C = A * B^T for every shape, leading dimension and alignment, on the
+// matrix cores.
+//
+// The boundary rule is the one of page 1 ("第 6 章 Shared Memory & Tile",
+// exercise 7 of section 6.9): loads outside the matrix read zero, stores
+// outside it are dropped.  Its motivating case on the NT page ("从零开始的 AI
+// Infra: 算子基础与GPU架构", sections 19 and 29) is a shape that is not a
+// multiple of any tile; here also K may be odd, so that rows start at any
+// 2-byte address.
+//
+//  * a workgroup of 4 waves (2 x 2) owns a 128 x 128 tile of C, each wave
+//    64 x 64 built from 16 x 16 blocks of v_mfma_f32_16x16x32_f16; two
+//    workgroups share a CU;
+//  * K is walked in slabs of 64.  Each thread fetches 4 chunks of 8 halves of
+//    A and 4 of B per slab into registers -- one 16-byte load per chunk that
+//    lies inside its row, element loads for the chunk that straddles K, zero
+//    for chunks outside the matrix -- and writes them to LDS one slab ahead
+//    of the MFMAs (two LDS stages, one barrier per slab).  The 16-byte global
+//    accesses carry only the alignment of the data (2 bytes for an odd K);
+//    the target runs with unaligned access enabled, which the compiler itself
+//    relies on for such loads;
+//  * LDS rows are 128 bytes, chunk c of row r at position c ^ ((r >> 1) & 7),
+//    the layout of the full-tile kernel, so the MFMA operand reads (lane l:
+//    row l % 16, chunk 4 s + l / 16) are free of bank conflicts;
+//  * the epilogue rounds to half, stages 16 rows at a time per wave through
+//    LDS and writes row segments of 8 halves: whole segments with one store,
+//    the segment that straddles N element by element, nothing past M or N.
+#include "hgemm_tile.hpp"
+
+namespace mi355gemm {
+namespace hedge {
+
+using hgemm::f4;
+using hgemm::h4;
+using hgemm::h8;
+using hgemm::map_tile;
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kThreads = 256;
+constexpr int WM = 64, WN = 64, kBlocks = 4;              // 4 x 4 blocks per wave
+constexpr int kRow = 2 * BK;                              // bytes per LDS slab row
+constexpr int kStage = (BM + BN) * kRow;                  // 32 KiB
+constexpr int kChunksPerThread = BM * (BK / 8) / kThreads;   // 4 per operand
+constexpr int kOutRowBytes = 2 * WN;                      // staging row: 64 halves
+constexpr int GM = 8;
+
+// One chunk of 8 halves of row `row` starting at column k: zero outside the
+// matrix, element loads where the chunk crosses K.
+__device__ __forceinline__ h8 load_chunk(const half_t* base, int64_t ld, int rows, int K, int row,
+                                         int k) {
+  h8 v = {};
+  if (row < rows && k < K) {
+    const half_t* src = base + (int64_t)row * ld + k;
+    if (k + 8 <= K) {
+      __builtin_memcpy(&v, src, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e < K) v[e] = src[e];
+    }
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, int64_t tile_base) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  map_tile<GM>(tile_base + blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // Chunk assignment: thread t fetches rows (t >> 3) + 32 i, chunk t & 7.
+  const int crow = tid >> 3, cchunk = tid & 7;
+  h8 ra[kChunksPerThread], rb[kChunksPerThread];
+  auto fetch = [&](int t) __attribute__((always_inline)) {
+    const int k = t * BK + 8 * cchunk;
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      ra[i] = load_chunk(p.A, p.lda, p.M, p.K, m0 + crow + 32 * i, k);
+      rb[i] = load_chunk(p.B, p.ldb, p.N, p.K, n0 + crow + 32 * i, k);
+    }
+  };
+  auto stash = [&](int stage) __attribute__((always_inline)) {
+    unsigned char* st = lds + stage * kStage;
+#pragma unroll
+    for (int i = 0; i < kChunksPerThread; ++i) {
+      const int r = crow + 32 * i;
+      const int pos = 16 * (cchunk ^ ((r >> 1) & 7));
+      *(h8*)(st + r * kRow + pos) = ra[i];
+      *(h8*)(st + (BM + r) * kRow + pos) = rb[i];
+    }
+  };
+
+  const int r = lane & 15, g = lane >> 4;
+  const int fr = (r >> 1) & 7;
+  f4 acc[kBlocks][kBlocks];
+#pragma unroll
+  for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int stage) __attribute__((always_inline)) {
+    const unsigned char* st = lds + stage * kStage;
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+      const int pos = 16 * ((4 * s + g) ^ fr);
+      h8 fa[kBlocks], fb[kBlocks];
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) fa[i] = *(const h8*)(st + (wm + 16 * i + r) * kRow + pos);
+#pragma unroll
+      for (int j = 0; j < kBlocks; ++j)
+        fb[j] = *(const h8*)(st + (BM + wn + 16 * j + r) * kRow + pos);
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+        for (int j = 0; j < kBlocks; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  const int nk = (p.K + BK - 1) / BK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) fetch(t + 1);
+    compute(t & 1);
+    if (t + 1 < nk) stash((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: acc[i][j][v] is C[m0 + wm + 16 i + r][n0 + wn + 16 j + 4 g + v].
+  // Row block i at a time: quads are rounded and written (8 bytes per lane)
+  // to this wave's 16-row staging area, chunk c of staging row R at slot
+  // c ^ (R & 7); then each lane writes 8 consecutive halves of one row.
+  unsigned char* out = lds + wave * (16 * kOutRowBytes);
+  const int orow = lane >> 3, ochunk = lane & 7;
+#pragma unroll
+  for (int i = 0; i < kBlocks; ++i) {
+#pragma unroll
+    for (int j = 0; j < kBlocks; ++j) {
+      h4 o;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+      const int c = 2 * j + (g >> 1);
+      *(h4*)(out + r * kOutRowBytes + 16 * (c ^ (r & 7)) + 8 * (g & 1)) = o;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int R = 8 * q + orow;
+      const h8 v = *(const h8*)(out + R * kOutRowBytes + 16 * (ochunk ^ (R & 7)));
+      const int m = m0 + wm + 16 * i + R, n = n0 + wn + 8 * ochunk;
+      if (m < p.M && n < p.N) {
+        half_t* dst = p.C + (int64_t)m * p.ldc + n;
+        if (n + 8 <= p.N) {
+          __builtin_memcpy(dst, &v, 16);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < p.N) dst[e] = v[e];
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
+}  // namespace hedge
+
+hipError_t launch_f16_edge(const F16Args& a, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((a.M + hedge::BM - 1) / hedge::BM) *
+                        ((a.N + hedge::BN - 1) / hedge::BN);
+  return launch_tiles((const void*)hedge::hgemm_nt_edge_kernel, a, tiles, hedge::kThreads, 0,
+                      stream);
+}
+
+}  // namespace mi355gemm

@@ -33,7 +33,7 @@ hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream);
 hipError_t launch_f32_general(const F32Args& a, hipStream_t stream);
 hipError_t launch_f32_mfma(const F32Args& a, hipStream_t stream);
 hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
-hipError_t launch_f16_general(const F16Args& a, hipStream_t stream);
+hipError_t launch_f16_edge(const F16Args& a, hipStream_t stream);
 hipError_t launch_f16_mfma(const F16Args& a, int cus, hipStream_t stream);
 // Output-tile width the fp16 fast path uses for an M x N product on `cus` CUs.
 int f16_mfma_tile_n(int M, int N, int cus);

@@ -251,6 +251,34 @@ def test_f16_padded_leading_dimensions(path_mode):
         assert np.all(got[:, N:] == 3.0)
 
 
+def test_f16_unaligned_operands(path_mode):
+    """Operands and C starting one element into their buffers, odd leading
+    dimensions and K tails of every length modulo 8: rows start at arbitrary
+    2-byte addresses, and the row ends fall inside 16-byte chunks."""
+    for (M, N, K) in [(133, 70, 45), (260, 129, 67), (64, 200, 130), (5, 300, 9)]:
+        lda, ldb, ldc = K + 3, K + 1, N + 5
+        A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+        bufA = torch.zeros(M * lda + 2, device=DEV, dtype=torch.float16)
+        bufB = torch.zeros(N * ldb + 2, device=DEV, dtype=torch.float16)
+        bufC = torch.full((M * ldc + 2,), 5.0, device=DEV, dtype=torch.float16)
+        dA = bufA[1:1 + M * lda].view(M, lda)[:, :K]
+        dB = bufB[1:1 + N * ldb].view(N, ldb)[:, :K]
+        dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+        dA.copy_(dev(A))
+        dB.copy_(dev(B))
+        assert dg.f16_nt_path(dA, dB, dC) == "f16_general"
+        dg.gemm_f16_nt(dA, dB, dC)
+        torch.cuda.synchronize()
+        f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
+                  oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+        # everything outside C's M x N window is untouched
+        full = bufC.cpu().numpy()
+        mask = np.ones(full.shape, bool)
+        idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+        mask[idx.ravel()] = False
+        assert np.all(full[mask] == 5.0)
+
+
 def test_f16_transpose_relation_and_determinism():
     """C(B, A) is C(A, B) transposed: both match the oracle, and runs repeat bitwise."""
     A, B = inputs.hgemm_nt_operands(512, 256, 256)

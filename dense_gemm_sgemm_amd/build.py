@@ -38,13 +38,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build")
 
 
+# Per-source compiler flags.  The fp16 tile kernel keeps two register sets of
+# operand fragments and 112-128 accumulator registers live in each of its
+# waves; LLVM's register-minimising scheduler spills less there than the
+# default one and measured about 1 % faster on 5376 x 5376 x 2048.
+FILE_FLAGS = {
+    "hgemm_mfma.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"],
+}
+
+
 def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))

@@ -84,8 +84,8 @@ MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (path) {
     case GEMM_PATH_F32_SCALE: return to_status(launch_f32_scale(a, s));
-    case GEMM_PATH_F32_MFMA: return to_status(launch_f32_mfma(a, s));
-    default: return to_status(launch_f32_general(a, s));
+    case GEMM_PATH_F32_MFMA: return to_status(launch_f32_mfma(a, cus, s));
+    default: return to_status(launch_f32_edge(a, cus, s));
   }
 }
 

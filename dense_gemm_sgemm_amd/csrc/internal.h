@@ -30,8 +30,8 @@ struct F16Args {
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the HIP
 // runtime's verdict on the launch.
 hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream);
-hipError_t launch_f32_general(const F32Args& a, hipStream_t stream);
-hipError_t launch_f32_mfma(const F32Args& a, hipStream_t stream);
+hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream);
+hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream);
 hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
 hipError_t launch_f16_edge(const F16Args& a, hipStream_t stream);
 hipError_t launch_f16_mfma(const F16Args& a, int cus, hipStream_t stream);

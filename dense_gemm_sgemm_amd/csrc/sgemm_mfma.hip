@@ -2,115 +2,157 @@
 //
 // Structure (prior art: the 2-D register-tiled, multi-stage SGEMM of the page
 // "异步拷贝与 Hopper/Blackwell 新特性", section "cp.async 与多级流水"; the
-// per-thread 8x8 FMA tile of that kernel becomes a per-wave 64x64 tile of
+// per-thread 8x8 FMA tile of that kernel becomes a per-wave tile of
 // v_mfma_f32_16x16x4_f32 products here):
 //
-//  * a 256-thread workgroup (4 waves, 2 x 2) owns a 128 x 128 tile of C;
-//  * K is walked in slabs of 16; each slab of A (128 x 16) and B (16 x 128) is
-//    fetched with 128-bit coalesced loads into registers one slab ahead and
-//    written to the other half of a double-buffered LDS ring, so one barrier
-//    per slab separates writers from readers;
-//  * a wave's 64 x 64 tile is 4 x 4 blocks of 16 x 16; per slab each block
-//    takes 4 MFMAs (K = 4 each).  Lane l = 16 g + r feeds the MFMA row/column
-//    r and, in MFMA step s, the slab column k = 4 g + s: the same bijection for
-//    both operands, so the four steps sum all 16 k of the slab.  With that
-//    mapping a lane's four A values are one 16-byte LDS read;
-//  * epilogue: alpha * acc (+ beta * C when beta != 0) straight from the
-//    accumulators (lane l, register v holds row 4 g + v, column r of a block).
+//  * a 256-thread workgroup (4 waves, 2 x 2) owns a BM x BN tile of C
+//    (128 x 128, or 64 x 64 when the larger tiles would leave CUs idle);
+//  * K is walked in slabs of 16; each slab of A (BM x 16) and B (16 x BN) is
+//    fetched with 16-byte loads into registers one slab ahead and written to
+//    the other half of a double-buffered LDS ring, so one barrier per slab
+//    separates writers from readers;
+//  * a wave's tile is blocks of 16 x 16; per slab each block takes 4 MFMAs
+//    (K = 4 each).  Lane l = 16 g + r feeds the MFMA row/column r and, in MFMA
+//    step s, the slab column k = 4 g + s: the same bijection for both
+//    operands, so the four steps sum all 16 k of the slab.  With that mapping
+//    a lane's four A values are one 16-byte LDS read;
+//  * epilogue: alpha * acc (+ beta * C when beta != 0, C is not read
+//    otherwise) straight from the accumulators (lane l, register v holds row
+//    4 g + v, column r of a block).
 //
-// Host-checked preconditions (f32_mfma_fits): M % 128 == N % 128 == K % 16 ==
-// 0, 16-byte aligned A, B, C and leading dimensions that are multiples of 4.
+// Two variants of every tile size: the full-tile kernel (M % BM == N % BN ==
+// K % 16 == 0, 16-byte aligned rows and leading dimensions that are
+// multiples of 4) loads and stores unchecked; the edge
+// kernel serves every other shape, leading dimension and alignment with the
+// boundary rule of page 1 ("第 6 章 Shared Memory & Tile", exercise 7 of
+// section 6.9): loads outside the matrix read zero, stores outside it are
+// dropped.  Its 16-byte loads of rows that are only 4-byte aligned rely on
+// the target's unaligned-access mode (the compiler emits the same loads for
+// such data itself); chunks that cross K or N are read element by element.
 #include "internal.h"
+#include "hgemm_tile.hpp"
 
 namespace mi355gemm {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int BK = 16;
 constexpr int kThreads = 256;
-constexpr int WM = 64, WN = 64;          // wave tile
-constexpr int kAStride = BK + 4;         // floats per A row in LDS
-constexpr int kBStride = BN + 4;         // floats per B row in LDS: 4 rows apart = 16 banks apart
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+template <int BM, int BN>
 struct Stage {
+  static constexpr int kAStride = BK + 4;   // floats per A row in LDS
+  static constexpr int kBStride = BN + 4;   // floats per B row in LDS: 4 rows apart = 16 banks apart
   float a[BM * kAStride];
   float b[BK * kBStride];
 };
 
+// Four consecutive floats of row `row`, columns col .. col + 3, of a matrix
+// with `rows` rows and `cols` columns: zero outside, element loads where the
+// chunk crosses the last column.
+__device__ __forceinline__ f4 load4(const float* base, int64_t ld, int rows, int cols, int row,
+                                    int col) {
+  f4 v = {0.f, 0.f, 0.f, 0.f};
+  if (row < rows && col < cols) {
+    const float* src = base + (int64_t)row * ld + col;
+    if (col + 4 <= cols) {
+      __builtin_memcpy(&v, src, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (col + e < cols) v[e] = src[e];
+    }
+  }
+  return v;
+}
+
+template <int BM, int BN, bool EDGE>
 __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int64_t tile_base) {
-  __shared__ __attribute__((aligned(16))) Stage st[2];
+  typedef Stage<BM, BN> S;
+  constexpr int WM = BM / 2, WN = BN / 2;              // wave tile
+  constexpr int IB = WM / 16, JB = WN / 16;            // blocks per wave
+  constexpr int kA = BM * BK / 4 / kThreads;           // A chunks per thread per slab
+  constexpr int kB = BK * BN / 4 / kThreads;           // B chunks per thread per slab
+  constexpr int kBRowChunks = BN / 4;
+  __shared__ __attribute__((aligned(16))) S st[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r = lane & 15;
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
 
-  const int64_t tile = tile_base + blockIdx.x;
-  const int tiles_n = p.N / BN;
-  const int m0 = (int)(tile / tiles_n) * BM, n0 = (int)(tile % tiles_n) * BN;
+  const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int tm, tn;
+  hgemm::map_tile<8>(tile_base + blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
 
-  // Global -> register assignment: two float4 of A and two of B per thread.
-  // A slab 128 x 16: chunk e -> row e / 4, column 4 (e % 4).
-  // B slab 16 x 128: chunk e -> row e / 32, column 4 (e % 32).
-  const float* gA[2];
-  const float* gB[2];
-  int lA[2], lB[2];
+  // Global -> register assignment.
+  // A slab BM x 16: chunk e -> row e / 4, column 4 (e % 4).
+  // B slab 16 x BN: chunk e -> row e / (BN / 4), column 4 (e % (BN / 4)).
+  int arow[kA], acol[kA], brow[kB], bcol[kB], lA[kA], lB[kB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kA; ++i) {
     const int e = tid + kThreads * i;
-    const int ar = e >> 2, ac = (e & 3) * 4;
-    gA[i] = p.A + (int64_t)(m0 + ar) * p.lda + ac;
-    lA[i] = ar * kAStride + ac;
-    const int br = e >> 5, bc = (e & 31) * 4;
-    gB[i] = p.B + (int64_t)br * p.ldb + n0 + bc;
-    lB[i] = br * kBStride + bc;
+    arow[i] = e >> 2;
+    acol[i] = (e & 3) * 4;
+    lA[i] = arow[i] * S::kAStride + acol[i];
   }
-  const int64_t bstep = (int64_t)BK * p.ldb;
-
-  f4 ra[2], rb[2];
-  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      ra[i] = *(const f4*)(gA[i] + k0);
-      rb[i] = *(const f4*)(gB[i] + (int64_t)(k0 / BK) * bstep);
+  for (int i = 0; i < kB; ++i) {
+    const int e = tid + kThreads * i;
+    brow[i] = e / kBRowChunks;
+    bcol[i] = (e % kBRowChunks) * 4;
+    lB[i] = brow[i] * S::kBStride + bcol[i];
+  }
+
+  f4 ra[kA], rb[kB];
+  auto fetch = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kA; ++i) {
+      if (EDGE) ra[i] = load4(p.A, p.lda, p.M, p.K, m0 + arow[i], k0 + acol[i]);
+      else ra[i] = *(const f4*)(p.A + (int64_t)(m0 + arow[i]) * p.lda + k0 + acol[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      if (EDGE) rb[i] = load4(p.B, p.ldb, p.K, p.N, k0 + brow[i], n0 + bcol[i]);
+      else rb[i] = *(const f4*)(p.B + (int64_t)(k0 + brow[i]) * p.ldb + n0 + bcol[i]);
     }
   };
-  auto stash = [&](Stage& s) {
+  auto stash = [&](S& s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(f4*)&s.a[lA[i]] = ra[i];
-      *(f4*)&s.b[lB[i]] = rb[i];
-    }
+    for (int i = 0; i < kA; ++i) *(f4*)&s.a[lA[i]] = ra[i];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) *(f4*)&s.b[lB[i]] = rb[i];
   };
 
-  f4 acc[4][4];
+  f4 acc[IB][JB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = p.K / BK;
+  const int nk = (p.K + BK - 1) / BK;
   fetch(0);
   stash(st[0]);
   __syncthreads();
 
   for (int t = 0; t < nk; ++t) {
-    const Stage& cur = st[t & 1];
+    const S& cur = st[t & 1];
     if (t + 1 < nk) fetch((t + 1) * BK);
 
-    f4 av[4];
+    f4 av[IB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = *(const f4*)&cur.a[(wm + 16 * i + r) * kAStride + 4 * g];
+    for (int i = 0; i < IB; ++i) av[i] = *(const f4*)&cur.a[(wm + 16 * i + r) * S::kAStride + 4 * g];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float bv[4];
+      float bv[JB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = cur.b[(4 * g + s) * kBStride + wn + 16 * j + r];
+      for (int j = 0; j < JB; ++j) bv[j] = cur.b[(4 * g + s) * S::kBStride + wn + 16 * j + r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < IB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[j], acc[i][j], 0, 0, 0);
     }
 
@@ -120,29 +162,50 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
 
   const float alpha = p.alpha, beta = p.beta;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float* c = p.C + (int64_t)(m0 + wm + 16 * i + 4 * g + v) * p.ldc + n0 + wn + 16 * j + r;
+        const int m = m0 + wm + 16 * i + 4 * g + v, n = n0 + wn + 16 * j + r;
+        if (EDGE && (m >= p.M || n >= p.N)) continue;
+        float* c = p.C + (int64_t)m * p.ldc + n;
         float out = alpha * acc[i][j][v];
         if (beta != 0.f) out = fmaf(beta, *c, out);
         *c = out;
       }
 }
 
+// Tile size for an M x N product: 128 x 128 while that gives every CU work,
+// 64 x 64 below.
+bool small_tiles(int M, int N, int cus) {
+  const int64_t tiles128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  return tiles128 < cus;
+}
+
+template <int BM, int BN, bool EDGE>
+hipError_t launch_tiled(const F32Args& a, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  return launch_tiles((const void*)sgemm_mfma_kernel<BM, BN, EDGE>, a, tiles, kThreads, 0, stream);
+}
+
 }  // namespace
 
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc) {
-  return M % BM == 0 && N % BN == 0 && K % BK == 0 && aligned16(A) && aligned16(B) &&
+  return M % 64 == 0 && N % 64 == 0 && K % BK == 0 && aligned16(A) && aligned16(B) &&
          aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0;
 }
 
-hipError_t launch_f32_mfma(const F32Args& a, hipStream_t stream) {
-  const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN);
-  return launch_tiles((const void*)sgemm_mfma_kernel, a, tiles, kThreads, 0, stream);
+hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
+  if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0)
+    return launch_tiled<128, 128, false>(a, stream);
+  return launch_tiled<64, 64, false>(a, stream);
+}
+
+hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream) {
+  if (small_tiles(a.M, a.N, cus)) return launch_tiled<64, 64, true>(a, stream);
+  return launch_tiled<128, 128, true>(a, stream);
 }
 
 }  // namespace mi355gemm

@@ -103,6 +103,8 @@ def test_path_selection(lib, monkeypatch):
     assert f32(lib, 256, 256, 256) == F32_MFMA and f32(lib, 1024, 1024, 1024) == F32_MFMA
     assert f32(lib, 4096, 4096, 4096, beta=0.5) == F32_MFMA
     assert f32(lib, 4000, 4096, 4096) == F32_GENERAL                # ragged M
+    assert f32(lib, 4032, 4096, 4096) == F32_MFMA                   # 64-row tiles
+    assert f32(lib, 192, 320, 48) == F32_MFMA
     assert f32(lib, 4096, 4096, 4096, A=ALIGNED + 4) == F32_GENERAL  # 4-byte aligned only
     assert f32(lib, 256, 256, 256, lda=258) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_MFMA

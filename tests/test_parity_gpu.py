@@ -77,7 +77,7 @@ def abs16(x: np.ndarray) -> np.ndarray:
 def expected_f32_path(mode, M, N, K):
     if mode == "general":
         return "f32_general"
-    return "f32_mfma" if (M % 128 == 0 and N % 128 == 0 and K % 16 == 0) else "f32_general"
+    return "f32_mfma" if (M % 64 == 0 and N % 64 == 0 and K % 16 == 0) else "f32_general"
 
 
 def expected_f16_path(mode, M, N, K):
@@ -90,7 +90,8 @@ def expected_f16_path(mode, M, N, K):
 # ----------------------------------------------------------------- fp32 -----
 F32_SHAPES = [(1, 1, 1), (3, 5, 7), (17, 33, 9), (64, 64, 16), (65, 63, 17), (128, 128, 16),
               (128, 256, 32), (256, 128, 48), (129, 127, 31), (256, 384, 160), (200, 300, 1),
-              (384, 256, 512)]
+              (384, 256, 512), (192, 320, 48), (1000, 700, 333), (2048, 2112, 64),
+              (4160, 4096, 32)]
 
 
 @pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -155,6 +156,34 @@ def test_f32_padded_leading_dimensions(path_mode):
         ref = oracle.gemm_f32(A, B, 1.0, 0.5, Cbig[:, :N])
         f32_check(got[:, :N], ref, f32_tolerance(K, 1.0, 1.0, 1.0, 0.5, 1.0))
         assert np.array_equal(got[:, N:], Cbig[:, N:])   # the padding is not written
+
+
+def test_f32_unaligned_operands(path_mode):
+    """A, B and C starting one float into their buffers with odd leading
+    dimensions, K and N tails of every length modulo 4; C outside its window
+    stays untouched, beta = 0.5 reads only the window."""
+    for (M, N, K) in [(133, 70, 45), (260, 129, 67), (64, 200, 130), (5, 301, 9)]:
+        lda, ldb, ldc = K + 3, N + 1, N + 5
+        A, B, C = inputs.sgemm_operands(M, N, K, with_c=True, dist="normal")
+        bufA = torch.zeros(M * lda + 2, device=DEV)
+        bufB = torch.zeros(K * ldb + 2, device=DEV)
+        bufC = torch.full((M * ldc + 2,), 5.0, device=DEV)
+        dA = bufA[1:1 + M * lda].view(M, lda)[:, :K]
+        dB = bufB[1:1 + K * ldb].view(K, ldb)[:, :N]
+        dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+        dA.copy_(dev(A))
+        dB.copy_(dev(B))
+        dC.copy_(dev(C))
+        assert dg.f32_path(dA, dB, dC, 1.0, 0.5) == "f32_general"
+        dg.gemm_f32(dA, dB, dC, 1.0, 0.5)
+        torch.cuda.synchronize()
+        tol = f32_tolerance(K, np.abs(A).max(), np.abs(B).max(), 1.0, 0.5, np.abs(C).max())
+        f32_check(dC.cpu().numpy(), oracle.gemm_f32(A, B, 1.0, 0.5, C), tol)
+        full = bufC.cpu().numpy()
+        mask = np.ones(full.shape, bool)
+        idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+        mask[idx.ravel()] = False
+        assert np.all(full[mask] == 5.0)
 
 
 def test_f32_deterministic():

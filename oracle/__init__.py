@@ -14,6 +14,9 @@ numpy arrays.  Definitions followed (see the header of ``oracle.c``):
 * ``gemm_f16_nt``: ``C = A*B^T`` with A[M][K], B[N][K] binary16 -- section "0.
   Naive Implementation" of the page "从零开始的 AI Infra: 算子基础与GPU架构",
   summed in double and rounded once to half (nearest, ties to even).
+* ``f16_epilogue`` / ``gemm_f16_nt_ex``: the fused write-back of page 1
+  section 6.5.4, ``C = act(A*B^T + bias) + residual`` (act none, ReLU or
+  SiLU), in double before the one rounding.
 """
 from __future__ import annotations
 
@@ -60,6 +63,7 @@ def _configure(lib):
     lib.oracle_gemm_f32_points.argtypes = [_i, _d, _p, _l, _p, _l, _d, _p, _l, _l, _p, _p, _p]
     lib.oracle_gemm_f16_nt.argtypes = [_i, _i, _i, _p, _l, _p, _l, _p, _l]
     lib.oracle_gemm_f16_nt_points.argtypes = [_i, _p, _l, _p, _l, _l, _p, _p, _p]
+    lib.oracle_f16_epilogue.argtypes = [_l, _p, _p, _p, _p, _i, _p, _l, _p]
     lib.oracle_max_threads.restype = _i
     lib.oracle_set_threads.argtypes = [_i]
     for fn in (lib.oracle_half_round_array, lib.oracle_half_decode_array, lib.oracle_gemm_f32,
@@ -192,3 +196,40 @@ def gemm_f16_nt_points(A, B, rows, cols) -> np.ndarray:
     _load().oracle_gemm_f16_nt_points(K, _ptr(A), lda, _ptr(B), ldb, rows.size,
                                       _ptr(rows), _ptr(cols), _ptr(out))
     return out
+
+
+ACTS = {"none": 0, "relu": 1, "silu": 2}
+
+
+def f16_epilogue(acc, rows, cols, bias=None, act="none", residual=None) -> np.ndarray:
+    """fp64 ``act(acc + bias[col]) + residual[row, col]`` at the outputs
+    (rows[t], cols[t]), ``acc[t]`` being the product's sum there."""
+    acc = np.ascontiguousarray(acc, dtype=np.float64).ravel()
+    rows = np.ascontiguousarray(rows, dtype=np.int32).ravel()
+    cols = np.ascontiguousarray(cols, dtype=np.int32).ravel()
+    if not (acc.size == rows.size == cols.size):
+        raise ValueError("acc, rows and cols differ in length")
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float16).ravel()
+    ldres = 0
+    if residual is not None:
+        residual, ldres = _rows(residual, np.float16)
+    out = np.empty(acc.shape, dtype=np.float64)
+    _load().oracle_f16_epilogue(acc.size, _ptr(acc), _ptr(rows), _ptr(cols),
+                                None if bias is None else _ptr(bias), ACTS[act],
+                                None if residual is None else _ptr(residual), ldres, _ptr(out))
+    return out
+
+
+def gemm_f16_nt_ex_exact(A, B, bias=None, act="none", residual=None) -> np.ndarray:
+    """fp64 ``act(A @ B.T + bias) + residual`` (before the output rounding)."""
+    acc = gemm_f16_nt_exact(A, B)
+    M, N = acc.shape
+    rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    return f16_epilogue(acc, rr, cc, bias, act, residual).reshape(M, N)
+
+
+def gemm_f16_nt_ex(A, B, bias=None, act="none", residual=None):
+    """(fp64 value, that value rounded to binary16) of the fused product."""
+    ref = gemm_f16_nt_ex_exact(A, B, bias, act, residual)
+    return ref, half_from_double(ref)

@@ -18,6 +18,8 @@
  *     (NaN included) never reaches the result.
  *
  *   fp16 "NT" GEMM         C = A * B^T,  A[M][K], B[N][K] row-major binary16
+ *     (and its fused write-back C = act(A * B^T + bias) + residual, see
+ *     oracle_f16_epilogue)
  *     The definition in section "0. Naive Implementation" of the page
  *     "从零开始的 AI Infra: 算子基础与GPU架构": C[m][n] is the sum over k of
  *     A[m*K+k] * B[n*K+k], and the result is rounded to half.  Section "19.
@@ -180,6 +182,36 @@ void oracle_gemm_f16_nt_points(int K,
     for (int k = 0; k < K; ++k)
       acc += oracle_half_to_double(A[i * lda + k]) * oracle_half_to_double(B[j * ldb + k]);
     out[t] = acc;
+  }
+}
+
+/* ---- fused write-back of an fp16 product -----------------------------------
+ * Page 1 ("第 6 章 Shared Memory & Tile", section 6.5.4) folds the work that
+ * follows a GEMM into its write-back: the column's bias is added to the
+ * accumulator, the sum goes through an activation, and the residual stream
+ * is added, before the one store of the output.  For output (i, j), in
+ * double:
+ *     v = acc + bias[j]              (bias NULL: nothing added)
+ *     v = act(v)                     act 0: v;  1 (ReLU): v if v > 0 else 0;
+ *                                    2 (SiLU): v / (1 + e^(-v))
+ *     v = v + residual[i*ldres + j]  (residual NULL: nothing added)
+ * bias and residual are binary16 bit patterns.  acc[t] is the product's sum
+ * at output (rows[t], cols[t]); out[t] is the value before rounding to half. */
+void oracle_f16_epilogue(long count, const double* acc, const int* rows, const int* cols,
+                         const uint16_t* bias, int act, const uint16_t* res, long ldres,
+                         double* out) {
+#pragma omp parallel for schedule(static)
+  for (long t = 0; t < count; ++t) {
+    const long i = rows[t], j = cols[t];
+    double v = acc[t];
+    if (bias) v += oracle_half_to_double(bias[j]);
+    if (act == 1) {
+      v = v > 0.0 ? v : 0.0;
+    } else if (act == 2) {
+      v = v / (1.0 + exp(-v));
+    }
+    if (res) v += oracle_half_to_double(res[i * ldres + j]);
+    out[t] = v;
   }
 }
 

@@ -307,6 +307,64 @@ def pin_empty_shapes():
     assert ref.shape == (2, 5) and np.all(ref == 0) and np.all(c16 == 0)
 
 
+# ---- fused write-back (page 1, section 6.5.4) ---------------------------------
+def pin_epilogue_identity_and_order():
+    A, B = inputs.hgemm_nt_operands(9, 7, 13, dist="normal")
+    assert np.array_equal(oracle.gemm_f16_nt_ex_exact(A, B), oracle.gemm_f16_nt_exact(A, B))
+    # A = 0: the product vanishes and leaves act(bias[j]) + residual[i, j].  The
+    # bias goes in before the activation (relu(-1) = 0, not -1), the residual
+    # after it (relu(-1) + 3 = 3, not relu(2) = 2), the bias is per column.
+    M, N = 3, 5
+    bias = np.array([-1.0, 2.0, -0.5, 0.0, 7.0], np.float16)
+    res = (np.arange(M * N).reshape(M, N) - 4).astype(np.float16)
+    Z, Bz = np.zeros((M, 4), np.float16), np.ones((N, 4), np.float16)
+    got = oracle.gemm_f16_nt_ex_exact(Z, Bz, bias, "relu", res)
+    assert got[0].tolist() == [0 - 4, 2 - 3, 0 - 2, 0 - 1, 7 + 0]
+    assert got[2].tolist() == [0 + 6, 2 + 7, 0 + 8, 0 + 9, 7 + 10]
+    got = oracle.gemm_f16_nt_ex_exact(Z, Bz, bias, "none", None)
+    assert np.array_equal(got, np.tile(bias.astype(np.float64), (M, 1)))
+    # residual rows may be strided
+    wide = np.zeros((M, N + 3), np.float16)
+    wide[:, :N] = res
+    assert np.array_equal(oracle.gemm_f16_nt_ex_exact(Z, Bz, None, "none", wide[:, :N]),
+                          res.astype(np.float64))
+
+
+def pin_activation_closed_forms():
+    """SiLU(x) = x * sigma(x): sigma(ln 3) = 3/4 and sigma(-ln 3) = 1/4;
+    SiLU(x) - SiLU(-x) = x and ReLU(x) - ReLU(-x) = x for every x; SiLU(x) = x
+    once e^-x is below half an ulp of 1, and -0 once e^-x overflows."""
+    x = np.array([np.log(3.0), -np.log(3.0), 0.0, 40.0, -800.0, 1.5, -2.25, 11.0, 1e-3])
+    z = np.zeros(x.size, np.int32)
+    s = oracle.f16_epilogue(x, z, z, act="silu")
+    assert abs(s[0] - 0.75 * np.log(3.0)) <= 4 * EPS64
+    assert abs(s[1] + 0.25 * np.log(3.0)) <= 4 * EPS64
+    assert s[2] == 0.0 and s[3] == 40.0 and s[4] == 0.0
+    sn = oracle.f16_epilogue(-x, z, z, act="silu")
+    assert np.all(np.abs((s - sn) - x) <= 8 * EPS64 * np.maximum(np.abs(x), 1.0))
+    r = oracle.f16_epilogue(x, z, z, act="relu")
+    rn = oracle.f16_epilogue(-x, z, z, act="relu")
+    assert np.array_equal(r - rn, x) and np.all(r >= 0)
+
+
+def pin_epilogue_rational_brute_force():
+    """ReLU with bias and residual is exact rational arithmetic: the rounded
+    oracle equals the correctly rounded exact value."""
+    rng = np.random.default_rng(31)
+    for (m, n, k) in [(2, 3, 5), (4, 4, 9), (5, 3, 17)]:
+        A = rng.normal(0, 0.5, (m, k)).astype(np.float16)
+        B = rng.normal(0, 0.5, (n, k)).astype(np.float16)
+        bias = rng.normal(0, 0.3, n).astype(np.float16)
+        res = rng.normal(0, 2.0, (m, n)).astype(np.float16)
+        _, c16 = oracle.gemm_f16_nt_ex(A, B, bias, "relu", res)
+        ex = exact_nt(A, B)
+        for i in range(m):
+            for j in range(n):
+                e = max(ex[i][j] + Fraction(float(bias[j])), Fraction(0))
+                e += Fraction(float(res[i, j]))
+                assert float(c16[i, j]) == exact_half_round(e), (m, n, k, i, j)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -359,6 +417,13 @@ MUTANTS = {
     "half_decode_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     "points_transposed": ("acc += (double)A[i * lda + k] * (double)B[(long)k * ldb + j];",
                           "acc += (double)A[i * lda + k] * (double)B[(long)j * ldb + k];"),
+    "epi_bias_by_row": ("if (bias) v += oracle_half_to_double(bias[j]);",
+                        "if (bias) v += oracle_half_to_double(bias[i]);"),
+    "epi_silu_sign": ("v = v / (1.0 + exp(-v));", "v = v / (1.0 + exp(v));"),
+    "epi_relu_leaky": ("v = v > 0.0 ? v : 0.0;", "v = v > 0.0 ? v : 0.01 * v;"),
+    "epi_residual_inside_act": ("    if (act == 1) {\n",
+                                "    if (res) v += oracle_half_to_double(res[i * ldres + j]);\n"
+                                "    if (act == 1) {\n"),
 }
 
 

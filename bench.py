@@ -148,14 +148,26 @@ def cpu_baseline(seconds: float) -> dict:
 
 def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     """Per-launch times of the workloads that are not part of the step: the
-    small SGEMMs, the 4096^3 SGEMM with beta = 0.5 and the ragged fp16 product.
-    Reported next to the step for context; not part of ``value``."""
+    small SGEMMs, the 4096^3 SGEMM with beta = 0.5, the ragged fp16 product and
+    the 5376^2 x 2048 fp16 product with the fused bias + SiLU + residual
+    write-back.  Reported next to the step for context; not part of ``value``."""
     res = {}
     cases = [("sgemm_256", 0.0), ("sgemm_1024", 0.0), ("sgemm_4096", 0.5),
-             ("hgemm_nt_5000x3001x1537", None)]
+             ("hgemm_nt_5000x3001x1537", None), ("hgemm_nt_5376x5376x2048", "fused")]
     for name, beta in cases:
         w = inputs.WORKLOADS[name]
-        if w["kind"] == "f32":
+        if beta == "fused":
+            # the fused write-back C = silu(A B^T + bias) + residual
+            A, B = inputs.workload_operands(name)
+            dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+            rng = np.random.default_rng(41)
+            dbias = torch.from_numpy(rng.normal(0, 1, w["N"]).astype(np.float16)).to(dev)
+            dres = torch.from_numpy(rng.normal(0, 1, (w["M"], w["N"])).astype(np.float16)).to(dev)
+            dC = torch.empty(w["M"], w["N"], device=dev, dtype=torch.float16)
+            run = lambda: dg.gemm_f16_nt_ex(dA, dB, dC, dbias, "silu", dres)
+            path = dg.f16_nt_ex_path(dA, dB, dC, dbias, "silu", dres)
+            dt = "f16"
+        elif w["kind"] == "f32":
             A, B, C = inputs.sgemm_operands(w["M"], w["N"], w["K"], with_c=True)
             dA, dB, dC = (torch.from_numpy(x).to(dev) for x in (A, B, C))
             run = lambda: dg.gemm_f32(dA, dB, dC, 1.0, beta)
@@ -180,7 +192,8 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
         tf = flops(w) / (ms * 1e-3) / 1e12
-        key = name if beta is None or beta == 0.0 else "%s_beta%g" % (name, beta)
+        key = (name + "_bias_silu_residual" if beta == "fused" else
+               name if beta is None or beta == 0.0 else "%s_beta%g" % (name, beta))
         res[key] = {"path": path, "avg_ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_TFLOPS[dt]}
     return res
 

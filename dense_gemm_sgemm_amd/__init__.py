@@ -8,6 +8,8 @@ library is missing the calls raise.
 
     gemm_f32(A, B, C, alpha=1.0, beta=0.0)   # C = alpha*A@B + beta*C, fp32
     gemm_f16_nt(A, B, C)                     # C = A@B.T, fp16 in/out, fp32 acc
+    gemm_f16_nt_ex(A, B, C, bias=None, act="none", residual=None)
+                                             # C = act(A@B.T + bias) + residual
 """
 from __future__ import annotations
 
@@ -18,8 +20,9 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmi355gemm.so")
 
-# Status and path codes, mirroring include/mi355gemm.h.
+# Status, path and activation codes, mirroring include/mi355gemm.h.
 GEMM_OK = 0
+ACTS = {"none": 0, "relu": 1, "silu": 2}
 PATHS = {0: "noop", 1: "f32_scale", 2: "f32_general", 3: "f32_mfma", 4: "f16_zero",
          5: "f16_general", 6: "f16_mfma"}
 
@@ -56,6 +59,10 @@ def load_library() -> ctypes.CDLL:
         lib.gemm_f32_path.restype = i
         lib.gemm_f16_nt_path.argtypes = [i, i, i, p, i, p, i, p, i]
         lib.gemm_f16_nt_path.restype = i
+        lib.gemm_f16_nt_ex.argtypes = [i, i, i, p, i, p, i, p, i, p, i, p, i, p]
+        lib.gemm_f16_nt_ex.restype = i
+        lib.gemm_f16_nt_ex_path.argtypes = [i, i, i, p, i, p, i, p, i, p, i, p, i]
+        lib.gemm_f16_nt_ex_path.restype = i
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_path_name.argtypes = [i]
@@ -84,7 +91,7 @@ def _matrix(t, name: str, dtype):
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError("%s must have unit stride along its rows (row-major)" % name)
-    ld = t.stride(0) if rows > 1 else max(1, cols)
+    ld = t.stride(0) if rows > 1 and cols > 0 else max(1, cols)
     return rows, cols, ld, (t.data_ptr() if t.numel() else None)
 
 
@@ -144,4 +151,53 @@ def f16_nt_path(A, B, C) -> str:
     N, _, ldb, pb = _matrix(B, "B", torch.float16)
     _, _, ldc, pc = _matrix(C, "C", torch.float16)
     code = load_library().gemm_f16_nt_path(M, N, K, pa, lda, pb, ldb, pc, ldc)
+    return PATHS.get(code, "error %d" % code)
+
+
+def _epilogue_args(bias, act, residual, M: int, N: int):
+    import torch
+    if act not in ACTS:
+        raise ValueError("act must be one of %s" % sorted(ACTS))
+    pbias = None
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float16 or \
+                bias.device.type != "cuda" or bias.numel() != N or \
+                (bias.dim() == 1 and N > 1 and bias.stride(0) != 1):
+            raise ValueError("bias must be a contiguous float16 GPU vector of length N = %d" % N)
+        pbias = bias.data_ptr()
+    pres, ldr = None, 0
+    if residual is not None:
+        Mr, Nr, ldr, pres = _matrix(residual, "residual", torch.float16)
+        if (Mr, Nr) != (M, N):
+            raise ValueError("residual must be %d x %d, got %s" % (M, N, tuple(residual.shape)))
+    return pbias, ACTS[act], pres, ldr
+
+
+def gemm_f16_nt_ex(A, B, C, bias=None, act: str = "none", residual=None, stream=None):
+    """Fused ``C = act(A @ B.T + bias) + residual`` for float16 A[M,K], B[N,K];
+    ``bias`` a float16 vector of length N or None, ``act`` "none", "relu" or
+    "silu", ``residual`` a float16 [M,N] tensor or None (it may be C itself).
+    fp32 accumulation and epilogue, one rounding to half.  Returns C."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float16)
+    N, K2, ldb, pb = _matrix(B, "B", torch.float16)
+    M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    pbias, code, pres, ldr = _epilogue_args(bias, act, residual, M, N)
+    _check(load_library().gemm_f16_nt_ex(M, N, K, pa, lda, pb, ldb, pbias, code, pres, ldr, pc,
+                                         ldc, _stream(stream)))
+    return C
+
+
+def f16_nt_ex_path(A, B, C, bias=None, act: str = "none", residual=None) -> str:
+    """Name of the kernel ``gemm_f16_nt_ex`` would launch for these tensors (host only)."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float16)
+    N, _, ldb, pb = _matrix(B, "B", torch.float16)
+    _, _, ldc, pc = _matrix(C, "C", torch.float16)
+    pbias, code, pres, ldr = _epilogue_args(bias, act, residual, M, N)
+    code = load_library().gemm_f16_nt_ex_path(M, N, K, pa, lda, pb, ldb, pbias, code, pres, ldr,
+                                              pc, ldc)
     return PATHS.get(code, "error %d" % code)

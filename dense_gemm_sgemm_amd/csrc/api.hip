@@ -68,6 +68,25 @@ int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int l
   return GEMM_PATH_F16_GENERAL;
 }
 
+// The fused call: the same checks plus its own arguments.  K == 0 runs the
+// edge kernel, whose product is then zero, so that C = act(bias) + residual.
+int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                  const void* bias, int act, const void* res, int ldr, const void* C, int ldc) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
+  if (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_SILU)
+    return GEMM_ERR_BAD_ARG;
+  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
+  if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1))
+    return GEMM_ERR_BAD_LD;
+  if (res != nullptr && ldr < (N > 1 ? N : 1)) return GEMM_ERR_BAD_LD;
+  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
+  if (K > 0 && !force_general() && f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) &&
+      f16_epi_fits(bias, res, ldr))
+    return GEMM_PATH_F16_MFMA;
+  return GEMM_PATH_F16_GENERAL;
+}
+
 int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
 
 }  // namespace
@@ -100,9 +119,27 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (path) {
     case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
-    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, cus, s));
-    default: return to_status(launch_f16_edge(a, s));
+    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, false, cus, s));
+    default: return to_status(launch_f16_edge(a, false, s));
   }
+}
+
+MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K, const void* A, int lda, const void* B,
+                                 int ldb, const void* bias, int act, const void* residual,
+                                 int ldr, void* C, int ldc, void* stream) {
+  const int path = f16_ex_select(M, N, K, A, lda, B, ldb, bias, act, residual, ldr, C, ldc);
+  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const int cus = check_device();
+  if (cus < 0) return cus;
+  F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+            static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
+  a.bias = static_cast<const half_t*>(bias);
+  a.res = static_cast<const half_t*>(residual);
+  a.ldr = residual ? ldr : 0;
+  a.act = act;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (path == GEMM_PATH_F16_MFMA) return to_status(launch_f16_mfma(a, true, cus, s));
+  return to_status(launch_f16_edge(a, true, s));
 }
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha, const float* A, int lda,
@@ -115,6 +152,12 @@ MI355GEMM_API int gemm_f16_nt_path(int M, int N, int K, const void* A, int lda, 
   return f16_select(M, N, K, A, lda, B, ldb, C, ldc);
 }
 
+MI355GEMM_API int gemm_f16_nt_ex_path(int M, int N, int K, const void* A, int lda, const void* B,
+                                      int ldb, const void* bias, int act, const void* residual,
+                                      int ldr, const void* C, int ldc) {
+  return f16_ex_select(M, N, K, A, lda, B, ldb, bias, act, residual, ldr, C, ldc);
+}
+
 MI355GEMM_API const char* gemm_status_string(int status) {
   switch (status) {
     case GEMM_OK: return "success";
@@ -123,6 +166,7 @@ MI355GEMM_API const char* gemm_status_string(int status) {
     case GEMM_ERR_NULL_POINTER: return "a matrix pointer that would be accessed is NULL";
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not gfx950";
     case GEMM_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
+    case GEMM_ERR_BAD_ARG: return "an enumerated argument (the activation) has no defined meaning";
     default: return "unknown status code";
   }
 }

@@ -24,7 +24,10 @@
 //    row l % 16, chunk 4 s + l / 16) are free of bank conflicts;
 //  * the epilogue rounds to half, stages 16 rows at a time per wave through
 //    LDS and writes row segments of 8 halves: whole segments with one store,
-//    the segment that straddles N element by element, nothing past M or N.
+//    the segment that straddles N element by element, nothing past M or N;
+//  * the EPI instance applies the fused write-back act(acc + bias) +
+//    residual in fp32 before the rounding, reading bias and residual element
+//    by element inside the matrix.
 #include "hgemm_tile.hpp"
 
 namespace mi355gemm {
@@ -62,6 +65,7 @@ __device__ __forceinline__ h8 load_chunk(const half_t* base, int64_t ld, int row
   return v;
 }
 
+template <bool EPI>
 __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, int64_t tile_base) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
 
@@ -143,8 +147,22 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
 #pragma unroll
     for (int j = 0; j < kBlocks; ++j) {
       h4 o;
+      if constexpr (EPI) {
+        // fused write-back, element by element inside the matrix
+        const int m = m0 + wm + 16 * i + r, n = n0 + wn + 16 * j + 4 * g;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+        for (int v = 0; v < 4; ++v) {
+          const bool in = m < p.M && n + v < p.N;
+          float x = acc[i][j][v];
+          if (p.bias && in) x += (float)p.bias[n + v];
+          x = epi_act(x, p.act);
+          if (p.res && in) x += (float)p.res[(int64_t)m * p.ldr + n + v];
+          o[v] = (half_t)x;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+      }
       const int c = 2 * j + (g >> 1);
       *(h4*)(out + r * kOutRowBytes + 16 * (c ^ (r & 7)) + 8 * (g & 1)) = o;
     }
@@ -171,11 +189,12 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
 
 }  // namespace hedge
 
-hipError_t launch_f16_edge(const F16Args& a, hipStream_t stream) {
+hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + hedge::BM - 1) / hedge::BM) *
                         ((a.N + hedge::BN - 1) / hedge::BN);
-  return launch_tiles((const void*)hedge::hgemm_nt_edge_kernel, a, tiles, hedge::kThreads, 0,
-                      stream);
+  const void* k = epi ? (const void*)hedge::hgemm_nt_edge_kernel<true>
+                      : (const void*)hedge::hgemm_nt_edge_kernel<false>;
+  return launch_tiles(k, a, tiles, hedge::kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

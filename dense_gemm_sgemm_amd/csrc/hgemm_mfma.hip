@@ -30,10 +30,18 @@ int f16_mfma_tile_n(int M, int N, int cus) {
   return cost224 < cost256 ? 224 : 256;
 }
 
-hipError_t launch_f16_mfma(const F16Args& a, int cus, hipStream_t stream) {
-  if (f16_mfma_tile_n(a.M, a.N, cus) == 224)
-    return hgemm::launch<BM, 224, BK, 4, 2, GM, 1>(a, cus, stream);
-  return hgemm::launch<BM, 256, BK, 4, 2, GM, 1>(a, cus, stream);
+hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream) {
+  const bool w224 = f16_mfma_tile_n(a.M, a.N, cus) == 224;
+  if (epi) {
+    return w224 ? hgemm::launch<BM, 224, BK, 4, 2, GM, 1, 0, true, true>(a, cus, stream)
+                : hgemm::launch<BM, 256, BK, 4, 2, GM, 1, 0, true, true>(a, cus, stream);
+  }
+  return w224 ? hgemm::launch<BM, 224, BK, 4, 2, GM, 1>(a, cus, stream)
+              : hgemm::launch<BM, 256, BK, 4, 2, GM, 1>(a, cus, stream);
+}
+
+bool f16_epi_fits(const void* bias, const void* res, int64_t ldr) {
+  return hgemm::epi_fits(bias, res, ldr);
 }
 
 }  // namespace mi355gemm

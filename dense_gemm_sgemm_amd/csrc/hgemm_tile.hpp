@@ -33,7 +33,11 @@
 //    c of staging row r at slot c ^ (r & 15): conflict-free both ways) and
 //    stores whole row segments of the wave tile to C, 16 bytes per lane;
 //  * tiles are handed out in an order that keeps each XCD's L2 warm (see
-//    map_tile).
+//    map_tile);
+//  * the EPI instances fuse the write-back of page 1 ("第 6 章 Shared Memory
+//    & Tile", section 6.5.4) into the rounding step: each accumulator quad
+//    gets its columns' bias, the activation and its residual quad in fp32
+//    before it is rounded to half.
 //
 // Preconditions (checked by the host): M % BM == N % BN == K % BK == 0,
 // 16-byte aligned A, B, C, leading dimensions that are multiples of 8.
@@ -109,7 +113,7 @@ struct TileArgs {
   int64_t tiles;
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileArgs ta) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
@@ -231,8 +235,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
 #pragma unroll
       for (int j = 0; j < C::kBlocksN; ++j) {
         h4 o;
+        if constexpr (EPI) {
+          // fused write-back: act(acc + bias[n]) + residual[m][n] in fp32
+          const int n = n0 + wn + 16 * j + 4 * g;
+          const h4 bq = p.bias ? *(const h4*)(p.bias + n) : h4{};
+          const h4 rq = p.res ? *(const h4*)(p.res + (int64_t)(m0 + wm + 16 * i + r) * p.ldr + n)
+                              : h4{};
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+          for (int v = 0; v < 4; ++v) {
+            float x = acc[i][j][v];
+            if (p.bias) x += (float)bq[v];
+            x = epi_act(x, p.act);
+            if (p.res) x += (float)rq[v];
+            o[v] = (half_t)x;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+        }
         const int c = 2 * j + (g >> 1);
         *(h4*)(stage_out + r * C::kOutRowBytes + 16 * (c ^ r) + 8 * (g & 1)) = o;
       }
@@ -381,7 +401,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
 // PERSISTENT: one workgroup per CU (at most) walking tiles; otherwise one
 // workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
-          bool PERSISTENT = true>
+          bool PERSISTENT = true, bool EPI = false>
 hipError_t launch(const F16Args& a, int cus, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN);
@@ -390,7 +410,7 @@ hipError_t launch(const F16Args& a, int cus, hipStream_t stream) {
   if (grid < 1) grid = 1;
   TileArgs ta{a, tiles};
   void* args[] = {&ta};
-  return hipLaunchKernel((const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT>,
+  return hipLaunchKernel((const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI>,
                          dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 
@@ -403,6 +423,13 @@ bool fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_
   return M % BM == 0 && N % BN == 0 && K % BK == 0 && aligned16(A) && aligned16(B) &&
          aligned16(Cp) && lda % 8 == 0 && ldb % 8 == 0 && ldc % 8 == 0 && lda < kMaxLd &&
          ldb < kMaxLd;
+}
+
+// The fused write-back reads bias and residual 4 halves (8 bytes) at a time
+// at column offsets that are multiples of 4.
+inline bool epi_fits(const void* bias, const void* res, int64_t ldr) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(bias), q = reinterpret_cast<uintptr_t>(res);
+  return (b & 7u) == 0 && (q & 7u) == 0 && (res == nullptr || ldr % 4 == 0);
 }
 
 }  // namespace hgemm

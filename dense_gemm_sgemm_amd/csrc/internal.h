@@ -18,14 +18,27 @@ struct F32Args {
   float alpha, beta;
 };
 
-// Arguments of one fp16 A*B^T call.
+// Arguments of one fp16 A*B^T call.  The last four describe the fused
+// write-back C = act(A*B^T + bias) + residual; kernels instantiated without
+// it ignore them.
 struct F16Args {
   const half_t* A;
   const half_t* B;
   half_t* C;
   int64_t lda, ldb, ldc;
   int M, N, K;
+  const half_t* bias = nullptr;   // [N] or null
+  const half_t* res = nullptr;    // [M][ldr] or null
+  int64_t ldr = 0;
+  int act = 0;                    // 0 none, 1 ReLU, 2 SiLU
 };
+
+// The fused write-back's activation on an fp32 value.
+__device__ __forceinline__ float epi_act(float x, int act) {
+  if (act == 1) return x > 0.f ? x : 0.f;
+  if (act == 2) return x / (1.f + __expf(-x));
+  return x;
+}
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the HIP
 // runtime's verdict on the launch.
@@ -33,14 +46,16 @@ hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream);
 hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream);
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream);
 hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
-hipError_t launch_f16_edge(const F16Args& a, hipStream_t stream);
-hipError_t launch_f16_mfma(const F16Args& a, int cus, hipStream_t stream);
+hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream);
+hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream);
 // Output-tile width the fp16 fast path uses for an M x N product on `cus` CUs.
 int f16_mfma_tile_n(int M, int N, int cus);
 
 // Shape and alignment conditions of the fast kernels (checked on the host).
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc);
+// Alignment conditions of the fast kernel's fused write-back.
+bool f16_epi_fits(const void* bias, const void* res, int64_t ldr);
 bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc);
 

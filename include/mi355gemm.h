@@ -42,7 +42,8 @@ enum {
   GEMM_ERR_BAD_LD = -2,            /* a leading dimension is too small               */
   GEMM_ERR_NULL_POINTER = -3,      /* NULL for an operand that would be read/written */
   GEMM_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or the current one is not gfx950 */
-  GEMM_ERR_LAUNCH = -5             /* the HIP runtime refused the kernel launch      */
+  GEMM_ERR_LAUNCH = -5,            /* the HIP runtime refused the kernel launch      */
+  GEMM_ERR_BAD_ARG = -6            /* an enumerated argument has no defined meaning  */
 };
 
 /*
@@ -91,6 +92,45 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K,
                               void* C, int ldc,
                               void* stream);
 
+/*
+ * fp16 "NT" GEMM with a fused write-back:
+ *
+ *     C = act(A * B^T + bias) + residual
+ *
+ * Page 1 ("第 6 章 Shared Memory & Tile", section 6.5.4, and exercise 6 of
+ * section 6.9) folds the work that follows a GEMM into its write-back while
+ * the accumulators are still in registers: the column's bias is added, the
+ * sum goes through an activation, and (the page's attention-output case) the
+ * residual stream is added, before the one store of C.  Here every output is
+ *
+ *     v = acc[i][j] + bias[j]          acc: the fp32 sum of gemm_f16_nt
+ *     v = act(v)                       GEMM_ACT_NONE: v, GEMM_ACT_RELU:
+ *                                      max(v, 0), GEMM_ACT_SILU: v / (1 + e^-v)
+ *     C[i][j] = half(v + residual[i][j])
+ *
+ * evaluated in fp32 and rounded to half once (nearest, ties to even).  SiLU
+ * uses the device's fast exponential.
+ *
+ *   A, B, C, lda, ldb, ldc : as for gemm_f16_nt
+ *   bias     : IEEE binary16 [N] (read), or NULL for no bias
+ *   act      : GEMM_ACT_NONE, GEMM_ACT_RELU or GEMM_ACT_SILU
+ *   residual : IEEE binary16 [M][ldr], ldr >= max(1, N) (read), or NULL.
+ *              It may be C itself (same pointer, ldr == ldc) for an in-place
+ *              residual add; any other overlap with C is undefined.
+ *
+ * K == 0 gives C = act(bias) + residual.  M == 0 or N == 0 is a no-op.  An
+ * unknown act is GEMM_ERR_BAD_ARG.
+ */
+enum { GEMM_ACT_NONE = 0, GEMM_ACT_RELU = 1, GEMM_ACT_SILU = 2 };
+
+MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K,
+                                 const void* A, int lda,
+                                 const void* B, int ldb,
+                                 const void* bias, int act,
+                                 const void* residual, int ldr,
+                                 void* C, int ldc,
+                                 void* stream);
+
 /* A static, human-readable message for a GEMM_* status code. */
 MI355GEMM_API const char* gemm_status_string(int status);
 
@@ -98,7 +138,8 @@ MI355GEMM_API const char* gemm_status_string(int status);
  * Kernel selection, exposed for inspection and testing.  These are pure host
  * functions: they make no HIP call and never touch the pointed-to memory
  * (the pointers are only checked for alignment).  They return the GEMM_PATH_*
- * value that gemm_f32 / gemm_f16_nt would launch for the same arguments, or a
+ * value that gemm_f32 / gemm_f16_nt / gemm_f16_nt_ex would launch for the
+ * same arguments, or a
  * negative GEMM_ERR_* code for arguments those calls would reject (a device
  * check excepted).
  *
@@ -108,11 +149,13 @@ MI355GEMM_API const char* gemm_status_string(int status);
 enum {
   GEMM_PATH_NOOP = 0,           /* M == 0 or N == 0: nothing is launched          */
   GEMM_PATH_F32_SCALE = 1,      /* K == 0 or alpha == 0: C = beta * C             */
-  GEMM_PATH_F32_GENERAL = 2,    /* LDS-tiled, any shape / leading dim / alignment */
-  GEMM_PATH_F32_MFMA = 3,       /* v_mfma f32 tiles; full tiles, 16-byte aligned  */
+  GEMM_PATH_F32_GENERAL = 2,    /* v_mfma f32 tiles with predicated loads/stores: */
+                                /*   any shape, leading dimension and alignment   */
+  GEMM_PATH_F32_MFMA = 3,       /* v_mfma f32 full tiles, 16-byte aligned rows    */
   GEMM_PATH_F16_ZERO = 4,       /* K == 0: C = 0                                  */
-  GEMM_PATH_F16_GENERAL = 5,    /* LDS-tiled, any shape / leading dim / alignment */
-  GEMM_PATH_F16_MFMA = 6        /* v_mfma f16 tiles; 16-byte aligned rows         */
+  GEMM_PATH_F16_GENERAL = 5,    /* v_mfma f16 tiles with predicated loads/stores: */
+                                /*   any shape, leading dimension and alignment   */
+  GEMM_PATH_F16_MFMA = 6        /* v_mfma f16 full tiles, 16-byte aligned rows    */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,
@@ -124,6 +167,13 @@ MI355GEMM_API int gemm_f16_nt_path(int M, int N, int K,
                                    const void* A, int lda,
                                    const void* B, int ldb,
                                    const void* C, int ldc);
+
+MI355GEMM_API int gemm_f16_nt_ex_path(int M, int N, int K,
+                                      const void* A, int lda,
+                                      const void* B, int ldb,
+                                      const void* bias, int act,
+                                      const void* residual, int ldr,
+                                      const void* C, int ldc);
 
 /* A static name for a GEMM_PATH_* value ("f32_mfma", ...); "?" if unknown. */
 MI355GEMM_API const char* gemm_path_name(int path);

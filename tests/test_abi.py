@@ -35,8 +35,10 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert declared_symbols() == sorted(["gemm_f32", "gemm_f16_nt", "gemm_status_string",
-                                         "gemm_f32_path", "gemm_f16_nt_path", "gemm_path_name"])
+    assert declared_symbols() == sorted(["gemm_f32", "gemm_f16_nt", "gemm_f16_nt_ex",
+                                         "gemm_status_string", "gemm_f32_path",
+                                         "gemm_f16_nt_path", "gemm_f16_nt_ex_path",
+                                         "gemm_path_name"])
 
 
 def test_library_exports_exactly_the_header(lib):
@@ -49,7 +51,7 @@ def test_library_exports_exactly_the_header(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = dg.status_string(code)
         assert s and s != "unknown status code"
     assert dg.status_string(17) == "unknown status code"
@@ -95,6 +97,36 @@ def test_entry_points_reject_bad_arguments_before_any_device_call(lib):
     assert lib.gemm_f16_nt(4, 4, 4, null, 4, p(ALIGNED), 4, p(ALIGNED), 4, null) == -3
     assert lib.gemm_f32(0, 5, 5, 1.0, null, 5, null, 5, 0.0, null, 5, null) == 0
     assert lib.gemm_f16_nt(5, 0, 5, null, 5, null, 5, null, 1, null) == 0
+
+
+def f16ex(lib, M, N, K, A=ALIGNED, B=ALIGNED, bias=ALIGNED, act=0, res=ALIGNED, ldr=None,
+          C=ALIGNED, ldc=None):
+    ldr = max(1, N) if ldr is None else ldr
+    ldc = max(1, N) if ldc is None else ldc
+    return lib.gemm_f16_nt_ex_path(M, N, K, p(A) if A else None, max(1, K), p(B) if B else None,
+                                   max(1, K), p(bias) if bias else None, act,
+                                   p(res) if res else None, ldr, p(C) if C else None, ldc)
+
+
+def test_fused_call_validation_and_paths(lib, monkeypatch):
+    assert f16ex(lib, 8, 8, 8, act=3) == -6 and f16ex(lib, 8, 8, 8, act=-1) == -6
+    assert f16ex(lib, 8, 8, 8, ldr=7) == -2
+    assert f16ex(lib, 8, 8, 8, res=0, ldr=1) == F16_GENERAL        # no residual: ldr unused
+    assert f16ex(lib, 8, 8, 8, C=0) == -3 and f16ex(lib, 8, 8, 8, A=0) == -3
+    assert f16ex(lib, 8, 8, 0, A=0, B=0) == F16_GENERAL              # K == 0: act(bias) + residual
+    assert f16ex(lib, 0, 8, 8, A=0, B=0, C=0, act=3) == -6
+    assert f16ex(lib, 0, 8, 8, A=0, B=0, C=0) == 0
+    assert f16ex(lib, 5376, 5376, 2048) == F16_MFMA
+    assert f16ex(lib, 5376, 5376, 2048, bias=0, res=0, act=2) == F16_MFMA
+    assert f16ex(lib, 5376, 5376, 2048, bias=ALIGNED + 2) == F16_GENERAL  # bias 2-byte aligned
+    assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_GENERAL          # residual rows unaligned
+    assert f16ex(lib, 5376, 5376, 2048, ldr=5380) == F16_MFMA
+    assert f16ex(lib, 5000, 3001, 1537) == F16_GENERAL
+    monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
+    assert f16ex(lib, 5376, 5376, 2048) == F16_GENERAL
+    null = None
+    assert lib.gemm_f16_nt_ex(4, 4, 4, p(ALIGNED), 4, p(ALIGNED), 4, null, 7, null, 4, p(ALIGNED),
+                              4, null) == -6
 
 
 def test_path_selection(lib, monkeypatch):

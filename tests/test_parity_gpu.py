@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 from dense_gemm_sgemm_amd import inputs
-from tolerance import f16_check, f32_check, f32_tolerance
+from tolerance import f16_check, f16_ex_check, f32_check, f32_tolerance
 
 torch = pytest.importorskip("torch")
 import dense_gemm_sgemm_amd as dg  # noqa: E402
@@ -318,6 +318,102 @@ def test_f16_transpose_relation_and_determinism():
     sab = oracle.gemm_f16_nt_exact(abs16(A), abs16(B))
     f16_check(c1, ref, sab)
     f16_check(ct.T, ref, sab)
+
+
+# ------------------------------------------------- fused write-back ------
+EPI_CASES = [("none", True, False), ("relu", True, True), ("silu", True, True),
+             ("silu", False, True), ("relu", False, False), ("none", False, False)]
+EPI_SHAPES = [(256, 224, 64), (512, 448, 128), (256, 512, 192), (133, 70, 45), (257, 255, 65)]
+
+
+def epi_operands(M, N, K, use_bias, use_res, seed=40):
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    rng = np.random.default_rng(seed)
+    bias = rng.normal(0, 1.5, N).astype(np.float16) if use_bias else None
+    res = rng.normal(0, 2.0, (M, N)).astype(np.float16) if use_res else None
+    return A, B, bias, res
+
+
+def check_ex(got, A, B, bias, act, res):
+    ref = oracle.gemm_f16_nt_ex_exact(A, B, bias, act, res)
+    sab = oracle.gemm_f16_nt_exact(abs16(A), abs16(B))
+    babs = 0.0 if bias is None else np.abs(bias.astype(np.float64))[None, :]
+    rabs = 0.0 if res is None else np.abs(res.astype(np.float64))
+    return f16_ex_check(got, ref, sab, babs, rabs)
+
+
+@pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)
+@pytest.mark.parametrize("shape", EPI_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_fused_epilogue(shape, act, use_bias, use_res, path_mode):
+    M, N, K = shape
+    A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
+    dA, dB = dev(A), dev(B)
+    dbias = dev(bias) if bias is not None else None
+    dres = dev(res) if res is not None else None
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+    want = expected_f16_path(path_mode, M, N, K).replace("f16_zero", "f16_general")
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == want
+    dg.gemm_f16_nt_ex(dA, dB, dC, dbias, act, dres)
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, act, res)
+
+
+def test_f16_fused_in_place_residual_and_saturation(path_mode):
+    """residual = C (in place), biases far out in SiLU's tails, and K = 0."""
+    M, N, K = 512, 448, 128
+    A, B, _, res = epi_operands(M, N, K, False, True)
+    bias = np.linspace(-30, 30, N).astype(np.float16)
+    dC = dev(res)
+    dg.gemm_f16_nt_ex(dev(A), dev(B), dC, dev(bias), "silu", dC)
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, "silu", res)
+    # K = 0: C = act(bias) + residual
+    Z = np.zeros((M, 0), np.float16)
+    Zb = np.zeros((N, 0), np.float16)
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+    dg.gemm_f16_nt_ex(dev(Z), dev(Zb), dC, dev(bias), "relu", dev(res))
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), Z, Zb, bias, "relu", res)
+
+
+def test_f16_fused_unaligned_bias_and_residual():
+    """bias one element into its buffer and residual rows of odd length: the
+    fused call still runs, on the edge kernel."""
+    M, N, K = 256, 224, 64
+    A, B, bias, res = epi_operands(M, N, K, True, True)
+    bbuf = torch.zeros(N + 1, device=DEV, dtype=torch.float16)
+    bbuf[1:].copy_(dev(bias))
+    rbuf = torch.zeros(M, N + 1, device=DEV, dtype=torch.float16)
+    rbuf[:, :N].copy_(dev(res))
+    dA, dB = dev(A), dev(B)
+    dC = torch.empty(M, N, device=DEV, dtype=torch.float16)
+    assert dg.f16_nt_ex_path(dA, dB, dC, bbuf[1:], "silu", rbuf[:, :N]) == "f16_general"
+    dg.gemm_f16_nt_ex(dA, dB, dC, bbuf[1:], "silu", rbuf[:, :N])
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, "silu", res)
+
+
+def test_workload_hgemm_fused():
+    """5376 x 5376 x 2048 with bias, SiLU and residual on the fast kernel,
+    sampled like the plain workload."""
+    M, N, K = 5376, 5376, 2048
+    A, B = inputs.workload_operands("hgemm_nt_5376x5376x2048")
+    rng = np.random.default_rng(41)
+    bias = rng.normal(0, 4.0, N).astype(np.float16)
+    res = rng.normal(0, 4.0, (M, N)).astype(np.float16)
+    dC = torch.empty(M, N, device=DEV, dtype=torch.float16)
+    dA, dB, dbias, dres = dev(A), dev(B), dev(bias), dev(res)
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, "silu", dres) == "f16_mfma"
+    dg.gemm_f16_nt_ex(dA, dB, dC, dbias, "silu", dres)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    rows, cols = sample_points(M, N, tile_windows(M, N, 256, 224))
+    acc = oracle.gemm_f16_nt_points(A, B, rows, cols)
+    ref = oracle.f16_epilogue(acc, rows, cols, bias, "silu", res)
+    sab = oracle.gemm_f16_nt_points(abs16(A), abs16(B), rows, cols)
+    r = f16_ex_check(got[rows, cols], ref, sab, np.abs(bias.astype(np.float64))[cols],
+                     np.abs(res.astype(np.float64))[rows, cols])
+    say("[fused 5376x5376x2048 silu] checked %d outputs, max %.2f ulp" % (r["count"], r["max_ulps"]))
 
 
 # ------------------------------------------------------ 64-bit offsets -------

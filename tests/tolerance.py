@@ -7,6 +7,11 @@ fp16: |C - half(Cref)| <= 2 ulp16(half(Cref)) + 2^-23 * sum_k |A_ik B_jk|.
   ulp16(x) = 2^(max(floor(log2|x|), -14) - 10), the binary16 spacing at x.
   The second term is the fp32-accumulation floor that matters only near zero,
   where two half ulps are smaller than any fp32 sum's rounding error.
+fp16 with the fused write-back act(A B^T + bias) + residual: the same 2-ulp
+  rule around the oracle's rounded value, with the floor widened to
+  2^-22 * (sum |A_ik B_jk| + |bias_j| + |residual_ij| + |Cref|): the fp32
+  additions of bias and residual, the activation's slope (at most 1.1 for
+  SiLU) and its fp32 evaluation each add at most a few fp32 roundings.
 """
 from __future__ import annotations
 
@@ -57,4 +62,20 @@ def f16_violations(got16: np.ndarray, ref: np.ndarray, sab: np.ndarray) -> dict:
 def f16_check(got16: np.ndarray, ref: np.ndarray, sab: np.ndarray) -> dict:
     res = f16_violations(got16, ref, sab)
     assert res["violations"] == 0, "fp16 tolerance violated: %s" % res
+    return res
+
+
+def f16_ex_check(got16: np.ndarray, ref: np.ndarray, sab: np.ndarray, bias_abs=0.0,
+                 res_abs=0.0) -> dict:
+    """The fused write-back rule; ``ref`` is the oracle's fp64 value of
+    act(A B^T + bias) + residual, ``sab`` the sums of |a*b|."""
+    ref16 = oracle.half_from_double(ref).astype(np.float64)
+    g = np.asarray(got16, dtype=np.float64)
+    diff = np.abs(g - ref16)
+    floor = 2.0 ** -22 * (sab + bias_abs + res_abs + np.abs(ref))
+    bad = ~(diff <= 2.0 * ulp16(ref16) + floor)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        worst = float(np.nanmax(diff / ulp16(ref16))) if g.size else 0.0
+    res = {"violations": int(bad.sum()), "max_ulps": worst, "count": int(g.size)}
+    assert res["violations"] == 0, "fused fp16 tolerance violated: %s" % res
     return res

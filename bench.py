@@ -31,6 +31,7 @@ PEAK_TFLOPS = {"f16": 2516.58, "f32": 157.29}
 HBM_PEAK_GBS = 8000.0
 
 H_NAME, F_NAME = "hgemm_nt_5376x5376x2048", "sgemm_4096"
+R_NAME = "hgemm_nt_5000x3001x1537"
 
 
 def parse_args():
@@ -38,8 +39,11 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["both", "hgemm", "sgemm"], default="both",
-                    help="time only one of the two products (for profiling)")
+    ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused"],
+                    default="both",
+                    help="time only one product (for profiling): one of the two step products, "
+                         "the ragged 5000x3001x1537 fp16 product or the 5376^2 x 2048 product "
+                         "with the fused bias + SiLU + residual write-back")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -56,9 +60,14 @@ def parse_args():
 # Kernel sources whose measured HBM traffic (profiles/traffic.json) stays valid
 # only while they are unchanged.
 KERNEL_SOURCES = {
-    H_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_mfma.hip"],
-    F_NAME: ["dense_gemm_sgemm_amd/csrc/sgemm_mfma.hip"],
+    H_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_mfma.hip",
+             "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
+    F_NAME: ["dense_gemm_sgemm_amd/csrc/sgemm_mfma.hip", "dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp",
+             "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
+    R_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_edge.hip", "dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp",
+             "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
 }
+KERNEL_SOURCES[H_NAME + "_bias_silu_residual"] = KERNEL_SOURCES[H_NAME]
 COPY_BYTES = 1 << 30
 
 
@@ -227,6 +236,24 @@ def main():
         assert dg.f16_nt_path(dAh, dBh, dCh) == "f16_mfma"
         parts.append((H_NAME, "f16", "hgemm_nt_kernel", flops(hw),
                       lambda: dg.gemm_f16_nt(dAh, dBh, dCh)))
+    if args.only == "hgemm_ragged":
+        rw = inputs.WORKLOADS[R_NAME]
+        Ar, Br = inputs.workload_operands(R_NAME)
+        dAr, dBr = torch.from_numpy(Ar).to(dev), torch.from_numpy(Br).to(dev)
+        dCr = torch.empty(rw["M"], rw["N"], device=dev, dtype=torch.float16)
+        assert dg.f16_nt_path(dAr, dBr, dCr) == "f16_general"
+        parts.append((R_NAME, "f16", "hgemm_nt_edge_kernel", flops(rw),
+                      lambda: dg.gemm_f16_nt(dAr, dBr, dCr)))
+    if args.only == "hgemm_fused":
+        Ah, Bh = inputs.workload_operands(H_NAME)
+        dAh, dBh = torch.from_numpy(Ah).to(dev), torch.from_numpy(Bh).to(dev)
+        rng = np.random.default_rng(41)
+        dbias = torch.from_numpy(rng.normal(0, 1, hw["N"]).astype(np.float16)).to(dev)
+        dres = torch.from_numpy(rng.normal(0, 1, (hw["M"], hw["N"])).astype(np.float16)).to(dev)
+        dCh = torch.empty(hw["M"], hw["N"], device=dev, dtype=torch.float16)
+        assert dg.f16_nt_ex_path(dAh, dBh, dCh, dbias, "silu", dres) == "f16_mfma"
+        parts.append((H_NAME + "_bias_silu_residual", "f16", "hgemm_nt_kernel", flops(hw),
+                      lambda: dg.gemm_f16_nt_ex(dAh, dBh, dCh, dbias, "silu", dres)))
     if args.only in ("both", "sgemm"):
         Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
@@ -293,8 +320,8 @@ def main():
         "dtype": "f16 (fp32 acc) + f32" if len(parts) == 2 else parts[0][1],
         "data": "synthetic (seeded uniform[-1,1); inputs resident in HBM)",
         "config": {"workload": " + ".join(p[0] for p in parts),
-                   "shapes": {p[0]: [inputs.WORKLOADS[p[0]][k] for k in ("M", "N", "K")]
-                              for p in parts},
+                   "shapes": {p[0]: [inputs.WORKLOADS[p[0].replace("_bias_silu_residual", "")][k]
+                                     for k in ("M", "N", "K")] for p in parts},
                    "parallelism": "single GPU"},
         "kernels": kernels,
         "roofline": roofline,

@@ -162,7 +162,8 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     write-back.  Reported next to the step for context; not part of ``value``."""
     res = {}
     cases = [("sgemm_256", 0.0), ("sgemm_1024", 0.0), ("sgemm_4096", 0.5),
-             ("hgemm_nt_5000x3001x1537", None), ("hgemm_nt_5376x5376x2048", "fused")]
+             ("hgemm_nt_5000x3001x1537", None), ("hgemm_nt_5376x5376x2048", "fused"),
+             ("hgemm_nt_2048x2304x768", None)]
     for name, beta in cases:
         w = inputs.WORKLOADS[name]
         if beta == "fused":

@@ -5,39 +5,61 @@
 namespace mi355gemm {
 
 namespace {
-// Tiles are 256 rows of C by 256 or 224 columns, K slabs of 64, 8 waves in a
-// 4 x 2 grid of which waves 0-3 (one per SIMD) issue the slab copies; tiles
-// are grouped 8 tile-rows at a time per XCD; one persistent workgroup per CU.
-constexpr int BM = 256, BK = 64, GM = 8;
+// Large tiles: 256 rows of C by 256 or 224 columns, 8 waves in a 4 x 2 grid
+// of which waves 0-3 (one per SIMD) issue the slab copies, one persistent
+// workgroup per CU.  Small tiles: 128 x 128, 4 waves in a 2 x 2 grid that all
+// copy, two persistent workgroups per CU.  K slabs of 64; tiles grouped 8
+// tile-rows at a time per XCD.
+constexpr int BK = 64, GM = 8;
+
+enum TileShape { kNone, k256x256, k256x224, k128x128 };
+
+// A launch takes about ceil(tiles / slots) tile-times.  A 256-row tile-time
+// is proportional to its width (one workgroup per CU); a 128 x 128 tile
+// shares its CU with a second workgroup, and its smaller operand reuse costs
+// a fifth more time per output (measured: 1.20-1.21x on 5376^2 x 2048 and
+// 8192^3), so its tile-time counts as 2 x 128 x 128 x 6/5 against 256 x BN.
+// Ties go to the larger tile.  5376 x 5376 on 256 CUs: 256 wide -> 441
+// tiles, 2 rounds x 65536; 224 wide -> 504 tiles, 2 rounds x 57344; 128 x 128
+// -> 1764 tiles, 4 rounds x 39321.  2048 x 2304: 256 wide -> 72 tiles, 1 round
+// x 65536; 128 x 128 -> 288 tiles, 1 round x 39321 (measured 1.44x faster).
+TileShape choose(int M, int N, int cus) {
+  TileShape best = kNone;
+  int64_t best_cost = 0;
+  auto consider = [&](TileShape t, int bm, int bn, int slots, int64_t tile_time) {
+    if (M % bm != 0 || N % bn != 0) return;
+    const int64_t tiles = (int64_t)(M / bm) * (N / bn);
+    const int64_t cost = (tiles + slots - 1) / slots * tile_time;
+    if (best == kNone || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  };
+  consider(k256x256, 256, 256, cus, 256 * 256);
+  consider(k256x224, 256, 224, cus, 256 * 224);
+  consider(k128x128, 128, 128, 2 * cus, 2 * 128 * 128 * 6 / 5);
+  return best;
+}
 }  // namespace
 
 bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc) {
-  return (hgemm::fits<BM, 256, BK>(M, N, K, A, lda, B, ldb, C, ldc) ||
-          hgemm::fits<BM, 224, BK>(M, N, K, A, lda, B, ldb, C, ldc));
+  return hgemm::fits<256, 256, BK>(M, N, K, A, lda, B, ldb, C, ldc) ||
+         hgemm::fits<256, 224, BK>(M, N, K, A, lda, B, ldb, C, ldc) ||
+         hgemm::fits<128, 128, BK>(M, N, K, A, lda, B, ldb, C, ldc);
 }
 
-// With one workgroup per CU at a time, a launch takes about ceil(tiles / cus)
-// tile-times, and a tile-time is proportional to the tile width: pick the
-// width with the smaller product (256 on a tie).  5376 x 5376 on 256 CUs:
-// 256 wide -> 441 tiles, 2 rounds x 256 = 512; 224 wide -> 504 tiles,
-// 2 rounds x 224 = 448.
-int f16_mfma_tile_n(int M, int N, int cus) {
-  const bool w256 = N % 256 == 0, w224 = N % 224 == 0;
-  if (!(w256 && w224)) return w256 ? 256 : 224;
-  const int64_t t256 = (int64_t)(M / BM) * (N / 256), t224 = (int64_t)(M / BM) * (N / 224);
-  const int64_t cost256 = (t256 + cus - 1) / cus * 256, cost224 = (t224 + cus - 1) / cus * 224;
-  return cost224 < cost256 ? 224 : 256;
+template <bool EPI>
+hipError_t launch_shape(const F16Args& a, int cus, hipStream_t stream) {
+  switch (choose(a.M, a.N, cus)) {
+    case k256x224: return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI>(a, cus, stream);
+    case k128x128: return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI>(a, 2 * cus, stream);
+    default: return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 0, true, EPI>(a, cus, stream);
+  }
 }
 
 hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream) {
-  const bool w224 = f16_mfma_tile_n(a.M, a.N, cus) == 224;
-  if (epi) {
-    return w224 ? hgemm::launch<BM, 224, BK, 4, 2, GM, 1, 0, true, true>(a, cus, stream)
-                : hgemm::launch<BM, 256, BK, 4, 2, GM, 1, 0, true, true>(a, cus, stream);
-  }
-  return w224 ? hgemm::launch<BM, 224, BK, 4, 2, GM, 1>(a, cus, stream)
-              : hgemm::launch<BM, 256, BK, 4, 2, GM, 1>(a, cus, stream);
+  return epi ? launch_shape<true>(a, cus, stream) : launch_shape<false>(a, cus, stream);
 }
 
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr) {

@@ -398,15 +398,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);   // drain the copies past the end of the stream
 }
 
-// PERSISTENT: one workgroup per CU (at most) walking tiles; otherwise one
-// workgroup per tile.
+// PERSISTENT: at most `slots` workgroups (as many as the GPU runs at once),
+// each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
           bool PERSISTENT = true, bool EPI = false>
-hipError_t launch(const F16Args& a, int cus, hipStream_t stream) {
+hipError_t launch(const F16Args& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN);
   const int64_t max_grid = int64_t(1) << 20;
-  int64_t grid = PERSISTENT ? (tiles < cus ? tiles : cus) : (tiles < max_grid ? tiles : max_grid);
+  int64_t grid = PERSISTENT ? (tiles < slots ? tiles : slots) : (tiles < max_grid ? tiles : max_grid);
   if (grid < 1) grid = 1;
   TileArgs ta{a, tiles};
   void* args[] = {&ta};

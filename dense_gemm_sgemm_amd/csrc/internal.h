@@ -48,8 +48,6 @@ hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream);
 hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
 hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream);
 hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream);
-// Output-tile width the fp16 fast path uses for an M x N product on `cus` CUs.
-int f16_mfma_tile_n(int M, int N, int cus);
 
 // Shape and alignment conditions of the fast kernels (checked on the host).
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,

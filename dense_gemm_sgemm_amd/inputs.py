@@ -25,6 +25,8 @@ WORKLOADS = {
                        dist="uniform"),
     "hgemm_nt_5376x5376x2048": dict(kind="f16_nt", M=5376, N=5376, K=2048, dist="uniform"),
     "hgemm_nt_5000x3001x1537": dict(kind="f16_nt", M=5000, N=3001, K=1537, dist="normal"),
+    # a fused-QKV projection: 2048 tokens x 768 hidden -> 3 x 768 outputs
+    "hgemm_nt_2048x2304x768": dict(kind="f16_nt", M=2048, N=2304, K=768, dist="uniform"),
 }
 
 

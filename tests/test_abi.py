@@ -144,6 +144,8 @@ def test_path_selection(lib, monkeypatch):
     assert f16(lib, 5376, 5376, 2048, ldb=2052) == F16_GENERAL
     assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_GENERAL
     assert f16(lib, 256, 224, 64) == F16_MFMA                       # 224-wide tiles
+    assert f16(lib, 2048, 2304, 768) == F16_MFMA                    # 128 x 128 tiles
+    assert f16(lib, 384, 640, 192) == F16_MFMA and f16(lib, 384, 640, 160) == F16_GENERAL
     assert f16(lib, 256, 256, 64, lda=(1 << 28) - 8) == F16_MFMA
     assert f16(lib, 256, 256, 64, lda=1 << 28) == F16_GENERAL         # 32-bit copy offsets
     monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")

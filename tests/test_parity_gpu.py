@@ -83,7 +83,10 @@ def expected_f32_path(mode, M, N, K):
 def expected_f16_path(mode, M, N, K):
     if mode == "general":
         return "f16_general"
-    fast = M % 256 == 0 and (N % 256 == 0 or N % 224 == 0) and K % 64 == 0
+    if K == 0:
+        return "f16_zero"
+    fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
+                            (M % 128 == 0 and N % 128 == 0))
     return "f16_mfma" if fast else "f16_general"
 
 
@@ -208,7 +211,8 @@ def test_f32_on_a_side_stream():
 # a single K slab, and several tiles in each direction.
 F16_SHAPES = [(1, 1, 1), (3, 5, 7), (17, 33, 9), (64, 64, 32), (65, 63, 33), (256, 256, 64),
               (256, 512, 128), (512, 256, 192), (257, 255, 65), (300, 200, 1), (512, 768, 320),
-              (129, 130, 1537), (256, 224, 64), (512, 448, 128), (768, 672, 256), (256, 1792, 576)]
+              (129, 130, 1537), (256, 224, 64), (512, 448, 128), (768, 672, 256), (256, 1792, 576),
+              (128, 128, 64), (384, 640, 192), (1152, 896, 448)]
 
 
 @pytest.mark.parametrize("shape", F16_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -492,7 +496,8 @@ def test_workload_sgemm_4096(beta):
 
 
 @pytest.mark.parametrize("name,path", [("hgemm_nt_5376x5376x2048", "f16_mfma"),
-                                       ("hgemm_nt_5000x3001x1537", "f16_general")])
+                                       ("hgemm_nt_5000x3001x1537", "f16_general"),
+                                       ("hgemm_nt_2048x2304x768", "f16_mfma")])
 def test_workload_hgemm(name, path):
     w = inputs.WORKLOADS[name]
     M, N = w["M"], w["N"]

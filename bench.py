@@ -32,6 +32,11 @@ HBM_PEAK_GBS = 8000.0
 
 H_NAME, F_NAME = "hgemm_nt_5376x5376x2048", "sgemm_4096"
 R_NAME = "hgemm_nt_5000x3001x1537"
+V_NAME = "hgemv_nt_1x16384x4096"
+# The decode product cycles through this many copies of its weight matrix
+# (4 x 134 MB), more than the 256 MB last-level cache, so that every launch
+# streams its weights from HBM as a decode step over many layers would.
+V_COPIES = 4
 
 
 def parse_args():
@@ -39,11 +44,13 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused"],
+    ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused",
+                                       "hgemv"],
                     default="both",
                     help="time only one product (for profiling): one of the two step products, "
-                         "the ragged 5000x3001x1537 fp16 product or the 5376^2 x 2048 product "
-                         "with the fused bias + SiLU + residual write-back")
+                         "the ragged 5000x3001x1537 fp16 product, the 5376^2 x 2048 product "
+                         "with the fused bias + SiLU + residual write-back, or the 1 x 16384 x "
+                         "4096 decode product")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -68,6 +75,8 @@ KERNEL_SOURCES = {
              "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
 }
 KERNEL_SOURCES[H_NAME + "_bias_silu_residual"] = KERNEL_SOURCES[H_NAME]
+KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sgemm_amd/csrc/internal.h",
+                          "dense_gemm_sgemm_amd/build.py"]
 COPY_BYTES = 1 << 30
 
 
@@ -107,6 +116,27 @@ def copy_calibration():
 
 def flops(w) -> float:
     return 2.0 * w["M"] * w["N"] * w["K"]
+
+
+def gemv_bytes(w) -> float:
+    """Algorithmic HBM bytes of an fp16 product: each operand read once, C written once."""
+    return 2.0 * (w["M"] * w["K"] + w["N"] * w["K"] + w["M"] * w["N"])
+
+
+def gemv_runner(dg, inputs, torch, dev):
+    """The 1 x 16384 x 4096 decode product, cycling through V_COPIES weight copies."""
+    w = inputs.WORKLOADS[V_NAME]
+    A, B = inputs.workload_operands(V_NAME)
+    dA = torch.from_numpy(A).to(dev)
+    dBs = [torch.from_numpy(B).to(dev) for _ in range(V_COPIES)]
+    dC = torch.empty(w["M"], w["N"], device=dev, dtype=torch.float16)
+    assert dg.f16_nt_path(dA, dBs[0], dC) == "f16_gemv"
+    state = {"i": 0}
+
+    def run():
+        dg.gemm_f16_nt(dA, dBs[state["i"] % V_COPIES], dC)
+        state["i"] += 1
+    return run
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -205,6 +235,24 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
         key = (name + "_bias_silu_residual" if beta == "fused" else
                name if beta is None or beta == 0.0 else "%s_beta%g" % (name, beta))
         res[key] = {"path": path, "avg_ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_TFLOPS[dt]}
+    # the decode product is bound by HBM bandwidth, not by the matrix cores
+    w = inputs.WORKLOADS[V_NAME]
+    run = gemv_runner(dg, inputs, torch, dev)
+    for _ in range(2 * V_COPIES):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    reps = 25 * V_COPIES
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = gemv_bytes(w) / (ms * 1e-3) / 1e9
+    res[V_NAME] = {"path": "f16_gemv", "avg_ms": ms, "gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+                   "tflops": flops(w) / (ms * 1e-3) / 1e12, "weight_copies": V_COPIES}
     return res
 
 
@@ -255,6 +303,9 @@ def main():
         assert dg.f16_nt_ex_path(dAh, dBh, dCh, dbias, "silu", dres) == "f16_mfma"
         parts.append((H_NAME + "_bias_silu_residual", "f16", "hgemm_nt_kernel", flops(hw),
                       lambda: dg.gemm_f16_nt_ex(dAh, dBh, dCh, dbias, "silu", dres)))
+    if args.only == "hgemv":
+        vw = inputs.WORKLOADS[V_NAME]
+        parts.append((V_NAME, "f16", "hgemv_kernel", flops(vw), gemv_runner(dg, inputs, torch, dev)))
     if args.only in ("both", "sgemm"):
         Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
@@ -299,6 +350,13 @@ def main():
         }
     rooflines = {}
     for name, kd in kernels.items():
+        if name == V_NAME:
+            gbs = gemv_bytes(inputs.WORKLOADS[V_NAME]) / (kd["avg_ms"] * 1e-3) / 1e9
+            rooflines[name] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                               "traffic": measured_traffic(name), "kernel": kd["kernel"],
+                               "workload": name}
+            continue
         rooflines[name] = {"bound": "mfma", "achieved": kd["tflops"], "peak": kd["peak_tflops"],
                            "unit": "TFLOP/s", "frac": kd["frac_of_peak"],
                            "traffic": measured_traffic(name), "kernel": kd["kernel"],

@@ -20,14 +20,19 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmi355gemm.so")
 
-# Status, path and activation codes, mirroring include/mi355gemm.h.
+# Status and activation codes, mirroring include/mi355gemm.h.
 GEMM_OK = 0
 ACTS = {"none": 0, "relu": 1, "silu": 2}
-PATHS = {0: "noop", 1: "f32_scale", 2: "f32_general", 3: "f32_mfma", 4: "f16_zero",
-         5: "f16_general", 6: "f16_mfma"}
 
 _lock = threading.Lock()
 _lib = None
+
+
+def _path_name(code: int) -> str:
+    """The library's name for a GEMM_PATH_* code, or "error <code>" for a status."""
+    if code < 0:
+        return "error %d" % code
+    return load_library().gemm_path_name(code).decode()
 
 
 class GemmError(RuntimeError):
@@ -141,7 +146,7 @@ def f32_path(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> str:
     _, _, ldc, pc = _matrix(C, "C", torch.float32)
     code = load_library().gemm_f32_path(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc,
                                         ldc)
-    return PATHS.get(code, "error %d" % code)
+    return _path_name(code)
 
 
 def f16_nt_path(A, B, C) -> str:
@@ -151,7 +156,7 @@ def f16_nt_path(A, B, C) -> str:
     N, _, ldb, pb = _matrix(B, "B", torch.float16)
     _, _, ldc, pc = _matrix(C, "C", torch.float16)
     code = load_library().gemm_f16_nt_path(M, N, K, pa, lda, pb, ldb, pc, ldc)
-    return PATHS.get(code, "error %d" % code)
+    return _path_name(code)
 
 
 def _epilogue_args(bias, act, residual, M: int, N: int):
@@ -200,4 +205,4 @@ def f16_nt_ex_path(A, B, C, bias=None, act: str = "none", residual=None) -> str:
     pbias, code, pres, ldr = _epilogue_args(bias, act, residual, M, N)
     code = load_library().gemm_f16_nt_ex_path(M, N, K, pa, lda, pb, ldb, pbias, code, pres, ldr,
                                               pc, ldc)
-    return PATHS.get(code, "error %d" % code)
+    return _path_name(code)

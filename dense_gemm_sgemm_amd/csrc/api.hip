@@ -63,8 +63,9 @@ int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int l
   if (C == nullptr) return GEMM_ERR_NULL_POINTER;
   if (K == 0) return GEMM_PATH_F16_ZERO;
   if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (!force_general() && f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc))
-    return GEMM_PATH_F16_MFMA;
+  if (force_general()) return GEMM_PATH_F16_GENERAL;
+  if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
+  if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F16_MFMA;
   return GEMM_PATH_F16_GENERAL;
 }
 
@@ -81,8 +82,9 @@ int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, in
   if (res != nullptr && ldr < (N > 1 ? N : 1)) return GEMM_ERR_BAD_LD;
   if (C == nullptr) return GEMM_ERR_NULL_POINTER;
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
-  if (K > 0 && !force_general() && f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) &&
-      f16_epi_fits(bias, res, ldr))
+  if (K == 0 || force_general()) return GEMM_PATH_F16_GENERAL;
+  if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
+  if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) && f16_epi_fits(bias, res, ldr))
     return GEMM_PATH_F16_MFMA;
   return GEMM_PATH_F16_GENERAL;
 }
@@ -120,6 +122,7 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const
   switch (path) {
     case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
     case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, false, cus, s));
+    case GEMM_PATH_F16_GEMV: return to_status(launch_f16_gemv(a, false, s));
     default: return to_status(launch_f16_edge(a, false, s));
   }
 }
@@ -139,6 +142,7 @@ MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K, const void* A, int lda, co
   a.act = act;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (path == GEMM_PATH_F16_MFMA) return to_status(launch_f16_mfma(a, true, cus, s));
+  if (path == GEMM_PATH_F16_GEMV) return to_status(launch_f16_gemv(a, true, s));
   return to_status(launch_f16_edge(a, true, s));
 }
 
@@ -180,6 +184,7 @@ MI355GEMM_API const char* gemm_path_name(int path) {
     case GEMM_PATH_F16_ZERO: return "f16_zero";
     case GEMM_PATH_F16_GENERAL: return "f16_general";
     case GEMM_PATH_F16_MFMA: return "f16_mfma";
+    case GEMM_PATH_F16_GEMV: return "f16_gemv";
     default: return "?";
   }
 }

@@ -48,6 +48,7 @@ hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream);
 hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
 hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream);
 hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream);
+hipError_t launch_f16_gemv(const F16Args& a, bool epi, hipStream_t stream);
 
 // Shape and alignment conditions of the fast kernels (checked on the host).
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -56,6 +57,8 @@ bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr);
 bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc);
+// M or N small enough for the matrix-vector kernel.
+bool f16_gemv_fits(int M, int N);
 
 // Launches `kernel(args, tile_base)` over `tiles` workgroups, split into
 // launches of at most 2^20 workgroups so that no grid exceeds the 32-bit

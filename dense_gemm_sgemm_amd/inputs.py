@@ -27,6 +27,9 @@ WORKLOADS = {
     "hgemm_nt_5000x3001x1537": dict(kind="f16_nt", M=5000, N=3001, K=1537, dist="normal"),
     # a fused-QKV projection: 2048 tokens x 768 hidden -> 3 x 768 outputs
     "hgemm_nt_2048x2304x768": dict(kind="f16_nt", M=2048, N=2304, K=768, dist="uniform"),
+    # a decode step: one token's hidden state (1 x 4096) times a 4096 -> 16384
+    # projection stored as B[16384][4096]
+    "hgemv_nt_1x16384x4096": dict(kind="f16_nt", M=1, N=16384, K=4096, dist="uniform"),
 }
 
 

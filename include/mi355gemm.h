@@ -155,7 +155,9 @@ enum {
   GEMM_PATH_F16_ZERO = 4,       /* K == 0: C = 0                                  */
   GEMM_PATH_F16_GENERAL = 5,    /* v_mfma f16 tiles with predicated loads/stores: */
                                 /*   any shape, leading dimension and alignment   */
-  GEMM_PATH_F16_MFMA = 6        /* v_mfma f16 full tiles, 16-byte aligned rows    */
+  GEMM_PATH_F16_MFMA = 6,       /* v_mfma f16 full tiles, 16-byte aligned rows    */
+  GEMM_PATH_F16_GEMV = 7        /* M <= 8 or N <= 8: matrix-vector kernel that    */
+                                /*   streams the long operand once (any ld/align) */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,

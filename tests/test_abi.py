@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
 F32_MFMA, F32_GENERAL, F32_SCALE = 3, 2, 1
-F16_MFMA, F16_GENERAL, F16_ZERO = 6, 5, 4
+F16_MFMA, F16_GENERAL, F16_ZERO, F16_GEMV = 6, 5, 4, 7
 ALIGNED = 0x100000          # fake device addresses: only their alignment is looked at
 p = ctypes.c_void_p
 
@@ -56,6 +56,7 @@ def test_status_strings(lib):
         assert s and s != "unknown status code"
     assert dg.status_string(17) == "unknown status code"
     assert lib.gemm_path_name(3) == b"f32_mfma" and lib.gemm_path_name(99) == b"?"
+    assert lib.gemm_path_name(F16_GEMV) == b"f16_gemv"
 
 
 def f32(lib, M, N, K, alpha=1.0, A=ALIGNED, lda=None, B=ALIGNED, ldb=None, beta=0.0, C=ALIGNED,
@@ -111,7 +112,8 @@ def f16ex(lib, M, N, K, A=ALIGNED, B=ALIGNED, bias=ALIGNED, act=0, res=ALIGNED, 
 def test_fused_call_validation_and_paths(lib, monkeypatch):
     assert f16ex(lib, 8, 8, 8, act=3) == -6 and f16ex(lib, 8, 8, 8, act=-1) == -6
     assert f16ex(lib, 8, 8, 8, ldr=7) == -2
-    assert f16ex(lib, 8, 8, 8, res=0, ldr=1) == F16_GENERAL        # no residual: ldr unused
+    assert f16ex(lib, 8, 8, 8, res=0, ldr=1) == F16_GEMV           # no residual: ldr unused
+    assert f16ex(lib, 16, 16, 8, res=0, ldr=1) == F16_GENERAL
     assert f16ex(lib, 8, 8, 8, C=0) == -3 and f16ex(lib, 8, 8, 8, A=0) == -3
     assert f16ex(lib, 8, 8, 0, A=0, B=0) == F16_GENERAL              # K == 0: act(bias) + residual
     assert f16ex(lib, 0, 8, 8, A=0, B=0, C=0, act=3) == -6
@@ -122,6 +124,9 @@ def test_fused_call_validation_and_paths(lib, monkeypatch):
     assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_GENERAL          # residual rows unaligned
     assert f16ex(lib, 5376, 5376, 2048, ldr=5380) == F16_MFMA
     assert f16ex(lib, 5000, 3001, 1537) == F16_GENERAL
+    assert f16ex(lib, 1, 16384, 4096, bias=ALIGNED + 2, ldr=16385) == F16_GEMV  # any alignment
+    assert f16ex(lib, 4096, 3, 4096, act=1) == F16_GEMV
+    assert f16ex(lib, 1, 16384, 0, A=0, B=0) == F16_GENERAL
     monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
     assert f16ex(lib, 5376, 5376, 2048) == F16_GENERAL
     null = None
@@ -148,7 +153,14 @@ def test_path_selection(lib, monkeypatch):
     assert f16(lib, 384, 640, 192) == F16_MFMA and f16(lib, 384, 640, 160) == F16_GENERAL
     assert f16(lib, 256, 256, 64, lda=(1 << 28) - 8) == F16_MFMA
     assert f16(lib, 256, 256, 64, lda=1 << 28) == F16_GENERAL         # 32-bit copy offsets
+    # M or N at most 8: the matrix-vector kernel, whatever the alignment
+    assert f16(lib, 1, 16384, 4096) == F16_GEMV and f16(lib, 16384, 1, 4096) == F16_GEMV
+    assert f16(lib, 8, 16384, 4096) == F16_GEMV and f16(lib, 4096, 8, 4096) == F16_GEMV
+    assert f16(lib, 1, 1, 1) == F16_GEMV and f16(lib, 3, 5, 7, A=ALIGNED + 2, lda=9) == F16_GEMV
+    assert f16(lib, 9, 16384, 4096) != F16_GEMV and f16(lib, 16384, 9, 4096) != F16_GEMV
+    assert f16(lib, 1, 16384, 0) == F16_ZERO
     monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
+    assert f16(lib, 1, 16384, 4096) == F16_GENERAL
     assert f32(lib, 4096, 4096, 4096) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_GENERAL
     assert f32(lib, 8, 8, 0) == F32_SCALE

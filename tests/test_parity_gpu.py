@@ -85,6 +85,8 @@ def expected_f16_path(mode, M, N, K):
         return "f16_general"
     if K == 0:
         return "f16_zero"
+    if min(M, N) <= 8:
+        return "f16_gemv"
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and N % 128 == 0))
     return "f16_mfma" if fast else "f16_general"
@@ -299,7 +301,8 @@ def test_f16_unaligned_operands(path_mode):
         dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
         dA.copy_(dev(A))
         dB.copy_(dev(B))
-        assert dg.f16_nt_path(dA, dB, dC) == "f16_general"
+        assert dg.f16_nt_path(dA, dB, dC) == (
+            "f16_gemv" if path_mode == "auto" and min(M, N) <= 8 else "f16_general")
         dg.gemm_f16_nt(dA, dB, dC)
         torch.cuda.synchronize()
         f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
@@ -418,6 +421,132 @@ def test_workload_hgemm_fused():
     r = f16_ex_check(got[rows, cols], ref, sab, np.abs(bias.astype(np.float64))[cols],
                      np.abs(res.astype(np.float64))[rows, cols])
     say("[fused 5376x5376x2048 silu] checked %d outputs, max %.2f ulp" % (r["count"], r["max_ulps"]))
+
+
+# ---------------------------------------------------- matrix-vector -------
+# M or N at most 8: one operand is streamed once and the other is a few
+# vectors.  Long rows (K >= 4096) are split over a workgroup, shorter ones over
+# a wave; K tails of every length modulo 8; M < N and N < M orientations.
+GEMV_SHAPES = [(1, 1, 1), (1, 7, 5), (1, 300, 9), (1, 1000, 4096), (1, 777, 4103),
+               (1, 513, 8192), (2, 300, 2055), (3, 129, 63), (8, 1030, 4096), (4, 64, 520),
+               (6, 70, 12345), (300, 1, 9), (1000, 1, 4096), (777, 3, 4103), (129, 8, 300),
+               (5, 7, 100), (7, 5, 100), (8, 8, 4100), (1, 2, 33001), (2, 100, 9001),
+               (1, 64, 2048), (3, 40, 1536)]
+
+
+@pytest.mark.parametrize("shape", GEMV_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_gemv_shapes(shape, path_mode):
+    M, N, K = shape
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    got = gpu_f16(A, B, expect=expected_f16_path(path_mode, M, N, K))
+    f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+
+
+def test_f16_gemv_strided_and_unaligned():
+    """Vectors and matrix rows at odd 2-byte offsets with padded leading
+    dimensions, and a C column written with stride ldc: nothing outside C's
+    window changes."""
+    for (M, N, K) in [(1, 500, 4099), (3, 200, 777), (500, 1, 4099), (200, 5, 777)]:
+        lda, ldb, ldc = K + 3, K + 1, N + 5
+        A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+        bufA = torch.zeros(M * lda + 2, device=DEV, dtype=torch.float16)
+        bufB = torch.zeros(N * ldb + 2, device=DEV, dtype=torch.float16)
+        bufC = torch.full((M * ldc + 2,), 5.0, device=DEV, dtype=torch.float16)
+        dA = bufA[1:1 + M * lda].view(M, lda)[:, :K]
+        dB = bufB[1:1 + N * ldb].view(N, ldb)[:, :K]
+        dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+        dA.copy_(dev(A))
+        dB.copy_(dev(B))
+        assert dg.f16_nt_path(dA, dB, dC) == "f16_gemv"
+        dg.gemm_f16_nt(dA, dB, dC)
+        torch.cuda.synchronize()
+        f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
+                  oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+        full = bufC.cpu().numpy()
+        mask = np.ones(full.shape, bool)
+        idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+        mask[idx.ravel()] = False
+        assert np.all(full[mask] == 5.0)
+
+
+def test_f16_gemv_exact_cases_and_determinism():
+    """Small-integer products are exact, sums past 2048 round ties to even,
+    and repeated runs agree bitwise."""
+    A = inputs.small_ints((1, 4096), 1, -2, 2, np.float16)
+    B = inputs.small_ints((3000, 4096), 2, -2, 2, np.float16)
+    got = gpu_f16(A, B, expect="f16_gemv")
+    exact = A.astype(np.int64) @ B.astype(np.int64).T
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
+    got_t = gpu_f16(B, A, expect="f16_gemv")
+    assert np.array_equal(got_t.T.view(np.uint16), got.view(np.uint16))
+    K = 4352
+    A = np.ones((1, K), np.float16)
+    B = np.zeros((6, K), np.float16)
+    for row, total in enumerate([2049, 2050, 2051, 2053, 2047, 4097]):
+        B[row, :total] = 1.0
+    got = gpu_f16(A, B, expect="f16_gemv")
+    assert list(got[0].astype(np.float64)) == [2048.0, 2050.0, 2052.0, 2052.0, 2047.0, 4096.0]
+    A, B = inputs.hgemm_nt_operands(4, 3000, 5000, dist="normal")
+    assert np.array_equal(gpu_f16(A, B).view(np.uint16), gpu_f16(A, B).view(np.uint16))
+
+
+GEMV_EPI_SHAPES = [(1, 300, 4096), (4, 129, 1000), (300, 2, 520), (1, 1000, 8200), (9, 8, 77)]
+
+
+@pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)
+@pytest.mark.parametrize("shape", GEMV_EPI_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_gemv_fused_epilogue(shape, act, use_bias, use_res):
+    M, N, K = shape
+    A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
+    dA, dB = dev(A), dev(B)
+    dbias = dev(bias) if bias is not None else None
+    dres = dev(res) if res is not None else None
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == "f16_gemv"
+    dg.gemm_f16_nt_ex(dA, dB, dC, dbias, act, dres)
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, act, res)
+
+
+def test_f16_gemv_fused_in_place_and_unaligned():
+    """residual = C in place, bias one element into its buffer, for both
+    orientations."""
+    for (M, N, K) in [(1, 1000, 4096), (700, 3, 999)]:
+        A, B, _, res = epi_operands(M, N, K, False, True)
+        bias = np.linspace(-30, 30, N).astype(np.float16)
+        bbuf = torch.zeros(N + 1, device=DEV, dtype=torch.float16)
+        bbuf[1:].copy_(dev(bias))
+        dC = dev(res)
+        assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], "silu", dC) == "f16_gemv"
+        dg.gemm_f16_nt_ex(dev(A), dev(B), dC, bbuf[1:], "silu", dC)
+        torch.cuda.synchronize()
+        check_ex(dC.cpu().numpy(), A, B, bias, "silu", res)
+
+
+def test_f16_gemv_many_launches():
+    """2^24 + 37 rows of 8: more row groups than one launch takes, so the
+    rows are split over two launches."""
+    M, N, K = 1, (1 << 24) + 37, 8
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    got = gpu_f16(A, B, expect="f16_gemv")
+    rows = np.zeros(200000, np.int32)
+    cols = np.concatenate([np.arange(100000), np.arange(N - 100000, N)]).astype(np.int32)
+    ref = oracle.gemm_f16_nt_points(A, B, rows, cols)
+    sab = oracle.gemm_f16_nt_points(abs16(A), abs16(B), rows, cols)
+    f16_check(got[rows, cols], ref, sab)
+    j = np.random.default_rng(5).integers(0, N, 100000).astype(np.int32)
+    f16_check(got[0, j], oracle.gemm_f16_nt_points(A, B, np.zeros_like(j), j),
+              oracle.gemm_f16_nt_points(abs16(A), abs16(B), np.zeros_like(j), j))
+
+
+def test_workload_hgemv_decode():
+    """The 1 x 16384 x 4096 decode product, every output checked."""
+    A, B = inputs.workload_operands("hgemv_nt_1x16384x4096")
+    got = gpu_f16(A, B, expect="f16_gemv")
+    res = f16_check(got, oracle.gemm_f16_nt_exact(A, B),
+                    oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+    say("[hgemv_nt_1x16384x4096] checked %d outputs, max %.2f ulp, literal-2ulp violations %d"
+        % (res["count"], res["max_ulps"], res["literal_2ulp_violations"]))
 
 
 # ------------------------------------------------------ 64-bit offsets -------

@@ -187,13 +187,13 @@ def cpu_baseline(seconds: float) -> dict:
 
 def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     """Per-launch times of the workloads that are not part of the step: the
-    small SGEMMs, the 4096^3 SGEMM with beta = 0.5, the ragged fp16 product and
+    small SGEMMs, the 4096^3 SGEMM with beta = 0.5, the ragged fp16 product,
     the 5376^2 x 2048 fp16 product with the fused bias + SiLU + residual
-    write-back.  Reported next to the step for context; not part of ``value``."""
+    write-back, the fused-QKV shape and the single-tile long-K product (split-K).  Reported next to the step for context; not part of ``value``."""
     res = {}
     cases = [("sgemm_256", 0.0), ("sgemm_1024", 0.0), ("sgemm_4096", 0.5),
              ("hgemm_nt_5000x3001x1537", None), ("hgemm_nt_5376x5376x2048", "fused"),
-             ("hgemm_nt_2048x2304x768", None)]
+             ("hgemm_nt_2048x2304x768", None), ("hgemm_nt_128x128x16384", None)]
     for name, beta in cases:
         w = inputs.WORKLOADS[name]
         if beta == "fused":

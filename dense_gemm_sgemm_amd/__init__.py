@@ -68,6 +68,15 @@ def load_library() -> ctypes.CDLL:
         lib.gemm_f16_nt_ex.restype = i
         lib.gemm_f16_nt_ex_path.argtypes = [i, i, i, p, i, p, i, p, i, p, i, p, i]
         lib.gemm_f16_nt_ex_path.restype = i
+        u64 = ctypes.c_ulonglong
+        lib.gemm_f32_splitk.argtypes = [i, i, i, f, p, i, p, i, f, p, i, i, p, u64, p]
+        lib.gemm_f32_splitk.restype = i
+        lib.gemm_f16_nt_splitk.argtypes = [i, i, i, p, i, p, i, p, i, i, p, u64, p]
+        lib.gemm_f16_nt_splitk.restype = i
+        lib.gemm_f32_splitk_workspace.argtypes = [i, i, i, i]
+        lib.gemm_f32_splitk_workspace.restype = u64
+        lib.gemm_f16_nt_splitk_workspace.argtypes = [i, i, i, i]
+        lib.gemm_f16_nt_splitk_workspace.restype = u64
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_path_name.argtypes = [i]
@@ -120,6 +129,63 @@ def gemm_f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
                                                                tuple(C.shape)))
     _check(load_library().gemm_f32(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta), pc, ldc,
                                    _stream(stream)))
+    return C
+
+
+def splitk_workspace_bytes(kind: str, M: int, N: int, K: int, splits: int = 0) -> int:
+    """Workspace bytes of ``gemm_f32_splitk`` (kind "f32") or ``gemm_f16_nt_splitk``
+    (kind "f16") for these sizes; 0 when the call would not split."""
+    lib = load_library()
+    fn = {"f32": lib.gemm_f32_splitk_workspace, "f16": lib.gemm_f16_nt_splitk_workspace}[kind]
+    return int(fn(int(M), int(N), int(K), int(splits)))
+
+
+def _workspace(workspace, need: int, device):
+    """(pointer, bytes) of a caller's workspace tensor, or of a new one."""
+    import torch
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or \
+            not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    return (workspace.data_ptr() if nbytes else None), nbytes
+
+
+def gemm_f32_splitk(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0,
+                    workspace=None, stream=None):
+    """``gemm_f32`` with K cut into ``splits`` ranges (0: the library's choice) and
+    the fp32 partial sums in ``workspace`` (a GPU tensor of at least
+    ``splitk_workspace_bytes("f32", M, N, K, splits)`` bytes; allocated here if None)."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float32)
+    K2, N, ldb, pb = _matrix(B, "B", torch.float32)
+    M2, N2, ldc, pc = _matrix(C, "C", torch.float32)
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    pw, nw = _workspace(workspace, splitk_workspace_bytes("f32", M, N, K, splits), C.device)
+    _check(load_library().gemm_f32_splitk(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta),
+                                          pc, ldc, int(splits), pw, nw, _stream(stream)))
+    return C
+
+
+def gemm_f16_nt_splitk(A, B, C, splits: int = 0, workspace=None, stream=None):
+    """``gemm_f16_nt`` with K cut into ``splits`` ranges (0: the library's choice)
+    and the fp32 partial sums in ``workspace`` (a GPU tensor of at least
+    ``splitk_workspace_bytes("f16", M, N, K, splits)`` bytes; allocated here if None)."""
+    import torch
+    M, K, lda, pa = _matrix(A, "A", torch.float16)
+    N, K2, ldb, pb = _matrix(B, "B", torch.float16)
+    M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    pw, nw = _workspace(workspace, splitk_workspace_bytes("f16", M, N, K, splits), C.device)
+    _check(load_library().gemm_f16_nt_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, int(splits), pw,
+                                             nw, _stream(stream)))
     return C
 
 

@@ -5,12 +5,21 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "internal.h"
 
 using namespace mi355gemm;
 
 namespace {
+
+// K slab depths of the tiled kernels, the granularity of split-K ranges, and
+// the shallowest ranges the automatic split-K choice makes.
+constexpr int kF32Slab = 16;
+constexpr int kF16Slab = 64;
+constexpr int kF32MinRange = 64;
+constexpr int kF16MinRange = 256;
 
 bool force_general() {
   const char* v = std::getenv("MI355GEMM_FORCE_PATH");
@@ -49,8 +58,9 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
   if (C == nullptr) return GEMM_ERR_NULL_POINTER;
   if (K == 0 || alpha == 0.f) return GEMM_PATH_F32_SCALE;
   if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (!force_general() && f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc))
-    return GEMM_PATH_F32_MFMA;
+  if (force_general()) return GEMM_PATH_F32_GENERAL;
+  if (splitk_plan(M, N, K, kF32Slab, kF32MinRange, 0).splits > 1) return GEMM_PATH_F32_SPLITK;
+  if (f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F32_MFMA;
   return GEMM_PATH_F32_GENERAL;
 }
 
@@ -65,6 +75,7 @@ int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int l
   if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
   if (force_general()) return GEMM_PATH_F16_GENERAL;
   if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
+  if (splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
   if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F16_MFMA;
   return GEMM_PATH_F16_GENERAL;
 }
@@ -84,12 +95,118 @@ int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, in
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
   if (K == 0 || force_general()) return GEMM_PATH_F16_GENERAL;
   if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
+  if (splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
   if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) && f16_epi_fits(bias, res, ldr))
     return GEMM_PATH_F16_MFMA;
   return GEMM_PATH_F16_GENERAL;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
+
+// The tiled kernel of a product that takes neither split-K nor the
+// matrix-vector kernel.
+hipError_t f32_tiled(const F32Args& a, int cus, hipStream_t s) {
+  if (!force_general() && f32_mfma_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc))
+    return launch_f32_mfma(a, cus, s);
+  return launch_f32_edge(a, cus, s);
+}
+
+hipError_t f16_tiled(const F16Args& a, bool epi, int cus, hipStream_t s) {
+  if (!force_general() && f16_mfma_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc) &&
+      (!epi || f16_epi_fits(a.bias, a.res, a.ldr)))
+    return launch_f16_mfma(a, epi, cus, s);
+  return launch_f16_edge(a, epi, s);
+}
+
+// Workspaces of the automatic split-K path, one per (device, stream): every
+// use of one is ordered on its stream, so calls on different streams never
+// share one.  An entry only grows (the old block is returned on the same
+// stream, after the work that used it), and lives until the process ends.
+struct StreamWorkspace {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<StreamWorkspace> g_ws;
+
+// A workspace of at least `bytes` for work on `s`, or nullptr; called with
+// g_ws_mutex held.  The caller keeps the lock until it has enqueued all the
+// work that uses a kept workspace, so that two host threads on one stream
+// cannot interleave their partial and reduction kernels.  *owned tells the
+// caller to return the workspace after use: so it is under stream capture,
+// where the allocation becomes part of the graph and must not be kept.
+void* stream_workspace(hipStream_t s, size_t bytes, bool* owned) {
+  *owned = false;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = nullptr;
+  if (cap != hipStreamCaptureStatusNone) {
+    if (hipMallocAsync(&p, bytes, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    *owned = true;
+    return p;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  for (StreamWorkspace& w : g_ws) {
+    if (w.dev != dev || w.stream != s) continue;
+    if (w.bytes >= bytes) return w.ptr;
+    if (hipMallocAsync(&p, bytes, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    (void)hipFreeAsync(w.ptr, s);
+    w.ptr = p;
+    w.bytes = bytes;
+    return p;
+  }
+  if (hipMallocAsync(&p, bytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_ws.push_back(StreamWorkspace{dev, s, p, bytes});
+  return p;
+}
+
+// The split-K path of the plain calls.  If no workspace can be had, the
+// tiled kernel runs instead.
+hipError_t f32_auto_split(F32Args a, int cus, hipStream_t s) {
+  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF32Slab, kF32MinRange, 0);
+  std::unique_lock<std::mutex> lock(g_ws_mutex);
+  bool owned = false;
+  void* ws = stream_workspace(s, plan.bytes, &owned);
+  if (owned || ws == nullptr) lock.unlock();
+  if (ws == nullptr) return f32_tiled(a, cus, s);
+  a.sk = splitk_args(plan, a.M, a.N, ws);
+  const hipError_t e = launch_f32_splitk(a, s);
+  const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
+  return e != hipSuccess ? e : f;
+}
+
+hipError_t f16_auto_split(F16Args a, bool epi, int cus, hipStream_t s) {
+  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF16Slab, kF16MinRange, 0);
+  std::unique_lock<std::mutex> lock(g_ws_mutex);
+  bool owned = false;
+  void* ws = stream_workspace(s, plan.bytes, &owned);
+  if (owned || ws == nullptr) lock.unlock();
+  if (ws == nullptr) return f16_tiled(a, epi, cus, s);
+  a.sk = splitk_args(plan, a.M, a.N, ws);
+  const hipError_t e = launch_f16_splitk(a, epi, s);
+  const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
+  return e != hipSuccess ? e : f;
+}
+
+// Checks a caller's workspace against a plan.
+bool workspace_ok(const SplitPlan& plan, const void* ws, unsigned long long bytes) {
+  return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 15u) == 0 && bytes >= plan.bytes;
+}
 
 }  // namespace
 
@@ -106,6 +223,7 @@ MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int
   switch (path) {
     case GEMM_PATH_F32_SCALE: return to_status(launch_f32_scale(a, s));
     case GEMM_PATH_F32_MFMA: return to_status(launch_f32_mfma(a, cus, s));
+    case GEMM_PATH_F32_SPLITK: return to_status(f32_auto_split(a, cus, s));
     default: return to_status(launch_f32_edge(a, cus, s));
   }
 }
@@ -123,6 +241,7 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const
     case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
     case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, false, cus, s));
     case GEMM_PATH_F16_GEMV: return to_status(launch_f16_gemv(a, false, s));
+    case GEMM_PATH_F16_SPLITK: return to_status(f16_auto_split(a, false, cus, s));
     default: return to_status(launch_f16_edge(a, false, s));
   }
 }
@@ -143,7 +262,74 @@ MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K, const void* A, int lda, co
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (path == GEMM_PATH_F16_MFMA) return to_status(launch_f16_mfma(a, true, cus, s));
   if (path == GEMM_PATH_F16_GEMV) return to_status(launch_f16_gemv(a, true, s));
+  if (path == GEMM_PATH_F16_SPLITK) return to_status(f16_auto_split(a, true, cus, s));
   return to_status(launch_f16_edge(a, true, s));
+}
+
+MI355GEMM_API int gemm_f32_splitk(int M, int N, int K, float alpha, const float* A, int lda,
+                                  const float* B, int ldb, float beta, float* C, int ldc,
+                                  int splits, void* workspace, unsigned long long workspace_bytes,
+                                  void* stream) {
+  const int path = f32_select(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  SplitPlan plan;
+  if (path != GEMM_PATH_F32_SCALE && (splits > 0 || path == GEMM_PATH_F32_SPLITK))
+    plan = splitk_plan(M, N, K, kF32Slab, kF32MinRange, splits);
+  if (plan.splits > 1 && !workspace_ok(plan, workspace, workspace_bytes))
+    return GEMM_ERR_WORKSPACE;
+  const int cus = check_device();
+  if (cus < 0) return cus;
+  F32Args a{A, B, C, lda, ldb, ldc, M, N, K, alpha, beta};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.splits > 1) {
+    a.sk = splitk_args(plan, M, N, workspace);
+    return to_status(launch_f32_splitk(a, s));
+  }
+  switch (path) {
+    case GEMM_PATH_F32_SCALE: return to_status(launch_f32_scale(a, s));
+    case GEMM_PATH_F32_MFMA: return to_status(launch_f32_mfma(a, cus, s));
+    case GEMM_PATH_F32_SPLITK: return to_status(f32_tiled(a, cus, s));   // splits == 1
+    default: return to_status(launch_f32_edge(a, cus, s));
+  }
+}
+
+MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K, const void* A, int lda, const void* B,
+                                     int ldb, void* C, int ldc, int splits, void* workspace,
+                                     unsigned long long workspace_bytes, void* stream) {
+  const int path = f16_select(M, N, K, A, lda, B, ldb, C, ldc);
+  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  SplitPlan plan;
+  if (path != GEMM_PATH_F16_ZERO && (splits > 0 || path == GEMM_PATH_F16_SPLITK))
+    plan = splitk_plan(M, N, K, kF16Slab, kF16MinRange, splits);
+  if (plan.splits > 1 && !workspace_ok(plan, workspace, workspace_bytes))
+    return GEMM_ERR_WORKSPACE;
+  const int cus = check_device();
+  if (cus < 0) return cus;
+  F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+            static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.splits > 1) {
+    a.sk = splitk_args(plan, M, N, workspace);
+    return to_status(launch_f16_splitk(a, false, s));
+  }
+  switch (path) {
+    case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
+    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, false, cus, s));
+    case GEMM_PATH_F16_GEMV: return to_status(launch_f16_gemv(a, false, s));
+    case GEMM_PATH_F16_SPLITK: return to_status(f16_tiled(a, false, cus, s));   // splits == 1
+    default: return to_status(launch_f16_edge(a, false, s));
+  }
+}
+
+MI355GEMM_API unsigned long long gemm_f32_splitk_workspace(int M, int N, int K, int splits) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return splitk_plan(M, N, K, kF32Slab, kF32MinRange, splits).bytes;
+}
+
+MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int K, int splits) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (splits <= 0 && f16_gemv_fits(M, N)) return 0;
+  return splitk_plan(M, N, K, kF16Slab, kF16MinRange, splits).bytes;
 }
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha, const float* A, int lda,
@@ -171,6 +357,9 @@ MI355GEMM_API const char* gemm_status_string(int status) {
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not gfx950";
     case GEMM_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
     case GEMM_ERR_BAD_ARG: return "an enumerated argument (the activation) has no defined meaning";
+    case GEMM_ERR_WORKSPACE:
+      return "the split-K workspace is NULL, smaller than the size query reports, or not 16-byte "
+             "aligned";
     default: return "unknown status code";
   }
 }
@@ -185,6 +374,8 @@ MI355GEMM_API const char* gemm_path_name(int path) {
     case GEMM_PATH_F16_GENERAL: return "f16_general";
     case GEMM_PATH_F16_MFMA: return "f16_mfma";
     case GEMM_PATH_F16_GEMV: return "f16_gemv";
+    case GEMM_PATH_F16_SPLITK: return "f16_splitk";
+    case GEMM_PATH_F32_SPLITK: return "f32_splitk";
     default: return "?";
   }
 }

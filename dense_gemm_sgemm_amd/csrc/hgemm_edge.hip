@@ -65,16 +65,27 @@ __device__ __forceinline__ h8 load_chunk(const half_t* base, int64_t ld, int row
   return v;
 }
 
-template <bool EPI>
+// MODE 0 writes C = half(acc), MODE 1 the fused write-back, MODE 2 the fp32
+// partial product of one split-K range (workgroup b: range b / tiles, tile
+// b % tiles) to the tile-padded workspace.
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, int64_t tile_base) {
+  constexpr bool EPI = MODE == 1;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int64_t item = tile_base + blockIdx.x;
+  int split = 0;
+  if constexpr (MODE == 2) {
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    split = (int)(item / tiles);
+    item -= split * tiles;
+  }
   int tm, tn;
-  map_tile<GM>(tile_base + blockIdx.x, tiles_m, tiles_n, tm, tn);
+  map_tile<GM>(item, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Chunk assignment: thread t fetches rows (t >> 3) + 32 i, chunk t & 7.
@@ -125,15 +136,33 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
     }
   };
 
-  const int nk = (p.K + BK - 1) / BK;
-  fetch(0);
+  // Slabs t0 .. t1 - 1: all of K, or this workgroup's split-K range.
+  int t0 = 0, t1 = (p.K + BK - 1) / BK;
+  if constexpr (MODE == 2) {
+    t0 = split * p.sk.per;
+    t1 = t0 + p.sk.per < t1 ? t0 + p.sk.per : t1;
+  }
+  fetch(t0);
   stash(0);
   __syncthreads();
-  for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) fetch(t + 1);
-    compute(t & 1);
-    if (t + 1 < nk) stash((t + 1) & 1);
+  for (int t = t0; t < t1; ++t) {
+    if (t + 1 < t1) fetch(t + 1);
+    compute((t - t0) & 1);
+    if (t + 1 < t1) stash((t + 1 - t0) & 1);
     __syncthreads();
+  }
+
+  if constexpr (MODE == 2) {
+    // acc[i][j][v] is row m0 + wm + 16 i + r, column n0 + wn + 16 j + 4 g + v:
+    // one 16-byte store per block into the padded workspace, no bounds.
+    float* ws = p.sk.ws + split * p.sk.split_stride;
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+      for (int j = 0; j < kBlocks; ++j)
+        *(f4*)(ws + (int64_t)(m0 + wm + 16 * i + r) * p.sk.ld + n0 + wn + 16 * j + 4 * g) =
+            acc[i][j];
+    return;
   }
 
   // Epilogue: acc[i][j][v] is C[m0 + wm + 16 i + r][n0 + wn + 16 j + 4 g + v].
@@ -192,9 +221,16 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
 hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + hedge::BM - 1) / hedge::BM) *
                         ((a.N + hedge::BN - 1) / hedge::BN);
-  const void* k = epi ? (const void*)hedge::hgemm_nt_edge_kernel<true>
-                      : (const void*)hedge::hgemm_nt_edge_kernel<false>;
+  const void* k = epi ? (const void*)hedge::hgemm_nt_edge_kernel<1>
+                      : (const void*)hedge::hgemm_nt_edge_kernel<0>;
   return launch_tiles(k, a, tiles, hedge::kThreads, 0, stream);
+}
+
+hipError_t launch_f16_partials(const F16Args& a, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((a.M + hedge::BM - 1) / hedge::BM) *
+                        ((a.N + hedge::BN - 1) / hedge::BN);
+  return launch_tiles((const void*)hedge::hgemm_nt_edge_kernel<2>, a, tiles * a.sk.splits,
+                      hedge::kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

@@ -8,6 +8,16 @@ namespace mi355gemm {
 
 typedef _Float16 half_t;
 
+// Split-K: the K slabs of a product are cut into `splits` ranges of `per`
+// slabs; the partial product of range s over output tile (tm, tn) goes to
+// ws[s * split_stride + m * ld + n] (fp32, the workspace padded to whole
+// tiles), and a second kernel adds the ranges in order s = 0, 1, ... .
+struct SplitK {
+  float* ws = nullptr;
+  int64_t ld = 0, split_stride = 0;
+  int splits = 1, per = 0;
+};
+
 // Arguments of one fp32 call, as validated by the C-ABI layer.
 struct F32Args {
   const float* A;
@@ -16,6 +26,7 @@ struct F32Args {
   int64_t lda, ldb, ldc;
   int M, N, K;
   float alpha, beta;
+  SplitK sk;                      // split-K partial products (partial kernels only)
 };
 
 // Arguments of one fp16 A*B^T call.  The last four describe the fused
@@ -31,6 +42,7 @@ struct F16Args {
   const half_t* res = nullptr;    // [M][ldr] or null
   int64_t ldr = 0;
   int act = 0;                    // 0 none, 1 ReLU, 2 SiLU
+  SplitK sk;                      // split-K partial products (partial kernels only)
 };
 
 // The fused write-back's activation on an fp32 value.
@@ -39,6 +51,18 @@ __device__ __forceinline__ float epi_act(float x, int act) {
   if (act == 2) return x / (1.f + __expf(-x));
   return x;
 }
+
+// A split-K decision: `splits` K ranges of `per` slabs each and the workspace
+// bytes they need; splits == 1 means no split.
+struct SplitPlan {
+  int splits = 1, per = 0;
+  size_t bytes = 0;
+};
+// For an M x N x K product walked in slabs of `slab`: `requested` ranges if
+// positive (at most one per slab), else the library's choice with ranges of
+// at least `min_range` of K.
+SplitPlan splitk_plan(int M, int N, int K, int slab, int min_range, int requested);
+SplitK splitk_args(const SplitPlan& plan, int M, int N, void* workspace);
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the HIP
 // runtime's verdict on the launch.
@@ -49,6 +73,11 @@ hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
 hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream);
 hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream);
 hipError_t launch_f16_gemv(const F16Args& a, bool epi, hipStream_t stream);
+// Split-K: the partial products (a.sk filled in), then the reduction.
+hipError_t launch_f16_partials(const F16Args& a, hipStream_t stream);
+hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);
+hipError_t launch_f16_splitk(const F16Args& a, bool epi, hipStream_t stream);
+hipError_t launch_f32_splitk(const F32Args& a, hipStream_t stream);
 
 // Shape and alignment conditions of the fast kernels (checked on the host).
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,

@@ -67,7 +67,10 @@ __device__ __forceinline__ f4 load4(const float* base, int64_t ld, int rows, int
   return v;
 }
 
-template <int BM, int BN, bool EDGE>
+// SPLIT instances write the fp32 partial product of one split-K range
+// (workgroup b: range b / tiles, tile b % tiles) to the tile-padded
+// workspace instead of C.
+template <int BM, int BN, bool EDGE, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int64_t tile_base) {
   typedef Stage<BM, BN> S;
   constexpr int WM = BM / 2, WN = BN / 2;              // wave tile
@@ -83,8 +86,15 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
   const int wm = (wave >> 1) * WM, wn = (wave & 1) * WN;
 
   const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+  int64_t item = tile_base + blockIdx.x;
+  int split = 0;
+  if constexpr (SPLIT) {
+    const int64_t tiles = (int64_t)tiles_m * tiles_n;
+    split = (int)(item / tiles);
+    item -= split * tiles;
+  }
   int tm, tn;
-  hgemm::map_tile<8>(tile_base + blockIdx.x, tiles_m, tiles_n, tm, tn);
+  hgemm::map_tile<8>(item, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Global -> register assignment.
@@ -132,14 +142,19 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
 #pragma unroll
     for (int j = 0; j < JB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (p.K + BK - 1) / BK;
-  fetch(0);
+  // Slabs t0 .. t1 - 1: all of K, or this workgroup's split-K range.
+  int t0 = 0, t1 = (p.K + BK - 1) / BK;
+  if constexpr (SPLIT) {
+    t0 = split * p.sk.per;
+    t1 = t0 + p.sk.per < t1 ? t0 + p.sk.per : t1;
+  }
+  fetch(t0 * BK);
   stash(st[0]);
   __syncthreads();
 
-  for (int t = 0; t < nk; ++t) {
-    const S& cur = st[t & 1];
-    if (t + 1 < nk) fetch((t + 1) * BK);
+  for (int t = t0; t < t1; ++t) {
+    const S& cur = st[(t - t0) & 1];
+    if (t + 1 < t1) fetch((t + 1) * BK);
 
     f4 av[IB];
 #pragma unroll
@@ -156,8 +171,21 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[j], acc[i][j], 0, 0, 0);
     }
 
-    if (t + 1 < nk) stash(st[(t + 1) & 1]);
+    if (t + 1 < t1) stash(st[(t + 1 - t0) & 1]);
     __syncthreads();
+  }
+
+  if constexpr (SPLIT) {
+    float* ws = p.sk.ws + split * p.sk.split_stride;
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          ws[(int64_t)(m0 + wm + 16 * i + 4 * g + v) * p.sk.ld + n0 + wn + 16 * j + r] =
+              acc[i][j][v];
+    return;
   }
 
   const float alpha = p.alpha, beta = p.beta;
@@ -206,6 +234,17 @@ hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
 hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream) {
   if (small_tiles(a.M, a.N, cus)) return launch_tiled<64, 64, true>(a, stream);
   return launch_tiled<128, 128, true>(a, stream);
+}
+
+// Split-K partial products over 128 x 128 tiles: the full-tile kernel where
+// the shape and alignment allow it, the edge kernel otherwise.
+hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream) {
+  const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  const bool full = a.M % 128 == 0 && a.N % 128 == 0 &&
+                    f32_mfma_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc);
+  const void* k = full ? (const void*)sgemm_mfma_kernel<128, 128, false, true>
+                       : (const void*)sgemm_mfma_kernel<128, 128, true, true>;
+  return launch_tiles(k, a, tiles * a.sk.splits, kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

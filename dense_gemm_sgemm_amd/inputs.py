@@ -30,6 +30,8 @@ WORKLOADS = {
     # a decode step: one token's hidden state (1 x 4096) times a 4096 -> 16384
     # projection stored as B[16384][4096]
     "hgemv_nt_1x16384x4096": dict(kind="f16_nt", M=1, N=16384, K=4096, dist="uniform"),
+    # a single 128 x 128 output tile over a long K
+    "hgemm_nt_128x128x16384": dict(kind="f16_nt", M=128, N=128, K=16384, dist="uniform"),
 }
 
 

@@ -9,8 +9,18 @@
  *    ldx sits at X[i*ldx + j].  Dimensions and leading dimensions are int;
  *    offsets are computed in 64 bits.
  *  - A, B and C are DEVICE pointers, allocated and owned by the caller.  The
- *    library never allocates, frees or keeps a pointer after the call returns,
- *    and keeps no per-call state.
+ *    library keeps no pointer to them after the call returns.  It allocates
+ *    nothing, with one exception: when gemm_f32, gemm_f16_nt or
+ *    gemm_f16_nt_ex choose split-K (GEMM_PATH_*_SPLITK), they need an fp32
+ *    workspace, which the library takes from the stream-ordered allocator
+ *    (hipMallocAsync on the call's stream) and keeps for later calls on the
+ *    same device and stream, growing it when a larger one is needed, until
+ *    the process ends.  Under stream capture the workspace is allocated and
+ *    returned inside the captured work instead.  gemm_f32_splitk /
+ *    gemm_f16_nt_splitk take a caller-owned workspace and allocate nothing.
+ *    A kept workspace is tied to the stream handle: destroying a stream
+ *    while its work still runs and creating one that reuses the handle is
+ *    not supported.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *    Work is enqueued on it and the call returns without synchronising; a
  *    fault during execution surfaces at the caller's next synchronisation.
@@ -43,7 +53,9 @@ enum {
   GEMM_ERR_NULL_POINTER = -3,      /* NULL for an operand that would be read/written */
   GEMM_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or the current one is not gfx950 */
   GEMM_ERR_LAUNCH = -5,            /* the HIP runtime refused the kernel launch      */
-  GEMM_ERR_BAD_ARG = -6            /* an enumerated argument has no defined meaning  */
+  GEMM_ERR_BAD_ARG = -6,           /* an enumerated argument has no defined meaning  */
+  GEMM_ERR_WORKSPACE = -7          /* split-K workspace NULL, too small or not       */
+                                   /*   16-byte aligned                               */
 };
 
 /*
@@ -131,6 +143,52 @@ MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K,
                                  void* C, int ldc,
                                  void* stream);
 
+/*
+ * Split-K with a caller-owned workspace.
+ *
+ * Page 1 ("第 6 章 Shared Memory & Tile", section 6.5.6) cuts the K dimension
+ * of a product with few output tiles into ranges, computes each range's
+ * partial sums in its own blocks and adds them afterwards.  Here the partial
+ * sums of range s are fp32 tiles of 128 x 128 in the workspace, and a second
+ * kernel adds the ranges in the fixed order 0, 1, ..., so results repeat
+ * bitwise from run to run; the final write-back is the one of gemm_f32
+ * (alpha * sum + beta * C) or of gemm_f16_nt (rounding to half).
+ *
+ *   M .. ldc, stream : as for gemm_f32 / gemm_f16_nt
+ *   splits    : number of K ranges.  <= 0 lets the library choose exactly as
+ *               gemm_f32 / gemm_f16_nt would (which may be no split, or the
+ *               matrix-vector kernel); 1 never splits; larger values are cut
+ *               to at most one range per 16 (fp32) or 64 (fp16) elements of K.
+ *   workspace : device memory, 16-byte aligned, of at least
+ *               workspace_bytes >= gemm_*_splitk_workspace(M, N, K, splits)
+ *               bytes; written and read by the call's kernels on `stream`,
+ *               so it must not be in use by other work until they finish.
+ *               May be NULL when that size is 0.
+ *
+ * Returns GEMM_ERR_WORKSPACE if a split is chosen and the workspace is NULL,
+ * too small or misaligned; otherwise as gemm_f32 / gemm_f16_nt.
+ */
+MI355GEMM_API int gemm_f32_splitk(int M, int N, int K, float alpha,
+                                  const float* A, int lda,
+                                  const float* B, int ldb,
+                                  float beta, float* C, int ldc,
+                                  int splits, void* workspace,
+                                  unsigned long long workspace_bytes,
+                                  void* stream);
+
+MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K,
+                                     const void* A, int lda,
+                                     const void* B, int ldb,
+                                     void* C, int ldc,
+                                     int splits, void* workspace,
+                                     unsigned long long workspace_bytes,
+                                     void* stream);
+
+/* Workspace bytes the calls above need for these sizes and `splits`; 0 when
+ * they would not split (negative M, N, K or splits count as no split). */
+MI355GEMM_API unsigned long long gemm_f32_splitk_workspace(int M, int N, int K, int splits);
+MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int K, int splits);
+
 /* A static, human-readable message for a GEMM_* status code. */
 MI355GEMM_API const char* gemm_status_string(int status);
 
@@ -156,8 +214,10 @@ enum {
   GEMM_PATH_F16_GENERAL = 5,    /* v_mfma f16 tiles with predicated loads/stores: */
                                 /*   any shape, leading dimension and alignment   */
   GEMM_PATH_F16_MFMA = 6,       /* v_mfma f16 full tiles, 16-byte aligned rows    */
-  GEMM_PATH_F16_GEMV = 7        /* M <= 8 or N <= 8: matrix-vector kernel that    */
+  GEMM_PATH_F16_GEMV = 7,       /* M <= 8 or N <= 8: matrix-vector kernel that    */
                                 /*   streams the long operand once (any ld/align) */
+  GEMM_PATH_F16_SPLITK = 8,     /* few output tiles, long K: K cut into ranges,   */
+  GEMM_PATH_F32_SPLITK = 9      /*   fp32 partials, ordered reduction             */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,

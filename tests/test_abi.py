@@ -17,6 +17,7 @@ HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
 F32_MFMA, F32_GENERAL, F32_SCALE = 3, 2, 1
 F16_MFMA, F16_GENERAL, F16_ZERO, F16_GEMV = 6, 5, 4, 7
+F16_SPLITK, F32_SPLITK = 8, 9
 ALIGNED = 0x100000          # fake device addresses: only their alignment is looked at
 p = ctypes.c_void_p
 
@@ -36,6 +37,9 @@ def declared_symbols():
 
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted(["gemm_f32", "gemm_f16_nt", "gemm_f16_nt_ex",
+                                         "gemm_f32_splitk", "gemm_f16_nt_splitk",
+                                         "gemm_f32_splitk_workspace",
+                                         "gemm_f16_nt_splitk_workspace",
                                          "gemm_status_string", "gemm_f32_path",
                                          "gemm_f16_nt_path", "gemm_f16_nt_ex_path",
                                          "gemm_path_name"])
@@ -51,7 +55,7 @@ def test_library_exports_exactly_the_header(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = dg.status_string(code)
         assert s and s != "unknown status code"
     assert dg.status_string(17) == "unknown status code"
@@ -164,6 +168,55 @@ def test_path_selection(lib, monkeypatch):
     assert f32(lib, 4096, 4096, 4096) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_GENERAL
     assert f32(lib, 8, 8, 0) == F32_SCALE
+
+
+def test_split_k_plans(lib, monkeypatch):
+    """Split-K applies to products with K >= 2048 whose 128 x 128 output tiles
+    leave room for at least three ranges in one wave of 512 workgroups (two per
+    CU of a 256-CU part); ranges at least 256 (fp16) or 64 (fp32) deep, at most
+    64 of them, at most one per K slab."""
+    monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
+    assert f16(lib, 512, 512, 16384) == F16_SPLITK and f16(lib, 128, 128, 16384) == F16_SPLITK
+    assert f16(lib, 1024, 1024, 4096) == F16_SPLITK and f16(lib, 300, 200, 5000) == F16_SPLITK
+    assert f16(lib, 512, 512, 1024) == F16_MFMA                       # K below 2048
+    assert f16(lib, 2048, 2048, 8192) == F16_MFMA                     # 256 tiles
+    assert f16(lib, 1536, 1536, 4096) == F16_SPLITK                   # 144 tiles: 3 ranges
+    assert f16(lib, 1792, 1792, 4096) == F16_MFMA                     # 196 tiles: 2 ranges
+    assert f16(lib, 8, 512, 16384) == F16_GEMV                        # the vector kernel first
+    assert f32(lib, 512, 512, 16384) == F32_SPLITK and f32(lib, 100, 70, 3000) == F32_SPLITK
+    assert f32(lib, 4096, 4096, 4096) == F32_MFMA and f32(lib, 512, 512, 16384, alpha=0.0) == 1
+    ws16, ws32 = lib.gemm_f16_nt_splitk_workspace, lib.gemm_f32_splitk_workspace
+    # 16 tiles -> 32 ranges of 8 slabs of 64
+    assert ws16(512, 512, 16384, 0) == 32 * 512 * 512 * 4
+    assert ws16(1, 4096, 4096, 0) == 0 and ws16(512, 512, 1024, 0) == 0
+    assert ws16(100, 100, 1000, 3) == 3 * 128 * 128 * 4                # 16 slabs -> 6, 6, 4
+    assert ws16(100, 100, 1000, 5) == 4 * 128 * 128 * 4                # 16 slabs -> 4 x 4
+    assert ws16(64, 64, 100, 50) == 2 * 128 * 128 * 4                  # one range per slab
+    assert ws16(64, 64, 100, 1) == 0 and ws16(0, 64, 100, 4) == 0 and ws16(64, 64, -1, 4) == 0
+    assert ws16(300, 200, 5000, 0) == 16 * 384 * 256 * 4               # 19 asked: 79 slabs / 5
+    assert ws16(128, 128, 65536, 0) == 64 * 128 * 128 * 4              # at most 64 ranges
+    assert ws32(512, 512, 16384, 0) == 32 * 512 * 512 * 4
+    assert ws32(300, 257, 4099, 0) == 52 * 384 * 384 * 4               # 257 slabs / 56 -> 5 each
+    assert ws32(130, 129, 40, 7) == 3 * 256 * 256 * 4                  # 3 slabs of 16
+    monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
+    assert f16(lib, 512, 512, 16384) == F16_GENERAL and f32(lib, 512, 512, 16384) == F32_GENERAL
+
+
+def test_split_k_workspace_errors_need_no_device(lib):
+    null = None
+    a = p(ALIGNED)
+    assert lib.gemm_f16_nt_splitk(512, 512, 16384, a, 16384, a, 16384, a, 512, 0, null, 0,
+                                  null) == -7
+    need = lib.gemm_f16_nt_splitk_workspace(512, 512, 16384, 0)
+    assert lib.gemm_f16_nt_splitk(512, 512, 16384, a, 16384, a, 16384, a, 512, 0, a, need - 1,
+                                  null) == -7
+    assert lib.gemm_f16_nt_splitk(512, 512, 16384, a, 16384, a, 16384, a, 512, 0,
+                                  p(ALIGNED + 8), need, null) == -7
+    assert lib.gemm_f32_splitk(256, 256, 4096, 1.0, a, 4096, a, 256, 0.0, a, 256, 4, null, 0,
+                               null) == -7
+    assert lib.gemm_f32_splitk(-1, 256, 4096, 1.0, a, 4096, a, 256, 0.0, a, 256, 4, null, 0,
+                               null) == -1
+    assert lib.gemm_f16_nt_splitk(0, 5, 5, null, 5, null, 5, null, 5, 4, null, 0, null) == 0
 
 
 def test_python_binding_validates_tensors(lib):

@@ -74,9 +74,21 @@ def abs16(x: np.ndarray) -> np.ndarray:
     return (x.view(np.uint16) & np.uint16(0x7FFF)).view(np.float16)
 
 
+def splitk_auto(M, N, K, slab):
+    """The library's split-K rule: K of at least 2048 and at least three ranges,
+    with tiles x ranges within 512 workgroups (tiles of 128 x 128) and ranges
+    at least 256 (fp16) or 64 (fp32) deep."""
+    tiles = -(-M // 128) * -(-N // 128)
+    if K < 2048:
+        return False
+    return min(512 // tiles, K // (256 if slab == 64 else 64), 64) >= 3
+
+
 def expected_f32_path(mode, M, N, K):
     if mode == "general":
         return "f32_general"
+    if splitk_auto(M, N, K, 16):
+        return "f32_splitk"
     return "f32_mfma" if (M % 64 == 0 and N % 64 == 0 and K % 16 == 0) else "f32_general"
 
 
@@ -87,6 +99,8 @@ def expected_f16_path(mode, M, N, K):
         return "f16_zero"
     if min(M, N) <= 8:
         return "f16_gemv"
+    if splitk_auto(M, N, K, 64):
+        return "f16_splitk"
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and N % 128 == 0))
     return "f16_mfma" if fast else "f16_general"
@@ -547,6 +561,125 @@ def test_workload_hgemv_decode():
                     oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
     say("[hgemv_nt_1x16384x4096] checked %d outputs, max %.2f ulp, literal-2ulp violations %d"
         % (res["count"], res["max_ulps"], res["literal_2ulp_violations"]))
+
+
+# ----------------------------------------------------------- split-K -------
+# Long K over few output tiles: K cut into ranges whose fp32 partial sums are
+# added in a fixed order.  Automatic (through gemm_f16_nt / gemm_f32, with a
+# stream-ordered workspace) and explicit (caller's split count and workspace).
+SPLITK_SHAPES = [(128, 128, 16384), (512, 512, 16384), (300, 200, 5000), (1000, 700, 3001),
+                 (136, 264, 2111), (64, 1000, 4099)]
+
+
+@pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_splitk_auto(shape):
+    M, N, K = shape
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    got = gpu_f16(A, B, expect="f16_splitk")
+    f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 64])
+def test_f16_splitk_explicit(splits):
+    for (M, N, K) in [(256, 384, 4096), (133, 70, 1045), (9, 300, 777)]:
+        A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+        dA, dB = dev(A), dev(B)
+        dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+        dg.gemm_f16_nt_splitk(dA, dB, dC, splits=splits)
+        torch.cuda.synchronize()
+        f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
+                  oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+
+
+def test_f16_splitk_unaligned_workspace_reuse_and_determinism():
+    """Operands at odd offsets with padded rows, a C window inside a larger
+    buffer, one workspace reused by two calls in a row (the second smaller),
+    and repeated runs bitwise equal."""
+    ws = torch.empty(dg.splitk_workspace_bytes("f16", 300, 200, 5001, 9), dtype=torch.uint8,
+                     device=DEV)
+    for (M, N, K, splits) in [(300, 200, 5001, 9), (133, 70, 2049, 4)]:
+        lda, ldb, ldc = K + 3, K + 1, N + 5
+        A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+        bufA = torch.zeros(M * lda + 2, device=DEV, dtype=torch.float16)
+        bufB = torch.zeros(N * ldb + 2, device=DEV, dtype=torch.float16)
+        bufC = torch.full((M * ldc + 2,), 5.0, device=DEV, dtype=torch.float16)
+        dA = bufA[1:1 + M * lda].view(M, lda)[:, :K]
+        dB = bufB[1:1 + N * ldb].view(N, ldb)[:, :K]
+        dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+        dA.copy_(dev(A))
+        dB.copy_(dev(B))
+        assert dg.splitk_workspace_bytes("f16", M, N, K, splits) <= ws.numel()
+        dg.gemm_f16_nt_splitk(dA, dB, dC, splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        first = bufC.cpu().numpy()
+        f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
+                  oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+        mask = np.ones(first.shape, bool)
+        idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+        mask[idx.ravel()] = False
+        assert np.all(first[mask] == 5.0)
+        dg.gemm_f16_nt_splitk(dA, dB, dC, splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bufC.cpu().numpy().view(np.uint16), first.view(np.uint16))
+
+
+@pytest.mark.parametrize("shape", [(512, 448, 8192), (300, 200, 5000)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES[:4])
+def test_f16_splitk_fused(shape, act, use_bias, use_res):
+    M, N, K = shape
+    A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
+    dA, dB = dev(A), dev(B)
+    dbias = dev(bias) if bias is not None else None
+    dres = dev(res) if res is not None else None
+    dC = dres if dres is not None else torch.full((M, N), float("nan"), device=DEV,
+                                                  dtype=torch.float16)
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == "f16_splitk"
+    dg.gemm_f16_nt_ex(dA, dB, dC, dbias, act, dres)          # in place when there is a residual
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, act, res)
+
+
+F32_SPLITK_SHAPES = [(512, 512, 16384), (100, 70, 3000), (300, 257, 4099), (128, 384, 2048)]
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+@pytest.mark.parametrize("shape", F32_SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_splitk_auto(shape, beta):
+    M, N, K = shape
+    A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
+    got = gpu_f32(A, B, 1.0, beta, C.copy(), expect="f32_splitk")
+    tol = f32_tolerance(K, np.abs(A).max(), np.abs(B).max(), 1.0, beta, np.abs(C).max())
+    f32_check(got, oracle.gemm_f32(A, B, 1.0, beta, C), tol)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 33])
+def test_f32_splitk_explicit(splits):
+    for (M, N, K, alpha, beta) in [(256, 256, 4096, -0.5, 1.25), (133, 70, 1043, 2.0, 0.0),
+                                   (64, 200, 530, 1.0, -1.0)]:
+        A, B, C = inputs.sgemm_operands(M, N, K, with_c=True, dist="normal")
+        dA, dB, dC = dev(A), dev(B), dev(C)
+        dg.gemm_f32_splitk(dA, dB, dC, alpha, beta, splits=splits)
+        torch.cuda.synchronize()
+        tol = f32_tolerance(K, np.abs(A).max(), np.abs(B).max(), alpha, beta, np.abs(C).max())
+        f32_check(dC.cpu().numpy(), oracle.gemm_f32(A, B, alpha, beta, C), tol)
+
+
+def test_f32_splitk_beta_zero_ignores_nan_and_repeats():
+    A, B, _ = inputs.sgemm_operands(512, 512, 16384)
+    one = gpu_f32(A, B, 1.0, 0.0, expect="f32_splitk")      # C prefilled with NaN
+    assert np.all(np.isfinite(one))
+    assert np.array_equal(one, gpu_f32(A, B, 1.0, 0.0))
+
+
+def test_workload_hgemm_splitk():
+    """The 128 x 128 x 16384 product of one output tile, every output checked."""
+    A, B = inputs.workload_operands("hgemm_nt_128x128x16384")
+    got = gpu_f16(A, B, expect="f16_splitk")
+    res = f16_check(got, oracle.gemm_f16_nt_exact(A, B),
+                    oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+    say("[hgemm_nt_128x128x16384] checked %d outputs, max %.2f ulp" % (res["count"],
+                                                                       res["max_ulps"]))
 
 
 # ------------------------------------------------------ 64-bit offsets -------

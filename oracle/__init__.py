@@ -17,6 +17,12 @@ numpy arrays.  Definitions followed (see the header of ``oracle.c``):
 * ``f16_epilogue`` / ``gemm_f16_nt_ex``: the fused write-back of page 1
   section 6.5.4, ``C = act(A*B^T + bias) + residual`` (act none, ReLU or
   SiLU), in double before the one rounding.
+* ``bf16_*`` and the ``fmt="bf16"`` arguments: the same products on bfloat16
+  operands (page 1 section 6.3.3 names bf16 beside fp16 as a matrix-unit
+  input type), rounded once to bfloat16.  numpy has no bfloat16 dtype, so
+  bfloat16 arrays are uint16 bit patterns here.
+* ``gemm_ex_exact``: the products for the other operand layouts (A stored
+  K x M, B stored K x N), by transposing the stored operands first.
 """
 from __future__ import annotations
 
@@ -61,14 +67,21 @@ def _configure(lib):
     lib.oracle_half_decode_array.argtypes = [_l, _p, _p]
     lib.oracle_gemm_f32.argtypes = [_i, _i, _i, _d, _p, _l, _p, _l, _d, _p, _l, _p, _l]
     lib.oracle_gemm_f32_points.argtypes = [_i, _d, _p, _l, _p, _l, _d, _p, _l, _l, _p, _p, _p]
-    lib.oracle_gemm_f16_nt.argtypes = [_i, _i, _i, _p, _l, _p, _l, _p, _l]
-    lib.oracle_gemm_f16_nt_points.argtypes = [_i, _p, _l, _p, _l, _l, _p, _p, _p]
-    lib.oracle_f16_epilogue.argtypes = [_l, _p, _p, _p, _p, _i, _p, _l, _p]
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = _d
+    lib.oracle_bf16_from_double.argtypes = [_d]
+    lib.oracle_bf16_from_double.restype = ctypes.c_uint16
+    lib.oracle_bf16_round_array.argtypes = [_l, _p, _p]
+    lib.oracle_bf16_decode_array.argtypes = [_l, _p, _p]
+    lib.oracle_gemm_16_nt.argtypes = [_i, _i, _i, _i, _p, _l, _p, _l, _p, _l]
+    lib.oracle_gemm_16_nt_points.argtypes = [_i, _i, _p, _l, _p, _l, _l, _p, _p, _p]
+    lib.oracle_epilogue16.argtypes = [_i, _l, _p, _p, _p, _p, _i, _p, _l, _p]
     lib.oracle_max_threads.restype = _i
     lib.oracle_set_threads.argtypes = [_i]
-    for fn in (lib.oracle_half_round_array, lib.oracle_half_decode_array, lib.oracle_gemm_f32,
-               lib.oracle_gemm_f32_points, lib.oracle_gemm_f16_nt,
-               lib.oracle_gemm_f16_nt_points, lib.oracle_set_threads):
+    for fn in (lib.oracle_half_round_array, lib.oracle_half_decode_array,
+               lib.oracle_bf16_round_array, lib.oracle_bf16_decode_array, lib.oracle_gemm_f32,
+               lib.oracle_gemm_f32_points, lib.oracle_gemm_16_nt, lib.oracle_gemm_16_nt_points,
+               lib.oracle_epilogue16, lib.oracle_set_threads):
         fn.restype = None
     return lib
 
@@ -122,6 +135,35 @@ def half_to_double(h) -> np.ndarray:
     return out
 
 
+def bf16_from_double(x) -> np.ndarray:
+    """Round float64 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_bf16_round_array(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def bf16_to_double(b) -> np.ndarray:
+    """Decode bfloat16 bit patterns (uint16) to float64."""
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint16))
+    out = np.empty(b.shape, dtype=np.float64)
+    _load().oracle_bf16_decode_array(b.size, _ptr(b), _ptr(out))
+    return out
+
+
+# 16-bit storage formats: numpy dtype of the arrays, code in oracle.c, rounding.
+_FMT = {"f16": (np.float16, 0), "bf16": (np.uint16, 1)}
+
+
+def round16(x, fmt: str) -> np.ndarray:
+    """Round float64 values to the format (float16 array, or uint16 bfloat16 bits)."""
+    return half_from_double(x) if fmt == "f16" else bf16_from_double(x)
+
+
+def decode16(a, fmt: str) -> np.ndarray:
+    return half_to_double(a) if fmt == "f16" else bf16_to_double(a)
+
+
 def gemm_f32(A: np.ndarray, B: np.ndarray, alpha: float = 1.0, beta: float = 0.0,
              C: np.ndarray | None = None) -> np.ndarray:
     """fp64 value of ``alpha*A@B + beta*C`` for float32 A[M,K], B[K,N], C[M,N]."""
@@ -166,17 +208,38 @@ def gemm_f32_points(A, B, rows, cols, alpha: float = 1.0, beta: float = 0.0, C=N
     return out
 
 
-def gemm_f16_nt_exact(A: np.ndarray, B: np.ndarray) -> np.ndarray:
-    """fp64 sum ``A @ B.T`` for binary16 A[M,K], B[N,K], before output rounding."""
-    A, lda = _rows(A, np.float16)
-    B, ldb = _rows(B, np.float16)
+def gemm_16_nt_exact(A: np.ndarray, B: np.ndarray, fmt: str = "f16") -> np.ndarray:
+    """fp64 sum ``A @ B.T`` for 16-bit A[M,K], B[N,K] (binary16 as float16 arrays,
+    bfloat16 as uint16 bit patterns), before output rounding."""
+    dtype, code = _FMT[fmt]
+    A, lda = _rows(A, dtype)
+    B, ldb = _rows(B, dtype)
     M, K = A.shape
     N, K2 = B.shape
     if K2 != K:
         raise ValueError("inner dimensions differ")
     out = np.empty((M, N), dtype=np.float64)
-    _load().oracle_gemm_f16_nt(M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(out), max(N, 1))
+    _load().oracle_gemm_16_nt(code, M, N, K, _ptr(A), lda, _ptr(B), ldb, _ptr(out), max(N, 1))
     return out
+
+
+def gemm_16_nt_points(A, B, rows, cols, fmt: str = "f16") -> np.ndarray:
+    """fp64 sums of :func:`gemm_16_nt_exact` at the outputs (rows[t], cols[t])."""
+    dtype, code = _FMT[fmt]
+    A, lda = _rows(A, dtype)
+    B, ldb = _rows(B, dtype)
+    K = A.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    out = np.empty(rows.shape, dtype=np.float64)
+    _load().oracle_gemm_16_nt_points(code, K, _ptr(A), lda, _ptr(B), ldb, rows.size,
+                                     _ptr(rows), _ptr(cols), _ptr(out))
+    return out
+
+
+def gemm_f16_nt_exact(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """fp64 sum ``A @ B.T`` for binary16 A[M,K], B[N,K], before output rounding."""
+    return gemm_16_nt_exact(A, B, "f16")
 
 
 def gemm_f16_nt(A: np.ndarray, B: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
@@ -187,49 +250,75 @@ def gemm_f16_nt(A: np.ndarray, B: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 
 def gemm_f16_nt_points(A, B, rows, cols) -> np.ndarray:
     """fp64 sums of :func:`gemm_f16_nt_exact` at the outputs (rows[t], cols[t])."""
-    A, lda = _rows(A, np.float16)
-    B, ldb = _rows(B, np.float16)
-    K = A.shape[1]
-    rows = np.ascontiguousarray(rows, dtype=np.int32)
-    cols = np.ascontiguousarray(cols, dtype=np.int32)
-    out = np.empty(rows.shape, dtype=np.float64)
-    _load().oracle_gemm_f16_nt_points(K, _ptr(A), lda, _ptr(B), ldb, rows.size,
-                                      _ptr(rows), _ptr(cols), _ptr(out))
-    return out
+    return gemm_16_nt_points(A, B, rows, cols, "f16")
+
+
+def gemm_bf16_nt(A: np.ndarray, B: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Returns (fp64 sum, that sum rounded to bfloat16 bits) for ``C = A @ B.T``
+    on bfloat16 bit patterns A[M,K], B[N,K] (uint16)."""
+    ref = gemm_16_nt_exact(A, B, "bf16")
+    return ref, bf16_from_double(ref)
 
 
 ACTS = {"none": 0, "relu": 1, "silu": 2}
 
 
-def f16_epilogue(acc, rows, cols, bias=None, act="none", residual=None) -> np.ndarray:
+def epilogue16(acc, rows, cols, bias=None, act="none", residual=None, fmt: str = "f16"):
     """fp64 ``act(acc + bias[col]) + residual[row, col]`` at the outputs
-    (rows[t], cols[t]), ``acc[t]`` being the product's sum there."""
+    (rows[t], cols[t]), ``acc[t]`` being the product's sum there; bias and
+    residual in the 16-bit format ``fmt``."""
+    dtype, code = _FMT[fmt]
     acc = np.ascontiguousarray(acc, dtype=np.float64).ravel()
     rows = np.ascontiguousarray(rows, dtype=np.int32).ravel()
     cols = np.ascontiguousarray(cols, dtype=np.int32).ravel()
     if not (acc.size == rows.size == cols.size):
         raise ValueError("acc, rows and cols differ in length")
     if bias is not None:
-        bias = np.ascontiguousarray(bias, dtype=np.float16).ravel()
+        bias = np.ascontiguousarray(bias, dtype=dtype).ravel()
     ldres = 0
     if residual is not None:
-        residual, ldres = _rows(residual, np.float16)
+        residual, ldres = _rows(residual, dtype)
     out = np.empty(acc.shape, dtype=np.float64)
-    _load().oracle_f16_epilogue(acc.size, _ptr(acc), _ptr(rows), _ptr(cols),
-                                None if bias is None else _ptr(bias), ACTS[act],
-                                None if residual is None else _ptr(residual), ldres, _ptr(out))
+    _load().oracle_epilogue16(code, acc.size, _ptr(acc), _ptr(rows), _ptr(cols),
+                              None if bias is None else _ptr(bias), ACTS[act],
+                              None if residual is None else _ptr(residual), ldres, _ptr(out))
     return out
 
 
-def gemm_f16_nt_ex_exact(A, B, bias=None, act="none", residual=None) -> np.ndarray:
+def f16_epilogue(acc, rows, cols, bias=None, act="none", residual=None) -> np.ndarray:
+    """:func:`epilogue16` on binary16 bias and residual."""
+    return epilogue16(acc, rows, cols, bias, act, residual, "f16")
+
+
+def gemm_16_nt_ex_exact(A, B, bias=None, act="none", residual=None, fmt: str = "f16"):
     """fp64 ``act(A @ B.T + bias) + residual`` (before the output rounding)."""
-    acc = gemm_f16_nt_exact(A, B)
+    acc = gemm_16_nt_exact(A, B, fmt)
     M, N = acc.shape
     rr, cc = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
-    return f16_epilogue(acc, rr, cc, bias, act, residual).reshape(M, N)
+    return epilogue16(acc, rr, cc, bias, act, residual, fmt).reshape(M, N)
+
+
+def gemm_f16_nt_ex_exact(A, B, bias=None, act="none", residual=None) -> np.ndarray:
+    return gemm_16_nt_ex_exact(A, B, bias, act, residual, "f16")
 
 
 def gemm_f16_nt_ex(A, B, bias=None, act="none", residual=None):
     """(fp64 value, that value rounded to binary16) of the fused product."""
     ref = gemm_f16_nt_ex_exact(A, B, bias, act, residual)
     return ref, half_from_double(ref)
+
+
+def nt_operands(A_stored, B_stored, op_a: str, op_b: str):
+    """The A[M,K] and B[N,K] of ``C = op(A) @ op(B)``: op "n" keeps A as M x K
+    and B as K x N, op "t" reads A stored K x M and B stored N x K."""
+    A = A_stored if op_a == "n" else np.ascontiguousarray(A_stored.T)
+    B = B_stored if op_b == "t" else np.ascontiguousarray(B_stored.T)
+    return A, B
+
+
+def gemm_ex_exact(A_stored, B_stored, op_a: str = "n", op_b: str = "t", bias=None, act="none",
+                  residual=None, fmt: str = "f16") -> np.ndarray:
+    """fp64 ``act(op(A) @ op(B) + bias) + residual`` for 16-bit operands in any
+    of the four layouts, before the output rounding."""
+    A, B = nt_operands(A_stored, B_stored, op_a, op_b)
+    return gemm_16_nt_ex_exact(A, B, bias, act, residual, fmt)

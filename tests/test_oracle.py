@@ -52,6 +52,43 @@ def exact_half_round(x: Fraction) -> float:
     return sign * float(v)
 
 
+def exact_bf16_round(x: Fraction) -> float:
+    """Nearest bfloat16 to the rational x, ties to even, as a Python float
+    (8 significant bits, normal exponents -126 .. 127, overflow at 2^128)."""
+    if x == 0:
+        return 0.0
+    sign = -1.0 if x < 0 else 1.0
+    a = abs(x)
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** E > a:
+        E -= 1
+    while Fraction(2) ** (E + 1) <= a:
+        E += 1
+    q = max(E, -126) - 7
+    s = a / Fraction(2) ** q
+    r = s.numerator // s.denominator
+    frac = s - r
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    v = Fraction(r) * Fraction(2) ** q
+    if v >= Fraction(2) ** 128:
+        return sign * float("inf")
+    return sign * float(v)
+
+
+def torch_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """torch's float32 -> bfloat16 conversion (nearest, ties to even), as bits."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def torch_bf16_decode(bits: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
 def exact_nt(A16: np.ndarray, B16: np.ndarray) -> list[list[Fraction]]:
     Af = [[Fraction(float(v)) for v in row] for row in A16.astype(np.float64)]
     Bf = [[Fraction(float(v)) for v in row] for row in B16.astype(np.float64)]
@@ -365,6 +402,157 @@ def pin_epilogue_rational_brute_force():
                 assert float(c16[i, j]) == exact_half_round(e), (m, n, k, i, j)
 
 
+# ---- bfloat16 (page 1, section 6.3.3) -----------------------------------------
+def bf16_values(rng, shape, sd=0.5):
+    """Random bfloat16 bit patterns from normal(0, sd), rounded by torch."""
+    return torch_bf16_bits(rng.normal(0, sd, shape).astype(np.float32))
+
+
+def pin_bf16_decode_all_patterns():
+    """Every bfloat16 bit pattern decodes to torch's bfloat16 -> float64 value,
+    and the format's landmarks come out as the definition says."""
+    got = oracle.bf16_to_double(ALL_HALF_BITS)
+    want = torch_bf16_decode(ALL_HALF_BITS)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2 * 127
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    marks = {0x3F80: 1.0, 0x4000: 2.0, 0xBF80: -1.0, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127,
+             0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x007F: 127 * 2.0 ** -133,
+             0x7F80: np.inf, 0xFF80: -np.inf, 0x3FC0: 1.5}
+    for bits, v in marks.items():
+        assert oracle.bf16_to_double(np.array([bits], np.uint16))[0] == v, hex(bits)
+
+
+def pin_bf16_round_trip_and_midpoints():
+    """Finite bfloat16 values round-trip; midpoints go to the even neighbour;
+    just off a midpoint the nearest neighbour wins; overflow goes to inf."""
+    vals = oracle.bf16_to_double(ALL_HALF_BITS)
+    fin = np.isfinite(vals)
+    assert np.array_equal(oracle.bf16_from_double(vals[fin]), ALL_HALF_BITS[fin])
+    pos = np.unique(vals[fin & (vals >= 0)])
+    mids = (pos[:-1] + pos[1:]) / 2.0                     # exact in double
+    got = oracle.bf16_to_double(oracle.bf16_from_double(mids))
+    lo_even = (oracle.bf16_from_double(pos[:-1]) & 1) == 0
+    assert np.array_equal(got, np.where(lo_even, pos[:-1], pos[1:]))
+    up, dn = np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf)
+    assert np.array_equal(oracle.bf16_to_double(oracle.bf16_from_double(up)), pos[1:])
+    assert np.array_equal(oracle.bf16_to_double(oracle.bf16_from_double(dn)), pos[:-1])
+    top = (2 - 2.0 ** -7) * 2.0 ** 127
+    edge = np.array([top, (2 - 2.0 ** -8) * 2.0 ** 127, np.nextafter((2 - 2.0 ** -8) * 2.0 ** 127, 0),
+                     2.0 ** 128, 1e300, -1e300])
+    assert list(oracle.bf16_from_double(edge)) == [0x7F7F, 0x7F80, 0x7F7F, 0x7F80, 0x7F80, 0xFF80]
+
+
+def pin_bf16_round_random_vs_torch():
+    """On float32 inputs the oracle's rounding equals torch's float32 -> bfloat16."""
+    rng = np.random.default_rng(17)
+    x = np.concatenate([
+        rng.normal(0, 1, 200000), rng.uniform(-3e38, 3e38, 50000),
+        np.ldexp(rng.uniform(1, 2, 100000), rng.integers(-140, 128, 100000)),
+        rng.normal(0, 1e-39, 50000),                        # bfloat16 subnormal range
+    ]).astype(np.float32)
+    x = x[np.isfinite(x)]
+    assert np.array_equal(oracle.bf16_from_double(x.astype(np.float64)), torch_bf16_bits(x))
+
+
+def pin_bf16_gemm_integers_outer_products_brute_force():
+    rng = np.random.default_rng(19)
+    # small integers: the fp64 sums are exact; past 256 bfloat16 rounds them
+    A = torch_bf16_bits(inputs.small_ints((21, 200), 1, -3, 3, np.float32))
+    B = torch_bf16_bits(inputs.small_ints((17, 200), 2, -3, 3, np.float32))
+    ia, ib = oracle.bf16_to_double(A), oracle.bf16_to_double(B)
+    want = ia @ ib.T
+    ref, c = oracle.gemm_bf16_nt(A, B)
+    assert np.array_equal(ref, want)
+    assert [float(v) for v in oracle.bf16_to_double(c).ravel()] == \
+        [exact_bf16_round(Fraction(int(v))) for v in want.ravel()]
+    # K = 1: a*b is exact in double and rounds once
+    a, b = bf16_values(rng, (40, 1), 30.0), bf16_values(rng, (30, 1), 1e-3)
+    ref, c = oracle.gemm_bf16_nt(a, b)
+    prod = oracle.bf16_to_double(a) @ oracle.bf16_to_double(b).T
+    assert np.array_equal(ref, prod)
+    assert [float(v) for v in oracle.bf16_to_double(c).ravel()] == \
+        [exact_bf16_round(Fraction(float(v))) for v in prod.ravel()]
+    # exact rational sums on tiny shapes
+    for (m, n, k) in [(1, 1, 1), (2, 3, 5), (3, 2, 9), (4, 4, 17)]:
+        A, B = bf16_values(rng, (m, k)), bf16_values(rng, (n, k))
+        ref, c = oracle.gemm_bf16_nt(A, B)
+        Af = [[Fraction(float(v)) for v in row] for row in oracle.bf16_to_double(A)]
+        Bf = [[Fraction(float(v)) for v in row] for row in oracle.bf16_to_double(B)]
+        for i in range(m):
+            for j in range(n):
+                e = sum((x * y for x, y in zip(Af[i], Bf[j])), Fraction(0))
+                assert abs(Fraction(ref[i, j]) - e) <= Fraction(k * EPS64) * sum(
+                    abs(x * y) for x, y in zip(Af[i], Bf[j]))
+                assert float(oracle.bf16_to_double(c[i:i + 1, j])[0]) == exact_bf16_round(e)
+    # the strided and point forms agree with the full product
+    Abig, Bbig = bf16_values(rng, (12, 40)), bf16_values(rng, (9, 33))
+    A, B = Abig[:, :31], Bbig[:, :31]
+    full = oracle.gemm_16_nt_exact(A, B, "bf16")
+    assert np.array_equal(full, oracle.gemm_16_nt_exact(np.ascontiguousarray(A),
+                                                        np.ascontiguousarray(B), "bf16"))
+    rows, cols = rng.integers(0, 12, 50), rng.integers(0, 9, 50)
+    assert np.array_equal(oracle.gemm_16_nt_points(A, B, rows, cols, "bf16"), full[rows, cols])
+
+
+def pin_bf16_epilogue_brute_force():
+    """bfloat16 bias and residual are decoded as bfloat16: ReLU with both is
+    exact rational arithmetic rounded once."""
+    rng = np.random.default_rng(23)
+    m, n, k = 3, 4, 7
+    A, B = bf16_values(rng, (m, k)), bf16_values(rng, (n, k))
+    bias, res = bf16_values(rng, (n,), 0.4), bf16_values(rng, (m, n), 2.0)
+    out = oracle.gemm_16_nt_ex_exact(A, B, bias, "relu", res, "bf16")
+    Af = oracle.bf16_to_double(A)
+    Bf = oracle.bf16_to_double(B)
+    for i in range(m):
+        for j in range(n):
+            e = sum((Fraction(float(x)) * Fraction(float(y)) for x, y in zip(Af[i], Bf[j])),
+                    Fraction(0))
+            e = max(e + Fraction(float(oracle.bf16_to_double(bias[j:j + 1])[0])), Fraction(0))
+            e += Fraction(float(oracle.bf16_to_double(res[i, j:j + 1])[0]))
+            assert exact_bf16_round(Fraction(out[i, j])) == exact_bf16_round(e)
+            assert abs(Fraction(out[i, j]) - e) <= Fraction(2 * k * EPS64) * (abs(e) + 8)
+
+
+# ---- operand layouts (page 1, section 6.3.3: row-major NN through GemmEx) -------
+def layout_exact(A_stored, B_stored, op_a, op_b, fmt):
+    """op(A) @ op(B) written out element by element from the stored arrays."""
+    dec = oracle.half_to_double if fmt == "f16" else oracle.bf16_to_double
+    Ad, Bd = dec(A_stored), dec(B_stored)
+    M = Ad.shape[0] if op_a == "n" else Ad.shape[1]
+    K = Ad.shape[1] if op_a == "n" else Ad.shape[0]
+    N = Bd.shape[1] if op_b == "n" else Bd.shape[0]
+    a = (lambda i, k: Ad[i, k]) if op_a == "n" else (lambda i, k: Ad[k, i])
+    b = (lambda k, j: Bd[k, j]) if op_b == "n" else (lambda k, j: Bd[j, k])
+    return [[sum((Fraction(float(a(i, kk))) * Fraction(float(b(kk, j))) for kk in range(K)),
+                 Fraction(0)) for j in range(N)] for i in range(M)]
+
+
+def pin_layouts_all_four():
+    """C = op(A) op(B) for N and T operands in both formats: A stored M x K (N)
+    or K x M (T), B stored K x N (N) or N x K (T)."""
+    rng = np.random.default_rng(29)
+    M, N, K = 5, 3, 7
+    for fmt in ("f16", "bf16"):
+        for op_a in ("n", "t"):
+            for op_b in ("n", "t"):
+                sa = (M, K) if op_a == "n" else (K, M)
+                sb = (K, N) if op_b == "n" else (N, K)
+                if fmt == "f16":
+                    A = rng.normal(0, 0.5, sa).astype(np.float16)
+                    B = rng.normal(0, 0.5, sb).astype(np.float16)
+                else:
+                    A, B = bf16_values(rng, sa), bf16_values(rng, sb)
+                got = oracle.gemm_ex_exact(A, B, op_a, op_b, fmt=fmt)
+                ex = layout_exact(A, B, op_a, op_b, fmt)
+                assert got.shape == (M, N)
+                for i in range(M):
+                    for j in range(N):
+                        assert abs(Fraction(got[i, j]) - ex[i][j]) <= Fraction(K * EPS64) * 8
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -402,8 +590,8 @@ def test_flop_count_golden():
 # planted mistakes: each mutant of oracle.c must fail at least one pin
 # --------------------------------------------------------------------------
 MUTANTS = {
-    "nt_transposed_B": ("Bd[j * K + k] = oracle_half_to_double(B[j * ldb + k]);",
-                        "Bd[j * K + k] = oracle_half_to_double(B[k * ldb + j]);"),
+    "nt_transposed_B": ("Bd[j * K + k] = dec(B[j * ldb + k]);",
+                        "Bd[j * K + k] = dec(B[k * ldb + j]);"),
     "nt_dropped_last_term": ("for (int k = 0; k < K; ++k) acc += arow[k] * brow[k];",
                              "for (int k = 0; k + 1 < K; ++k) acc += arow[k] * brow[k];"),
     "nn_wrong_index": ("acc[j] += a * (double)brow[j];", "acc[j] += a * (double)brow[j == 0 ? 0 : j - 1];"),
@@ -417,13 +605,19 @@ MUTANTS = {
     "half_decode_bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     "points_transposed": ("acc += (double)A[i * lda + k] * (double)B[(long)k * ldb + j];",
                           "acc += (double)A[i * lda + k] * (double)B[(long)j * ldb + k];"),
-    "epi_bias_by_row": ("if (bias) v += oracle_half_to_double(bias[j]);",
-                        "if (bias) v += oracle_half_to_double(bias[i]);"),
+    "epi_bias_by_row": ("if (bias) v += dec(bias[j]);", "if (bias) v += dec(bias[i]);"),
     "epi_silu_sign": ("v = v / (1.0 + exp(-v));", "v = v / (1.0 + exp(v));"),
     "epi_relu_leaky": ("v = v > 0.0 ? v : 0.0;", "v = v > 0.0 ? v : 0.01 * v;"),
     "epi_residual_inside_act": ("    if (act == 1) {\n",
-                                "    if (res) v += oracle_half_to_double(res[i * ldres + j]);\n"
+                                "    if (res) v += dec(res[i * ldres + j]);\n"
                                 "    if (act == 1) {\n"),
+    "bf16_decode_bias": ("v = ldexp((double)(128 + f), e - 134);",
+                         "v = ldexp((double)(128 + f), e - 133);"),
+    "bf16_ties_away": ("(frac == 0.5 && odd)", "(frac == 0.5)"),
+    "bf16_no_subnormals": ("if (E < -126) E = -126;", "if (E < -127) E = -127;"),
+    "bf16_fraction_bits": ("const int q = E - 7;", "const int q = E - 8;"),
+    "bf16_decoded_as_half": ("return fmt == 1 ? oracle_bf16_to_double : oracle_half_to_double;",
+                             "return oracle_half_to_double;"),
 }
 
 
@@ -441,6 +635,23 @@ for pin in T.PINS:
         sys.exit(3)
 sys.exit(0)
 """
+
+
+def test_planted_layout_mistakes_are_caught(oracle_mod, monkeypatch):
+    """Wrong operand handling in the layout layer (a transpose dropped, or
+    applied to the wrong layout) fails the layout pin."""
+    right = oracle.nt_operands
+    wrong = {
+        "b_n_not_transposed": lambda A, B, oa, ob: (right(A, B, oa, "t")[0], B),
+        "a_t_not_transposed": lambda A, B, oa, ob: (A, right(A, B, "n", ob)[1]),
+        "ops_swapped": lambda A, B, oa, ob: right(A, B, ob if ob == oa else oa, oa),
+    }
+    for name, fn in wrong.items():
+        monkeypatch.setattr(oracle, "nt_operands", fn)
+        with pytest.raises(Exception):
+            pin_layouts_all_four()
+    monkeypatch.setattr(oracle, "nt_operands", right)
+    pin_layouts_all_four()
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))

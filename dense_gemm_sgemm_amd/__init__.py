@@ -77,6 +77,10 @@ def load_library() -> ctypes.CDLL:
         lib.gemm_f32_splitk_workspace.restype = u64
         lib.gemm_f16_nt_splitk_workspace.argtypes = [i, i, i, i]
         lib.gemm_f16_nt_splitk_workspace.restype = u64
+        lib.gemm_ex.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, p, i, p, i, p]
+        lib.gemm_ex.restype = i
+        lib.gemm_ex_path.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, p, i, p, i]
+        lib.gemm_ex_path.restype = i
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_path_name.argtypes = [i]
@@ -225,20 +229,22 @@ def f16_nt_path(A, B, C) -> str:
     return _path_name(code)
 
 
-def _epilogue_args(bias, act, residual, M: int, N: int):
+def _epilogue_args(bias, act, residual, M: int, N: int, dtype=None):
     import torch
+    dtype = dtype or torch.float16
     if act not in ACTS:
         raise ValueError("act must be one of %s" % sorted(ACTS))
     pbias = None
     if bias is not None:
-        if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float16 or \
+        if not isinstance(bias, torch.Tensor) or bias.dtype != dtype or \
                 bias.device.type != "cuda" or bias.numel() != N or \
                 (bias.dim() == 1 and N > 1 and bias.stride(0) != 1):
-            raise ValueError("bias must be a contiguous float16 GPU vector of length N = %d" % N)
+            raise ValueError("bias must be a contiguous %s GPU vector of length N = %d"
+                             % (dtype, N))
         pbias = bias.data_ptr()
     pres, ldr = None, 0
     if residual is not None:
-        Mr, Nr, ldr, pres = _matrix(residual, "residual", torch.float16)
+        Mr, Nr, ldr, pres = _matrix(residual, "residual", dtype)
         if (Mr, Nr) != (M, N):
             raise ValueError("residual must be %d x %d, got %s" % (M, N, tuple(residual.shape)))
     return pbias, ACTS[act], pres, ldr
@@ -272,3 +278,43 @@ def f16_nt_ex_path(A, B, C, bias=None, act: str = "none", residual=None) -> str:
     code = load_library().gemm_f16_nt_ex_path(M, N, K, pa, lda, pb, ldb, pbias, code, pres, ldr,
                                               pc, ldc)
     return _path_name(code)
+
+
+OPS = {"n": 0, "t": 1}
+
+
+def _ex_args(A, B, C, op_a, op_b, bias, act, residual):
+    import torch
+    if op_a not in OPS or op_b not in OPS:
+        raise ValueError("op_a and op_b must be 'n' or 't'")
+    dtype = A.dtype if isinstance(A, torch.Tensor) else None
+    if dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("A must be a float16 or bfloat16 tensor")
+    ra, ca, lda, pa = _matrix(A, "A", dtype)
+    rb, cb, ldb, pb = _matrix(B, "B", dtype)
+    M, N, ldc, pc = _matrix(C, "C", dtype)
+    M2, K = (ra, ca) if op_a == "n" else (ca, ra)
+    K2, N2 = (rb, cb) if op_b == "n" else (cb, rb)
+    if M2 != M or N2 != N or K2 != K:
+        raise ValueError("shape mismatch: op_a %s A %s, op_b %s B %s, C %s"
+                         % (op_a, tuple(A.shape), op_b, tuple(B.shape), tuple(C.shape)))
+    pbias, code, pres, ldr = _epilogue_args(bias, act, residual, M, N, dtype)
+    typ = 1 if dtype == torch.bfloat16 else 0
+    return (typ, OPS[op_a], OPS[op_b], M, N, K, pa, lda, pb, ldb, pbias, code, pres, ldr, pc, ldc)
+
+
+def gemm_ex(A, B, C, op_a: str = "n", op_b: str = "t", bias=None, act: str = "none",
+            residual=None, stream=None):
+    """``C = act(op(A) @ op(B) + bias) + residual`` for float16 or bfloat16
+    tensors (all of one dtype).  op "n": A is [M,K], B is [K,N]; op "t": A is
+    [K,M], B is [N,K].  fp32 accumulation, one rounding to the dtype.  Returns C."""
+    args = _ex_args(A, B, C, op_a, op_b, bias, act, residual)
+    _check(load_library().gemm_ex(*args, _stream(stream)))
+    return C
+
+
+def ex_path(A, B, C, op_a: str = "n", op_b: str = "t", bias=None, act: str = "none",
+            residual=None) -> str:
+    """Name of the A*B^T kernel ``gemm_ex`` would run for these tensors (host only)."""
+    return _path_name(load_library().gemm_ex_path(*_ex_args(A, B, C, op_a, op_b, bias, act,
+                                                            residual)))

@@ -101,6 +101,57 @@ int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, in
   return GEMM_PATH_F16_GENERAL;
 }
 
+// gemm_ex: the operands the A * B^T kernels read.  An operand that is not
+// K-contiguous (A for OP_T, B for OP_N) is read from a transposed copy with
+// rows padded to a multiple of 8 elements at a 256-byte aligned address.
+struct ExLayout {
+  bool copy_a, copy_b;
+  int64_t lda, ldb;   // leading dimensions the kernels see
+};
+
+int64_t padded_row(int K) { return ((int64_t)(K > 1 ? K : 1) + 7) / 8 * 8; }
+
+ExLayout ex_layout(int op_a, int op_b, int K, int lda, int ldb) {
+  ExLayout l;
+  l.copy_a = op_a == GEMM_OP_T && K > 0;
+  l.copy_b = op_b == GEMM_OP_N && K > 0;
+  l.lda = l.copy_a ? padded_row(K) : lda;
+  l.ldb = l.copy_b ? padded_row(K) : ldb;
+  return l;
+}
+
+// Stands for the address of a transposed copy in the path choice.
+const void* const kCopyAddress = reinterpret_cast<const void*>(uintptr_t(256));
+
+int ex_select(int type, int op_a, int op_b, int M, int N, int K, const void* A, int lda,
+              const void* B, int ldb, const void* bias, int act, const void* res, int ldr,
+              const void* C, int ldc) {
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
+  if ((type != GEMM_TYPE_F16 && type != GEMM_TYPE_BF16) ||
+      (op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T) ||
+      (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_SILU))
+    return GEMM_ERR_BAD_ARG;
+  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
+  const int need_a = op_a == GEMM_OP_N ? K : M, need_b = op_b == GEMM_OP_N ? N : K;
+  if (lda < (need_a > 1 ? need_a : 1) || ldb < (need_b > 1 ? need_b : 1) ||
+      ldc < (N > 1 ? N : 1))
+    return GEMM_ERR_BAD_LD;
+  if (res != nullptr && ldr < (N > 1 ? N : 1)) return GEMM_ERR_BAD_LD;
+  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
+  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
+  const bool epi = bias != nullptr || res != nullptr || act != GEMM_ACT_NONE;
+  if (K == 0) return epi ? GEMM_PATH_F16_GENERAL : GEMM_PATH_F16_ZERO;
+  if (force_general()) return GEMM_PATH_F16_GENERAL;
+  if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
+  if (splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
+  const ExLayout l = ex_layout(op_a, op_b, K, lda, ldb);
+  if (f16_mfma_fits(M, N, K, l.copy_a ? kCopyAddress : A, l.lda, l.copy_b ? kCopyAddress : B,
+                    l.ldb, C, ldc) &&
+      (!epi || f16_epi_fits(bias, res, ldr)))
+    return GEMM_PATH_F16_MFMA;
+  return GEMM_PATH_F16_GENERAL;
+}
+
 int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
 
 // The tiled kernel of a product that takes neither split-K nor the
@@ -111,7 +162,7 @@ hipError_t f32_tiled(const F32Args& a, int cus, hipStream_t s) {
   return launch_f32_edge(a, cus, s);
 }
 
-hipError_t f16_tiled(const F16Args& a, bool epi, int cus, hipStream_t s) {
+hipError_t f16_tiled(const Args16& a, bool epi, int cus, hipStream_t s) {
   if (!force_general() && f16_mfma_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc) &&
       (!epi || f16_epi_fits(a.bias, a.res, a.ldr)))
     return launch_f16_mfma(a, epi, cus, s);
@@ -190,7 +241,7 @@ hipError_t f32_auto_split(F32Args a, int cus, hipStream_t s) {
   return e != hipSuccess ? e : f;
 }
 
-hipError_t f16_auto_split(F16Args a, bool epi, int cus, hipStream_t s) {
+hipError_t f16_auto_split(Args16 a, bool epi, int cus, hipStream_t s) {
   const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF16Slab, kF16MinRange, 0);
   std::unique_lock<std::mutex> lock(g_ws_mutex);
   bool owned = false;
@@ -234,7 +285,7 @@ MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
   const int cus = check_device();
   if (cus < 0) return cus;
-  const F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+  const Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
                   static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (path) {
@@ -253,7 +304,7 @@ MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K, const void* A, int lda, co
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
   const int cus = check_device();
   if (cus < 0) return cus;
-  F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+  Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
             static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
   a.bias = static_cast<const half_t*>(bias);
   a.res = static_cast<const half_t*>(residual);
@@ -264,6 +315,69 @@ MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K, const void* A, int lda, co
   if (path == GEMM_PATH_F16_GEMV) return to_status(launch_f16_gemv(a, true, s));
   if (path == GEMM_PATH_F16_SPLITK) return to_status(f16_auto_split(a, true, cus, s));
   return to_status(launch_f16_edge(a, true, s));
+}
+
+MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K, const void* A,
+                          int lda, const void* B, int ldb, const void* bias, int act,
+                          const void* residual, int ldr, void* C, int ldc, void* stream) {
+  const int path = ex_select(type, op_a, op_b, M, N, K, A, lda, B, ldb, bias, act, residual, ldr,
+                             C, ldc);
+  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const int cus = check_device();
+  if (cus < 0) return cus;
+  const bool epi = bias != nullptr || residual != nullptr || act != GEMM_ACT_NONE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const ExLayout l = ex_layout(op_a, op_b, K, lda, ldb);
+  Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+           static_cast<half_t*>(C), l.lda, l.ldb, ldc, M, N, K};
+  a.bias = static_cast<const half_t*>(bias);
+  a.res = static_cast<const half_t*>(residual);
+  a.ldr = residual ? ldr : 0;
+  a.act = act;
+  a.fmt = type == GEMM_TYPE_BF16 ? kFmtBF16 : kFmtF16;
+  if (path == GEMM_PATH_F16_ZERO) return to_status(launch_f16_zero(a, s));
+
+  // Workspace: the transposed copies, then the split-K partial sums.
+  auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bytes_a = l.copy_a ? round256((size_t)M * l.lda * 2) : 0;
+  const size_t bytes_b = l.copy_b ? round256((size_t)N * l.ldb * 2) : 0;
+  const SplitPlan plan = path == GEMM_PATH_F16_SPLITK
+                             ? splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0)
+                             : SplitPlan{};
+  const size_t total = bytes_a + bytes_b + (plan.splits > 1 ? plan.bytes : 0);
+  std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
+  bool owned = false;
+  char* ws = nullptr;
+  if (total > 0) {
+    lock.lock();
+    ws = static_cast<char*>(stream_workspace(s, total, &owned));
+    if (owned) lock.unlock();
+    if (ws == nullptr) return GEMM_ERR_WORKSPACE;
+  }
+  hipError_t e = hipSuccess;
+  if (l.copy_a) {   // A is [K][lda]: its transpose is op(A), M x K
+    a.A = reinterpret_cast<const half_t*>(ws);
+    e = launch_transpose16(static_cast<const half_t*>(A), lda, K, M, reinterpret_cast<half_t*>(ws),
+                           l.lda, s);
+  }
+  if (e == hipSuccess && l.copy_b) {   // B is [K][ldb]: its transpose is B^T stored N x K
+    a.B = reinterpret_cast<const half_t*>(ws + bytes_a);
+    e = launch_transpose16(static_cast<const half_t*>(B), ldb, K, N,
+                           reinterpret_cast<half_t*>(ws + bytes_a), l.ldb, s);
+  }
+  if (e == hipSuccess) {
+    switch (path) {
+      case GEMM_PATH_F16_GEMV: e = launch_f16_gemv(a, epi, s); break;
+      case GEMM_PATH_F16_SPLITK:
+        a.sk = splitk_args(plan, M, N, ws + bytes_a + bytes_b);
+        e = launch_f16_splitk(a, epi, s);
+        break;
+      case GEMM_PATH_F16_MFMA: e = launch_f16_mfma(a, epi, cus, s); break;
+      default: e = launch_f16_edge(a, epi, s); break;
+    }
+  }
+  const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
+  return to_status(e != hipSuccess ? e : f);
 }
 
 MI355GEMM_API int gemm_f32_splitk(int M, int N, int K, float alpha, const float* A, int lda,
@@ -305,7 +419,7 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K, const void* A, int lda
     return GEMM_ERR_WORKSPACE;
   const int cus = check_device();
   if (cus < 0) return cus;
-  F16Args a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+  Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
             static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.splits > 1) {
@@ -348,6 +462,12 @@ MI355GEMM_API int gemm_f16_nt_ex_path(int M, int N, int K, const void* A, int ld
   return f16_ex_select(M, N, K, A, lda, B, ldb, bias, act, residual, ldr, C, ldc);
 }
 
+MI355GEMM_API int gemm_ex_path(int type, int op_a, int op_b, int M, int N, int K, const void* A,
+                               int lda, const void* B, int ldb, const void* bias, int act,
+                               const void* residual, int ldr, const void* C, int ldc) {
+  return ex_select(type, op_a, op_b, M, N, K, A, lda, B, ldb, bias, act, residual, ldr, C, ldc);
+}
+
 MI355GEMM_API const char* gemm_status_string(int status) {
   switch (status) {
     case GEMM_OK: return "success";
@@ -356,10 +476,11 @@ MI355GEMM_API const char* gemm_status_string(int status) {
     case GEMM_ERR_NULL_POINTER: return "a matrix pointer that would be accessed is NULL";
     case GEMM_ERR_UNSUPPORTED_DEVICE: return "no HIP device, or the current device is not gfx950";
     case GEMM_ERR_LAUNCH: return "the HIP runtime rejected the kernel launch";
-    case GEMM_ERR_BAD_ARG: return "an enumerated argument (the activation) has no defined meaning";
+    case GEMM_ERR_BAD_ARG:
+      return "an enumerated argument (type, operation or activation) has no defined meaning";
     case GEMM_ERR_WORKSPACE:
-      return "the split-K workspace is NULL, smaller than the size query reports, or not 16-byte "
-             "aligned";
+      return "a workspace the call needs is NULL, smaller than the size query reports, not "
+             "16-byte aligned, or could not be allocated";
     default: return "unknown status code";
   }
 }

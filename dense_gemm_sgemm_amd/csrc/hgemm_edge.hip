@@ -1,5 +1,5 @@
-// fp16 C = A * B^T for every shape, leading dimension and alignment, on the
-// matrix cores.
+// 16-bit (fp16 or bf16) C = A * B^T for every shape, leading dimension and
+// alignment, on the matrix cores.
 //
 // The boundary rule is the one of page 1 ("第 6 章 Shared Memory & Tile",
 // exercise 7 of section 6.9): loads outside the matrix read zero, stores
@@ -68,8 +68,8 @@ __device__ __forceinline__ h8 load_chunk(const half_t* base, int64_t ld, int row
 // MODE 0 writes C = half(acc), MODE 1 the fused write-back, MODE 2 the fp32
 // partial product of one split-K range (workgroup b: range b / tiles, tile
 // b % tiles) to the tile-padded workspace.
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, int64_t tile_base) {
+template <int MODE, int FMT>
+__global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(Args16 p, int64_t tile_base) {
   constexpr bool EPI = MODE == 1;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
 
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
       for (int i = 0; i < kBlocks; ++i)
 #pragma unroll
         for (int j = 0; j < kBlocks; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          acc[i][j] = hgemm::mfma16<FMT>(fb[j], fa[i], acc[i][j]);
     }
   };
 
@@ -183,14 +183,14 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
         for (int v = 0; v < 4; ++v) {
           const bool in = m < p.M && n + v < p.N;
           float x = acc[i][j][v];
-          if (p.bias && in) x += (float)p.bias[n + v];
+          if (p.bias && in) x += word_to_f32<FMT>(p.bias[n + v]);
           x = epi_act(x, p.act);
-          if (p.res && in) x += (float)p.res[(int64_t)m * p.ldr + n + v];
-          o[v] = (half_t)x;
+          if (p.res && in) x += word_to_f32<FMT>(p.res[(int64_t)m * p.ldr + n + v]);
+          o[v] = f32_to_word<FMT>(x);
         }
       } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+        for (int v = 0; v < 4; ++v) o[v] = f32_to_word<FMT>(acc[i][j][v]);
       }
       const int c = 2 * j + (g >> 1);
       *(h4*)(out + r * kOutRowBytes + 16 * (c ^ (r & 7)) + 8 * (g & 1)) = o;
@@ -218,19 +218,29 @@ __global__ __launch_bounds__(kThreads, 2) void hgemm_nt_edge_kernel(F16Args p, i
 
 }  // namespace hedge
 
-hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream) {
+namespace {
+const void* edge_kernel(int mode, int fmt) {
+  using hedge::hgemm_nt_edge_kernel;
+  if (fmt == kFmtBF16)
+    return mode == 0 ? (const void*)hgemm_nt_edge_kernel<0, kFmtBF16>
+         : mode == 1 ? (const void*)hgemm_nt_edge_kernel<1, kFmtBF16>
+                     : (const void*)hgemm_nt_edge_kernel<2, kFmtBF16>;
+  return mode == 0 ? (const void*)hgemm_nt_edge_kernel<0, kFmtF16>
+       : mode == 1 ? (const void*)hgemm_nt_edge_kernel<1, kFmtF16>
+                   : (const void*)hgemm_nt_edge_kernel<2, kFmtF16>;
+}
+}  // namespace
+
+hipError_t launch_f16_edge(const Args16& a, bool epi, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + hedge::BM - 1) / hedge::BM) *
                         ((a.N + hedge::BN - 1) / hedge::BN);
-  const void* k = epi ? (const void*)hedge::hgemm_nt_edge_kernel<1>
-                      : (const void*)hedge::hgemm_nt_edge_kernel<0>;
-  return launch_tiles(k, a, tiles, hedge::kThreads, 0, stream);
+  return launch_tiles(edge_kernel(epi ? 1 : 0, a.fmt), a, tiles, hedge::kThreads, 0, stream);
 }
 
-hipError_t launch_f16_partials(const F16Args& a, hipStream_t stream) {
+hipError_t launch_f16_partials(const Args16& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + hedge::BM - 1) / hedge::BM) *
                         ((a.N + hedge::BN - 1) / hedge::BN);
-  return launch_tiles((const void*)hedge::hgemm_nt_edge_kernel<2>, a, tiles * a.sk.splits,
-                      hedge::kThreads, 0, stream);
+  return launch_tiles(edge_kernel(2, a.fmt), a, tiles * a.sk.splits, hedge::kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

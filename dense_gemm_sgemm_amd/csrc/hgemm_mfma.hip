@@ -1,5 +1,5 @@
-// The fp16 A * B^T fast path: instances of the tile kernel template and the
-// choice between them.
+// The 16-bit A * B^T fast path (fp16 and bf16): instances of the tile kernel
+// template and the choice between them.
 #include "hgemm_tile.hpp"
 
 namespace mi355gemm {
@@ -49,17 +49,24 @@ bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
          hgemm::fits<128, 128, BK>(M, N, K, A, lda, B, ldb, C, ldc);
 }
 
-template <bool EPI>
-hipError_t launch_shape(const F16Args& a, int cus, hipStream_t stream) {
+template <bool EPI, int FMT>
+hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
   switch (choose(a.M, a.N, cus)) {
-    case k256x224: return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI>(a, cus, stream);
-    case k128x128: return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI>(a, 2 * cus, stream);
-    default: return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 0, true, EPI>(a, cus, stream);
+    case k256x224:
+      return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT>(a, cus, stream);
+    case k128x128:
+      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT>(a, 2 * cus, stream);
+    default:
+      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 0, true, EPI, FMT>(a, cus, stream);
   }
 }
 
-hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream) {
-  return epi ? launch_shape<true>(a, cus, stream) : launch_shape<false>(a, cus, stream);
+hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {
+  if (a.fmt == kFmtBF16)
+    return epi ? launch_shape<true, kFmtBF16>(a, cus, stream)
+               : launch_shape<false, kFmtBF16>(a, cus, stream);
+  return epi ? launch_shape<true, kFmtF16>(a, cus, stream)
+             : launch_shape<false, kFmtF16>(a, cus, stream);
 }
 
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr) {

@@ -53,6 +53,19 @@ namespace hgemm {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+// One 16 x 16 x 32 matrix-core product of 16-bit operands in format FMT,
+// accumulated in fp32.  Operands travel as 8 16-bit words.
+template <int FMT>
+__device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
+  if constexpr (FMT == kFmtF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a),
+                                                   __builtin_bit_cast(b8, b), c, 0, 0, 0);
+  }
+}
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
@@ -109,15 +122,16 @@ constexpr int kWaitLgkm0 = 0xC07F;     // lgkmcnt(0)
 // launch has `grid` workgroups; workgroup b handles tiles b, b + grid, ...
 // (< tiles), one after another, as one continuous stream of K slabs.
 struct TileArgs {
-  F16Args p;
+  Args16 p;
   int64_t tiles;
 };
 
-template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI>
+template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
+          int FMT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileArgs ta) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
-  const F16Args& p = ta.p;
+  const Args16& p = ta.p;
   // Two slab stages, then the epilogue staging area (16 rows of 256 bytes per
   // wave, see below).
   constexpr int kOutRows = 16;
@@ -218,7 +232,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
     for (int i = 0; i < C::kBlocksM; ++i)
 #pragma unroll
       for (int j = 0; j < C::kBlocksN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma16<FMT>(fb[set][j], fa[set][i], acc[i][j]);
   };
 
   // Epilogue of the tile with origin (m0, n0): acc[i][j][v] is
@@ -244,14 +258,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             float x = acc[i][j][v];
-            if (p.bias) x += (float)bq[v];
+            if (p.bias) x += word_to_f32<FMT>(bq[v]);
             x = epi_act(x, p.act);
-            if (p.res) x += (float)rq[v];
-            o[v] = (half_t)x;
+            if (p.res) x += word_to_f32<FMT>(rq[v]);
+            o[v] = f32_to_word<FMT>(x);
           }
         } else {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = (half_t)acc[i][j][v];
+          for (int v = 0; v < 4; ++v) o[v] = f32_to_word<FMT>(acc[i][j][v]);
         }
         const int c = 2 * j + (g >> 1);
         *(h4*)(stage_out + r * C::kOutRowBytes + 16 * (c ^ r) + 8 * (g & 1)) = o;
@@ -401,8 +415,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
 // PERSISTENT: at most `slots` workgroups (as many as the GPU runs at once),
 // each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
-          bool PERSISTENT = true, bool EPI = false>
-hipError_t launch(const F16Args& a, int slots, hipStream_t stream) {
+          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16>
+hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN);
   const int64_t max_grid = int64_t(1) << 20;
@@ -410,8 +424,9 @@ hipError_t launch(const F16Args& a, int slots, hipStream_t stream) {
   if (grid < 1) grid = 1;
   TileArgs ta{a, tiles};
   void* args[] = {&ta};
-  return hipLaunchKernel((const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI>,
-                         dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
+  return hipLaunchKernel(
+      (const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT>,
+      dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 
 // Leading dimensions must also keep a lane's 32-bit copy offset (up to 8 rows

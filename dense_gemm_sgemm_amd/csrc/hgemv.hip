@@ -1,5 +1,6 @@
-// fp16 C = A * B^T when M or N is at most 8: the matrix-vector case of decode
-// steps (page "第 6 章 Shared Memory & Tile", section 6.5.5).
+// 16-bit (fp16 or bf16) C = A * B^T when M or N is at most 8: the
+// matrix-vector case of decode steps (page "第 6 章 Shared Memory & Tile",
+// section 6.5.5).
 //
 // With M <= 8 each output is C[v][r] = dot(B row r, A row v); with N <= 8 it
 // is C[r][v] = dot(A row r, B row v).  Either way one long operand W (B or A)
@@ -7,8 +8,8 @@
 // operand) are re-read from cache.  A tile of a tiled kernel would be almost
 // empty here and the matrix cores idle; the bound is HBM bandwidth for W, so
 // the kernel keeps as many W bytes in flight as it can and does its
-// arithmetic with v_dot2_f32_f16 (two fp16 products added into an fp32
-// accumulator):
+// arithmetic with v_dot2_f32_f16 / v_dot2_f32_bf16 (two products added into
+// an fp32 accumulator):
 //
 //  * a row group is 4 rows of W and TPR threads (one wave, or the whole
 //    workgroup of 4 waves for long rows); thread t of the group takes the
@@ -74,10 +75,24 @@ __device__ __forceinline__ h8 load_part(const char* base, uint32_t off, int n) {
   return v;
 }
 
+typedef __bf16 bh2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bh8 __attribute__((ext_vector_type(8)));
+
+// acc + the dot product of 8 16-bit words of format FMT, two products at a
+// time into the fp32 accumulator (v_dot2_f32_f16 / v_dot2_f32_bf16).
+template <int FMT>
 __device__ __forceinline__ float dot8(h8 w, h8 x, float acc) {
+  if constexpr (FMT == kFmtF16) {
 #pragma unroll
-  for (int e = 0; e < 8; e += 2)
-    acc = __builtin_amdgcn_fdot2(h2{w[e], w[e + 1]}, h2{x[e], x[e + 1]}, acc, false);
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2(h2{w[e], w[e + 1]}, h2{x[e], x[e + 1]}, acc, false);
+  } else {
+    const bh8 wb = __builtin_bit_cast(bh8, w), xb = __builtin_bit_cast(bh8, x);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(bh2{wb[e], wb[e + 1]}, bh2{xb[e], xb[e + 1]}, acc,
+                                            false);
+  }
   return acc;
 }
 
@@ -109,7 +124,7 @@ __device__ __forceinline__ float wave_reduce(float (&a)[P], int lane) {
 
 // U chunk steps of one thread: every load is issued before the first
 // product, so that 4 U + V U loads are in flight at once.
-template <int U, int V>
+template <int U, int V, int FMT>
 __device__ __forceinline__ void chunk_steps(const char* const (&w)[kRows],
                                             const char* const (&x)[V], uint32_t off,
                                             uint32_t stride, float* acc) {
@@ -128,10 +143,10 @@ __device__ __forceinline__ void chunk_steps(const char* const (&w)[kRows],
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[r * V + v] = dot8(wv[u][r], xv[u][v], acc[r * V + v]);
+      for (int v = 0; v < V; ++v) acc[r * V + v] = dot8<FMT>(wv[u][r], xv[u][v], acc[r * V + v]);
 }
 
-template <int V, int TPR, int U, bool EPI>
+template <int V, int TPR, int U, bool EPI, int FMT>
 __global__ __launch_bounds__(kThreads) void hgemv_kernel(GemvArgs p, int64_t wg_base) {
   constexpr int kRV = kRows * V;
   constexpr int P = pow2_at_least(kRV);
@@ -166,14 +181,14 @@ __global__ __launch_bounds__(kThreads) void hgemv_kernel(GemvArgs p, int64_t wg_
   uint32_t off = 16u * t;
   constexpr uint32_t kStride = 16u * TPR;
   int i = 0;
-  for (; i + U <= nfull; i += U, off += U * kStride) chunk_steps<U, V>(w, x, off, kStride, acc);
-  for (; i < nfull; ++i, off += kStride) chunk_steps<1, V>(w, x, off, kStride, acc);
+  for (; i + U <= nfull; i += U, off += U * kStride) chunk_steps<U, V, FMT>(w, x, off, kStride, acc);
+  for (; i < nfull; ++i, off += kStride) chunk_steps<1, V, FMT>(w, x, off, kStride, acc);
   // The last, partial chunk step: whole chunks below Kc, then the thread
   // whose next chunk is Kc takes the K % 8 tail.
   const int c = t + nfull * TPR;
   const int tail = p.K & 7;
   if (c < Kc) {
-    chunk_steps<1, V>(w, x, off, kStride, acc);
+    chunk_steps<1, V, FMT>(w, x, off, kStride, acc);
   } else if (c == Kc && tail != 0) {
     h8 wv[kRows], xv[V];
 #pragma unroll
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void hgemv_kernel(GemvArgs p, int64_t wg_
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[r * V + v] = dot8(wv[r], xv[v], acc[r * V + v]);
+      for (int v = 0; v < V; ++v) acc[r * V + v] = dot8<FMT>(wv[r], xv[v], acc[r * V + v]);
   }
 
   float s = wave_reduce<P>(acc, lane);
@@ -206,34 +221,46 @@ __global__ __launch_bounds__(kThreads) void hgemv_kernel(GemvArgs p, int64_t wg_
   const int64_t row = r0 + r;
   if (row >= p.R) return;
   if constexpr (EPI) {
-    if (p.bias) s += (float)p.bias[row * p.b_r + v * p.b_v];
+    if (p.bias) s += word_to_f32<FMT>(p.bias[row * p.b_r + v * p.b_v]);
     s = epi_act(s, p.act);
-    if (p.res) s += (float)p.res[row * p.res_r + v * p.res_v];
+    if (p.res) s += word_to_f32<FMT>(p.res[row * p.res_r + v * p.res_v]);
   }
-  p.Y[row * p.y_r + v * p.y_v] = (half_t)s;
+  p.Y[row * p.y_r + v * p.y_v] = f32_to_word<FMT>(s);
 }
 
 typedef void (*KernelFn)(GemvArgs, int64_t);
 
-template <int TPR, int U, bool EPI>
-KernelFn pick(int V) {
+template <int TPR, int U, bool EPI, int FMT>
+KernelFn pick_v(int V) {
   switch (V) {
-    case 1: return hgemv_kernel<1, TPR, U, EPI>;
-    case 2: return hgemv_kernel<2, TPR, U, EPI>;
-    case 3: return hgemv_kernel<3, TPR, U, EPI>;
-    case 4: return hgemv_kernel<4, TPR, U, EPI>;
-    case 5: return hgemv_kernel<5, TPR, U, EPI>;
-    case 6: return hgemv_kernel<6, TPR, U, EPI>;
-    case 7: return hgemv_kernel<7, TPR, U, EPI>;
-    default: return hgemv_kernel<8, TPR, U, EPI>;
+    case 1: return hgemv_kernel<1, TPR, U, EPI, FMT>;
+    case 2: return hgemv_kernel<2, TPR, U, EPI, FMT>;
+    case 3: return hgemv_kernel<3, TPR, U, EPI, FMT>;
+    case 4: return hgemv_kernel<4, TPR, U, EPI, FMT>;
+    case 5: return hgemv_kernel<5, TPR, U, EPI, FMT>;
+    case 6: return hgemv_kernel<6, TPR, U, EPI, FMT>;
+    case 7: return hgemv_kernel<7, TPR, U, EPI, FMT>;
+    default: return hgemv_kernel<8, TPR, U, EPI, FMT>;
   }
+}
+
+// Rows of K >= 2048 go to a whole workgroup per row group, with four chunk
+// steps in flight for very long rows and one or two vectors; shorter rows to
+// one wave per row group.
+template <bool EPI, int FMT>
+KernelFn pick(int V, int kc, bool& wide) {
+  wide = kc >= kThreads;
+  if (!wide) return pick_v<64, 2, EPI, FMT>(V);
+  if (V <= 2 && kc >= 4 * kThreads)
+    return V == 1 ? hgemv_kernel<1, kThreads, 4, EPI, FMT> : hgemv_kernel<2, kThreads, 4, EPI, FMT>;
+  return pick_v<kThreads, 2, EPI, FMT>(V);
 }
 
 }  // namespace hgemv
 
 bool f16_gemv_fits(int M, int N) { return M <= hgemv::kMaxV || N <= hgemv::kMaxV; }
 
-hipError_t launch_f16_gemv(const F16Args& a, bool epi, hipStream_t stream) {
+hipError_t launch_f16_gemv(const Args16& a, bool epi, hipStream_t stream) {
   using namespace hgemv;
   GemvArgs g;
   int V;
@@ -255,16 +282,13 @@ hipError_t launch_f16_gemv(const F16Args& a, bool epi, hipStream_t stream) {
   // 4.1 us against 5.7 us).  Very long rows with one or two vectors keep four
   // chunk steps in flight (K = 16384: 83 us against 87 us).
   const int kc = a.K >> 3;
-  const bool wide = kc >= kThreads;
-  const int tpr = wide ? kThreads : 64;
+  bool wide = false;
   KernelFn fn;
-  if (!wide)
-    fn = epi ? pick<64, 2, true>(V) : pick<64, 2, false>(V);
-  else if (V <= 2 && kc >= 4 * kThreads)
-    fn = V == 1 ? (epi ? hgemv_kernel<1, kThreads, 4, true> : hgemv_kernel<1, kThreads, 4, false>)
-                : (epi ? hgemv_kernel<2, kThreads, 4, true> : hgemv_kernel<2, kThreads, 4, false>);
+  if (a.fmt == kFmtBF16)
+    fn = epi ? pick<true, kFmtBF16>(V, kc, wide) : pick<false, kFmtBF16>(V, kc, wide);
   else
-    fn = epi ? pick<kThreads, 2, true>(V) : pick<kThreads, 2, false>(V);
+    fn = epi ? pick<true, kFmtF16>(V, kc, wide) : pick<false, kFmtF16>(V, kc, wide);
+  const int tpr = wide ? kThreads : 64;
   const int64_t per_wg = kThreads / tpr;
   const int64_t wgs = (groups + per_wg - 1) / per_wg;
   return launch_tiles(reinterpret_cast<const void*>(fn), g, wgs, kThreads, 0, stream);

@@ -29,10 +29,16 @@ struct F32Args {
   SplitK sk;                      // split-K partial products (partial kernels only)
 };
 
-// Arguments of one fp16 A*B^T call.  The last four describe the fused
-// write-back C = act(A*B^T + bias) + residual; kernels instantiated without
-// it ignore them.
-struct F16Args {
+// 16-bit storage formats.  Kernels move both as 16-bit words (half_t
+// pointers) and convert through word_to_f32 / f32_to_word.
+enum { kFmtF16 = 0, kFmtBF16 = 1 };
+typedef __bf16 bf16_t;
+
+// Arguments of one 16-bit A*B^T call (A, B, C, bias and residual all in
+// format `fmt`).  bias .. act describe the fused write-back
+// C = act(A*B^T + bias) + residual; kernels instantiated without it ignore
+// them.
+struct Args16 {
   const half_t* A;
   const half_t* B;
   half_t* C;
@@ -43,7 +49,28 @@ struct F16Args {
   int64_t ldr = 0;
   int act = 0;                    // 0 none, 1 ReLU, 2 SiLU
   SplitK sk;                      // split-K partial products (partial kernels only)
+  int fmt = kFmtF16;              // storage format of every 16-bit operand
 };
+
+// A 16-bit storage word as fp32, and fp32 rounded to a storage word (nearest,
+// ties to even; bfloat16 through the hardware conversion).
+template <int FMT>
+__device__ __forceinline__ float word_to_f32(half_t w) {
+  if constexpr (FMT == kFmtF16) {
+    return (float)w;
+  } else {
+    return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, w) << 16);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ half_t f32_to_word(float x) {
+  if constexpr (FMT == kFmtF16) {
+    return (half_t)x;
+  } else {
+    return __builtin_bit_cast(half_t, (bf16_t)x);
+  }
+}
 
 // The fused write-back's activation on an fp32 value.
 __device__ __forceinline__ float epi_act(float x, int act) {
@@ -69,14 +96,17 @@ SplitK splitk_args(const SplitPlan& plan, int M, int N, void* workspace);
 hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream);
 hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream);
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream);
-hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream);
-hipError_t launch_f16_edge(const F16Args& a, bool epi, hipStream_t stream);
-hipError_t launch_f16_mfma(const F16Args& a, bool epi, int cus, hipStream_t stream);
-hipError_t launch_f16_gemv(const F16Args& a, bool epi, hipStream_t stream);
+hipError_t launch_f16_zero(const Args16& a, hipStream_t stream);
+hipError_t launch_f16_edge(const Args16& a, bool epi, hipStream_t stream);
+hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream);
+hipError_t launch_f16_gemv(const Args16& a, bool epi, hipStream_t stream);
+// dst[c * ldd + r] = src[r * lds + c] for a rows x cols matrix of 16-bit words.
+hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols, half_t* dst,
+                              int64_t ldd, hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.
-hipError_t launch_f16_partials(const F16Args& a, hipStream_t stream);
+hipError_t launch_f16_partials(const Args16& a, hipStream_t stream);
 hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);
-hipError_t launch_f16_splitk(const F16Args& a, bool epi, hipStream_t stream);
+hipError_t launch_f16_splitk(const Args16& a, bool epi, hipStream_t stream);
 hipError_t launch_f32_splitk(const F32Args& a, hipStream_t stream);
 
 // Shape and alignment conditions of the fast kernels (checked on the host).

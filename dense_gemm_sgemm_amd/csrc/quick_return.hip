@@ -22,7 +22,7 @@ __global__ __launch_bounds__(kThreads) void sgemm_scale_kernel(F32Args p) {
 }
 
 // ---------------------------------------------------------------- fp16 -------
-__global__ __launch_bounds__(kThreads) void hgemm_zero_kernel(F16Args p) {
+__global__ __launch_bounds__(kThreads) void hgemm_zero_kernel(Args16 p) {
   const int64_t total = (int64_t)p.M * p.N;
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * kThreads) {
@@ -45,8 +45,8 @@ hipError_t launch_f32_scale(const F32Args& a, hipStream_t stream) {
                          dim3(kThreads), args, 0, stream);
 }
 
-hipError_t launch_f16_zero(const F16Args& a, hipStream_t stream) {
-  F16Args p = a;
+hipError_t launch_f16_zero(const Args16& a, hipStream_t stream) {
+  Args16 p = a;
   void* args[] = {&p};
   return hipLaunchKernel((const void*)hgemm_zero_kernel, dim3(fill_blocks(a.M, a.N)),
                          dim3(kThreads), args, 0, stream);

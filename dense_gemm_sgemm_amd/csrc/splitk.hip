@@ -11,8 +11,9 @@
 //  * the reduction kernel gives each thread four consecutive outputs of one
 //    row and adds the ranges in order 0, 1, ..., splits - 1, so the result
 //    does not depend on timing; it then applies the call's write-back (fp32:
-//    alpha * sum + beta * C, C not read when beta == 0; fp16: rounding to
-//    half, or the fused bias / activation / residual);
+//    alpha * sum + beta * C, C not read when beta == 0; fp16 and bf16:
+//    rounding to the storage format, or the fused bias / activation /
+//    residual);
 //  * the split count (measured on MI355X over 1 to 144 tiles of 128 x 128
 //    and K from 2048 to 16384): as many ranges as keep tiles x splits within
 //    one wave of two workgroups per CU, at most 64, each range at least 256
@@ -71,8 +72,8 @@ __device__ __forceinline__ bool gather(const SplitK& sk, int M, int N, int64_t b
   return true;
 }
 
-template <bool EPI>
-__global__ __launch_bounds__(kThreads) void reduce_f16_kernel(F16Args p, int64_t base) {
+template <bool EPI, int FMT>
+__global__ __launch_bounds__(kThreads) void reduce_f16_kernel(Args16 p, int64_t base) {
   Quad q;
   if (!gather(p.sk, p.M, p.N, base, q)) return;
   h4 o;
@@ -81,11 +82,11 @@ __global__ __launch_bounds__(kThreads) void reduce_f16_kernel(F16Args p, int64_t
     float x = q.acc[e];
     if constexpr (EPI) {
       const bool in = q.n + e < p.N;
-      if (p.bias && in) x += (float)p.bias[q.n + e];
+      if (p.bias && in) x += word_to_f32<FMT>(p.bias[q.n + e]);
       x = epi_act(x, p.act);
-      if (p.res && in) x += (float)p.res[q.m * p.ldr + q.n + e];
+      if (p.res && in) x += word_to_f32<FMT>(p.res[q.m * p.ldr + q.n + e]);
     }
-    o[e] = (half_t)x;
+    o[e] = f32_to_word<FMT>(x);
   }
   half_t* dst = p.C + q.m * p.ldc + q.n;
   if (q.n + 4 <= p.N) {
@@ -168,10 +169,14 @@ SplitK splitk_args(const SplitPlan& plan, int M, int N, void* workspace) {
   return sk;
 }
 
-hipError_t launch_f16_splitk(const F16Args& a, bool epi, hipStream_t stream) {
+hipError_t launch_f16_splitk(const Args16& a, bool epi, hipStream_t stream) {
   const hipError_t e = launch_f16_partials(a, stream);
   if (e != hipSuccess) return e;
-  const void* k = epi ? (const void*)reduce_f16_kernel<true> : (const void*)reduce_f16_kernel<false>;
+  const void* k = a.fmt == kFmtBF16
+                      ? (epi ? (const void*)reduce_f16_kernel<true, kFmtBF16>
+                             : (const void*)reduce_f16_kernel<false, kFmtBF16>)
+                      : (epi ? (const void*)reduce_f16_kernel<true, kFmtF16>
+                             : (const void*)reduce_f16_kernel<false, kFmtF16>);
   return launch_tiles(k, a, reduce_blocks(a.M, a.N), kThreads, 0, stream);
 }
 

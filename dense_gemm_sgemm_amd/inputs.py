@@ -9,7 +9,9 @@ Recipe: ``numpy.random.default_rng(seed)``; seeds 1, 2 and 3 for A, B and C_in
 B from seeds 1 and 2).  fp32 operands are uniform on [-1, 1) converted to
 float32; fp16 operands are drawn in float64 and rounded to binary16 by numpy's
 round-to-nearest-even cast.  The ragged fp16 workload draws normal(0, sd=0.5).
-All operands are packed row-major.
+bfloat16 operands are the same draws converted to float32 and rounded to
+bfloat16 (nearest, ties to even), kept as uint16 bit patterns since numpy has
+no bfloat16 type.  All operands are packed row-major in their stored layout.
 """
 from __future__ import annotations
 
@@ -65,6 +67,29 @@ def hgemm_nt_operands(M: int, N: int, K: int, dist: str = "uniform"):
     if dist == "uniform":
         return uniform((M, K), SEED_A, np.float16), uniform((N, K), SEED_B, np.float16)
     return normal((M, K), SEED_A), normal((N, K), SEED_B)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float64 draws: converted to float32,
+    then rounded to bfloat16 on the float32 bits (nearest, ties to even).  The
+    draws are finite."""
+    bits = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    bits = bits + 0x7FFF + ((bits >> 16) & 1)
+    return (bits >> 16).astype(np.uint16)
+
+
+def operands16(shape_a, shape_b, fmt: str = "f16", dist: str = "normal"):
+    """A and B of the given stored shapes, binary16 (float16 arrays) or
+    bfloat16 (uint16 bit patterns), from seeds SEED_A and SEED_B."""
+    if dist == "uniform":
+        a = np.random.default_rng(SEED_A).uniform(-1.0, 1.0, size=shape_a)
+        b = np.random.default_rng(SEED_B).uniform(-1.0, 1.0, size=shape_b)
+    else:
+        a = np.random.default_rng(SEED_A).normal(0.0, 0.5, size=shape_a)
+        b = np.random.default_rng(SEED_B).normal(0.0, 0.5, size=shape_b)
+    if fmt == "f16":
+        return a.astype(np.float16), b.astype(np.float16)
+    return bf16_bits(a), bf16_bits(b)
 
 
 def workload_operands(name: str):

@@ -54,8 +54,8 @@ enum {
   GEMM_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or the current one is not gfx950 */
   GEMM_ERR_LAUNCH = -5,            /* the HIP runtime refused the kernel launch      */
   GEMM_ERR_BAD_ARG = -6,           /* an enumerated argument has no defined meaning  */
-  GEMM_ERR_WORKSPACE = -7          /* split-K workspace NULL, too small or not       */
-                                   /*   16-byte aligned                               */
+  GEMM_ERR_WORKSPACE = -7          /* a workspace the call needs is NULL, too small, */
+                                   /*   misaligned, or could not be allocated        */
 };
 
 /*
@@ -189,6 +189,47 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K,
 MI355GEMM_API unsigned long long gemm_f32_splitk_workspace(int M, int N, int K, int splits);
 MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int K, int splits);
 
+/*
+ * 16-bit GEMM in any operand layout, fp16 or bf16, with the fused write-back:
+ *
+ *     C = act(op(A) * op(B) + bias) + residual
+ *
+ * Page 1 ("第 6 章 Shared Memory & Tile", section 6.3.3) drives the matrix
+ * units through the library GEMM with a storage type (fp16 or bf16) and an
+ * operation per operand; the NT page ("从零开始的 AI Infra: 算子基础与GPU架构",
+ * section "19. 去掉转置") compares B stored [n][k] with its transpose stored
+ * [k][n].  Here, all row-major:
+ *
+ *   type : GEMM_TYPE_F16 (IEEE binary16) or GEMM_TYPE_BF16 (bfloat16); A, B,
+ *          C, bias and residual are all of this type.  Products accumulate
+ *          in fp32; each output is rounded once to the type (nearest, ties
+ *          to even).
+ *   op_a : GEMM_OP_N: A is [M][lda], lda >= max(1, K), op(A) = A.
+ *          GEMM_OP_T: A is [K][lda], lda >= max(1, M), op(A) = A^T.
+ *   op_b : GEMM_OP_N: B is [K][ldb], ldb >= max(1, N), op(B) = B.
+ *          GEMM_OP_T: B is [N][ldb], ldb >= max(1, K), op(B) = B^T.
+ *   bias, act, residual, ldr, C, ldc : as for gemm_f16_nt_ex (bias NULL,
+ *          GEMM_ACT_NONE and residual NULL give the plain product).
+ *
+ * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  Other
+ * layouts first copy each operand that is not K-contiguous (A for OP_T, B for
+ * OP_N) into a K-contiguous workspace with a transposition kernel, then run
+ * the A * B^T kernels; the workspace comes from the same stream-ordered,
+ * per-stream store as the split-K workspace.  Unknown type, op or act values
+ * are GEMM_ERR_BAD_ARG; a workspace that cannot be allocated is
+ * GEMM_ERR_WORKSPACE.
+ */
+enum { GEMM_TYPE_F16 = 0, GEMM_TYPE_BF16 = 1 };
+enum { GEMM_OP_N = 0, GEMM_OP_T = 1 };
+
+MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K,
+                          const void* A, int lda,
+                          const void* B, int ldb,
+                          const void* bias, int act,
+                          const void* residual, int ldr,
+                          void* C, int ldc,
+                          void* stream);
+
 /* A static, human-readable message for a GEMM_* status code. */
 MI355GEMM_API const char* gemm_status_string(int status);
 
@@ -196,8 +237,8 @@ MI355GEMM_API const char* gemm_status_string(int status);
  * Kernel selection, exposed for inspection and testing.  These are pure host
  * functions: they make no HIP call and never touch the pointed-to memory
  * (the pointers are only checked for alignment).  They return the GEMM_PATH_*
- * value that gemm_f32 / gemm_f16_nt / gemm_f16_nt_ex would launch for the
- * same arguments, or a
+ * value that gemm_f32 / gemm_f16_nt / gemm_f16_nt_ex / gemm_ex would launch
+ * for the same arguments, or a
  * negative GEMM_ERR_* code for arguments those calls would reject (a device
  * check excepted).
  *
@@ -236,6 +277,16 @@ MI355GEMM_API int gemm_f16_nt_ex_path(int M, int N, int K,
                                       const void* bias, int act,
                                       const void* residual, int ldr,
                                       const void* C, int ldc);
+
+/* For gemm_ex: the path of the A * B^T kernels that run after any
+ * transposition of the operands (transposed copies are 16-byte aligned with
+ * rows padded to a multiple of 8 elements). */
+MI355GEMM_API int gemm_ex_path(int type, int op_a, int op_b, int M, int N, int K,
+                               const void* A, int lda,
+                               const void* B, int ldb,
+                               const void* bias, int act,
+                               const void* residual, int ldr,
+                               const void* C, int ldc);
 
 /* A static name for a GEMM_PATH_* value ("f32_mfma", ...); "?" if unknown. */
 MI355GEMM_API const char* gemm_path_name(int path);

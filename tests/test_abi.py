@@ -39,7 +39,8 @@ def test_header_declares_the_abi():
     assert declared_symbols() == sorted(["gemm_f32", "gemm_f16_nt", "gemm_f16_nt_ex",
                                          "gemm_f32_splitk", "gemm_f16_nt_splitk",
                                          "gemm_f32_splitk_workspace",
-                                         "gemm_f16_nt_splitk_workspace",
+                                         "gemm_f16_nt_splitk_workspace", "gemm_ex",
+                                         "gemm_ex_path",
                                          "gemm_status_string", "gemm_f32_path",
                                          "gemm_f16_nt_path", "gemm_f16_nt_ex_path",
                                          "gemm_path_name"])
@@ -200,6 +201,47 @@ def test_split_k_plans(lib, monkeypatch):
     assert ws32(130, 129, 40, 7) == 3 * 256 * 256 * 4                  # 3 slabs of 16
     monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
     assert f16(lib, 512, 512, 16384) == F16_GENERAL and f32(lib, 512, 512, 16384) == F32_GENERAL
+
+
+def ex(lib, type_, op_a, op_b, M, N, K, A=ALIGNED, lda=None, B=ALIGNED, ldb=None, bias=None,
+       act=0, res=None, ldr=None, C=ALIGNED, ldc=None):
+    lda = (max(1, K) if op_a == 0 else max(1, M)) if lda is None else lda
+    ldb = (max(1, N) if op_b == 0 else max(1, K)) if ldb is None else ldb
+    ldr = max(1, N) if ldr is None else ldr
+    ldc = max(1, N) if ldc is None else ldc
+    return lib.gemm_ex_path(type_, op_a, op_b, M, N, K, p(A) if A else None, lda,
+                            p(B) if B else None, ldb, p(bias) if bias else None, act,
+                            p(res) if res else None, ldr, p(C) if C else None, ldc)
+
+
+def test_gemm_ex_validation_and_paths(lib, monkeypatch):
+    """Layouts: op N/T per operand with their leading-dimension rules; the
+    A * B^T kernels behind them; unknown enumerations are GEMM_ERR_BAD_ARG."""
+    monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
+    N_, T_ = 0, 1
+    for t in (0, 1):
+        assert ex(lib, t, N_, T_, 5376, 5376, 2048) == F16_MFMA
+        assert ex(lib, t, N_, N_, 5376, 5376, 2048) == F16_MFMA      # B through a copy
+        assert ex(lib, t, T_, N_, 5376, 5376, 2048) == F16_MFMA
+        assert ex(lib, t, T_, T_, 5000, 3001, 1537) == F16_GENERAL
+        assert ex(lib, t, N_, N_, 1, 4096, 4096) == F16_GEMV
+        assert ex(lib, t, T_, N_, 512, 512, 16384) == F16_SPLITK
+        # a copy has aligned, padded rows whatever the original alignment
+        assert ex(lib, t, T_, T_, 256, 256, 64, A=ALIGNED + 2, lda=257) == F16_MFMA
+        assert ex(lib, t, N_, T_, 256, 256, 64, A=ALIGNED + 2, lda=67) == F16_GENERAL
+    assert ex(lib, 2, 0, 1, 8, 8, 8) == -6 and ex(lib, 0, 2, 1, 8, 8, 8) == -6
+    assert ex(lib, 0, 0, -1, 8, 8, 8) == -6 and ex(lib, 0, 0, 1, 8, 8, 8, act=5) == -6
+    # leading dimensions follow the stored shapes
+    assert ex(lib, 0, T_, T_, 100, 8, 50, lda=99) == -2 and ex(lib, 0, T_, T_, 100, 8, 50) == F16_GEMV
+    assert ex(lib, 0, N_, N_, 16, 100, 50, ldb=99) == -2 and ex(lib, 0, N_, N_, 16, 100, 50) > 0
+    assert ex(lib, 0, N_, T_, 16, 16, 0, A=0, B=0) == F16_ZERO
+    assert ex(lib, 0, N_, T_, 16, 16, 0, A=0, B=0, bias=ALIGNED) == F16_GENERAL
+    assert ex(lib, 1, N_, T_, 0, 16, 5, A=0, B=0, C=0) == 0
+    monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
+    assert ex(lib, 1, N_, N_, 5376, 5376, 2048) == F16_GENERAL
+    null = None
+    assert lib.gemm_ex(3, 0, 1, 4, 4, 4, p(ALIGNED), 4, p(ALIGNED), 4, null, 0, null, 4,
+                       p(ALIGNED), 4, null) == -6
 
 
 def test_split_k_workspace_errors_need_no_device(lib):

@@ -1,0 +1,200 @@
+"""GPU parity of gemm_ex: bf16 and fp16 in all four operand layouts, with and
+without the fused write-back, against the CPU oracle.
+
+Layout N/T follows the library: op "n" means A stored M x K and B stored
+K x N, op "t" means A stored K x M and B stored N x K, so ("n", "t") is the
+A * B^T product of gemm_f16_nt.  bfloat16 arrays travel as uint16 bit
+patterns on the host (numpy has no bfloat16) and as torch.bfloat16 tensors on
+the GPU.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_gemm_sgemm_amd import inputs
+from expect import expected_f16_path
+from tolerance import check16
+
+torch = pytest.importorskip("torch")
+import dense_gemm_sgemm_amd as dg  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+LAYOUTS = [("n", "t"), ("n", "n"), ("t", "n"), ("t", "t")]
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print("\n[gpu case] %s" % request.node.nodeid, flush=True)
+    sys.stdout.flush()
+    yield
+
+
+def to_dev(x: np.ndarray, fmt: str):
+    x = np.ascontiguousarray(x)
+    if fmt == "f16":
+        return torch.from_numpy(x).to(DEV)
+    return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def to_host(t, fmt: str) -> np.ndarray:
+    if fmt == "f16":
+        return t.cpu().numpy()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dtype_of(fmt: str):
+    return torch.float16 if fmt == "f16" else torch.bfloat16
+
+
+def stored_shapes(M, N, K, op_a, op_b):
+    return ((M, K) if op_a == "n" else (K, M)), ((K, N) if op_b == "n" else (N, K))
+
+
+def absval(x: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == "f16":
+        return (x.view(np.uint16) & np.uint16(0x7FFF)).view(np.float16)
+    return x & np.uint16(0x7FFF)
+
+
+def reference(A, B, op_a, op_b, fmt, bias=None, act="none", res=None):
+    """(fp64 value, fp64 sums of |a*b|) of the product from the oracle."""
+    ref = oracle.gemm_ex_exact(A, B, op_a, op_b, bias, act, res, fmt)
+    sab = oracle.gemm_ex_exact(absval(A, fmt), absval(B, fmt), op_a, op_b, fmt=fmt)
+    return ref, sab
+
+
+def run_ex(A, B, op_a, op_b, fmt, M, N, bias=None, act="none", res=None, expect=None):
+    dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+    dbias = to_dev(bias, fmt) if bias is not None else None
+    dres = to_dev(res, fmt) if res is not None else None
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=dtype_of(fmt))
+    if expect is not None:
+        assert dg.ex_path(dA, dB, dC, op_a, op_b, dbias, act, dres) == expect
+    dg.gemm_ex(dA, dB, dC, op_a, op_b, dbias, act, dres)
+    torch.cuda.synchronize()
+    return to_host(dC, fmt)
+
+
+# Shapes reach each kernel: fast tiles 256 x 256, 256 x 224 and 128 x 128, the
+# edge kernel (ragged, odd K), the matrix-vector kernel both ways, split-K.
+SHAPES = [(256, 256, 64), (512, 448, 128), (128, 128, 192), (133, 70, 45), (257, 255, 65),
+          (1, 300, 777), (300, 3, 1000), (4, 129, 4100), (512, 512, 16384), (300, 200, 5000)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=lambda l: "".join(l))
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_layouts(shape, layout, fmt):
+    M, N, K = shape
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect=expected_f16_path("auto", M, N, K))
+    ref, sab = reference(A, B, op_a, op_b, fmt)
+    check16(got, ref, sab, fmt)
+
+
+EPI_CASES = [("silu", True, True), ("relu", True, False), ("none", False, True)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", [("n", "t"), ("n", "n"), ("t", "n")], ids=lambda l: "".join(l))
+@pytest.mark.parametrize("shape", [(256, 224, 64), (133, 70, 45), (1, 300, 4096),
+                                   (300, 200, 5000)], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)
+def test_layouts_fused(shape, layout, fmt, act, use_bias, use_res):
+    M, N, K = shape
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    rng = np.random.default_rng(43)
+    bias = res = None
+    if use_bias:
+        b = rng.normal(0, 1.5, N)
+        bias = b.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(b)
+    if use_res:
+        r = rng.normal(0, 2.0, (M, N))
+        res = r.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(r)
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, bias, act, res)
+    ref, sab = reference(A, B, op_a, op_b, fmt, bias, act, res)
+    dec = oracle.half_to_double if fmt == "f16" else oracle.bf16_to_double
+    babs = 0.0 if bias is None else np.abs(dec(bias))[None, :]
+    rabs = 0.0 if res is None else np.abs(dec(res))
+    check16(got, ref, sab, fmt, babs, rabs, fused=True)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_layouts_strided_unaligned_operands(fmt):
+    """Stored operands one element into their buffers with padded rows, for
+    every layout; C's padding is not written."""
+    for (op_a, op_b) in LAYOUTS:
+        for (M, N, K) in [(256, 256, 128), (133, 70, 45), (1, 200, 300)]:
+            sa, sb = stored_shapes(M, N, K, op_a, op_b)
+            A, B = inputs.operands16(sa, sb, fmt)
+            lda, ldb, ldc = sa[1] + 3, sb[1] + 1, N + 5
+            dt = dtype_of(fmt)
+            bufA = torch.zeros(sa[0] * lda + 2, device=DEV, dtype=dt)
+            bufB = torch.zeros(sb[0] * ldb + 2, device=DEV, dtype=dt)
+            bufC = torch.full((M * ldc + 2,), 5.0, device=DEV, dtype=dt)
+            dA = bufA[1:1 + sa[0] * lda].view(sa[0], lda)[:, :sa[1]]
+            dB = bufB[1:1 + sb[0] * ldb].view(sb[0], ldb)[:, :sb[1]]
+            dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+            dA.copy_(to_dev(A, fmt))
+            dB.copy_(to_dev(B, fmt))
+            dg.gemm_ex(dA, dB, dC, op_a, op_b)
+            torch.cuda.synchronize()
+            ref, sab = reference(A, B, op_a, op_b, fmt)
+            check16(to_host(dC.contiguous(), fmt), ref, sab, fmt)
+            full = to_host(bufC, fmt)
+            mask = np.ones(full.shape, bool)
+            idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+            mask[idx.ravel()] = False
+            five = np.float16(5.0) if fmt == "f16" else inputs.bf16_bits(np.array([5.0]))[0]
+            assert np.all(full[mask] == five)
+
+
+def test_bf16_exact_cases_and_determinism():
+    """Small-integer bf16 products are exact below 256 and round ties to even
+    above; repeated runs agree bitwise."""
+    A = inputs.bf16_bits(inputs.small_ints((256, 128), 1, -1, 1, np.float64))
+    B = inputs.bf16_bits(inputs.small_ints((256, 128), 2, -1, 1, np.float64))
+    got = run_ex(A, B, "n", "t", "bf16", 256, 256)
+    exact = oracle.bf16_to_double(A) @ oracle.bf16_to_double(B).T
+    assert np.array_equal(got, oracle.bf16_from_double(exact))
+    K = 576
+    A = inputs.bf16_bits(np.ones((256, K)))
+    B = np.zeros((256, K), np.uint16)
+    for row, total in enumerate([257, 258, 259, 261, 255, 513]):
+        B[row, :total] = inputs.bf16_bits(np.ones(total))
+    got = run_ex(A, B, "n", "t", "bf16", 256, 256)
+    assert list(oracle.bf16_to_double(got[0, :6])) == [256.0, 258.0, 260.0, 260.0, 255.0, 512.0]
+    A, B = inputs.operands16((512, 256), (256, 256), "bf16")
+    assert np.array_equal(run_ex(A, B, "n", "n", "bf16", 512, 256),
+                          run_ex(A, B, "n", "n", "bf16", 512, 256))
+
+
+@pytest.mark.parametrize("fmt,layout", [("bf16", ("n", "t")), ("f16", ("n", "n")),
+                                        ("bf16", ("t", "n"))])
+def test_workload_5376_layouts(fmt, layout):
+    """5376 x 5376 x 2048 in bf16 and in the other layouts, on the fast
+    kernel, sampled: whole rows and columns, three tiles and random points."""
+    from test_parity_gpu import sample_points, tile_windows
+    M = N = 5376
+    K = 2048
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt, dist="uniform")
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect="f16_mfma")
+    An, Bn = oracle.nt_operands(A, B, op_a, op_b)
+    rows, cols = sample_points(M, N, tile_windows(M, N, 256, 224))
+    ref = oracle.gemm_16_nt_points(An, Bn, rows, cols, fmt)
+    sab = oracle.gemm_16_nt_points(absval(An, fmt), absval(Bn, fmt), rows, cols, fmt)
+    r = check16(got[rows, cols], ref, sab, fmt)
+    print("[5376^2 x 2048 %s %s] checked %d outputs, max %.2f ulp"
+          % (fmt, "".join(layout), r["count"], r["max_ulps"]), flush=True)

@@ -15,6 +15,7 @@ import pytest
 
 import oracle
 from dense_gemm_sgemm_amd import inputs
+from expect import expected_f16_path, expected_f32_path
 from tolerance import f16_check, f16_ex_check, f32_check, f32_tolerance
 
 torch = pytest.importorskip("torch")
@@ -72,38 +73,6 @@ def gpu_f16(A, B, expect=None):
 
 def abs16(x: np.ndarray) -> np.ndarray:
     return (x.view(np.uint16) & np.uint16(0x7FFF)).view(np.float16)
-
-
-def splitk_auto(M, N, K, slab):
-    """The library's split-K rule: K of at least 2048 and at least three ranges,
-    with tiles x ranges within 512 workgroups (tiles of 128 x 128) and ranges
-    at least 256 (fp16) or 64 (fp32) deep."""
-    tiles = -(-M // 128) * -(-N // 128)
-    if K < 2048:
-        return False
-    return min(512 // tiles, K // (256 if slab == 64 else 64), 64) >= 3
-
-
-def expected_f32_path(mode, M, N, K):
-    if mode == "general":
-        return "f32_general"
-    if splitk_auto(M, N, K, 16):
-        return "f32_splitk"
-    return "f32_mfma" if (M % 64 == 0 and N % 64 == 0 and K % 16 == 0) else "f32_general"
-
-
-def expected_f16_path(mode, M, N, K):
-    if mode == "general":
-        return "f16_general"
-    if K == 0:
-        return "f16_zero"
-    if min(M, N) <= 8:
-        return "f16_gemv"
-    if splitk_auto(M, N, K, 64):
-        return "f16_splitk"
-    fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
-                            (M % 128 == 0 and N % 128 == 0))
-    return "f16_mfma" if fast else "f16_general"
 
 
 # ----------------------------------------------------------------- fp32 -----

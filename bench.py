@@ -37,6 +37,7 @@ V_NAME = "hgemv_nt_1x16384x4096"
 # (4 x 134 MB), more than the 256 MB last-level cache, so that every launch
 # streams its weights from HBM as a decode step over many layers would.
 V_COPIES = 4
+S_NAME = "hgemm_nt_128x128x16384"
 
 
 def parse_args():
@@ -45,12 +46,12 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused",
-                                       "hgemv"],
+                                       "hgemv", "hgemm_splitk"],
                     default="both",
                     help="time only one product (for profiling): one of the two step products, "
                          "the ragged 5000x3001x1537 fp16 product, the 5376^2 x 2048 product "
-                         "with the fused bias + SiLU + residual write-back, or the 1 x 16384 x "
-                         "4096 decode product")
+                         "with the fused bias + SiLU + residual write-back, the 1 x 16384 x "
+                         "4096 decode product, or the 128 x 128 x 16384 split-K product")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -77,6 +78,7 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES[H_NAME + "_bias_silu_residual"] = KERNEL_SOURCES[H_NAME]
 KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sgemm_amd/csrc/internal.h",
                           "dense_gemm_sgemm_amd/build.py"]
+KERNEL_SOURCES[S_NAME] = KERNEL_SOURCES[R_NAME] + ["dense_gemm_sgemm_amd/csrc/splitk.hip"]
 COPY_BYTES = 1 << 30
 
 
@@ -306,6 +308,14 @@ def main():
     if args.only == "hgemv":
         vw = inputs.WORKLOADS[V_NAME]
         parts.append((V_NAME, "f16", "hgemv_kernel", flops(vw), gemv_runner(dg, inputs, torch, dev)))
+    if args.only == "hgemm_splitk":
+        sw = inputs.WORKLOADS[S_NAME]
+        As, Bs = inputs.workload_operands(S_NAME)
+        dAs, dBs = torch.from_numpy(As).to(dev), torch.from_numpy(Bs).to(dev)
+        dCs = torch.empty(sw["M"], sw["N"], device=dev, dtype=torch.float16)
+        assert dg.f16_nt_path(dAs, dBs, dCs) == "f16_splitk"
+        parts.append((S_NAME, "f16", "hgemm_nt_edge_kernel", flops(sw),
+                      lambda: dg.gemm_f16_nt(dAs, dBs, dCs)))
     if args.only in ("both", "sgemm"):
         Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)

@@ -14,12 +14,14 @@ using namespace mi355gemm;
 
 namespace {
 
-// K slab depths of the tiled kernels, the granularity of split-K ranges, and
-// the shallowest ranges the automatic split-K choice makes.
+// K slab depths of the tiled kernels (the granularity of split-K ranges) and
+// the automatic split-K rules, measured on MI355X: the 16-bit partials run
+// on the full-tile kernel, fastest at 256-400 workgroups with ranges that
+// divide K; the fp32 partial kernel is fastest at about 512.
 constexpr int kF32Slab = 16;
 constexpr int kF16Slab = 64;
-constexpr int kF32MinRange = 64;
-constexpr int kF16MinRange = 256;
+constexpr SplitRule kF32Rule{64, 512, 3, false};
+constexpr SplitRule kF16Rule{256, 400, 2, true};
 
 bool force_general() {
   const char* v = std::getenv("MI355GEMM_FORCE_PATH");
@@ -59,7 +61,7 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
   if (K == 0 || alpha == 0.f) return GEMM_PATH_F32_SCALE;
   if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
   if (force_general()) return GEMM_PATH_F32_GENERAL;
-  if (splitk_plan(M, N, K, kF32Slab, kF32MinRange, 0).splits > 1) return GEMM_PATH_F32_SPLITK;
+  if (splitk_plan(M, N, K, kF32Slab, kF32Rule, 0).splits > 1) return GEMM_PATH_F32_SPLITK;
   if (f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F32_MFMA;
   return GEMM_PATH_F32_GENERAL;
 }
@@ -75,7 +77,7 @@ int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int l
   if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
   if (force_general()) return GEMM_PATH_F16_GENERAL;
   if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
-  if (splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
+  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
   if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F16_MFMA;
   return GEMM_PATH_F16_GENERAL;
 }
@@ -95,7 +97,7 @@ int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, in
   if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
   if (K == 0 || force_general()) return GEMM_PATH_F16_GENERAL;
   if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
-  if (splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
+  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
   if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) && f16_epi_fits(bias, res, ldr))
     return GEMM_PATH_F16_MFMA;
   return GEMM_PATH_F16_GENERAL;
@@ -143,7 +145,7 @@ int ex_select(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
   if (K == 0) return epi ? GEMM_PATH_F16_GENERAL : GEMM_PATH_F16_ZERO;
   if (force_general()) return GEMM_PATH_F16_GENERAL;
   if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
-  if (splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
+  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
   const ExLayout l = ex_layout(op_a, op_b, K, lda, ldb);
   if (f16_mfma_fits(M, N, K, l.copy_a ? kCopyAddress : A, l.lda, l.copy_b ? kCopyAddress : B,
                     l.ldb, C, ldc) &&
@@ -229,7 +231,7 @@ void* stream_workspace(hipStream_t s, size_t bytes, bool* owned) {
 // The split-K path of the plain calls.  If no workspace can be had, the
 // tiled kernel runs instead.
 hipError_t f32_auto_split(F32Args a, int cus, hipStream_t s) {
-  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF32Slab, kF32MinRange, 0);
+  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF32Slab, kF32Rule, 0);
   std::unique_lock<std::mutex> lock(g_ws_mutex);
   bool owned = false;
   void* ws = stream_workspace(s, plan.bytes, &owned);
@@ -242,14 +244,14 @@ hipError_t f32_auto_split(F32Args a, int cus, hipStream_t s) {
 }
 
 hipError_t f16_auto_split(Args16 a, bool epi, int cus, hipStream_t s) {
-  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF16Slab, kF16MinRange, 0);
+  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF16Slab, kF16Rule, 0);
   std::unique_lock<std::mutex> lock(g_ws_mutex);
   bool owned = false;
   void* ws = stream_workspace(s, plan.bytes, &owned);
   if (owned || ws == nullptr) lock.unlock();
   if (ws == nullptr) return f16_tiled(a, epi, cus, s);
   a.sk = splitk_args(plan, a.M, a.N, ws);
-  const hipError_t e = launch_f16_splitk(a, epi, s);
+  const hipError_t e = launch_f16_splitk(a, epi, cus, s);
   const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
   return e != hipSuccess ? e : f;
 }
@@ -342,7 +344,7 @@ MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K, con
   const size_t bytes_a = l.copy_a ? round256((size_t)M * l.lda * 2) : 0;
   const size_t bytes_b = l.copy_b ? round256((size_t)N * l.ldb * 2) : 0;
   const SplitPlan plan = path == GEMM_PATH_F16_SPLITK
-                             ? splitk_plan(M, N, K, kF16Slab, kF16MinRange, 0)
+                             ? splitk_plan(M, N, K, kF16Slab, kF16Rule, 0)
                              : SplitPlan{};
   const size_t total = bytes_a + bytes_b + (plan.splits > 1 ? plan.bytes : 0);
   std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
@@ -370,7 +372,7 @@ MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K, con
       case GEMM_PATH_F16_GEMV: e = launch_f16_gemv(a, epi, s); break;
       case GEMM_PATH_F16_SPLITK:
         a.sk = splitk_args(plan, M, N, ws + bytes_a + bytes_b);
-        e = launch_f16_splitk(a, epi, s);
+        e = launch_f16_splitk(a, epi, cus, s);
         break;
       case GEMM_PATH_F16_MFMA: e = launch_f16_mfma(a, epi, cus, s); break;
       default: e = launch_f16_edge(a, epi, s); break;
@@ -388,7 +390,7 @@ MI355GEMM_API int gemm_f32_splitk(int M, int N, int K, float alpha, const float*
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
   SplitPlan plan;
   if (path != GEMM_PATH_F32_SCALE && (splits > 0 || path == GEMM_PATH_F32_SPLITK))
-    plan = splitk_plan(M, N, K, kF32Slab, kF32MinRange, splits);
+    plan = splitk_plan(M, N, K, kF32Slab, kF32Rule, splits);
   if (plan.splits > 1 && !workspace_ok(plan, workspace, workspace_bytes))
     return GEMM_ERR_WORKSPACE;
   const int cus = check_device();
@@ -414,7 +416,7 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K, const void* A, int lda
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
   SplitPlan plan;
   if (path != GEMM_PATH_F16_ZERO && (splits > 0 || path == GEMM_PATH_F16_SPLITK))
-    plan = splitk_plan(M, N, K, kF16Slab, kF16MinRange, splits);
+    plan = splitk_plan(M, N, K, kF16Slab, kF16Rule, splits);
   if (plan.splits > 1 && !workspace_ok(plan, workspace, workspace_bytes))
     return GEMM_ERR_WORKSPACE;
   const int cus = check_device();
@@ -424,7 +426,7 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K, const void* A, int lda
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.splits > 1) {
     a.sk = splitk_args(plan, M, N, workspace);
-    return to_status(launch_f16_splitk(a, false, s));
+    return to_status(launch_f16_splitk(a, false, cus, s));
   }
   switch (path) {
     case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
@@ -437,13 +439,13 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K, const void* A, int lda
 
 MI355GEMM_API unsigned long long gemm_f32_splitk_workspace(int M, int N, int K, int splits) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return splitk_plan(M, N, K, kF32Slab, kF32MinRange, splits).bytes;
+  return splitk_plan(M, N, K, kF32Slab, kF32Rule, splits).bytes;
 }
 
 MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int K, int splits) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (splits <= 0 && f16_gemv_fits(M, N)) return 0;
-  return splitk_plan(M, N, K, kF16Slab, kF16MinRange, splits).bytes;
+  return splitk_plan(M, N, K, kF16Slab, kF16Rule, splits).bytes;
 }
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha, const float* A, int lda,

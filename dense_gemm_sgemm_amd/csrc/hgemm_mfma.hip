@@ -69,6 +69,22 @@ hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t strea
              : launch_shape<false, kFmtF16>(a, cus, stream);
 }
 
+// Split-K partial products on 128 x 128 full tiles (two workgroups per CU):
+// needs whole tiles and the fast path's alignment, and ranges of exactly
+// per slabs each.
+bool f16_partials_fit(const Args16& a) {
+  return a.M % 128 == 0 && a.N % 128 == 0 &&
+         hgemm::fits<128, 128, BK>(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc) &&
+         (int64_t)a.sk.splits * a.sk.per == a.K / BK;
+}
+
+hipError_t launch_f16_partials_mfma(const Args16& a, int cus, hipStream_t stream) {
+  if (a.fmt == kFmtBF16)
+    return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, false, kFmtBF16, true>(a, 2 * cus,
+                                                                                     stream);
+  return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, false, kFmtF16, true>(a, 2 * cus, stream);
+}
+
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr) {
   return hgemm::epi_fits(bias, res, ldr);
 }

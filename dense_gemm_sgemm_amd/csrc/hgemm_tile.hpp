@@ -126,8 +126,12 @@ struct TileArgs {
   int64_t tiles;
 };
 
+// SPLIT instances walk (tile, K range) work items -- item i is range
+// i / tiles of tile i % tiles, p.sk.per slabs from slab (i / tiles) * per --
+// and store each item's fp32 partial tile to the split-K workspace instead of
+// writing C.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
-          int FMT>
+          int FMT, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileArgs ta) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
@@ -146,9 +150,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   const int tiles_m = p.M / BM, tiles_n = p.N / BN;
   const int64_t stride = gridDim.x;
   const int ntiles = (int)((ta.tiles - blockIdx.x + stride - 1) / stride);
-  auto tile_origin = [&](int j, int& m0, int& n0) __attribute__((always_inline)) {
+  // Work item j of this workgroup: tile origin (m0, n0), first K slab kb and
+  // split-K range sp (both 0 without SPLIT).
+  auto tile_origin = [&](int j, int& m0, int& n0, int& kb, int& sp) __attribute__((always_inline)) {
+    int64_t item = blockIdx.x + j * stride;
+    sp = 0;
+    if constexpr (SPLIT) {
+      const int64_t tiles = (int64_t)tiles_m * tiles_n;
+      sp = (int)(item / tiles);
+      item -= sp * tiles;
+    }
+    kb = sp * (SPLIT ? p.sk.per : 0);
     int tm, tn;
-    map_tile<GM>(blockIdx.x + j * stride, tiles_m, tiles_n, tm, tn);
+    map_tile<GM>(item, tiles_m, tiles_n, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
   };
@@ -288,6 +302,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
     }
   };
 
+  // Split-K partial tile: acc[i][j] is row m0 + wm + 16 i + r, columns
+  // n0 + wn + 16 j + 4 g .. + 3; one 16-byte store per block into the
+  // workspace (padded to whole tiles, no bounds).
+  auto epilogue_partial = [&](int m0, int n0, int sp) __attribute__((always_inline)) {
+    float* ws = p.sk.ws + sp * p.sk.split_stride;
+#pragma unroll
+    for (int i = 0; i < C::kBlocksM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kBlocksN; ++j)
+        *(f4*)(ws + (int64_t)(m0 + wm + 16 * i + r) * p.sk.ld + n0 + wn + 16 * j + 4 * g) =
+            acc[i][j];
+  };
+
   // Software pipeline over the workgroup's slab stream (ntiles x nk slabs,
   // two k-steps each).  The one barrier per slab sits between the slab's two
   // steps: before it, every wave has landed its copy of the next slab and has
@@ -307,18 +334,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   constexpr int kReads = C::kBlocksM + C::kBlocksN;
   constexpr int kCopies = C::kPerWaveA + C::kPerWaveB;
   static_assert(kReads + kCopies <= kMfma, "interleave pattern");
-  const int nk = p.K / BK;
+  const int nk = SPLIT ? p.sk.per : p.K / BK;   // slabs per work item
   const int total = ntiles * nk;
   // The copy target runs two slabs ahead of the compute: slab tc of the tile
   // `ahead` tiles after the current one (origins o[0..2] are refreshed once
   // per tile, outside the MFMA loop).  Past the end of the stream it stays on
   // the last slab of the last tile.
   int tc = 0, ahead = 0, cur = 0;
-  int om[3], on[3];
+  int om[3], on[3], ok[3], os[3];
   auto refresh_origins = [&](int j) __attribute__((always_inline)) {
     cur = j;
 #pragma unroll
-    for (int d = 0; d < 3; ++d) tile_origin(j + d < ntiles ? j + d : ntiles - 1, om[d], on[d]);
+    for (int d = 0; d < 3; ++d)
+      tile_origin(j + d < ntiles ? j + d : ntiles - 1, om[d], on[d], ok[d], os[d]);
   };
   refresh_origins(0);
   auto advance_copy = [&]() __attribute__((always_inline)) {
@@ -332,7 +360,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
     const int d = ahead < 2 ? ahead : 2;
     const int m0 = d == 0 ? om[0] : d == 1 ? om[1] : om[2];
     const int n0 = d == 0 ? on[0] : d == 1 ? on[1] : on[2];
-    copy_slab(stage, m0, n0, past ? nk - 1 : tc);
+    const int kb = d == 0 ? ok[0] : d == 1 ? ok[1] : ok[2];
+    copy_slab(stage, m0, n0, kb + (past ? nk - 1 : tc));
   };
   auto slab = [&](int gs, auto copy, auto next, auto is_copier) __attribute__((always_inline)) {
     constexpr bool kCp = decltype(is_copier)::value && decltype(copy)::value;
@@ -390,11 +419,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   auto stream = [&](auto cp) __attribute__((always_inline)) {
     int gs = 0;
     for (int j = 0; j < ntiles; ++j) {
-      const int m0 = om[0], n0 = on[0];
+      const int m0 = om[0], n0 = on[0], sp = os[0];
       for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), yes(), cp);
       slab(gs, yes(), no(), cp);
       ++gs;
-      epilogue(m0, n0);
+      if constexpr (SPLIT) {
+        epilogue_partial(m0, n0, sp);
+      } else {
+        (void)sp;
+        epilogue(m0, n0);
+      }
       zero_acc();
       --ahead;
       refresh_origins(j + 1);
@@ -415,17 +449,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
 // PERSISTENT: at most `slots` workgroups (as many as the GPU runs at once),
 // each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
-          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16>
+          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false>
 hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
-  const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN);
+  const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN) * (SPLIT ? a.sk.splits : 1);
   const int64_t max_grid = int64_t(1) << 20;
   int64_t grid = PERSISTENT ? (tiles < slots ? tiles : slots) : (tiles < max_grid ? tiles : max_grid);
   if (grid < 1) grid = 1;
   TileArgs ta{a, tiles};
   void* args[] = {&ta};
   return hipLaunchKernel(
-      (const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT>,
+      (const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT>,
       dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 

@@ -85,10 +85,16 @@ struct SplitPlan {
   int splits = 1, per = 0;
   size_t bytes = 0;
 };
+// The library's choice of a split count: ranges = workgroup budget / tiles
+// (tiles of 128 x 128), capped at K / min_range and 64, rounded down to a
+// power of two if asked; no split below min_splits ranges.
+struct SplitRule {
+  int min_range, max_workgroups, min_splits;
+  bool power_of_two;
+};
 // For an M x N x K product walked in slabs of `slab`: `requested` ranges if
-// positive (at most one per slab), else the library's choice with ranges of
-// at least `min_range` of K.
-SplitPlan splitk_plan(int M, int N, int K, int slab, int min_range, int requested);
+// positive (at most one per slab), else the rule's choice.
+SplitPlan splitk_plan(int M, int N, int K, int slab, const SplitRule& rule, int requested);
 SplitK splitk_args(const SplitPlan& plan, int M, int N, void* workspace);
 
 // Launchers.  Each enqueues its kernel(s) on `stream` and returns the HIP
@@ -106,7 +112,10 @@ hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols
 // Split-K: the partial products (a.sk filled in), then the reduction.
 hipError_t launch_f16_partials(const Args16& a, hipStream_t stream);
 hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);
-hipError_t launch_f16_splitk(const Args16& a, bool epi, hipStream_t stream);
+hipError_t launch_f16_splitk(const Args16& a, bool epi, int cus, hipStream_t stream);
+// The fast partial-product kernel, and when it applies.
+bool f16_partials_fit(const Args16& a);
+hipError_t launch_f16_partials_mfma(const Args16& a, int cus, hipStream_t stream);
 hipError_t launch_f32_splitk(const F32Args& a, hipStream_t stream);
 
 // Shape and alignment conditions of the fast kernels (checked on the host).

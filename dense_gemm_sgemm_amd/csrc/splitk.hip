@@ -5,21 +5,29 @@
 // adds the ranges and writes C.
 //
 //  * the partial kernels are the tiled MFMA kernels (128 x 128 tiles) run
-//    over a slab range; they store whole tiles into a workspace padded to
+//    over a slab range -- the 16-bit full-tile kernel where the shape,
+//    alignment and an exact division of K into the ranges allow it, the edge
+//    kernels otherwise; they store whole tiles into a workspace padded to
 //    whole tiles, [splits][Mp][Np] fp32 with Mp, Np rounded up to 128, so
 //    their stores need no bounds;
-//  * the reduction kernel gives each thread four consecutive outputs of one
-//    row and adds the ranges in order 0, 1, ..., splits - 1, so the result
-//    does not depend on timing; it then applies the call's write-back (fp32:
+//  * the reduction kernel gives each group of G threads four consecutive
+//    outputs of one row; thread g of a group adds a contiguous block of
+//    ranges in order, and the G block sums are added in block order, so the
+//    result does not depend on timing (G = 1 to 8, about eight ranges per
+//    thread); it then applies the call's write-back (fp32:
 //    alpha * sum + beta * C, C not read when beta == 0; fp16 and bf16:
 //    rounding to the storage format, or the fused bias / activation /
 //    residual);
 //  * the split count (measured on MI355X over 1 to 144 tiles of 128 x 128
-//    and K from 2048 to 16384): as many ranges as keep tiles x splits within
-//    one wave of two workgroups per CU, at most 64, each range at least 256
-//    (fp16) or 64 (fp32) deep in K; no split below three ranges or for K
-//    under 2048.  A second wave of workgroups, or ranges shallower than
-//    that, cost more than the partial sums' traffic saves.
+//    and K from 2048 to 16384) follows a SplitRule: as many ranges as keep
+//    tiles x splits within a workgroup budget, at most 64, each range at
+//    least a minimum depth of K, never for K under 2048.  16-bit: budget
+//    400, ranges of at least 256, a power of two (so that the ranges divide
+//    K exactly and the full-tile kernel computes the partials), at least
+//    two.  fp32: budget 512 (one wave of two workgroups per CU), ranges of
+//    at least 64, at least three.  Beyond the budget a second wave of
+//    workgroups, and below the depth the partial sums' traffic and the
+//    workgroups' startup, cost more than the split gains.
 #include "internal.h"
 
 namespace mi355gemm {
@@ -27,10 +35,7 @@ namespace {
 
 constexpr int kTile = 128;
 constexpr int kThreads = 256;
-// Workgroup slots of an MI355X: 256 CUs, two partial-product workgroups each.
-constexpr int kSlots = 2 * 256;
 constexpr int kMaxSplits = 64;
-constexpr int kMinSplits = 3;
 constexpr int kMinSplitK = 2048;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -45,37 +50,66 @@ struct Quad {
   f4 acc;
 };
 
-__device__ __forceinline__ bool gather(const SplitK& sk, int M, int N, int64_t base, Quad& q) {
-  const int64_t idx = (base + blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t qn = (N + 3) / 4;
-  q.m = idx / qn;
-  if (q.m >= M) return false;
-  q.n = (int)(idx - q.m * qn) * 4;
-  const float* src = sk.ws + q.m * sk.ld + q.n;
-  q.acc = *(const f4*)src;
-  // Eight ranges' loads in flight at a time, added in range order.
-  int s = 1;
-  for (; s + 8 <= sk.splits; s += 8) {
+// Ranges s0 .. s1 - 1 (s0 < s1) of the partial sums at src, added in order
+// with eight ranges' loads in flight at a time.
+__device__ __forceinline__ f4 sum_ranges(const float* src, int64_t stride, int s0, int s1) {
+  f4 acc = *(const f4*)(src + s0 * stride);
+  int s = s0 + 1;
+  for (; s + 8 <= s1; s += 8) {
     f4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = *(const f4*)(src + (s + u) * sk.split_stride);
+    for (int u = 0; u < 8; ++u) v[u] = *(const f4*)(src + (s + u) * stride);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q.acc[e] += v[u][e];
+      for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
   }
-  for (; s < sk.splits; ++s) {
-    const f4 v = *(const f4*)(src + s * sk.split_stride);
+  for (; s < s1; ++s) {
+    const f4 v = *(const f4*)(src + s * stride);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) q.acc[e] += v[e];
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
   }
-  return true;
+  return acc;
 }
 
-template <bool EPI, int FMT>
+// G threads share one quad: thread group g adds ranges [S g / G, S (g+1) / G)
+// in order, and the G group sums are added in group order through LDS, so
+// the result is the same from run to run.  G > 1 keeps many loads in flight
+// when there are few outputs and many ranges.  Returns false for threads
+// that write nothing (past the matrix, or not in group 0).
+template <int G>
+__device__ __forceinline__ bool gather(const SplitK& sk, int M, int N, int64_t base, Quad& q) {
+  constexpr int kQuads = kThreads / G;   // quads per workgroup
+  const int t = threadIdx.x, g = t / kQuads, ql = t % kQuads;
+  const int64_t idx = (base + blockIdx.x) * kQuads + ql;
+  const int64_t qn = (N + 3) / 4;
+  q.m = idx / qn;
+  const bool in = q.m < M;
+  q.n = (int)(idx - q.m * qn) * 4;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int s0 = (int)((int64_t)sk.splits * g / G), s1 = (int)((int64_t)sk.splits * (g + 1) / G);
+  if (in && s0 < s1) acc = sum_ranges(sk.ws + q.m * sk.ld + q.n, sk.split_stride, s0, s1);
+  if constexpr (G == 1) {
+    q.acc = acc;
+    return in;
+  } else {
+    __shared__ f4 red[G][kQuads];
+    red[g][ql] = acc;
+    __syncthreads();
+    if (g != 0 || !in) return false;
+    q.acc = red[0][ql];
+#pragma unroll
+    for (int h = 1; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q.acc[e] += red[h][ql][e];
+    return true;
+  }
+}
+
+template <bool EPI, int FMT, int G>
 __global__ __launch_bounds__(kThreads) void reduce_f16_kernel(Args16 p, int64_t base) {
   Quad q;
-  if (!gather(p.sk, p.M, p.N, base, q)) return;
+  if (!gather<G>(p.sk, p.M, p.N, base, q)) return;
   h4 o;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -98,9 +132,10 @@ __global__ __launch_bounds__(kThreads) void reduce_f16_kernel(Args16 p, int64_t 
   }
 }
 
+template <int G>
 __global__ __launch_bounds__(kThreads) void reduce_f32_kernel(F32Args p, int64_t base) {
   Quad q;
-  if (!gather(p.sk, p.M, p.N, base, q)) return;
+  if (!gather<G>(p.sk, p.M, p.N, base, q)) return;
   float* dst = p.C + q.m * p.ldc + q.n;
   f4 c = {0.f, 0.f, 0.f, 0.f};
   const bool whole = q.n + 4 <= p.N;
@@ -128,13 +163,27 @@ __global__ __launch_bounds__(kThreads) void reduce_f32_kernel(F32Args p, int64_t
   }
 }
 
-int64_t reduce_blocks(int M, int N) {
-  return ((int64_t)M * ((N + 3) / 4) + kThreads - 1) / kThreads;
+// Threads per quad: about eight ranges per thread (one round of loads).
+int reduce_groups(int splits) { return splits >= 64 ? 8 : splits >= 32 ? 4 : splits >= 16 ? 2 : 1; }
+
+int64_t reduce_blocks(int M, int N, int groups) {
+  const int64_t quads_per_block = kThreads / groups;
+  return ((int64_t)M * ((N + 3) / 4) + quads_per_block - 1) / quads_per_block;
+}
+
+template <bool EPI, int FMT>
+const void* reduce16(int groups) {
+  switch (groups) {
+    case 8: return (const void*)reduce_f16_kernel<EPI, FMT, 8>;
+    case 4: return (const void*)reduce_f16_kernel<EPI, FMT, 4>;
+    case 2: return (const void*)reduce_f16_kernel<EPI, FMT, 2>;
+    default: return (const void*)reduce_f16_kernel<EPI, FMT, 1>;
+  }
 }
 
 }  // namespace
 
-SplitPlan splitk_plan(int M, int N, int K, int slab, int min_range, int requested) {
+SplitPlan splitk_plan(int M, int N, int K, int slab, const SplitRule& rule, int requested) {
   SplitPlan plan;
   const int64_t nk = ((int64_t)K + slab - 1) / slab;
   if (M <= 0 || N <= 0 || K <= 0) return plan;
@@ -144,10 +193,12 @@ SplitPlan splitk_plan(int M, int N, int K, int slab, int min_range, int requeste
   } else {
     const int64_t tiles = (round_tile(M) / kTile) * (round_tile(N) / kTile);
     if (K < kMinSplitK) return plan;
-    s = kSlots / tiles;
-    if (s > K / min_range) s = K / min_range;
+    s = rule.max_workgroups / tiles;
+    if (s > K / rule.min_range) s = K / rule.min_range;
     if (s > kMaxSplits) s = kMaxSplits;
-    if (s < kMinSplits) return plan;
+    if (rule.power_of_two)
+      while (s & (s - 1)) s &= s - 1;   // keep the highest set bit
+    if (s < rule.min_splits) return plan;
   }
   if (s > nk) s = nk;
   if (s < 2) return plan;
@@ -169,22 +220,26 @@ SplitK splitk_args(const SplitPlan& plan, int M, int N, void* workspace) {
   return sk;
 }
 
-hipError_t launch_f16_splitk(const Args16& a, bool epi, hipStream_t stream) {
-  const hipError_t e = launch_f16_partials(a, stream);
+hipError_t launch_f16_splitk(const Args16& a, bool epi, int cus, hipStream_t stream) {
+  const hipError_t e = f16_partials_fit(a) ? launch_f16_partials_mfma(a, cus, stream)
+                                           : launch_f16_partials(a, stream);
   if (e != hipSuccess) return e;
+  const int g = reduce_groups(a.sk.splits);
   const void* k = a.fmt == kFmtBF16
-                      ? (epi ? (const void*)reduce_f16_kernel<true, kFmtBF16>
-                             : (const void*)reduce_f16_kernel<false, kFmtBF16>)
-                      : (epi ? (const void*)reduce_f16_kernel<true, kFmtF16>
-                             : (const void*)reduce_f16_kernel<false, kFmtF16>);
-  return launch_tiles(k, a, reduce_blocks(a.M, a.N), kThreads, 0, stream);
+                      ? (epi ? reduce16<true, kFmtBF16>(g) : reduce16<false, kFmtBF16>(g))
+                      : (epi ? reduce16<true, kFmtF16>(g) : reduce16<false, kFmtF16>(g));
+  return launch_tiles(k, a, reduce_blocks(a.M, a.N, g), kThreads, 0, stream);
 }
 
 hipError_t launch_f32_splitk(const F32Args& a, hipStream_t stream) {
   const hipError_t e = launch_f32_partials(a, stream);
   if (e != hipSuccess) return e;
-  return launch_tiles((const void*)reduce_f32_kernel, a, reduce_blocks(a.M, a.N), kThreads, 0,
-                      stream);
+  const int g = reduce_groups(a.sk.splits);
+  const void* k = g == 8 ? (const void*)reduce_f32_kernel<8>
+                : g == 4 ? (const void*)reduce_f32_kernel<4>
+                : g == 2 ? (const void*)reduce_f32_kernel<2>
+                         : (const void*)reduce_f32_kernel<1>;
+  return launch_tiles(k, a, reduce_blocks(a.M, a.N, g), kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

@@ -3,14 +3,25 @@ restated for the GPU tests)."""
 from __future__ import annotations
 
 
-def splitk_auto(M, N, K, slab):
-    """The library's split-K rule: K of at least 2048 and at least three ranges,
-    with tiles x ranges within 512 workgroups (tiles of 128 x 128) and ranges
-    at least 256 (fp16) or 64 (fp32) deep."""
+def splitk_ranges(M, N, K, slab):
+    """The library's automatic split count (1 = no split).  16-bit: tiles x
+    ranges within 400 workgroups, ranges at least 256 deep, a power of two,
+    at least two.  fp32: within 512 workgroups, at least 64 deep, at least
+    three.  Tiles of 128 x 128, K at least 2048, at most 64 ranges."""
     tiles = -(-M // 128) * -(-N // 128)
     if K < 2048:
-        return False
-    return min(512 // tiles, K // (256 if slab == 64 else 64), 64) >= 3
+        return 1
+    if slab == 64:
+        s = min(400 // tiles, K // 256, 64)
+        while s & (s - 1):
+            s &= s - 1
+        return s if s >= 2 else 1
+    s = min(512 // tiles, K // 64, 64)
+    return s if s >= 3 else 1
+
+
+def splitk_auto(M, N, K, slab):
+    return splitk_ranges(M, N, K, slab) > 1
 
 
 def expected_f32_path(mode, M, N, K):

@@ -172,29 +172,30 @@ def test_path_selection(lib, monkeypatch):
 
 
 def test_split_k_plans(lib, monkeypatch):
-    """Split-K applies to products with K >= 2048 whose 128 x 128 output tiles
-    leave room for at least three ranges in one wave of 512 workgroups (two per
-    CU of a 256-CU part); ranges at least 256 (fp16) or 64 (fp32) deep, at most
-    64 of them, at most one per K slab."""
+    """Split-K applies to products with K >= 2048 and few 128 x 128 output
+    tiles.  16-bit: tiles x ranges within 400 workgroups, ranges at least 256
+    deep, a power of two, at least two.  fp32: within 512 workgroups, at least
+    64 deep, at least three.  At most 64 ranges, at most one per K slab."""
     monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
     assert f16(lib, 512, 512, 16384) == F16_SPLITK and f16(lib, 128, 128, 16384) == F16_SPLITK
     assert f16(lib, 1024, 1024, 4096) == F16_SPLITK and f16(lib, 300, 200, 5000) == F16_SPLITK
     assert f16(lib, 512, 512, 1024) == F16_MFMA                       # K below 2048
     assert f16(lib, 2048, 2048, 8192) == F16_MFMA                     # 256 tiles
-    assert f16(lib, 1536, 1536, 4096) == F16_SPLITK                   # 144 tiles: 3 ranges
-    assert f16(lib, 1792, 1792, 4096) == F16_MFMA                     # 196 tiles: 2 ranges
+    assert f16(lib, 1536, 1536, 4096) == F16_SPLITK                   # 144 tiles: 2 ranges
+    assert f16(lib, 1792, 1792, 4096) == F16_SPLITK                   # 196 tiles: 2 ranges
+    assert f16(lib, 2304, 2304, 4096) == F16_MFMA                     # 324 tiles: 1 range
     assert f16(lib, 8, 512, 16384) == F16_GEMV                        # the vector kernel first
     assert f32(lib, 512, 512, 16384) == F32_SPLITK and f32(lib, 100, 70, 3000) == F32_SPLITK
     assert f32(lib, 4096, 4096, 4096) == F32_MFMA and f32(lib, 512, 512, 16384, alpha=0.0) == 1
     ws16, ws32 = lib.gemm_f16_nt_splitk_workspace, lib.gemm_f32_splitk_workspace
-    # 16 tiles -> 32 ranges of 8 slabs of 64
-    assert ws16(512, 512, 16384, 0) == 32 * 512 * 512 * 4
+    # 16 tiles -> 16 ranges of 16 slabs of 64
+    assert ws16(512, 512, 16384, 0) == 16 * 512 * 512 * 4
     assert ws16(1, 4096, 4096, 0) == 0 and ws16(512, 512, 1024, 0) == 0
     assert ws16(100, 100, 1000, 3) == 3 * 128 * 128 * 4                # 16 slabs -> 6, 6, 4
     assert ws16(100, 100, 1000, 5) == 4 * 128 * 128 * 4                # 16 slabs -> 4 x 4
     assert ws16(64, 64, 100, 50) == 2 * 128 * 128 * 4                  # one range per slab
     assert ws16(64, 64, 100, 1) == 0 and ws16(0, 64, 100, 4) == 0 and ws16(64, 64, -1, 4) == 0
-    assert ws16(300, 200, 5000, 0) == 16 * 384 * 256 * 4               # 19 asked: 79 slabs / 5
+    assert ws16(300, 200, 5000, 0) == 16 * 384 * 256 * 4               # 5000 // 256 -> 16
     assert ws16(128, 128, 65536, 0) == 64 * 128 * 128 * 4              # at most 64 ranges
     assert ws32(512, 512, 16384, 0) == 32 * 512 * 512 * 4
     assert ws32(300, 257, 4099, 0) == 52 * 384 * 384 * 4               # 257 slabs / 56 -> 5 each

@@ -66,95 +66,115 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
   return GEMM_PATH_F32_GENERAL;
 }
 
-int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb, const void* C,
-               int ldc) {
-  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
-  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
-  if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1))
-    return GEMM_ERR_BAD_LD;
-  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (K == 0) return GEMM_PATH_F16_ZERO;
-  if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (force_general()) return GEMM_PATH_F16_GENERAL;
-  if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
-  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
-  if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F16_MFMA;
-  return GEMM_PATH_F16_GENERAL;
-}
-
-// The fused call: the same checks plus its own arguments.  K == 0 runs the
-// edge kernel, whose product is then zero, so that C = act(bias) + residual.
-int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
-                  const void* bias, int act, const void* res, int ldr, const void* C, int ldc) {
-  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
-  if (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_SILU)
-    return GEMM_ERR_BAD_ARG;
-  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
-  if (lda < (K > 1 ? K : 1) || ldb < (K > 1 ? K : 1) || ldc < (N > 1 ? N : 1))
-    return GEMM_ERR_BAD_LD;
-  if (res != nullptr && ldr < (N > 1 ? N : 1)) return GEMM_ERR_BAD_LD;
-  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
-  if (K == 0 || force_general()) return GEMM_PATH_F16_GENERAL;
-  if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
-  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
-  if (f16_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) && f16_epi_fits(bias, res, ldr))
-    return GEMM_PATH_F16_MFMA;
-  return GEMM_PATH_F16_GENERAL;
-}
-
-// gemm_ex: the operands the A * B^T kernels read.  An operand that is not
-// K-contiguous (A for OP_T, B for OP_N) is read from a transposed copy with
-// rows padded to a multiple of 8 elements at a 256-byte aligned address.
-struct ExLayout {
-  bool copy_a, copy_b;
-  int64_t lda, ldb;   // leading dimensions the kernels see
+// The 16-bit calls share one selection.  Plan16 records the kernel path and
+// which operands the kernels read from a workspace copy instead of in place:
+// an operand that is not K-contiguous (gemm_ex's A for OP_T, B for OP_N) is
+// copied transposed; on the padded path an operand whose rows are not whole
+// tiles, not 16-byte aligned or whose K is not a multiple of the slab is
+// copied into zero-padded rows of round64(K) elements, 128-row multiples.
+struct Plan16 {
+  int path = GEMM_PATH_NOOP;
+  bool copy_a = false, copy_b = false;
+  int Mp = 0, Np = 0, Kp = 0;   // the extent the kernels see
+  int64_t lda = 0, ldb = 0;     // leading dimensions the kernels see
 };
 
-int64_t padded_row(int K) { return ((int64_t)(K > 1 ? K : 1) + 7) / 8 * 8; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-ExLayout ex_layout(int op_a, int op_b, int K, int lda, int ldb) {
-  ExLayout l;
-  l.copy_a = op_a == GEMM_OP_T && K > 0;
-  l.copy_b = op_b == GEMM_OP_N && K > 0;
-  l.lda = l.copy_a ? padded_row(K) : lda;
-  l.ldb = l.copy_b ? padded_row(K) : ldb;
-  return l;
+// Stands for the address of a workspace copy in the path choice.
+const void* const kCopyAddress = reinterpret_cast<const void*>(uintptr_t(256));
+
+// Large enough that copying A and B into padded rows and running the
+// full-tile kernel beats the edge kernel (at least 2^30 multiply-adds; the
+// copies then cost about a fifth of the product on MI355X).
+bool padding_pays(int M, int N, int K) { return (int64_t)M * N * K >= (int64_t(1) << 30); }
+
+// The validated plan of a 16-bit call, or a negative GEMM_ERR_* code in
+// plan.path.  K == 0 gives C = act(bias) + residual: zero when there is no
+// write-back, else the edge kernel with an empty product.
+Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, int lda,
+              const void* B, int ldb, const void* bias, int act, const void* res, int ldr,
+              const void* C, int ldc) {
+  Plan16 pl;
+  auto fail = [&](int code) {
+    pl.path = code;
+    return pl;
+  };
+  if (M < 0 || N < 0 || K < 0) return fail(GEMM_ERR_NEGATIVE_DIM);
+  if ((type != GEMM_TYPE_F16 && type != GEMM_TYPE_BF16) ||
+      (op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T) ||
+      (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_SILU))
+    return fail(GEMM_ERR_BAD_ARG);
+  if (M == 0 || N == 0) return fail(GEMM_PATH_NOOP);
+  const int need_a = op_a == GEMM_OP_N ? K : M, need_b = op_b == GEMM_OP_N ? N : K;
+  if (lda < (need_a > 1 ? need_a : 1) || ldb < (need_b > 1 ? need_b : 1) ||
+      ldc < (N > 1 ? N : 1))
+    return fail(GEMM_ERR_BAD_LD);
+  if (res != nullptr && ldr < (N > 1 ? N : 1)) return fail(GEMM_ERR_BAD_LD);
+  if (C == nullptr) return fail(GEMM_ERR_NULL_POINTER);
+  if (K > 0 && (A == nullptr || B == nullptr)) return fail(GEMM_ERR_NULL_POINTER);
+  const bool epi = bias != nullptr || res != nullptr || act != GEMM_ACT_NONE;
+  pl.Mp = M;
+  pl.Np = N;
+  pl.Kp = K;
+  pl.lda = lda;
+  pl.ldb = ldb;
+  if (K == 0) return fail(epi ? GEMM_PATH_F16_GENERAL : GEMM_PATH_F16_ZERO);
+  // Transposed copies (gemm_ex layouts other than A * B^T).
+  pl.copy_a = op_a == GEMM_OP_T;
+  pl.copy_b = op_b == GEMM_OP_N;
+  const int64_t row8 = round_up(K, 8);
+  if (pl.copy_a) pl.lda = row8;
+  if (pl.copy_b) pl.ldb = row8;
+  const void* a_read = pl.copy_a ? kCopyAddress : A;
+  const void* b_read = pl.copy_b ? kCopyAddress : B;
+  if (force_general()) return fail(GEMM_PATH_F16_GENERAL);
+  if (f16_gemv_fits(M, N)) return fail(GEMM_PATH_F16_GEMV);
+  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return fail(GEMM_PATH_F16_SPLITK);
+  if (f16_mfma_fits(M, N, K, a_read, pl.lda, b_read, pl.ldb, C, ldc) &&
+      (!epi || f16_epi_fits(bias, res, ldr)))
+    return fail(GEMM_PATH_F16_MFMA);
+  // The masked full-tile kernel: copy what the tiles cannot read in place.
+  const bool k_ok = K % kF16Slab == 0;
+  const bool a_ok = !pl.copy_a && k_ok && M % 128 == 0 && f16_operand_fits(A, lda);
+  const bool b_ok = !pl.copy_b && k_ok && N % 128 == 0 && f16_operand_fits(B, ldb);
+  if ((!a_ok || !b_ok) && !padding_pays(M, N, K)) return fail(GEMM_PATH_F16_GENERAL);
+  pl.copy_a = !a_ok;
+  pl.copy_b = !b_ok;
+  pl.Kp = (int)round_up(K, kF16Slab);
+  pl.Mp = pl.copy_a ? (int)round_up(M, 128) : M;
+  pl.Np = pl.copy_b ? (int)round_up(N, 128) : N;
+  if (pl.copy_a) pl.lda = pl.Kp;
+  if (pl.copy_b) pl.ldb = pl.Kp;
+  return fail(GEMM_PATH_F16_PADDED);
 }
 
-// Stands for the address of a transposed copy in the path choice.
-const void* const kCopyAddress = reinterpret_cast<const void*>(uintptr_t(256));
+int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb, const void* C,
+               int ldc) {
+  return plan16(GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T, M, N, K, A, lda, B, ldb, nullptr,
+                GEMM_ACT_NONE, nullptr, 0, C, ldc)
+      .path;
+}
+
+int f16_ex_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
+                  const void* bias, int act, const void* res, int ldr, const void* C, int ldc) {
+  return plan16(GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T, M, N, K, A, lda, B, ldb, bias, act, res, ldr,
+                C, ldc)
+      .path;
+}
 
 int ex_select(int type, int op_a, int op_b, int M, int N, int K, const void* A, int lda,
               const void* B, int ldb, const void* bias, int act, const void* res, int ldr,
               const void* C, int ldc) {
-  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
-  if ((type != GEMM_TYPE_F16 && type != GEMM_TYPE_BF16) ||
-      (op_a != GEMM_OP_N && op_a != GEMM_OP_T) || (op_b != GEMM_OP_N && op_b != GEMM_OP_T) ||
-      (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_SILU))
-    return GEMM_ERR_BAD_ARG;
-  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
-  const int need_a = op_a == GEMM_OP_N ? K : M, need_b = op_b == GEMM_OP_N ? N : K;
-  if (lda < (need_a > 1 ? need_a : 1) || ldb < (need_b > 1 ? need_b : 1) ||
-      ldc < (N > 1 ? N : 1))
-    return GEMM_ERR_BAD_LD;
-  if (res != nullptr && ldr < (N > 1 ? N : 1)) return GEMM_ERR_BAD_LD;
-  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (K > 0 && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL_POINTER;
-  const bool epi = bias != nullptr || res != nullptr || act != GEMM_ACT_NONE;
-  if (K == 0) return epi ? GEMM_PATH_F16_GENERAL : GEMM_PATH_F16_ZERO;
-  if (force_general()) return GEMM_PATH_F16_GENERAL;
-  if (f16_gemv_fits(M, N)) return GEMM_PATH_F16_GEMV;
-  if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return GEMM_PATH_F16_SPLITK;
-  const ExLayout l = ex_layout(op_a, op_b, K, lda, ldb);
-  if (f16_mfma_fits(M, N, K, l.copy_a ? kCopyAddress : A, l.lda, l.copy_b ? kCopyAddress : B,
-                    l.ldb, C, ldc) &&
-      (!epi || f16_epi_fits(bias, res, ldr)))
-    return GEMM_PATH_F16_MFMA;
-  return GEMM_PATH_F16_GENERAL;
+  return plan16(type, op_a, op_b, M, N, K, A, lda, B, ldb, bias, act, res, ldr, C, ldc).path;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH; }
+
+// As to_status, with a workspace that could not be allocated reported as such.
+int run_status(hipError_t e) {
+  return e == hipErrorOutOfMemory ? GEMM_ERR_WORKSPACE : to_status(e);
+}
 
 // The tiled kernel of a product that takes neither split-K nor the
 // matrix-vector kernel.
@@ -243,15 +263,72 @@ hipError_t f32_auto_split(F32Args a, int cus, hipStream_t s) {
   return e != hipSuccess ? e : f;
 }
 
-hipError_t f16_auto_split(Args16 a, bool epi, int cus, hipStream_t s) {
-  const SplitPlan plan = splitk_plan(a.M, a.N, a.K, kF16Slab, kF16Rule, 0);
-  std::unique_lock<std::mutex> lock(g_ws_mutex);
+// Runs a validated 16-bit plan: the operand copies (transposed and/or
+// padded) into the workspace, then the kernels of the plan's path.  a holds
+// the caller's operands and output; op_a / op_b say how A and B are stored.
+hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int cus, hipStream_t s) {
+  if (pl.path == GEMM_PATH_F16_ZERO) return launch_f16_zero(a, s);
+  auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bytes_a = pl.copy_a ? round256((size_t)pl.Mp * pl.lda * 2) : 0;
+  const size_t bytes_b = pl.copy_b ? round256((size_t)pl.Np * pl.ldb * 2) : 0;
+  const SplitPlan split = pl.path == GEMM_PATH_F16_SPLITK
+                              ? splitk_plan(a.M, a.N, a.K, kF16Slab, kF16Rule, 0)
+                              : SplitPlan{};
+  const size_t total = bytes_a + bytes_b + (split.splits > 1 ? split.bytes : 0);
+  std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
   bool owned = false;
-  void* ws = stream_workspace(s, plan.bytes, &owned);
-  if (owned || ws == nullptr) lock.unlock();
-  if (ws == nullptr) return f16_tiled(a, epi, cus, s);
-  a.sk = splitk_args(plan, a.M, a.N, ws);
-  const hipError_t e = launch_f16_splitk(a, epi, cus, s);
+  char* ws = nullptr;
+  if (total > 0) {
+    lock.lock();
+    ws = static_cast<char*>(stream_workspace(s, total, &owned));
+    if (owned) lock.unlock();
+    if (ws == nullptr) {
+      // Without a workspace: the plain split-K product runs unsplit; the
+      // copies cannot be done.
+      if (!pl.copy_a && !pl.copy_b) return f16_tiled(a, epi, cus, s);
+      return hipErrorOutOfMemory;
+    }
+  }
+  hipError_t e = hipSuccess;
+  const bool padded = pl.path == GEMM_PATH_F16_PADDED;
+  // Transposed copies: A is [K][lda] (its transpose is op(A), M x K), B is
+  // [K][ldb] (its transpose is B^T stored N x K).  Plain padding copies of
+  // both operands share one launch.
+  half_t* dst_a = reinterpret_cast<half_t*>(ws);
+  half_t* dst_b = reinterpret_cast<half_t*>(ws + bytes_a);
+  const PadCopy pad_a{a.A, dst_a, a.lda, pl.lda, a.M, a.K, pl.Mp, pl.Kp};
+  const PadCopy pad_b{a.B, dst_b, a.ldb, pl.ldb, a.N, a.K, pl.Np, pl.Kp};
+  const bool plain_a = pl.copy_a && op_a == GEMM_OP_N, plain_b = pl.copy_b && op_b == GEMM_OP_T;
+  if (pl.copy_a && !plain_a)
+    e = launch_transpose16(a.A, a.lda, a.K, a.M, dst_a, pl.lda, s, pl.Kp, pl.Mp);
+  if (e == hipSuccess && pl.copy_b && !plain_b)
+    e = launch_transpose16(a.B, a.ldb, a.K, a.N, dst_b, pl.ldb, s, pl.Kp, pl.Np);
+  if (e == hipSuccess && (plain_a || plain_b))
+    e = plain_a ? launch_pad16(pad_a, plain_b ? &pad_b : nullptr, s) : launch_pad16(pad_b, nullptr, s);
+  if (pl.copy_a) a.A = dst_a;
+  if (pl.copy_b) a.B = dst_b;
+  a.lda = pl.lda;
+  a.ldb = pl.ldb;
+  if (e == hipSuccess) {
+    if (padded) {
+      a.m_out = a.M;
+      a.n_out = a.N;
+      a.M = pl.Mp;
+      a.N = pl.Np;
+      a.K = pl.Kp;
+      e = launch_f16_mfma_masked(a, epi, cus, s);
+    } else {
+      switch (pl.path) {
+        case GEMM_PATH_F16_GEMV: e = launch_f16_gemv(a, epi, s); break;
+        case GEMM_PATH_F16_SPLITK:
+          a.sk = splitk_args(split, a.M, a.N, ws + bytes_a + bytes_b);
+          e = launch_f16_splitk(a, epi, cus, s);
+          break;
+        case GEMM_PATH_F16_MFMA: e = launch_f16_mfma(a, epi, cus, s); break;
+        default: e = launch_f16_edge(a, epi, s); break;
+      }
+    }
+  }
   const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
   return e != hipSuccess ? e : f;
 }
@@ -283,103 +360,52 @@ MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int
 
 MI355GEMM_API int gemm_f16_nt(int M, int N, int K, const void* A, int lda, const void* B, int ldb,
                               void* C, int ldc, void* stream) {
-  const int path = f16_select(M, N, K, A, lda, B, ldb, C, ldc);
-  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const Plan16 pl = plan16(GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T, M, N, K, A, lda, B, ldb, nullptr,
+                           GEMM_ACT_NONE, nullptr, 0, C, ldc);
+  if (pl.path < 0 || pl.path == GEMM_PATH_NOOP) return pl.path < 0 ? pl.path : GEMM_OK;
   const int cus = check_device();
   if (cus < 0) return cus;
   const Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
-                  static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (path) {
-    case GEMM_PATH_F16_ZERO: return to_status(launch_f16_zero(a, s));
-    case GEMM_PATH_F16_MFMA: return to_status(launch_f16_mfma(a, false, cus, s));
-    case GEMM_PATH_F16_GEMV: return to_status(launch_f16_gemv(a, false, s));
-    case GEMM_PATH_F16_SPLITK: return to_status(f16_auto_split(a, false, cus, s));
-    default: return to_status(launch_f16_edge(a, false, s));
-  }
+                 static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
+  return run_status(run16(pl, a, GEMM_OP_N, GEMM_OP_T, false, cus,
+                          static_cast<hipStream_t>(stream)));
 }
 
 MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K, const void* A, int lda, const void* B,
                                  int ldb, const void* bias, int act, const void* residual,
                                  int ldr, void* C, int ldc, void* stream) {
-  const int path = f16_ex_select(M, N, K, A, lda, B, ldb, bias, act, residual, ldr, C, ldc);
-  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const Plan16 pl = plan16(GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T, M, N, K, A, lda, B, ldb, bias, act,
+                           residual, ldr, C, ldc);
+  if (pl.path < 0 || pl.path == GEMM_PATH_NOOP) return pl.path < 0 ? pl.path : GEMM_OK;
   const int cus = check_device();
   if (cus < 0) return cus;
   Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
-            static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
+           static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
   a.bias = static_cast<const half_t*>(bias);
   a.res = static_cast<const half_t*>(residual);
   a.ldr = residual ? ldr : 0;
   a.act = act;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (path == GEMM_PATH_F16_MFMA) return to_status(launch_f16_mfma(a, true, cus, s));
-  if (path == GEMM_PATH_F16_GEMV) return to_status(launch_f16_gemv(a, true, s));
-  if (path == GEMM_PATH_F16_SPLITK) return to_status(f16_auto_split(a, true, cus, s));
-  return to_status(launch_f16_edge(a, true, s));
+  return run_status(run16(pl, a, GEMM_OP_N, GEMM_OP_T, true, cus,
+                          static_cast<hipStream_t>(stream)));
 }
 
 MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K, const void* A,
                           int lda, const void* B, int ldb, const void* bias, int act,
                           const void* residual, int ldr, void* C, int ldc, void* stream) {
-  const int path = ex_select(type, op_a, op_b, M, N, K, A, lda, B, ldb, bias, act, residual, ldr,
-                             C, ldc);
-  if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
+  const Plan16 pl = plan16(type, op_a, op_b, M, N, K, A, lda, B, ldb, bias, act, residual, ldr, C,
+                           ldc);
+  if (pl.path < 0 || pl.path == GEMM_PATH_NOOP) return pl.path < 0 ? pl.path : GEMM_OK;
   const int cus = check_device();
   if (cus < 0) return cus;
   const bool epi = bias != nullptr || residual != nullptr || act != GEMM_ACT_NONE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const ExLayout l = ex_layout(op_a, op_b, K, lda, ldb);
   Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
-           static_cast<half_t*>(C), l.lda, l.ldb, ldc, M, N, K};
+           static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
   a.bias = static_cast<const half_t*>(bias);
   a.res = static_cast<const half_t*>(residual);
   a.ldr = residual ? ldr : 0;
   a.act = act;
   a.fmt = type == GEMM_TYPE_BF16 ? kFmtBF16 : kFmtF16;
-  if (path == GEMM_PATH_F16_ZERO) return to_status(launch_f16_zero(a, s));
-
-  // Workspace: the transposed copies, then the split-K partial sums.
-  auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t bytes_a = l.copy_a ? round256((size_t)M * l.lda * 2) : 0;
-  const size_t bytes_b = l.copy_b ? round256((size_t)N * l.ldb * 2) : 0;
-  const SplitPlan plan = path == GEMM_PATH_F16_SPLITK
-                             ? splitk_plan(M, N, K, kF16Slab, kF16Rule, 0)
-                             : SplitPlan{};
-  const size_t total = bytes_a + bytes_b + (plan.splits > 1 ? plan.bytes : 0);
-  std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
-  bool owned = false;
-  char* ws = nullptr;
-  if (total > 0) {
-    lock.lock();
-    ws = static_cast<char*>(stream_workspace(s, total, &owned));
-    if (owned) lock.unlock();
-    if (ws == nullptr) return GEMM_ERR_WORKSPACE;
-  }
-  hipError_t e = hipSuccess;
-  if (l.copy_a) {   // A is [K][lda]: its transpose is op(A), M x K
-    a.A = reinterpret_cast<const half_t*>(ws);
-    e = launch_transpose16(static_cast<const half_t*>(A), lda, K, M, reinterpret_cast<half_t*>(ws),
-                           l.lda, s);
-  }
-  if (e == hipSuccess && l.copy_b) {   // B is [K][ldb]: its transpose is B^T stored N x K
-    a.B = reinterpret_cast<const half_t*>(ws + bytes_a);
-    e = launch_transpose16(static_cast<const half_t*>(B), ldb, K, N,
-                           reinterpret_cast<half_t*>(ws + bytes_a), l.ldb, s);
-  }
-  if (e == hipSuccess) {
-    switch (path) {
-      case GEMM_PATH_F16_GEMV: e = launch_f16_gemv(a, epi, s); break;
-      case GEMM_PATH_F16_SPLITK:
-        a.sk = splitk_args(plan, M, N, ws + bytes_a + bytes_b);
-        e = launch_f16_splitk(a, epi, cus, s);
-        break;
-      case GEMM_PATH_F16_MFMA: e = launch_f16_mfma(a, epi, cus, s); break;
-      default: e = launch_f16_edge(a, epi, s); break;
-    }
-  }
-  const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
-  return to_status(e != hipSuccess ? e : f);
+  return run_status(run16(pl, a, op_a, op_b, epi, cus, static_cast<hipStream_t>(stream)));
 }
 
 MI355GEMM_API int gemm_f32_splitk(int M, int N, int K, float alpha, const float* A, int lda,
@@ -499,6 +525,7 @@ MI355GEMM_API const char* gemm_path_name(int path) {
     case GEMM_PATH_F16_GEMV: return "f16_gemv";
     case GEMM_PATH_F16_SPLITK: return "f16_splitk";
     case GEMM_PATH_F32_SPLITK: return "f32_splitk";
+    case GEMM_PATH_F16_PADDED: return "f16_padded";
     default: return "?";
   }
 }

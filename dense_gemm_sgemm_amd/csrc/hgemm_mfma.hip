@@ -49,24 +49,40 @@ bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
          hgemm::fits<128, 128, BK>(M, N, K, A, lda, B, ldb, C, ldc);
 }
 
-template <bool EPI, int FMT>
+template <bool EPI, int FMT, bool MASK>
 hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
   switch (choose(a.M, a.N, cus)) {
     case k256x224:
-      return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT>(a, cus, stream);
+      return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, MASK>(a, cus,
+                                                                                      stream);
     case k128x128:
-      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT>(a, 2 * cus, stream);
+      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false, MASK>(a, 2 * cus,
+                                                                                      stream);
     default:
-      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 0, true, EPI, FMT>(a, cus, stream);
+      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, MASK>(a, cus,
+                                                                                      stream);
   }
 }
 
-hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {
+template <bool MASK>
+hipError_t launch_any(const Args16& a, bool epi, int cus, hipStream_t stream) {
   if (a.fmt == kFmtBF16)
-    return epi ? launch_shape<true, kFmtBF16>(a, cus, stream)
-               : launch_shape<false, kFmtBF16>(a, cus, stream);
-  return epi ? launch_shape<true, kFmtF16>(a, cus, stream)
-             : launch_shape<false, kFmtF16>(a, cus, stream);
+    return epi ? launch_shape<true, kFmtBF16, MASK>(a, cus, stream)
+               : launch_shape<false, kFmtBF16, MASK>(a, cus, stream);
+  return epi ? launch_shape<true, kFmtF16, MASK>(a, cus, stream)
+             : launch_shape<false, kFmtF16, MASK>(a, cus, stream);
+}
+
+hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {
+  return launch_any<false>(a, epi, cus, stream);
+}
+
+hipError_t launch_f16_mfma_masked(const Args16& a, bool epi, int cus, hipStream_t stream) {
+  return launch_any<true>(a, epi, cus, stream);
+}
+
+bool f16_operand_fits(const void* X, int64_t ld) {
+  return aligned16(X) && ld % 8 == 0 && ld < (int64_t(1) << 28);
 }
 
 // Split-K partial products on 128 x 128 full tiles (two workgroups per CU):

@@ -129,9 +129,11 @@ struct TileArgs {
 // SPLIT instances walk (tile, K range) work items -- item i is range
 // i / tiles of tile i % tiles, p.sk.per slabs from slab (i / tiles) * per --
 // and store each item's fp32 partial tile to the split-K workspace instead of
-// writing C.
+// writing C.  MASK instances read zero-padded operand copies (whole tiles)
+// and store, and read bias and residual, only inside p.m_out x p.n_out, with
+// C, bias and residual at any alignment.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
-          int FMT, bool SPLIT = false>
+          int FMT, bool SPLIT = false, bool MASK = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileArgs ta) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
@@ -266,9 +268,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
         if constexpr (EPI) {
           // fused write-back: act(acc + bias[n]) + residual[m][n] in fp32
           const int n = n0 + wn + 16 * j + 4 * g;
-          const h4 bq = p.bias ? *(const h4*)(p.bias + n) : h4{};
-          const h4 rq = p.res ? *(const h4*)(p.res + (int64_t)(m0 + wm + 16 * i + r) * p.ldr + n)
-                              : h4{};
+          const int64_t m = m0 + wm + 16 * i + r;
+          h4 bq = {}, rq = {};
+          if constexpr (MASK) {
+            // element reads inside the output only, any alignment
+            if (p.bias) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (n + v < p.n_out) bq[v] = p.bias[n + v];
+            }
+            if (p.res && m < p.m_out) {
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (n + v < p.n_out) rq[v] = p.res[m * p.ldr + n + v];
+            }
+          } else {
+            if (p.bias) bq = *(const h4*)(p.bias + n);
+            if (p.res) rq = *(const h4*)(p.res + m * p.ldr + n);
+          }
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             float x = acc[i][j][v];
@@ -289,7 +306,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
       for (int q = 0; q < kOutRows / 4; ++q) {
         const int R = 4 * q + (lane >> 4);
         const h8 v = *(const h8*)(stage_out + R * C::kOutRowBytes + 16 * (cc ^ R));
-        if (C::WN == 128 || cc < C::WN / 8) {
+        if constexpr (MASK) {
+          const int64_t m = m0 + wm + 16 * i + R;
+          const int n = n0 + wn + 8 * cc;
+          if ((C::WN == 128 || cc < C::WN / 8) && m < p.m_out && n < p.n_out) {
+            half_t* dst = p.C + m * p.ldc + n;
+            if (n + 8 <= p.n_out) {
+              __builtin_memcpy(dst, &v, 16);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (n + e < p.n_out) dst[e] = v[e];
+            }
+          }
+        } else if (C::WN == 128 || cc < C::WN / 8) {
           h8* dst = (h8*)(p.C + (int64_t)(m0 + wm + 16 * i + R) * p.ldc + n0 + wn + 8 * cc);
           if (OPT & 1) {
             __builtin_nontemporal_store(v, dst);   // OPT bit 0: streaming stores of C
@@ -449,7 +479,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
 // PERSISTENT: at most `slots` workgroups (as many as the GPU runs at once),
 // each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
-          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false>
+          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false,
+          bool MASK = false>
 hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN) * (SPLIT ? a.sk.splits : 1);
@@ -459,7 +490,8 @@ hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   TileArgs ta{a, tiles};
   void* args[] = {&ta};
   return hipLaunchKernel(
-      (const void*)hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT>,
+      (const void*)
+          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT, MASK>,
       dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 

@@ -50,6 +50,10 @@ struct Args16 {
   int act = 0;                    // 0 none, 1 ReLU, 2 SiLU
   SplitK sk;                      // split-K partial products (partial kernels only)
   int fmt = kFmtF16;              // storage format of every 16-bit operand
+  // Masked full-tile instances: M x N are whole tiles of zero-padded copies
+  // of A and B, and only rows < m_out, columns < n_out of C (and of the
+  // residual and bias) exist.
+  int m_out = 0, n_out = 0;
 };
 
 // A 16-bit storage word as fp32, and fp32 rounded to a storage word (nearest,
@@ -106,9 +110,23 @@ hipError_t launch_f16_zero(const Args16& a, hipStream_t stream);
 hipError_t launch_f16_edge(const Args16& a, bool epi, hipStream_t stream);
 hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream);
 hipError_t launch_f16_gemv(const Args16& a, bool epi, hipStream_t stream);
-// dst[c * ldd + r] = src[r * lds + c] for a rows x cols matrix of 16-bit words.
+// dst[c * ldd + r] = src[r * lds + c] for a rows x cols matrix of 16-bit words;
+// the destination's rows_p x cols_p extent (source orientation) is written,
+// zero outside the source.
 hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols, half_t* dst,
-                              int64_t ldd, hipStream_t stream);
+                              int64_t ldd, hipStream_t stream, int rows_p = 0, int cols_p = 0);
+// A padding copy: dst[r * ldd + k] = src[r * lds + k] inside rows x cols,
+// zero elsewhere in rows_p x cols_p (cols_p and ldd multiples of 8, dst
+// 16-byte aligned).  launch_pad16 runs one or two of them in one launch.
+struct PadCopy {
+  const half_t* src;
+  half_t* dst;
+  int64_t lds, ldd;
+  int rows, cols, rows_p, cols_p;
+};
+hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
+// The full-tile kernel on zero-padded copies, storing only m_out x n_out.
+hipError_t launch_f16_mfma_masked(const Args16& a, bool epi, int cus, hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.
 hipError_t launch_f16_partials(const Args16& a, hipStream_t stream);
 hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);
@@ -125,6 +143,10 @@ bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr);
 bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc);
+// An operand the full-tile kernel can read in place (rows 16-byte aligned,
+// leading dimension within its 32-bit copy offsets); K must also be a
+// multiple of the slab and the rows whole tiles.
+bool f16_operand_fits(const void* X, int64_t ld);
 // M or N small enough for the matrix-vector kernel.
 bool f16_gemv_fits(int M, int N);
 

@@ -7,8 +7,14 @@
 // dst[c * ldd + r] = src[r * lds + c] for r < rows, c < cols, in 64 x 64 tiles
 // through LDS: each thread reads 16 bytes of a source row (8 consecutive
 // columns) and writes 16 bytes of a destination row (8 consecutive source
-// rows), so both sides of HBM see whole 128-byte row segments.  Elements
-// outside the matrix are neither read nor written.
+// rows), so both sides of HBM see whole 128-byte row segments.  The
+// destination may be padded: every element of its rows_p x cols_p extent
+// (source orientation) is written, zero outside the source matrix, which is
+// never read outside.
+//
+// pad16_kernel copies without transposing: dst[r * ldd + k] = src[r * lds + k]
+// inside rows x cols, zero elsewhere in rows_p x cols_p (cols_p a multiple of
+// 8), 16 bytes per thread.
 #include "internal.h"
 
 namespace mi355gemm {
@@ -24,13 +30,14 @@ struct TransposeArgs {
   const half_t* src;
   half_t* dst;
   int64_t lds, ldd;
-  int rows, cols;
+  int rows, cols;       // the source matrix
+  int rows_p, cols_p;   // the extent written (>= rows, cols)
 };
 
 __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs p, int64_t tile_base) {
   __shared__ half_t tile[kT][kT + kPad];
   const int t = threadIdx.x;
-  const int tiles_c = (p.cols + kT - 1) / kT;
+  const int tiles_c = (p.cols_p + kT - 1) / kT;
   const int64_t idx = tile_base + blockIdx.x;
   const int r0 = (int)(idx / tiles_c) * kT, c0 = (int)(idx % tiles_c) * kT;
 
@@ -59,29 +66,88 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs p, 
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = t / 8 + 32 * i, r = 8 * (t % 8);
-    if (c0 + c >= p.cols || r0 + r >= p.rows) continue;
+    if (c0 + c >= p.cols_p || r0 + r >= p.rows_p) continue;
     h8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = tile[r + e][c];
     half_t* d = p.dst + (int64_t)(c0 + c) * p.ldd + r0 + r;
-    if (r0 + r + 8 <= p.rows) {
+    if (r0 + r + 8 <= p.rows_p) {
       __builtin_memcpy(d, &v, 16);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (r0 + r + e < p.rows) d[e] = v[e];
+        if (r0 + r + e < p.rows_p) d[e] = v[e];
     }
   }
+}
+
+// Two padding copies in one launch: blocks below split_block copy `first`,
+// the others `second`.
+struct PadPair {
+  TransposeArgs first, second;
+  int64_t split_block;
+};
+
+__device__ __forceinline__ void pad16_block(const TransposeArgs& p, int64_t block) {
+  const int chunks = p.cols_p / 8;   // per destination row
+  const int64_t idx = block * kThreads + threadIdx.x;
+  const int64_t r = idx / chunks;
+  if (r >= p.rows_p) return;
+  const int k = (int)(idx - r * chunks) * 8;
+  h8 v = {};
+  if (r < p.rows && k < p.cols) {
+    const half_t* s = p.src + r * p.lds + k;
+    if (k + 8 <= p.cols) {
+      __builtin_memcpy(&v, s, 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e < p.cols) v[e] = s[e];
+    }
+  }
+  __builtin_memcpy(p.dst + r * p.ldd + k, &v, 16);
+}
+
+__global__ __launch_bounds__(kThreads) void pad16_kernel(PadPair p, int64_t block_base) {
+  const int64_t b = block_base + blockIdx.x;
+  if (b < p.split_block)
+    pad16_block(p.first, b);
+  else
+    pad16_block(p.second, b - p.split_block);
+}
+
+int64_t pad_blocks(int rows_p, int cols_p) {
+  return ((int64_t)rows_p * (cols_p / 8) + kThreads - 1) / kThreads;
 }
 
 }  // namespace
 
 hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols, half_t* dst,
-                              int64_t ldd, hipStream_t stream) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
-  const TransposeArgs p{src, dst, lds, ldd, rows, cols};
-  const int64_t tiles = (int64_t)((rows + kT - 1) / kT) * ((cols + kT - 1) / kT);
+                              int64_t ldd, hipStream_t stream, int rows_p, int cols_p) {
+  if (rows_p < rows) rows_p = rows;
+  if (cols_p < cols) cols_p = cols;
+  if (rows_p <= 0 || cols_p <= 0) return hipSuccess;
+  const TransposeArgs p{src, dst, lds, ldd, rows, cols, rows_p, cols_p};
+  const int64_t tiles = (int64_t)((rows_p + kT - 1) / kT) * ((cols_p + kT - 1) / kT);
   return launch_tiles((const void*)transpose16_kernel, p, tiles, kThreads, 0, stream);
+}
+
+hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream) {
+  auto args = [](const PadCopy& c) {
+    return TransposeArgs{c.src, c.dst, c.lds, c.ldd, c.rows, c.cols, c.rows_p, c.cols_p};
+  };
+  PadPair p;
+  p.first = args(first);
+  p.split_block = pad_blocks(first.rows_p, first.cols_p);
+  int64_t blocks = p.split_block;
+  if (second) {
+    p.second = args(*second);
+    blocks += pad_blocks(second->rows_p, second->cols_p);
+  } else {
+    p.second = p.first;
+  }
+  if (blocks <= 0) return hipSuccess;
+  return launch_tiles((const void*)pad16_kernel, p, blocks, kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

@@ -258,7 +258,10 @@ enum {
   GEMM_PATH_F16_GEMV = 7,       /* M <= 8 or N <= 8: matrix-vector kernel that    */
                                 /*   streams the long operand once (any ld/align) */
   GEMM_PATH_F16_SPLITK = 8,     /* few output tiles, long K: K cut into ranges,   */
-  GEMM_PATH_F32_SPLITK = 9      /*   fp32 partials, ordered reduction             */
+  GEMM_PATH_F32_SPLITK = 9,     /*   fp32 partials, ordered reduction             */
+  GEMM_PATH_F16_PADDED = 10     /* large ragged or unaligned: A / B copied into   */
+                                /*   zero-padded aligned rows where needed, full  */
+                                /*   tiles with masked stores                     */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,

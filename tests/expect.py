@@ -43,4 +43,7 @@ def expected_f16_path(mode, M, N, K):
         return "f16_splitk"
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and N % 128 == 0))
-    return "f16_mfma" if fast else "f16_general"
+    if fast:
+        return "f16_mfma"
+    # contiguous operands: copies are needed, which pay from 2^30 multiply-adds
+    return "f16_padded" if M * N * K >= 1 << 30 else "f16_general"

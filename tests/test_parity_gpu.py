@@ -651,6 +651,80 @@ def test_workload_hgemm_splitk():
                                                                        res["max_ulps"]))
 
 
+# ------------------------------------------------------ padded path ------
+# Large ragged or unaligned products: A and/or B copied into zero-padded,
+# aligned rows, full tiles with masked stores (and masked bias / residual
+# reads).  Shapes copy A only, B only, both, or nothing (C misaligned only).
+PADDED_SHAPES = [(1000, 1001, 1111), (2048, 1000, 640), (1000, 2048, 640), (1024, 1024, 1025),
+                 (1536, 1000, 777), (1111, 1152, 896)]
+
+
+@pytest.mark.parametrize("shape", PADDED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_padded_shapes(shape, path_mode):
+    M, N, K = shape
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    got = gpu_f16(A, B, expect=expected_f16_path(path_mode, M, N, K))
+    f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+
+
+def test_f16_padded_unaligned_and_c_only():
+    """Operands one element into their buffers with odd leading dimensions;
+    then aligned operands with only C misaligned (no copies).  Nothing outside
+    C's window changes."""
+    for (M, N, K, off_ab) in [(1030, 1100, 1000, 1), (1024, 1024, 1024, 0), (256, 256, 64, 0)]:
+        lda, ldb = (K + 3, K + 1) if off_ab else (K, K)
+        ldc = N + 5
+        A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+        bufA = torch.zeros(M * lda + 8, device=DEV, dtype=torch.float16)
+        bufB = torch.zeros(N * ldb + 8, device=DEV, dtype=torch.float16)
+        bufC = torch.full((M * ldc + 2,), 5.0, device=DEV, dtype=torch.float16)
+        dA = bufA[off_ab:off_ab + M * lda].view(M, lda)[:, :K]
+        dB = bufB[off_ab:off_ab + N * ldb].view(N, ldb)[:, :K]
+        dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+        dA.copy_(dev(A))
+        dB.copy_(dev(B))
+        assert dg.f16_nt_path(dA, dB, dC) == "f16_padded"
+        dg.gemm_f16_nt(dA, dB, dC)
+        torch.cuda.synchronize()
+        f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
+                  oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+        full = bufC.cpu().numpy()
+        mask = np.ones(full.shape, bool)
+        idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+        mask[idx.ravel()] = False
+        assert np.all(full[mask] == 5.0)
+
+
+@pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)
+def test_f16_padded_fused(act, use_bias, use_res):
+    """The fused write-back on the padded path: a ragged shape (copies), then
+    an aligned shape with the bias one element into its buffer and the
+    residual rows of odd length (no copies), in place."""
+    M, N, K = 1000, 1001, 1111
+    A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
+    dA, dB = dev(A), dev(B)
+    dbias = dev(bias) if bias is not None else None
+    dres = dev(res) if res is not None else None
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == "f16_padded"
+    dg.gemm_f16_nt_ex(dA, dB, dC, dbias, act, dres)
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, act, res)
+    if not use_bias:
+        return
+    M, N, K = 1024, 1024, 1024
+    A, B, bias, res = epi_operands(M, N, K, True, True)
+    bbuf = torch.zeros(N + 1, device=DEV, dtype=torch.float16)
+    bbuf[1:].copy_(dev(bias))
+    cbuf = torch.zeros(M, N + 1, device=DEV, dtype=torch.float16)
+    cbuf[:, :N].copy_(dev(res))
+    dC = cbuf[:, :N]
+    assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], act, dC) == "f16_padded"
+    dg.gemm_f16_nt_ex(dev(A), dev(B), dC, bbuf[1:], act, dC)
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, act, res)
+
+
 # ------------------------------------------------------ 64-bit offsets -------
 def test_offsets_beyond_4_gib():
     """Leading dimensions large enough that row offsets exceed 2^32 bytes."""
@@ -727,7 +801,7 @@ def test_workload_sgemm_4096(beta):
 
 
 @pytest.mark.parametrize("name,path", [("hgemm_nt_5376x5376x2048", "f16_mfma"),
-                                       ("hgemm_nt_5000x3001x1537", "f16_general"),
+                                       ("hgemm_nt_5000x3001x1537", "f16_padded"),
                                        ("hgemm_nt_2048x2304x768", "f16_mfma")])
 def test_workload_hgemm(name, path):
     w = inputs.WORKLOADS[name]

@@ -191,24 +191,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   const int64_t firstA = (int64_t)cwp * C::kRowsPerCopy * p.lda * 2;
   const int64_t firstB = (int64_t)cwp * C::kRowsPerCopy * p.ldb * 2;
 
-  // Issues this wave's copies of K slab `t` of the tile with origin (m0, n0)
-  // into `stage`.
-  auto copy_slab = [&](int stage, int m0, int n0, int t) __attribute__((always_inline)) {
-    unsigned char* base = lds + stage * C::kStageBytes;
-    const char* srcA = (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
-    const char* srcB = (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
-#pragma unroll
-    for (int i = 0; i < C::kPerWaveA; ++i)
-      if (C::kCopiesA % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesA)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(srcA + i * copy_strideA + offA),
-                                         (lds_void_t*)(base + (i * C::kCopyWaves + cw) * 1024),
+  // This wave's copies of one K slab: the sources of its A and B rows and
+  // the slab's LDS stage, then copy instruction c (A copies first) one at a
+  // time, so that the main loop can place each one between two MFMAs.
+  struct CopyBase {
+    const char* a;
+    const char* b;
+    unsigned char* l;
+  };
+  auto slab_base = [&](int stage, int m0, int n0, int t) __attribute__((always_inline)) {
+    CopyBase cb;
+    cb.l = lds + stage * C::kStageBytes;
+    cb.a = (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
+    cb.b = (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
+    return cb;
+  };
+  auto copy_one = [&](const CopyBase& cb, int c) __attribute__((always_inline)) {
+    if (c < C::kPerWaveA) {
+      if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(cb.a + c * copy_strideA + offA),
+                                         (lds_void_t*)(cb.l + (c * C::kCopyWaves + cw) * 1024),
                                          16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < C::kPerWaveB; ++i)
+    } else {
+      const int i = c - C::kPerWaveA;
       if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB)
         __builtin_amdgcn_global_load_lds(
-            (gbl_void_t*)(srcB + i * copy_strideB + offB),
-            (lds_void_t*)(base + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024), 16, 0, 0);
+            (gbl_void_t*)(cb.b + i * copy_strideB + offB),
+            (lds_void_t*)(cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024), 16, 0, 0);
+    }
   };
   // All of this wave's copies have landed in LDS, and all of its LDS reads
   // have returned; then every wave of the workgroup meets.  The waits use the
@@ -250,6 +260,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
       for (int j = 0; j < C::kBlocksN; ++j)
         acc[i][j] = mfma16<FMT>(fb[set][j], fa[set][i], acc[i][j]);
   };
+  // Fragment q of a k-step (the A blocks, then the B blocks), and MFMA q of a
+  // k-step (row block q / kBlocksN, column block q % kBlocksN).
+  auto read_one = [&](int set, int stage, int step, int q) __attribute__((always_inline)) {
+    const h8* st = (const h8*)(lds + stage * C::kStageBytes);
+    const int pc = (4 * step + g) ^ fr;
+    if (q < C::kBlocksM)
+      fa[set][q] = st[a_off + 16 * kChunks * q + pc];
+    else
+      fb[set][q - C::kBlocksM] = st[b_off + 16 * kChunks * (q - C::kBlocksM) + pc];
+  };
+  auto mfma_one = [&](int set, int q) __attribute__((always_inline)) {
+    const int i = q / C::kBlocksN, j = q % C::kBlocksN;
+    acc[i][j] = mfma16<FMT>(fb[set][j], fa[set][i], acc[i][j]);
+  };
 
   // Epilogue of the tile with origin (m0, n0): acc[i][j][v] is
   // C[m0 + wm + 16 i + r][n0 + wn + 16 j + 4 g + v].  Row block i at a time,
@@ -257,43 +281,71 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   // wave's 16-row staging area, chunk c (8 columns) of staging row R in slot
   // c ^ R (conflict-free for the writes and for the row reads), then whole
   // row segments are stored to C with 16 bytes per lane.
+  //
+  // The EPI instances first load the bias and residual quads of the whole
+  // wave tile (an absent operand reads as zeros), so that one memory latency
+  // covers them all, then compute act(acc + bias) + residual in fp32, the
+  // activation chosen once per quad.  The accumulator is never -0 (its sum
+  // starts at +0), so adding a zero for an absent operand changes nothing.
   unsigned char* stage_out = lds + 2 * C::kStageBytes + wave * (kOutRows * C::kOutRowBytes);
   auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
     const int cc = lane & 15;
+    h4 bq[C::kBlocksN], rq[C::kBlocksM][C::kBlocksN];
+    if constexpr (EPI) {
+#pragma unroll
+      for (int j = 0; j < C::kBlocksN; ++j) {
+        const int n = n0 + wn + 16 * j + 4 * g;
+        bq[j] = h4{};
+        if (p.bias) {
+          if constexpr (MASK) {
+            // element reads inside the output only, any alignment
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (n + v < p.n_out) bq[j][v] = p.bias[n + v];
+          } else {
+            bq[j] = *(const h4*)(p.bias + n);
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < C::kBlocksM; ++i) {
+        const int64_t m = m0 + wm + 16 * i + r;
+#pragma unroll
+        for (int j = 0; j < C::kBlocksN; ++j) {
+          const int n = n0 + wn + 16 * j + 4 * g;
+          rq[i][j] = h4{};
+          if (p.res) {
+            if constexpr (MASK) {
+              if (m < p.m_out) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  if (n + v < p.n_out) rq[i][j][v] = p.res[m * p.ldr + n + v];
+              }
+            } else {
+              rq[i][j] = *(const h4*)(p.res + m * p.ldr + n);
+            }
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::kBlocksM; ++i) {
 #pragma unroll
       for (int j = 0; j < C::kBlocksN; ++j) {
         h4 o;
         if constexpr (EPI) {
-          // fused write-back: act(acc + bias[n]) + residual[m][n] in fp32
-          const int n = n0 + wn + 16 * j + 4 * g;
-          const int64_t m = m0 + wm + 16 * i + r;
-          h4 bq = {}, rq = {};
-          if constexpr (MASK) {
-            // element reads inside the output only, any alignment
-            if (p.bias) {
+          f4 x = acc[i][j];
 #pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (n + v < p.n_out) bq[v] = p.bias[n + v];
-            }
-            if (p.res && m < p.m_out) {
+          for (int v = 0; v < 4; ++v) x[v] += word_to_f32<FMT>(bq[j][v]);
+          if (p.act == GEMM_ACT_SILU) {
 #pragma unroll
-              for (int v = 0; v < 4; ++v)
-                if (n + v < p.n_out) rq[v] = p.res[m * p.ldr + n + v];
-            }
-          } else {
-            if (p.bias) bq = *(const h4*)(p.bias + n);
-            if (p.res) rq = *(const h4*)(p.res + m * p.ldr + n);
+            for (int v = 0; v < 4; ++v) x[v] = epi_silu(x[v]);
+          } else if (p.act == GEMM_ACT_RELU) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) x[v] = epi_relu(x[v]);
           }
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float x = acc[i][j][v];
-            if (p.bias) x += word_to_f32<FMT>(bq[v]);
-            x = epi_act(x, p.act);
-            if (p.res) x += word_to_f32<FMT>(rq[v]);
-            o[v] = f32_to_word<FMT>(x);
-          }
+          for (int v = 0; v < 4; ++v) o[v] = f32_to_word<FMT>(x[v] + word_to_f32<FMT>(rq[i][j][v]));
         } else {
 #pragma unroll
           for (int v = 0; v < 4; ++v) o[v] = f32_to_word<FMT>(acc[i][j][v]);
@@ -355,17 +407,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   // previous step's MFMAs and every copy has one slab of MFMAs to land; the
   // next tile's first two slabs land while this tile finishes and stores.
   //
-  // Within each half the copies and LDS reads are interleaved one by one with
-  // the MFMAs (sched_group_barrier), so that the two waves sharing a SIMD's
-  // matrix pipe -- which the barrier keeps in the same phase -- never both
-  // stop issuing MFMAs to issue memory instructions.  sched_barrier(0) fences
-  // keep the phases apart.
+  // The first half interleaves its LDS reads one by one with the MFMAs
+  // (sched_group_barrier).  The second half is written out in issue order --
+  // MFMA q, then copy q and read q while there are any -- with
+  // sched_barrier(0) fences after each group: left to itself the scheduler
+  // bunches the copies (each one holds the copying wave at issue until the
+  // CU's copy path takes it) and the LDS reads, both of which stall the
+  // wave's MFMAs.  Copies go first, since each one has to land before the
+  // next barrier.
   constexpr int kMfma = C::kBlocksM * C::kBlocksN;
   constexpr int kReads = C::kBlocksM + C::kBlocksN;
   constexpr int kCopies = C::kPerWaveA + C::kPerWaveB;
-  static_assert(kReads + kCopies <= kMfma, "interleave pattern");
+  static_assert(kReads <= kMfma && kCopies <= kMfma, "interleave pattern");
   const int nk = SPLIT ? p.sk.per : p.K / BK;   // slabs per work item
-  const int total = ntiles * nk;
   // The copy target runs two slabs ahead of the compute: slab tc of the tile
   // `ahead` tiles after the current one (origins o[0..2] are refreshed once
   // per tile, outside the MFMA loop).  Past the end of the stream it stays on
@@ -385,16 +439,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
       ++ahead;
     }
   };
-  auto copy_next = [&](int stage) __attribute__((always_inline)) {
+  // The copy target's sources and LDS stage.
+  auto next_base = [&](int stage) __attribute__((always_inline)) {
     const bool past = cur + ahead >= ntiles;
     const int d = ahead < 2 ? ahead : 2;
     const int m0 = d == 0 ? om[0] : d == 1 ? om[1] : om[2];
     const int n0 = d == 0 ? on[0] : d == 1 ? on[1] : on[2];
     const int kb = d == 0 ? ok[0] : d == 1 ? ok[1] : ok[2];
-    copy_slab(stage, m0, n0, kb + (past ? nk - 1 : tc));
+    return slab_base(stage, m0, n0, kb + (past ? nk - 1 : tc));
   };
-  auto slab = [&](int gs, auto copy, auto next, auto is_copier) __attribute__((always_inline)) {
-    constexpr bool kCp = decltype(is_copier)::value && decltype(copy)::value;
+  auto copy_next = [&](int stage) __attribute__((always_inline)) {
+    const CopyBase cb = next_base(stage);
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) copy_one(cb, c);
+  };
+  auto slab = [&](int gs, auto next, auto is_copier) __attribute__((always_inline)) {
+    constexpr bool kCp = decltype(is_copier)::value;
+    constexpr bool kNext = decltype(next)::value;
+    CopyBase cb{};
+    if constexpr (kCp) cb = next_base(gs & 1);
     // First half: step 0 of slab gs, with the loads of step 1.
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     load_frags(1, gs & 1, 1);
@@ -410,20 +473,19 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
     __builtin_amdgcn_sched_barrier(0);
     // Second half: step 1 of slab gs, with the copy of slab gs + 2 and the
     // loads of slab gs + 1's step 0.
-    if constexpr (kCp) copy_next(gs & 1);
-    if constexpr (decltype(next)::value) load_frags(0, (gs + 1) & 1, 0);
-    mfma_step(1);
-    constexpr int kR = decltype(next)::value ? kReads : 0;
-    constexpr int kV = kCp ? kCopies : 0;
+    const int rstage = (gs + 1) & 1;
 #pragma unroll
-    for (int q = 0; q < (kR > kV ? kR : kV); ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (q < kV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);   // one copy
-      if (q < kR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    for (int q = 0; q < kMfma; ++q) {
+      mfma_one(1, q);
+      if constexpr (kCp) {
+        if (q < kCopies) copy_one(cb, q);
+      }
+      if constexpr (kNext) {
+        if (q < kReads) read_one(0, rstage, 0, q);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - (kR > kV ? kR : kV), 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(copy)::value) advance_copy();
+    advance_copy();
   };
   typedef std::integral_constant<bool, true> yes;
   typedef std::integral_constant<bool, false> no;
@@ -434,44 +496,41 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   wait_and_sync();
   if (copier) copy_next(1);
   advance_copy();
-  // (jc, tc) now names slab 2 of the stream.
+  // (ahead, tc) now names slab 2 of the stream.
   load_frags(0, 0, 0);
   zero_acc();
 
-  // The stream, once for waves that issue copies and once for waves that do
-  // not (a wave-uniform branch outside the loop keeps each body
-  // straight-line; both execute the same sequence of barriers).  A tile's
-  // last slab loads no fragments: the next tile's first ones are loaded after
-  // the epilogue, which keeps the epilogue's registers free.  Past the end of
-  // the stream the copies repeat the last slab into a stage nothing reads
-  // any more (harmless; drained before the kernel ends), so every slab has
-  // the same shape.
-  auto stream = [&](auto cp) __attribute__((always_inline)) {
-    int gs = 0;
-    for (int j = 0; j < ntiles; ++j) {
-      const int m0 = om[0], n0 = on[0], sp = os[0];
-      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), yes(), cp);
-      slab(gs, yes(), no(), cp);
-      ++gs;
-      if constexpr (SPLIT) {
-        epilogue_partial(m0, n0, sp);
-      } else {
-        (void)sp;
-        epilogue(m0, n0);
-      }
-      zero_acc();
-      --ahead;
-      refresh_origins(j + 1);
-      load_frags(0, gs & 1, 0);
+  // The stream: one loop over the tiles, and inside it the slab loop once
+  // for waves that issue copies and once for waves that do not (a
+  // wave-uniform branch keeps each body straight-line; both execute the same
+  // sequence of barriers) -- the epilogue's code exists once.  A tile's last
+  // slab loads no fragments: the next tile's first ones are loaded after the
+  // epilogue, which keeps the epilogue's registers free.  Past the end of the
+  // stream the copies repeat the last slab into a stage nothing reads any
+  // more (harmless; drained before the kernel ends), so every slab has the
+  // same shape.
+  const bool copies = C::kCopyWaves == C::kWaves || copier;
+  int gs = 0;
+  for (int j = 0; j < ntiles; ++j) {
+    const int m0 = om[0], n0 = on[0], sp = os[0];
+    if (copies) {
+      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), yes());
+      slab(gs, no(), yes());
+    } else {
+      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), no());
+      slab(gs, no(), no());
     }
-  };
-  if (C::kCopyWaves == C::kWaves || copier) {
-    // OPT bit 1: copying waves take issue priority over their SIMD partner.
-    if ((OPT & 2) && C::kCopyWaves != C::kWaves) __builtin_amdgcn_s_setprio(2);
-    stream(yes());
-    if ((OPT & 2) && C::kCopyWaves != C::kWaves) __builtin_amdgcn_s_setprio(0);
-  } else {
-    stream(no());
+    ++gs;
+    if constexpr (SPLIT) {
+      epilogue_partial(m0, n0, sp);
+    } else {
+      (void)sp;
+      epilogue(m0, n0);
+    }
+    zero_acc();
+    --ahead;
+    refresh_origins(j + 1);
+    load_frags(0, gs & 1, 0);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);   // drain the copies past the end of the stream
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mi355gemm.h"
+
 namespace mi355gemm {
 
 typedef _Float16 half_t;
@@ -76,10 +78,16 @@ __device__ __forceinline__ half_t f32_to_word(float x) {
   }
 }
 
-// The fused write-back's activation on an fp32 value.
+// The fused write-back's activations on an fp32 value.  SiLU x / (1 + e^-x)
+// takes the hardware exponential and reciprocal (each within a few fp32 ulps;
+// x = -inf gives NaN, as the quotient does).
+__device__ __forceinline__ float epi_relu(float x) { return x > 0.f ? x : 0.f; }
+__device__ __forceinline__ float epi_silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __expf(-x));
+}
 __device__ __forceinline__ float epi_act(float x, int act) {
-  if (act == 1) return x > 0.f ? x : 0.f;
-  if (act == 2) return x / (1.f + __expf(-x));
+  if (act == GEMM_ACT_RELU) return epi_relu(x);
+  if (act == GEMM_ACT_SILU) return epi_silu(x);
   return x;
 }
 

@@ -59,7 +59,9 @@ hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
       return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false, MASK>(a, 2 * cus,
                                                                                       stream);
     default:
-      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, MASK>(a, cus,
+      // 64 x 128 per wave: 128 accumulator registers leave room for one set
+      // of B fragments only (OPT bit 1)
+      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false, MASK>(a, cus,
                                                                                       stream);
   }
 }

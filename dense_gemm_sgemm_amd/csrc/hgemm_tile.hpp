@@ -44,6 +44,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -125,6 +126,17 @@ struct TileArgs {
   Args16 p;
   int64_t tiles;
 };
+
+// f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()):
+// a loop whose index is a compile-time constant in the body.
+template <typename F, int... Q>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 // SPLIT instances walk (tile, K range) work items -- item i is range
 // i / tiles of tile i % tiles, p.sk.per slabs from slab (i / tiles) * per --
@@ -244,14 +256,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
   };
 
   // Two register sets of operand fragments: set s holds k-step s of a slab.
-  h8 fa[2][C::kBlocksM], fb[2][C::kBlocksN];
+  // OPT bit 1: one set of B fragments (fb[0]), for tiles whose accumulators
+  // and two full sets would not fit the 256 registers of a wave.
+  constexpr bool kOneB = (OPT & 2) != 0;
+  h8 fa[2][C::kBlocksM], fb[kOneB ? 1 : 2][C::kBlocksN];
   auto load_frags = [&](int set, int stage, int s) __attribute__((always_inline)) {
     const h8* st = (const h8*)(lds + stage * C::kStageBytes);
     const int pc = (4 * s + g) ^ fr;
 #pragma unroll
     for (int i = 0; i < C::kBlocksM; ++i) fa[set][i] = st[a_off + 16 * kChunks * i + pc];
 #pragma unroll
-    for (int j = 0; j < C::kBlocksN; ++j) fb[set][j] = st[b_off + 16 * kChunks * j + pc];
+    for (int j = 0; j < C::kBlocksN; ++j) fb[kOneB ? 0 : set][j] = st[b_off + 16 * kChunks * j + pc];
   };
   auto mfma_step = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
@@ -458,6 +473,56 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileAr
     constexpr bool kNext = decltype(next)::value;
     CopyBase cb{};
     if constexpr (kCp) cb = next_base(gs & 1);
+    if constexpr (kOneB) {
+      // One set of B fragments: each k-step runs its MFMAs column block by
+      // column block, and B fragment j is reloaded (for the next step) right
+      // after its column's last MFMA.  The barrier comes after the first
+      // column of step 1, once every read of this slab's stage has been
+      // issued and one column of MFMAs covers the last read's latency; reads
+      // of the next slab's stage follow it.
+      constexpr int MB = C::kBlocksM, NB = C::kBlocksN;
+      constexpr int kB = kMfma + MB;
+      static_assert(kB + kCopies <= 2 * kMfma, "copies after the barrier");
+      const h8* cur_st = (const h8*)(lds + (gs & 1) * C::kStageBytes);
+      const h8* nxt_st = (const h8*)(lds + ((gs + 1) & 1) * C::kStageBytes);
+      const int pc1 = (4 + g) ^ fr, pc0 = g ^ fr;
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<2 * kMfma>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        if constexpr (q == kB) {
+          wait_and_sync();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        constexpr int step = q / kMfma, qq = q % kMfma, j = qq / MB, i = qq % MB;
+        acc[i][j] = mfma16<FMT>(fb[0][j], fa[step][i], acc[i][j]);
+        if constexpr (step == 0) {
+          // step 1 of this slab: A fragment qq, B fragment j after its last use
+          if constexpr (qq < MB) fa[1][qq] = cur_st[a_off + 16 * kChunks * qq + pc1];
+          if constexpr (i == MB - 1) fb[0][j] = cur_st[b_off + 16 * kChunks * j + pc1];
+        }
+        if constexpr (kNext) {
+          // step 0 of the next slab, after the barrier
+          static_for<MB>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i2 = decltype(ic)::value;
+            if constexpr (q == (kB > kMfma + i2 ? kB : kMfma + i2))
+              fa[0][i2] = nxt_st[a_off + 16 * kChunks * i2 + pc0];
+          });
+          static_for<NB>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j2 = decltype(jc)::value;
+            constexpr int last = kMfma + MB * j2 + MB - 1;
+            if constexpr (q == (kB > last ? kB : last))
+              fb[0][j2] = nxt_st[b_off + 16 * kChunks * j2 + pc0];
+          });
+        }
+        if constexpr (kCp) {
+          if constexpr (q >= kB && q - kB < kCopies) copy_one(cb, q - kB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      advance_copy();
+      return;
+    }
     // First half: step 0 of slab gs, with the loads of step 1.
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     load_frags(1, gs & 1, 1);

@@ -8,11 +8,12 @@ namespace {
 // Large tiles: 256 rows of C by 256 or 224 columns, 8 waves in a 4 x 2 grid
 // of which waves 0-3 (one per SIMD) issue the slab copies, one persistent
 // workgroup per CU.  Small tiles: 128 x 128, 4 waves in a 2 x 2 grid that all
-// copy, two persistent workgroups per CU.  K slabs of 64; tiles grouped 8
-// tile-rows at a time per XCD.
+// copy, two persistent workgroups per CU; or 128 x 192, the same 4 waves
+// (64 x 96 each), one workgroup per CU (its two LDS stages take 80 KiB).  K
+// slabs of 64; tiles grouped 8 tile-rows at a time per XCD.
 constexpr int BK = 64, GM = 8;
 
-enum TileShape { kNone, k256x256, k256x224, k128x128 };
+enum TileShape { kNone, k256x256, k256x224, k128x128, k128x192 };
 
 // A launch takes about ceil(tiles / slots) tile-times.  A 256-row tile-time
 // is proportional to its width (one workgroup per CU); a 128 x 128 tile
@@ -22,7 +23,10 @@ enum TileShape { kNone, k256x256, k256x224, k128x128 };
 // Ties go to the larger tile.  5376 x 5376 on 256 CUs: 256 wide -> 441
 // tiles, 2 rounds x 65536; 224 wide -> 504 tiles, 2 rounds x 57344; 128 x 128
 // -> 1764 tiles, 4 rounds x 39321.  2048 x 2304: 256 wide -> 72 tiles, 1 round
-// x 65536; 128 x 128 -> 288 tiles, 1 round x 39321 (measured 1.44x faster).
+// x 65536; 128 x 128 -> 288 tiles, 1 round x 39321 (measured 1.44x faster);
+// 128 x 192 -> 192 tiles, 1 round x 32768 (measured 1.19x faster than
+// 128 x 128).  A 128 x 192 tile runs alone on its CU with 4 waves: a third
+// more time per output than the 256-row tiles (tile-time 128 x 192 x 4/3).
 TileShape choose(int M, int N, int cus) {
   TileShape best = kNone;
   int64_t best_cost = 0;
@@ -38,6 +42,7 @@ TileShape choose(int M, int N, int cus) {
   consider(k256x256, 256, 256, cus, 256 * 256);
   consider(k256x224, 256, 224, cus, 256 * 224);
   consider(k128x128, 128, 128, 2 * cus, 2 * 128 * 128 * 6 / 5);
+  consider(k128x192, 128, 192, cus, 128 * 192 * 4 / 3);
   return best;
 }
 }  // namespace
@@ -46,7 +51,8 @@ bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
                    const void* C, int64_t ldc) {
   return hgemm::fits<256, 256, BK>(M, N, K, A, lda, B, ldb, C, ldc) ||
          hgemm::fits<256, 224, BK>(M, N, K, A, lda, B, ldb, C, ldc) ||
-         hgemm::fits<128, 128, BK>(M, N, K, A, lda, B, ldb, C, ldc);
+         hgemm::fits<128, 128, BK>(M, N, K, A, lda, B, ldb, C, ldc) ||
+         hgemm::fits<128, 192, BK>(M, N, K, A, lda, B, ldb, C, ldc);
 }
 
 template <bool EPI, int FMT, bool MASK>
@@ -57,6 +63,9 @@ hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
                                                                                       stream);
     case k128x128:
       return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false, MASK>(a, 2 * cus,
+                                                                                      stream);
+    case k128x192:
+      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false, MASK>(a, cus,
                                                                                       stream);
     default:
       // 64 x 128 per wave: 128 accumulator registers leave room for one set

@@ -42,7 +42,7 @@ def expected_f16_path(mode, M, N, K):
     if splitk_auto(M, N, K, 64):
         return "f16_splitk"
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
-                            (M % 128 == 0 and N % 128 == 0))
+                            (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
     if fast:
         return "f16_mfma"
     # contiguous operands: copies are needed, which pay from 2^30 multiply-adds

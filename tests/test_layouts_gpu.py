@@ -81,11 +81,11 @@ def run_ex(A, B, op_a, op_b, fmt, M, N, bias=None, act="none", res=None, expect=
     return to_host(dC, fmt)
 
 
-# Shapes reach each kernel: fast tiles 256 x 256, 256 x 224 and 128 x 128, the
+# Shapes reach each kernel: fast tiles 256 x 256, 256 x 224, 128 x 128 and 128 x 192, the
 # edge kernel (ragged, odd K), the matrix-vector kernel both ways, split-K.
-SHAPES = [(256, 256, 64), (512, 448, 128), (128, 128, 192), (133, 70, 45), (257, 255, 65),
-          (1, 300, 777), (300, 3, 1000), (4, 129, 4100), (512, 512, 16384), (300, 200, 5000),
-          (1000, 1001, 1111)]
+SHAPES = [(256, 256, 64), (512, 448, 128), (128, 128, 192), (384, 576, 192), (133, 70, 45),
+          (257, 255, 65), (1, 300, 777), (300, 3, 1000), (4, 129, 4100), (512, 512, 16384),
+          (300, 200, 5000), (1000, 1001, 1111)]
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
@@ -106,7 +106,7 @@ EPI_CASES = [("silu", True, True), ("relu", True, False), ("none", False, True)]
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("layout", [("n", "t"), ("n", "n"), ("t", "n")], ids=lambda l: "".join(l))
-@pytest.mark.parametrize("shape", [(256, 224, 64), (133, 70, 45), (1, 300, 4096),
+@pytest.mark.parametrize("shape", [(256, 224, 64), (256, 384, 128), (133, 70, 45), (1, 300, 4096),
                                    (300, 200, 5000), (1000, 1001, 1111)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)

@@ -127,6 +127,13 @@ struct TileArgs {
   int64_t tiles;
 };
 
+// Waves of the kernel that share each SIMD: 8-wave workgroups put two on
+// each; 4-wave 128 x 128 tiles run two workgroups per CU (the launcher's
+// slot count), so their register budget must leave room for the second.
+constexpr int waves_per_simd(int bm, int bn, int waves) {
+  return waves == 8 ? 2 : (bm * bn <= 128 * 128 ? 2 : 1);
+}
+
 // f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()):
 // a loop whose index is a compile-time constant in the body.
 template <typename F, int... Q>
@@ -146,7 +153,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // C, bias and residual at any alignment.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
           int FMT, bool SPLIT = false, bool MASK = false>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void hgemm_nt_kernel(TileArgs ta) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVES_M * WAVES_N))
+void hgemm_nt_kernel(TileArgs ta) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
   const Args16& p = ta.p;

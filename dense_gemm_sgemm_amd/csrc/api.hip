@@ -75,6 +75,7 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
 struct Plan16 {
   int path = GEMM_PATH_NOOP;
   bool copy_a = false, copy_b = false;
+  bool gemv_kn = false;         // matrix-vector path with the long operand K-major
   int Mp = 0, Np = 0, Kp = 0;   // the extent the kernels see
   int64_t lda = 0, ldb = 0;     // leading dimensions the kernels see
 };
@@ -129,7 +130,18 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
   const void* a_read = pl.copy_a ? kCopyAddress : A;
   const void* b_read = pl.copy_b ? kCopyAddress : B;
   if (force_general()) return fail(GEMM_PATH_F16_GENERAL);
-  if (f16_gemv_fits(M, N)) return fail(GEMM_PATH_F16_GEMV);
+  if (f16_gemv_fits(M, N)) {
+    // A long operand stored K-major is read in place by the K-major kernel,
+    // which also reads the short one in either layout: no copies.
+    const bool wb = f16_gemv_w_is_b(M, N);
+    if (wb ? op_b == GEMM_OP_N : op_a == GEMM_OP_T) {
+      pl.gemv_kn = true;
+      pl.copy_a = pl.copy_b = false;
+      pl.lda = lda;
+      pl.ldb = ldb;
+    }
+    return fail(GEMM_PATH_F16_GEMV);
+  }
   if (splitk_plan(M, N, K, kF16Slab, kF16Rule, 0).splits > 1) return fail(GEMM_PATH_F16_SPLITK);
   if (f16_mfma_fits(M, N, K, a_read, pl.lda, b_read, pl.ldb, C, ldc) &&
       (!epi || f16_epi_fits(bias, res, ldr)))
@@ -273,8 +285,9 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
   const size_t bytes_b = pl.copy_b ? round256((size_t)pl.Np * pl.ldb * 2) : 0;
   const SplitPlan split = pl.path == GEMM_PATH_F16_SPLITK
                               ? splitk_plan(a.M, a.N, a.K, kF16Slab, kF16Rule, 0)
-                              : SplitPlan{};
-  const size_t total = bytes_a + bytes_b + (split.splits > 1 ? split.bytes : 0);
+                          : pl.gemv_kn ? gemv_kn_plan(a.M, a.N, a.K)
+                                       : SplitPlan{};
+  const size_t total = bytes_a + bytes_b + (split.splits > 1 || pl.gemv_kn ? split.bytes : 0);
   std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
   bool owned = false;
   char* ws = nullptr;
@@ -284,8 +297,8 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
     if (owned) lock.unlock();
     if (ws == nullptr) {
       // Without a workspace: the plain split-K product runs unsplit; the
-      // copies cannot be done.
-      if (!pl.copy_a && !pl.copy_b) return f16_tiled(a, epi, cus, s);
+      // copies and the K-major matrix-vector partial sums cannot be done.
+      if (!pl.copy_a && !pl.copy_b && !pl.gemv_kn) return f16_tiled(a, epi, cus, s);
       return hipErrorOutOfMemory;
     }
   }
@@ -319,7 +332,10 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
       e = launch_f16_mfma_masked(a, epi, cus, s);
     } else {
       switch (pl.path) {
-        case GEMM_PATH_F16_GEMV: e = launch_f16_gemv(a, epi, s); break;
+        case GEMM_PATH_F16_GEMV:
+          e = pl.gemv_kn ? launch_f16_gemv_kn(a, op_a, op_b, epi, split, ws + bytes_a + bytes_b, s)
+                         : launch_f16_gemv(a, epi, s);
+          break;
         case GEMM_PATH_F16_SPLITK:
           a.sk = splitk_args(split, a.M, a.N, ws + bytes_a + bytes_b);
           e = launch_f16_splitk(a, epi, cus, s);

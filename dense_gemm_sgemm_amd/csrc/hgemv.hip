@@ -256,9 +256,267 @@ KernelFn pick(int V, int kc, bool& wide) {
   return pick_v<kThreads, 2, EPI, FMT>(V);
 }
 
+
+// ---------------------------------------------------------------------------
+// The long operand stored K-major: W[k][l] with each row (one k) contiguous in
+// l, as B is for op_b = N (l = n) and A for op_a = T (l = m).  Then
+// Y[v][l] = sum_k X[v][k] W[k][l], and a thread's neighbours in a row hold
+// different outputs, so the kernel walks W row by row instead of along K:
+//
+//  * each lane owns 8 consecutive columns; the workgroups are spread over
+//    column blocks and over ranges of `per` rows of K, so that every row of W
+//    is read once and enough loads are in flight to stream it from HBM (see
+//    kn_wg_cols for how the four waves of a workgroup divide the work);
+//  * each 16-byte load brings 8 columns of one row; two rows k, k + 1 are
+//    paired column by column into v_dot2 operands (W[k][l], W[k+1][l]) and
+//    multiplied with (X[v][k], X[v][k+1]), staged in LDS in that packed form
+//    (X may be stored in either layout: it is read with both strides);
+//  * each range writes its fp32 partial sums to a workspace laid out as the
+//    split-K partials, [range][M][round4(N)], and the split-K reduction adds
+//    the ranges in order and applies the write-back.
+struct KnArgs {
+  const half_t* W;
+  const half_t* X;
+  float* ws;
+  int64_t ldw, x_v, x_k;
+  int64_t ws_s, ws_v, ws_l;   // partial (range s, v, l) at ws[s ws_s + v ws_v + l ws_l]
+  int L, K, per, colblocks;
+};
+
+constexpr int kKnCols = 8;                     // columns per thread
+constexpr int kKnMaxPer = 1024;                // rows of K per range (X staging in LDS)
+
+// Columns l .. l + 7 of one row, zero past L.
+__device__ __forceinline__ h8 load_cols(const half_t* row, int64_t l, int L) {
+  h8 v;
+  if (l + kKnCols <= L) {
+    __builtin_memcpy(&v, row + l, 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < kKnCols; ++e) v[e] = l + e < L ? row[l + e] : (half_t)0;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t word_bits(half_t h) {
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// acc + w.lo * x.lo + w.hi * x.hi, both operands two 16-bit words of format FMT.
+template <int FMT>
+__device__ __forceinline__ float dot2w(uint32_t w, uint32_t x, float acc) {
+  if constexpr (FMT == kFmtF16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, x), acc,
+                                  false);
+  else
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bh2, w), __builtin_bit_cast(bh2, x),
+                                           acc, false);
+}
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+// Rows k (w0) and k + 1 (w1) of the thread's 8 columns into the accumulators;
+// xp[v] = (X[v][k], X[v][k+1]).
+template <int V, int FMT>
+__device__ __forceinline__ void kn_pair(h8 w0, h8 w1, const uint32_t* xp, float (&acc)[V][kKnCols]) {
+  const u4 a = __builtin_bit_cast(u4, w0), b = __builtin_bit_cast(u4, w1);
+  uint32_t pr[kKnCols];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[2 * j] = (a[j] & 0xffffu) | (b[j] << 16);            // column 2j: (W[k], W[k+1])
+    pr[2 * j + 1] = (a[j] >> 16) | (b[j] & 0xffff0000u);     // column 2j + 1
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const uint32_t x = xp[v];
+#pragma unroll
+    for (int e = 0; e < kKnCols; ++e) acc[v][e] = dot2w<FMT>(pr[e], x, acc[v][e]);
+  }
+}
+
+// Columns a workgroup of the K-major kernel owns: with one or two vectors its
+// four waves share 512 columns and take every fourth row pair of the range
+// (their sums meet in LDS); with more, each wave owns 512 columns of its own
+// and walks the whole range (an LDS exchange of 8 V sums per lane would cost
+// more than it saves).
+constexpr int kn_wg_cols(int V) { return V <= 2 ? 64 * kKnCols : kThreads * kKnCols; }
+
+// U row pairs (2 U 16-byte loads) in flight per thread; sums of the waves
+// that share columns are added in wave order.
+template <int V, int U, int FMT>
+__global__ __launch_bounds__(kThreads) void hgemv_kn_kernel(KnArgs p, int64_t base) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr bool kShare = V <= 2;            // the waves share their columns
+  constexpr int kStep = kShare ? kWaves : 1;  // row-pair stride of one wave
+  __shared__ uint32_t xs[kKnMaxPer / 2][V];
+  __shared__ float red[kShare ? kWaves - 1 : 1][V][64 * kKnCols];
+  const int64_t b = base + blockIdx.x;
+  const int s = (int)(b / p.colblocks), cb = (int)(b % p.colblocks);
+  const int k0 = s * p.per;
+  const int k1 = p.K < k0 + p.per ? p.K : k0 + p.per;
+  const int rows = k1 - k0;   // at least 1
+  const int pairs = (rows + 1) / 2;
+  for (int i = threadIdx.x; i < pairs * V; i += kThreads) {
+    const int kp = i / V, v = i % V;
+    const int k = k0 + 2 * kp;
+    const half_t* x = p.X + v * p.x_v;
+    const uint32_t lo = word_bits(x[(int64_t)k * p.x_k]);
+    const uint32_t hi = k + 1 < k1 ? word_bits(x[(int64_t)(k + 1) * p.x_k]) : 0u;
+    xs[kp][v] = lo | (hi << 16);
+  }
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t l =
+      (int64_t)cb * kn_wg_cols(V) + (kShare ? lane : (int)threadIdx.x) * (int64_t)kKnCols;
+  // Lanes past L load nothing but still reach the barrier below.
+  const bool active = l < p.L;
+
+  float acc[V][kKnCols];
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int e = 0; e < kKnCols; ++e) acc[v][e] = 0.f;
+  const half_t* w = p.W + (int64_t)k0 * p.ldw;
+  const int full = rows / 2;         // pairs whose two rows are both in the range
+  const int first = kShare ? wave : 0;
+  if (active) {
+    int j = first;
+    for (; j + kStep * (U - 1) < full; j += kStep * U) {
+      h8 w0[U], w1[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kp = j + kStep * u;
+        w0[u] = load_cols(w + (int64_t)(2 * kp) * p.ldw, l, p.L);
+        w1[u] = load_cols(w + (int64_t)(2 * kp + 1) * p.ldw, l, p.L);
+      }
+      // Keeps the scheduler from sinking the loads next to their first use.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) kn_pair<V, FMT>(w0[u], w1[u], xs[j + kStep * u], acc);
+    }
+    for (; j < full; j += kStep)
+      kn_pair<V, FMT>(load_cols(w + (int64_t)(2 * j) * p.ldw, l, p.L),
+                      load_cols(w + (int64_t)(2 * j + 1) * p.ldw, l, p.L), xs[j], acc);
+    if ((rows & 1) && full % kStep == first)   // the range's last row alone
+      kn_pair<V, FMT>(load_cols(w + (int64_t)(2 * full) * p.ldw, l, p.L), h8{}, xs[full], acc);
+  }
+  if constexpr (kShare) {
+    if (wave > 0) {
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < kKnCols; ++e) red[wave - 1][v][lane * kKnCols + e] = acc[v][e];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int q = 0; q < kWaves - 1; ++q)
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+#pragma unroll
+        for (int e = 0; e < kKnCols; ++e) acc[v][e] += red[q][v][lane * kKnCols + e];
+  }
+  if (!active) return;
+  float* dst = p.ws + s * p.ws_s + l * p.ws_l;
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int e = 0; e < kKnCols; ++e)
+      if (l + e < p.L) dst[v * p.ws_v + e * p.ws_l] = acc[v][e];
+}
+
+typedef void (*KnKernelFn)(KnArgs, int64_t);
+
+template <int FMT>
+KnKernelFn pick_kn(int V) {
+  switch (V) {
+    case 1: return hgemv_kn_kernel<1, 8, FMT>;
+    case 2: return hgemv_kn_kernel<2, 8, FMT>;
+    case 3: return hgemv_kn_kernel<3, 8, FMT>;
+    case 4: return hgemv_kn_kernel<4, 8, FMT>;
+    case 5: return hgemv_kn_kernel<5, 4, FMT>;
+    case 6: return hgemv_kn_kernel<6, 4, FMT>;
+    case 7: return hgemv_kn_kernel<7, 4, FMT>;
+    default: return hgemv_kn_kernel<8, 4, FMT>;
+  }
+}
+
+// The small side and the long one: B is W when M is the small side.
+inline bool w_is_b(int M, int N) { return M <= kMaxV && M <= N; }
+
 }  // namespace hgemv
 
 bool f16_gemv_fits(int M, int N) { return M <= hgemv::kMaxV || N <= hgemv::kMaxV; }
+bool f16_gemv_w_is_b(int M, int N) { return hgemv::w_is_b(M, N); }
+
+// Ranges of K for the K-major kernel: about 2048 workgroups in all, at most
+// 256 ranges of at least 16 and at most kKnMaxPer rows (an even number), and
+// partial sums of at most an eighth of W's bytes (S V L 4 <= K L 2 / 8).
+SplitPlan gemv_kn_plan(int M, int N, int K) {
+  using namespace hgemv;
+  SplitPlan plan;
+  const bool wb = w_is_b(M, N);
+  const int L = wb ? N : M, V = wb ? M : N;
+  const int64_t colblocks = ((int64_t)L + kn_wg_cols(V) - 1) / kn_wg_cols(V);
+  int64_t s = 2048 / colblocks;
+  if (s > (int64_t)K / (16 * V)) s = (int64_t)K / (16 * V);
+  if (s < 1) s = 1;
+  if (s > 256) s = 256;
+  int64_t per = ((int64_t)K + s - 1) / s;
+  per = (per + 1) / 2 * 2;
+  if (per < 16) per = 16;
+  if (per > kKnMaxPer) per = kKnMaxPer;
+  plan.splits = (int)(((int64_t)K + per - 1) / per);
+  plan.per = (int)per;
+  plan.bytes = (size_t)plan.splits * M * ((N + 3) / 4 * 4) * 4;
+  return plan;
+}
+
+hipError_t launch_f16_gemv_kn(const Args16& a, int op_a, int op_b, bool epi, const SplitPlan& plan,
+                              void* workspace, hipStream_t stream) {
+  using namespace hgemv;
+  const bool wb = w_is_b(a.M, a.N);
+  const int V = wb ? a.M : a.N;
+  const int64_t ld = (a.N + 3) / 4 * 4;
+  KnArgs k;
+  k.ws = static_cast<float*>(workspace);
+  k.ws_s = (int64_t)a.M * ld;
+  k.K = a.K;
+  k.per = plan.per;
+  if (wb) {
+    // W = B stored [K][ldb] (op_b = N); X = A; partial (v = m, l = n).
+    k.W = a.B;
+    k.ldw = a.ldb;
+    k.X = a.A;
+    k.x_v = op_a == GEMM_OP_N ? a.lda : 1;
+    k.x_k = op_a == GEMM_OP_N ? 1 : a.lda;
+    k.L = a.N;
+    k.ws_v = ld;
+    k.ws_l = 1;
+  } else {
+    // W = A stored [K][lda] (op_a = T); X = B; partial (v = n, l = m).
+    k.W = a.A;
+    k.ldw = a.lda;
+    k.X = a.B;
+    k.x_v = op_b == GEMM_OP_T ? a.ldb : 1;
+    k.x_k = op_b == GEMM_OP_T ? 1 : a.ldb;
+    k.L = a.M;
+    k.ws_v = 1;
+    k.ws_l = ld;
+  }
+  k.colblocks = (k.L + kn_wg_cols(V) - 1) / kn_wg_cols(V);
+  const KnKernelFn fn = a.fmt == kFmtBF16 ? pick_kn<kFmtBF16>(V) : pick_kn<kFmtF16>(V);
+  hipError_t e = launch_tiles(reinterpret_cast<const void*>(fn), k,
+                              (int64_t)k.colblocks * plan.splits, kThreads, 0, stream);
+  if (e != hipSuccess) return e;
+  Args16 r = a;
+  r.sk.ws = k.ws;
+  r.sk.ld = ld;
+  r.sk.split_stride = k.ws_s;
+  r.sk.splits = plan.splits;
+  r.sk.per = plan.per;
+  return launch_f16_reduce(r, epi, stream);
+}
 
 hipError_t launch_f16_gemv(const Args16& a, bool epi, hipStream_t stream) {
   using namespace hgemv;

@@ -118,6 +118,15 @@ hipError_t launch_f16_zero(const Args16& a, hipStream_t stream);
 hipError_t launch_f16_edge(const Args16& a, bool epi, hipStream_t stream);
 hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream);
 hipError_t launch_f16_gemv(const Args16& a, bool epi, hipStream_t stream);
+// The matrix-vector case with the long operand stored K-major (B for
+// op_b = N when M is the small side, A for op_a = T when N is): partial sums
+// over ranges of K into an fp32 workspace, then the split-K reduction with
+// the call's write-back.  gemv_kn_plan gives the ranges and workspace bytes.
+SplitPlan gemv_kn_plan(int M, int N, int K);
+hipError_t launch_f16_gemv_kn(const Args16& a, int op_a, int op_b, bool epi, const SplitPlan& plan,
+                              void* workspace, hipStream_t stream);
+// The split-K reduction alone: a.sk names the partial sums.
+hipError_t launch_f16_reduce(const Args16& a, bool epi, hipStream_t stream);
 // dst[c * ldd + r] = src[r * lds + c] for a rows x cols matrix of 16-bit words;
 // the destination's rows_p x cols_p extent (source orientation) is written,
 // zero outside the source.
@@ -157,6 +166,9 @@ bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
 bool f16_operand_fits(const void* X, int64_t ld);
 // M or N small enough for the matrix-vector kernel.
 bool f16_gemv_fits(int M, int N);
+// Which operand the matrix-vector kernels stream: B when M is the small side
+// (M <= 8 and M <= N), else A.
+bool f16_gemv_w_is_b(int M, int N);
 
 // Launches `kernel(args, tile_base)` over `tiles` workgroups, split into
 // launches of at most 2^20 workgroups so that no grid exceeds the 32-bit

@@ -224,6 +224,10 @@ hipError_t launch_f16_splitk(const Args16& a, bool epi, int cus, hipStream_t str
   const hipError_t e = f16_partials_fit(a) ? launch_f16_partials_mfma(a, cus, stream)
                                            : launch_f16_partials(a, stream);
   if (e != hipSuccess) return e;
+  return launch_f16_reduce(a, epi, stream);
+}
+
+hipError_t launch_f16_reduce(const Args16& a, bool epi, hipStream_t stream) {
   const int g = reduce_groups(a.sk.splits);
   const void* k = a.fmt == kFmtBF16
                       ? (epi ? reduce16<true, kFmtBF16>(g) : reduce16<false, kFmtBF16>(g))

@@ -200,3 +200,19 @@ def test_workload_5376_layouts(fmt, layout):
     r = check16(got[rows, cols], ref, sab, fmt)
     print("[5376^2 x 2048 %s %s] checked %d outputs, max %.2f ulp"
           % (fmt, "".join(layout), r["count"], r["max_ulps"]), flush=True)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,N,K,op_a,op_b", [(1, 16384, 4096, "n", "n"), (2, 6000, 3001, "t", "n"),
+                                             (8, 4096, 2048, "n", "n"), (5000, 1, 4099, "t", "t"),
+                                             (3000, 6, 1024, "t", "n")])
+def test_gemv_kmajor_weight(fmt, M, N, K, op_a, op_b):
+    """Matrix-vector products whose long operand is stored K-major (B for
+    op_b = "n", A for op_a = "t"): read in place, every output checked."""
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect="f16_gemv")
+    ref, sab = reference(A, B, op_a, op_b, fmt)
+    r = check16(got, ref, sab, fmt)
+    print("[gemv K-major %dx%dx%d %s%s %s] max %.2f ulp" % (M, N, K, op_a, op_b, fmt, r["max_ulps"]),
+          flush=True)

@@ -7,15 +7,16 @@
 //
 //  * a 256-thread workgroup (4 waves, 2 x 2) owns a BM x BN tile of C
 //    (128 x 128, or 64 x 64 when the larger tiles would leave CUs idle);
-//  * K is walked in slabs of 16; each slab of A (BM x 16) and B (16 x BN) is
+//  * K is walked in slabs of 16 (32 for the 64 x 64 full tiles when K allows);
+//    each slab of A (BM x BK) and B (BK x BN) is
 //    fetched with 16-byte loads into registers one slab ahead and written to
 //    the other half of a double-buffered LDS ring, so one barrier per slab
 //    separates writers from readers;
-//  * a wave's tile is blocks of 16 x 16; per slab each block takes 4 MFMAs
-//    (K = 4 each).  Lane l = 16 g + r feeds the MFMA row/column r and, in MFMA
-//    step s, the slab column k = 4 g + s: the same bijection for both
-//    operands, so the four steps sum all 16 k of the slab.  With that mapping
-//    a lane's four A values are one 16-byte LDS read;
+//  * a wave's tile is blocks of 16 x 16; per 16 k of a slab each block takes
+//    4 MFMAs (K = 4 each).  Lane l = 16 g + r feeds the MFMA row/column r
+//    and, in MFMA step s of part q, the slab column k = 16 q + 4 g + s: the
+//    same bijection for both operands, so the four steps sum all 16 k of the
+//    part.  With that mapping a lane's four A values are one 16-byte LDS read;
 //  * epilogue: alpha * acc (+ beta * C when beta != 0, C is not read
 //    otherwise) straight from the accumulators (lane l, register v holds row
 //    4 g + v, column r of a block).
@@ -35,17 +36,21 @@
 namespace mi355gemm {
 namespace {
 
-constexpr int BK = 16;
+constexpr int BK = 16;   // K granularity of the full-tile kernel
 constexpr int kThreads = 256;
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int BM, int BN>
+// One LDS stage of a BKT-deep slab.  A rows are BKT + 4 floats apart for
+// BKT = 16 (measured fastest there) and BKT + 8 for BKT = 32 (bank-conflict
+// free 16-byte fragment reads); B rows BN + 4 floats apart: 4 rows apart = 16
+// banks apart.
+template <int BM, int BN, int BKT>
 struct Stage {
-  static constexpr int kAStride = BK + 4;   // floats per A row in LDS
-  static constexpr int kBStride = BN + 4;   // floats per B row in LDS: 4 rows apart = 16 banks apart
+  static constexpr int kAStride = BKT == 16 ? BKT + 4 : BKT + 8;
+  static constexpr int kBStride = BN + 4;
   float a[BM * kAStride];
-  float b[BK * kBStride];
+  float b[BKT * kBStride];
 };
 
 // Four consecutive floats of row `row`, columns col .. col + 3, of a matrix
@@ -70,9 +75,10 @@ __device__ __forceinline__ f4 load4(const float* base, int64_t ld, int rows, int
 // SPLIT instances write the fp32 partial product of one split-K range
 // (workgroup b: range b / tiles, tile b % tiles) to the tile-padded
 // workspace instead of C.
-template <int BM, int BN, bool EDGE, bool SPLIT = false>
+template <int BM, int BN, bool EDGE, bool SPLIT = false, int BKT = 16>
 __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int64_t tile_base) {
-  typedef Stage<BM, BN> S;
+  constexpr int BK = BKT;   // slab depth of this instance
+  typedef Stage<BM, BN, BKT> S;
   constexpr int WM = BM / 2, WN = BN / 2;              // wave tile
   constexpr int IB = WM / 16, JB = WN / 16;            // blocks per wave
   constexpr int kA = BM * BK / 4 / kThreads;           // A chunks per thread per slab
@@ -98,14 +104,14 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Global -> register assignment.
-  // A slab BM x 16: chunk e -> row e / 4, column 4 (e % 4).
+  // A slab BM x BK: chunk e -> row e / (BK / 4), column 4 (e % (BK / 4)).
   // B slab 16 x BN: chunk e -> row e / (BN / 4), column 4 (e % (BN / 4)).
   int arow[kA], acol[kA], brow[kB], bcol[kB], lA[kA], lB[kB];
 #pragma unroll
   for (int i = 0; i < kA; ++i) {
     const int e = tid + kThreads * i;
-    arow[i] = e >> 2;
-    acol[i] = (e & 3) * 4;
+    arow[i] = e / (BK / 4);
+    acol[i] = (e % (BK / 4)) * 4;
     lA[i] = arow[i] * S::kAStride + acol[i];
   }
 #pragma unroll
@@ -156,19 +162,24 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
     const S& cur = st[(t - t0) & 1];
     if (t + 1 < t1) fetch((t + 1) * BK);
 
-    f4 av[IB];
+    // 16-deep sub-slabs q of the slab, k = 16 q + 4 g + s.
 #pragma unroll
-    for (int i = 0; i < IB; ++i) av[i] = *(const f4*)&cur.a[(wm + 16 * i + r) * S::kAStride + 4 * g];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float bv[JB];
-#pragma unroll
-      for (int j = 0; j < JB; ++j) bv[j] = cur.b[(4 * g + s) * S::kBStride + wn + 16 * j + r];
+    for (int q = 0; q < BK / 16; ++q) {
+      f4 av[IB];
 #pragma unroll
       for (int i = 0; i < IB; ++i)
+        av[i] = *(const f4*)&cur.a[(wm + 16 * i + r) * S::kAStride + 16 * q + 4 * g];
 #pragma unroll
-        for (int j = 0; j < JB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[j], acc[i][j], 0, 0, 0);
+      for (int s = 0; s < 4; ++s) {
+        float bv[JB];
+#pragma unroll
+        for (int j = 0; j < JB; ++j) bv[j] = cur.b[(16 * q + 4 * g + s) * S::kBStride + wn + 16 * j + r];
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+#pragma unroll
+          for (int j = 0; j < JB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i][s], bv[j], acc[i][j], 0, 0, 0);
+      }
     }
 
     if (t + 1 < t1) stash(st[(t + 1 - t0) & 1]);
@@ -211,10 +222,11 @@ bool small_tiles(int M, int N, int cus) {
   return tiles128 < cus;
 }
 
-template <int BM, int BN, bool EDGE>
+template <int BM, int BN, bool EDGE, int BKT = 16>
 hipError_t launch_tiled(const F32Args& a, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  return launch_tiles((const void*)sgemm_mfma_kernel<BM, BN, EDGE>, a, tiles, kThreads, 0, stream);
+  return launch_tiles((const void*)sgemm_mfma_kernel<BM, BN, EDGE, false, BKT>, a, tiles, kThreads,
+                      0, stream);
 }
 
 }  // namespace
@@ -228,6 +240,9 @@ bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
   if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0)
     return launch_tiled<128, 128, false>(a, stream);
+  // The small tiles run one workgroup per CU; 32-deep slabs halve their
+  // barriers (1024^3: 28 us against 30 us).
+  if (a.K % 32 == 0) return launch_tiled<64, 64, false, 32>(a, stream);
   return launch_tiled<64, 64, false>(a, stream);
 }
 

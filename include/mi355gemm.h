@@ -214,10 +214,14 @@ MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int 
  * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  Other
  * layouts first copy each operand that is not K-contiguous (A for OP_T, B for
  * OP_N) into a K-contiguous workspace with a transposition kernel, then run
- * the A * B^T kernels; the workspace comes from the same stream-ordered,
- * per-stream store as the split-K workspace.  Unknown type, op or act values
- * are GEMM_ERR_BAD_ARG; a workspace that cannot be allocated is
- * GEMM_ERR_WORKSPACE.
+ * the A * B^T kernels -- except on the matrix-vector path (M <= 8 or N <= 8),
+ * where a long operand stored K-major (B for OP_N when M is the small side,
+ * A for OP_T when N is) is read in place, row by row, and the short one in
+ * either layout: its ranges of K leave fp32 partial sums in the workspace and
+ * the split-K reduction adds them in order.  The workspace comes from the
+ * same stream-ordered, per-stream store as the split-K workspace.  Unknown
+ * type, op or act values are GEMM_ERR_BAD_ARG; a workspace that cannot be
+ * allocated is GEMM_ERR_WORKSPACE.
  */
 enum { GEMM_TYPE_F16 = 0, GEMM_TYPE_BF16 = 1 };
 enum { GEMM_OP_N = 0, GEMM_OP_T = 1 };

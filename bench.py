@@ -59,6 +59,12 @@ def parse_args():
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the timing of the remaining workloads (256^3, 1024^3, 4096^3 with "
                          "beta 0.5, ragged 5000x3001x1537)")
+    ap.add_argument("--operands", choices=["seeded", "ones", "zeros"], default="seeded",
+                    help="operand values of the step products: the seeded uniform[-1,1) draws "
+                         "(the workload), or constant matrices (same shapes and code path; the "
+                         "matrix cores draw less power on constant data, so the clock holds "
+                         "higher -- a measure of how much of the gap to peak is the power "
+                         "limit, never the reported workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of a known size (the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -81,6 +87,9 @@ KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sge
                           "dense_gemm_sgemm_amd/build.py"]
 KERNEL_SOURCES[S_NAME] = KERNEL_SOURCES[H_NAME] + ["dense_gemm_sgemm_amd/csrc/splitk.hip"]
 COPY_BYTES = 1 << 30
+# Bytes written between launches for the cold-cache figure: twice the 256 MB
+# last-level cache.
+COLD_FLUSH_BYTES = 512 << 20
 
 
 def source_sha(name: str) -> str:
@@ -115,6 +124,15 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+
+
+def operand_values(kind: str, *arrays):
+    """The step products' operands: as drawn, or constant matrices of the same
+    shapes and dtypes."""
+    if kind == "seeded":
+        return arrays
+    fill = 1.0 if kind == "ones" else 0.0
+    return tuple(np.full_like(x, fill) for x in arrays)
 
 
 def flops(w) -> float:
@@ -192,7 +210,9 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     """Per-launch times of the workloads that are not part of the step: the
     small SGEMMs, the 4096^3 SGEMM with beta = 0.5, the ragged fp16 product,
     the 5376^2 x 2048 fp16 product with the fused bias + SiLU + residual
-    write-back, the fused-QKV shape and the single-tile long-K product (split-K).  Reported next to the step for context; not part of ``value``."""
+    write-back, the fused-QKV shape, the single-tile long-K product (split-K),
+    the step's fp16 product from a cold cache and the decode product.  Reported
+    next to the step for context; not part of ``value``."""
     res = {}
     cases = [("sgemm_256", 0.0), ("sgemm_1024", 0.0), ("sgemm_4096", 0.5),
              ("hgemm_nt_5000x3001x1537", None), ("hgemm_nt_5376x5376x2048", "fused"),
@@ -238,6 +258,31 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
         key = (name + "_bias_silu_residual" if beta == "fused" else
                name if beta is None or beta == 0.0 else "%s_beta%g" % (name, beta))
         res[key] = {"path": path, "avg_ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_TFLOPS[dt]}
+    # the step's fp16 product from a cold cache: before each launch a 512 MiB
+    # fill evicts the operands from L2 and the 256 MB last-level cache; only
+    # the product's own launch is timed
+    w = inputs.WORKLOADS[H_NAME]
+    A, B = inputs.workload_operands(H_NAME)
+    dA, dB = torch.from_numpy(A).to(dev), torch.from_numpy(B).to(dev)
+    dC = torch.empty(w["M"], w["N"], device=dev, dtype=torch.float16)
+    scratch = torch.empty(COLD_FLUSH_BYTES // 4, device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    dg.gemm_f16_nt(dA, dB, dC)
+    torch.cuda.synchronize()
+    for i in range(reps):
+        scratch.fill_(float(i))
+        evs[i][0].record(stream)
+        dg.gemm_f16_nt(dA, dB, dC)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    tf = flops(w) / (ms * 1e-3) / 1e12
+    res[H_NAME + "_cold"] = {"path": dg.f16_nt_path(dA, dB, dC), "avg_ms": ms, "tflops": tf,
+                             "frac_of_peak": tf / PEAK_TFLOPS["f16"],
+                             "flush_bytes_before_each_launch": COLD_FLUSH_BYTES}
+    del scratch
     # the decode product is bound by HBM bandwidth, not by the matrix cores
     w = inputs.WORKLOADS[V_NAME]
     run = gemv_runner(dg, inputs, torch, dev)
@@ -282,7 +327,7 @@ def main():
     hw, fw = inputs.WORKLOADS[H_NAME], inputs.WORKLOADS[F_NAME]
     parts = []
     if args.only in ("both", "hgemm"):
-        Ah, Bh = inputs.workload_operands(H_NAME)
+        Ah, Bh = operand_values(args.operands, *inputs.workload_operands(H_NAME))
         dAh, dBh = torch.from_numpy(Ah).to(dev), torch.from_numpy(Bh).to(dev)
         dCh = torch.empty(hw["M"], hw["N"], device=dev, dtype=torch.float16)
         assert dg.f16_nt_path(dAh, dBh, dCh) == "f16_mfma"
@@ -318,7 +363,7 @@ def main():
         parts.append((S_NAME, "f16", "hgemm_nt_edge_kernel", flops(sw),
                       lambda: dg.gemm_f16_nt(dAs, dBs, dCs)))
     if args.only in ("both", "sgemm"):
-        Af, Bf, _ = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])
+        Af, Bf = operand_values(args.operands, *inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])[:2])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
         dCf = torch.empty(fw["M"], fw["N"], device=dev, dtype=torch.float32)
         assert dg.f32_path(dAf, dBf, dCf) == "f32_mfma"
@@ -388,7 +433,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16 (fp32 acc) + f32" if len(parts) == 2 else parts[0][1],
-        "data": "synthetic (seeded uniform[-1,1); inputs resident in HBM)",
+        "data": ("synthetic (seeded uniform[-1,1); inputs resident in HBM)" if args.operands == "seeded"
+                 else "constant %s operands (power-limit measurement, not the workload)" % args.operands),
         "config": {"workload": " + ".join(p[0] for p in parts),
                    "shapes": {p[0]: [inputs.WORKLOADS[p[0].replace("_bias_silu_residual", "")][k]
                                      for k in ("M", "N", "K")] for p in parts},
@@ -397,9 +443,10 @@ def main():
         "roofline": roofline,
         "roofline_by_kernel": rooflines,
     }
-    if not args.no_other_configs and args.only == "both":
+    seeded = args.operands == "seeded"
+    if not args.no_other_configs and args.only == "both" and seeded:
         out["other_configs"] = other_configs(dg, inputs, torch, dev)
-    if not args.no_cpu_baseline and args.only == "both":
+    if not args.no_cpu_baseline and args.only == "both" and seeded:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -367,7 +367,7 @@ def main():
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
         dCf = torch.empty(fw["M"], fw["N"], device=dev, dtype=torch.float32)
         assert dg.f32_path(dAf, dBf, dCf) == "f32_mfma"
-        parts.append((F_NAME, "f32", "sgemm_mfma_kernel", flops(fw),
+        parts.append((F_NAME, "f32", "sgemm_stream_kernel", flops(fw),
                       lambda: dg.gemm_f32(dAf, dBf, dCf, 1.0, 0.0)))
     torch.cuda.synchronize()
 

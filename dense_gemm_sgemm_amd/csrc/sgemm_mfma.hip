@@ -21,6 +21,9 @@
 //    otherwise) straight from the accumulators (lane l, register v holds row
 //    4 g + v, column r of a block).
 //
+// Large products whose K is a multiple of 64 take the streaming kernel
+// further down instead (direct-to-LDS copies by dedicated copying waves).
+//
 // Two variants of every tile size: the full-tile kernel (M % BM == N % BN ==
 // K % 16 == 0, 16-byte aligned rows and leading dimensions that are
 // multiples of 4) loads and stores unchecked; the edge
@@ -32,6 +35,8 @@
 // such data itself); chunks that cross K or N are read element by element.
 #include "internal.h"
 #include "hgemm_tile.hpp"
+
+#include <utility>
 
 namespace mi355gemm {
 namespace {
@@ -215,6 +220,221 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
       }
 }
 
+// ---------------------------------------------------------------------------
+// The streaming kernel for large fp32 products (M, N multiples of 128, K a
+// multiple of 64): one persistent 512-thread workgroup per CU walks its
+// 128 x 128 tiles as one stream of 64-deep K slabs.
+//
+//  * waves 0-3 (one per SIMD) compute: each owns 64 x 64 of the tile, 16
+//    blocks of v_mfma_f32_16x16x4_f32 with 16 accumulators in rotation;
+//  * waves 4-7 only copy: every slab of A (128 x 64) and B (64 x 128) goes
+//    global -> LDS with global_load_lds_dwordx4 into a two-stage ring
+//    (2 x 64 KiB), one barrier per slab.  A copying wave shares its SIMD with
+//    a computing wave, so its copies carry no vector address arithmetic: the
+//    source is a wave-uniform base in scalar registers plus a lane offset
+//    computed once (a vector add per copy waits behind the other wave's
+//    matrix instructions and stalls the stream);
+//  * LDS layouts: A row a (64 floats, 16 chunks of 16 bytes) holds logical
+//    chunk c at position c ^ (a & 15); B row k (128 floats, 32 chunks) holds
+//    logical chunk c at position c ^ (4 ((k >> 2) & 3)).  One copy fills 4 A
+//    rows or 2 B rows (1 KiB, lane i writing position i); the permutation is
+//    realised by the global addresses the lanes load;
+//  * operands: per 16-deep part q of a slab, lane l = 16 g + r reads A row
+//    r of block i at k = 16 q + 4 g .. + 3 (one 16-byte read) and B column r
+//    of block j at k = 16 q + 4 g + s, s = 0..3 (four 4-byte reads); MFMA
+//    step s takes element s of both -- the k bijection of the register-staged
+//    kernel above, so both kernels sum in the same order and agree bit for
+//    bit.  Both reads are free of bank conflicts with these layouts;
+//  * B is the MFMA's first operand, so a lane's accumulator quad holds four
+//    consecutive columns of one row of C: one 16-byte store per block;
+//  * the barrier of slab t sits after 240 of its 256 MFMAs: before it every
+//    computing wave has read all of slab t and the copying waves have landed
+//    slab t + 1; after it they copy slab t + 2 into slab t's stage while the
+//    computing waves read the first fragments of slab t + 1.
+namespace stream {
+constexpr int BM = 128, BN = 128, BKS = 64;
+constexpr int kStageA = BM * BKS * 4, kStageB = BKS * BN * 4;   // bytes
+constexpr int kStage = kStageA + kStageB;
+constexpr int kThreads = 512;          // 4 computing + 4 copying waves
+constexpr int kCopiers = 4;
+constexpr int kCopies = 64 / kCopiers;   // copy instructions per copying wave per slab
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()).
+template <typename F, int... Q>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// A wave-uniform pointer, held in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* q) {
+  const uint64_t v = (uint64_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(((uint64_t)hi << 32) | lo);
+}
+
+// One direct-to-LDS copy: lane i loads 16 bytes from sbase + voff and they
+// land at dst + 16 i.  Written out so that the scalar-base form is the one
+// issued; M0 (the LDS destination) is set here, one wait state ahead of the
+// copy as the hardware requires.  Completion is the caller's explicit
+// vmcnt wait.
+__device__ __forceinline__ void copy16(const char* sbase, uint32_t voff, lds_void_t* dst) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(m0v)
+               : "memory", "m0");
+}
+
+constexpr int kWaitVmLgkm0 = 0x0070;   // s_waitcnt vmcnt(0) lgkmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;     // s_waitcnt lgkmcnt(0)
+
+__global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, int64_t tiles) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+  const int64_t stride = gridDim.x;
+  const int ntiles = (int)((tiles - blockIdx.x + stride - 1) / stride);
+  const int nk = p.K / BKS;
+  const int total = ntiles * nk;   // slabs of this workgroup's stream
+  auto origin = [&](int jt, int& m0, int& n0) __attribute__((always_inline)) {
+    int tm, tn;
+    hgemm::map_tile<8>(blockIdx.x + (int64_t)jt * stride, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+  };
+
+  if (wave >= 4) {
+    // Copying wave cw issues A copies c = cw + 4 i (rows 4 c .. 4 c + 3; lane
+    // l writes row 4 c + l / 16 at position l % 16, so it loads logical chunk
+    // (l % 16) ^ ((4 c + l / 16) & 15), where c & 3 = cw) and B copies
+    // c = cw + 4 i (rows 2 c, 2 c + 1; lane l writes row 2 c + l / 32 at
+    // position l % 32, logical chunk (l % 32) ^ (4 ((c >> 1) & 3)), where
+    // (c >> 1) & 3 = ((cw >> 1) + 2 i) & 3).
+    const int cw = wave - 4;
+    const uint32_t la = (uint32_t)((lane >> 4) * p.lda * 4);
+    const uint32_t lb = (uint32_t)((lane >> 5) * p.ldb * 4);
+    const uint32_t offA = la + 16 * ((lane & 15) ^ ((4 * cw + (lane >> 4)) & 15));
+    const uint32_t offB0 = lb + 16 * ((lane & 31) ^ (4 * ((cw >> 1) & 3)));
+    const uint32_t offB1 = lb + 16 * ((lane & 31) ^ (4 * (((cw >> 1) + 2) & 3)));
+    auto copy_slab = [&](int it) __attribute__((always_inline)) {
+      int m0, n0;
+      origin(it / nk, m0, n0);
+      const int t = it % nk;
+      const char* a = (const char*)(p.A + (int64_t)m0 * p.lda + t * BKS);
+      const char* b = (const char*)(p.B + (int64_t)(t * BKS) * p.ldb + n0);
+      unsigned char* st = lds + (it & 1) * kStage;
+#pragma unroll
+      for (int i = 0; i < kCopies / 2; ++i) {
+        const int c = cw + kCopiers * i;
+        copy16(uniform_ptr(a + (int64_t)c * 16 * p.lda), offA, (lds_void_t*)(st + c * 1024));
+      }
+#pragma unroll
+      for (int i = 0; i < kCopies / 2; ++i) {
+        const int c = cw + kCopiers * i;
+        copy16(uniform_ptr(b + (int64_t)c * 8 * p.ldb), (i & 1) ? offB1 : offB0,
+               (lds_void_t*)(st + kStageA + c * 1024));
+      }
+    };
+    // Slab 0, then after the barrier of slab t the slab t + 1 (into the stage
+    // slab t - 1 used), so that it has landed by the barrier of slab t.
+    copy_slab(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    asm volatile("s_barrier" ::: "memory");
+    for (int it = 0; it < total; ++it) {
+      if (it + 1 < total) copy_slab(it + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+      asm volatile("s_barrier" ::: "memory");
+    }
+    return;
+  }
+
+  const int g = lane >> 4, r = lane & 15;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+  // Two register sets of one 16-deep part: A blocks (16 bytes each) and the
+  // B values (s, j).
+  f4 av[2][4];
+  float bv[2][4][4];
+  // Read q of part `part` (q < 4: A block q; else B value ((q - 4) / 4, (q - 4) % 4)).
+  auto read_one = [&](const unsigned char* st, int set, int part, int q) __attribute__((always_inline)) {
+    if (q < 4) {
+      const int row = wm + 16 * q + r;   // row & 15 == r
+      av[set][q] = *(const f4*)(st + row * 256 + (((4 * part + g) ^ r) * 16));
+    } else {
+      const int s = (q - 4) >> 2, j = (q - 4) & 3;
+      const int k = 16 * part + 4 * g + s;   // (k >> 2) & 3 == g
+      const int chunk = ((wn + 16 * j) >> 2) + (r >> 2);
+      bv[set][s][j] = *(const float*)(st + kStageA + k * 512 + (4 * (chunk ^ (4 * g)) + (r & 3)) * 4);
+    }
+  };
+
+  asm volatile("s_barrier" ::: "memory");   // slab 0 has landed
+#pragma unroll
+  for (int q = 0; q < 20; ++q) read_one(lds, 0, 0, q);
+
+  // One slab in issue order: MFMA m of 256 is part m / 64, step s, block
+  // (i, j); the reads of part q + 1 go out during part q (one per three
+  // MFMAs), the barrier before MFMA 240, the next slab's first part after it.
+  auto slab = [&](int gs) __attribute__((always_inline)) {
+    const unsigned char* cur = lds + (gs & 1) * kStage;
+    const unsigned char* nxt = lds + ((gs + 1) & 1) * kStage;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<256>([&](auto mc) __attribute__((always_inline)) {
+      constexpr int m = decltype(mc)::value;
+      constexpr int part = m / 64, s = (m % 64) / 16, i = (m % 16) / 4, j = m % 4;
+      if constexpr (m == 240) {
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[part & 1][s][j], av[part & 1][i][s],
+                                                       acc[i][j], 0, 0, 0);
+      if constexpr (part < 3 && (m % 64) % 3 == 0 && (m % 64) / 3 < 20)
+        read_one(cur, (part + 1) & 1, part + 1, (m % 64) / 3);
+      if constexpr (m >= 240) {
+        read_one(nxt, 0, 0, m - 240);
+        if constexpr (m - 240 < 4) read_one(nxt, 0, 0, 16 + (m - 240));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // acc[i][j][v] is C[m0 + wm + 16 i + r][n0 + wn + 16 j + 4 g + v].
+  const float alpha = p.alpha, beta = p.beta;
+  int gs = 0;
+  for (int jt = 0; jt < ntiles; ++jt) {
+    int m0, n0;
+    origin(jt, m0, n0);
+    for (int t = 0; t < nk; ++t, ++gs) slab(gs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float* c = p.C + (int64_t)(m0 + wm + 16 * i + r) * p.ldc + n0 + wn + 16 * j + 4 * g;
+        f4 out = alpha * acc[i][j];
+        if (beta != 0.f) {
+          const f4 old = *(const f4*)c;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) out[v] = fmaf(beta, old[v], out[v]);
+        }
+        *(f4*)c = out;
+        acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+}
+}  // namespace stream
+
 // Tile size for an M x N product: 128 x 128 while that gives every CU work,
 // 64 x 64 below.
 bool small_tiles(int M, int N, int cus) {
@@ -238,8 +458,21 @@ bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
 }
 
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
-  if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0)
+  if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0) {
+    // The streaming kernel's lane offsets (3 rows into A or 1 row into B, in
+    // bytes) must fit in 32 bits.
+    constexpr int64_t kMaxLd = int64_t(1) << 28;
+    if (a.K % stream::BKS == 0 && a.lda < kMaxLd && a.ldb < kMaxLd) {
+      const int64_t tiles = (int64_t)(a.M / stream::BM) * (a.N / stream::BN);
+      const int64_t grid = tiles < cus ? tiles : cus;
+      F32Args p = a;
+      int64_t t = tiles;
+      void* args[] = {&p, &t};
+      return hipLaunchKernel((const void*)stream::sgemm_stream_kernel, dim3((unsigned)grid),
+                             dim3(stream::kThreads), args, 0, stream);
+    }
     return launch_tiled<128, 128, false>(a, stream);
+  }
   // The small tiles run one workgroup per CU; 32-deep slabs halve their
   // barriers (1024^3: 28 us against 30 us).
   if (a.K % 32 == 0) return launch_tiled<64, 64, false, 32>(a, stream);

@@ -789,6 +789,60 @@ def test_workload_sgemm_small_full(name):
     f32_check(got, oracle.gemm_f32(A, B), f32_tolerance(w["K"], np.abs(A).max(), np.abs(B).max()))
 
 
+# The streaming fp32 kernel: M and N multiples of 128 with at least one 128 x 128
+# tile per CU (256 on MI355X) and K a multiple of 64.  2048 x 2048 x 64: one
+# slab per tile, one tile per CU; 2176 x 2048: 272 tiles, so some workgroups
+# walk two tiles (the copy stream crosses a tile boundary); 4096 x 2048: two
+# tiles each.  Sampled outputs: whole rows, columns and tiles, and random points.
+STREAM_SHAPES = [(2048, 2048, 64), (2176, 2048, 192), (4096, 2048, 128), (2048, 2304, 320)]
+
+
+@pytest.mark.parametrize("shape", STREAM_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_stream_shapes(shape):
+    M, N, K = shape
+    A, B, _ = inputs.sgemm_operands(M, N, K)
+    got = gpu_f32(A, B, expect="f32_mfma")
+    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128), n_random=5000)
+    ref = oracle.gemm_f32_points(A, B, rows, cols)
+    f32_check(got[rows, cols], ref, f32_tolerance(K, 1.0, 1.0))
+
+
+def test_f32_stream_alpha_beta_padded_and_exact():
+    """alpha, beta and padded leading dimensions (16-byte loads of C, copies
+    at a row stride that is not a power of two), then small integers, which
+    make the fp32 result exact and independent of the summation order."""
+    M, N, K = 2176, 2048, 128
+    pad = 4
+    Abig, Bbig, Cbig = inputs.sgemm_operands(M, N + pad, K + pad, with_c=True)
+    A, B, C = Abig[:, :K], Bbig[:K, :N], Cbig[:, :N]
+    dA, dB, dC = dev(Abig), dev(Bbig), dev(Cbig)
+    dAv, dBv, dCv = dA[:, :K], dB[:K, :N], dC[:, :N]
+    assert dg.f32_path(dAv, dBv, dCv, -0.5, 0.5) == "f32_mfma"
+    dg.gemm_f32(dAv, dBv, dCv, -0.5, 0.5)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128), n_random=5000)
+    ref = oracle.gemm_f32_points(A, B, rows, cols, -0.5, 0.5, C)
+    f32_check(got[:, :N][rows, cols], ref, f32_tolerance(K, 1.0, 1.0, -0.5, 0.5, 1.0))
+    # the padding columns of C are untouched
+    assert np.array_equal(got[:, N:], Cbig[:, N:])
+
+    Ai = inputs.small_ints((M, 1024), 11, -3, 3, np.float32)
+    Bi = inputs.small_ints((1024, N), 12, -3, 3, np.float32)
+    goti = gpu_f32(Ai, Bi, expect="f32_mfma")
+    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128), n_random=5000)
+    assert np.array_equal(goti[rows, cols].astype(np.float64), oracle.gemm_f32_points(Ai, Bi, rows, cols))
+
+
+def test_f32_stream_fallback_k_not_a_multiple_of_64():
+    """K % 64 != 0 keeps the register-staged 128 x 128 kernel."""
+    M, N, K = 2048, 2048, 80
+    A, B, _ = inputs.sgemm_operands(M, N, K)
+    got = gpu_f32(A, B, expect="f32_mfma")
+    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128), n_random=5000)
+    f32_check(got[rows, cols], oracle.gemm_f32_points(A, B, rows, cols), f32_tolerance(K, 1.0, 1.0))
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.5])
 def test_workload_sgemm_4096(beta):
     M = N = K = 4096

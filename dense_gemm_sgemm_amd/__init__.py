@@ -48,6 +48,8 @@ def library_path() -> str:
 def load_library() -> ctypes.CDLL:
     """Load the C-ABI library; raises if it has not been built."""
     global _lib
+    if _lib is not None:
+        return _lib
     with _lock:
         if _lib is not None:
             return _lib
@@ -98,25 +100,58 @@ def _check(status: int) -> None:
         raise GemmError(status, status_string(status))
 
 
+_torch = None
+
+
+def _torch_module():
+    global _torch
+    if _torch is None:
+        import torch
+        _torch = torch
+    return _torch
+
+
 def _matrix(t, name: str, dtype):
-    import torch
+    """(rows, cols, leading dimension, device pointer or None) of a row-major
+    2-D GPU tensor; raises on anything else.  Runs on every call, so it uses
+    the cheapest tensor queries."""
+    torch = _torch_module()
     if not isinstance(t, torch.Tensor) or t.dim() != 2:
         raise TypeError("%s must be a 2-D torch tensor" % name)
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise TypeError("%s must live on the GPU" % name)
     rows, cols = t.shape
-    if cols > 1 and t.stride(1) != 1:
+    s0, s1 = t.stride()
+    if cols > 1 and s1 != 1:
         raise ValueError("%s must have unit stride along its rows (row-major)" % name)
-    ld = t.stride(0) if rows > 1 and cols > 0 else max(1, cols)
-    return rows, cols, ld, (t.data_ptr() if t.numel() else None)
+    ld = s0 if rows > 1 and cols > 0 else max(1, cols)
+    return rows, cols, ld, (t.data_ptr() if rows and cols else None)
+
+
+_raw_stream = None
+
+
+def _current_stream_handle() -> int:
+    """The HIP handle of torch's current stream on the current device.  torch's
+    raw-handle query costs about 0.1 us against about 3 us for building a
+    ``torch.cuda.Stream``; the public route is the fallback."""
+    global _raw_stream
+    torch = _torch_module()
+    if _raw_stream is None:
+        get_raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        get_dev = getattr(torch._C, "_cuda_getDevice", None)
+        if get_raw is not None and get_dev is not None:
+            _raw_stream = lambda: get_raw(get_dev())
+        else:
+            _raw_stream = lambda: torch.cuda.current_stream().cuda_stream
+    return _raw_stream()
 
 
 def _stream(stream):
-    import torch
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return _current_stream_handle()
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -124,7 +159,7 @@ def gemm_f32(A, B, C, alpha: float = 1.0, beta: float = 0.0, stream=None):
     """In place ``C = alpha * A @ B + beta * C`` for float32 A[M,K], B[K,N], C[M,N].
 
     Enqueued on ``stream`` (default: torch's current stream); returns C."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float32)
     K2, N, ldb, pb = _matrix(B, "B", torch.float32)
     M2, N2, ldc, pc = _matrix(C, "C", torch.float32)
@@ -146,7 +181,7 @@ def splitk_workspace_bytes(kind: str, M: int, N: int, K: int, splits: int = 0) -
 
 def _workspace(workspace, need: int, device):
     """(pointer, bytes) of a caller's workspace tensor, or of a new one."""
-    import torch
+    torch = _torch_module()
     if workspace is None:
         if need == 0:
             return None, 0
@@ -163,7 +198,7 @@ def gemm_f32_splitk(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int 
     """``gemm_f32`` with K cut into ``splits`` ranges (0: the library's choice) and
     the fp32 partial sums in ``workspace`` (a GPU tensor of at least
     ``splitk_workspace_bytes("f32", M, N, K, splits)`` bytes; allocated here if None)."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float32)
     K2, N, ldb, pb = _matrix(B, "B", torch.float32)
     M2, N2, ldc, pc = _matrix(C, "C", torch.float32)
@@ -180,7 +215,7 @@ def gemm_f16_nt_splitk(A, B, C, splits: int = 0, workspace=None, stream=None):
     """``gemm_f16_nt`` with K cut into ``splits`` ranges (0: the library's choice)
     and the fp32 partial sums in ``workspace`` (a GPU tensor of at least
     ``splitk_workspace_bytes("f16", M, N, K, splits)`` bytes; allocated here if None)."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float16)
     N, K2, ldb, pb = _matrix(B, "B", torch.float16)
     M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
@@ -197,7 +232,7 @@ def gemm_f16_nt(A, B, C, stream=None):
     """``C = A @ B.T`` for float16 A[M,K], B[N,K]; fp32 accumulation, result in C[M,N].
 
     Enqueued on ``stream`` (default: torch's current stream); returns C."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float16)
     N, K2, ldb, pb = _matrix(B, "B", torch.float16)
     M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
@@ -210,7 +245,7 @@ def gemm_f16_nt(A, B, C, stream=None):
 
 def f32_path(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> str:
     """Name of the kernel ``gemm_f32`` would launch for these tensors (host only)."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float32)
     _, N, ldb, pb = _matrix(B, "B", torch.float32)
     _, _, ldc, pc = _matrix(C, "C", torch.float32)
@@ -221,7 +256,7 @@ def f32_path(A, B, C, alpha: float = 1.0, beta: float = 0.0) -> str:
 
 def f16_nt_path(A, B, C) -> str:
     """Name of the kernel ``gemm_f16_nt`` would launch for these tensors (host only)."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float16)
     N, _, ldb, pb = _matrix(B, "B", torch.float16)
     _, _, ldc, pc = _matrix(C, "C", torch.float16)
@@ -230,7 +265,7 @@ def f16_nt_path(A, B, C) -> str:
 
 
 def _epilogue_args(bias, act, residual, M: int, N: int, dtype=None):
-    import torch
+    torch = _torch_module()
     dtype = dtype or torch.float16
     if act not in ACTS:
         raise ValueError("act must be one of %s" % sorted(ACTS))
@@ -255,7 +290,7 @@ def gemm_f16_nt_ex(A, B, C, bias=None, act: str = "none", residual=None, stream=
     ``bias`` a float16 vector of length N or None, ``act`` "none", "relu" or
     "silu", ``residual`` a float16 [M,N] tensor or None (it may be C itself).
     fp32 accumulation and epilogue, one rounding to half.  Returns C."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float16)
     N, K2, ldb, pb = _matrix(B, "B", torch.float16)
     M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
@@ -270,7 +305,7 @@ def gemm_f16_nt_ex(A, B, C, bias=None, act: str = "none", residual=None, stream=
 
 def f16_nt_ex_path(A, B, C, bias=None, act: str = "none", residual=None) -> str:
     """Name of the kernel ``gemm_f16_nt_ex`` would launch for these tensors (host only)."""
-    import torch
+    torch = _torch_module()
     M, K, lda, pa = _matrix(A, "A", torch.float16)
     N, _, ldb, pb = _matrix(B, "B", torch.float16)
     _, _, ldc, pc = _matrix(C, "C", torch.float16)
@@ -284,7 +319,7 @@ OPS = {"n": 0, "t": 1}
 
 
 def _ex_args(A, B, C, op_a, op_b, bias, act, residual):
-    import torch
+    torch = _torch_module()
     if op_a not in OPS or op_b not in OPS:
         raise ValueError("op_a and op_b must be 'n' or 't'")
     dtype = A.dtype if isinstance(A, torch.Tensor) else None

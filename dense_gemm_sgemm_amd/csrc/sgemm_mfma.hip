@@ -435,6 +435,194 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
 }
 }  // namespace stream
 
+// The streaming kernel for mid-size products (M, N multiples of 64 with
+// fewer 128 x 128 tiles than CUs, K a multiple of 64): 64 x 64 tiles, so that
+// every CU gets work, with the structure of the kernel above -- one
+// persistent 512-thread workgroup per CU, 4 computing and 4 copying waves,
+// direct-to-LDS copies of 64-deep slabs in the scalar-base form.  A 64 x 64
+// tile split four ways would leave each wave 4 accumulators, too few to cover
+// the matrix instruction's latency; instead each computing wave w owns the
+// whole tile (16 accumulators) for the 16-deep part w of every slab, and at
+// the end of the tile the four partial tiles are added in LDS in the fixed
+// order w = 0, 1, 2, 3.
+//
+//  * LDS: three slab stages (A 64 x 64 and B 64 x 64, 32 KiB each stage),
+//    then 4 x 16 KiB of partial tiles.  A row a holds logical chunk c at
+//    c ^ (a & 15), B row k at c ^ (4 ((k >> 2) & 3)), partial-tile row a at
+//    c ^ (a & 15): every read and write of them is free of bank conflicts;
+//  * barrier B_t opens slab t: slab t + 1 has landed, and every computing
+//    wave has read slab t (its fragments went to registers during slab
+//    t - 1), so the copying waves refill slab t's stage with slab t + 3;
+//  * during slab t a computing wave runs its 64 MFMAs on slab t and reads
+//    its part of slab t + 1;
+//  * after a tile's last slab each computing wave stores its partial tile,
+//    all eight waves meet (the copying waves count the slabs of each tile),
+//    and computing wave w adds the four partials of rows 16 w .. 16 w + 15
+//    and writes them to C, 16 bytes per lane.
+namespace stream64 {
+constexpr int BT = 64, BKS = 64;
+constexpr int kStage = 2 * BT * BKS * 4;    // A and B of one slab: 32 KiB
+constexpr int kStages = 3;
+constexpr int kPartial = BT * BT * 4;       // one wave's partial tile: 16 KiB
+constexpr int kLds = kStages * kStage + 4 * kPartial;
+constexpr int kThreads = 512;
+constexpr int kCopies = 8;                  // per copying wave per slab: 4 of A, 4 of B
+static_assert(kLds <= 160 * 1024, "LDS");
+
+__global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, int64_t tiles) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tiles_m = p.M / BT, tiles_n = p.N / BT;
+  const int64_t stride = gridDim.x;
+  const int ntiles = (int)((tiles - blockIdx.x + stride - 1) / stride);
+  const int nk = p.K / BKS;
+  const int total = ntiles * nk;
+  auto origin = [&](int jt, int& m0, int& n0) __attribute__((always_inline)) {
+    int tm, tn;
+    hgemm::map_tile<8>(blockIdx.x + (int64_t)jt * stride, tiles_m, tiles_n, tm, tn);
+    m0 = tm * BT;
+    n0 = tn * BT;
+  };
+  unsigned char* partials = lds + kStages * kStage;
+
+  if (wave >= 4) {
+    // Copy c (0..15) of A fills rows 4 c .. 4 c + 3 and copy c of B rows
+    // 4 c .. 4 c + 3 (rows of 256 bytes; lane l writes row 4 c + l / 16 at
+    // position l % 16).  Copying wave cw issues c = cw + 4 i, so c & 3 = cw
+    // and one lane offset serves all its copies of each operand.
+    const int cw = wave - 4;
+    const int row = lane >> 4, pos = lane & 15;
+    const uint32_t offA = (uint32_t)(row * p.lda * 4) + 16 * (pos ^ ((4 * cw + row) & 15));
+    const uint32_t offB = (uint32_t)(row * p.ldb * 4) + 16 * (pos ^ (4 * (cw & 3)));
+    auto copy_slab = [&](int it) __attribute__((always_inline)) {
+      int m0, n0;
+      origin(it / nk, m0, n0);
+      const int t = it % nk;
+      const char* a = (const char*)(p.A + (int64_t)m0 * p.lda + t * BKS);
+      const char* b = (const char*)(p.B + (int64_t)(t * BKS) * p.ldb + n0);
+      unsigned char* st = lds + (it % kStages) * kStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = cw + 4 * i;
+        stream::copy16(stream::uniform_ptr(a + (int64_t)c * 16 * p.lda), offA,
+                       (stream::lds_void_t*)(st + c * 1024));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = cw + 4 * i;
+        stream::copy16(stream::uniform_ptr(b + (int64_t)c * 16 * p.ldb), offB,
+                       (stream::lds_void_t*)(st + BT * BKS * 4 + c * 1024));
+      }
+    };
+    // Slabs 0 and 1 before the opening barrier, slab 2 after it; after B_t
+    // slab t + 3.  Before B_t slab t + 1 must have landed: all copies but
+    // the latest slab's (slab t + 2, if it exists) are complete.
+    copy_slab(0);
+    if (total > 1) copy_slab(1);
+    __builtin_amdgcn_s_waitcnt(stream::kWaitVmLgkm0);
+    asm volatile("s_barrier" ::: "memory");
+    if (total > 2) copy_slab(2);
+    for (int it = 0; it < total; ++it) {
+      if (it + 2 < total) {
+        __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8): slab it + 2's copies may stay in flight
+      } else {
+        __builtin_amdgcn_s_waitcnt(stream::kWaitVmLgkm0);
+      }
+      asm volatile("s_barrier" ::: "memory");   // B_it
+      if (it + 3 < total) copy_slab(it + 3);
+      if (it % nk == nk - 1) asm volatile("s_barrier" ::: "memory");   // the tile's reduction
+    }
+    __builtin_amdgcn_s_waitcnt(stream::kWaitVmLgkm0);
+    return;
+  }
+
+  const int g = lane >> 4, r = lane & 15;
+  const int w = wave;   // this wave's 16-deep part of every slab
+  f4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 av[2][4];          // set 0: the current slab, set 1: the next
+  float bv[2][4][4];
+  // Read q of this wave's part of a slab: q < 4 A block q (row 16 q + r,
+  // k = 16 w + 4 g .. + 3), else B value (s, j) = ((q - 4) / 4, (q - 4) % 4)
+  // (row k = 16 w + 4 g + s, column 16 j + r).
+  auto read_one = [&](const unsigned char* st, int set, int q) __attribute__((always_inline)) {
+    if (q < 4) {
+      const int row = 16 * q + r;
+      av[set][q] = *(const f4*)(st + row * 256 + (((4 * w + g) ^ r) * 16));
+    } else {
+      const int s = (q - 4) >> 2, j = (q - 4) & 3;
+      const int k = 16 * w + 4 * g + s;   // (k >> 2) & 3 == g
+      const int chunk = 4 * j + (r >> 2);
+      bv[set][s][j] = *(const float*)(st + BT * BKS * 4 + k * 256 + (4 * (chunk ^ (4 * g)) + (r & 3)) * 4);
+    }
+  };
+
+  asm volatile("s_barrier" ::: "memory");   // slabs 0 and 1 have landed
+#pragma unroll
+  for (int q = 0; q < 20; ++q) read_one(lds, 0, q);
+
+  const float alpha = p.alpha, beta = p.beta;
+  int gs = 0;
+  for (int jt = 0; jt < ntiles; ++jt) {
+    int m0, n0;
+    origin(jt, m0, n0);
+    for (int t = 0; t < nk; ++t, ++gs) {
+      __builtin_amdgcn_s_waitcnt(stream::kWaitLgkm0);
+      asm volatile("s_barrier" ::: "memory");   // B_gs
+      const unsigned char* nxt = lds + ((gs + 1) % kStages) * kStage;
+      __builtin_amdgcn_sched_barrier(0);
+      stream::static_for<64>([&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int s = m / 16, i = (m % 16) / 4, j = m % 4;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[0][s][j], av[0][i][s], acc[i][j], 0, 0, 0);
+        if constexpr (m % 3 == 0 && m / 3 < 20) read_one(nxt, 1, m / 3);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // the next slab's fragments become the current set (register moves:
+      // a set index that changes from slab to slab would need indexed
+      // register access)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av[0][i] = av[1][i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[0][i][j] = bv[1][i][j];
+      }
+    }
+    // acc[i][j][v] is this wave's part of C[m0 + 16 i + r][n0 + 16 j + 4 g + v].
+    unsigned char* mine = partials + w * kPartial;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *(f4*)(mine + (16 * i + r) * 256 + (((4 * j + g) ^ r) * 16)) = acc[i][j];
+        acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+      }
+    __builtin_amdgcn_s_waitcnt(stream::kWaitLgkm0);
+    asm volatile("s_barrier" ::: "memory");   // the tile's reduction
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 16 * w + 4 * u + g, chunk = r;
+      const int off = row * 256 + ((chunk ^ (row & 15)) * 16);
+      f4 sum = *(const f4*)(partials + off);
+#pragma unroll
+      for (int v = 1; v < 4; ++v) sum += *(const f4*)(partials + v * kPartial + off);
+      float* c = p.C + (int64_t)(m0 + row) * p.ldc + n0 + 4 * chunk;
+      f4 out = alpha * sum;
+      if (beta != 0.f) {
+        const f4 old = *(const f4*)c;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, old[e], out[e]);
+      }
+      *(f4*)c = out;
+    }
+  }
+}
+}  // namespace stream64
+
 // Tile size for an M x N product: 128 x 128 while that gives every CU work,
 // 64 x 64 below.
 bool small_tiles(int M, int N, int cus) {
@@ -472,6 +660,16 @@ hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
                              dim3(stream::kThreads), args, 0, stream);
     }
     return launch_tiled<128, 128, false>(a, stream);
+  }
+  constexpr int64_t kMaxLd = int64_t(1) << 28;
+  if (a.K % stream64::BKS == 0 && a.lda < kMaxLd && a.ldb < kMaxLd) {
+    const int64_t tiles = (int64_t)(a.M / stream64::BT) * (a.N / stream64::BT);
+    const int64_t grid = tiles < cus ? tiles : cus;
+    F32Args p = a;
+    int64_t t = tiles;
+    void* args[] = {&p, &t};
+    return hipLaunchKernel((const void*)stream64::sgemm_stream64_kernel, dim3((unsigned)grid),
+                           dim3(stream64::kThreads), args, 0, stream);
   }
   // The small tiles run one workgroup per CU; 32-deep slabs halve their
   // barriers (1024^3: 28 us against 30 us).

@@ -834,6 +834,41 @@ def test_f32_stream_alpha_beta_padded_and_exact():
     assert np.array_equal(goti[rows, cols].astype(np.float64), oracle.gemm_f32_points(Ai, Bi, rows, cols))
 
 
+# The 64 x 64 streaming kernel: M and N multiples of 64 with fewer 128 x 128
+# tiles than CUs (or not multiples of 128), K a multiple of 64.  64^3: a
+# stream of one slab; 64 x 128 x 128: two workgroups of two slabs; 192 x 64 x
+# 320: odd slab counts; 1088 x 1024 x 192: 272 tiles, so some workgroups
+# reduce two tiles in turn.  Compared element by element with the oracle.
+STREAM64_SHAPES = [(64, 64, 64), (64, 128, 128), (192, 64, 320), (1088, 1024, 192), (512, 768, 1024)]
+
+
+@pytest.mark.parametrize("shape", STREAM64_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_stream64_shapes(shape):
+    M, N, K = shape
+    A, B, _ = inputs.sgemm_operands(M, N, K)
+    got = gpu_f32(A, B, expect="f32_mfma")
+    f32_check(got, oracle.gemm_f32(A, B), f32_tolerance(K, 1.0, 1.0))
+
+
+def test_f32_stream64_alpha_beta_padded_and_exact():
+    M, N, K = 1088, 1024, 128
+    pad = 4
+    Abig, Bbig, Cbig = inputs.sgemm_operands(M, N + pad, K + pad, with_c=True)
+    A, B, C = Abig[:, :K], Bbig[:K, :N], Cbig[:, :N]
+    dA, dB, dC = dev(Abig), dev(Bbig), dev(Cbig)
+    dAv, dBv, dCv = dA[:, :K], dB[:K, :N], dC[:, :N]
+    assert dg.f32_path(dAv, dBv, dCv, 1.5, -0.75) == "f32_mfma"
+    dg.gemm_f32(dAv, dBv, dCv, 1.5, -0.75)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    ref = oracle.gemm_f32(A, B, 1.5, -0.75, C)
+    f32_check(got[:, :N], ref, f32_tolerance(K, 1.0, 1.0, 1.5, -0.75, 1.0))
+    assert np.array_equal(got[:, N:], Cbig[:, N:])
+    Ai = inputs.small_ints((M, 640), 13, -3, 3, np.float32)
+    Bi = inputs.small_ints((640, N), 14, -3, 3, np.float32)
+    assert np.array_equal(gpu_f32(Ai, Bi, expect="f32_mfma").astype(np.float64), oracle.gemm_f32(Ai, Bi))
+
+
 def test_f32_stream_fallback_k_not_a_multiple_of_64():
     """K % 64 != 0 keeps the register-staged 128 x 128 kernel."""
     M, N, K = 2048, 2048, 80

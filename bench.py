@@ -90,6 +90,8 @@ COPY_BYTES = 1 << 30
 # Bytes written between launches for the cold-cache figure: twice the 256 MB
 # last-level cache.
 COLD_FLUSH_BYTES = 512 << 20
+# Wall time each of the other workloads runs untimed before it is timed.
+WARM_SECONDS = 0.05
 
 
 def source_sha(name: str) -> str:
@@ -206,6 +208,18 @@ def cpu_baseline(seconds: float) -> dict:
     }
 
 
+def warm_up(run, torch, seconds: float = WARM_SECONDS, least: int = 3):
+    """Calls ``run`` (one call in flight at a time) for at least ``least``
+    calls and ``seconds`` of wall time, so that a workload is timed once the
+    clock has settled for it rather than right after the previous one."""
+    deadline = time.perf_counter() + seconds
+    n = 0
+    while n < least or time.perf_counter() < deadline:
+        run()
+        torch.cuda.synchronize()
+        n += 1
+
+
 def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     """Per-launch times of the workloads that are not part of the step: the
     small SGEMMs, the 4096^3 SGEMM with beta = 0.5, the ragged fp16 product,
@@ -243,8 +257,7 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
             run = lambda: dg.gemm_f16_nt(dA, dB, dC)
             path = dg.f16_nt_path(dA, dB, dC)
             dt = "f16"
-        for _ in range(3):
-            run()
+        warm_up(run, torch)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         stream = torch.cuda.current_stream()
         torch.cuda.synchronize()
@@ -286,8 +299,7 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     # the decode product is bound by HBM bandwidth, not by the matrix cores
     w = inputs.WORKLOADS[V_NAME]
     run = gemv_runner(dg, inputs, torch, dev)
-    for _ in range(2 * V_COPIES):
-        run()
+    warm_up(run, torch, least=2 * V_COPIES)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     stream = torch.cuda.current_stream()
     reps = 25 * V_COPIES

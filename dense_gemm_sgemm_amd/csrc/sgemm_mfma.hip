@@ -342,8 +342,9 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
                (lds_void_t*)(st + kStageA + c * 1024));
       }
     };
-    // Slab 0, then after the barrier of slab t the slab t + 1 (into the stage
-    // slab t - 1 used), so that it has landed by the barrier of slab t.
+    // Slab 0 before the opening barrier; then, after the barrier of slab
+    // t - 1 (the opening one for t = 0), slab t + 1 into the stage slab t - 1
+    // used, landed before the barrier of slab t.
     copy_slab(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
     asm volatile("s_barrier" ::: "memory");
@@ -468,6 +469,7 @@ constexpr int kLds = kStages * kStage + 4 * kPartial;
 constexpr int kThreads = 512;
 constexpr int kCopies = 8;                  // per copying wave per slab: 4 of A, 4 of B
 static_assert(kLds <= 160 * 1024, "LDS");
+static_assert(kCopies < 16, "a vmcnt immediate below 16");
 
 __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, int64_t tiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
@@ -525,7 +527,8 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, 
     if (total > 2) copy_slab(2);
     for (int it = 0; it < total; ++it) {
       if (it + 2 < total) {
-        __builtin_amdgcn_s_waitcnt(0x0078);   // vmcnt(8): slab it + 2's copies may stay in flight
+        // vmcnt(kCopies) lgkmcnt(0): slab it + 2's copies may stay in flight
+        __builtin_amdgcn_s_waitcnt(0x0070 | kCopies);
       } else {
         __builtin_amdgcn_s_waitcnt(stream::kWaitVmLgkm0);
       }

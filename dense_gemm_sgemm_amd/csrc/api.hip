@@ -50,20 +50,69 @@ int check_device() {
   return s > 0 ? s : GEMM_ERR_UNSUPPORTED_DEVICE;
 }
 
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Stands for the address of a workspace copy in the path choice.
+const void* const kCopyAddress = reinterpret_cast<const void*>(uintptr_t(256));
+
+// Large enough that copying A and B into padded rows and running the
+// full-tile kernel beats the edge kernel (at least 2^30 multiply-adds; the
+// copies then cost about a fifth of the product on MI355X).
+bool padding_pays(int M, int N, int K) { return (int64_t)M * N * K >= (int64_t(1) << 30); }
+
+// The fp32 path, and for GEMM_PATH_F32_PADDED the extent the streaming
+// kernels see: an operand whose rows are not whole tiles, not 16-byte aligned
+// or whose K is not a multiple of 64 is copied into zero-padded rows (A:
+// Mp x Kp, B: Kp x Np); the other is read in place.  Tiles are 128 x 128
+// when the padded product has at least kPadTiles of them, else 64 x 64.
+struct Plan32 {
+  int path = GEMM_PATH_NOOP;
+  bool copy_a = false, copy_b = false;
+  int Mp = 0, Np = 0, Kp = 0;
+  int64_t lda = 0, ldb = 0;
+};
+constexpr int64_t kPadTiles = 256;   // the CU count of MI355X
+
+Plan32 plan32(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
+              float beta, const float* C, int ldc) {
+  (void)beta;
+  Plan32 pl;
+  auto done = [&](int code) {
+    pl.path = code;
+    return pl;
+  };
+  if (M < 0 || N < 0 || K < 0) return done(GEMM_ERR_NEGATIVE_DIM);
+  if (M == 0 || N == 0) return done(GEMM_PATH_NOOP);
+  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    return done(GEMM_ERR_BAD_LD);
+  if (C == nullptr) return done(GEMM_ERR_NULL_POINTER);
+  if (K == 0 || alpha == 0.f) return done(GEMM_PATH_F32_SCALE);
+  if (A == nullptr || B == nullptr) return done(GEMM_ERR_NULL_POINTER);
+  if (force_general()) return done(GEMM_PATH_F32_GENERAL);
+  if (splitk_plan(M, N, K, kF32Slab, kF32Rule, 0).splits > 1) return done(GEMM_PATH_F32_SPLITK);
+  const bool tiles = f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc);
+  if (f32_stream_fits(M, N, K, A, lda, B, ldb, C, ldc) || (tiles && !padding_pays(M, N, K)))
+    return done(GEMM_PATH_F32_MFMA);
+  if (!padding_pays(M, N, K)) return done(GEMM_PATH_F32_GENERAL);
+  const int64_t big = round_up(M, 128) * round_up(N, 128) / (128 * 128);
+  const int bt = big >= kPadTiles ? 128 : 64;
+  const bool k_ok = K % 64 == 0;
+  pl.copy_a = !(k_ok && M % bt == 0 && f32_operand_fits(A, lda));
+  pl.copy_b = !(k_ok && N % bt == 0 && f32_operand_fits(B, ldb));
+  pl.Kp = (int)round_up(K, 64);
+  pl.Mp = pl.copy_a ? (int)round_up(M, bt) : M;
+  pl.Np = pl.copy_b ? (int)round_up(N, bt) : N;
+  pl.lda = pl.copy_a ? pl.Kp : lda;
+  pl.ldb = pl.copy_b ? pl.Np : ldb;
+  // the copies' leading dimensions must also suit the kernels' lane offsets
+  if (!f32_operand_fits(kCopyAddress, pl.lda) || !f32_operand_fits(kCopyAddress, pl.ldb))
+    return done(GEMM_PATH_F32_GENERAL);
+  return done(GEMM_PATH_F32_PADDED);
+}
+
 int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const float* B, int ldb,
                float beta, const float* C, int ldc) {
-  (void)beta;
-  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_NEGATIVE_DIM;
-  if (M == 0 || N == 0) return GEMM_PATH_NOOP;
-  if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
-    return GEMM_ERR_BAD_LD;
-  if (C == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (K == 0 || alpha == 0.f) return GEMM_PATH_F32_SCALE;
-  if (A == nullptr || B == nullptr) return GEMM_ERR_NULL_POINTER;
-  if (force_general()) return GEMM_PATH_F32_GENERAL;
-  if (splitk_plan(M, N, K, kF32Slab, kF32Rule, 0).splits > 1) return GEMM_PATH_F32_SPLITK;
-  if (f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc)) return GEMM_PATH_F32_MFMA;
-  return GEMM_PATH_F32_GENERAL;
+  return plan32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc).path;
 }
 
 // The 16-bit calls share one selection.  Plan16 records the kernel path and
@@ -80,15 +129,6 @@ struct Plan16 {
   int64_t lda = 0, ldb = 0;     // leading dimensions the kernels see
 };
 
-int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-// Stands for the address of a workspace copy in the path choice.
-const void* const kCopyAddress = reinterpret_cast<const void*>(uintptr_t(256));
-
-// Large enough that copying A and B into padded rows and running the
-// full-tile kernel beats the edge kernel (at least 2^30 multiply-adds; the
-// copies then cost about a fifth of the product on MI355X).
-bool padding_pays(int M, int N, int K) { return (int64_t)M * N * K >= (int64_t(1) << 30); }
 
 // The validated plan of a 16-bit call, or a negative GEMM_ERR_* code in
 // plan.path.  K == 0 gives C = act(bias) + residual: zero when there is no
@@ -275,6 +315,46 @@ hipError_t f32_auto_split(F32Args a, int cus, hipStream_t s) {
   return e != hipSuccess ? e : f;
 }
 
+// The padded fp32 path: zero-padded copies of the operands that need them
+// (one launch), then the masked streaming kernel on the padded extent.
+// Without a workspace the edge kernel runs instead.
+hipError_t run32_padded(const Plan32& pl, F32Args a, int cus, hipStream_t s) {
+  auto round256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bytes_a = pl.copy_a ? round256((size_t)pl.Mp * pl.lda * 4) : 0;
+  const size_t bytes_b = pl.copy_b ? round256((size_t)pl.Kp * pl.ldb * 4) : 0;
+  std::unique_lock<std::mutex> lock(g_ws_mutex, std::defer_lock);
+  bool owned = false;
+  char* ws = nullptr;
+  if (bytes_a + bytes_b > 0) {   // else only C is unaligned: no copies
+    lock.lock();
+    ws = static_cast<char*>(stream_workspace(s, bytes_a + bytes_b, &owned));
+    if (owned || ws == nullptr) lock.unlock();
+    if (ws == nullptr) return launch_f32_edge(a, cus, s);
+  }
+  float* dst_a = reinterpret_cast<float*>(ws);
+  float* dst_b = reinterpret_cast<float*>(ws + bytes_a);
+  const PadCopy32 pad_a{a.A, dst_a, a.lda, pl.lda, a.M, a.K, pl.Mp, pl.Kp};
+  const PadCopy32 pad_b{a.B, dst_b, a.ldb, pl.ldb, a.K, a.N, pl.Kp, pl.Np};
+  hipError_t e = hipSuccess;
+  if (pl.copy_a || pl.copy_b)
+    e = pl.copy_a ? launch_pad32(pad_a, pl.copy_b ? &pad_b : nullptr, s)
+                  : launch_pad32(pad_b, nullptr, s);
+  if (e == hipSuccess) {
+    if (pl.copy_a) a.A = dst_a;
+    if (pl.copy_b) a.B = dst_b;
+    a.lda = pl.lda;
+    a.ldb = pl.ldb;
+    a.m_out = a.M;
+    a.n_out = a.N;
+    a.M = pl.Mp;
+    a.N = pl.Np;
+    a.K = pl.Kp;
+    e = launch_f32_mfma_masked(a, cus, s);
+  }
+  const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
+  return e != hipSuccess ? e : f;
+}
+
 // Runs a validated 16-bit plan: the operand copies (transposed and/or
 // padded) into the workspace, then the kernels of the plan's path.  a holds
 // the caller's operands and output; op_a / op_b say how A and B are stored.
@@ -360,7 +440,8 @@ extern "C" {
 
 MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
                            const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
-  const int path = f32_select(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  const Plan32 pl = plan32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+  const int path = pl.path;
   if (path < 0 || path == GEMM_PATH_NOOP) return path < 0 ? path : GEMM_OK;
   const int cus = check_device();
   if (cus < 0) return cus;
@@ -370,6 +451,7 @@ MI355GEMM_API int gemm_f32(int M, int N, int K, float alpha, const float* A, int
     case GEMM_PATH_F32_SCALE: return to_status(launch_f32_scale(a, s));
     case GEMM_PATH_F32_MFMA: return to_status(launch_f32_mfma(a, cus, s));
     case GEMM_PATH_F32_SPLITK: return to_status(f32_auto_split(a, cus, s));
+    case GEMM_PATH_F32_PADDED: return to_status(run32_padded(pl, a, cus, s));
     default: return to_status(launch_f32_edge(a, cus, s));
   }
 }
@@ -542,6 +624,7 @@ MI355GEMM_API const char* gemm_path_name(int path) {
     case GEMM_PATH_F16_SPLITK: return "f16_splitk";
     case GEMM_PATH_F32_SPLITK: return "f32_splitk";
     case GEMM_PATH_F16_PADDED: return "f16_padded";
+    case GEMM_PATH_F32_PADDED: return "f32_padded";
     default: return "?";
   }
 }

@@ -29,6 +29,9 @@ struct F32Args {
   int M, N, K;
   float alpha, beta;
   SplitK sk;                      // split-K partial products (partial kernels only)
+  // Masked instances: M x N are whole tiles of zero-padded copies of A and B,
+  // and only rows < m_out, columns < n_out of C exist.
+  int m_out = 0, n_out = 0;
 };
 
 // 16-bit storage formats.  Kernels move both as 16-bit words (half_t
@@ -142,6 +145,18 @@ struct PadCopy {
   int rows, cols, rows_p, cols_p;
 };
 hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
+// The same for fp32 matrices (cols_p and ldd multiples of 4, dst 16-byte
+// aligned).
+struct PadCopy32 {
+  const float* src;
+  float* dst;
+  int64_t lds, ldd;
+  int rows, cols, rows_p, cols_p;
+};
+hipError_t launch_pad32(const PadCopy32& first, const PadCopy32* second, hipStream_t stream);
+// The fp32 streaming kernels on zero-padded copies (a.M, a.N multiples of 64,
+// a.K of 64), storing only a.m_out x a.n_out of C at any alignment.
+hipError_t launch_f32_mfma_masked(const F32Args& a, int cus, hipStream_t stream);
 // The full-tile kernel on zero-padded copies, storing only m_out x n_out.
 hipError_t launch_f16_mfma_masked(const Args16& a, bool epi, int cus, hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.
@@ -156,6 +171,14 @@ hipError_t launch_f32_splitk(const F32Args& a, hipStream_t stream);
 // Shape and alignment conditions of the fast kernels (checked on the host).
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc);
+// The fp32 streaming kernels apply in place (full tiles, K a multiple of 64,
+// leading dimensions within their 32-bit lane offsets).
+bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                     const void* C, int64_t ldc);
+// An fp32 operand the streaming kernels can read in place (rows 16-byte
+// aligned, leading dimension within their lane offsets); its rows must also
+// be whole tiles and K a multiple of 64.
+bool f32_operand_fits(const void* X, int64_t ld);
 // Alignment conditions of the fast kernel's fused write-back.
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr);
 bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,

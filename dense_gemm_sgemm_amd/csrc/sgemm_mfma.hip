@@ -294,6 +294,10 @@ __device__ __forceinline__ void copy16(const char* sbase, uint32_t voff, lds_voi
 constexpr int kWaitVmLgkm0 = 0x0070;   // s_waitcnt vmcnt(0) lgkmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;     // s_waitcnt lgkmcnt(0)
 
+// MASK instances read zero-padded copies of A and B (whole tiles) and read
+// and write C only inside p.m_out x p.n_out, element by element, at any
+// alignment.
+template <bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, int64_t tiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
   const int lane = threadIdx.x & 63;
@@ -422,14 +426,28 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float* c = p.C + (int64_t)(m0 + wm + 16 * i + r) * p.ldc + n0 + wn + 16 * j + 4 * g;
-        f4 out = alpha * acc[i][j];
-        if (beta != 0.f) {
-          const f4 old = *(const f4*)c;
+        const int m = m0 + wm + 16 * i + r, n = n0 + wn + 16 * j + 4 * g;
+        float* c = p.C + (int64_t)m * p.ldc + n;
+        if constexpr (MASK) {
+          if (m < p.m_out) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) out[v] = fmaf(beta, old[v], out[v]);
+            for (int v = 0; v < 4; ++v) {
+              if (n + v < p.n_out) {
+                float out = alpha * acc[i][j][v];
+                if (beta != 0.f) out = fmaf(beta, c[v], out);
+                c[v] = out;
+              }
+            }
+          }
+        } else {
+          f4 out = alpha * acc[i][j];
+          if (beta != 0.f) {
+            const f4 old = *(const f4*)c;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) out[v] = fmaf(beta, old[v], out[v]);
+          }
+          *(f4*)c = out;
         }
-        *(f4*)c = out;
         acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
       }
   }
@@ -471,6 +489,7 @@ constexpr int kCopies = 8;                  // per copying wave per slab: 4 of A
 static_assert(kLds <= 160 * 1024, "LDS");
 static_assert(kCopies < 16, "a vmcnt immediate below 16");
 
+template <bool MASK>   // as for the 128 x 128 kernel
 __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, int64_t tiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
   const int lane = threadIdx.x & 63;
@@ -613,14 +632,28 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, 
       f4 sum = *(const f4*)(partials + off);
 #pragma unroll
       for (int v = 1; v < 4; ++v) sum += *(const f4*)(partials + v * kPartial + off);
-      float* c = p.C + (int64_t)(m0 + row) * p.ldc + n0 + 4 * chunk;
-      f4 out = alpha * sum;
-      if (beta != 0.f) {
-        const f4 old = *(const f4*)c;
+      const int m = m0 + row, n = n0 + 4 * chunk;
+      float* c = p.C + (int64_t)m * p.ldc + n;
+      if constexpr (MASK) {
+        if (m < p.m_out) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, old[e], out[e]);
+          for (int e = 0; e < 4; ++e) {
+            if (n + e < p.n_out) {
+              float out = alpha * sum[e];
+              if (beta != 0.f) out = fmaf(beta, c[e], out);
+              c[e] = out;
+            }
+          }
+        }
+      } else {
+        f4 out = alpha * sum;
+        if (beta != 0.f) {
+          const f4 old = *(const f4*)c;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, old[e], out[e]);
+        }
+        *(f4*)c = out;
       }
-      *(f4*)c = out;
     }
   }
 }
@@ -640,6 +673,24 @@ hipError_t launch_tiled(const F32Args& a, hipStream_t stream) {
                       0, stream);
 }
 
+// The streaming kernels over a.M x a.N (multiples of 64; a.K of 64): 128 x 128
+// tiles where there are at least as many as CUs, 64 x 64 otherwise.  One
+// persistent workgroup per CU.
+template <bool MASK>
+hipError_t launch_stream(const F32Args& a, int cus, hipStream_t stream) {
+  const bool big = !small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0;
+  const int bt = big ? stream::BM : stream64::BT;
+  const int64_t tiles = (int64_t)(a.M / bt) * (a.N / bt);
+  const int64_t grid = tiles < cus ? tiles : cus;
+  F32Args p = a;
+  int64_t t = tiles;
+  void* args[] = {&p, &t};
+  const void* kernel = big ? (const void*)stream::sgemm_stream_kernel<MASK>
+                           : (const void*)stream64::sgemm_stream64_kernel<MASK>;
+  static_assert(stream::kThreads == stream64::kThreads, "one block size");
+  return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(stream::kThreads), args, 0, stream);
+}
+
 }  // namespace
 
 bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -648,36 +699,33 @@ bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
          aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0;
 }
 
+// The streaming kernels' lane offsets (3 rows into A or B, in bytes) must fit
+// in 32 bits.
+constexpr int64_t kStreamMaxLd = int64_t(1) << 28;
+
+bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                     const void* C, int64_t ldc) {
+  return f32_mfma_fits(M, N, K, A, lda, B, ldb, C, ldc) && K % 64 == 0 && lda < kStreamMaxLd &&
+         ldb < kStreamMaxLd;
+}
+
+bool f32_operand_fits(const void* X, int64_t ld) {
+  return aligned16(X) && ld % 4 == 0 && ld < kStreamMaxLd;
+}
+
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
-  if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0) {
-    // The streaming kernel's lane offsets (3 rows into A or 1 row into B, in
-    // bytes) must fit in 32 bits.
-    constexpr int64_t kMaxLd = int64_t(1) << 28;
-    if (a.K % stream::BKS == 0 && a.lda < kMaxLd && a.ldb < kMaxLd) {
-      const int64_t tiles = (int64_t)(a.M / stream::BM) * (a.N / stream::BN);
-      const int64_t grid = tiles < cus ? tiles : cus;
-      F32Args p = a;
-      int64_t t = tiles;
-      void* args[] = {&p, &t};
-      return hipLaunchKernel((const void*)stream::sgemm_stream_kernel, dim3((unsigned)grid),
-                             dim3(stream::kThreads), args, 0, stream);
-    }
+  if (f32_stream_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc))
+    return launch_stream<false>(a, cus, stream);
+  if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0)
     return launch_tiled<128, 128, false>(a, stream);
-  }
-  constexpr int64_t kMaxLd = int64_t(1) << 28;
-  if (a.K % stream64::BKS == 0 && a.lda < kMaxLd && a.ldb < kMaxLd) {
-    const int64_t tiles = (int64_t)(a.M / stream64::BT) * (a.N / stream64::BT);
-    const int64_t grid = tiles < cus ? tiles : cus;
-    F32Args p = a;
-    int64_t t = tiles;
-    void* args[] = {&p, &t};
-    return hipLaunchKernel((const void*)stream64::sgemm_stream64_kernel, dim3((unsigned)grid),
-                           dim3(stream64::kThreads), args, 0, stream);
-  }
   // The small tiles run one workgroup per CU; 32-deep slabs halve their
   // barriers (1024^3: 28 us against 30 us).
   if (a.K % 32 == 0) return launch_tiled<64, 64, false, 32>(a, stream);
   return launch_tiled<64, 64, false>(a, stream);
+}
+
+hipError_t launch_f32_mfma_masked(const F32Args& a, int cus, hipStream_t stream) {
+  return launch_stream<true>(a, cus, stream);
 }
 
 hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream) {

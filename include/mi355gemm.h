@@ -10,14 +10,17 @@
  *    offsets are computed in 64 bits.
  *  - A, B and C are DEVICE pointers, allocated and owned by the caller.  The
  *    library keeps no pointer to them after the call returns.  It allocates
- *    nothing, with one exception: when gemm_f32, gemm_f16_nt or
- *    gemm_f16_nt_ex choose split-K (GEMM_PATH_*_SPLITK), they need an fp32
- *    workspace, which the library takes from the stream-ordered allocator
- *    (hipMallocAsync on the call's stream) and keeps for later calls on the
- *    same device and stream, growing it when a larger one is needed, until
- *    the process ends.  Under stream capture the workspace is allocated and
- *    returned inside the captured work instead.  gemm_f32_splitk /
- *    gemm_f16_nt_splitk take a caller-owned workspace and allocate nothing.
+ *    nothing except a workspace on the paths that need one: split-K
+ *    (GEMM_PATH_*_SPLITK: fp32 partial sums), the padded paths
+ *    (GEMM_PATH_*_PADDED: zero-padded copies of A and/or B) and gemm_ex's
+ *    transposed operand copies.  The library takes it from the
+ *    stream-ordered allocator (hipMallocAsync on the call's stream) and keeps
+ *    it for later calls on the same device and stream, growing it when a
+ *    larger one is needed, until the process ends.  Under stream capture the
+ *    workspace is allocated and returned inside the captured work instead.
+ *    gemm_f32_splitk / gemm_f16_nt_splitk take a caller-owned workspace and
+ *    allocate nothing (where those calls do not split, they run the kernels
+ *    that need no workspace).
  *    A kept workspace is tied to the stream handle: destroying a stream
  *    while its work still runs and creating one that reuses the handle is
  *    not supported.
@@ -263,9 +266,12 @@ enum {
                                 /*   streams the long operand once (any ld/align) */
   GEMM_PATH_F16_SPLITK = 8,     /* few output tiles, long K: K cut into ranges,   */
   GEMM_PATH_F32_SPLITK = 9,     /*   fp32 partials, ordered reduction             */
-  GEMM_PATH_F16_PADDED = 10     /* large ragged or unaligned: A / B copied into   */
+  GEMM_PATH_F16_PADDED = 10,    /* large ragged or unaligned: A / B copied into   */
                                 /*   zero-padded aligned rows where needed, full  */
                                 /*   tiles with masked stores                     */
+  GEMM_PATH_F32_PADDED = 11     /* the same for fp32 (at least 2^30 multiply-adds */
+                                /*   that the fp32 full tiles cannot read in      */
+                                /*   place, or whose K is not a multiple of 64)   */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,

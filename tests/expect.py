@@ -25,11 +25,16 @@ def splitk_auto(M, N, K, slab):
 
 
 def expected_f32_path(mode, M, N, K):
+    """For contiguous, 16-byte aligned operands."""
     if mode == "general":
         return "f32_general"
     if splitk_auto(M, N, K, 16):
         return "f32_splitk"
-    return "f32_mfma" if (M % 64 == 0 and N % 64 == 0 and K % 16 == 0) else "f32_general"
+    tiles = M % 64 == 0 and N % 64 == 0 and K % 16 == 0
+    pays = M * N * K >= 1 << 30
+    if (tiles and K % 64 == 0) or (tiles and not pays):
+        return "f32_mfma"
+    return "f32_padded" if pays else "f32_general"
 
 
 def expected_f16_path(mode, M, N, K):

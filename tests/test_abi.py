@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
 F32_MFMA, F32_GENERAL, F32_SCALE = 3, 2, 1
 F16_MFMA, F16_GENERAL, F16_ZERO, F16_GEMV = 6, 5, 4, 7
-F16_SPLITK, F32_SPLITK, F16_PADDED = 8, 9, 10
+F16_SPLITK, F32_SPLITK, F16_PADDED, F32_PADDED = 8, 9, 10, 11
 ALIGNED = 0x100000          # fake device addresses: only their alignment is looked at
 p = ctypes.c_void_p
 
@@ -149,10 +149,16 @@ def test_path_selection(lib, monkeypatch):
     assert f32(lib, 4096, 4096, 4096) == F32_MFMA
     assert f32(lib, 256, 256, 256) == F32_MFMA and f32(lib, 1024, 1024, 1024) == F32_MFMA
     assert f32(lib, 4096, 4096, 4096, beta=0.5) == F32_MFMA
-    assert f32(lib, 4000, 4096, 4096) == F32_GENERAL                # ragged M
+    assert f32(lib, 4000, 4096, 4096) == F32_PADDED                 # ragged M, large
     assert f32(lib, 4032, 4096, 4096) == F32_MFMA                   # 64-row tiles
     assert f32(lib, 192, 320, 48) == F32_MFMA
-    assert f32(lib, 4096, 4096, 4096, A=ALIGNED + 4) == F32_GENERAL  # 4-byte aligned only
+    assert f32(lib, 4096, 4096, 4096, A=ALIGNED + 4) == F32_PADDED   # 4-byte aligned only
+    assert f32(lib, 4096, 4096, 4096, C=ALIGNED + 4) == F32_PADDED   # no copy, masked stores
+    assert f32(lib, 4096, 4096, 4000) == F32_PADDED                 # K not a multiple of 64
+    assert f32(lib, 2000, 2000, 2000) == F32_PADDED
+    assert f32(lib, 1024, 1024, 1008) == F32_MFMA                   # below 2^30: 16-deep slabs
+    assert f32(lib, 1000, 1000, 1000) == F32_GENERAL                # below 2^30, ragged
+    assert f32(lib, 4096, 4096, 4096, lda=1 << 28) == F32_PADDED    # 32-bit lane offsets
     assert f32(lib, 256, 256, 256, lda=258) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_MFMA
     # ragged or unaligned and large: copies where needed, masked full tiles

@@ -869,6 +869,59 @@ def test_f32_stream64_alpha_beta_padded_and_exact():
     assert np.array_equal(gpu_f32(Ai, Bi, expect="f32_mfma").astype(np.float64), oracle.gemm_f32(Ai, Bi))
 
 
+# The padded fp32 path: at least 2^30 multiply-adds that the streaming kernels
+# cannot read in place.  1030 x 1100 x 1000: ragged M, N and K, 64 x 64 tiles
+# (fewer 128 x 128 tiles than CUs), both operands copied; 2048 x 2048 x 2000:
+# K not a multiple of 64, 128 x 128 tiles; 2000^3: ragged everything on
+# 128 x 128 tiles.  The masked stores leave C outside M x N untouched.
+PADDED32_SHAPES = [(1030, 1100, 1000), (2048, 2048, 2000), (2000, 2000, 2000)]
+
+
+@pytest.mark.parametrize("shape", PADDED32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_padded_path(shape):
+    M, N, K = shape
+    A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
+    dA, dB = dev(A), dev(B)
+    big = torch.full((M + 3, N + 5), 7.0, device=DEV)
+    dC = big[1:1 + M, 2:2 + N]                 # C not 16-byte aligned, odd leading dimension
+    dC.copy_(dev(C))
+    assert dg.f32_path(dA, dB, dC, 0.75, 0.5) == "f32_padded"
+    dg.gemm_f32(dA, dB, dC, 0.75, 0.5)
+    torch.cuda.synchronize()
+    got = big.cpu().numpy()
+    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128), n_random=5000)
+    ref = oracle.gemm_f32_points(A, B, rows, cols, 0.75, 0.5, C)
+    f32_check(got[1:1 + M, 2:2 + N][rows, cols], ref, f32_tolerance(K, 1.0, 1.0, 0.75, 0.5, 1.0))
+    outside = np.ones(got.shape, bool)
+    outside[1:1 + M, 2:2 + N] = False
+    assert np.all(got[outside] == 7.0)
+
+
+def test_f32_padded_path_copy_one_or_none():
+    """A starting one float into its buffer (only A is copied), then aligned
+    operands with an unaligned C (no copies: the masked kernel reads A and B
+    in place); small integers make both results exact."""
+    M, N, K = 1024, 1024, 1024
+    A = inputs.small_ints((M, K), 21, -3, 3, np.float32)
+    B = inputs.small_ints((K, N), 22, -3, 3, np.float32)
+    ref = oracle.gemm_f32(A, B)
+    bufA = torch.zeros(M * K + 1, device=DEV)
+    dA = bufA[1:].view(M, K)
+    dA.copy_(dev(A))
+    dC = torch.full((M, N), float("nan"), device=DEV)
+    assert dg.f32_path(dA, dev(B), dC) == "f32_padded"
+    dg.gemm_f32(dA, dev(B), dC)
+    torch.cuda.synchronize()
+    assert np.array_equal(dC.cpu().numpy().astype(np.float64), ref)
+    bufC = torch.full((M * N + 1,), float("nan"), device=DEV)
+    dC2 = bufC[1:].view(M, N)
+    assert dg.f32_path(dev(A), dev(B), dC2) == "f32_padded"
+    dg.gemm_f32(dev(A), dev(B), dC2)
+    torch.cuda.synchronize()
+    assert np.array_equal(dC2.cpu().numpy().astype(np.float64), ref)
+    assert np.isnan(bufC[0].item())
+
+
 def test_f32_stream_fallback_k_not_a_multiple_of_64():
     """K % 64 != 0 keeps the register-staged 128 x 128 kernel."""
     M, N, K = 2048, 2048, 80

@@ -838,8 +838,11 @@ def test_f32_stream_alpha_beta_padded_and_exact():
 # tiles than CUs (or not multiples of 128), K a multiple of 64.  64^3: a
 # stream of one slab; 64 x 128 x 128: two workgroups of two slabs; 192 x 64 x
 # 320: odd slab counts; 1088 x 1024 x 192: 272 tiles, so some workgroups
-# reduce two tiles in turn.  Compared element by element with the oracle.
-STREAM64_SHAPES = [(64, 64, 64), (64, 128, 128), (192, 64, 320), (1088, 1024, 192), (512, 768, 1024)]
+# reduce two tiles in turn; 32768 x 64 x 64 and 16384 x 128 x 128: 512 tiles
+# of one or two slabs, two per workgroup (a reduction barrier every slab or
+# two).  Compared element by element with the oracle.
+STREAM64_SHAPES = [(64, 64, 64), (64, 128, 128), (192, 64, 320), (1088, 1024, 192), (512, 768, 1024),
+                   (32768, 64, 64), (16384, 128, 128)]
 
 
 @pytest.mark.parametrize("shape", STREAM64_SHAPES, ids=lambda s: "x".join(map(str, s)))

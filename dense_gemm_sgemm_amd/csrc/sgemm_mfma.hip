@@ -221,9 +221,10 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
 }
 
 // ---------------------------------------------------------------------------
-// The streaming kernel for large fp32 products (M, N multiples of 128, K a
-// multiple of 64): one persistent 512-thread workgroup per CU walks its
-// 128 x 128 tiles as one stream of 64-deep K slabs.
+// The streaming kernel for large fp32 products (M, N multiples of 128 with
+// at least as many 128 x 128 tiles as CUs, K a multiple of 64): one
+// persistent 512-thread workgroup per CU walks its 128 x 128 tiles as one
+// stream of 64-deep K slabs.
 //
 //  * waves 0-3 (one per SIMD) compute: each owns 64 x 64 of the tile, 16
 //    blocks of v_mfma_f32_16x16x4_f32 with 16 accumulators in rotation;
@@ -454,9 +455,10 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
 }
 }  // namespace stream
 
-// The streaming kernel for mid-size products (M, N multiples of 64 with
-// fewer 128 x 128 tiles than CUs, K a multiple of 64): 64 x 64 tiles, so that
-// every CU gets work, with the structure of the kernel above -- one
+// The streaming kernel for the products the 128 x 128 kernel does not take
+// (M, N multiples of 64 with fewer 128 x 128 tiles than CUs, or not multiples
+// of 128; K a multiple of 64): 64 x 64 tiles, so that mid-size products give
+// every CU work, with the structure of the kernel above -- one
 // persistent 512-thread workgroup per CU, 4 computing and 4 copying waves,
 // direct-to-LDS copies of 64-deep slabs in the scalar-base form.  A 64 x 64
 // tile split four ways would leave each wave 4 accumulators, too few to cover
@@ -477,7 +479,8 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
 //  * after a tile's last slab each computing wave stores its partial tile,
 //    all eight waves meet (the copying waves count the slabs of each tile),
 //    and computing wave w adds the four partials of rows 16 w .. 16 w + 15
-//    and writes them to C, 16 bytes per lane.
+//    and writes them to C, 16 bytes per lane (MASK instances: element by
+//    element inside p.m_out x p.n_out).
 namespace stream64 {
 constexpr int BT = 64, BKS = 64;
 constexpr int kStage = 2 * BT * BKS * 4;    // A and B of one slab: 32 KiB

@@ -228,7 +228,9 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
 //
 //  * waves 0-3 (one per SIMD) compute: each owns 64 x 64 of the tile, 16
 //    blocks of v_mfma_f32_16x16x4_f32 with 16 accumulators in rotation;
-//  * waves 4-7 only copy: every slab of A (128 x 64) and B (64 x 128) goes
+//  * waves 4-7 only copy -- the producer / consumer split of the page "第 6 章
+//    Shared Memory & Tile" (section 6.10.1), with the workgroup barrier in
+//    place of mbarriers: every slab of A (128 x 64) and B (64 x 128) goes
 //    global -> LDS with global_load_lds_dwordx4 into a two-stage ring
 //    (2 x 64 KiB), one barrier per slab.  A copying wave shares its SIMD with
 //    a computing wave, so its copies carry no vector address arithmetic: the

@@ -284,14 +284,22 @@ __device__ __forceinline__ const char* uniform_ptr(const char* q) {
 
 // One direct-to-LDS copy: lane i loads 16 bytes from sbase + voff and they
 // land at dst + 16 i.  Written out so that the scalar-base form is the one
-// issued; M0 (the LDS destination) is set here, one wait state ahead of the
-// copy as the hardware requires.  Completion is the caller's explicit
-// vmcnt wait.
+// issued.  M0 (the LDS destination, read when the copy issues) is set here
+// one wait state ahead of the copy, as the hardware requires, and restored
+// after it, since the compiler reserves M0 and does not track a change made
+// inside an asm statement.  Completion is the caller's explicit vmcnt wait.
 __device__ __forceinline__ void copy16(const char* sbase, uint32_t voff, lds_void_t* dst) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(sbase), "s"(m0v)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(m0v)
+      : "memory");
 }
 
 constexpr int kWaitVmLgkm0 = 0x0070;   // s_waitcnt vmcnt(0) lgkmcnt(0)

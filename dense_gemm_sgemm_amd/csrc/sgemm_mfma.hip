@@ -264,15 +264,7 @@ constexpr int kCopies = 64 / kCopiers;   // copy instructions per copying wave p
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()).
-template <typename F, int... Q>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Q...>) {
-  (f(std::integral_constant<int, Q>()), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>());
-}
+using hgemm::static_for;   // compile-time loop indices (hgemm_tile.hpp)
 
 // A wave-uniform pointer, held in scalar registers.
 __device__ __forceinline__ const char* uniform_ptr(const char* q) {
@@ -610,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, 
       asm volatile("s_barrier" ::: "memory");   // B_gs
       const unsigned char* nxt = lds + ((gs + 1) % kStages) * kStage;
       __builtin_amdgcn_sched_barrier(0);
-      stream::static_for<64>([&](auto mc) __attribute__((always_inline)) {
+      hgemm::static_for<64>([&](auto mc) __attribute__((always_inline)) {
         constexpr int m = decltype(mc)::value;
         constexpr int s = m / 16, i = (m % 16) / 4, j = m % 4;
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[0][s][j], av[0][i][s], acc[i][j], 0, 0, 0);

@@ -4,10 +4,12 @@
 // layout once so that neighbouring threads read neighbouring elements; here
 // the copy goes the other way, into the layout the matrix-core kernels read.
 //
-// dst[c * ldd + r] = src[r * lds + c] for r < rows, c < cols, in 64 x 64 tiles
-// through LDS: each thread reads 16 bytes of a source row (8 consecutive
-// columns) and writes 16 bytes of a destination row (8 consecutive source
-// rows), so both sides of HBM see whole 128-byte row segments.  The
+// dst[c * ldd + r] = src[r * lds + c] for r < rows, c < cols, one 64 x 64 tile
+// per wave and no LDS: lane (i, j) = (l / 8, l % 8) loads the 8 x 8 block at
+// source rows 8 i .. 8 i + 7 and columns 8 j .. 8 j + 7 of its tile as eight
+// 16-byte row pieces, transposes it in registers, and stores it as eight
+// 16-byte pieces of destination rows 8 j .. 8 j + 7.  Every load and store
+// instruction of a wave covers 8 rows x 128 contiguous bytes.  The
 // destination may be padded: every element of its rows_p x cols_p extent
 // (source orientation) is written, zero outside the source matrix, which is
 // never read outside.
@@ -23,9 +25,10 @@ namespace {
 
 constexpr int kT = 64;
 constexpr int kThreads = 256;
-constexpr int kPad = 2;   // LDS row = 66 words: 8 consecutive rows of one column fall in 2-way banks
+constexpr int kWaves = kThreads / 64;   // transpose tiles per workgroup
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct TransposeArgs {
   const half_t* src;
@@ -35,51 +38,60 @@ struct TransposeArgs {
   int rows_p, cols_p;   // the extent written (>= rows, cols)
 };
 
-__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs p, int64_t tile_base) {
-  __shared__ half_t tile[kT][kT + kPad];
-  const int t = threadIdx.x;
-  const int tiles_c = (p.cols_p + kT - 1) / kT;
-  const int64_t idx = tile_base + blockIdx.x;
-  const int r0 = (int)(idx / tiles_c) * kT, c0 = (int)(idx % tiles_c) * kT;
-
-  // Source rows r0 + t / 8 + 32 i, columns c0 + 8 (t % 8) .. + 7.
+// One lane's 8 x 8 block: source rows r0 .. r0 + 7, columns c0 .. c0 + 7.
+// INSIDE: the wave's whole tile lies inside the source matrix (hence inside
+// the written extent) and takes whole 16-byte pieces; edge tiles check every
+// row and element.
+template <bool INSIDE>
+__device__ __forceinline__ void transpose_block(const TransposeArgs& p, int r0, int c0) {
+  // x[e] word q: source row r0 + e, columns c0 + 2q (low half) and c0 + 2q + 1.
+  u32x4 x[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = t / 8 + 32 * i, c = 8 * (t % 8);
+  for (int e = 0; e < 8; ++e) {
+    const half_t* s = p.src + (int64_t)(r0 + e) * p.lds + c0;
     h8 v = {};
-    if (r0 + r < p.rows && c0 + c < p.cols) {
-      const half_t* s = p.src + (int64_t)(r0 + r) * p.lds + c0 + c;
-      if (c0 + c + 8 <= p.cols) {
-        __builtin_memcpy(&v, s, 16);
-      } else {
+    if (INSIDE) {
+      __builtin_memcpy(&v, s, 16);
+    } else if (r0 + e < p.rows) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (c0 + c + e < p.cols) v[e] = s[e];
-      }
+      for (int k = 0; k < 8; ++k)
+        if (c0 + k < p.cols) v[k] = s[k];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[r][c + e] = v[e];
+    x[e] = __builtin_bit_cast(u32x4, v);
   }
-  __syncthreads();
-
-  // Destination rows c0 + t / 8 + 32 i (source columns), 8 source rows from
-  // r0 + 8 (t % 8).
+  // Destination row c0 + k holds source column c0 + k: word q of it pairs
+  // rows r0 + 2q (low half) and r0 + 2q + 1.
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int c = t / 8 + 32 * i, r = 8 * (t % 8);
-    if (c0 + c >= p.cols_p || r0 + r >= p.rows_p) continue;
-    h8 v;
+  for (int k = 0; k < 8; ++k) {
+    const int sh = 16 * (k & 1);
+    u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[r + e][c];
-    half_t* d = p.dst + (int64_t)(c0 + c) * p.ldd + r0 + r;
-    if (r0 + r + 8 <= p.rows_p) {
-      __builtin_memcpy(d, &v, 16);
-    } else {
+    for (int q = 0; q < 4; ++q)
+      w[q] = ((x[2 * q][k >> 1] >> sh) & 0xFFFFu) | (((x[2 * q + 1][k >> 1] >> sh) & 0xFFFFu) << 16);
+    half_t* d = p.dst + (int64_t)(c0 + k) * p.ldd + r0;
+    if (INSIDE) {
+      __builtin_memcpy(d, &w, 16);
+    } else if (c0 + k < p.cols_p) {
+      const h8 v = __builtin_bit_cast(h8, w);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (r0 + r + e < p.rows_p) d[e] = v[e];
+        if (r0 + e < p.rows_p) d[e] = v[e];
     }
   }
+}
+
+__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs p, int64_t block_base) {
+  const int lane = threadIdx.x & 63;
+  const int tiles_c = (p.cols_p + kT - 1) / kT;
+  const int64_t tiles = (int64_t)((p.rows_p + kT - 1) / kT) * tiles_c;
+  const int64_t idx = (block_base + blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (idx >= tiles) return;
+  const int tr = (int)(idx / tiles_c) * kT, tc = (int)(idx % tiles_c) * kT;
+  const int r0 = tr + 8 * (lane >> 3), c0 = tc + 8 * (lane & 7);
+  if (tr + kT <= p.rows && tc + kT <= p.cols)
+    transpose_block<true>(p, r0, c0);
+  else
+    transpose_block<false>(p, r0, c0);
 }
 
 // Two padding copies in one launch: blocks below split_block copy `first`,
@@ -178,7 +190,8 @@ hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols
   if (rows_p <= 0 || cols_p <= 0) return hipSuccess;
   const TransposeArgs p{src, dst, lds, ldd, rows, cols, rows_p, cols_p};
   const int64_t tiles = (int64_t)((rows_p + kT - 1) / kT) * ((cols_p + kT - 1) / kT);
-  return launch_tiles((const void*)transpose16_kernel, p, tiles, kThreads, 0, stream);
+  return launch_tiles((const void*)transpose16_kernel, p, (tiles + kWaves - 1) / kWaves, kThreads,
+                      0, stream);
 }
 
 hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream) {

@@ -46,12 +46,13 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused",
-                                       "hgemv", "hgemm_splitk"],
+                                       "hgemv", "hgemm_splitk", "sgemm_256", "sgemm_1024"],
                     default="both",
                     help="time only one product (for profiling): one of the two step products, "
                          "the ragged 5000x3001x1537 fp16 product, the 5376^2 x 2048 product "
                          "with the fused bias + SiLU + residual write-back, the 1 x 16384 x "
-                         "4096 decode product, or the 128 x 128 x 16384 split-K product")
+                         "4096 decode product, the 128 x 128 x 16384 split-K product, or the "
+                         "256^3 or 1024^3 SGEMM")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -86,6 +87,7 @@ KERNEL_SOURCES[H_NAME + "_bias_silu_residual"] = KERNEL_SOURCES[H_NAME]
 KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sgemm_amd/csrc/internal.h",
                           "dense_gemm_sgemm_amd/build.py"]
 KERNEL_SOURCES[S_NAME] = KERNEL_SOURCES[H_NAME] + ["dense_gemm_sgemm_amd/csrc/splitk.hip"]
+KERNEL_SOURCES["sgemm_256"] = KERNEL_SOURCES["sgemm_1024"] = KERNEL_SOURCES[F_NAME]
 COPY_BYTES = 1 << 30
 # Bytes written between launches for the cold-cache figure: twice the 256 MB
 # last-level cache.
@@ -374,6 +376,14 @@ def main():
         assert dg.f16_nt_path(dAs, dBs, dCs) == "f16_splitk"
         parts.append((S_NAME, "f16", "hgemm_nt_edge_kernel", flops(sw),
                       lambda: dg.gemm_f16_nt(dAs, dBs, dCs)))
+    if args.only in ("sgemm_256", "sgemm_1024"):
+        sw = inputs.WORKLOADS[args.only]
+        As, Bs = inputs.sgemm_operands(sw["M"], sw["N"], sw["K"])[:2]
+        dAs, dBs = torch.from_numpy(As).to(dev), torch.from_numpy(Bs).to(dev)
+        dCs = torch.empty(sw["M"], sw["N"], device=dev, dtype=torch.float32)
+        assert dg.f32_path(dAs, dBs, dCs) == "f32_mfma"
+        parts.append((args.only, "f32", "sgemm_stream64_kernel", flops(sw),
+                      lambda: dg.gemm_f32(dAs, dBs, dCs, 1.0, 0.0)))
     if args.only in ("both", "sgemm"):
         Af, Bf = operand_values(args.operands, *inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])[:2])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)

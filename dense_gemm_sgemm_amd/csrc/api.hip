@@ -385,17 +385,19 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
   hipError_t e = hipSuccess;
   const bool padded = pl.path == GEMM_PATH_F16_PADDED;
   // Transposed copies: A is [K][lda] (its transpose is op(A), M x K), B is
-  // [K][ldb] (its transpose is B^T stored N x K).  Plain padding copies of
-  // both operands share one launch.
+  // [K][ldb] (its transpose is B^T stored N x K).  The transpositions of both
+  // operands share one launch, and so do plain padding copies.
   half_t* dst_a = reinterpret_cast<half_t*>(ws);
   half_t* dst_b = reinterpret_cast<half_t*>(ws + bytes_a);
   const PadCopy pad_a{a.A, dst_a, a.lda, pl.lda, a.M, a.K, pl.Mp, pl.Kp};
   const PadCopy pad_b{a.B, dst_b, a.ldb, pl.ldb, a.N, a.K, pl.Np, pl.Kp};
   const bool plain_a = pl.copy_a && op_a == GEMM_OP_N, plain_b = pl.copy_b && op_b == GEMM_OP_T;
-  if (pl.copy_a && !plain_a)
-    e = launch_transpose16(a.A, a.lda, a.K, a.M, dst_a, pl.lda, s, pl.Kp, pl.Mp);
-  if (e == hipSuccess && pl.copy_b && !plain_b)
-    e = launch_transpose16(a.B, a.ldb, a.K, a.N, dst_b, pl.ldb, s, pl.Kp, pl.Np);
+  const PadCopy tr_a{a.A, dst_a, a.lda, pl.lda, a.K, a.M, pl.Kp, pl.Mp};
+  const PadCopy tr_b{a.B, dst_b, a.ldb, pl.ldb, a.K, a.N, pl.Kp, pl.Np};
+  const bool trans_a = pl.copy_a && !plain_a, trans_b = pl.copy_b && !plain_b;
+  if (trans_a || trans_b)
+    e = trans_a ? launch_transpose16(tr_a, trans_b ? &tr_b : nullptr, s)
+                : launch_transpose16(tr_b, nullptr, s);
   if (e == hipSuccess && (plain_a || plain_b))
     e = plain_a ? launch_pad16(pad_a, plain_b ? &pad_b : nullptr, s) : launch_pad16(pad_b, nullptr, s);
   if (pl.copy_a) a.A = dst_a;

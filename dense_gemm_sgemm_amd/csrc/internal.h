@@ -130,11 +130,6 @@ hipError_t launch_f16_gemv_kn(const Args16& a, int op_a, int op_b, bool epi, con
                               void* workspace, hipStream_t stream);
 // The split-K reduction alone: a.sk names the partial sums.
 hipError_t launch_f16_reduce(const Args16& a, bool epi, hipStream_t stream);
-// dst[c * ldd + r] = src[r * lds + c] for a rows x cols matrix of 16-bit words;
-// the destination's rows_p x cols_p extent (source orientation) is written,
-// zero outside the source.
-hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols, half_t* dst,
-                              int64_t ldd, hipStream_t stream, int rows_p = 0, int cols_p = 0);
 // A padding copy: dst[r * ldd + k] = src[r * lds + k] inside rows x cols,
 // zero elsewhere in rows_p x cols_p (cols_p and ldd multiples of 8, dst
 // 16-byte aligned).  launch_pad16 runs one or two of them in one launch.
@@ -145,6 +140,11 @@ struct PadCopy {
   int rows, cols, rows_p, cols_p;
 };
 hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
+// A transposition with the same fields: dst[c * ldd + r] = src[r * lds + c]
+// for the rows x cols source; the destination's rows_p x cols_p extent
+// (source orientation) is written, zero outside the source.  One or two of
+// them in one launch.
+hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
 // The same for fp32 matrices (cols_p and ldd multiples of 4, dst 16-byte
 // aligned).
 struct PadCopy32 {

@@ -38,6 +38,13 @@ struct TransposeArgs {
   int rows_p, cols_p;   // the extent written (>= rows, cols)
 };
 
+// Two copies in one launch (transpositions or padding copies): blocks below
+// split_block copy `first`, the others `second`.
+struct PadPair {
+  TransposeArgs first, second;
+  int64_t split_block;
+};
+
 // One lane's 8 x 8 block: source rows r0 .. r0 + 7, columns c0 .. c0 + 7.
 // INSIDE: the wave's whole tile lies inside the source matrix (hence inside
 // the written extent) and takes whole 16-byte pieces; edge tiles check every
@@ -80,11 +87,20 @@ __device__ __forceinline__ void transpose_block(const TransposeArgs& p, int r0, 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs p, int64_t block_base) {
+int64_t transpose_blocks(int rows_p, int cols_p) {
+  const int64_t tiles = (int64_t)((rows_p + kT - 1) / kT) * ((cols_p + kT - 1) / kT);
+  return (tiles + kWaves - 1) / kWaves;
+}
+
+__global__ __launch_bounds__(kThreads) void transpose16_kernel(PadPair pair, int64_t block_base) {
+  int64_t block = block_base + blockIdx.x;
+  const bool first = block < pair.split_block;
+  const TransposeArgs& p = first ? pair.first : pair.second;
+  if (!first) block -= pair.split_block;
   const int lane = threadIdx.x & 63;
   const int tiles_c = (p.cols_p + kT - 1) / kT;
   const int64_t tiles = (int64_t)((p.rows_p + kT - 1) / kT) * tiles_c;
-  const int64_t idx = (block_base + blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t idx = block * kWaves + (threadIdx.x >> 6);
   if (idx >= tiles) return;
   const int tr = (int)(idx / tiles_c) * kT, tc = (int)(idx % tiles_c) * kT;
   const int r0 = tr + 8 * (lane >> 3), c0 = tc + 8 * (lane & 7);
@@ -93,13 +109,6 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(TransposeArgs p, 
   else
     transpose_block<false>(p, r0, c0);
 }
-
-// Two padding copies in one launch: blocks below split_block copy `first`,
-// the others `second`.
-struct PadPair {
-  TransposeArgs first, second;
-  int64_t split_block;
-};
 
 __device__ __forceinline__ void pad16_block(const TransposeArgs& p, int64_t block) {
   const int chunks = p.cols_p / 8;   // per destination row
@@ -183,15 +192,23 @@ int64_t pad32_blocks(int rows_p, int cols_p) {
 
 }  // namespace
 
-hipError_t launch_transpose16(const half_t* src, int64_t lds, int rows, int cols, half_t* dst,
-                              int64_t ldd, hipStream_t stream, int rows_p, int cols_p) {
-  if (rows_p < rows) rows_p = rows;
-  if (cols_p < cols) cols_p = cols;
-  if (rows_p <= 0 || cols_p <= 0) return hipSuccess;
-  const TransposeArgs p{src, dst, lds, ldd, rows, cols, rows_p, cols_p};
-  const int64_t tiles = (int64_t)((rows_p + kT - 1) / kT) * ((cols_p + kT - 1) / kT);
-  return launch_tiles((const void*)transpose16_kernel, p, (tiles + kWaves - 1) / kWaves, kThreads,
-                      0, stream);
+hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipStream_t stream) {
+  auto args = [](const PadCopy& c) {
+    return TransposeArgs{c.src, c.dst, c.lds, c.ldd, c.rows, c.cols,
+                         c.rows_p > c.rows ? c.rows_p : c.rows, c.cols_p > c.cols ? c.cols_p : c.cols};
+  };
+  PadPair p;
+  p.first = args(first);
+  p.split_block = transpose_blocks(p.first.rows_p, p.first.cols_p);
+  int64_t blocks = p.split_block;
+  if (second) {
+    p.second = args(*second);
+    blocks += transpose_blocks(p.second.rows_p, p.second.cols_p);
+  } else {
+    p.second = p.first;
+  }
+  if (blocks <= 0) return hipSuccess;
+  return launch_tiles((const void*)transpose16_kernel, p, blocks, kThreads, 0, stream);
 }
 
 hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream) {

@@ -179,18 +179,28 @@ def splitk_workspace_bytes(kind: str, M: int, N: int, K: int, splits: int = 0) -
     return int(fn(int(M), int(N), int(K), int(splits)))
 
 
-def _workspace(workspace, need: int, device):
-    """(pointer, bytes) of a caller's workspace tensor, or of a new one."""
+def _workspace(workspace, need: int, device, stream=None):
+    """(pointer, bytes, tensor) of a caller's workspace tensor, or of a new one.
+
+    A new one comes from torch's caching allocator on the stream the kernels
+    will run on (``stream``, default the current one): the tensor is dropped
+    when the call returns, and the allocator hands its block only to later
+    allocations on that same stream, which are ordered after the kernels that
+    use it."""
     torch = _torch_module()
     if workspace is None:
         if need == 0:
-            return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+            return None, 0, None
+        if stream is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        else:
+            with torch.cuda.stream(stream):
+                workspace = torch.empty(need, dtype=torch.uint8, device=device)
     if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda" or \
             not workspace.is_contiguous():
         raise TypeError("workspace must be a contiguous GPU tensor")
     nbytes = workspace.numel() * workspace.element_size()
-    return (workspace.data_ptr() if nbytes else None), nbytes
+    return (workspace.data_ptr() if nbytes else None), nbytes, workspace
 
 
 def gemm_f32_splitk(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0,
@@ -205,7 +215,8 @@ def gemm_f32_splitk(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int 
     if K2 != K or M2 != M or N2 != N:
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
                                                                tuple(C.shape)))
-    pw, nw = _workspace(workspace, splitk_workspace_bytes("f32", M, N, K, splits), C.device)
+    pw, nw, _ws = _workspace(workspace, splitk_workspace_bytes("f32", M, N, K, splits), C.device,
+                             stream)
     _check(load_library().gemm_f32_splitk(M, N, K, float(alpha), pa, lda, pb, ldb, float(beta),
                                           pc, ldc, int(splits), pw, nw, _stream(stream)))
     return C
@@ -222,7 +233,8 @@ def gemm_f16_nt_splitk(A, B, C, splits: int = 0, workspace=None, stream=None):
     if K2 != K or M2 != M or N2 != N:
         raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
                                                                tuple(C.shape)))
-    pw, nw = _workspace(workspace, splitk_workspace_bytes("f16", M, N, K, splits), C.device)
+    pw, nw, _ws = _workspace(workspace, splitk_workspace_bytes("f16", M, N, K, splits), C.device,
+                             stream)
     _check(load_library().gemm_f16_nt_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, int(splits), pw,
                                              nw, _stream(stream)))
     return C

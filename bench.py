@@ -79,9 +79,8 @@ KERNEL_SOURCES = {
              "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
     F_NAME: ["dense_gemm_sgemm_amd/csrc/sgemm_mfma.hip", "dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp",
              "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
-    R_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_mfma.hip",
-             "dense_gemm_sgemm_amd/csrc/transpose.hip", "dense_gemm_sgemm_amd/csrc/internal.h",
-             "dense_gemm_sgemm_amd/build.py"],
+    R_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_staged.hip",
+             "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
 }
 KERNEL_SOURCES[H_NAME + "_bias_silu_residual"] = KERNEL_SOURCES[H_NAME]
 KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sgemm_amd/csrc/internal.h",
@@ -352,8 +351,8 @@ def main():
         Ar, Br = inputs.workload_operands(R_NAME)
         dAr, dBr = torch.from_numpy(Ar).to(dev), torch.from_numpy(Br).to(dev)
         dCr = torch.empty(rw["M"], rw["N"], device=dev, dtype=torch.float16)
-        assert dg.f16_nt_path(dAr, dBr, dCr) == "f16_padded"
-        parts.append((R_NAME, "f16", "hgemm_nt_kernel (masked, on padded copies)", flops(rw),
+        assert dg.f16_nt_path(dAr, dBr, dCr) == "f16_staged"
+        parts.append((R_NAME, "f16", "hgemm_staged_kernel", flops(rw),
                       lambda: dg.gemm_f16_nt(dAr, dBr, dCr)))
     if args.only == "hgemm_fused":
         Ah, Bh = inputs.workload_operands(H_NAME)

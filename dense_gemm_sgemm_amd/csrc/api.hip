@@ -186,19 +186,13 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
   if (f16_mfma_fits(M, N, K, a_read, pl.lda, b_read, pl.ldb, C, ldc) &&
       (!epi || f16_epi_fits(bias, res, ldr)))
     return fail(GEMM_PATH_F16_MFMA);
-  // The masked full-tile kernel: copy what the tiles cannot read in place.
-  const bool k_ok = K % kF16Slab == 0;
-  const bool a_ok = !pl.copy_a && k_ok && M % 128 == 0 && f16_operand_fits(A, lda);
-  const bool b_ok = !pl.copy_b && k_ok && N % 128 == 0 && f16_operand_fits(B, ldb);
-  if ((!a_ok || !b_ok) && !padding_pays(M, N, K)) return fail(GEMM_PATH_F16_GENERAL);
-  pl.copy_a = !a_ok;
-  pl.copy_b = !b_ok;
-  pl.Kp = (int)round_up(K, kF16Slab);
-  pl.Mp = pl.copy_a ? (int)round_up(M, 128) : M;
-  pl.Np = pl.copy_b ? (int)round_up(N, 128) : N;
-  if (pl.copy_a) pl.lda = pl.Kp;
-  if (pl.copy_b) pl.ldb = pl.Kp;
-  return fail(GEMM_PATH_F16_PADDED);
+  // Large products the full tiles cannot take in place (ragged, unaligned
+  // rows, odd leading dimensions, C or the write-back operands unaligned):
+  // the register-staged kernel reads the operands (or their transposed
+  // copies) where they are.
+  if (padding_pays(M, N, K) && f16_staged_fits(M, N, K, pl.lda, pl.ldb))
+    return fail(GEMM_PATH_F16_STAGED);
+  return fail(GEMM_PATH_F16_GENERAL);
 }
 
 int f16_select(int M, int N, int K, const void* A, int lda, const void* B, int ldb, const void* C,
@@ -383,48 +377,35 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
     }
   }
   hipError_t e = hipSuccess;
-  const bool padded = pl.path == GEMM_PATH_F16_PADDED;
   // Transposed copies: A is [K][lda] (its transpose is op(A), M x K), B is
   // [K][ldb] (its transpose is B^T stored N x K).  The transpositions of both
-  // operands share one launch, and so do plain padding copies.
+  // operands share one launch.
   half_t* dst_a = reinterpret_cast<half_t*>(ws);
   half_t* dst_b = reinterpret_cast<half_t*>(ws + bytes_a);
-  const PadCopy pad_a{a.A, dst_a, a.lda, pl.lda, a.M, a.K, pl.Mp, pl.Kp};
-  const PadCopy pad_b{a.B, dst_b, a.ldb, pl.ldb, a.N, a.K, pl.Np, pl.Kp};
-  const bool plain_a = pl.copy_a && op_a == GEMM_OP_N, plain_b = pl.copy_b && op_b == GEMM_OP_T;
   const PadCopy tr_a{a.A, dst_a, a.lda, pl.lda, a.K, a.M, pl.Kp, pl.Mp};
   const PadCopy tr_b{a.B, dst_b, a.ldb, pl.ldb, a.K, a.N, pl.Kp, pl.Np};
-  const bool trans_a = pl.copy_a && !plain_a, trans_b = pl.copy_b && !plain_b;
-  if (trans_a || trans_b)
-    e = trans_a ? launch_transpose16(tr_a, trans_b ? &tr_b : nullptr, s)
-                : launch_transpose16(tr_b, nullptr, s);
-  if (e == hipSuccess && (plain_a || plain_b))
-    e = plain_a ? launch_pad16(pad_a, plain_b ? &pad_b : nullptr, s) : launch_pad16(pad_b, nullptr, s);
+  (void)op_a;
+  (void)op_b;
+  if (pl.copy_a || pl.copy_b)
+    e = pl.copy_a ? launch_transpose16(tr_a, pl.copy_b ? &tr_b : nullptr, s)
+                  : launch_transpose16(tr_b, nullptr, s);
   if (pl.copy_a) a.A = dst_a;
   if (pl.copy_b) a.B = dst_b;
   a.lda = pl.lda;
   a.ldb = pl.ldb;
   if (e == hipSuccess) {
-    if (padded) {
-      a.m_out = a.M;
-      a.n_out = a.N;
-      a.M = pl.Mp;
-      a.N = pl.Np;
-      a.K = pl.Kp;
-      e = launch_f16_mfma_masked(a, epi, cus, s);
-    } else {
-      switch (pl.path) {
-        case GEMM_PATH_F16_GEMV:
-          e = pl.gemv_kn ? launch_f16_gemv_kn(a, op_a, op_b, epi, split, ws + bytes_a + bytes_b, s)
-                         : launch_f16_gemv(a, epi, s);
-          break;
-        case GEMM_PATH_F16_SPLITK:
-          a.sk = splitk_args(split, a.M, a.N, ws + bytes_a + bytes_b);
-          e = launch_f16_splitk(a, epi, cus, s);
-          break;
-        case GEMM_PATH_F16_MFMA: e = launch_f16_mfma(a, epi, cus, s); break;
-        default: e = launch_f16_edge(a, epi, s); break;
-      }
+    switch (pl.path) {
+      case GEMM_PATH_F16_GEMV:
+        e = pl.gemv_kn ? launch_f16_gemv_kn(a, op_a, op_b, epi, split, ws + bytes_a + bytes_b, s)
+                       : launch_f16_gemv(a, epi, s);
+        break;
+      case GEMM_PATH_F16_SPLITK:
+        a.sk = splitk_args(split, a.M, a.N, ws + bytes_a + bytes_b);
+        e = launch_f16_splitk(a, epi, cus, s);
+        break;
+      case GEMM_PATH_F16_MFMA: e = launch_f16_mfma(a, epi, cus, s); break;
+      case GEMM_PATH_F16_STAGED: e = launch_f16_staged(a, epi, cus, s); break;
+      default: e = launch_f16_edge(a, epi, s); break;
     }
   }
   const hipError_t f = owned ? hipFreeAsync(ws, s) : hipSuccess;
@@ -625,7 +606,7 @@ MI355GEMM_API const char* gemm_path_name(int path) {
     case GEMM_PATH_F16_GEMV: return "f16_gemv";
     case GEMM_PATH_F16_SPLITK: return "f16_splitk";
     case GEMM_PATH_F32_SPLITK: return "f32_splitk";
-    case GEMM_PATH_F16_PADDED: return "f16_padded";
+    case GEMM_PATH_F16_STAGED: return "f16_staged";
     case GEMM_PATH_F32_PADDED: return "f32_padded";
     default: return "?";
   }

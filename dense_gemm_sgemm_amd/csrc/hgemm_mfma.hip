@@ -88,9 +88,6 @@ hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t strea
   return launch_any<false>(a, epi, cus, stream);
 }
 
-hipError_t launch_f16_mfma_masked(const Args16& a, bool epi, int cus, hipStream_t stream) {
-  return launch_any<true>(a, epi, cus, stream);
-}
 
 bool f16_operand_fits(const void* X, int64_t ld) {
   return aligned16(X) && ld % 8 == 0 && ld < (int64_t(1) << 28);

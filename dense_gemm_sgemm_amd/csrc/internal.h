@@ -130,23 +130,20 @@ hipError_t launch_f16_gemv_kn(const Args16& a, int op_a, int op_b, bool epi, con
                               void* workspace, hipStream_t stream);
 // The split-K reduction alone: a.sk names the partial sums.
 hipError_t launch_f16_reduce(const Args16& a, bool epi, hipStream_t stream);
-// A padding copy: dst[r * ldd + k] = src[r * lds + k] inside rows x cols,
-// zero elsewhere in rows_p x cols_p (cols_p and ldd multiples of 8, dst
-// 16-byte aligned).  launch_pad16 runs one or two of them in one launch.
+// A transposition: dst[c * ldd + r] = src[r * lds + c] for the rows x cols
+// source; the destination's rows_p x cols_p extent (source orientation) is
+// written, zero outside the source (dst 16-byte aligned, ldd a multiple of
+// 8).  launch_transpose16 runs one or two of them in one launch.
 struct PadCopy {
   const half_t* src;
   half_t* dst;
   int64_t lds, ldd;
   int rows, cols, rows_p, cols_p;
 };
-hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
-// A transposition with the same fields: dst[c * ldd + r] = src[r * lds + c]
-// for the rows x cols source; the destination's rows_p x cols_p extent
-// (source orientation) is written, zero outside the source.  One or two of
-// them in one launch.
 hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
-// The same for fp32 matrices (cols_p and ldd multiples of 4, dst 16-byte
-// aligned).
+// A padding copy of an fp32 matrix: dst[r * ldd + k] = src[r * lds + k]
+// inside rows x cols, zero elsewhere in rows_p x cols_p (cols_p and ldd
+// multiples of 4, dst 16-byte aligned); one or two of them in one launch.
 struct PadCopy32 {
   const float* src;
   float* dst;
@@ -157,8 +154,10 @@ hipError_t launch_pad32(const PadCopy32& first, const PadCopy32* second, hipStre
 // The fp32 streaming kernels on zero-padded copies (a.M, a.N multiples of 64,
 // a.K of 64), storing only a.m_out x a.n_out of C at any alignment.
 hipError_t launch_f32_mfma_masked(const F32Args& a, int cus, hipStream_t stream);
-// The full-tile kernel on zero-padded copies, storing only m_out x n_out.
-hipError_t launch_f16_mfma_masked(const Args16& a, bool epi, int cus, hipStream_t stream);
+// The register-staged wide-tile kernel: any shape (K >= 8), leading
+// dimension (below 2^23) and 2-byte alignment, no copies, no workspace.
+bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb);
+hipError_t launch_f16_staged(const Args16& a, bool epi, int cus, hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.
 hipError_t launch_f16_partials(const Args16& a, hipStream_t stream);
 hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);

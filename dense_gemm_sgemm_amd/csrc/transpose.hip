@@ -14,10 +14,9 @@
 // (source orientation) is written, zero outside the source matrix, which is
 // never read outside.
 //
-// pad16_kernel copies without transposing: dst[r * ldd + k] = src[r * lds + k]
-// inside rows x cols, zero elsewhere in rows_p x cols_p (cols_p a multiple of
-// 8), 16 bytes per thread; pad32_kernel does the same for fp32 matrices
-// (cols_p a multiple of 4).
+// pad32_kernel copies an fp32 matrix without transposing: dst[r * ldd + k] =
+// src[r * lds + k] inside rows x cols, zero elsewhere in rows_p x cols_p
+// (cols_p a multiple of 4), 16 bytes per thread.
 #include "internal.h"
 
 namespace mi355gemm {
@@ -110,38 +109,6 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(PadPair pair, int
     transpose_block<false>(p, r0, c0);
 }
 
-__device__ __forceinline__ void pad16_block(const TransposeArgs& p, int64_t block) {
-  const int chunks = p.cols_p / 8;   // per destination row
-  const int64_t idx = block * kThreads + threadIdx.x;
-  const int64_t r = idx / chunks;
-  if (r >= p.rows_p) return;
-  const int k = (int)(idx - r * chunks) * 8;
-  h8 v = {};
-  if (r < p.rows && k < p.cols) {
-    const half_t* s = p.src + r * p.lds + k;
-    if (k + 8 <= p.cols) {
-      __builtin_memcpy(&v, s, 16);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (k + e < p.cols) v[e] = s[e];
-    }
-  }
-  __builtin_memcpy(p.dst + r * p.ldd + k, &v, 16);
-}
-
-__global__ __launch_bounds__(kThreads) void pad16_kernel(PadPair p, int64_t block_base) {
-  const int64_t b = block_base + blockIdx.x;
-  if (b < p.split_block)
-    pad16_block(p.first, b);
-  else
-    pad16_block(p.second, b - p.split_block);
-}
-
-int64_t pad_blocks(int rows_p, int cols_p) {
-  return ((int64_t)rows_p * (cols_p / 8) + kThreads - 1) / kThreads;
-}
-
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 struct Pad32Args {
@@ -209,24 +176,6 @@ hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipSt
   }
   if (blocks <= 0) return hipSuccess;
   return launch_tiles((const void*)transpose16_kernel, p, blocks, kThreads, 0, stream);
-}
-
-hipError_t launch_pad16(const PadCopy& first, const PadCopy* second, hipStream_t stream) {
-  auto args = [](const PadCopy& c) {
-    return TransposeArgs{c.src, c.dst, c.lds, c.ldd, c.rows, c.cols, c.rows_p, c.cols_p};
-  };
-  PadPair p;
-  p.first = args(first);
-  p.split_block = pad_blocks(first.rows_p, first.cols_p);
-  int64_t blocks = p.split_block;
-  if (second) {
-    p.second = args(*second);
-    blocks += pad_blocks(second->rows_p, second->cols_p);
-  } else {
-    p.second = p.first;
-  }
-  if (blocks <= 0) return hipSuccess;
-  return launch_tiles((const void*)pad16_kernel, p, blocks, kThreads, 0, stream);
 }
 
 hipError_t launch_pad32(const PadCopy32& first, const PadCopy32* second, hipStream_t stream) {

@@ -266,9 +266,10 @@ enum {
                                 /*   streams the long operand once (any ld/align) */
   GEMM_PATH_F16_SPLITK = 8,     /* few output tiles, long K: K cut into ranges,   */
   GEMM_PATH_F32_SPLITK = 9,     /*   fp32 partials, ordered reduction             */
-  GEMM_PATH_F16_PADDED = 10,    /* large ragged or unaligned: A / B copied into   */
-                                /*   zero-padded aligned rows where needed, full  */
-                                /*   tiles with masked stores                     */
+  GEMM_PATH_F16_STAGED = 10,    /* large ragged or unaligned: v_mfma f16 wide     */
+                                /*   tiles with register-staged loads (any shape, */
+                                /*   leading dimension, 2-byte alignment), masked */
+                                /*   stores; no copies                            */
   GEMM_PATH_F32_PADDED = 11     /* the same for fp32 (at least 2^30 multiply-adds */
                                 /*   that the fp32 full tiles cannot read in      */
                                 /*   place, or whose K is not a multiple of 64)   */

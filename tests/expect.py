@@ -50,5 +50,6 @@ def expected_f16_path(mode, M, N, K):
                             (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
     if fast:
         return "f16_mfma"
-    # contiguous operands: copies are needed, which pay from 2^30 multiply-adds
-    return "f16_padded" if M * N * K >= 1 << 30 else "f16_general"
+    # the register-staged wide tiles take large products (from 2^30
+    # multiply-adds, K at least 8) that the full tiles cannot read in place
+    return "f16_staged" if M * N * K >= 1 << 30 and K >= 8 else "f16_general"

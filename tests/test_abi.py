@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
 F32_MFMA, F32_GENERAL, F32_SCALE = 3, 2, 1
 F16_MFMA, F16_GENERAL, F16_ZERO, F16_GEMV = 6, 5, 4, 7
-F16_SPLITK, F32_SPLITK, F16_PADDED, F32_PADDED = 8, 9, 10, 11
+F16_SPLITK, F32_SPLITK, F16_STAGED, F32_PADDED = 8, 9, 10, 11
 ALIGNED = 0x100000          # fake device addresses: only their alignment is looked at
 p = ctypes.c_void_p
 
@@ -62,7 +62,7 @@ def test_status_strings(lib):
     assert dg.status_string(17) == "unknown status code"
     assert lib.gemm_path_name(3) == b"f32_mfma" and lib.gemm_path_name(99) == b"?"
     assert lib.gemm_path_name(F16_GEMV) == b"f16_gemv"
-    assert lib.gemm_path_name(F16_PADDED) == b"f16_padded"
+    assert lib.gemm_path_name(F16_STAGED) == b"f16_staged"
 
 
 def f32(lib, M, N, K, alpha=1.0, A=ALIGNED, lda=None, B=ALIGNED, ldb=None, beta=0.0, C=ALIGNED,
@@ -126,14 +126,15 @@ def test_fused_call_validation_and_paths(lib, monkeypatch):
     assert f16ex(lib, 0, 8, 8, A=0, B=0, C=0) == 0
     assert f16ex(lib, 5376, 5376, 2048) == F16_MFMA
     assert f16ex(lib, 5376, 5376, 2048, bias=0, res=0, act=2) == F16_MFMA
-    # bias 2-byte aligned, residual rows unaligned: masked full tiles, no copies
-    assert f16ex(lib, 5376, 5376, 2048, bias=ALIGNED + 2) == F16_PADDED
-    assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_PADDED
-    assert f16ex(lib, 256, 256, 64, bias=ALIGNED + 2) == F16_PADDED      # no copy needed
-    assert f16ex(lib, 256, 224, 64, bias=ALIGNED + 2) == F16_GENERAL     # B copy, too small
+    # bias 2-byte aligned, residual rows unaligned: the register-staged wide
+    # tiles (element reads of bias and residual), from 2^30 multiply-adds on
+    assert f16ex(lib, 5376, 5376, 2048, bias=ALIGNED + 2) == F16_STAGED
+    assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_STAGED
+    assert f16ex(lib, 256, 256, 64, bias=ALIGNED + 2) == F16_GENERAL     # too small
+    assert f16ex(lib, 256, 224, 64, bias=ALIGNED + 2) == F16_GENERAL
     assert f16ex(lib, 5376, 5376, 2048, ldr=5380) == F16_MFMA
-    assert f16ex(lib, 5000, 3001, 1537) == F16_PADDED
-    assert f16ex(lib, 500, 301, 153) == F16_GENERAL                      # too small to copy
+    assert f16ex(lib, 5000, 3001, 1537) == F16_STAGED
+    assert f16ex(lib, 500, 301, 153) == F16_GENERAL                      # too small
     assert f16ex(lib, 1, 16384, 4096, bias=ALIGNED + 2, ldr=16385) == F16_GEMV  # any alignment
     assert f16ex(lib, 4096, 3, 4096, act=1) == F16_GEMV
     assert f16ex(lib, 1, 16384, 0, A=0, B=0) == F16_GENERAL
@@ -162,12 +163,15 @@ def test_path_selection(lib, monkeypatch):
     assert f32(lib, 256, 256, 256, lda=258) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_MFMA
     # ragged or unaligned and large: copies where needed, masked full tiles
-    assert f16(lib, 5000, 3001, 1537) == F16_PADDED
-    assert f16(lib, 5376, 5376, 2048, ldb=2052) == F16_PADDED
-    assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_PADDED
-    assert f16(lib, 1024, 1024, 1025) == F16_PADDED and f16(lib, 1024, 1024, 1000) == F16_GENERAL
+    assert f16(lib, 5000, 3001, 1537) == F16_STAGED
+    assert f16(lib, 5376, 5376, 2048, ldb=2052) == F16_STAGED
+    assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_STAGED
+    assert f16(lib, 1024, 1024, 1025) == F16_STAGED and f16(lib, 1024, 1024, 1000) == F16_GENERAL
     assert f16(lib, 1000, 1000, 1000) == F16_GENERAL                    # below 2^30 multiply-adds
-    assert f16(lib, 128, 128, 64, C=ALIGNED + 2) == F16_PADDED          # no copy needed
+    assert f16(lib, 128, 128, 64, C=ALIGNED + 2) == F16_GENERAL         # too small for wide tiles
+    assert f16(lib, 1024, 1024, 1024, A=ALIGNED + 2, lda=1025) == F16_STAGED   # any alignment
+    assert f16(lib, 1024, 1024, 7, A=ALIGNED + 2, lda=1025) == F16_GENERAL     # K < 8
+    assert f16(lib, 1024, 1024, 1024, A=ALIGNED + 2, lda=(1 << 23) + 1) == F16_GENERAL  # offsets past 2^32
     assert f16(lib, 256, 224, 64) == F16_MFMA                       # 224-wide tiles
     assert f16(lib, 2048, 2304, 768) == F16_MFMA                    # 128 x 128 tiles
     assert f16(lib, 384, 640, 192) == F16_MFMA and f16(lib, 384, 640, 160) == F16_GENERAL
@@ -239,7 +243,7 @@ def test_gemm_ex_validation_and_paths(lib, monkeypatch):
         assert ex(lib, t, N_, T_, 5376, 5376, 2048) == F16_MFMA
         assert ex(lib, t, N_, N_, 5376, 5376, 2048) == F16_MFMA      # B through a copy
         assert ex(lib, t, T_, N_, 5376, 5376, 2048) == F16_MFMA
-        assert ex(lib, t, T_, T_, 5000, 3001, 1537) == F16_PADDED
+        assert ex(lib, t, T_, T_, 5000, 3001, 1537) == F16_STAGED
         assert ex(lib, t, T_, T_, 500, 301, 153) == F16_GENERAL
         assert ex(lib, t, N_, N_, 1, 4096, 4096) == F16_GEMV
         assert ex(lib, t, T_, N_, 512, 512, 16384) == F16_SPLITK

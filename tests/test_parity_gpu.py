@@ -681,27 +681,46 @@ def test_workload_hgemm_splitk():
                                                                        res["max_ulps"]))
 
 
-# ------------------------------------------------------ padded path ------
-# Large ragged or unaligned products: A and/or B copied into zero-padded,
-# aligned rows, full tiles with masked stores (and masked bias / residual
-# reads).  Shapes copy A only, B only, both, or nothing (C misaligned only).
-PADDED_SHAPES = [(1000, 1001, 1111), (2048, 1000, 640), (1000, 2048, 640), (1024, 1024, 1025),
-                 (1536, 1000, 777), (1111, 1152, 896)]
+# ---------------------------------------------- register-staged path ------
+# Large products the full tiles cannot read in place (ragged M, N or K, rows
+# at 2-byte offsets, odd leading dimensions, C unaligned): the wide-tile
+# kernel with register-staged loads reads the operands where they are.  The
+# K values reach every tail form of the last slab: whole slabs (640, 896),
+# one element past a slab (1025), 9, 23 and 4 elements into the slab with the
+# last chunk shifted by 7, 1 and 4 (777, 1111, 1100), K % 8 = 2, 3, 5, 6
+# (1002, 1003, 1005, 1006), and a slab wholly past K when the slab count is
+# rounded up to an even number (1025, 1111).  N = 3001 and 1000 exercise the
+# 256 x 224 tiles as well as the 256 x 256 ones.
+STAGED_SHAPES = [(1000, 1001, 1111), (2048, 1000, 640), (1000, 2048, 640), (1024, 1024, 1025),
+                 (1536, 1000, 777), (1111, 1152, 896), (1300, 1000, 1100), (1024, 1100, 1002),
+                 (1100, 1024, 1003), (1024, 1024, 1005), (1050, 1030, 1006), (700, 3001, 600)]
 
 
-@pytest.mark.parametrize("shape", PADDED_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_f16_padded_shapes(shape, path_mode):
+@pytest.mark.parametrize("shape", STAGED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_staged_shapes(shape, path_mode):
     M, N, K = shape
     A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
     got = gpu_f16(A, B, expect=expected_f16_path(path_mode, M, N, K))
     f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
 
 
-def test_f16_padded_unaligned_and_c_only():
+def test_f16_staged_small_integers_are_exact():
+    """Small-integer operands make every partial sum exact, so the staged
+    kernel (ragged M, N, K with a K tail) must equal the exact product
+    rounded once, bit for bit; ties to even included."""
+    M, N, K = 1030, 1040, 1027
+    A = inputs.small_ints((M, K), 31, -2, 2, np.float16)
+    B = inputs.small_ints((N, K), 32, -2, 2, np.float16)
+    got = gpu_f16(A, B, expect="f16_staged")
+    exact = A.astype(np.float64) @ B.astype(np.float64).T
+    assert np.array_equal(got.view(np.uint16), oracle.half_from_double(exact).view(np.uint16))
+
+
+def test_f16_staged_unaligned_and_c_only():
     """Operands one element into their buffers with odd leading dimensions;
-    then aligned operands with only C misaligned (no copies).  Nothing outside
-    C's window changes."""
-    for (M, N, K, off_ab) in [(1030, 1100, 1000, 1), (1024, 1024, 1024, 0), (256, 256, 64, 0)]:
+    then aligned operands with only C misaligned.  Nothing outside C's window
+    changes."""
+    for (M, N, K, off_ab) in [(1030, 1100, 1000, 1), (1024, 1024, 1024, 0)]:
         lda, ldb = (K + 3, K + 1) if off_ab else (K, K)
         ldc = N + 5
         A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
@@ -713,7 +732,7 @@ def test_f16_padded_unaligned_and_c_only():
         dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
         dA.copy_(dev(A))
         dB.copy_(dev(B))
-        assert dg.f16_nt_path(dA, dB, dC) == "f16_padded"
+        assert dg.f16_nt_path(dA, dB, dC) == "f16_staged"
         dg.gemm_f16_nt(dA, dB, dC)
         torch.cuda.synchronize()
         f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
@@ -726,17 +745,17 @@ def test_f16_padded_unaligned_and_c_only():
 
 
 @pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)
-def test_f16_padded_fused(act, use_bias, use_res):
-    """The fused write-back on the padded path: a ragged shape (copies), then
-    an aligned shape with the bias one element into its buffer and the
-    residual rows of odd length (no copies), in place."""
+def test_f16_staged_fused(act, use_bias, use_res):
+    """The fused write-back on the staged path: a ragged shape, then an
+    aligned shape with the bias one element into its buffer and the residual
+    rows of odd length, in place."""
     M, N, K = 1000, 1001, 1111
     A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
     dA, dB = dev(A), dev(B)
     dbias = dev(bias) if bias is not None else None
     dres = dev(res) if res is not None else None
     dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
-    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == "f16_padded"
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == "f16_staged"
     dg.gemm_f16_nt_ex(dA, dB, dC, dbias, act, dres)
     torch.cuda.synchronize()
     check_ex(dC.cpu().numpy(), A, B, bias, act, res)
@@ -749,7 +768,7 @@ def test_f16_padded_fused(act, use_bias, use_res):
     cbuf = torch.zeros(M, N + 1, device=DEV, dtype=torch.float16)
     cbuf[:, :N].copy_(dev(res))
     dC = cbuf[:, :N]
-    assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], act, dC) == "f16_padded"
+    assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], act, dC) == "f16_staged"
     dg.gemm_f16_nt_ex(dev(A), dev(B), dC, bbuf[1:], act, dC)
     torch.cuda.synchronize()
     check_ex(dC.cpu().numpy(), A, B, bias, act, res)
@@ -979,7 +998,7 @@ def test_workload_sgemm_4096(beta):
 
 
 @pytest.mark.parametrize("name,path", [("hgemm_nt_5376x5376x2048", "f16_mfma"),
-                                       ("hgemm_nt_5000x3001x1537", "f16_padded"),
+                                       ("hgemm_nt_5000x3001x1537", "f16_staged"),
                                        ("hgemm_nt_2048x2304x768", "f16_mfma")])
 def test_workload_hgemm(name, path):
     """Every output of the workload against the oracle; the count of outputs

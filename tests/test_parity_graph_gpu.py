@@ -1,6 +1,6 @@
 """HIP graph capture: the library's calls recorded with torch.cuda.graph and
-replayed.  Calls whose path needs a workspace (padded copies, split-K
-partials) allocate and free it inside the captured work.  Each graph is
+replayed.  Calls whose path needs a workspace (the fp32 padded copies,
+split-K partials) allocate and free it inside the captured work.  Each graph is
 replayed several times, with the program's own eager work and
 synchronisations in between, and every replay must equal the eager result bit
 for bit (the kernels are deterministic and the path choice is the same)."""
@@ -24,7 +24,7 @@ CASES = [
     ("f32", (1030, 1100, 1000), "f32_padded"),
     ("f32", (512, 512, 16384), "f32_splitk"),
     ("f16", (512, 512, 512), "f16_mfma"),
-    ("f16", (1000, 1030, 1100), "f16_padded"),
+    ("f16", (1000, 1030, 1100), "f16_staged"),
     ("f16", (128, 128, 16384), "f16_splitk"),
 ]
 

@@ -29,7 +29,7 @@ def draw(seed):
         M, N, K = (int(x) for x in rng.integers(1, 300, 3))
     elif family == 1:     # whole tiles
         M, N, K = (int(x) for x in 64 * rng.integers(1, 40, 3))
-    elif family == 2:     # large and ragged (padded paths)
+    elif family == 2:     # large and ragged (register-staged fp16, padded fp32)
         M, N, K = (int(x) for x in rng.integers(900, 2600, 3))
     elif family == 3:     # few tiles, long K (split-K)
         M, N, K = int(rng.integers(1, 400)), int(rng.integers(1, 400)), int(rng.integers(2048, 9000))

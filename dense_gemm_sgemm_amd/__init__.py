@@ -10,6 +10,14 @@ library is missing the calls raise.
     gemm_f16_nt(A, B, C)                     # C = A@B.T, fp16 in/out, fp32 acc
     gemm_f16_nt_ex(A, B, C, bias=None, act="none", residual=None)
                                              # C = act(A@B.T + bias) + residual
+    gemm_ex(A, B, C, op_a="n", op_b="t", ...) # any layout, fp16 or bf16
+    gemm_f32_splitk / gemm_f16_nt_splitk     # K cut into ranges (split-K)
+
+The library allocates no memory.  Where a call's kernels need scratch memory
+(split-K partial sums, gemm_ex's transposed copies and matrix-vector partial
+sums) the caller may pass a ``workspace`` tensor; if it does not, this module
+takes one of the size the library reports from torch's caching allocator, on
+the stream the call runs on, for the duration of the call.
 """
 from __future__ import annotations
 
@@ -79,8 +87,10 @@ def load_library() -> ctypes.CDLL:
         lib.gemm_f32_splitk_workspace.restype = u64
         lib.gemm_f16_nt_splitk_workspace.argtypes = [i, i, i, i]
         lib.gemm_f16_nt_splitk_workspace.restype = u64
-        lib.gemm_ex.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, p, i, p, i, p]
+        lib.gemm_ex.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, p, i, p, i, p, u64, p]
         lib.gemm_ex.restype = i
+        lib.gemm_ex_workspace.argtypes = [i, i, i, i, i, i, i, i]
+        lib.gemm_ex_workspace.restype = u64
         lib.gemm_ex_path.argtypes = [i, i, i, i, i, i, p, i, p, i, p, i, p, i, p, i]
         lib.gemm_ex_path.restype = i
         lib.gemm_status_string.argtypes = [i]
@@ -350,18 +360,32 @@ def _ex_args(A, B, C, op_a, op_b, bias, act, residual):
     return (typ, OPS[op_a], OPS[op_b], M, N, K, pa, lda, pb, ldb, pbias, code, pres, ldr, pc, ldc)
 
 
+def ex_workspace_bytes(A, B, C, op_a: str = "n", op_b: str = "t") -> int:
+    """Workspace bytes ``gemm_ex`` uses for these tensors (0 when none)."""
+    a = _ex_args(A, B, C, op_a, op_b, None, "none", None)
+    return int(load_library().gemm_ex_workspace(a[0], a[1], a[2], a[3], a[4], a[5], a[7], a[9]))
+
+
 def gemm_ex(A, B, C, op_a: str = "n", op_b: str = "t", bias=None, act: str = "none",
-            residual=None, stream=None):
+            residual=None, workspace=None, stream=None):
     """``C = act(op(A) @ op(B) + bias) + residual`` for float16 or bfloat16
     tensors (all of one dtype).  op "n": A is [M,K], B is [K,N]; op "t": A is
-    [K,M], B is [N,K].  fp32 accumulation, one rounding to the dtype.  Returns C."""
+    [K,M], B is [N,K].  fp32 accumulation, one rounding to the dtype.
+    ``workspace``: a contiguous GPU tensor of at least ``ex_workspace_bytes``
+    bytes, or None (one is taken from torch's allocator when the call uses
+    one).  Returns C."""
     args = _ex_args(A, B, C, op_a, op_b, bias, act, residual)
-    _check(load_library().gemm_ex(*args, _stream(stream)))
+    lib = load_library()
+    need = 0 if workspace is not None else int(lib.gemm_ex_workspace(
+        args[0], args[1], args[2], args[3], args[4], args[5], args[7], args[9]))
+    pw, nw, _ws = _workspace(workspace, need, C.device, stream)
+    _check(lib.gemm_ex(*args, pw, nw, _stream(stream)))
     return C
 
 
 def ex_path(A, B, C, op_a: str = "n", op_b: str = "t", bias=None, act: str = "none",
             residual=None) -> str:
-    """Name of the A*B^T kernel ``gemm_ex`` would run for these tensors (host only)."""
+    """Name of the kernel ``gemm_ex`` would run for these tensors with a
+    workspace of ``ex_workspace_bytes`` (host only)."""
     return _path_name(load_library().gemm_ex_path(*_ex_args(A, B, C, op_a, op_b, bias, act,
                                                             residual)))

@@ -55,43 +55,34 @@ bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
          hgemm::fits<128, 192, BK>(M, N, K, A, lda, B, ldb, C, ldc);
 }
 
-template <bool EPI, int FMT, bool MASK>
+template <bool EPI, int FMT>
 hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
   switch (choose(a.M, a.N, cus)) {
     case k256x224:
-      return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, MASK>(a, cus,
+      return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false>(a, cus,
                                                                                       stream);
     case k128x128:
-      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false, MASK>(a, 2 * cus,
+      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false>(a, 2 * cus,
                                                                                       stream);
     case k128x192:
-      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false, MASK>(a, cus,
+      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false>(a, cus,
                                                                                       stream);
     default:
       // 64 x 128 per wave: 128 accumulator registers leave room for one set
       // of B fragments only (OPT bit 1)
-      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false, MASK>(a, cus,
+      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false>(a, cus,
                                                                                       stream);
   }
 }
 
-template <bool MASK>
-hipError_t launch_any(const Args16& a, bool epi, int cus, hipStream_t stream) {
-  if (a.fmt == kFmtBF16)
-    return epi ? launch_shape<true, kFmtBF16, MASK>(a, cus, stream)
-               : launch_shape<false, kFmtBF16, MASK>(a, cus, stream);
-  return epi ? launch_shape<true, kFmtF16, MASK>(a, cus, stream)
-             : launch_shape<false, kFmtF16, MASK>(a, cus, stream);
-}
-
 hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {
-  return launch_any<false>(a, epi, cus, stream);
+  if (a.fmt == kFmtBF16)
+    return epi ? launch_shape<true, kFmtBF16>(a, cus, stream)
+               : launch_shape<false, kFmtBF16>(a, cus, stream);
+  return epi ? launch_shape<true, kFmtF16>(a, cus, stream)
+             : launch_shape<false, kFmtF16>(a, cus, stream);
 }
 
-
-bool f16_operand_fits(const void* X, int64_t ld) {
-  return aligned16(X) && ld % 8 == 0 && ld < (int64_t(1) << 28);
-}
 
 // Split-K partial products on 128 x 128 full tiles (two workgroups per CU):
 // needs whole tiles and the fast path's alignment, and ranges of exactly

@@ -148,11 +148,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // SPLIT instances walk (tile, K range) work items -- item i is range
 // i / tiles of tile i % tiles, p.sk.per slabs from slab (i / tiles) * per --
 // and store each item's fp32 partial tile to the split-K workspace instead of
-// writing C.  MASK instances read zero-padded operand copies (whole tiles)
-// and store, and read bias and residual, only inside p.m_out x p.n_out, with
-// C, bias and residual at any alignment.
+// writing C.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
-          int FMT, bool SPLIT = false, bool MASK = false>
+          int FMT, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVES_M * WAVES_N))
 void hgemm_nt_kernel(TileArgs ta) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
@@ -319,16 +317,7 @@ void hgemm_nt_kernel(TileArgs ta) {
       for (int j = 0; j < C::kBlocksN; ++j) {
         const int n = n0 + wn + 16 * j + 4 * g;
         bq[j] = h4{};
-        if (p.bias) {
-          if constexpr (MASK) {
-            // element reads inside the output only, any alignment
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              if (n + v < p.n_out) bq[j][v] = p.bias[n + v];
-          } else {
-            bq[j] = *(const h4*)(p.bias + n);
-          }
-        }
+        if (p.bias) bq[j] = *(const h4*)(p.bias + n);
       }
 #pragma unroll
       for (int i = 0; i < C::kBlocksM; ++i) {
@@ -337,17 +326,7 @@ void hgemm_nt_kernel(TileArgs ta) {
         for (int j = 0; j < C::kBlocksN; ++j) {
           const int n = n0 + wn + 16 * j + 4 * g;
           rq[i][j] = h4{};
-          if (p.res) {
-            if constexpr (MASK) {
-              if (m < p.m_out) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                  if (n + v < p.n_out) rq[i][j][v] = p.res[m * p.ldr + n + v];
-              }
-            } else {
-              rq[i][j] = *(const h4*)(p.res + m * p.ldr + n);
-            }
-          }
+          if (p.res) rq[i][j] = *(const h4*)(p.res + m * p.ldr + n);
         }
       }
     }
@@ -381,20 +360,7 @@ void hgemm_nt_kernel(TileArgs ta) {
       for (int q = 0; q < kOutRows / 4; ++q) {
         const int R = 4 * q + (lane >> 4);
         const h8 v = *(const h8*)(stage_out + R * C::kOutRowBytes + 16 * (cc ^ R));
-        if constexpr (MASK) {
-          const int64_t m = m0 + wm + 16 * i + R;
-          const int n = n0 + wn + 8 * cc;
-          if ((C::WN == 128 || cc < C::WN / 8) && m < p.m_out && n < p.n_out) {
-            half_t* dst = p.C + m * p.ldc + n;
-            if (n + 8 <= p.n_out) {
-              __builtin_memcpy(dst, &v, 16);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (n + e < p.n_out) dst[e] = v[e];
-            }
-          }
-        } else if (C::WN == 128 || cc < C::WN / 8) {
+        if (C::WN == 128 || cc < C::WN / 8) {
           h8* dst = (h8*)(p.C + (int64_t)(m0 + wm + 16 * i + R) * p.ldc + n0 + wn + 8 * cc);
           if (OPT & 1) {
             __builtin_nontemporal_store(v, dst);   // OPT bit 0: streaming stores of C
@@ -611,8 +577,7 @@ void hgemm_nt_kernel(TileArgs ta) {
 // PERSISTENT: at most `slots` workgroups (as many as the GPU runs at once),
 // each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
-          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false,
-          bool MASK = false>
+          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false>
 hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN) * (SPLIT ? a.sk.splits : 1);
@@ -623,7 +588,7 @@ hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   void* args[] = {&ta};
   return hipLaunchKernel(
       (const void*)
-          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT, MASK>,
+          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT>,
       dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 

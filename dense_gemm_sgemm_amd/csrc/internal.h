@@ -29,9 +29,6 @@ struct F32Args {
   int M, N, K;
   float alpha, beta;
   SplitK sk;                      // split-K partial products (partial kernels only)
-  // Masked instances: M x N are whole tiles of zero-padded copies of A and B,
-  // and only rows < m_out, columns < n_out of C exist.
-  int m_out = 0, n_out = 0;
 };
 
 // 16-bit storage formats.  Kernels move both as 16-bit words (half_t
@@ -55,10 +52,6 @@ struct Args16 {
   int act = 0;                    // 0 none, 1 ReLU, 2 SiLU
   SplitK sk;                      // split-K partial products (partial kernels only)
   int fmt = kFmtF16;              // storage format of every 16-bit operand
-  // Masked full-tile instances: M x N are whole tiles of zero-padded copies
-  // of A and B, and only rows < m_out, columns < n_out of C (and of the
-  // residual and bias) exist.
-  int m_out = 0, n_out = 0;
 };
 
 // A 16-bit storage word as fp32, and fp32 rounded to a storage word (nearest,
@@ -141,23 +134,13 @@ struct PadCopy {
   int rows, cols, rows_p, cols_p;
 };
 hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
-// A padding copy of an fp32 matrix: dst[r * ldd + k] = src[r * lds + k]
-// inside rows x cols, zero elsewhere in rows_p x cols_p (cols_p and ldd
-// multiples of 4, dst 16-byte aligned); one or two of them in one launch.
-struct PadCopy32 {
-  const float* src;
-  float* dst;
-  int64_t lds, ldd;
-  int rows, cols, rows_p, cols_p;
-};
-hipError_t launch_pad32(const PadCopy32& first, const PadCopy32* second, hipStream_t stream);
-// The fp32 streaming kernels on zero-padded copies (a.M, a.N multiples of 64,
-// a.K of 64), storing only a.m_out x a.n_out of C at any alignment.
-hipError_t launch_f32_mfma_masked(const F32Args& a, int cus, hipStream_t stream);
-// The register-staged wide-tile kernel: any shape (K >= 8), leading
-// dimension (below 2^23) and 2-byte alignment, no copies, no workspace.
-bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb);
-hipError_t launch_f16_staged(const Args16& a, bool epi, int cus, hipStream_t stream);
+// The register-staged wide-tile kernel: any shape (K >= 8; M >= 8 when A
+// is K-major, N >= 8 when B is), leading dimension (below 2^23), 2-byte
+// alignment and operand layout (op_a / op_b as in gemm_ex; a.A, a.B in their
+// stored layouts), no copies, no workspace.
+bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb, int op_a, int op_b);
+hipError_t launch_f16_staged(const Args16& a, bool epi, int op_a, int op_b, int cus,
+                             hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.
 hipError_t launch_f16_partials(const Args16& a, hipStream_t stream);
 hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);
@@ -174,18 +157,10 @@ bool f32_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* 
 // leading dimensions within their 32-bit lane offsets).
 bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                      const void* C, int64_t ldc);
-// An fp32 operand the streaming kernels can read in place (rows 16-byte
-// aligned, leading dimension within their lane offsets); its rows must also
-// be whole tiles and K a multiple of 64.
-bool f32_operand_fits(const void* X, int64_t ld);
 // Alignment conditions of the fast kernel's fused write-back.
 bool f16_epi_fits(const void* bias, const void* res, int64_t ldr);
 bool f16_mfma_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
                    const void* C, int64_t ldc);
-// An operand the full-tile kernel can read in place (rows 16-byte aligned,
-// leading dimension within its 32-bit copy offsets); K must also be a
-// multiple of the slab and the rows whole tiles.
-bool f16_operand_fits(const void* X, int64_t ld);
 // M or N small enough for the matrix-vector kernel.
 bool f16_gemv_fits(int M, int N);
 // Which operand the matrix-vector kernels stream: B when M is the small side

@@ -297,10 +297,6 @@ __device__ __forceinline__ void copy16(const char* sbase, uint32_t voff, lds_voi
 constexpr int kWaitVmLgkm0 = 0x0070;   // s_waitcnt vmcnt(0) lgkmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;     // s_waitcnt lgkmcnt(0)
 
-// MASK instances read zero-padded copies of A and B (whole tiles) and read
-// and write C only inside p.m_out x p.n_out, element by element, at any
-// alignment.
-template <bool MASK>
 __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, int64_t tiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
   const int lane = threadIdx.x & 63;
@@ -431,18 +427,7 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
       for (int j = 0; j < 4; ++j) {
         const int m = m0 + wm + 16 * i + r, n = n0 + wn + 16 * j + 4 * g;
         float* c = p.C + (int64_t)m * p.ldc + n;
-        if constexpr (MASK) {
-          if (m < p.m_out) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              if (n + v < p.n_out) {
-                float out = alpha * acc[i][j][v];
-                if (beta != 0.f) out = fmaf(beta, c[v], out);
-                c[v] = out;
-              }
-            }
-          }
-        } else {
+        {
           f4 out = alpha * acc[i][j];
           if (beta != 0.f) {
             const f4 old = *(const f4*)c;
@@ -481,8 +466,7 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
 //  * after a tile's last slab each computing wave stores its partial tile,
 //    all eight waves meet (the copying waves count the slabs of each tile),
 //    and computing wave w adds the four partials of rows 16 w .. 16 w + 15
-//    and writes them to C, 16 bytes per lane (MASK instances: element by
-//    element inside p.m_out x p.n_out).
+//    and writes them to C, 16 bytes per lane.
 namespace stream64 {
 constexpr int BT = 64, BKS = 64;
 constexpr int kStage = 2 * BT * BKS * 4;    // A and B of one slab: 32 KiB
@@ -494,7 +478,6 @@ constexpr int kCopies = 8;                  // per copying wave per slab: 4 of A
 static_assert(kLds <= 160 * 1024, "LDS");
 static_assert(kCopies < 16, "a vmcnt immediate below 16");
 
-template <bool MASK>   // as for the 128 x 128 kernel
 __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, int64_t tiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
   const int lane = threadIdx.x & 63;
@@ -639,18 +622,7 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, 
       for (int v = 1; v < 4; ++v) sum += *(const f4*)(partials + v * kPartial + off);
       const int m = m0 + row, n = n0 + 4 * chunk;
       float* c = p.C + (int64_t)m * p.ldc + n;
-      if constexpr (MASK) {
-        if (m < p.m_out) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (n + e < p.n_out) {
-              float out = alpha * sum[e];
-              if (beta != 0.f) out = fmaf(beta, c[e], out);
-              c[e] = out;
-            }
-          }
-        }
-      } else {
+      {
         f4 out = alpha * sum;
         if (beta != 0.f) {
           const f4 old = *(const f4*)c;
@@ -681,7 +653,6 @@ hipError_t launch_tiled(const F32Args& a, hipStream_t stream) {
 // The streaming kernels over a.M x a.N (multiples of 64; a.K of 64): 128 x 128
 // tiles where there are at least as many as CUs, 64 x 64 otherwise.  One
 // persistent workgroup per CU.
-template <bool MASK>
 hipError_t launch_stream(const F32Args& a, int cus, hipStream_t stream) {
   const bool big = !small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0;
   const int bt = big ? stream::BM : stream64::BT;
@@ -690,8 +661,8 @@ hipError_t launch_stream(const F32Args& a, int cus, hipStream_t stream) {
   F32Args p = a;
   int64_t t = tiles;
   void* args[] = {&p, &t};
-  const void* kernel = big ? (const void*)stream::sgemm_stream_kernel<MASK>
-                           : (const void*)stream64::sgemm_stream64_kernel<MASK>;
+  const void* kernel = big ? (const void*)stream::sgemm_stream_kernel
+                           : (const void*)stream64::sgemm_stream64_kernel;
   static_assert(stream::kThreads == stream64::kThreads, "one block size");
   return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(stream::kThreads), args, 0, stream);
 }
@@ -714,23 +685,15 @@ bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void
          ldb < kStreamMaxLd;
 }
 
-bool f32_operand_fits(const void* X, int64_t ld) {
-  return aligned16(X) && ld % 4 == 0 && ld < kStreamMaxLd;
-}
-
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
   if (f32_stream_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc))
-    return launch_stream<false>(a, cus, stream);
+    return launch_stream(a, cus, stream);
   if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0)
     return launch_tiled<128, 128, false>(a, stream);
   // The small tiles run one workgroup per CU; 32-deep slabs halve their
   // barriers (1024^3: 28 us against 30 us).
   if (a.K % 32 == 0) return launch_tiled<64, 64, false, 32>(a, stream);
   return launch_tiled<64, 64, false>(a, stream);
-}
-
-hipError_t launch_f32_mfma_masked(const F32Args& a, int cus, hipStream_t stream) {
-  return launch_stream<true>(a, cus, stream);
 }
 
 hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream) {

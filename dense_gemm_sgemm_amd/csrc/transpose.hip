@@ -13,10 +13,7 @@
 // destination may be padded: every element of its rows_p x cols_p extent
 // (source orientation) is written, zero outside the source matrix, which is
 // never read outside.
-//
-// pad32_kernel copies an fp32 matrix without transposing: dst[r * ldd + k] =
-// src[r * lds + k] inside rows x cols, zero elsewhere in rows_p x cols_p
-// (cols_p a multiple of 4), 16 bytes per thread.
+
 #include "internal.h"
 
 namespace mi355gemm {
@@ -109,54 +106,6 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(PadPair pair, int
     transpose_block<false>(p, r0, c0);
 }
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-
-struct Pad32Args {
-  const float* src;
-  float* dst;
-  int64_t lds, ldd;
-  int rows, cols, rows_p, cols_p;
-};
-
-struct Pad32Pair {
-  Pad32Args first, second;
-  int64_t split_block;
-};
-
-// 16-byte source reads rely on the target's unaligned-access mode where a
-// row is only 4-byte aligned.
-__device__ __forceinline__ void pad32_block(const Pad32Args& p, int64_t block) {
-  const int chunks = p.cols_p / 4;   // per destination row
-  const int64_t idx = block * kThreads + threadIdx.x;
-  const int64_t r = idx / chunks;
-  if (r >= p.rows_p) return;
-  const int k = (int)(idx - r * chunks) * 4;
-  f4 v = {0.f, 0.f, 0.f, 0.f};
-  if (r < p.rows && k < p.cols) {
-    const float* s = p.src + r * p.lds + k;
-    if (k + 4 <= p.cols) {
-      __builtin_memcpy(&v, s, 16);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (k + e < p.cols) v[e] = s[e];
-    }
-  }
-  *(f4*)(p.dst + r * p.ldd + k) = v;
-}
-
-__global__ __launch_bounds__(kThreads) void pad32_kernel(Pad32Pair p, int64_t block_base) {
-  const int64_t b = block_base + blockIdx.x;
-  if (b < p.split_block)
-    pad32_block(p.first, b);
-  else
-    pad32_block(p.second, b - p.split_block);
-}
-
-int64_t pad32_blocks(int rows_p, int cols_p) {
-  return ((int64_t)rows_p * (cols_p / 4) + kThreads - 1) / kThreads;
-}
-
 }  // namespace
 
 hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipStream_t stream) {
@@ -176,24 +125,6 @@ hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipSt
   }
   if (blocks <= 0) return hipSuccess;
   return launch_tiles((const void*)transpose16_kernel, p, blocks, kThreads, 0, stream);
-}
-
-hipError_t launch_pad32(const PadCopy32& first, const PadCopy32* second, hipStream_t stream) {
-  auto args = [](const PadCopy32& c) {
-    return Pad32Args{c.src, c.dst, c.lds, c.ldd, c.rows, c.cols, c.rows_p, c.cols_p};
-  };
-  Pad32Pair p;
-  p.first = args(first);
-  p.split_block = pad32_blocks(first.rows_p, first.cols_p);
-  int64_t blocks = p.split_block;
-  if (second) {
-    p.second = args(*second);
-    blocks += pad32_blocks(second->rows_p, second->cols_p);
-  } else {
-    p.second = p.first;
-  }
-  if (blocks <= 0) return hipSuccess;
-  return launch_tiles((const void*)pad32_kernel, p, blocks, kThreads, 0, stream);
 }
 
 }  // namespace mi355gemm

@@ -9,29 +9,22 @@
  *    ldx sits at X[i*ldx + j].  Dimensions and leading dimensions are int;
  *    offsets are computed in 64 bits.
  *  - A, B and C are DEVICE pointers, allocated and owned by the caller.  The
- *    library keeps no pointer to them after the call returns.  It allocates
- *    nothing except a workspace on the paths that need one: split-K
- *    (GEMM_PATH_*_SPLITK: fp32 partial sums), the padded paths
- *    (GEMM_PATH_*_PADDED: zero-padded copies of A and/or B) and gemm_ex's
- *    transposed operand copies.  The library takes it from the
- *    stream-ordered allocator (hipMallocAsync on the call's stream) and keeps
- *    it for later calls on the same device and stream, growing it when a
- *    larger one is needed, until the process ends.  Under stream capture the
- *    workspace is allocated and returned inside the captured work instead.
- *    gemm_f32_splitk / gemm_f16_nt_splitk take a caller-owned workspace and
- *    allocate nothing (where those calls do not split, they run the kernels
- *    that need no workspace).
- *    A kept workspace is tied to the stream handle: destroying a stream
- *    while its work still runs and creating one that reuses the handle is
- *    not supported.
+ *    library never allocates, frees or keeps device memory, and keeps no
+ *    pointer after a call returns.  gemm_f32, gemm_f16_nt and gemm_f16_nt_ex
+ *    need nothing beyond their operands.  The calls whose kernels need
+ *    scratch memory take it from the caller as a `workspace` argument and
+ *    say how much through a size query: gemm_f32_splitk / gemm_f16_nt_splitk
+ *    (fp32 partial sums of the K ranges) and gemm_ex (transposed operand
+ *    copies for smaller products in the other layouts, partial sums of the
+ *    K-major matrix-vector kernel).
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *    Work is enqueued on it and the call returns without synchronising; a
  *    fault during execution surfaces at the caller's next synchronisation.
  *  - C must not overlap A or B (undefined otherwise).  A and B may alias.
  *  - Misaligned pointers or leading dimensions are never an error: they only
  *    select a slower kernel.
- *  - Calls are thread-safe.  The first call on a device checks, once, that
- *    the device is a gfx950.
+ *  - Calls are thread-safe: the library's only state is a per-device record,
+ *    set once, that the device is a gfx950.
  *
  * Return value: GEMM_OK (0) or one of the negative GEMM_ERR_* codes below.
  * On an error no work is enqueued and C is untouched.
@@ -57,8 +50,8 @@ enum {
   GEMM_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or the current one is not gfx950 */
   GEMM_ERR_LAUNCH = -5,            /* the HIP runtime refused the kernel launch      */
   GEMM_ERR_BAD_ARG = -6,           /* an enumerated argument has no defined meaning  */
-  GEMM_ERR_WORKSPACE = -7          /* a workspace the call needs is NULL, too small, */
-                                   /*   misaligned, or could not be allocated        */
+  GEMM_ERR_WORKSPACE = -7          /* a workspace the call needs is NULL, smaller    */
+                                   /*   than its size query, or not 16-byte aligned  */
 };
 
 /*
@@ -158,10 +151,15 @@ MI355GEMM_API int gemm_f16_nt_ex(int M, int N, int K,
  * (alpha * sum + beta * C) or of gemm_f16_nt (rounding to half).
  *
  *   M .. ldc, stream : as for gemm_f32 / gemm_f16_nt
- *   splits    : number of K ranges.  <= 0 lets the library choose exactly as
- *               gemm_f32 / gemm_f16_nt would (which may be no split, or the
- *               matrix-vector kernel); 1 never splits; larger values are cut
- *               to at most one range per 16 (fp32) or 64 (fp16) elements of K.
+ *   splits    : number of K ranges.  <= 0 lets the library choose: ranges
+ *               only when K >= 2048 and the product has few output tiles of
+ *               128 x 128 (16-bit: as many as keep tiles x ranges within 400
+ *               workgroups, a power of two, at least 2, ranges at least 256
+ *               deep; fp32: within 512, at least 3, at least 64 deep; at
+ *               most 64), never for the matrix-vector shapes (M or N <= 8);
+ *               1 never splits; larger values are cut to at most one range
+ *               per 16 (fp32) or 64 (fp16) elements of K.  Without a split
+ *               the call runs exactly as gemm_f32 / gemm_f16_nt.
  *   workspace : device memory, 16-byte aligned, of at least
  *               workspace_bytes >= gemm_*_splitk_workspace(M, N, K, splits)
  *               bytes; written and read by the call's kernels on `stream`,
@@ -214,17 +212,32 @@ MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int 
  *   bias, act, residual, ldr, C, ldc : as for gemm_f16_nt_ex (bias NULL,
  *          GEMM_ACT_NONE and residual NULL give the plain product).
  *
- * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  Other
- * layouts first copy each operand that is not K-contiguous (A for OP_T, B for
- * OP_N) into a K-contiguous workspace with a transposition kernel, then run
- * the A * B^T kernels -- except on the matrix-vector path (M <= 8 or N <= 8),
- * where a long operand stored K-major (B for OP_N when M is the small side,
- * A for OP_T when N is) is read in place, row by row, and the short one in
- * either layout: its ranges of K leave fp32 partial sums in the workspace and
- * the split-K reduction adds them in order.  The workspace comes from the
- * same stream-ordered, per-stream store as the split-K workspace.  Unknown
- * type, op or act values are GEMM_ERR_BAD_ARG; a workspace that cannot be
- * allocated is GEMM_ERR_WORKSPACE.
+ * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  The other
+ * layouts read the stored operands in place in products of at least 2^30
+ * multiply-adds (the register-staged wide tiles transpose 8 x 8 blocks of a
+ * K-major operand in registers on their way into LDS).  Smaller products
+ * first copy each operand that is not K-contiguous (A for OP_T, B for OP_N)
+ * into the workspace, transposed, then run the A * B^T kernels -- except on
+ * the matrix-vector path (M <= 8 or N <= 8), where a long operand stored
+ * K-major (B for OP_N when M is the small side, A for OP_T when N is) is read
+ * in place, row by row, and the short one in either layout: its ranges of K
+ * leave fp32 partial sums in the workspace and the split-K reduction adds
+ * them in order.  A product of few output tiles and long K (the rule of
+ * gemm_f16_nt_splitk's splits <= 0) is split into ranges of K -- on the
+ * transposed copies in the other layouts -- with the fused write-back applied
+ * by the ordered reduction, when the workspace also holds the ranges' fp32
+ * partial sums; with a smaller one it runs unsplit.
+ *
+ *   workspace       : device memory, 16-byte aligned, of at least
+ *                     gemm_ex_workspace(...) bytes for the same arguments
+ *                     (written and read by the call's kernels on `stream`, so
+ *                     not in use by other work until they finish); may be
+ *                     NULL when that size is 0.
+ *   workspace_bytes : its size.
+ *
+ * Unknown type, op or act values are GEMM_ERR_BAD_ARG; a workspace the call
+ * needs that is NULL, too small or misaligned is GEMM_ERR_WORKSPACE (checked
+ * before any work is enqueued).
  */
 enum { GEMM_TYPE_F16 = 0, GEMM_TYPE_BF16 = 1 };
 enum { GEMM_OP_N = 0, GEMM_OP_T = 1 };
@@ -235,7 +248,15 @@ MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K,
                           const void* bias, int act,
                           const void* residual, int ldr,
                           void* C, int ldc,
+                          void* workspace, unsigned long long workspace_bytes,
                           void* stream);
+
+/* Workspace bytes gemm_ex uses for these sizes, layouts and leading
+ * dimensions, split-K partial sums included (0 when none, or for arguments
+ * gemm_ex rejects).  Without the split-K part gemm_ex runs unsplit and needs
+ * only the rest. */
+MI355GEMM_API unsigned long long gemm_ex_workspace(int type, int op_a, int op_b, int M, int N,
+                                                   int K, int lda, int ldb);
 
 /* A static, human-readable message for a GEMM_* status code. */
 MI355GEMM_API const char* gemm_status_string(int status);
@@ -264,15 +285,14 @@ enum {
   GEMM_PATH_F16_MFMA = 6,       /* v_mfma f16 full tiles, 16-byte aligned rows    */
   GEMM_PATH_F16_GEMV = 7,       /* M <= 8 or N <= 8: matrix-vector kernel that    */
                                 /*   streams the long operand once (any ld/align) */
-  GEMM_PATH_F16_SPLITK = 8,     /* few output tiles, long K: K cut into ranges,   */
-  GEMM_PATH_F32_SPLITK = 9,     /*   fp32 partials, ordered reduction             */
-  GEMM_PATH_F16_STAGED = 10,    /* large ragged or unaligned: v_mfma f16 wide     */
-                                /*   tiles with register-staged loads (any shape, */
-                                /*   leading dimension, 2-byte alignment), masked */
-                                /*   stores; no copies                            */
-  GEMM_PATH_F32_PADDED = 11     /* the same for fp32 (at least 2^30 multiply-adds */
-                                /*   that the fp32 full tiles cannot read in      */
-                                /*   place, or whose K is not a multiple of 64)   */
+  GEMM_PATH_F16_SPLITK = 8,     /* gemm_ex only, long K over few output tiles: K   */
+                                /*   cut into ranges, fp32 partial sums in the    */
+                                /*   workspace, ordered reduction                 */
+  /* 9 is not used */
+  GEMM_PATH_F16_STAGED = 10     /* large ragged, unaligned or (gemm_ex) K-major:  */
+                                /*   v_mfma wide tiles with register-staged loads */
+                                /*   (any shape, leading dimension, 2-byte        */
+                                /*   alignment, layout), masked stores; no copies */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,
@@ -292,9 +312,9 @@ MI355GEMM_API int gemm_f16_nt_ex_path(int M, int N, int K,
                                       const void* residual, int ldr,
                                       const void* C, int ldc);
 
-/* For gemm_ex: the path of the A * B^T kernels that run after any
- * transposition of the operands (transposed copies are 16-byte aligned with
- * rows padded to a multiple of 8 elements). */
+/* For gemm_ex: the path of the kernels that run (after the transposed copies
+ * of a smaller product in another layout, which are 16-byte aligned with rows
+ * padded to a multiple of 8 elements). */
 MI355GEMM_API int gemm_ex_path(int type, int op_a, int op_b, int M, int N, int K,
                                const void* A, int lda,
                                const void* B, int ldb,

@@ -25,16 +25,12 @@ def splitk_auto(M, N, K, slab):
 
 
 def expected_f32_path(mode, M, N, K):
-    """For contiguous, 16-byte aligned operands."""
+    """For contiguous, 16-byte aligned operands.  The plain calls never split
+    K; what the full tiles cannot read in place runs on the edge kernel."""
     if mode == "general":
         return "f32_general"
-    if splitk_auto(M, N, K, 16):
-        return "f32_splitk"
     tiles = M % 64 == 0 and N % 64 == 0 and K % 16 == 0
-    pays = M * N * K >= 1 << 30
-    if (tiles and K % 64 == 0) or (tiles and not pays):
-        return "f32_mfma"
-    return "f32_padded" if pays else "f32_general"
+    return "f32_mfma" if tiles else "f32_general"
 
 
 def expected_f16_path(mode, M, N, K):
@@ -44,8 +40,6 @@ def expected_f16_path(mode, M, N, K):
         return "f16_zero"
     if min(M, N) <= 8:
         return "f16_gemv"
-    if splitk_auto(M, N, K, 64):
-        return "f16_splitk"
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
     if fast:
@@ -53,3 +47,23 @@ def expected_f16_path(mode, M, N, K):
     # the register-staged wide tiles take large products (from 2^30
     # multiply-adds, K at least 8) that the full tiles cannot read in place
     return "f16_staged" if M * N * K >= 1 << 30 and K >= 8 else "f16_general"
+
+
+def expected_ex_path(M, N, K, op_a, op_b):
+    """gemm_ex with the binding's workspace (contiguous, aligned operands)."""
+    nt = op_a == "n" and op_b == "t"
+    if K == 0:
+        return "f16_zero"
+    if min(M, N) <= 8:
+        return "f16_gemv"
+    if splitk_auto(M, N, K, 64):
+        return "f16_splitk"
+    large = M * N * K >= 1 << 30 and K >= 8
+    if not nt and large and (op_a == "n" or M >= 8) and (op_b == "t" or N >= 8):
+        return "f16_staged"        # K-major operands read in place
+    # NT in place, or the other layouts through 16-byte aligned transposed copies
+    fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
+                            (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
+    if fast:
+        return "f16_mfma"
+    return "f16_staged" if large else "f16_general"

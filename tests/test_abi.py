@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "mi355gemm.h")
 
 F32_MFMA, F32_GENERAL, F32_SCALE = 3, 2, 1
 F16_MFMA, F16_GENERAL, F16_ZERO, F16_GEMV = 6, 5, 4, 7
-F16_SPLITK, F32_SPLITK, F16_STAGED, F32_PADDED = 8, 9, 10, 11
+F16_SPLITK, F16_STAGED = 8, 10
 ALIGNED = 0x100000          # fake device addresses: only their alignment is looked at
 p = ctypes.c_void_p
 
@@ -40,6 +40,7 @@ def test_header_declares_the_abi():
                                          "gemm_f32_splitk", "gemm_f16_nt_splitk",
                                          "gemm_f32_splitk_workspace",
                                          "gemm_f16_nt_splitk_workspace", "gemm_ex",
+                                         "gemm_ex_workspace",
                                          "gemm_ex_path",
                                          "gemm_status_string", "gemm_f32_path",
                                          "gemm_f16_nt_path", "gemm_f16_nt_ex_path",
@@ -150,16 +151,17 @@ def test_path_selection(lib, monkeypatch):
     assert f32(lib, 4096, 4096, 4096) == F32_MFMA
     assert f32(lib, 256, 256, 256) == F32_MFMA and f32(lib, 1024, 1024, 1024) == F32_MFMA
     assert f32(lib, 4096, 4096, 4096, beta=0.5) == F32_MFMA
-    assert f32(lib, 4000, 4096, 4096) == F32_PADDED                 # ragged M, large
+    # ragged or unaligned fp32: the edge kernel reads the operands in place
+    assert f32(lib, 4000, 4096, 4096) == F32_GENERAL                # ragged M
     assert f32(lib, 4032, 4096, 4096) == F32_MFMA                   # 64-row tiles
     assert f32(lib, 192, 320, 48) == F32_MFMA
-    assert f32(lib, 4096, 4096, 4096, A=ALIGNED + 4) == F32_PADDED   # 4-byte aligned only
-    assert f32(lib, 4096, 4096, 4096, C=ALIGNED + 4) == F32_PADDED   # no copy, masked stores
-    assert f32(lib, 4096, 4096, 4000) == F32_PADDED                 # K not a multiple of 64
-    assert f32(lib, 2000, 2000, 2000) == F32_PADDED
-    assert f32(lib, 1024, 1024, 1008) == F32_MFMA                   # below 2^30: 16-deep slabs
-    assert f32(lib, 1000, 1000, 1000) == F32_GENERAL                # below 2^30, ragged
-    assert f32(lib, 4096, 4096, 4096, lda=1 << 28) == F32_PADDED    # 32-bit lane offsets
+    assert f32(lib, 4096, 4096, 4096, A=ALIGNED + 4) == F32_GENERAL  # 4-byte aligned only
+    assert f32(lib, 4096, 4096, 4096, C=ALIGNED + 4) == F32_GENERAL
+    assert f32(lib, 4096, 4096, 4000) == F32_MFMA                   # K % 16 == 0: 16-deep slabs
+    assert f32(lib, 2000, 2000, 2000) == F32_GENERAL
+    assert f32(lib, 1024, 1024, 1008) == F32_MFMA
+    assert f32(lib, 1000, 1000, 1000) == F32_GENERAL
+    assert f32(lib, 4096, 4096, 4096, lda=1 << 28) == F32_MFMA      # register-staged tiles
     assert f32(lib, 256, 256, 256, lda=258) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_MFMA
     # ragged or unaligned and large: copies where needed, masked full tiles
@@ -191,25 +193,27 @@ def test_path_selection(lib, monkeypatch):
 
 
 def test_split_k_plans(lib, monkeypatch):
-    """Split-K applies to products with K >= 2048 and few 128 x 128 output
-    tiles.  16-bit: tiles x ranges within 400 workgroups, ranges at least 256
-    deep, a power of two, at least two.  fp32: within 512 workgroups, at least
-    64 deep, at least three.  At most 64 ranges, at most one per K slab."""
+    """The plain calls never split K (they need no workspace).  The explicit
+    calls' automatic rule (splits <= 0) splits products with K >= 2048 and
+    few 128 x 128 output tiles.  16-bit: tiles x ranges within 400
+    workgroups, ranges at least 256 deep, a power of two, at least two.
+    fp32: within 512 workgroups, at least 64 deep, at least three.  At most
+    64 ranges, at most one per K slab; never for the matrix-vector shapes."""
     monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
-    assert f16(lib, 512, 512, 16384) == F16_SPLITK and f16(lib, 128, 128, 16384) == F16_SPLITK
-    assert f16(lib, 1024, 1024, 4096) == F16_SPLITK and f16(lib, 300, 200, 5000) == F16_SPLITK
-    assert f16(lib, 512, 512, 1024) == F16_MFMA                       # K below 2048
-    assert f16(lib, 2048, 2048, 8192) == F16_MFMA                     # 256 tiles
-    assert f16(lib, 1536, 1536, 4096) == F16_SPLITK                   # 144 tiles: 2 ranges
-    assert f16(lib, 1792, 1792, 4096) == F16_SPLITK                   # 196 tiles: 2 ranges
-    assert f16(lib, 2304, 2304, 4096) == F16_MFMA                     # 324 tiles: 1 range
-    assert f16(lib, 8, 512, 16384) == F16_GEMV                        # the vector kernel first
-    assert f32(lib, 512, 512, 16384) == F32_SPLITK and f32(lib, 100, 70, 3000) == F32_SPLITK
-    assert f32(lib, 4096, 4096, 4096) == F32_MFMA and f32(lib, 512, 512, 16384, alpha=0.0) == 1
+    assert f16(lib, 512, 512, 16384) == F16_MFMA and f16(lib, 128, 128, 16384) == F16_MFMA
+    assert f16(lib, 300, 200, 5000) == F16_GENERAL
+    assert f32(lib, 512, 512, 16384) == F32_MFMA and f32(lib, 100, 70, 3000) == F32_GENERAL
     ws16, ws32 = lib.gemm_f16_nt_splitk_workspace, lib.gemm_f32_splitk_workspace
     # 16 tiles -> 16 ranges of 16 slabs of 64
     assert ws16(512, 512, 16384, 0) == 16 * 512 * 512 * 4
-    assert ws16(1, 4096, 4096, 0) == 0 and ws16(512, 512, 1024, 0) == 0
+    assert ws16(128, 128, 16384, 0) > 0 and ws16(1024, 1024, 4096, 0) > 0
+    assert ws16(512, 512, 1024, 0) == 0                                # K below 2048
+    assert ws16(2048, 2048, 8192, 0) == 0                              # 256 tiles
+    assert ws16(1536, 1536, 4096, 0) == 2 * 1536 * 1536 * 4            # 144 tiles: 2 ranges
+    assert ws16(1792, 1792, 4096, 0) == 2 * 1792 * 1792 * 4            # 196 tiles: 2 ranges
+    assert ws16(2304, 2304, 4096, 0) == 0                              # 324 tiles: 1 range
+    assert ws16(8, 512, 16384, 0) == 0                                 # the vector kernel
+    assert ws16(1, 4096, 4096, 0) == 0
     assert ws16(100, 100, 1000, 3) == 3 * 128 * 128 * 4                # 16 slabs -> 6, 6, 4
     assert ws16(100, 100, 1000, 5) == 4 * 128 * 128 * 4                # 16 slabs -> 4 x 4
     assert ws16(64, 64, 100, 50) == 2 * 128 * 128 * 4                  # one range per slab
@@ -217,6 +221,7 @@ def test_split_k_plans(lib, monkeypatch):
     assert ws16(300, 200, 5000, 0) == 16 * 384 * 256 * 4               # 5000 // 256 -> 16
     assert ws16(128, 128, 65536, 0) == 64 * 128 * 128 * 4              # at most 64 ranges
     assert ws32(512, 512, 16384, 0) == 32 * 512 * 512 * 4
+    assert ws32(100, 70, 3000, 0) > 0 and ws32(4096, 4096, 4096, 0) == 0
     assert ws32(300, 257, 4099, 0) == 52 * 384 * 384 * 4               # 257 slabs / 56 -> 5 each
     assert ws32(130, 129, 40, 7) == 3 * 256 * 256 * 4                  # 3 slabs of 16
     monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
@@ -234,22 +239,44 @@ def ex(lib, type_, op_a, op_b, M, N, K, A=ALIGNED, lda=None, B=ALIGNED, ldb=None
                             p(res) if res else None, ldr, p(C) if C else None, ldc)
 
 
+def ex_ws(lib, type_, op_a, op_b, M, N, K, lda=None, ldb=None):
+    lda = (max(1, K) if op_a == 0 else max(1, M)) if lda is None else lda
+    ldb = (max(1, N) if op_b == 0 else max(1, K)) if ldb is None else ldb
+    return lib.gemm_ex_workspace(type_, op_a, op_b, M, N, K, lda, ldb)
+
+
 def test_gemm_ex_validation_and_paths(lib, monkeypatch):
-    """Layouts: op N/T per operand with their leading-dimension rules; the
-    A * B^T kernels behind them; unknown enumerations are GEMM_ERR_BAD_ARG."""
+    """Layouts: op N/T per operand with their leading-dimension rules; large
+    products read K-major operands in place (the register-staged wide tiles),
+    smaller ones through transposed copies in the workspace; unknown
+    enumerations are GEMM_ERR_BAD_ARG."""
     monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
     N_, T_ = 0, 1
     for t in (0, 1):
         assert ex(lib, t, N_, T_, 5376, 5376, 2048) == F16_MFMA
-        assert ex(lib, t, N_, N_, 5376, 5376, 2048) == F16_MFMA      # B through a copy
-        assert ex(lib, t, T_, N_, 5376, 5376, 2048) == F16_MFMA
+        assert ex(lib, t, N_, N_, 5376, 5376, 2048) == F16_STAGED    # B read K-major in place
+        assert ex(lib, t, T_, N_, 5376, 5376, 2048) == F16_STAGED
+        assert ex(lib, t, T_, T_, 5376, 5376, 2048) == F16_STAGED
         assert ex(lib, t, T_, T_, 5000, 3001, 1537) == F16_STAGED
-        assert ex(lib, t, T_, T_, 500, 301, 153) == F16_GENERAL
+        assert ex(lib, t, T_, T_, 500, 301, 153) == F16_GENERAL      # through copies
         assert ex(lib, t, N_, N_, 1, 4096, 4096) == F16_GEMV
-        assert ex(lib, t, T_, N_, 512, 512, 16384) == F16_SPLITK
+        assert ex(lib, t, T_, N_, 512, 512, 16384) == F16_SPLITK     # with its workspace
         # a copy has aligned, padded rows whatever the original alignment
         assert ex(lib, t, T_, T_, 256, 256, 64, A=ALIGNED + 2, lda=257) == F16_MFMA
         assert ex(lib, t, N_, T_, 256, 256, 64, A=ALIGNED + 2, lda=67) == F16_GENERAL
+        # a K-major operand needs 8 of its M or N columns for the wide tiles
+        assert ex(lib, t, T_, T_, 1024 * 1024, 9, 1024) == F16_STAGED
+    # workspace sizes: none for NT, the wide tiles and the plain vector
+    # kernel; copies for smaller products; partial sums for K-major vectors
+    assert ex_ws(lib, 0, N_, T_, 5376, 5376, 2048) == 0
+    assert ex_ws(lib, 0, N_, N_, 5376, 5376, 2048) == 0
+    assert ex_ws(lib, 0, N_, T_, 1, 4096, 4096) == 0
+    assert ex_ws(lib, 0, T_, T_, 500, 301, 153) == (500 * 160 * 2 + 255) // 256 * 256
+    assert ex_ws(lib, 0, N_, N_, 100, 300, 153) == 300 * 160 * 2
+    assert ex_ws(lib, 0, N_, N_, 1, 16384, 4096) > 0                  # K-major weight
+    assert ex_ws(lib, 0, N_, T_, 512, 512, 16384) == 16 * 512 * 512 * 4   # split-K partials
+    assert ex_ws(lib, 0, N_, N_, 512, 512, 16384) == 512 * 16384 * 2 + 16 * 512 * 512 * 4
+    assert ex_ws(lib, 0, N_, T_, -1, 5, 5) == 0 and ex_ws(lib, 7, N_, T_, 5, 5, 5) == 0
     assert ex(lib, 2, 0, 1, 8, 8, 8) == -6 and ex(lib, 0, 2, 1, 8, 8, 8) == -6
     assert ex(lib, 0, 0, -1, 8, 8, 8) == -6 and ex(lib, 0, 0, 1, 8, 8, 8, act=5) == -6
     # leading dimensions follow the stored shapes
@@ -261,8 +288,18 @@ def test_gemm_ex_validation_and_paths(lib, monkeypatch):
     monkeypatch.setenv("MI355GEMM_FORCE_PATH", "general")
     assert ex(lib, 1, N_, N_, 5376, 5376, 2048) == F16_GENERAL
     null = None
-    assert lib.gemm_ex(3, 0, 1, 4, 4, 4, p(ALIGNED), 4, p(ALIGNED), 4, null, 0, null, 4,
-                       p(ALIGNED), 4, null) == -6
+    a = p(ALIGNED)
+    assert lib.gemm_ex(3, 0, 1, 4, 4, 4, a, 4, a, 4, null, 0, null, 4, a, 4, null, 0, null) == -6
+    monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
+    # a workspace the call needs is checked before any work: missing, too
+    # small or misaligned
+    need = ex_ws(lib, 0, T_, T_, 500, 301, 153)
+    assert lib.gemm_ex(0, T_, T_, 500, 301, 153, a, 500, a, 153, null, 0, null, 0, a, 301, null,
+                       0, null) == -7
+    assert lib.gemm_ex(0, T_, T_, 500, 301, 153, a, 500, a, 153, null, 0, null, 0, a, 301, a,
+                       need - 1, null) == -7
+    assert lib.gemm_ex(0, T_, T_, 500, 301, 153, a, 500, a, 153, null, 0, null, 0, a, 301,
+                       p(ALIGNED + 8), need, null) == -7
 
 
 def test_split_k_workspace_errors_need_no_device(lib):

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from dense_gemm_sgemm_amd import inputs
-from expect import expected_f16_path
+from expect import expected_ex_path
 from tolerance import check16
 
 torch = pytest.importorskip("torch")
@@ -81,8 +81,10 @@ def run_ex(A, B, op_a, op_b, fmt, M, N, bias=None, act="none", res=None, expect=
     return to_host(dC, fmt)
 
 
-# Shapes reach each kernel: fast tiles 256 x 256, 256 x 224, 128 x 128 and 128 x 192, the
-# edge kernel (ragged, odd K), the matrix-vector kernel both ways, split-K.
+# Shapes reach each kernel: fast tiles 256 x 256, 256 x 224, 128 x 128 and 128 x 192 (in the
+# other layouts on transposed copies), the edge kernel (ragged, odd K), the matrix-vector
+# kernel both ways, split-K, and the register-staged wide tiles (1000 x 1001 x 1111: every
+# layout read in place, the K-major operands transposed in registers).
 SHAPES = [(256, 256, 64), (512, 448, 128), (128, 128, 192), (384, 576, 192), (133, 70, 45),
           (257, 255, 65), (1, 300, 777), (300, 3, 1000), (4, 129, 4100), (512, 512, 16384),
           (300, 200, 5000), (1000, 1001, 1111)]
@@ -96,7 +98,7 @@ def test_layouts(shape, layout, fmt):
     op_a, op_b = layout
     sa, sb = stored_shapes(M, N, K, op_a, op_b)
     A, B = inputs.operands16(sa, sb, fmt)
-    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect=expected_f16_path("auto", M, N, K))
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect=expected_ex_path(M, N, K, op_a, op_b))
     ref, sab = reference(A, B, op_a, op_b, fmt)
     check16(got, ref, sab, fmt)
 
@@ -129,6 +131,77 @@ def test_layouts_fused(shape, layout, fmt, act, use_bias, use_res):
     babs = 0.0 if bias is None else np.abs(dec(bias))[None, :]
     rabs = 0.0 if res is None else np.abs(dec(res))
     check16(got, ref, sab, fmt, babs, rabs, fused=True)
+
+
+# The register-staged wide tiles on K-major operands: ragged M and N at every
+# residue of a K-major operand's 8-column pieces (1030 = 8 x 128 + 6, 1100 = 8 x
+# 137 + 4, 1001, 1023, 2049 = 8 x 256 + 1), K tails of 9, 23 and 4 elements and a
+# slab wholly past K (777, 1111, 1100), a 256 x 224 tile choice (N = 3001), and
+# an N of 9 (one column past a piece) for a K-major B.
+STAGED_LAYOUT_SHAPES = [(1030, 1100, 1000), (1000, 1001, 1111), (1023, 2049, 777),
+                        (2049, 1023, 1100), (700, 3001, 600), (1024 * 128, 9, 1024)]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", LAYOUTS[1:], ids=lambda l: "".join(l))
+@pytest.mark.parametrize("shape", STAGED_LAYOUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_layouts_staged_in_place(shape, layout, fmt):
+    M, N, K = shape
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    dA, dB = to_dev(A, fmt), to_dev(B, fmt)
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=dtype_of(fmt))
+    assert dg.ex_path(dA, dB, dC, op_a, op_b) == "f16_staged"
+    assert dg.ex_workspace_bytes(dA, dB, dC, op_a, op_b) == 0
+    dg.gemm_ex(dA, dB, dC, op_a, op_b)
+    torch.cuda.synchronize()
+    ref, sab = reference(A, B, op_a, op_b, fmt)
+    check16(to_host(dC, fmt), ref, sab, fmt)
+
+
+def test_layouts_staged_unaligned_exact_and_fused():
+    """K-major operands one element into their buffers with odd leading
+    dimensions, C unaligned; small-integer operands make every product exact
+    (bit for bit against the exact sum rounded once).  Then the fused
+    write-back on the same path."""
+    for (op_a, op_b) in LAYOUTS[1:]:
+        M, N, K = 1030, 1100, 1003
+        sa, sb = stored_shapes(M, N, K, op_a, op_b)
+        A = inputs.small_ints(sa, 51, -2, 2, np.float16)
+        B = inputs.small_ints(sb, 52, -2, 2, np.float16)
+        lda, ldb, ldc = sa[1] + 3, sb[1] + 1, N + 5
+        bufA = torch.zeros(sa[0] * lda + 2, device=DEV, dtype=torch.float16)
+        bufB = torch.zeros(sb[0] * ldb + 2, device=DEV, dtype=torch.float16)
+        bufC = torch.full((M * ldc + 2,), 5.0, device=DEV, dtype=torch.float16)
+        dA = bufA[1:1 + sa[0] * lda].view(sa[0], lda)[:, :sa[1]]
+        dB = bufB[1:1 + sb[0] * ldb].view(sb[0], ldb)[:, :sb[1]]
+        dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
+        dA.copy_(to_dev(A, "f16"))
+        dB.copy_(to_dev(B, "f16"))
+        assert dg.ex_path(dA, dB, dC, op_a, op_b) == "f16_staged"
+        dg.gemm_ex(dA, dB, dC, op_a, op_b)
+        torch.cuda.synchronize()
+        An, Bn = oracle.nt_operands(A, B, op_a, op_b)
+        exact = An.astype(np.float64) @ Bn.astype(np.float64).T
+        got = dC.contiguous().cpu().numpy()
+        assert np.array_equal(got.view(np.uint16), oracle.half_from_double(exact).view(np.uint16))
+        full = bufC.cpu().numpy()
+        mask = np.ones(full.shape, bool)
+        idx = 1 + np.arange(M)[:, None] * ldc + np.arange(N)[None, :]
+        mask[idx.ravel()] = False
+        assert np.all(full[mask] == 5.0)
+    for (op_a, op_b) in LAYOUTS[1:]:
+        M, N, K = 1000, 1001, 1111
+        sa, sb = stored_shapes(M, N, K, op_a, op_b)
+        A, B = inputs.operands16(sa, sb, "f16")
+        rng = np.random.default_rng(44)
+        bias = rng.normal(0, 1.5, N).astype(np.float16)
+        res = rng.normal(0, 2.0, (M, N)).astype(np.float16)
+        got = run_ex(A, B, op_a, op_b, "f16", M, N, bias, "silu", res, expect="f16_staged")
+        ref, sab = reference(A, B, op_a, op_b, "f16", bias, "silu", res)
+        check16(got, ref, sab, "f16", np.abs(bias.astype(np.float64))[None, :],
+                np.abs(res.astype(np.float64)), fused=True)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
@@ -191,7 +264,7 @@ def test_workload_5376_layouts(fmt, layout):
     op_a, op_b = layout
     sa, sb = stored_shapes(M, N, K, op_a, op_b)
     A, B = inputs.operands16(sa, sb, fmt, dist="uniform")
-    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect="f16_mfma")
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect=expected_ex_path(M, N, K, op_a, op_b))
     An, Bn = oracle.nt_operands(A, B, op_a, op_b)
     ref = oracle.gemm_16_nt_exact(An, Bn, fmt)
     sab = oracle.gemm_16_nt_exact(absval(An, fmt), absval(Bn, fmt), fmt)

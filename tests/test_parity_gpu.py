@@ -541,11 +541,23 @@ SPLITK_SHAPES = [(128, 128, 16384), (512, 512, 16384), (300, 200, 5000), (1000, 
                  (136, 264, 2111), (64, 1000, 4099)]
 
 
+def gpu_f16_splitk(A, B, splits=0):
+    """gemm_f16_nt_splitk with the binding's own workspace; asserts that the
+    library's rule splits these sizes when splits <= 0."""
+    M, N, K = A.shape[0], B.shape[0], A.shape[1]
+    if splits <= 0:
+        assert dg.splitk_workspace_bytes("f16", M, N, K, 0) > 0
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+    dg.gemm_f16_nt_splitk(dev(A), dev(B), dC, splits=splits)
+    torch.cuda.synchronize()
+    return dC.cpu().numpy()
+
+
 @pytest.mark.parametrize("shape", SPLITK_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_f16_splitk_auto(shape):
     M, N, K = shape
     A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
-    got = gpu_f16(A, B, expect="f16_splitk")
+    got = gpu_f16_splitk(A, B)
     f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
 
 
@@ -626,6 +638,8 @@ def test_splitk_binding_workspace_on_a_side_stream():
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES[:4])
 def test_f16_splitk_fused(shape, act, use_bias, use_res):
+    """The fused write-back on gemm_ex's split-K path (the binding passes a
+    workspace of the size query's bytes), in place when there is a residual."""
     M, N, K = shape
     A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
     dA, dB = dev(A), dev(B)
@@ -633,8 +647,9 @@ def test_f16_splitk_fused(shape, act, use_bias, use_res):
     dres = dev(res) if res is not None else None
     dC = dres if dres is not None else torch.full((M, N), float("nan"), device=DEV,
                                                   dtype=torch.float16)
-    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) == "f16_splitk"
-    dg.gemm_f16_nt_ex(dA, dB, dC, dbias, act, dres)          # in place when there is a residual
+    assert dg.ex_path(dA, dB, dC, "n", "t", dbias, act, dres) == "f16_splitk"
+    assert dg.f16_nt_ex_path(dA, dB, dC, dbias, act, dres) != "f16_splitk"
+    dg.gemm_ex(dA, dB, dC, "n", "t", dbias, act, dres)
     torch.cuda.synchronize()
     check_ex(dC.cpu().numpy(), A, B, bias, act, res)
 
@@ -647,7 +662,11 @@ F32_SPLITK_SHAPES = [(512, 512, 16384), (100, 70, 3000), (300, 257, 4099), (128,
 def test_f32_splitk_auto(shape, beta):
     M, N, K = shape
     A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
-    got = gpu_f32(A, B, 1.0, beta, C.copy(), expect="f32_splitk")
+    assert dg.splitk_workspace_bytes("f32", M, N, K, 0) > 0
+    dC = dev(C)
+    dg.gemm_f32_splitk(dev(A), dev(B), dC, 1.0, beta)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
     tol = f32_tolerance(K, np.abs(A).max(), np.abs(B).max(), 1.0, beta, np.abs(C).max())
     f32_check(got, oracle.gemm_f32(A, B, 1.0, beta, C), tol)
 
@@ -666,15 +685,21 @@ def test_f32_splitk_explicit(splits):
 
 def test_f32_splitk_beta_zero_ignores_nan_and_repeats():
     A, B, _ = inputs.sgemm_operands(512, 512, 16384)
-    one = gpu_f32(A, B, 1.0, 0.0, expect="f32_splitk")      # C prefilled with NaN
+
+    def run():
+        dC = torch.full((512, 512), float("nan"), device=DEV)
+        dg.gemm_f32_splitk(dev(A), dev(B), dC, 1.0, 0.0)
+        torch.cuda.synchronize()
+        return dC.cpu().numpy()
+    one = run()
     assert np.all(np.isfinite(one))
-    assert np.array_equal(one, gpu_f32(A, B, 1.0, 0.0))
+    assert np.array_equal(one, run())
 
 
 def test_workload_hgemm_splitk():
     """The 128 x 128 x 16384 product of one output tile, every output checked."""
     A, B = inputs.workload_operands("hgemm_nt_128x128x16384")
-    got = gpu_f16(A, B, expect="f16_splitk")
+    got = gpu_f16_splitk(A, B)
     res = f16_check(got, oracle.gemm_f16_nt_exact(A, B),
                     oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
     say("[hgemm_nt_128x128x16384] checked %d outputs, max %.2f ulp" % (res["count"],
@@ -921,38 +946,35 @@ def test_f32_stream64_alpha_beta_padded_and_exact():
     assert np.array_equal(gpu_f32(Ai, Bi, expect="f32_mfma").astype(np.float64), oracle.gemm_f32(Ai, Bi))
 
 
-# The padded fp32 path: at least 2^30 multiply-adds that the streaming kernels
-# cannot read in place.  1030 x 1100 x 1000: ragged M, N and K, 64 x 64 tiles
-# (fewer 128 x 128 tiles than CUs), both operands copied; 2048 x 2048 x 2000:
-# K not a multiple of 64, 128 x 128 tiles; 2000^3: ragged everything on
-# 128 x 128 tiles.  The masked stores leave C outside M x N untouched.
-PADDED32_SHAPES = [(1030, 1100, 1000), (2048, 2048, 2000), (2000, 2000, 2000)]
+# Large ragged or unaligned fp32 products run on the edge kernel, which reads
+# the operands in place: 1030 x 1100 x 1000 (ragged M, N and K), 2048 x 2048 x
+# 2000 (K not a multiple of 64: the 16-deep full tiles), 2000^3.  The masked
+# stores leave C outside M x N untouched.
+RAGGED32_SHAPES = [(1030, 1100, 1000), (2048, 2048, 2000), (2000, 2000, 2000)]
 
 
-@pytest.mark.parametrize("shape", PADDED32_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_f32_padded_path(shape):
+@pytest.mark.parametrize("shape", RAGGED32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_ragged_large(shape):
     M, N, K = shape
     A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
     dA, dB = dev(A), dev(B)
     big = torch.full((M + 3, N + 5), 7.0, device=DEV)
     dC = big[1:1 + M, 2:2 + N]                 # C not 16-byte aligned, odd leading dimension
     dC.copy_(dev(C))
-    assert dg.f32_path(dA, dB, dC, 0.75, 0.5) == "f32_padded"
+    assert dg.f32_path(dA, dB, dC, 0.75, 0.5) == "f32_general"
     dg.gemm_f32(dA, dB, dC, 0.75, 0.5)
     torch.cuda.synchronize()
     got = big.cpu().numpy()
-    rows, cols = sample_points(M, N, tile_windows(M, N, 128, 128), n_random=5000)
-    ref = oracle.gemm_f32_points(A, B, rows, cols, 0.75, 0.5, C)
-    f32_check(got[1:1 + M, 2:2 + N][rows, cols], ref, f32_tolerance(K, 1.0, 1.0, 0.75, 0.5, 1.0))
+    ref = oracle.gemm_f32(A, B, 0.75, 0.5, C)
+    f32_check(got[1:1 + M, 2:2 + N], ref, f32_tolerance(K, 1.0, 1.0, 0.75, 0.5, 1.0))
     outside = np.ones(got.shape, bool)
     outside[1:1 + M, 2:2 + N] = False
     assert np.all(got[outside] == 7.0)
 
 
-def test_f32_padded_path_copy_one_or_none():
-    """A starting one float into its buffer (only A is copied), then aligned
-    operands with an unaligned C (no copies: the masked kernel reads A and B
-    in place); small integers make both results exact."""
+def test_f32_unaligned_operand_and_c_exact():
+    """A starting one float into its buffer, then aligned operands with an
+    unaligned C; small integers make both results exact."""
     M, N, K = 1024, 1024, 1024
     A = inputs.small_ints((M, K), 21, -3, 3, np.float32)
     B = inputs.small_ints((K, N), 22, -3, 3, np.float32)
@@ -961,13 +983,13 @@ def test_f32_padded_path_copy_one_or_none():
     dA = bufA[1:].view(M, K)
     dA.copy_(dev(A))
     dC = torch.full((M, N), float("nan"), device=DEV)
-    assert dg.f32_path(dA, dev(B), dC) == "f32_padded"
+    assert dg.f32_path(dA, dev(B), dC) == "f32_general"
     dg.gemm_f32(dA, dev(B), dC)
     torch.cuda.synchronize()
     assert np.array_equal(dC.cpu().numpy().astype(np.float64), ref)
     bufC = torch.full((M * N + 1,), float("nan"), device=DEV)
     dC2 = bufC[1:].view(M, N)
-    assert dg.f32_path(dev(A), dev(B), dC2) == "f32_padded"
+    assert dg.f32_path(dev(A), dev(B), dC2) == "f32_general"
     dg.gemm_f32(dev(A), dev(B), dC2)
     torch.cuda.synchronize()
     assert np.array_equal(dC2.cpu().numpy().astype(np.float64), ref)

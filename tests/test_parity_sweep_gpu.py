@@ -1,7 +1,7 @@
 """A seeded random sweep across the paths: shapes drawn so that every kernel
-family is reached (streaming, register-staged, padded, edge, split-K,
-matrix-vector), with padded leading dimensions and, for fp32, random alpha
-and beta.  Products up to 2^27 multiply-adds are compared element by element
+family is reached (streaming, register-staged full and wide tiles, edge,
+split-K through the explicit calls, matrix-vector), with padded leading
+dimensions and, for fp32, random alpha and beta.  Products up to 2^27 multiply-adds are compared element by element
 with the oracle, larger ones on sampled outputs."""
 from __future__ import annotations
 
@@ -29,7 +29,7 @@ def draw(seed):
         M, N, K = (int(x) for x in rng.integers(1, 300, 3))
     elif family == 1:     # whole tiles
         M, N, K = (int(x) for x in 64 * rng.integers(1, 40, 3))
-    elif family == 2:     # large and ragged (register-staged fp16, padded fp32)
+    elif family == 2:     # large and ragged (register-staged wide fp16 tiles, fp32 edge)
         M, N, K = (int(x) for x in rng.integers(900, 2600, 3))
     elif family == 3:     # few tiles, long K (split-K)
         M, N, K = int(rng.integers(1, 400)), int(rng.integers(1, 400)), int(rng.integers(2048, 9000))
@@ -39,7 +39,7 @@ def draw(seed):
             M, N = N, M
     pad = int(rng.choice([0, 0, 1, 4, 8]))
     alpha, beta = [(1.0, 0.0), (0.5, 1.0), (-1.5, 0.25)][int(rng.integers(0, 3))]
-    return kind, M, N, K, pad, alpha, beta
+    return kind, M, N, K, pad, alpha, beta, int(family) == 3
 
 
 SEEDS = list(range(48))
@@ -47,7 +47,7 @@ SEEDS = list(range(48))
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_sweep(seed):
-    kind, M, N, K, pad, alpha, beta = draw(seed)
+    kind, M, N, K, pad, alpha, beta, split = draw(seed)
     print("\n[sweep] seed %d %s %dx%dx%d pad %d alpha %g beta %g" % (seed, kind, M, N, K, pad, alpha, beta),
           flush=True)
     sys.stdout.flush()
@@ -64,7 +64,11 @@ def test_random_sweep(seed):
         bB = torch.zeros(K, N + pad, device=DEV); bB[:, :N] = torch.from_numpy(B).to(DEV)
         bC = torch.full((M, N + pad), 3.0, device=DEV); bC[:, :N] = torch.from_numpy(C).to(DEV)
         path = dg.f32_path(bA[:, :K], bB[:, :N], bC[:, :N], alpha, beta)
-        dg.gemm_f32(bA[:, :K], bB[:, :N], bC[:, :N], alpha, beta)
+        if split:
+            path += " (split-K call)"
+            dg.gemm_f32_splitk(bA[:, :K], bB[:, :N], bC[:, :N], alpha, beta)
+        else:
+            dg.gemm_f32(bA[:, :K], bB[:, :N], bC[:, :N], alpha, beta)
         torch.cuda.synchronize()
         got = bC.cpu().numpy()
         assert np.all(got[:, N:] == 3.0)
@@ -79,7 +83,11 @@ def test_random_sweep(seed):
         bB = torch.zeros(N, K + pad, device=DEV, dtype=torch.float16); bB[:, :K] = torch.from_numpy(B).to(DEV)
         bC = torch.full((M, N + pad), 3.0, device=DEV, dtype=torch.float16)
         path = dg.f16_nt_path(bA[:, :K], bB[:, :K], bC[:, :N])
-        dg.gemm_f16_nt(bA[:, :K], bB[:, :K], bC[:, :N])
+        if split:
+            path += " (split-K call)"
+            dg.gemm_f16_nt_splitk(bA[:, :K], bB[:, :K], bC[:, :N])
+        else:
+            dg.gemm_f16_nt(bA[:, :K], bB[:, :K], bC[:, :N])
         torch.cuda.synchronize()
         got = bC.cpu().numpy()
         assert np.all(got[:, N:] == 3.0)

@@ -1,7 +1,8 @@
-"""Two host threads calling the library at once, each on its own stream, with
-calls whose paths take a workspace from the library's per-stream store
-(padded copies and split-K partials) mixed with plain ones.  Every result must
-equal the one-thread result bit for bit."""
+"""Two host threads calling the library at once, each on its own stream:
+plain calls (the streaming, edge and register-staged kernels) mixed with
+calls that take a workspace (explicit split-K and gemm_ex's transposed
+copies, the workspace taken per call from torch's allocator on the thread's
+stream).  Every result must equal the one-thread result bit for bit."""
 from __future__ import annotations
 
 import threading
@@ -15,21 +16,31 @@ import dense_gemm_sgemm_amd as dg  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SHAPES = [("f32", (1030, 1100, 1000)), ("f32", (512, 512, 16384)), ("f16", (1000, 1030, 1100)),
-          ("f16", (128, 128, 16384)), ("f32", (1024, 1024, 1024))]
+SHAPES = [("f32", (1030, 1100, 1000)), ("f32_splitk", (512, 512, 16384)),
+          ("f16", (1000, 1030, 1100)), ("f16_splitk", (128, 128, 16384)),
+          ("f32", (1024, 1024, 1024)), ("ex_nn", (500, 301, 153)), ("ex_nn", (1000, 1030, 1100))]
 
 
 def make(kind, M, N, K):
-    if kind == "f32":
+    if kind.startswith("f32"):
         A, B, _ = inputs.sgemm_operands(M, N, K)
         return torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV), torch.float32
     A, B = inputs.hgemm_nt_operands(M, N, K)
-    return torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV), torch.float16
+    dA, dB = torch.from_numpy(A).to(DEV), torch.from_numpy(B).to(DEV)
+    if kind == "ex_nn":
+        dB = dB.t().contiguous()            # B stored K x N
+    return dA, dB, torch.float16
 
 
 def run(kind, A, B, C, stream):
     if kind == "f32":
         dg.gemm_f32(A, B, C, 1.0, 0.0, stream=stream)
+    elif kind == "f32_splitk":
+        dg.gemm_f32_splitk(A, B, C, 1.0, 0.0, stream=stream)
+    elif kind == "f16_splitk":
+        dg.gemm_f16_nt_splitk(A, B, C, stream=stream)
+    elif kind == "ex_nn":
+        dg.gemm_ex(A, B, C, "n", "n", stream=stream)
     else:
         dg.gemm_f16_nt(A, B, C, stream=stream)
 

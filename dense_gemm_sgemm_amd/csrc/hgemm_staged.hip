@@ -172,12 +172,25 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   //
   // With BN = 224 the B waves have 7 chunk rows (u < 7) or 28 blocks (lanes
   // with mb >= 28 re-read block mb - 4 and write nothing).
+  //
+  // Every selection below between two variables is written on values (+x):
+  // a conditional on two lvalues selects between their addresses, and the
+  // captured variables behind such an address stay in scratch memory.  For
+  // the same reason the operand's layout is a compile-time argument of each
+  // staging step (by_role), never a run-time flag inside one.
   const int t = tid & 127;
-  const bool stA = tid < 128;                  // wave-uniform
-  const bool trans = stA ? TA : TB;            // this wave's operand is K-major
-  const half_t* const X = stA ? p.A : p.B;
-  const int64_t ldx = stA ? p.lda : p.ldb;
-  const int limx = stA ? p.M : p.N, bx = stA ? BM : BN;
+  const bool stA = wave < 2;                   // wave-uniform
+  const half_t* const X = stA ? +p.A : +p.B;
+  const int64_t ldx = stA ? +p.lda : +p.ldb;
+  const int limx = stA ? +p.M : +p.N, bx = stA ? BM : BN;
+  auto by_role = [&](auto&& f) __attribute__((always_inline)) {
+    if constexpr (TA == TB) {
+      f(std::bool_constant<TA>());
+    } else {
+      if (stA) f(std::bool_constant<TA>());
+      else f(std::bool_constant<TB>());
+    }
+  };
   int cj = 0, ct = 0, cm0 = 0, cn0 = 0;        // the load target: slab ct of tile cj
   origin(0, cm0, cn0);
   const int kmax = p.K - 8;
@@ -194,12 +207,15 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   uint32_t coff = 0;         // the piece's column byte offset in its K row
   uint32_t toff = 0;         // the piece's K row byte offset from the slab's base row
   int tbase_k = 0;           // the slab's base K row (wave-uniform)
-  auto set_offsets = [&]() __attribute__((always_inline)) {
-    const int x0 = stA ? cm0 : cn0;
-    if (!trans) {
+  auto set_offsets = [&](auto tr) __attribute__((always_inline)) {
+    constexpr bool trans = decltype(tr)::value;
+    const int x0 = stA ? +cm0 : +cn0;
+    if constexpr (!trans) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        int row = x0 + (t >> 2) + 32 * u;
+        // the B waves of a 224-wide tile load their last chunk row again
+        const int ue = 32 * u < bx ? u : u - 1;
+        int row = x0 + (t >> 2) + 32 * ue;
         row = row < limx ? row : limx - 1;
         roff[u] = (uint32_t)((int64_t)(row - x0) * ldx * 2);
       }
@@ -208,43 +224,50 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
       coff = (uint32_t)(2 * (c < limx - 8 ? c : limx - 8));
     }
   };
-  auto set_koff = [&]() __attribute__((always_inline)) {
+  auto set_koff = [&](auto tr) __attribute__((always_inline)) {
+    constexpr bool trans = decltype(tr)::value;
     const int k0 = ct * C::BK;
-    if (!trans) {
+    if constexpr (!trans) {
       const int k = k0 + 8 * lchunk;
-      koff = (uint32_t)(2 * (k < kmax ? k : kmax));
+      koff = (uint32_t)(2 * (k < kmax ? +k : +kmax));
     } else {
-      tbase_k = k0 < kmax ? k0 : kmax;
+      tbase_k = k0 < kmax ? +k0 : +kmax;
       const int k = k0 + 8 * kb;
-      toff = (uint32_t)((int64_t)((k < kmax ? k : kmax) - tbase_k) * ldx * 2);
+      toff = (uint32_t)((int64_t)((k < kmax ? +k : +kmax) - tbase_k) * ldx * 2);
     }
   };
-  set_offsets();
-  set_koff();
+  by_role([&](auto tr) __attribute__((always_inline)) {
+    set_offsets(tr);
+    set_koff(tr);
+  });
   // Past the end of the stream the target stays on the last slab of the last
   // tile, so that every slab issues the same loads (their data is not used).
   auto advance_load = [&]() __attribute__((always_inline)) {
+    bool new_tile = false;
     if (++ct == nk) {
       if (cj + 1 < ntiles) {
         ct = 0;
         origin(++cj, cm0, cn0);
-        set_offsets();
+        new_tile = true;
       } else {
         ct = nk - 1;
       }
     }
-    set_koff();
+    by_role([&](auto tr) __attribute__((always_inline)) {
+      if (new_tile) set_offsets(tr);
+      set_koff(tr);
+    });
   };
   // One load, the same instruction for either kind of operand: a
   // wave-uniform base (K-contiguous: the tile's first row; K-major: K row
   // tbase_k + u) plus a 32-bit lane offset.  The B waves of a 224-wide tile
   // load their last chunk row again (it is not written).
   h8 stg[2][8];
-  auto load_one = [&](int set, int u) __attribute__((always_inline)) {
-    const int uu = (BN < 256 && !TB && !stA && u >= BN / 32) ? u - 1 : u;
+  auto load_one = [&](int set, int u, auto tr) __attribute__((always_inline)) {
+    constexpr bool trans = decltype(tr)::value;
     const half_t* base = trans ? X + (int64_t)(tbase_k + u) * ldx
-                               : X + (int64_t)(stA ? cm0 : cn0) * ldx;
-    const uint32_t off = trans ? toff + coff : roff[uu] + koff;
+                               : X + (int64_t)(stA ? +cm0 : +cn0) * ldx;
+    const uint32_t off = trans ? toff + coff : roff[u] + koff;
     h8 v;
     __builtin_memcpy(&v, (const char*)base + off, 16);
     if (set == 0) stg[0][u] = v;
@@ -283,13 +306,14 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   // shifted along K where the slab reaches past K; a K-contiguous chunk is
   // shifted along K where the slab does.  These branches are wave-uniform
   // and hold no memory operation.
-  auto write_one = [&](int set, int stage, int u) __attribute__((always_inline)) {
+  auto write_one = [&](int set, int stage, int u, auto tr) __attribute__((always_inline)) {
+    constexpr bool trans = decltype(tr)::value;
     h8(&x)[8] = set == 0 ? stg[0] : stg[1];
     const int k0 = wt * C::BK;
     const bool ktail = k0 + C::BK > p.K;
-    if constexpr (TA || TB) {
-      if (trans && u == 0) {
-        const int x0 = stA ? wm0 : wn0;
+    if constexpr (trans) {
+      if (u == 0) {
+        const int x0 = stA ? +wm0 : +wn0;
         if (x0 + bx > limx) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) x[e] = tail_fix(x[e], x0 + 8 * mb, limx);
@@ -304,7 +328,7 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
     h8 v = x[u];
     if (!trans && ktail) v = tail_fix(v, k0 + 8 * lchunk, p.K);
     const int row = trans ? 8 * mb + u : (t >> 2) + 32 * u;
-    const int pos = trans ? tpos : lpos;
+    const int pos = trans ? +tpos : +lpos;
     const bool live = trans ? mb_raw < bx / 8 : (t >> 2) + 32 * u < bx;
     unsigned char* st = lds + stage * C::kStage + (stA ? 0 : BM * C::kRow);
     if (live) *(h8*)(st + row * C::kRow + pos) = v;
@@ -315,13 +339,11 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   const int rpos = 16 * (g ^ swz(r));
   const int a_off = (wm + r) * C::kRow + rpos;
   const int b_off = (BM + wn + r) * C::kRow + rpos;
-  h8 fa[2][kBM], fb[2][kBN];
+  h8 fa[kBM], fb[2][kBN];
   auto read_frag = [&](int set, int stage, int f) __attribute__((always_inline)) {
     const unsigned char* st = lds + stage * C::kStage;
     if (f < kBM) {
-      const h8 v = *(const h8*)(st + a_off + f * 16 * C::kRow);
-      if (set == 0) fa[0][f] = v;
-      else fa[1][f] = v;
+      fa[f] = *(const h8*)(st + a_off + f * 16 * C::kRow);
     } else {
       const int j = f - kBM;
       const h8 v = *(const h8*)(st + b_off + j * 16 * C::kRow);
@@ -339,7 +361,9 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   };
 
   // One slab (index gs, of parity SET): its matrix instructions on fragment
-  // set SET, with the fragment reads of slab gs + 1 into the other set, the
+  // set SET (B; A has one set), with the fragment reads of slab gs + 1 (A
+  // fragment i into the registers row i has finished with, B into the other
+  // set), the
   // LDS writes of slab gs + 2 from staging set SET and the loads of slab
   // gs + 3 into staging set 1 - SET spread over them.  Past the end of the
   // stream the reads, loads and writes still happen (on a stage or registers
@@ -352,16 +376,19 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
     static_for<C::kMfma>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
       constexpr int i = q / kBN, j = q % kBN;
-      mma<FMT>(acc[i][j], fb[SET][j], fa[SET][i]);
-      static_for<C::kReads>([&](auto fc) __attribute__((always_inline)) {
-        constexpr int f = decltype(fc)::value;
-        if constexpr (q == f * C::kMfma / C::kReads) read_frag(1 - SET, rstage, f);
-      });
+      mma<FMT>(acc[i][j], fb[SET][j], fa[i]);
+      // A fragment i of the next slab replaces this slab's after row i's
+      // last product; the next slab's B fragments go to the other set, one
+      // per row.
+      if constexpr (j == kBN - 1) read_frag(1 - SET, rstage, i);
+      if constexpr (j == kBN / 2 - 1 && i < kBN) read_frag(1 - SET, rstage, kBM + i);
       static_for<8>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         if constexpr (q == u * C::kMfma / 8 + 2) {
-          write_one(SET, wstage, u);
-          load_one(1 - SET, u);
+          by_role([&](auto tr) __attribute__((always_inline)) {
+            write_one(SET, wstage, u, tr);
+            load_one(1 - SET, u, tr);
+          });
         }
       });
       __builtin_amdgcn_sched_barrier(0);
@@ -470,20 +497,30 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   // Prologue: slab 0 written to stage 0 and slab 1 to stage 1, slab 2 loaded
   // into staging set 0 (the stream has at least two slabs); then slab 0's
   // fragments are read into set 0.
+  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) load_one(0, u);
+    for (int u = 0; u < 8; ++u) load_one(0, u, tr);
+  });
   advance_load();
+  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) load_one(1, u);
+    for (int u = 0; u < 8; ++u) load_one(1, u, tr);
+  });
   advance_load();
+  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) write_one(0, 0, u);
+    for (int u = 0; u < 8; ++u) write_one(0, 0, u, tr);
+  });
   advance_write();
+  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) write_one(1, 1, u);
+    for (int u = 0; u < 8; ++u) write_one(1, 1, u, tr);
+  });
   advance_write();
+  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) load_one(0, u);
+    for (int u = 0; u < 8; ++u) load_one(0, u, tr);
+  });
   advance_load();
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   asm volatile("s_barrier" ::: "memory");

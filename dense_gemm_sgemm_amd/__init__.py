@@ -12,6 +12,8 @@ library is missing the calls raise.
                                              # C = act(A@B.T + bias) + residual
     gemm_ex(A, B, C, op_a="n", op_b="t", ...) # any layout, fp16 or bf16
     gemm_f32_splitk / gemm_f16_nt_splitk     # K cut into ranges (split-K)
+    gemm_f16_nt_splitk_static(A, B, C)       # split-K into the library's static
+                                             # scratch area: allocates nothing
 
 The library allocates no memory.  Where a call's kernels need scratch memory
 (split-K partial sums, gemm_ex's transposed copies and matrix-vector partial
@@ -30,6 +32,8 @@ LIB_PATH = os.path.join(HERE, "libmi355gemm.so")
 
 # Status and activation codes, mirroring include/mi355gemm.h.
 GEMM_OK = 0
+GEMM_ERR_SCRATCH_LIMIT = -8
+STATIC_SCRATCH_BYTES = 32 << 20
 ACTS = {"none": 0, "relu": 1, "silu": 2}
 
 _lock = threading.Lock()
@@ -83,6 +87,8 @@ def load_library() -> ctypes.CDLL:
         lib.gemm_f32_splitk.restype = i
         lib.gemm_f16_nt_splitk.argtypes = [i, i, i, p, i, p, i, p, i, i, p, u64, p]
         lib.gemm_f16_nt_splitk.restype = i
+        lib.gemm_f16_nt_splitk_static.argtypes = [i, i, i, p, i, p, i, p, i, i, p]
+        lib.gemm_f16_nt_splitk_static.restype = i
         lib.gemm_f32_splitk_workspace.argtypes = [i, i, i, i]
         lib.gemm_f32_splitk_workspace.restype = u64
         lib.gemm_f16_nt_splitk_workspace.argtypes = [i, i, i, i]
@@ -247,6 +253,23 @@ def gemm_f16_nt_splitk(A, B, C, splits: int = 0, workspace=None, stream=None):
                              stream)
     _check(load_library().gemm_f16_nt_splitk(M, N, K, pa, lda, pb, ldb, pc, ldc, int(splits), pw,
                                              nw, _stream(stream)))
+    return C
+
+
+def gemm_f16_nt_splitk_static(A, B, C, splits: int = 0, stream=None):
+    """``gemm_f16_nt_splitk`` without a workspace: the partial sums go to the
+    library's static scratch area (``STATIC_SCRATCH_BYTES`` per GPU), so the
+    call allocates nothing.  Calls that overlap in time on one GPU race on
+    that area; order them (e.g. on one stream).  Returns C."""
+    torch = _torch_module()
+    M, K, lda, pa = _matrix(A, "A", torch.float16)
+    N, K2, ldb, pb = _matrix(B, "B", torch.float16)
+    M2, N2, ldc, pc = _matrix(C, "C", torch.float16)
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError("shape mismatch: A %s, B %s, C %s" % (tuple(A.shape), tuple(B.shape),
+                                                               tuple(C.shape)))
+    _check(load_library().gemm_f16_nt_splitk_static(M, N, K, pa, lda, pb, ldb, pc, ldc,
+                                                    int(splits), _stream(stream)))
     return C
 
 

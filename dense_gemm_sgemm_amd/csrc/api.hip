@@ -12,6 +12,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "internal.h"
 
@@ -32,6 +33,9 @@ bool force_general() {
   const char* v = std::getenv("MI355GEMM_FORCE_PATH");
   return v != nullptr && std::strcmp(v, "general") == 0;
 }
+
+// Size of the static scratch area behind gemm_f16_nt_splitk_static.
+constexpr size_t kStaticScratchBytes = GEMM_STATIC_SCRATCH_BYTES;
 
 // Per-device verdict of the gfx950 check: 0 unknown, -1 not supported, else
 // the device's compute-unit count.
@@ -390,6 +394,66 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K, const void* A, int lda
   return to_status(run16(pl, a, GEMM_OP_N, GEMM_OP_T, false, cus, nullptr, s));
 }
 
+}  // extern "C"
+
+// ---- gemm_f16_nt_splitk_static: the split-K call with library-held scratch.
+//
+// The partial sums live in `scratch`, a device array of fixed size in this
+// library's code object (one copy per GPU, for the life of the process).  In
+// host code the name `scratch` is only a stand-in for the symbol: the kernels
+// get its device address, looked up once per device with
+// hipGetSymbolAddress while that device is current and kept in
+// g_scratch_addr.  The partial kernels store every element of every tile the
+// reduction reads, so nothing has to be cleared between calls.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_lock;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// The device address of the current device's `scratch`, or nullptr if the
+// runtime cannot give it.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> guard(g_scratch_lock);
+  ptr = g_scratch_addr[dev].load(std::memory_order_relaxed);
+  if (ptr == nullptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+MI355GEMM_API int gemm_f16_nt_splitk_static(int M, int N, int K, const void* A, int lda,
+                                            const void* B, int ldb, void* C, int ldc, int splits,
+                                            void* stream) {
+  const Plan16 pl = plan16(GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T, M, N, K, A, lda, B, ldb, nullptr,
+                           GEMM_ACT_NONE, nullptr, 0, C, ldc);
+  if (pl.path < 0 || pl.path == GEMM_PATH_NOOP) return pl.path < 0 ? pl.path : GEMM_OK;
+  const SplitPlan plan = f16_split(pl.path, M, N, K, splits);
+  if (plan.splits > 1 && plan.bytes > kStaticScratchBytes) return GEMM_ERR_SCRATCH_LIMIT;
+  const int cus = check_device();
+  if (cus < 0) return cus;
+  Args16 a{static_cast<const half_t*>(A), static_cast<const half_t*>(B),
+           static_cast<half_t*>(C), lda, ldb, ldc, M, N, K};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.splits > 1) {
+    void* ws = scratch_address();
+    if (ws == nullptr) return GEMM_ERR_LAUNCH;
+    a.sk = splitk_args(plan, M, N, ws);
+    return to_status(launch_f16_splitk(a, false, cus, s));
+  }
+  return to_status(run16(pl, a, GEMM_OP_N, GEMM_OP_T, false, cus, nullptr, s));
+}
+
 MI355GEMM_API unsigned long long gemm_f32_splitk_workspace(int M, int N, int K, int splits) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   return f32_split(GEMM_PATH_F32_MFMA, M, N, K, splits).bytes;
@@ -440,6 +504,10 @@ MI355GEMM_API const char* gemm_status_string(int status) {
     case GEMM_ERR_WORKSPACE:
       return "the call needs a workspace and the one given is NULL, smaller than the size "
              "query reports, or not 16-byte aligned";
+    case GEMM_ERR_SCRATCH_LIMIT:
+      return "the split-K partial sums would exceed the library's static scratch area "
+             "(GEMM_STATIC_SCRATCH_BYTES, 32 MiB); use fewer splits or gemm_f16_nt_splitk "
+             "with a workspace";
     default: return "unknown status code";
   }
 }

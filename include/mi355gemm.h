@@ -10,7 +10,9 @@
  *    offsets are computed in 64 bits.
  *  - A, B and C are DEVICE pointers, allocated and owned by the caller.  The
  *    library never allocates, frees or keeps device memory, and keeps no
- *    pointer after a call returns.  gemm_f32, gemm_f16_nt and gemm_f16_nt_ex
+ *    pointer after a call returns; the one exception is the static scratch
+ *    area of gemm_f16_nt_splitk_static, part of the library's code object
+ *    (see there).  gemm_f32, gemm_f16_nt and gemm_f16_nt_ex
  *    need nothing beyond their operands.  The calls whose kernels need
  *    scratch memory take it from the caller as a `workspace` argument and
  *    say how much through a size query: gemm_f32_splitk / gemm_f16_nt_splitk
@@ -24,7 +26,8 @@
  *  - Misaligned pointers or leading dimensions are never an error: they only
  *    select a slower kernel.
  *  - Calls are thread-safe: the library's only state is a per-device record,
- *    set once, that the device is a gfx950.
+ *    set once, that the device is a gfx950 (and, for
+ *    gemm_f16_nt_splitk_static, the device address of its scratch area).
  *
  * Return value: GEMM_OK (0) or one of the negative GEMM_ERR_* codes below.
  * On an error no work is enqueued and C is untouched.
@@ -50,8 +53,10 @@ enum {
   GEMM_ERR_UNSUPPORTED_DEVICE = -4,/* no HIP device, or the current one is not gfx950 */
   GEMM_ERR_LAUNCH = -5,            /* the HIP runtime refused the kernel launch      */
   GEMM_ERR_BAD_ARG = -6,           /* an enumerated argument has no defined meaning  */
-  GEMM_ERR_WORKSPACE = -7          /* a workspace the call needs is NULL, smaller    */
+  GEMM_ERR_WORKSPACE = -7,         /* a workspace the call needs is NULL, smaller    */
                                    /*   than its size query, or not 16-byte aligned  */
+  GEMM_ERR_SCRATCH_LIMIT = -8      /* gemm_f16_nt_splitk_static: the partial sums    */
+                                   /*   need more than GEMM_STATIC_SCRATCH_BYTES     */
 };
 
 /*
@@ -189,6 +194,35 @@ MI355GEMM_API int gemm_f16_nt_splitk(int M, int N, int K,
  * they would not split (negative M, N, K or splits count as no split). */
 MI355GEMM_API unsigned long long gemm_f32_splitk_workspace(int M, int N, int K, int splits);
 MI355GEMM_API unsigned long long gemm_f16_nt_splitk_workspace(int M, int N, int K, int splits);
+
+/*
+ * gemm_f16_nt_splitk for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and allocates nothing; the fp32 partial
+ * sums go to a static scratch area of GEMM_STATIC_SCRATCH_BYTES (32 MiB) that
+ * the library's code object holds on every GPU it runs on, until the process
+ * ends.
+ *
+ *   arguments  : as gemm_f16_nt_splitk, without workspace / workspace_bytes
+ *   limit      : a split whose partial sums need more than
+ *                GEMM_STATIC_SCRATCH_BYTES (gemm_f16_nt_splitk_workspace for
+ *                the same M, N, K, splits) returns GEMM_ERR_SCRATCH_LIMIT
+ *                before any work is enqueued.  Without a split the call runs
+ *                exactly as gemm_f16_nt and uses no scratch.
+ *   sharing    : every call on one GPU uses that GPU's one scratch area, and
+ *                the area keeps the last call's partial sums.  Calls that
+ *                overlap in time on one GPU (other streams, other host
+ *                threads, replays of graphs on other streams) race on it:
+ *                the caller must order them, e.g. on one stream.
+ *
+ * Results are bit for bit those of gemm_f16_nt_splitk with the same splits.
+ */
+#define GEMM_STATIC_SCRATCH_BYTES (32ull << 20)
+MI355GEMM_API int gemm_f16_nt_splitk_static(int M, int N, int K,
+                                            const void* A, int lda,
+                                            const void* B, int ldb,
+                                            void* C, int ldc,
+                                            int splits, void* stream);
 
 /*
  * 16-bit GEMM in any operand layout, fp16 or bf16, with the fused write-back:

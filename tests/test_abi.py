@@ -38,6 +38,7 @@ def declared_symbols():
 def test_header_declares_the_abi():
     assert declared_symbols() == sorted(["gemm_f32", "gemm_f16_nt", "gemm_f16_nt_ex",
                                          "gemm_f32_splitk", "gemm_f16_nt_splitk",
+                                         "gemm_f16_nt_splitk_static",
                                          "gemm_f32_splitk_workspace",
                                          "gemm_f16_nt_splitk_workspace", "gemm_ex",
                                          "gemm_ex_workspace",
@@ -57,7 +58,7 @@ def test_library_exports_exactly_the_header(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         s = dg.status_string(code)
         assert s and s != "unknown status code"
     assert dg.status_string(17) == "unknown status code"
@@ -317,6 +318,23 @@ def test_split_k_workspace_errors_need_no_device(lib):
     assert lib.gemm_f32_splitk(-1, 256, 4096, 1.0, a, 4096, a, 256, 0.0, a, 256, 4, null, 0,
                                null) == -1
     assert lib.gemm_f16_nt_splitk(0, 5, 5, null, 5, null, 5, null, 5, 4, null, 0, null) == 0
+
+
+def test_static_scratch_split_k_errors_need_no_device(lib):
+    """gemm_f16_nt_splitk_static refuses, before any HIP call, a split whose
+    partial sums exceed the static scratch area, and validates like the
+    workspace call."""
+    null = None
+    a = p(ALIGNED)
+    assert dg.STATIC_SCRATCH_BYTES == 32 << 20
+    assert lib.gemm_f16_nt_splitk_workspace(1024, 1024, 16384, 16) > dg.STATIC_SCRATCH_BYTES
+    assert lib.gemm_f16_nt_splitk_static(1024, 1024, 16384, a, 16384, a, 16384, a, 1024, 16,
+                                         null) == dg.GEMM_ERR_SCRATCH_LIMIT
+    assert lib.gemm_f16_nt_splitk_static(-1, 5, 5, a, 5, a, 5, a, 5, 0, null) == -1
+    assert lib.gemm_f16_nt_splitk_static(5, 5, 5, a, 4, a, 5, a, 5, 0, null) == -2
+    assert lib.gemm_f16_nt_splitk_static(5, 5, 5, null, 5, a, 5, a, 5, 0, null) == -3
+    assert lib.gemm_f16_nt_splitk_static(0, 5, 5, null, 5, null, 5, null, 5, 4, null) == 0
+    assert "static scratch" in dg.status_string(dg.GEMM_ERR_SCRATCH_LIMIT)
 
 
 def test_python_binding_validates_tensors(lib):

@@ -89,8 +89,7 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
 
 // The 16-bit calls share one selection.  Plan16 records the kernel path and
 // the workspace it needs: an operand that is not K-contiguous (gemm_ex's A
-// for OP_T, B for OP_N) is read in place by the register-staged wide tiles in
-// large products and otherwise copied transposed into the workspace
+// for OP_T, B for OP_N) is copied transposed into the workspace
 // ([rows][round8(K)], 256-byte aligned) for the A * B^T kernels; the
 // matrix-vector kernel with its long operand K-major leaves partial sums over
 // ranges of K there; gemm_ex's split-K leaves the partial sums of its ranges
@@ -133,7 +132,6 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
   pl.lda = lda;
   pl.ldb = ldb;
   if (K == 0) return done(epi ? GEMM_PATH_F16_GENERAL : GEMM_PATH_F16_ZERO);
-  const bool nt = op_a == GEMM_OP_N && op_b == GEMM_OP_T;
   // Transposed copies of the operands that are not K-contiguous, for the
   // A * B^T kernels (16-byte aligned, rows of round8(K) elements).
   auto copies = [&](bool ca, bool cb) {
@@ -178,10 +176,10 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
       return done(GEMM_PATH_F16_SPLITK);
     }
   }
-  // Large products in the other layouts: the register-staged wide tiles read
-  // the K-major operands in place.
-  if (!nt && large_product(M, N, K) && f16_staged_fits(M, N, K, lda, ldb, op_a, op_b))
-    return done(GEMM_PATH_F16_STAGED);
+  // The other layouts run on transposed copies: on 5376 x 5376 x 2048 the
+  // copy and the full-tile kernel take 113-122 us, where the register-staged
+  // wide tiles reading the K-major operands in place (8 x 8 blocks
+  // transposed in registers) took 164-481 us.
   copies(ca, cb);
   const void* a_read = ca ? kCopyAddress : A;
   const void* b_read = cb ? kCopyAddress : B;
@@ -191,8 +189,7 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
   // Large products the full tiles cannot take (ragged, unaligned rows, odd
   // leading dimensions, C or the write-back operands unaligned): the
   // register-staged wide tiles read the operands (or the copies) in place.
-  if (large_product(M, N, K) &&
-      f16_staged_fits(M, N, K, pl.lda, pl.ldb, GEMM_OP_N, GEMM_OP_T))
+  if (large_product(M, N, K) && f16_staged_fits(M, N, K, pl.lda, pl.ldb))
     return done(GEMM_PATH_F16_STAGED);
   return done(GEMM_PATH_F16_GENERAL);
 }
@@ -213,9 +210,6 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
                  hipStream_t s) {
   switch (pl.path) {
     case GEMM_PATH_F16_ZERO: return launch_f16_zero(a, s);
-    case GEMM_PATH_F16_STAGED:
-      if (!pl.copy_a && !pl.copy_b) return launch_f16_staged(a, epi, op_a, op_b, cus, s);
-      break;
     case GEMM_PATH_F16_GEMV:
       if (pl.gemv_kn)
         return launch_f16_gemv_kn(a, op_a, op_b, epi, gemv_kn_plan(a.M, a.N, a.K), ws, s);
@@ -245,8 +239,7 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
                          ws + pl.bytes_a + pl.bytes_b);
       return launch_f16_splitk(a, epi, cus, s);
     case GEMM_PATH_F16_MFMA: return launch_f16_mfma(a, epi, cus, s);
-    case GEMM_PATH_F16_STAGED:
-      return launch_f16_staged(a, epi, GEMM_OP_N, GEMM_OP_T, cus, s);
+    case GEMM_PATH_F16_STAGED: return launch_f16_staged(a, epi, cus, s);
     default: return launch_f16_edge(a, epi, s);
   }
 }

@@ -70,6 +70,9 @@ struct Cfg {
   static constexpr int kReads = kBM + kBN;                   // fragments per wave per slab
   static constexpr int kRow = 2 * BK;                        // bytes per slab row
   static constexpr int kStage = (BM + BN) * kRow;
+  // thread t stages chunks t + 256 u: slab row (t >> 2) + 64 u, chunk t & 3
+  static constexpr int kLoads = (BM + BN + 63) / 64;         // 8
+  static constexpr int kLoadsA = BM / 64;                    // the first 4 are rows of A
   static constexpr int kOutRowBytes = 256;
   static constexpr int kOutBytes = 4 * 16 * kOutRowBytes;
   static constexpr int kLds = 2 * kStage + kOutBytes;
@@ -125,7 +128,7 @@ struct Args {
   int64_t tiles;
 };
 
-template <int BN, int FMT, bool EPI, bool TA, bool TB>
+template <int BN, int FMT, bool EPI>
 __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   typedef Cfg<BN> C;
   constexpr int BM = C::BM, kBM = C::kBM, kBN = C::kBN;
@@ -147,191 +150,75 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
     n0 = tn * BN;
   };
 
-  // ---- staging.  Waves 0-1 stage the slab rows of A, waves 2-3 those of B
-  // (wave-uniform role); t = tid % 128 is the thread's index in its pair of
-  // waves.  Slab rows of an operand are its tile's rows (m for A, n for B),
-  // each 32 elements of K.
-  //
-  // K-contiguous operand (A for op_a = N, B for op_b = T): thread t loads
-  // chunks u = 0 .. 7: slab row (t >> 2) + 32 u, chunk t & 3 (8 elements of
-  // K), written at position (t & 3) ^ swz(row) -- the same for every u since
-  // 32 u keeps the row's bits 2-3.  Each load is the row's base (re-computed
-  // per tile, rows past the matrix clamped to its last row) plus the chunk's
-  // start in the row, clamped to K - 8 (re-computed per slab).
-  //
-  // K-major operand (A stored [K][lda] for op_a = T, B stored [K][ldb] for
-  // op_b = N): thread t takes the 8 x 8 block of K rows 8 kb .. 8 kb + 7 of
-  // the slab (kb = t & 3) and tile rows 8 mb .. 8 mb + 7 (mb = t >> 2), loads
-  // its 8 K rows as 16-byte pieces (u = 0 .. 7), transposes the block in
-  // registers and writes the 8 resulting chunks (tile rows 8 mb + u, chunk
-  // kb) at position kb ^ swz(8 mb + u) = kb ^ 2 (mb & 1).  A piece starts at
-  // the column min(x0 + 8 mb, L - 8) (L: M or N) and at the K row
-  // min(k0 + 8 kb, K - 8); in a tile that reaches past L the pieces are
-  // shifted and zero-filled along the row before the transposition, in a
-  // slab that reaches past K the chunks after it -- every piece is one load.
-  //
-  // With BN = 224 the B waves have 7 chunk rows (u < 7) or 28 blocks (lanes
-  // with mb >= 28 re-read block mb - 4 and write nothing).
-  //
-  // Every selection below between two variables is written on values (+x):
-  // a conditional on two lvalues selects between their addresses, and the
-  // captured variables behind such an address stay in scratch memory.  For
-  // the same reason the operand's layout is a compile-time argument of each
-  // staging step (by_role), never a run-time flag inside one.
-  const int t = tid & 127;
-  const bool stA = wave < 2;                   // wave-uniform
-  const half_t* const X = stA ? +p.A : +p.B;
-  const int64_t ldx = stA ? +p.lda : +p.ldb;
-  const int limx = stA ? +p.M : +p.N, bx = stA ? BM : BN;
-  auto by_role = [&](auto&& f) __attribute__((always_inline)) {
-    if constexpr (TA == TB) {
-      f(std::bool_constant<TA>());
-    } else {
-      if (stA) f(std::bool_constant<TA>());
-      else f(std::bool_constant<TB>());
-    }
-  };
+  // ---- staging.  Thread t loads chunks t + 256 u: slab row R = (t >> 2) +
+  // 64 u -- rows of A for u < 4, then of B -- chunk t & 3, and writes each
+  // one to row R at position (t & 3) ^ swz(R), the same for every u since
+  // 64 u keeps R's bits 2-3.  With BN = 224 the last chunk of threads
+  // 128-255 lies past the slab (R >= 480): it re-reads the chunk 64 rows up
+  // and is not written.  roff[u] is the byte offset of the chunk's row from
+  // the tile's first row (re-computed per tile: rows past the matrix clamp
+  // to its last row).
+  const int lrow = tid >> 2, lchunk = tid & 3;
+  const int lpos = 16 * (lchunk ^ swz(lrow));
   int cj = 0, ct = 0, cm0 = 0, cn0 = 0;        // the load target: slab ct of tile cj
   origin(0, cm0, cn0);
-  const int kmax = p.K - 8;
-  // K-contiguous operands
-  const int lchunk = t & 3;
-  const int lpos = 16 * (lchunk ^ swz(t >> 2));
-  uint32_t roff[8];          // row byte offsets from the tile's first row
-  uint32_t koff = 0;         // the chunk's byte offset in its row
-  // K-major operands
-  const int kb = t & 3;
-  const int mb_raw = t >> 2;
-  const int mb = mb_raw < bx / 8 ? mb_raw : mb_raw - 4;
-  const int tpos = 16 * (kb ^ (2 * (mb & 1)));
-  uint32_t coff = 0;         // the piece's column byte offset in its K row
-  uint32_t toff = 0;         // the piece's K row byte offset from the slab's base row
-  int tbase_k = 0;           // the slab's base K row (wave-uniform)
-  auto set_offsets = [&](auto tr) __attribute__((always_inline)) {
-    constexpr bool trans = decltype(tr)::value;
-    const int x0 = stA ? +cm0 : +cn0;
-    if constexpr (!trans) {
+  uint32_t roff[C::kLoads];
+  auto set_offsets = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        // the B waves of a 224-wide tile load their last chunk row again
-        const int ue = 32 * u < bx ? u : u - 1;
-        int row = x0 + (t >> 2) + 32 * ue;
-        row = row < limx ? row : limx - 1;
-        roff[u] = (uint32_t)((int64_t)(row - x0) * ldx * 2);
-      }
-    } else {
-      const int c = x0 + 8 * mb;
-      coff = (uint32_t)(2 * (c < limx - 8 ? c : limx - 8));
+    for (int u = 0; u < C::kLoads; ++u) {
+      int R = lrow + 64 * u;
+      if (R >= BM + BN) R -= 64;
+      const bool isA = u < C::kLoadsA;
+      const int row0 = isA ? cm0 : cn0, lim = isA ? p.M : p.N;
+      int row = row0 + (isA ? R : R - BM);
+      row = row < lim ? row : lim - 1;
+      roff[u] = (uint32_t)((int64_t)(row - row0) * (isA ? p.lda : p.ldb) * 2);
     }
   };
-  auto set_koff = [&](auto tr) __attribute__((always_inline)) {
-    constexpr bool trans = decltype(tr)::value;
-    const int k0 = ct * C::BK;
-    if constexpr (!trans) {
-      const int k = k0 + 8 * lchunk;
-      koff = (uint32_t)(2 * (k < kmax ? +k : +kmax));
-    } else {
-      tbase_k = k0 < kmax ? +k0 : +kmax;
-      const int k = k0 + 8 * kb;
-      toff = (uint32_t)((int64_t)((k < kmax ? +k : +kmax) - tbase_k) * ldx * 2);
-    }
+  set_offsets();
+  // koff: byte offset of this lane's chunk in its row for the load target
+  // slab, the chunk start clamped to K - 8 (re-computed once per slab); each
+  // load is then a wave-uniform row-0 base plus one 32-bit lane offset.
+  const int kmax = p.K - 8;
+  uint32_t koff = 0;
+  auto set_koff = [&]() __attribute__((always_inline)) {
+    const int k = ct * C::BK + 8 * lchunk;
+    koff = (uint32_t)(2 * (k < kmax ? k : kmax));
   };
-  by_role([&](auto tr) __attribute__((always_inline)) {
-    set_offsets(tr);
-    set_koff(tr);
-  });
+  set_koff();
   // Past the end of the stream the target stays on the last slab of the last
   // tile, so that every slab issues the same loads (their data is not used).
   auto advance_load = [&]() __attribute__((always_inline)) {
-    bool new_tile = false;
     if (++ct == nk) {
       if (cj + 1 < ntiles) {
         ct = 0;
         origin(++cj, cm0, cn0);
-        new_tile = true;
+        set_offsets();
       } else {
         ct = nk - 1;
       }
     }
-    by_role([&](auto tr) __attribute__((always_inline)) {
-      if (new_tile) set_offsets(tr);
-      set_koff(tr);
-    });
+    set_koff();
   };
-  // One load, the same instruction for either kind of operand: a
-  // wave-uniform base (K-contiguous: the tile's first row; K-major: K row
-  // tbase_k + u) plus a 32-bit lane offset.  The B waves of a 224-wide tile
-  // load their last chunk row again (it is not written).
-  h8 stg[2][8];
-  auto load_one = [&](int set, int u, auto tr) __attribute__((always_inline)) {
-    constexpr bool trans = decltype(tr)::value;
-    const half_t* base = trans ? X + (int64_t)(tbase_k + u) * ldx
-                               : X + (int64_t)(stA ? +cm0 : +cn0) * ldx;
-    const uint32_t off = trans ? toff + coff : roff[u] + koff;
+  h8 stg[2][C::kLoads];
+  auto load_one = [&](int set, int u) __attribute__((always_inline)) {
+    const bool isA = u < C::kLoadsA;
+    const char* base = isA ? (const char*)(p.A + (int64_t)cm0 * p.lda)
+                           : (const char*)(p.B + (int64_t)cn0 * p.ldb);
+    const uint32_t off = roff[u] + koff;
     h8 v;
-    __builtin_memcpy(&v, (const char*)base + off, 16);
+    __builtin_memcpy(&v, base + off, 16);
     if (set == 0) stg[0][u] = v;
     else stg[1][u] = v;
   };
-  // The slab the LDS writes store: slab wt of tile wj, origin (wm0, wn0).
-  int wt = 0, wj = 0, wm0 = 0, wn0 = 0;
-  origin(0, wm0, wn0);
-  auto advance_write = [&]() __attribute__((always_inline)) {
-    if (++wt == nk) {
-      wt = 0;
-      if (wj + 1 < ntiles) origin(++wj, wm0, wn0);
-    }
-  };
-  // 8 x 8 transposition of a staging set in place: piece u (8 columns of K
-  // row u) becomes chunk u (8 K rows of column u).  On 32-bit words: word a
-  // of chunk j holds K rows 2a and 2a + 1 of column j, the low or high halves
-  // of word j / 2 of pieces 2a and 2a + 1.
-  auto transpose_set = [&](h8 (&x)[8]) __attribute__((always_inline)) {
-    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-    u4 w[8], y[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = __builtin_bit_cast(u4, x[u]);
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        y[2 * q][a] = __builtin_amdgcn_perm(w[2 * a + 1][q], w[2 * a][q], 0x05040100u);
-        y[2 * q + 1][a] = __builtin_amdgcn_perm(w[2 * a + 1][q], w[2 * a][q], 0x07060302u);
-      }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = __builtin_bit_cast(h8, y[j]);
-  };
-  // LDS write u of a staging set.  A K-major set is first (u == 0) shifted
-  // along the tile rows where the tile reaches past M or N, transposed, and
-  // shifted along K where the slab reaches past K; a K-contiguous chunk is
-  // shifted along K where the slab does.  These branches are wave-uniform
-  // and hold no memory operation.
-  auto write_one = [&](int set, int stage, int u, auto tr) __attribute__((always_inline)) {
-    constexpr bool trans = decltype(tr)::value;
-    h8(&x)[8] = set == 0 ? stg[0] : stg[1];
-    const int k0 = wt * C::BK;
-    const bool ktail = k0 + C::BK > p.K;
-    if constexpr (trans) {
-      if (u == 0) {
-        const int x0 = stA ? +wm0 : +wn0;
-        if (x0 + bx > limx) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = tail_fix(x[e], x0 + 8 * mb, limx);
-        }
-        transpose_set(x);
-        if (ktail) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = tail_fix(x[j], k0 + 8 * kb, p.K);
-        }
-      }
-    }
-    h8 v = x[u];
-    if (!trans && ktail) v = tail_fix(v, k0 + 8 * lchunk, p.K);
-    const int row = trans ? 8 * mb + u : (t >> 2) + 32 * u;
-    const int pos = trans ? +tpos : +lpos;
-    const bool live = trans ? mb_raw < bx / 8 : (t >> 2) + 32 * u < bx;
-    unsigned char* st = lds + stage * C::kStage + (stA ? 0 : BM * C::kRow);
-    if (live) *(h8*)(st + row * C::kRow + pos) = v;
+  // wt: the slab (within its tile) whose chunks the LDS writes store
+  int wt = 0;
+  auto write_one = [&](int set, int stage, int u) __attribute__((always_inline)) {
+    const int R = lrow + 64 * u;
+    if (C::kLoads * 64 > BM + BN && u == C::kLoads - 1 && R >= BM + BN) return;
+    h8 v = set == 0 ? stg[0][u] : stg[1][u];
+    if (wt * C::BK + C::BK > p.K) v = tail_fix(v, wt * C::BK + 8 * lchunk, p.K);
+    *(h8*)(lds + stage * C::kStage + R * C::kRow + lpos) = v;
   };
 
   // ---- fragment reads: lane l reads row (block base) + l % 16, chunk l / 16.
@@ -363,9 +250,8 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   // One slab (index gs, of parity SET): its matrix instructions on fragment
   // set SET (B; A has one set), with the fragment reads of slab gs + 1 (A
   // fragment i into the registers row i has finished with, B into the other
-  // set), the
-  // LDS writes of slab gs + 2 from staging set SET and the loads of slab
-  // gs + 3 into staging set 1 - SET spread over them.  Past the end of the
+  // set), the LDS writes of slab gs + 2 from staging set SET and the loads of
+  // slab gs + 3 into staging set 1 - SET spread over them.  Past the end of the
   // stream the reads, loads and writes still happen (on a stage or registers
   // nothing uses any more), so that every slab has the same instruction
   // stream; the compiler then waits for exactly the load each LDS write
@@ -382,18 +268,16 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
       // per row.
       if constexpr (j == kBN - 1) read_frag(1 - SET, rstage, i);
       if constexpr (j == kBN / 2 - 1 && i < kBN) read_frag(1 - SET, rstage, kBM + i);
-      static_for<8>([&](auto uc) __attribute__((always_inline)) {
+      static_for<C::kLoads>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
-        if constexpr (q == u * C::kMfma / 8 + 2) {
-          by_role([&](auto tr) __attribute__((always_inline)) {
-            write_one(SET, wstage, u, tr);
-            load_one(1 - SET, u, tr);
-          });
+        if constexpr (q == u * C::kMfma / C::kLoads + 2) {
+          write_one(SET, wstage, u);
+          load_one(1 - SET, u);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    advance_write();
+    if (++wt == nk) wt = 0;
     advance_load();
   };
 
@@ -497,30 +381,20 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   // Prologue: slab 0 written to stage 0 and slab 1 to stage 1, slab 2 loaded
   // into staging set 0 (the stream has at least two slabs); then slab 0's
   // fragments are read into set 0.
-  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_one(0, u, tr);
-  });
+  for (int u = 0; u < C::kLoads; ++u) load_one(0, u);
   advance_load();
-  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_one(1, u, tr);
-  });
+  for (int u = 0; u < C::kLoads; ++u) load_one(1, u);
   advance_load();
-  by_role([&](auto tr) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) write_one(0, 0, u, tr);
-  });
-  advance_write();
-  by_role([&](auto tr) __attribute__((always_inline)) {
+  for (int u = 0; u < C::kLoads; ++u) write_one(0, 0, u);
+  if (++wt == nk) wt = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) write_one(1, 1, u, tr);
-  });
-  advance_write();
-  by_role([&](auto tr) __attribute__((always_inline)) {
+  for (int u = 0; u < C::kLoads; ++u) write_one(1, 1, u);
+  if (++wt == nk) wt = 0;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_one(0, u, tr);
-  });
+  for (int u = 0; u < C::kLoads; ++u) load_one(0, u);
   advance_load();
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   asm volatile("s_barrier" ::: "memory");
@@ -549,55 +423,42 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
 }
 
-template <int BN, int FMT, bool EPI, bool TA, bool TB>
+template <int BN, int FMT, bool EPI>
 hipError_t launch_bn(const Args16& a, int cus, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
   int64_t grid = tiles < cus ? tiles : cus;
   if (grid < 1) grid = 1;
   Args ta{a, tiles};
   void* args[] = {&ta};
-  return hipLaunchKernel((const void*)hgemm_staged_kernel<BN, FMT, EPI, TA, TB>,
-                         dim3((unsigned)grid), dim3(256), args, 0, stream);
+  return hipLaunchKernel((const void*)hgemm_staged_kernel<BN, FMT, EPI>, dim3((unsigned)grid),
+                         dim3(256), args, 0, stream);
 }
 
 // 256 x 256 or 256 x 224 tiles, whichever takes fewer rounds of persistent
 // workgroups times tile width (5000 x 3001 on 256 CUs: 240 tiles of 256 x 256
 // in one round, against 280 of 256 x 224 in two).
-template <int FMT, bool EPI, bool TA, bool TB>
-hipError_t launch_layout(const Args16& a, int cus, hipStream_t stream) {
+template <int FMT, bool EPI>
+hipError_t launch_fmt(const Args16& a, int cus, hipStream_t stream) {
   const int64_t tm = (a.M + 255) / 256;
   const int64_t r256 = (tm * ((a.N + 255) / 256) + cus - 1) / cus;
   const int64_t r224 = (tm * ((a.N + 223) / 224) + cus - 1) / cus;
-  if (r224 * 224 < r256 * 256) return launch_bn<224, FMT, EPI, TA, TB>(a, cus, stream);
-  return launch_bn<256, FMT, EPI, TA, TB>(a, cus, stream);
-}
-
-template <int FMT, bool EPI>
-hipError_t launch_fmt(const Args16& a, bool ta, bool tb, int cus, hipStream_t stream) {
-  if (!ta && !tb) return launch_layout<FMT, EPI, false, false>(a, cus, stream);
-  if (!ta) return launch_layout<FMT, EPI, false, true>(a, cus, stream);
-  if (!tb) return launch_layout<FMT, EPI, true, false>(a, cus, stream);
-  return launch_layout<FMT, EPI, true, true>(a, cus, stream);
+  if (r224 * 224 < r256 * 256) return launch_bn<224, FMT, EPI>(a, cus, stream);
+  return launch_bn<256, FMT, EPI>(a, cus, stream);
 }
 
 }  // namespace hstaged
 
-bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb, int op_a, int op_b) {
+bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb) {
   constexpr int64_t kMaxLd = int64_t(1) << 23;
-  // a K-major operand's pieces span 8 of its M or N columns
-  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_N;
-  return M >= 1 && N >= 1 && K >= 8 && lda < kMaxLd && ldb < kMaxLd && (!ta || M >= 8) &&
-         (!tb || N >= 8);
+  return M >= 1 && N >= 1 && K >= 8 && lda < kMaxLd && ldb < kMaxLd;
 }
 
-hipError_t launch_f16_staged(const Args16& a, bool epi, int op_a, int op_b, int cus,
-                             hipStream_t stream) {
-  const bool ta = op_a == GEMM_OP_T, tb = op_b == GEMM_OP_N;
+hipError_t launch_f16_staged(const Args16& a, bool epi, int cus, hipStream_t stream) {
   if (a.fmt == kFmtBF16)
-    return epi ? hstaged::launch_fmt<kFmtBF16, true>(a, ta, tb, cus, stream)
-               : hstaged::launch_fmt<kFmtBF16, false>(a, ta, tb, cus, stream);
-  return epi ? hstaged::launch_fmt<kFmtF16, true>(a, ta, tb, cus, stream)
-             : hstaged::launch_fmt<kFmtF16, false>(a, ta, tb, cus, stream);
+    return epi ? hstaged::launch_fmt<kFmtBF16, true>(a, cus, stream)
+               : hstaged::launch_fmt<kFmtBF16, false>(a, cus, stream);
+  return epi ? hstaged::launch_fmt<kFmtF16, true>(a, cus, stream)
+             : hstaged::launch_fmt<kFmtF16, false>(a, cus, stream);
 }
 
 }  // namespace mi355gemm

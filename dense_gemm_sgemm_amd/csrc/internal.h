@@ -134,13 +134,11 @@ struct PadCopy {
   int rows, cols, rows_p, cols_p;
 };
 hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipStream_t stream);
-// The register-staged wide-tile kernel: any shape (K >= 8; M >= 8 when A
-// is K-major, N >= 8 when B is), leading dimension (below 2^23), 2-byte
-// alignment and operand layout (op_a / op_b as in gemm_ex; a.A, a.B in their
-// stored layouts), no copies, no workspace.
-bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb, int op_a, int op_b);
-hipError_t launch_f16_staged(const Args16& a, bool epi, int op_a, int op_b, int cus,
-                             hipStream_t stream);
+// The register-staged wide-tile kernel for A * B^T: any shape (K >= 8),
+// leading dimension (below 2^23) and 2-byte alignment, no copies, no
+// workspace.
+bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb);
+hipError_t launch_f16_staged(const Args16& a, bool epi, int cus, hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.
 hipError_t launch_f16_partials(const Args16& a, hipStream_t stream);
 hipError_t launch_f32_partials(const F32Args& a, hipStream_t stream);

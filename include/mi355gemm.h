@@ -247,11 +247,8 @@ MI355GEMM_API int gemm_f16_nt_splitk_static(int M, int N, int K,
  *          GEMM_ACT_NONE and residual NULL give the plain product).
  *
  * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  The other
- * layouts read the stored operands in place in products of at least 2^30
- * multiply-adds (the register-staged wide tiles transpose 8 x 8 blocks of a
- * K-major operand in registers on their way into LDS).  Smaller products
- * first copy each operand that is not K-contiguous (A for OP_T, B for OP_N)
- * into the workspace, transposed, then run the A * B^T kernels -- except on
+ * layouts first copy each operand that is not K-contiguous (A for OP_T, B for
+ * OP_N) into the workspace, transposed, then run the A * B^T kernels -- except on
  * the matrix-vector path (M <= 8 or N <= 8), where a long operand stored
  * K-major (B for OP_N when M is the small side, A for OP_T when N is) is read
  * in place, row by row, and the short one in either layout: its ranges of K

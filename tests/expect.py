@@ -59,8 +59,6 @@ def expected_ex_path(M, N, K, op_a, op_b):
     if splitk_auto(M, N, K, 64):
         return "f16_splitk"
     large = M * N * K >= 1 << 30 and K >= 8
-    if not nt and large and (op_a == "n" or M >= 8) and (op_b == "t" or N >= 8):
-        return "f16_staged"        # K-major operands read in place
     # NT in place, or the other layouts through 16-byte aligned transposed copies
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))

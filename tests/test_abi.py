@@ -247,30 +247,29 @@ def ex_ws(lib, type_, op_a, op_b, M, N, K, lda=None, ldb=None):
 
 
 def test_gemm_ex_validation_and_paths(lib, monkeypatch):
-    """Layouts: op N/T per operand with their leading-dimension rules; large
-    products read K-major operands in place (the register-staged wide tiles),
-    smaller ones through transposed copies in the workspace; unknown
-    enumerations are GEMM_ERR_BAD_ARG."""
+    """Layouts: op N/T per operand with their leading-dimension rules; the
+    other layouts run through transposed copies in the workspace, then on the
+    A * B^T kernels the copies fit; unknown enumerations are
+    GEMM_ERR_BAD_ARG."""
     monkeypatch.delenv("MI355GEMM_FORCE_PATH", raising=False)
     N_, T_ = 0, 1
     for t in (0, 1):
         assert ex(lib, t, N_, T_, 5376, 5376, 2048) == F16_MFMA
-        assert ex(lib, t, N_, N_, 5376, 5376, 2048) == F16_STAGED    # B read K-major in place
-        assert ex(lib, t, T_, N_, 5376, 5376, 2048) == F16_STAGED
-        assert ex(lib, t, T_, T_, 5376, 5376, 2048) == F16_STAGED
-        assert ex(lib, t, T_, T_, 5000, 3001, 1537) == F16_STAGED
+        assert ex(lib, t, N_, N_, 5376, 5376, 2048) == F16_MFMA      # B copied transposed
+        assert ex(lib, t, T_, N_, 5376, 5376, 2048) == F16_MFMA
+        assert ex(lib, t, T_, T_, 5376, 5376, 2048) == F16_MFMA
+        assert ex(lib, t, T_, T_, 5000, 3001, 1537) == F16_STAGED    # ragged, on the copy
         assert ex(lib, t, T_, T_, 500, 301, 153) == F16_GENERAL      # through copies
         assert ex(lib, t, N_, N_, 1, 4096, 4096) == F16_GEMV
         assert ex(lib, t, T_, N_, 512, 512, 16384) == F16_SPLITK     # with its workspace
         # a copy has aligned, padded rows whatever the original alignment
         assert ex(lib, t, T_, T_, 256, 256, 64, A=ALIGNED + 2, lda=257) == F16_MFMA
         assert ex(lib, t, N_, T_, 256, 256, 64, A=ALIGNED + 2, lda=67) == F16_GENERAL
-        # a K-major operand needs 8 of its M or N columns for the wide tiles
         assert ex(lib, t, T_, T_, 1024 * 1024, 9, 1024) == F16_STAGED
-    # workspace sizes: none for NT, the wide tiles and the plain vector
-    # kernel; copies for smaller products; partial sums for K-major vectors
+    # workspace sizes: none for NT and the plain vector kernel; the copies in
+    # the other layouts; partial sums for K-major vectors
     assert ex_ws(lib, 0, N_, T_, 5376, 5376, 2048) == 0
-    assert ex_ws(lib, 0, N_, N_, 5376, 5376, 2048) == 0
+    assert ex_ws(lib, 0, N_, N_, 5376, 5376, 2048) == 5376 * 2048 * 2
     assert ex_ws(lib, 0, N_, T_, 1, 4096, 4096) == 0
     assert ex_ws(lib, 0, T_, T_, 500, 301, 153) == (500 * 160 * 2 + 255) // 256 * 256
     assert ex_ws(lib, 0, N_, N_, 100, 300, 153) == 300 * 160 * 2

@@ -83,8 +83,8 @@ def run_ex(A, B, op_a, op_b, fmt, M, N, bias=None, act="none", res=None, expect=
 
 # Shapes reach each kernel: fast tiles 256 x 256, 256 x 224, 128 x 128 and 128 x 192 (in the
 # other layouts on transposed copies), the edge kernel (ragged, odd K), the matrix-vector
-# kernel both ways, split-K, and the register-staged wide tiles (1000 x 1001 x 1111: every
-# layout read in place, the K-major operands transposed in registers).
+# kernel both ways, split-K, and the register-staged wide tiles (1000 x 1001 x 1111, on the
+# transposed copies in the other layouts).
 SHAPES = [(256, 256, 64), (512, 448, 128), (128, 128, 192), (384, 576, 192), (133, 70, 45),
           (257, 255, 65), (1, 300, 777), (300, 3, 1000), (4, 129, 4100), (512, 512, 16384),
           (300, 200, 5000), (1000, 1001, 1111)]
@@ -133,11 +133,11 @@ def test_layouts_fused(shape, layout, fmt, act, use_bias, use_res):
     check16(got, ref, sab, fmt, babs, rabs, fused=True)
 
 
-# The register-staged wide tiles on K-major operands: ragged M and N at every
-# residue of a K-major operand's 8-column pieces (1030 = 8 x 128 + 6, 1100 = 8 x
-# 137 + 4, 1001, 1023, 2049 = 8 x 256 + 1), K tails of 9, 23 and 4 elements and a
-# slab wholly past K (777, 1111, 1100), a 256 x 224 tile choice (N = 3001), and
-# an N of 9 (one column past a piece) for a K-major B.
+# Large ragged products in the other layouts: the K-major operands are copied
+# transposed (rows of round8(K)) and the register-staged wide tiles run on the
+# copies -- ragged M and N at several residues of 8 (1030, 1100, 1001, 1023,
+# 2049), K tails of 9, 23 and 4 elements and a slab wholly past K (777, 1111,
+# 1100), a 256 x 224 tile choice (N = 3001), and an N of 9 for a K-major B.
 STAGED_LAYOUT_SHAPES = [(1030, 1100, 1000), (1000, 1001, 1111), (1023, 2049, 777),
                         (2049, 1023, 1100), (700, 3001, 600), (1024 * 128, 9, 1024)]
 
@@ -145,7 +145,7 @@ STAGED_LAYOUT_SHAPES = [(1030, 1100, 1000), (1000, 1001, 1111), (1023, 2049, 777
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("layout", LAYOUTS[1:], ids=lambda l: "".join(l))
 @pytest.mark.parametrize("shape", STAGED_LAYOUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_layouts_staged_in_place(shape, layout, fmt):
+def test_layouts_staged_on_copies(shape, layout, fmt):
     M, N, K = shape
     op_a, op_b = layout
     sa, sb = stored_shapes(M, N, K, op_a, op_b)
@@ -153,7 +153,7 @@ def test_layouts_staged_in_place(shape, layout, fmt):
     dA, dB = to_dev(A, fmt), to_dev(B, fmt)
     dC = torch.full((M, N), float("nan"), device=DEV, dtype=dtype_of(fmt))
     assert dg.ex_path(dA, dB, dC, op_a, op_b) == "f16_staged"
-    assert dg.ex_workspace_bytes(dA, dB, dC, op_a, op_b) == 0
+    assert dg.ex_workspace_bytes(dA, dB, dC, op_a, op_b) > 0
     dg.gemm_ex(dA, dB, dC, op_a, op_b)
     torch.cuda.synchronize()
     ref, sab = reference(A, B, op_a, op_b, fmt)
@@ -162,7 +162,8 @@ def test_layouts_staged_in_place(shape, layout, fmt):
 
 def test_layouts_staged_unaligned_exact_and_fused():
     """K-major operands one element into their buffers with odd leading
-    dimensions, C unaligned; small-integer operands make every product exact
+    dimensions (copied transposed, then the register-staged wide tiles), C
+    unaligned; small-integer operands make every product exact
     (bit for bit against the exact sum rounded once).  Then the fused
     write-back on the same path."""
     for (op_a, op_b) in LAYOUTS[1:]:

@@ -38,6 +38,7 @@ V_NAME = "hgemv_nt_1x16384x4096"
 # streams its weights from HBM as a decode step over many layers would.
 V_COPIES = 4
 S_NAME = "hgemm_nt_128x128x16384"
+Q_NAME = "hgemm_nt_2048x2304x768"
 
 
 def parse_args():
@@ -46,13 +47,15 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused",
-                                       "hgemv", "hgemm_splitk", "sgemm_256", "sgemm_1024"],
+                                       "hgemv", "hgemm_splitk", "sgemm_256", "sgemm_1024",
+                                       "sgemm_beta", "hgemm_qkv"],
                     default="both",
                     help="time only one product (for profiling): one of the two step products, "
                          "the ragged 5000x3001x1537 fp16 product, the 5376^2 x 2048 product "
                          "with the fused bias + SiLU + residual write-back, the 1 x 16384 x "
-                         "4096 decode product, the 128 x 128 x 16384 split-K product, or the "
-                         "256^3 or 1024^3 SGEMM")
+                         "4096 decode product, the 128 x 128 x 16384 split-K product, the "
+                         "256^3 or 1024^3 SGEMM, the 4096^3 SGEMM with beta = 0.5, or the "
+                         "2048 x 2304 x 768 fused-QKV fp16 product")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -87,6 +90,8 @@ KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sge
                           "dense_gemm_sgemm_amd/build.py"]
 KERNEL_SOURCES[S_NAME] = KERNEL_SOURCES[H_NAME] + ["dense_gemm_sgemm_amd/csrc/splitk.hip"]
 KERNEL_SOURCES["sgemm_256"] = KERNEL_SOURCES["sgemm_1024"] = KERNEL_SOURCES[F_NAME]
+KERNEL_SOURCES[F_NAME + "_beta0.5"] = KERNEL_SOURCES[F_NAME]
+KERNEL_SOURCES[Q_NAME] = KERNEL_SOURCES[H_NAME]
 COPY_BYTES = 1 << 30
 # Bytes written between launches for the cold-cache figure: twice the 256 MB
 # last-level cache.
@@ -395,6 +400,21 @@ def main():
         assert dg.f32_path(dAs, dBs, dCs) == "f32_mfma"
         parts.append((args.only, "f32", "sgemm_stream64_kernel", flops(sw),
                       lambda: dg.gemm_f32(dAs, dBs, dCs, 1.0, 0.0)))
+    if args.only == "sgemm_beta":
+        Ab, Bb, Cb = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"], with_c=True)
+        dAb, dBb, dCb = (torch.from_numpy(x).to(dev) for x in (Ab, Bb, Cb))
+        assert dg.f32_path(dAb, dBb, dCb, 1.0, 0.5) == "f32_mfma"
+        # C accumulates 0.5 C + A B from launch to launch: bounded (C -> 2 A B)
+        parts.append((F_NAME + "_beta0.5", "f32", "sgemm_stream_kernel", flops(fw),
+                      lambda: dg.gemm_f32(dAb, dBb, dCb, 1.0, 0.5)))
+    if args.only == "hgemm_qkv":
+        qw = inputs.WORKLOADS[Q_NAME]
+        Aq, Bq = inputs.workload_operands(Q_NAME)
+        dAq, dBq = torch.from_numpy(Aq).to(dev), torch.from_numpy(Bq).to(dev)
+        dCq = torch.empty(qw["M"], qw["N"], device=dev, dtype=torch.float16)
+        assert dg.f16_nt_path(dAq, dBq, dCq) == "f16_mfma"
+        parts.append((Q_NAME, "f16", "hgemm_nt_kernel", flops(qw),
+                      lambda: dg.gemm_f16_nt(dAq, dBq, dCq)))
     if args.only in ("both", "sgemm"):
         Af, Bf = operand_values(args.operands, *inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])[:2])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
@@ -469,7 +489,8 @@ def main():
         "data": ("synthetic (seeded uniform[-1,1); inputs resident in HBM)" if args.operands == "seeded"
                  else "constant %s operands (power-limit measurement, not the workload)" % args.operands),
         "config": {"workload": " + ".join(p[0] for p in parts),
-                   "shapes": {p[0]: [inputs.WORKLOADS[p[0].replace("_bias_silu_residual", "")][k]
+                   "shapes": {p[0]: [inputs.WORKLOADS[p[0].replace("_bias_silu_residual", "")
+                                                     .replace("_beta0.5", "")][k]
                                      for k in ("M", "N", "K")] for p in parts},
                    "parallelism": "single GPU"},
         "kernels": kernels,

@@ -946,6 +946,51 @@ def test_f32_stream64_alpha_beta_padded_and_exact():
     assert np.array_equal(gpu_f32(Ai, Bi, expect="f32_mfma").astype(np.float64), oracle.gemm_f32(Ai, Bi))
 
 
+# Products with at most a quarter as many 64 x 64 tiles as CUs (K a multiple
+# of 64, at most 4096) run on the 32 x 32 kernel whose four waves split each
+# K chunk of up to 256 four ways: one chunk (256^3, 64^3), a short last chunk
+# (320 = 256 + 64, 192), sixteen chunks (512 x 512 x 4096: 256 workgroups),
+# a wide strip.  Element by element against the oracle; the smallest of
+# these shapes also appear in the stream64 list above, which the 32 x 32
+# kernel now takes.
+SMALL32_SHAPES = [(256, 256, 256), (64, 64, 64), (128, 512, 320), (512, 512, 4096),
+                  (64, 1024, 192), (256, 128, 1088)]
+
+
+@pytest.mark.parametrize("shape", SMALL32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_small32_shapes(shape):
+    M, N, K = shape
+    A, B, _ = inputs.sgemm_operands(M, N, K)
+    got = gpu_f32(A, B, expect="f32_mfma")
+    f32_check(got, oracle.gemm_f32(A, B), f32_tolerance(K, 1.0, 1.0))
+
+
+def test_f32_small32_alpha_beta_nan_exact_and_repeats():
+    """alpha / beta with C read, beta = 0 with NaN in C, padded leading
+    dimensions (the padding untouched), small integers exact, and bitwise
+    repeats (the four partial tiles are added in a fixed order)."""
+    M, N, K = 256, 320, 576
+    pad = 4
+    Abig, Bbig, Cbig = inputs.sgemm_operands(M, N + pad, K + pad, with_c=True)
+    A, B, C = Abig[:, :K], Bbig[:K, :N], Cbig[:, :N]
+    dA, dB, dC = dev(Abig), dev(Bbig), dev(Cbig)
+    dAv, dBv, dCv = dA[:, :K], dB[:K, :N], dC[:, :N]
+    assert dg.f32_path(dAv, dBv, dCv, 1.5, -0.75) == "f32_mfma"
+    dg.gemm_f32(dAv, dBv, dCv, 1.5, -0.75)
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    f32_check(got[:, :N], oracle.gemm_f32(A, B, 1.5, -0.75, C),
+              f32_tolerance(K, 1.0, 1.0, 1.5, -0.75, 1.0))
+    assert np.array_equal(got[:, N:], Cbig[:, N:])
+    one = gpu_f32(A, B, 1.0, 0.0)                     # C prefilled with NaN
+    assert np.all(np.isfinite(one))
+    assert np.array_equal(gpu_f32(A, B, 1.0, 0.0), one)
+    assert np.array_equal(gpu_f32(A, B, 2.0, 0.0), 2.0 * one)
+    Ai = inputs.small_ints((M, 1024), 15, -3, 3, np.float32)
+    Bi = inputs.small_ints((1024, N), 16, -3, 3, np.float32)
+    assert np.array_equal(gpu_f32(Ai, Bi, expect="f32_mfma").astype(np.float64), oracle.gemm_f32(Ai, Bi))
+
+
 # Large ragged or unaligned fp32 products run on the edge kernel, which reads
 # the operands in place: 1030 x 1100 x 1000 (ragged M, N and K), 2048 x 2048 x
 # 2000 (K not a multiple of 64: the 16-deep full tiles), 2000^3.  The masked

@@ -320,10 +320,11 @@ enum {
                                 /*   cut into ranges, fp32 partial sums in the    */
                                 /*   workspace, ordered reduction                 */
   /* 9 is not used */
-  GEMM_PATH_F16_STAGED = 10     /* large ragged, unaligned or (gemm_ex) K-major:  */
-                                /*   v_mfma wide tiles with register-staged loads */
-                                /*   (any shape, leading dimension, 2-byte        */
-                                /*   alignment, layout), masked stores; no copies */
+  GEMM_PATH_F16_STAGED = 10     /* large ragged or unaligned products: v_mfma     */
+                                /*   wide tiles with register-staged loads (any   */
+                                /*   shape, leading dimension, 2-byte alignment), */
+                                /*   masked stores; the operands read in place    */
+                                /*   (gemm_ex: after any transposed copy)         */
 };
 
 MI355GEMM_API int gemm_f32_path(int M, int N, int K, float alpha,

@@ -48,14 +48,16 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused",
                                        "hgemv", "hgemm_splitk", "sgemm_256", "sgemm_1024",
-                                       "sgemm_beta", "hgemm_qkv"],
+                                       "sgemm_beta", "hgemm_qkv", "blas_context"],
                     default="both",
                     help="time only one product (for profiling): one of the two step products, "
                          "the ragged 5000x3001x1537 fp16 product, the 5376^2 x 2048 product "
                          "with the fused bias + SiLU + residual write-back, the 1 x 16384 x "
                          "4096 decode product, the 128 x 128 x 16384 split-K product, the "
                          "256^3 or 1024^3 SGEMM, the 4096^3 SGEMM with beta = 0.5, or the "
-                         "2048 x 2304 x 768 fused-QKV fp16 product")
+                         "2048 x 2304 x 768 fused-QKV fp16 product; blas_context times "
+                         "torch.matmul (hipBLASLt) instead, on the step's operands and on "
+                         "4096^3 and 8192^3 fp16 A*B^T, for context only")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -332,6 +334,16 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     return res
 
 
+def shape_of(inputs, name: str):
+    """[M, N, K] of a part of the step (the workload named, or the shape its
+    name carries)."""
+    base = name.replace("_bias_silu_residual", "").replace("_beta0.5", "")
+    base = base.replace("torch_matmul_f16_nt_", "").replace("torch_matmul_", "")
+    if base in inputs.WORKLOADS:
+        return [inputs.WORKLOADS[base][k] for k in ("M", "N", "K")]
+    return [int(x) for x in base.split("x")]
+
+
 def main():
     args = parse_args()
     if args.copy_calibration:
@@ -415,6 +427,19 @@ def main():
         assert dg.f16_nt_path(dAq, dBq, dCq) == "f16_mfma"
         parts.append((Q_NAME, "f16", "hgemm_nt_kernel", flops(qw),
                       lambda: dg.gemm_f16_nt(dAq, dBq, dCq)))
+    if args.only == "blas_context":
+        # Context, never the library: the vendor GEMM on the same operands.
+        # B^T is passed as a transposed view, as an A*B^T caller would.
+        for (M, N, K) in [(hw["M"], hw["N"], hw["K"]), (4096, 4096, 4096), (8192, 8192, 8192)]:
+            Ab, Bb = inputs.hgemm_nt_operands(M, N, K)
+            dAb, dBb = torch.from_numpy(Ab).to(dev), torch.from_numpy(Bb).to(dev)
+            name = "torch_matmul_f16_nt_%dx%dx%d" % (M, N, K)
+            parts.append((name, "f16", "torch.matmul (hipBLASLt)", 2.0 * M * N * K,
+                          (lambda a, b: lambda: torch.matmul(a, b.t()))(dAb, dBb)))
+        Af, Bf = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])[:2]
+        dAx, dBx = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
+        parts.append(("torch_matmul_" + F_NAME, "f32", "torch.matmul (hipBLASLt)", flops(fw),
+                      lambda: torch.matmul(dAx, dBx)))
     if args.only in ("both", "sgemm"):
         Af, Bf = operand_values(args.operands, *inputs.sgemm_operands(fw["M"], fw["N"], fw["K"])[:2])
         dAf, dBf = torch.from_numpy(Af).to(dev), torch.from_numpy(Bf).to(dev)
@@ -489,9 +514,7 @@ def main():
         "data": ("synthetic (seeded uniform[-1,1); inputs resident in HBM)" if args.operands == "seeded"
                  else "constant %s operands (power-limit measurement, not the workload)" % args.operands),
         "config": {"workload": " + ".join(p[0] for p in parts),
-                   "shapes": {p[0]: [inputs.WORKLOADS[p[0].replace("_bias_silu_residual", "")
-                                                     .replace("_beta0.5", "")][k]
-                                     for k in ("M", "N", "K")] for p in parts},
+                   "shapes": {p[0]: shape_of(inputs, p[0]) for p in parts},
                    "parallelism": "single GPU"},
         "kernels": kernels,
         "roofline": roofline,

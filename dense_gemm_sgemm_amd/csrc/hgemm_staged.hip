@@ -16,7 +16,9 @@
 //    wave may hold 512 registers: the 64 (or 56) accumulator quads live in
 //    the AGPRs for the whole tile -- the matrix instructions are asm
 //    statements whose accumulator operand is an AGPR tuple, so the compiler
-//    never moves them -- and two k-steps of operand fragments in the VGPRs;
+//    never moves them -- and the operand fragments in the VGPRs: B fragments
+//    of the current and the next slab, A fragments of one slab (A fragment i
+//    of the next slab is read into the registers row i has finished with);
 //  * rows that start at any 2-byte address rule out the direct global -> LDS
 //    copies, so slabs are register-staged: each thread loads 16-byte chunks
 //    with ordinary loads (unaligned access is enabled on this target) and

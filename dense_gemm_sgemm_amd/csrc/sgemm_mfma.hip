@@ -637,34 +637,40 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream64_kernel(F32Args p, 
 }  // namespace stream64
 
 // Products too small to give every CU a 64 x 64 tile (256^3: 16 tiles).  One
-// 256-thread workgroup per 32 x 32 tile of C, four times as many workgroups
-// as 64 x 64 tiles; each of its four waves computes the whole tile over its
-// own quarter of every K chunk, so the tile's K is walked four ways at once
-// (the per-wave split of the pages' split-K, section 6.5.6 of page 1, inside
-// one workgroup), and the four partial tiles are added through LDS in the
-// fixed order 0, 1, 2, 3 (results repeat bitwise).
+// 256-thread workgroup per BT x BT tile of C (BT = 32, or 16 when even 32 x 32
+// tiles leave CUs idle), four or sixteen times as many workgroups as 64 x 64
+// tiles; each of its four waves computes the whole tile over its own quarter
+// of every K chunk, so the tile's K is walked four ways at once (the per-wave
+// split of the pages' split-K, section 6.5.6 of page 1, inside one
+// workgroup), and the four partial tiles are added through LDS in the fixed
+// order 0, 1, 2, 3 (results repeat bitwise).
 //
 //  * K is taken in chunks of up to 256 (a multiple of 64): every thread loads
-//    8 chunks of 4 floats of A (rows of the tile) and 8 of B (K rows) with
-//    16-byte loads, all issued before the first is written to LDS, and the
-//    next chunk's loads are issued before the current chunk's products;
-//  * LDS rows are padded by 4 floats: A [32][260] (a lane's four k of one
-//    row are one conflict-free 16-byte read), B [256][36] (the four K rows of
+//    BT / 4 chunks of 4 floats of A (rows of the tile) and BT / 4 of B (K
+//    rows) with 16-byte loads, all issued before the first is written to LDS,
+//    and the next chunk's loads are issued before the current chunk's
+//    products;
+//  * LDS rows are padded by 4 floats: A [BT][260] (a lane's four k of one row
+//    are one conflict-free 16-byte read), B [256][BT + 4] (the four K rows of
 //    a lane group land 16 banks apart);
-//  * wave w takes k = w * kc / 4 .. (w + 1) * kc / 4 of a chunk of kc, 2 x 2
-//    blocks of v_mfma_f32_16x16x4_f32 with the MFMA step bijection of the
-//    register-staged kernel (step s of 16-k part q: lane group g takes
+//  * wave w takes k = w * kc / 4 .. (w + 1) * kc / 4 of a chunk of kc,
+//    (BT / 16)^2 blocks of v_mfma_f32_16x16x4_f32 with the MFMA step bijection
+//    of the register-staged kernel (step s of 16-k part q: lane group g takes
 //    k = 16 q + 4 g + s for both operands), B as the first operand so that a
 //    lane's accumulator quad holds four consecutive columns of one row;
 //  * the write-back is the other kernels' alpha * sum (+ beta * C, C read
-//    only when beta != 0), one 16-byte store per thread.
-namespace small32 {
-constexpr int BT = 32, KC = 256;
-constexpr int kAPitch = KC + 4, kBPitch = BT + 4;   // floats
+//    only when beta != 0), one 16-byte store per output quad.
+namespace smallk {
+constexpr int KC = 256;
 constexpr int kThreads = 256;
-constexpr int kLoads = BT * KC / 4 / kThreads;      // 16-byte chunks per thread per operand: 8
 
-__global__ __launch_bounds__(kThreads, 1) void sgemm_small32_kernel(F32Args p, int64_t tile_base) {
+template <int BT>
+__global__ __launch_bounds__(kThreads, 1) void sgemm_small_kernel(F32Args p, int64_t tile_base) {
+  constexpr int IB = BT / 16;                         // blocks per wave per dimension
+  constexpr int kAPitch = KC + 4, kBPitch = BT + 4;   // floats
+  constexpr int kLoads = BT * KC / 4 / kThreads;      // 16-byte chunks per thread per operand
+  constexpr int kBRowChunks = BT / 4;                 // chunks per K row of B
+  constexpr int kBRowStep = kThreads / kBRowChunks;   // K rows between a thread's B chunks
   __shared__ __attribute__((aligned(16))) float sa[BT * kAPitch];
   __shared__ __attribute__((aligned(16))) float sb[KC * kBPitch];
   const int tid = threadIdx.x;
@@ -677,17 +683,19 @@ __global__ __launch_bounds__(kThreads, 1) void sgemm_small32_kernel(F32Args p, i
   const int m0 = tm * BT, n0 = tn * BT;
 
   // Chunk u of this thread: A row (tid / 64) + 4 u, k 4 (tid % 64) .. + 3;
-  // B K row (tid / 8) + 32 u, columns 4 (tid % 8) .. + 3.
+  // B K row tid / kBRowChunks + kBRowStep u, columns 4 (tid % kBRowChunks) .. + 3.
+  const int brow = tid / kBRowChunks, bcol = 4 * (tid % kBRowChunks);
   const float* a_src = p.A + (int64_t)(m0 + (tid >> 6)) * p.lda + 4 * (tid & 63);
-  const float* b_src = p.B + (int64_t)(tid >> 3) * p.ldb + n0 + 4 * (tid & 7);
+  const float* b_src = p.B + (int64_t)brow * p.ldb + n0 + bcol;
   f4 ra[kLoads], rb[kLoads];
   auto load_chunk = [&](int k0, int kc) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kLoads; ++u) {
       // A: rows 4 u + tid / 64 hold k 4 (tid % 64) .. + 3 of the chunk, which
-      // exist while 4 (tid % 64) < kc; B: K row (tid / 8) + 32 u < kc
+      // exist while 4 (tid % 64) < kc; B: K row brow + kBRowStep u < kc
       if (4 * (tid & 63) < kc) ra[u] = *(const f4*)(a_src + (int64_t)(4 * u) * p.lda + k0);
-      if ((tid >> 3) + 32 * u < kc) rb[u] = *(const f4*)(b_src + (int64_t)(k0 + 32 * u) * p.ldb);
+      if (brow + kBRowStep * u < kc)
+        rb[u] = *(const f4*)(b_src + (int64_t)(k0 + kBRowStep * u) * p.ldb);
     }
   };
   auto store_chunk = [&](int kc) __attribute__((always_inline)) {
@@ -695,16 +703,16 @@ __global__ __launch_bounds__(kThreads, 1) void sgemm_small32_kernel(F32Args p, i
     for (int u = 0; u < kLoads; ++u) {
       if (4 * (tid & 63) < kc)
         *(f4*)(sa + ((tid >> 6) + 4 * u) * kAPitch + 4 * (tid & 63)) = ra[u];
-      if ((tid >> 3) + 32 * u < kc)
-        *(f4*)(sb + ((tid >> 3) + 32 * u) * kBPitch + 4 * (tid & 7)) = rb[u];
+      if (brow + kBRowStep * u < kc)
+        *(f4*)(sb + (brow + kBRowStep * u) * kBPitch + bcol) = rb[u];
     }
   };
 
-  f4 acc[2][2];
+  f4 acc[IB][IB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < IB; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
 
   int kc = p.K < KC ? p.K : KC;
   load_chunk(0, kc);
@@ -720,20 +728,20 @@ __global__ __launch_bounds__(kThreads, 1) void sgemm_small32_kernel(F32Args p, i
     const int kw = w * (kc / 4);
     for (int q = 0; q < parts; ++q) {
       const int kk = kw + 16 * q + 4 * g;
-      f4 av[2];
+      f4 av[IB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) av[i] = *(const f4*)(sa + (16 * i + r) * kAPitch + kk);
-      f4 bv[2];
+      for (int i = 0; i < IB; ++i) av[i] = *(const f4*)(sa + (16 * i + r) * kAPitch + kk);
+      f4 bv[IB];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < IB; ++j)
 #pragma unroll
         for (int s = 0; s < 4; ++s) bv[j][s] = sb[(kk + s) * kBPitch + 16 * j + r];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < IB; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < IB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[j][s], av[i][s], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(stream::kWaitLgkm0);
@@ -742,32 +750,37 @@ __global__ __launch_bounds__(kThreads, 1) void sgemm_small32_kernel(F32Args p, i
   }
 
   // acc[i][j][v] is this wave's part of C[m0 + 16 i + r][n0 + 16 j + 4 g + v]:
-  // the four partial tiles go to LDS (over A's rows), then thread t adds the
-  // four partials of row t / 8, columns 4 (t % 8) .. + 3, in wave order.
+  // the four partial tiles go to LDS (over A's rows), then each output quad
+  // (row t / (BT / 4), columns 4 (t % (BT / 4)) .. + 3 for thread t) adds the
+  // four partials in wave order.
   constexpr int kPart = BT * kBPitch;   // floats per partial tile
   static_assert(4 * kPart <= BT * kAPitch, "partials fit over A");
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < IB; ++j)
       *(f4*)(sa + w * kPart + (16 * i + r) * kBPitch + 16 * j + 4 * g) = acc[i][j];
   __builtin_amdgcn_s_waitcnt(stream::kWaitLgkm0);
   asm volatile("s_barrier" ::: "memory");
-  const int row = tid >> 3, col = 4 * (tid & 7);
-  f4 sum = *(const f4*)(sa + row * kBPitch + col);
+  constexpr int kQuads = BT * BT / 4;
+  if (kQuads >= kThreads || tid < kQuads) {
+    const int row = tid / (BT / 4), col = 4 * (tid % (BT / 4));
+    f4 sum = *(const f4*)(sa + row * kBPitch + col);
 #pragma unroll
-  for (int v = 1; v < 4; ++v) sum += *(const f4*)(sa + v * kPart + row * kBPitch + col);
-  float* c = p.C + (int64_t)(m0 + row) * p.ldc + n0 + col;
-  const float alpha = p.alpha, beta = p.beta;
-  f4 out = alpha * sum;
-  if (beta != 0.f) {
-    const f4 old = *(const f4*)c;
+    for (int v = 1; v < 4; ++v) sum += *(const f4*)(sa + v * kPart + row * kBPitch + col);
+    float* c = p.C + (int64_t)(m0 + row) * p.ldc + n0 + col;
+    const float alpha = p.alpha, beta = p.beta;
+    f4 out = alpha * sum;
+    if (beta != 0.f) {
+      const f4 old = *(const f4*)c;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, old[e], out[e]);
+      for (int e = 0; e < 4; ++e) out[e] = fmaf(beta, old[e], out[e]);
+    }
+    *(f4*)c = out;
   }
-  *(f4*)c = out;
+  static_assert(BT * BT / 4 <= kThreads, "one output quad per thread at most");
 }
-}  // namespace small32
+}  // namespace smallk
 
 // Tile size for an M x N product: 128 x 128 while that gives every CU work,
 // 64 x 64 below.
@@ -818,9 +831,10 @@ bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void
          ldb < kStreamMaxLd;
 }
 
-// The 32 x 32 kernel: whole tiles, K a multiple of 64 up to 4096, and at
+// The small-tile kernel: whole tiles, K a multiple of 64 up to 4096, and at
 // most a quarter as many 64 x 64 tiles as CUs (it then runs at least four
-// times as many workgroups as the 64 x 64 kernels would).
+// times as many workgroups as the 64 x 64 kernels would); 16 x 16 tiles when
+// even 32 x 32 tiles would leave CUs idle.
 static bool f32_small32_fits(int M, int N, int K, const void* A, int64_t lda, const void* B,
                              int64_t ldb, const void* C, int64_t ldc, int cus) {
   const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
@@ -830,10 +844,14 @@ static bool f32_small32_fits(int M, int N, int K, const void* A, int64_t lda, co
 }
 
 hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
-  if (f32_small32_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, cus))
-    return launch_tiles((const void*)small32::sgemm_small32_kernel, a,
-                        (int64_t)(a.M / small32::BT) * (a.N / small32::BT), small32::kThreads, 0,
-                        stream);
+  if (f32_small32_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, cus)) {
+    const int64_t tiles32 = (int64_t)(a.M / 32) * (a.N / 32);
+    if (tiles32 < cus)
+      return launch_tiles((const void*)smallk::sgemm_small_kernel<16>, a, 4 * tiles32,
+                          smallk::kThreads, 0, stream);
+    return launch_tiles((const void*)smallk::sgemm_small_kernel<32>, a, tiles32,
+                        smallk::kThreads, 0, stream);
+  }
   if (f32_stream_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc))
     return launch_stream(a, cus, stream);
   if (!small_tiles(a.M, a.N, cus) && a.M % 128 == 0 && a.N % 128 == 0)

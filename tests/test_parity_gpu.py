@@ -947,14 +947,16 @@ def test_f32_stream64_alpha_beta_padded_and_exact():
 
 
 # Products with at most a quarter as many 64 x 64 tiles as CUs (K a multiple
-# of 64, at most 4096) run on the 32 x 32 kernel whose four waves split each
-# K chunk of up to 256 four ways: one chunk (256^3, 64^3), a short last chunk
-# (320 = 256 + 64, 192), sixteen chunks (512 x 512 x 4096: 256 workgroups),
-# a wide strip.  Element by element against the oracle; the smallest of
-# these shapes also appear in the stream64 list above, which the 32 x 32
-# kernel now takes.
+# of 64, at most 4096) run on the small-tile kernel whose four waves split
+# each K chunk of up to 256 four ways, with 16 x 16 tiles while 32 x 32 ones
+# would leave CUs idle: one chunk (256^3, 64^3), a short last chunk (320 =
+# 256 + 64, 192, 1088), sixteen chunks (512 x 512 x 4096), a wide strip; the
+# 32 x 32 tiles at 512 x 512 x 4096 and 256 x 1024 x 320 (256 tiles each),
+# the 16 x 16 ones at the others.  Element by element against the oracle;
+# the smallest of these shapes also appear in the stream64 list above, which
+# the small-tile kernel now takes.
 SMALL32_SHAPES = [(256, 256, 256), (64, 64, 64), (128, 512, 320), (512, 512, 4096),
-                  (64, 1024, 192), (256, 128, 1088)]
+                  (64, 1024, 192), (256, 128, 1088), (256, 1024, 320)]
 
 
 @pytest.mark.parametrize("shape", SMALL32_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -965,11 +967,13 @@ def test_f32_small32_shapes(shape):
     f32_check(got, oracle.gemm_f32(A, B), f32_tolerance(K, 1.0, 1.0))
 
 
-def test_f32_small32_alpha_beta_nan_exact_and_repeats():
+@pytest.mark.parametrize("shape", [(256, 320, 576), (512, 512, 576)], ids=["16x16", "32x32"])
+def test_f32_small32_alpha_beta_nan_exact_and_repeats(shape):
     """alpha / beta with C read, beta = 0 with NaN in C, padded leading
     dimensions (the padding untouched), small integers exact, and bitwise
-    repeats (the four partial tiles are added in a fixed order)."""
-    M, N, K = 256, 320, 576
+    repeats (the four partial tiles are added in a fixed order), on both tile
+    sizes."""
+    M, N, K = shape
     pad = 4
     Abig, Bbig, Cbig = inputs.sgemm_operands(M, N + pad, K + pad, with_c=True)
     A, B, C = Abig[:, :K], Bbig[:K, :N], Cbig[:, :N]

@@ -410,7 +410,8 @@ def main():
         dAs, dBs = torch.from_numpy(As).to(dev), torch.from_numpy(Bs).to(dev)
         dCs = torch.empty(sw["M"], sw["N"], device=dev, dtype=torch.float32)
         assert dg.f32_path(dAs, dBs, dCs) == "f32_mfma"
-        parts.append((args.only, "f32", "sgemm_stream64_kernel", flops(sw),
+        kern = "sgemm_small_kernel" if args.only == "sgemm_256" else "sgemm_stream64_kernel"
+        parts.append((args.only, "f32", kern, flops(sw),
                       lambda: dg.gemm_f32(dAs, dBs, dCs, 1.0, 0.0)))
     if args.only == "sgemm_beta":
         Ab, Bb, Cb = inputs.sgemm_operands(fw["M"], fw["N"], fw["K"], with_c=True)

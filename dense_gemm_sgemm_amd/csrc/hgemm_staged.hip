@@ -19,14 +19,19 @@
 //    never moves them -- and the operand fragments in the VGPRs: B fragments
 //    of the current and the next slab, A fragments of one slab (A fragment i
 //    of the next slab is read into the registers row i has finished with);
-//  * rows that start at any 2-byte address rule out the direct global -> LDS
-//    copies, so slabs are register-staged: each thread loads 16-byte chunks
-//    with ordinary loads (unaligned access is enabled on this target) and
-//    writes them to LDS one slab later.  K is walked in slabs of 32 (rows of
-//    64 bytes, 4 chunks); during slab s the loads of slab s + 3, the LDS
-//    writes of slab s + 2 and the fragment reads of slab s + 1 are spread
-//    over the slab's 64 (56) matrix instructions, with one barrier per slab
-//    and two LDS stages;
+//  * K is walked in slabs of 32 (rows of 64 bytes, 4 chunks), with one
+//    barrier per slab.  Rows at 16-byte addresses (DIRECT) are copied global
+//    -> LDS with global_load_lds_dwordx4 into a ring of four LDS stages:
+//    during slab s the copies of slab s + 4 and the fragment reads of slab
+//    s + 1 are spread over the slab's 64 (56) matrix instructions, and the
+//    barrier at the top of slab s waits for this wave's copies of slab s + 1
+//    only (the two slabs after it stay in flight).  Rows at 2-byte addresses
+//    are register-staged instead (the direct copies of such rows measured
+//    slower): each thread loads 16-byte chunks with ordinary loads
+//    (unaligned access is enabled on this target) and writes them to LDS one
+//    slab later; during slab s the loads of slab s + 3, the LDS writes of
+//    slab s + 2 and the fragment reads of slab s + 1 share the slab's matrix
+//    instructions, with two LDS stages;
 //  * chunk c of slab row r sits at position c ^ ((r >> 2) & 2).  Under the
 //    measured ds_read_b128 bank model (64 banks of 4 bytes, 16 lanes served
 //    per cycle in the groups {0-3, 12-15, 20-23, 24-27} and {4-7, 8-11,
@@ -35,9 +40,11 @@
 //    8-lane group of LDS writes covers 128 contiguous bytes;
 //  * boundaries: a row past M or N re-reads the matrix's last row (its
 //    products are never stored); in a slab that reaches past K each chunk is
-//    loaded from a start clamped to K - 8 and shifted and zero-filled in
-//    registers before its LDS write, so every chunk is always exactly one
-//    load instruction and the compiler's wait counts stay exact;
+//    loaded from a start clamped to K - 8 and shifted and zero-filled --
+//    in registers before its LDS write, or (DIRECT) in LDS by the thread
+//    whose copy wrote it, once the copy has landed and before the barrier
+//    after which the slab is read -- so every chunk is always exactly one
+//    load instruction;
 //  * B is the first MFMA operand, so a lane's accumulator quad holds four
 //    consecutive columns of one row; the epilogue applies the fused
 //    write-back (bias, activation, residual in fp32) where asked, rounds
@@ -62,7 +69,7 @@ using hgemm::h8;
 using hgemm::map_tile;
 using hgemm::static_for;
 
-template <int BN_>
+template <int BN_, bool DIRECT_>
 struct Cfg {
   static constexpr int BM = 256, BN = BN_, BK = 32;
   static constexpr int kThreads = 256;
@@ -77,7 +84,8 @@ struct Cfg {
   static constexpr int kLoadsA = BM / 64;                    // the first 4 are rows of A
   static constexpr int kOutRowBytes = 256;
   static constexpr int kOutBytes = 4 * 16 * kOutRowBytes;
-  static constexpr int kLds = 2 * kStage + kOutBytes;
+  static constexpr int kStages = DIRECT_ ? 4 : 2;
+  static constexpr int kLds = kStages * kStage + kOutBytes;
   static_assert(kLds <= 160 * 1024, "LDS");
 };
 
@@ -124,15 +132,17 @@ __device__ __forceinline__ h8 tail_fix(h8 x, int k, int K) {
 
 constexpr int kWaitLgkm0 = 0xC07F;      // s_waitcnt lgkmcnt(0)
 constexpr int kWaitVmLgkm0 = 0x0070;    // s_waitcnt vmcnt(0) lgkmcnt(0)
+// s_waitcnt vmcnt(vm) (vm < 64)
+constexpr int wait_vm(int vm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct Args {
   Args16 p;
   int64_t tiles;
 };
 
-template <int BN, int FMT, bool EPI>
+template <int BN, int FMT, bool EPI, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
-  typedef Cfg<BN> C;
+  typedef Cfg<BN, DIRECT> C;
   constexpr int BM = C::BM, kBM = C::kBM, kBN = C::kBN;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[C::kLds];
   const Args16& p = ta.p;
@@ -180,11 +190,14 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   set_offsets();
   // koff: byte offset of this lane's chunk in its row for the load target
   // slab, the chunk start clamped to K - 8 (re-computed once per slab); each
-  // load is then a wave-uniform row-0 base plus one 32-bit lane offset.
+  // load is then a wave-uniform row-0 base plus one 32-bit lane offset.  A
+  // direct copy writes lane l's 16 bytes to position l & 3 of its row, so the
+  // lane loads logical chunk kchunk = (l & 3) ^ swz(row) there.
+  const int kchunk = DIRECT ? lchunk ^ swz(lrow) : lchunk;
   const int kmax = p.K - 8;
   uint32_t koff = 0;
   auto set_koff = [&]() __attribute__((always_inline)) {
-    const int k = ct * C::BK + 8 * lchunk;
+    const int k = ct * C::BK + 8 * kchunk;
     koff = (uint32_t)(2 * (k < kmax ? k : kmax));
   };
   set_koff();
@@ -201,6 +214,30 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
       }
     }
     set_koff();
+  };
+  // DIRECT: copy u of this wave fills slab rows 16 w + 64 u .. + 15 (with
+  // BN = 224, waves 2 and 3 have no eighth row group and repeat their seventh,
+  // the same data to the same place, so that every wave issues the same
+  // number of copies per slab and one wait count serves them all).
+  auto copy_one = [&](int stage, int u) __attribute__((always_inline)) {
+    const int uu = (C::kLoads * 64 > BM + BN && u == C::kLoads - 1 && 16 * wave + 64 * u >= BM + BN)
+                       ? u - 1 : u;
+    const char* base = uu < C::kLoadsA ? (const char*)(p.A + (int64_t)cm0 * p.lda)
+                                       : (const char*)(p.B + (int64_t)cn0 * p.ldb);
+    __builtin_amdgcn_global_load_lds(
+        (hgemm::gbl_void_t*)(base + roff[uu] + koff),
+        (hgemm::lds_void_t*)(lds + stage * C::kStage + (16 * wave + 64 * uu) * C::kRow), 16, 0, 0);
+  };
+  // DIRECT: slab ts of a tile reaches past K and has landed in `stage`: each
+  // thread shifts and zero-fills the chunks its own copies wrote.
+  auto fix_tail = [&](int stage, int ts) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < C::kLoads; ++u) {
+      const int R = lrow + 64 * u;
+      if (C::kLoads * 64 > BM + BN && u == C::kLoads - 1 && R >= BM + BN) continue;
+      h8* q = (h8*)(lds + stage * C::kStage + R * C::kRow + 16 * lchunk);
+      *q = tail_fix(*q, ts * C::BK + 8 * kchunk, p.K);
+    }
   };
   h8 stg[2][C::kLoads];
   auto load_one = [&](int set, int u) __attribute__((always_inline)) {
@@ -260,7 +297,7 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   // needs.
   auto slab = [&](auto set_c, int gs) __attribute__((always_inline)) {
     constexpr int SET = decltype(set_c)::value;
-    const int rstage = (gs + 1) & 1, wstage = gs & 1;
+    const int rstage = (gs + 1) & (C::kStages - 1), wstage = gs & (C::kStages - 1);
     static_for<C::kMfma>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
       constexpr int i = q / kBN, j = q % kBN;
@@ -273,24 +310,41 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
       static_for<C::kLoads>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         if constexpr (q == u * C::kMfma / C::kLoads + 2) {
-          write_one(SET, wstage, u);
-          load_one(1 - SET, u);
+          if constexpr (DIRECT) {
+            copy_one(wstage, u);         // slab gs + 4, into slab gs's stage
+          } else {
+            write_one(SET, wstage, u);
+            load_one(1 - SET, u);
+          }
         }
       });
       __builtin_amdgcn_sched_barrier(0);
     });
-    if (++wt == nk) wt = 0;
+    if constexpr (!DIRECT) {
+      if (++wt == nk) wt = 0;
+    }
     advance_load();
   };
 
   // Top of a slab: this wave's fragment reads of the slab and its LDS writes
-  // of the next one are done; then the workgroup meets, after which the next
-  // slab is complete in LDS and every read of the previous slab's stage is
-  // done.  Right after an epilogue (whose stores follow the loads in flight)
-  // every memory operation is waited for.
-  auto top = [&](bool after_epi) __attribute__((always_inline)) {
-    if (after_epi) __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
-    else __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  // of the next one are done (DIRECT: its copies of the next slab -- index ts
+  // in its tile, in `stage` -- have landed, and are fixed if that slab
+  // reaches past K); then the workgroup meets, after which the next slab is
+  // complete in LDS and every read of the previous slab's stage is done.
+  // Right after an epilogue (whose stores follow the loads in flight) every
+  // memory operation is waited for.
+  auto top = [&](bool after_epi, int stage, int ts) __attribute__((always_inline)) {
+    if constexpr (DIRECT) {
+      if (after_epi) __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+      else __builtin_amdgcn_s_waitcnt(wait_vm(2 * C::kLoads));
+      if ((ts + 1) * C::BK > p.K) fix_tail(stage, ts);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    } else {
+      (void)stage;
+      (void)ts;
+      if (after_epi) __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+      else __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    }
     asm volatile("s_barrier" ::: "memory");
   };
 
@@ -299,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   // the quads are rounded and written (8 bytes per lane) to this wave's
   // 16-row staging area, chunk c of staging row R at slot c ^ R, then row
   // segments of 8 are stored, element by element where a segment crosses N.
-  unsigned char* stage_out = lds + 2 * C::kStage + wave * (16 * C::kOutRowBytes);
+  unsigned char* stage_out = lds + C::kStages * C::kStage + wave * (16 * C::kOutRowBytes);
   auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
     const int cc = lane & 15;
     h4 bq[kBN];
@@ -380,24 +434,35 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   typedef std::integral_constant<int, 0> S0;
   typedef std::integral_constant<int, 1> S1;
 
-  // Prologue: slab 0 written to stage 0 and slab 1 to stage 1, slab 2 loaded
-  // into staging set 0 (the stream has at least two slabs); then slab 0's
-  // fragments are read into set 0.
+  // Prologue.  DIRECT: slabs 0-3 copied to stages 0-3, then slab 0 waited
+  // for (and fixed if it reaches past K).  Otherwise slab 0 written to stage
+  // 0 and slab 1 to stage 1, slab 2 loaded into staging set 0 (the stream has
+  // at least two slabs).  Then slab 0's fragments are read into set 0.
+  if constexpr (DIRECT) {
+    for (int st = 0; st < C::kStages; ++st) {
 #pragma unroll
-  for (int u = 0; u < C::kLoads; ++u) load_one(0, u);
-  advance_load();
+      for (int u = 0; u < C::kLoads; ++u) copy_one(st, u);
+      advance_load();
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(3 * C::kLoads));
+    if (C::BK > p.K) fix_tail(0, 0);
+  } else {
 #pragma unroll
-  for (int u = 0; u < C::kLoads; ++u) load_one(1, u);
-  advance_load();
+    for (int u = 0; u < C::kLoads; ++u) load_one(0, u);
+    advance_load();
 #pragma unroll
-  for (int u = 0; u < C::kLoads; ++u) write_one(0, 0, u);
-  if (++wt == nk) wt = 0;
+    for (int u = 0; u < C::kLoads; ++u) load_one(1, u);
+    advance_load();
 #pragma unroll
-  for (int u = 0; u < C::kLoads; ++u) write_one(1, 1, u);
-  if (++wt == nk) wt = 0;
+    for (int u = 0; u < C::kLoads; ++u) write_one(0, 0, u);
+    if (++wt == nk) wt = 0;
 #pragma unroll
-  for (int u = 0; u < C::kLoads; ++u) load_one(0, u);
-  advance_load();
+    for (int u = 0; u < C::kLoads; ++u) write_one(1, 1, u);
+    if (++wt == nk) wt = 0;
+#pragma unroll
+    for (int u = 0; u < C::kLoads; ++u) load_one(0, u);
+    advance_load();
+  }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   asm volatile("s_barrier" ::: "memory");
 #pragma unroll
@@ -410,11 +475,11 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
     int m0, n0;
     origin(j, m0, n0);
     for (int t = 0; t < nk; t += 2) {
-      top(after_epi);
+      top(after_epi, (gs + 1) & (C::kStages - 1), t + 1);
       after_epi = false;
       slab(S0(), gs);
       ++gs;
-      top(false);
+      top(false, (gs + 1) & (C::kStages - 1), t + 2 == nk ? 0 : t + 2);
       slab(S1(), gs);
       ++gs;
     }
@@ -425,27 +490,35 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
 }
 
-template <int BN, int FMT, bool EPI>
+template <int BN, int FMT, bool EPI, bool DIRECT>
 hipError_t launch_bn(const Args16& a, int cus, hipStream_t stream) {
   const int64_t tiles = (int64_t)((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
   int64_t grid = tiles < cus ? tiles : cus;
   if (grid < 1) grid = 1;
   Args ta{a, tiles};
   void* args[] = {&ta};
-  return hipLaunchKernel((const void*)hgemm_staged_kernel<BN, FMT, EPI>, dim3((unsigned)grid),
+  return hipLaunchKernel((const void*)hgemm_staged_kernel<BN, FMT, EPI, DIRECT>, dim3((unsigned)grid),
                          dim3(256), args, 0, stream);
 }
 
 // 256 x 256 or 256 x 224 tiles, whichever takes fewer rounds of persistent
 // workgroups times tile width (5000 x 3001 on 256 CUs: 240 tiles of 256 x 256
 // in one round, against 280 of 256 x 224 in two).
-template <int FMT, bool EPI>
-hipError_t launch_fmt(const Args16& a, int cus, hipStream_t stream) {
+template <int FMT, bool EPI, bool DIRECT>
+hipError_t launch_tiles(const Args16& a, int cus, hipStream_t stream) {
   const int64_t tm = (a.M + 255) / 256;
   const int64_t r256 = (tm * ((a.N + 255) / 256) + cus - 1) / cus;
   const int64_t r224 = (tm * ((a.N + 223) / 224) + cus - 1) / cus;
-  if (r224 * 224 < r256 * 256) return launch_bn<224, FMT, EPI>(a, cus, stream);
-  return launch_bn<256, FMT, EPI>(a, cus, stream);
+  if (r224 * 224 < r256 * 256) return launch_bn<224, FMT, EPI, DIRECT>(a, cus, stream);
+  return launch_bn<256, FMT, EPI, DIRECT>(a, cus, stream);
+}
+
+// Direct copies when every row of A and B starts at a 16-byte address.
+template <int FMT, bool EPI>
+hipError_t launch_fmt(const Args16& a, int cus, hipStream_t stream) {
+  const bool direct = aligned16(a.A) && aligned16(a.B) && a.lda % 8 == 0 && a.ldb % 8 == 0;
+  return direct ? launch_tiles<FMT, EPI, true>(a, cus, stream)
+                : launch_tiles<FMT, EPI, false>(a, cus, stream);
 }
 
 }  // namespace hstaged

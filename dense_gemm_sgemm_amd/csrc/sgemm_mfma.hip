@@ -831,14 +831,16 @@ bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void
          ldb < kStreamMaxLd;
 }
 
-// The small-tile kernel: whole tiles, K a multiple of 64 up to 4096, and at
-// most a quarter as many 64 x 64 tiles as CUs (it then runs at least four
-// times as many workgroups as the 64 x 64 kernels would); 16 x 16 tiles when
-// even 32 x 32 tiles would leave CUs idle.
+// The small-tile kernel: whole tiles, K a multiple of 64, and at most a
+// quarter as many 64 x 64 tiles as CUs (it then runs at least four times as
+// many workgroups as the 64 x 64 kernels would); 16 x 16 tiles when even
+// 32 x 32 tiles would leave CUs idle.  Long K included: 512 x 512 x 16384 in
+// 144 us against 272 us on the 64 x 64 streaming tiles (256 x 256 x 16384:
+// 66 against 271 us; even at K = 4096).
 static bool f32_small32_fits(int M, int N, int K, const void* A, int64_t lda, const void* B,
                              int64_t ldb, const void* C, int64_t ldc, int cus) {
   const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
-  return M % 32 == 0 && N % 32 == 0 && K % 64 == 0 && K <= 4096 && 4 * tiles64 <= cus &&
+  return M % 32 == 0 && N % 32 == 0 && K % 64 == 0 && 4 * tiles64 <= cus &&
          aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
          ldc % 4 == 0;
 }

@@ -952,16 +952,17 @@ def test_f32_stream64_alpha_beta_padded_and_exact():
 
 
 # Products with at most a quarter as many 64 x 64 tiles as CUs (K a multiple
-# of 64, at most 4096) run on the small-tile kernel whose four waves split
-# each K chunk of up to 256 four ways, with 16 x 16 tiles while 32 x 32 ones
-# would leave CUs idle: one chunk (256^3, 64^3), a short last chunk (320 =
-# 256 + 64, 192, 1088), sixteen chunks (512 x 512 x 4096), a wide strip; the
-# 32 x 32 tiles at 512 x 512 x 4096 and 256 x 1024 x 320 (256 tiles each),
-# the 16 x 16 ones at the others.  Element by element against the oracle;
+# of 64) run on the small-tile kernel whose four waves split each K chunk of
+# up to 256 four ways, with 16 x 16 tiles while 32 x 32 ones would leave CUs
+# idle: one chunk (256^3, 64^3), a short last chunk (320 = 256 + 64, 192,
+# 1088), sixteen chunks (512 x 512 x 4096), long K (256 x 256 x 16384, 512 x
+# 256 x 8192), a wide strip; the 32 x 32 tiles at 512 x 512 x 4096 and
+# 256 x 1024 x 320 (256 tiles each), the 16 x 16 ones at the others.  Element by element against the oracle;
 # the smallest of these shapes also appear in the stream64 list above, which
 # the small-tile kernel now takes.
 SMALL32_SHAPES = [(256, 256, 256), (64, 64, 64), (128, 512, 320), (512, 512, 4096),
-                  (64, 1024, 192), (256, 128, 1088), (256, 1024, 320)]
+                  (64, 1024, 192), (256, 128, 1088), (256, 1024, 320), (256, 256, 16384),
+                  (512, 256, 8192)]
 
 
 @pytest.mark.parametrize("shape", SMALL32_SHAPES, ids=lambda s: "x".join(map(str, s)))

@@ -222,9 +222,9 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
 
 // ---------------------------------------------------------------------------
 // The streaming kernel for large fp32 products (M, N multiples of 128 with
-// at least as many 128 x 128 tiles as CUs, K a multiple of 64): one
-// persistent 512-thread workgroup per CU walks its 128 x 128 tiles as one
-// stream of 64-deep K slabs.
+// at least as many 128 x 128 tiles as CUs, K a multiple of 64; or, RAG, any
+// M, N >= 128 and K a multiple of 4): one persistent 512-thread workgroup per
+// CU walks its 128 x 128 tiles as one stream of 64-deep K slabs.
 //
 //  * waves 0-3 (one per SIMD) compute: each owns 64 x 64 of the tile, 16
 //    blocks of v_mfma_f32_16x16x4_f32 with 16 accumulators in rotation;
@@ -253,7 +253,15 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_mfma_kernel(F32Args p, int6
 //  * the barrier of slab t sits after 240 of its 256 MFMAs: before it every
 //    computing wave has read all of slab t and the copying waves have landed
 //    slab t + 1; after it they copy slab t + 2 into slab t's stage while the
-//    computing waves read the first fragments of slab t + 1.
+//    computing waves read the first fragments of slab t + 1;
+//  * RAG (the boundary rule of page 1, "第 6 章 Shared Memory & Tile",
+//    exercise 7 of section 6.9: arbitrary M, N, K): the last tile row and
+//    column are shifted back to end at M and N, so every row a copy reads
+//    exists, and store only the rows and columns no earlier tile owns; the
+//    last slab of a K that is not a multiple of 64 copies its chunks and rows
+//    past K from the last ones inside (in bounds), and the copying wave that
+//    wrote them zeroes them in LDS before the barrier that publishes the slab
+//    (whole 16-byte chunks, since K is a multiple of 4).
 namespace stream {
 constexpr int BM = 128, BN = 128, BKS = 64;
 constexpr int kStageA = BM * BKS * 4, kStageB = BKS * BN * 4;   // bytes
@@ -297,20 +305,33 @@ __device__ __forceinline__ void copy16(const char* sbase, uint32_t voff, lds_voi
 constexpr int kWaitVmLgkm0 = 0x0070;   // s_waitcnt vmcnt(0) lgkmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;     // s_waitcnt lgkmcnt(0)
 
+template <bool RAG>
 __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, int64_t tiles) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+  const int tiles_m = RAG ? (p.M + BM - 1) / BM : p.M / BM;
+  const int tiles_n = RAG ? (p.N + BN - 1) / BN : p.N / BN;
   const int64_t stride = gridDim.x;
   const int ntiles = (int)((tiles - blockIdx.x + stride - 1) / stride);
-  const int nk = p.K / BKS;
-  const int total = ntiles * nk;   // slabs of this workgroup's stream
-  auto origin = [&](int jt, int& m0, int& n0) __attribute__((always_inline)) {
+  const int nk = RAG ? (p.K + BKS - 1) / BKS : p.K / BKS;
+  const int kv = p.K - (nk - 1) * BKS;   // K values in the last slab (RAG: 4 .. 64)
+  const int total = ntiles * nk;         // slabs of this workgroup's stream
+  // Tile jt of this workgroup: origin (m0, n0) of the rows and columns it
+  // computes, and (mlo, nlo), the first it stores (RAG: the last tile row
+  // and column start at M - 128 and N - 128 and leave the rows and columns
+  // of the tile before them to it).
+  auto origin = [&](int jt, int& m0, int& n0, int& mlo, int& nlo) __attribute__((always_inline)) {
     int tm, tn;
     hgemm::map_tile<8>(blockIdx.x + (int64_t)jt * stride, tiles_m, tiles_n, tm, tn);
-    m0 = tm * BM;
-    n0 = tn * BN;
+    mlo = tm * BM;
+    nlo = tn * BN;
+    m0 = RAG && mlo > p.M - BM ? p.M - BM : mlo;
+    n0 = RAG && nlo > p.N - BN ? p.N - BN : nlo;
+  };
+  // Slab it of the stream reaches past K.
+  auto tail_slab = [&](int it) __attribute__((always_inline)) {
+    return RAG && kv < BKS && it % nk == nk - 1;
   };
 
   if (wave >= 4) {
@@ -326,23 +347,46 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
     const uint32_t offA = la + 16 * ((lane & 15) ^ ((4 * cw + (lane >> 4)) & 15));
     const uint32_t offB0 = lb + 16 * ((lane & 31) ^ (4 * ((cw >> 1) & 3)));
     const uint32_t offB1 = lb + 16 * ((lane & 31) ^ (4 * (((cw >> 1) + 2) & 3)));
+    // RAG: this lane's A chunk (the same logical chunk in every A copy of the
+    // wave) lies past K in the last slab when 4 lc >= kv; it then loads the
+    // slab's last chunk inside K instead.
+    const int lcA = (lane & 15) ^ ((4 * cw + (lane >> 4)) & 15);
+    const bool a_past = 4 * lcA >= kv;
+    const uint32_t offA_tail = a_past ? la + 16 * (kv / 4 - 1) : offA;
     auto copy_slab = [&](int it) __attribute__((always_inline)) {
-      int m0, n0;
-      origin(it / nk, m0, n0);
+      int m0, n0, mlo, nlo;
+      origin(it / nk, m0, n0, mlo, nlo);
       const int t = it % nk;
+      const bool tail = tail_slab(it);
       const char* a = (const char*)(p.A + (int64_t)m0 * p.lda + t * BKS);
       const char* b = (const char*)(p.B + (int64_t)(t * BKS) * p.ldb + n0);
       unsigned char* st = lds + (it & 1) * kStage;
+      const uint32_t oa = tail ? offA_tail : offA;
 #pragma unroll
       for (int i = 0; i < kCopies / 2; ++i) {
         const int c = cw + kCopiers * i;
-        copy16(uniform_ptr(a + (int64_t)c * 16 * p.lda), offA, (lds_void_t*)(st + c * 1024));
+        copy16(uniform_ptr(a + (int64_t)c * 16 * p.lda), oa, (lds_void_t*)(st + c * 1024));
       }
 #pragma unroll
       for (int i = 0; i < kCopies / 2; ++i) {
         const int c = cw + kCopiers * i;
-        copy16(uniform_ptr(b + (int64_t)c * 8 * p.ldb), (i & 1) ? offB1 : offB0,
+        // B rows 2 c, 2 c + 1 of the slab (in the last slab, rows kv - 2 and
+        // kv - 1 stand in for rows past K)
+        const int row = tail && 2 * c + 1 >= kv ? kv - 2 : 2 * c;
+        copy16(uniform_ptr(b + (int64_t)row * 4 * p.ldb), (i & 1) ? offB1 : offB0,
                (lds_void_t*)(st + kStageA + c * 1024));
+      }
+    };
+    // RAG: after the last slab has landed, this wave's chunks and rows past K
+    // become zeros (each lane rewrites the 16 bytes its own copies wrote).
+    auto zero_tail = [&](int it) __attribute__((always_inline)) {
+      unsigned char* st = lds + (it & 1) * kStage;
+#pragma unroll
+      for (int i = 0; i < kCopies / 2; ++i) {
+        const int c = cw + kCopiers * i;
+        if (a_past) *(f4*)(st + c * 1024 + 16 * lane) = f4{0.f, 0.f, 0.f, 0.f};
+        if (2 * c + (lane >> 5) >= kv)
+          *(f4*)(st + kStageA + c * 1024 + 16 * lane) = f4{0.f, 0.f, 0.f, 0.f};
       }
     };
     // Slab 0 before the opening barrier; then, after the barrier of slab
@@ -350,10 +394,18 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
     // used, landed before the barrier of slab t.
     copy_slab(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    if constexpr (RAG) {
+      if (tail_slab(0)) zero_tail(0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    }
     asm volatile("s_barrier" ::: "memory");
     for (int it = 0; it < total; ++it) {
       if (it + 1 < total) copy_slab(it + 1);
       __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+      if constexpr (RAG) {
+        if (it + 1 < total && tail_slab(it + 1)) zero_tail(it + 1);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      }
       asm volatile("s_barrier" ::: "memory");
     }
     return;
@@ -418,8 +470,8 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
   const float alpha = p.alpha, beta = p.beta;
   int gs = 0;
   for (int jt = 0; jt < ntiles; ++jt) {
-    int m0, n0;
-    origin(jt, m0, n0);
+    int m0, n0, mlo, nlo;
+    origin(jt, m0, n0, mlo, nlo);
     for (int t = 0; t < nk; ++t, ++gs) slab(gs);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -427,14 +479,24 @@ __global__ __launch_bounds__(kThreads, 2) void sgemm_stream_kernel(F32Args p, in
       for (int j = 0; j < 4; ++j) {
         const int m = m0 + wm + 16 * i + r, n = n0 + wn + 16 * j + 4 * g;
         float* c = p.C + (int64_t)m * p.ldc + n;
-        {
-          f4 out = alpha * acc[i][j];
+        const f4 out0 = alpha * acc[i][j];
+        if (!RAG || (m >= mlo && n >= nlo)) {
+          f4 out = out0;
           if (beta != 0.f) {
             const f4 old = *(const f4*)c;
 #pragma unroll
             for (int v = 0; v < 4; ++v) out[v] = fmaf(beta, old[v], out[v]);
           }
           *(f4*)c = out;
+        } else if (m >= mlo && n + 4 > nlo) {
+          // a quad that straddles the first column this tile owns
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (n + v < nlo) continue;
+            float o = out0[v];
+            if (beta != 0.f) o = fmaf(beta, c[v], o);
+            c[v] = o;
+          }
         }
         acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
       }
@@ -807,7 +869,7 @@ hipError_t launch_stream(const F32Args& a, int cus, hipStream_t stream) {
   F32Args p = a;
   int64_t t = tiles;
   void* args[] = {&p, &t};
-  const void* kernel = big ? (const void*)stream::sgemm_stream_kernel
+  const void* kernel = big ? (const void*)stream::sgemm_stream_kernel<false>
                            : (const void*)stream64::sgemm_stream64_kernel;
   static_assert(stream::kThreads == stream64::kThreads, "one block size");
   return hipLaunchKernel(kernel, dim3((unsigned)grid), dim3(stream::kThreads), args, 0, stream);
@@ -864,7 +926,27 @@ hipError_t launch_f32_mfma(const F32Args& a, int cus, hipStream_t stream) {
   return launch_tiled<64, 64, false>(a, stream);
 }
 
+// The streaming kernel's ragged form (RAG): M, N at least 128 with at least
+// as many 128 x 128 tiles as CUs, K a multiple of 4, the fast path's
+// alignment.
+bool f32_stream_ragged_fits(int M, int N, int K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, const void* C, int64_t ldc, int cus) {
+  return M >= 128 && N >= 128 && K >= 4 && K % 4 == 0 && !small_tiles(M, N, cus) &&
+         aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
+         ldc % 4 == 0 && lda < kStreamMaxLd && ldb < kStreamMaxLd;
+}
+
 hipError_t launch_f32_edge(const F32Args& a, int cus, hipStream_t stream) {
+  if (f32_stream_ragged_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, cus)) {
+    const int64_t tiles = (int64_t)((a.M + stream::BM - 1) / stream::BM) *
+                          ((a.N + stream::BN - 1) / stream::BN);
+    const int64_t grid = tiles < cus ? tiles : cus;
+    F32Args p = a;
+    int64_t t = tiles;
+    void* args[] = {&p, &t};
+    return hipLaunchKernel((const void*)stream::sgemm_stream_kernel<true>, dim3((unsigned)grid),
+                           dim3(stream::kThreads), args, 0, stream);
+  }
   if (small_tiles(a.M, a.N, cus)) return launch_tiled<64, 64, true>(a, stream);
   return launch_tiled<128, 128, true>(a, stream);
 }

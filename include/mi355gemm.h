@@ -309,6 +309,8 @@ enum {
   GEMM_PATH_F32_SCALE = 1,      /* K == 0 or alpha == 0: C = beta * C             */
   GEMM_PATH_F32_GENERAL = 2,    /* v_mfma f32 tiles with predicated loads/stores: */
                                 /*   any shape, leading dimension and alignment   */
+                                /*   (16-byte aligned rows, K % 4 == 0, M, N >=   */
+                                /*   128: streaming tiles with shifted edges)     */
   GEMM_PATH_F32_MFMA = 3,       /* v_mfma f32 full tiles, 16-byte aligned rows    */
   GEMM_PATH_F16_ZERO = 4,       /* K == 0: C = 0                                  */
   GEMM_PATH_F16_GENERAL = 5,    /* v_mfma f16 tiles with predicated loads/stores: */

@@ -1027,6 +1027,48 @@ def test_f32_ragged_large(shape):
     assert np.all(got[outside] == 7.0)
 
 
+# Large ragged fp32 products with 16-byte aligned rows (K a multiple of 4,
+# at least as many 128 x 128 tiles as CUs) run on the streaming kernel's
+# ragged form: the last tile row and column shifted back to end at M and N,
+# the last slab's chunks and rows past K zeroed in LDS.  Tails of 40 and 56
+# (2000 x 2100 x 1000, 3000^3), K below one slab (36: the only slab is the
+# tail), no tail (4000 x 4096 x 4096, ragged M only), and leading dimensions
+# of 2052 for N = 2050, so that the shifted last column of tiles starts 8
+# bytes past a 16-byte boundary; every output against the oracle, alpha /
+# beta with C read, then beta = 0 over NaN, C outside M x N untouched.
+STREAM_RAGGED32_SHAPES = [(2000, 2100, 1000), (3000, 3000, 3000), (2100, 2048, 36),
+                          (4000, 4096, 4096)]
+
+
+@pytest.mark.parametrize("shape", STREAM_RAGGED32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_stream_ragged(shape):
+    M, N, K = shape
+    A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
+    got = gpu_f32(A, B, 0.75, 0.5, C.copy(), expect="f32_general")
+    ref = oracle.gemm_f32(A, B, 0.75, 0.5, C)
+    f32_check(got, ref, f32_tolerance(K, 1.0, 1.0, 0.75, 0.5, 1.0))
+    got0 = gpu_f32(A, B, 1.0, 0.0, expect="f32_general")     # C prefilled with NaN
+    f32_check(got0, oracle.gemm_f32(A, B), f32_tolerance(K, 1.0, 1.0))
+
+
+def test_f32_stream_ragged_padded_rows():
+    M, N, K, ld = 2048, 2050, 1000, 2052
+    A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
+    bufB = torch.zeros(K, ld, device=DEV)
+    dB = bufB[:, :N]
+    dB.copy_(dev(B))
+    bufC = torch.full((M, ld), 7.0, device=DEV)
+    dC = bufC[:, :N]
+    dC.copy_(dev(C))
+    assert dg.f32_path(dev(A), dB, dC, 0.75, 0.5) == "f32_general"
+    dg.gemm_f32(dev(A), dB, dC, 0.75, 0.5)
+    torch.cuda.synchronize()
+    got = bufC.cpu().numpy()
+    f32_check(got[:, :N], oracle.gemm_f32(A, B, 0.75, 0.5, C),
+              f32_tolerance(K, 1.0, 1.0, 0.75, 0.5, 1.0))
+    assert np.all(got[:, N:] == 7.0)
+
+
 def test_f32_unaligned_operand_and_c_exact():
     """A starting one float into its buffer, then aligned operands with an
     unaligned C; small integers make both results exact."""

@@ -186,6 +186,10 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
   if (f16_mfma_fits(M, N, K, a_read, pl.lda, b_read, pl.ldb, C, ldc) &&
       (!epi || f16_epi_fits(bias, res, ldr)))
     return done(GEMM_PATH_F16_MFMA);
+  // Large products that are not whole tiles but whose A and B rows start at
+  // 16-byte addresses (K % 8 == 0): the full-tile kernels' ragged form.
+  if (large_product(M, N, K) && f16_ragged_fits(M, N, K, a_read, pl.lda, b_read, pl.ldb))
+    return done(GEMM_PATH_F16_MFMA);
   // Large products the full tiles cannot take (ragged, unaligned rows, odd
   // leading dimensions, C or the write-back operands unaligned): the
   // register-staged wide tiles read the operands (or the copies) in place.

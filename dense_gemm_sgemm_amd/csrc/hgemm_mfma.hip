@@ -81,7 +81,35 @@ hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
   }
 }
 
+// Products that are not whole tiles (RAG instances): 256 x 256 or 256 x 224
+// tiles, whichever takes fewer rounds times tile width, over ceil(M / 256)
+// tile rows.
+template <bool EPI, int FMT>
+hipError_t launch_ragged(const Args16& a, int cus, hipStream_t stream) {
+  const int64_t tm = (a.M + 255) / 256;
+  const int64_t r256 = (tm * ((a.N + 255) / 256) + cus - 1) / cus;
+  const int64_t r224 = (tm * ((a.N + 223) / 224) + cus - 1) / cus;
+  if (r224 * 224 < r256 * 256)
+    return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, true>(a, cus, stream);
+  return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false, true>(a, cus, stream);
+}
+
+bool f16_ragged_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb) {
+  constexpr int64_t kMaxLd = int64_t(1) << 28;
+  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  return M >= 256 && N >= 256 && K > BK && K % 8 == 0 && aligned16(A) && aligned16(B) &&
+         lda % 8 == 0 && ldb % 8 == 0 && lda < kMaxLd && ldb < kMaxLd && tiles >= kRaggedTiles;
+}
+
 hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {
+  if (!f16_mfma_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc) ||
+      (epi && !hgemm::epi_fits(a.bias, a.res, a.ldr))) {
+    if (a.fmt == kFmtBF16)
+      return epi ? launch_ragged<true, kFmtBF16>(a, cus, stream)
+                 : launch_ragged<false, kFmtBF16>(a, cus, stream);
+    return epi ? launch_ragged<true, kFmtF16>(a, cus, stream)
+               : launch_ragged<false, kFmtF16>(a, cus, stream);
+  }
   if (a.fmt == kFmtBF16)
     return epi ? launch_shape<true, kFmtBF16>(a, cus, stream)
                : launch_shape<false, kFmtBF16>(a, cus, stream);

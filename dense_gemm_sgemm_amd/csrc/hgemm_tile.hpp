@@ -41,6 +41,15 @@
 //
 // Preconditions (checked by the host): M % BM == N % BN == K % BK == 0,
 // 16-byte aligned A, B, C, leading dimensions that are multiples of 8.
+//
+// RAG instances take any M >= BM, N >= BN and K > BK with K % 8 == 0, A and
+// B rows at 16-byte addresses and C at any 2-byte address (the boundary rule
+// of page 1, "第 6 章 Shared Memory & Tile", exercise 7 of section 6.9): the
+// last tile row and column are shifted back to end at M and N -- every row a
+// copy reads exists -- and store only the rows and columns no earlier tile
+// owns; the last slab of K copies its chunks past K from the last chunk
+// inside, and the copying wave that wrote them zeroes them in LDS after its
+// wait and before the barrier that publishes the slab.
 #pragma once
 
 #include <type_traits>
@@ -150,9 +159,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // and store each item's fp32 partial tile to the split-K workspace instead of
 // writing C.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
-          int FMT, bool SPLIT = false>
+          int FMT, bool SPLIT = false, bool RAG = false>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVES_M * WAVES_N))
 void hgemm_nt_kernel(TileArgs ta) {
+  static_assert(!(RAG && SPLIT), "ragged tiles store C");
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr int kChunks = C::kChunks;
   const Args16& p = ta.p;
@@ -167,12 +177,18 @@ void hgemm_nt_kernel(TileArgs ta) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wm = (wave / WAVES_N) * C::WM, wn = (wave % WAVES_N) * C::WN;
-  const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+  const int tiles_m = RAG ? (p.M + BM - 1) / BM : p.M / BM;
+  const int tiles_n = RAG ? (p.N + BN - 1) / BN : p.N / BN;
+  // K values in the last slab of a tile (RAG: 8 .. 64)
+  const int kv = RAG ? p.K - ((p.K + BK - 1) / BK - 1) * BK : BK;
   const int64_t stride = gridDim.x;
   const int ntiles = (int)((ta.tiles - blockIdx.x + stride - 1) / stride);
   // Work item j of this workgroup: tile origin (m0, n0), first K slab kb and
   // split-K range sp (both 0 without SPLIT).
-  auto tile_origin = [&](int j, int& m0, int& n0, int& kb, int& sp) __attribute__((always_inline)) {
+  // (m0, n0): the rows and columns the tile computes; (mlo, nlo): the first
+  // it stores (RAG: the last tile row and column start at M - BM, N - BN).
+  auto tile_origin = [&](int j, int& m0, int& n0, int& kb, int& sp, int& mlo, int& nlo)
+                         __attribute__((always_inline)) {
     int64_t item = blockIdx.x + j * stride;
     sp = 0;
     if constexpr (SPLIT) {
@@ -183,8 +199,10 @@ void hgemm_nt_kernel(TileArgs ta) {
     kb = sp * (SPLIT ? p.sk.per : 0);
     int tm, tn;
     map_tile<GM>(item, tiles_m, tiles_n, tm, tn);
-    m0 = tm * BM;
-    n0 = tn * BN;
+    mlo = tm * BM;
+    nlo = tn * BN;
+    m0 = RAG && mlo > p.M - BM ? p.M - BM : mlo;
+    n0 = RAG && nlo > p.N - BN ? p.N - BN : nlo;
   };
 
   // Copy assignment: copy instruction c of a slab fills rows [8 c, 8 c + 8);
@@ -204,6 +222,12 @@ void hgemm_nt_kernel(TileArgs ta) {
   const int lane_chunk = (lane % kChunks) ^ ((4 * (cwp & 1) + (lane >> 4)) & 7);
   const uint32_t offA = (uint32_t)(lane_row * p.lda + 8 * lane_chunk) * 2;   // bytes
   const uint32_t offB = (uint32_t)(lane_row * p.ldb + 8 * lane_chunk) * 2;
+  // RAG, the last slab of K: a lane whose chunk lies past K loads the last
+  // chunk inside K instead (zeroed once it has landed).
+  const bool chunk_past = RAG && 8 * lane_chunk >= kv;
+  const int tail_chunk = chunk_past ? kv / 8 - 1 : lane_chunk;
+  const uint32_t offA_tail = (uint32_t)(lane_row * p.lda + 8 * tail_chunk) * 2;
+  const uint32_t offB_tail = (uint32_t)(lane_row * p.ldb + 8 * tail_chunk) * 2;
   const int64_t copy_strideA = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.lda * 2;
   const int64_t copy_strideB = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.ldb * 2;
   const int64_t firstA = (int64_t)cwp * C::kRowsPerCopy * p.lda * 2;
@@ -216,25 +240,28 @@ void hgemm_nt_kernel(TileArgs ta) {
     const char* a;
     const char* b;
     unsigned char* l;
+    uint32_t oa, ob;   // this lane's offsets (RAG: the clamped ones in a tile's last slab)
   };
-  auto slab_base = [&](int stage, int m0, int n0, int t) __attribute__((always_inline)) {
+  auto slab_base = [&](int stage, int m0, int n0, int t, bool tail) __attribute__((always_inline)) {
     CopyBase cb;
     cb.l = lds + stage * C::kStageBytes;
     cb.a = (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
     cb.b = (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
+    cb.oa = RAG && tail ? offA_tail : offA;
+    cb.ob = RAG && tail ? offB_tail : offB;
     return cb;
   };
   auto copy_one = [&](const CopyBase& cb, int c) __attribute__((always_inline)) {
     if (c < C::kPerWaveA) {
       if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(cb.a + c * copy_strideA + offA),
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(cb.a + c * copy_strideA + cb.oa),
                                          (lds_void_t*)(cb.l + (c * C::kCopyWaves + cw) * 1024),
                                          16, 0, 0);
     } else {
       const int i = c - C::kPerWaveA;
       if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB)
         __builtin_amdgcn_global_load_lds(
-            (gbl_void_t*)(cb.b + i * copy_strideB + offB),
+            (gbl_void_t*)(cb.b + i * copy_strideB + cb.ob),
             (lds_void_t*)(cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024), 16, 0, 0);
     }
   };
@@ -245,6 +272,24 @@ void hgemm_nt_kernel(TileArgs ta) {
   // access is moved across it.
   auto wait_and_sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // RAG: the same, and before the barrier this wave zeroes its chunks past K
+  // of the slab in `stage` when that slab is the last of its tile.
+  auto wait_zero_sync = [&](bool zero, int stage) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+    if (zero && copier && chunk_past) {
+      unsigned char* l = lds + stage * C::kStageBytes;
+#pragma unroll
+      for (int c = 0; c < C::kPerWaveA; ++c)
+        if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA)
+          *(h8*)(l + (c * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
+#pragma unroll
+      for (int i = 0; i < C::kPerWaveB; ++i)
+        if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB)
+          *(h8*)(l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("s_barrier" ::: "memory");
   };
 
@@ -309,7 +354,9 @@ void hgemm_nt_kernel(TileArgs ta) {
   // activation chosen once per quad.  The accumulator is never -0 (its sum
   // starts at +0), so adding a zero for an absent operand changes nothing.
   unsigned char* stage_out = lds + 2 * C::kStageBytes + wave * (kOutRows * C::kOutRowBytes);
-  auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
+  auto epilogue = [&](int m0, int n0, int mlo, int nlo) __attribute__((always_inline)) {
+    (void)mlo;
+    (void)nlo;
     const int cc = lane & 15;
     h4 bq[C::kBlocksN], rq[C::kBlocksM][C::kBlocksN];
     if constexpr (EPI) {
@@ -360,7 +407,20 @@ void hgemm_nt_kernel(TileArgs ta) {
       for (int q = 0; q < kOutRows / 4; ++q) {
         const int R = 4 * q + (lane >> 4);
         const h8 v = *(const h8*)(stage_out + R * C::kOutRowBytes + 16 * (cc ^ R));
-        if (C::WN == 128 || cc < C::WN / 8) {
+        if constexpr (RAG) {
+          // only rows and columns no earlier tile owns; C at any 2-byte address
+          const int m = m0 + wm + 16 * i + R, n = n0 + wn + 8 * cc;
+          if ((C::WN == 128 || cc < C::WN / 8) && m >= mlo && n + 8 > nlo) {
+            half_t* dst = p.C + (int64_t)m * p.ldc + n;
+            if (n >= nlo) {
+              __builtin_memcpy(dst, &v, 16);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (n + e >= nlo) dst[e] = v[e];
+            }
+          }
+        } else if (C::WN == 128 || cc < C::WN / 8) {
           h8* dst = (h8*)(p.C + (int64_t)(m0 + wm + 16 * i + R) * p.ldc + n0 + wn + 8 * cc);
           if (OPT & 1) {
             __builtin_nontemporal_store(v, dst);   // OPT bit 0: streaming stores of C
@@ -408,18 +468,25 @@ void hgemm_nt_kernel(TileArgs ta) {
   constexpr int kReads = C::kBlocksM + C::kBlocksN;
   constexpr int kCopies = C::kPerWaveA + C::kPerWaveB;
   static_assert(kReads <= kMfma && kCopies <= kMfma, "interleave pattern");
-  const int nk = SPLIT ? p.sk.per : p.K / BK;   // slabs per work item
+  const int nk = SPLIT ? p.sk.per : RAG ? (p.K + BK - 1) / BK : p.K / BK;   // slabs per work item
   // The copy target runs two slabs ahead of the compute: slab tc of the tile
   // `ahead` tiles after the current one (origins o[0..2] are refreshed once
   // per tile, outside the MFMA loop).  Past the end of the stream it stays on
   // the last slab of the last tile.
   int tc = 0, ahead = 0, cur = 0;
   int om[3], on[3], ok[3], os[3];
+  int mlo0 = 0, nlo0 = 0;   // the current tile's first stored row and column
   auto refresh_origins = [&](int j) __attribute__((always_inline)) {
     cur = j;
 #pragma unroll
-    for (int d = 0; d < 3; ++d)
-      tile_origin(j + d < ntiles ? j + d : ntiles - 1, om[d], on[d], ok[d], os[d]);
+    for (int d = 0; d < 3; ++d) {
+      int mlo, nlo;
+      tile_origin(j + d < ntiles ? j + d : ntiles - 1, om[d], on[d], ok[d], os[d], mlo, nlo);
+      if (d == 0) {
+        mlo0 = mlo;
+        nlo0 = nlo;
+      }
+    }
   };
   refresh_origins(0);
   auto advance_copy = [&]() __attribute__((always_inline)) {
@@ -435,14 +502,20 @@ void hgemm_nt_kernel(TileArgs ta) {
     const int m0 = d == 0 ? om[0] : d == 1 ? om[1] : om[2];
     const int n0 = d == 0 ? on[0] : d == 1 ? on[1] : on[2];
     const int kb = d == 0 ? ok[0] : d == 1 ? ok[1] : ok[2];
-    return slab_base(stage, m0, n0, kb + (past ? nk - 1 : tc));
+    const int t = past ? nk - 1 : tc;
+    return slab_base(stage, m0, n0, kb + t, RAG && kv < BK && t == nk - 1);
   };
   auto copy_next = [&](int stage) __attribute__((always_inline)) {
     const CopyBase cb = next_base(stage);
 #pragma unroll
     for (int c = 0; c < kCopies; ++c) copy_one(cb, c);
   };
-  auto slab = [&](int gs, auto next, auto is_copier) __attribute__((always_inline)) {
+  // zero_next (RAG): the next slab is the last of its tile and reaches past K.
+  auto slab = [&](int gs, auto next, auto is_copier, bool zero_next) __attribute__((always_inline)) {
+    auto sync = [&]() __attribute__((always_inline)) {
+      if constexpr (RAG) wait_zero_sync(zero_next, (gs + 1) & 1);
+      else wait_and_sync();
+    };
     constexpr bool kCp = decltype(is_copier)::value;
     constexpr bool kNext = decltype(next)::value;
     CopyBase cb{};
@@ -465,7 +538,7 @@ void hgemm_nt_kernel(TileArgs ta) {
       static_for<2 * kMfma>([&](auto qc) __attribute__((always_inline)) {
         constexpr int q = decltype(qc)::value;
         if constexpr (q == kB) {
-          wait_and_sync();
+          sync();
           __builtin_amdgcn_sched_barrier(0);
         }
         constexpr int step = q / kMfma, qq = q % kMfma, j = qq / MB, i = qq % MB;
@@ -508,7 +581,7 @@ void hgemm_nt_kernel(TileArgs ta) {
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
     __builtin_amdgcn_sched_barrier(0);
-    wait_and_sync();
+    sync();
     __builtin_amdgcn_sched_barrier(0);
     // Second half: step 1 of slab gs, with the copy of slab gs + 2 and the
     // loads of slab gs + 1's step 0.
@@ -552,19 +625,22 @@ void hgemm_nt_kernel(TileArgs ta) {
   int gs = 0;
   for (int j = 0; j < ntiles; ++j) {
     const int m0 = om[0], n0 = on[0], sp = os[0];
+    // RAG: slab nk - 1 reaches past K when kv < BK; it is the next slab of
+    // slab nk - 2 (nk >= 2: K > BK).  The next tile's first slab never is.
+    const int zt = RAG && kv < BK ? nk - 2 : -1;
     if (copies) {
-      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), yes());
-      slab(gs, no(), yes());
+      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), yes(), t == zt);
+      slab(gs, no(), yes(), false);
     } else {
-      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), no());
-      slab(gs, no(), no());
+      for (int t = 0; t + 1 < nk; ++t, ++gs) slab(gs, yes(), no(), t == zt);
+      slab(gs, no(), no(), false);
     }
     ++gs;
     if constexpr (SPLIT) {
       epilogue_partial(m0, n0, sp);
     } else {
       (void)sp;
-      epilogue(m0, n0);
+      epilogue(m0, n0, mlo0, nlo0);
     }
     zero_acc();
     --ahead;
@@ -577,10 +653,12 @@ void hgemm_nt_kernel(TileArgs ta) {
 // PERSISTENT: at most `slots` workgroups (as many as the GPU runs at once),
 // each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
-          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false>
+          bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false,
+          bool RAG = false>
 hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
-  const int64_t tiles = (int64_t)(a.M / BM) * (a.N / BN) * (SPLIT ? a.sk.splits : 1);
+  const int64_t tiles = RAG ? (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN)
+                            : (int64_t)(a.M / BM) * (a.N / BN) * (SPLIT ? a.sk.splits : 1);
   const int64_t max_grid = int64_t(1) << 20;
   int64_t grid = PERSISTENT ? (tiles < slots ? tiles : slots) : (tiles < max_grid ? tiles : max_grid);
   if (grid < 1) grid = 1;
@@ -588,7 +666,7 @@ hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   void* args[] = {&ta};
   return hipLaunchKernel(
       (const void*)
-          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT>,
+          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT, RAG>,
       dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 

@@ -44,9 +44,19 @@ def expected_f16_path(mode, M, N, K):
                             (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
     if fast:
         return "f16_mfma"
+    large = M * N * K >= 1 << 30
+    if large and ragged_fits(M, N, K):
+        return "f16_mfma"
     # the register-staged wide tiles take large products (from 2^30
     # multiply-adds, K at least 8) that the full tiles cannot read in place
-    return "f16_staged" if M * N * K >= 1 << 30 and K >= 8 else "f16_general"
+    return "f16_staged" if large and K >= 8 else "f16_general"
+
+
+def ragged_fits(M, N, K):
+    """The full tiles' ragged form (contiguous operands: rows of K elements):
+    M, N >= 256, K > 64 with K % 8 == 0, at least 256 tiles of 256 x 256."""
+    return (M >= 256 and N >= 256 and K > 64 and K % 8 == 0 and
+            -(-M // 256) * -(-N // 256) >= 256)
 
 
 def expected_ex_path(M, N, K, op_a, op_b):
@@ -63,5 +73,7 @@ def expected_ex_path(M, N, K, op_a, op_b):
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
     if fast:
+        return "f16_mfma"
+    if large and ragged_fits(M, N, K):
         return "f16_mfma"
     return "f16_staged" if large else "f16_general"

@@ -128,10 +128,16 @@ def test_fused_call_validation_and_paths(lib, monkeypatch):
     assert f16ex(lib, 0, 8, 8, A=0, B=0, C=0) == 0
     assert f16ex(lib, 5376, 5376, 2048) == F16_MFMA
     assert f16ex(lib, 5376, 5376, 2048, bias=0, res=0, act=2) == F16_MFMA
-    # bias 2-byte aligned, residual rows unaligned: the register-staged wide
-    # tiles (element reads of bias and residual), from 2^30 multiply-adds on
-    assert f16ex(lib, 5376, 5376, 2048, bias=ALIGNED + 2) == F16_STAGED
-    assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_STAGED
+    # bias 2-byte aligned, residual rows unaligned: the full tiles' ragged form
+    # (any alignment of C and the write-back operands) from 256 tiles of
+    # 256 x 256, the register-staged wide tiles below that (from 2^30
+    # multiply-adds)
+    assert f16ex(lib, 5376, 5376, 2048, bias=ALIGNED + 2) == F16_MFMA
+    assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_MFMA
+    assert f16ex(lib, 2048, 4096, 2048, bias=ALIGNED + 2) == F16_STAGED
+    assert f16ex(lib, 4100, 4200, 1000) == F16_MFMA                     # ragged, rows aligned
+    assert f16ex(lib, 4100, 4200, 1001) == F16_STAGED                   # rows 2-byte aligned
+    assert f16ex(lib, 3000, 3000, 3000) == F16_STAGED                   # 144 tiles
     assert f16ex(lib, 256, 256, 64, bias=ALIGNED + 2) == F16_GENERAL     # too small
     assert f16ex(lib, 256, 224, 64, bias=ALIGNED + 2) == F16_GENERAL
     assert f16ex(lib, 5376, 5376, 2048, ldr=5380) == F16_MFMA
@@ -165,10 +171,13 @@ def test_path_selection(lib, monkeypatch):
     assert f32(lib, 4096, 4096, 4096, lda=1 << 28) == F32_MFMA      # register-staged tiles
     assert f32(lib, 256, 256, 256, lda=258) == F32_GENERAL
     assert f16(lib, 5376, 5376, 2048) == F16_MFMA
-    # ragged or unaligned and large: copies where needed, masked full tiles
+    # ragged or unaligned and large: the full tiles' ragged form where A and
+    # B rows start at 16-byte addresses (C anywhere) and there are 256 tiles
+    # of 256 x 256, the register-staged wide tiles otherwise
     assert f16(lib, 5000, 3001, 1537) == F16_STAGED
     assert f16(lib, 5376, 5376, 2048, ldb=2052) == F16_STAGED
-    assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_STAGED
+    assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_MFMA
+    assert f16(lib, 4096, 4104, 2048) == F16_MFMA and f16(lib, 6000, 6000, 64) == F16_STAGED  # K > 64
     assert f16(lib, 1024, 1024, 1025) == F16_STAGED and f16(lib, 1024, 1024, 1000) == F16_GENERAL
     assert f16(lib, 1000, 1000, 1000) == F16_GENERAL                    # below 2^30 multiply-adds
     assert f16(lib, 128, 128, 64, C=ALIGNED + 2) == F16_GENERAL         # too small for wide tiles

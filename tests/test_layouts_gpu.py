@@ -288,3 +288,30 @@ def test_gemv_kmajor_weight(fmt, M, N, K, op_a, op_b):
     r = check16(got, ref, sab, fmt)
     print("[gemv K-major %dx%dx%d %s%s %s] max %.2f ulp" % (M, N, K, op_a, op_b, fmt, r["max_ulps"]),
           flush=True)
+
+
+# Large ragged products whose copies (or operands) have rows at 16-byte
+# addresses run on the full-tile kernels' ragged form (K % 8 == 0, at least
+# 256 tiles of 256 x 256): NT in place, NN and TN on the transposed copies,
+# bf16 as well as fp16, with the fused write-back in NT.
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout", [("n", "t"), ("n", "n"), ("t", "n")], ids=lambda l: "".join(l))
+def test_layouts_ragged_full_tiles(layout, fmt):
+    M, N, K = 4100, 4104, 520
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, expect="f16_mfma")
+    ref, sab = reference(A, B, op_a, op_b, fmt)
+    check16(got, ref, sab, fmt)
+    if layout != ("n", "t"):
+        return
+    rng = np.random.default_rng(44)
+    b = rng.normal(0, 1.5, N)
+    r = rng.normal(0, 2.0, (M, N))
+    bias = b.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(b)
+    res = r.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(r)
+    got = run_ex(A, B, op_a, op_b, fmt, M, N, bias, "silu", res, expect="f16_mfma")
+    ref, sab = reference(A, B, op_a, op_b, fmt, bias, "silu", res)
+    dec = oracle.half_to_double if fmt == "f16" else oracle.bf16_to_double
+    check16(got, ref, sab, fmt, np.abs(dec(bias))[None, :], np.abs(dec(res)), fused=True)

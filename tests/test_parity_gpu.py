@@ -734,6 +734,53 @@ def test_f16_staged_shapes(shape, path_mode):
     f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
 
 
+# Large products that are not whole tiles but whose rows start at 16-byte
+# addresses (K % 8 == 0, at least 256 tiles of 256 x 256) run on the full-tile
+# kernels' ragged form: the last tile row and column shifted back to end at M
+# and N, the last slab's chunks past K zeroed in LDS.  Ragged M and N with 40
+# K values in the last slab (4100 x 4200 x 1000), two slabs of which the
+# second holds 8 (4000 x 4000 x 72), N ragged only and K whole slabs (4096 x
+# 4104 x 2048: 256 x 224 tiles would need 2 rounds against 2 of 256 x 256),
+# and bf16.  Every output against the oracle.
+RAGGED16_SHAPES = [(4100, 4200, 1000), (4000, 4000, 72), (4096, 4104, 2048)]
+
+
+@pytest.mark.parametrize("shape", RAGGED16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_ragged_full_tiles(shape, path_mode):
+    M, N, K = shape
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    got = gpu_f16(A, B, expect=expected_f16_path(path_mode, M, N, K))
+    f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+
+
+def test_f16_ragged_full_tiles_c_unaligned_and_fused():
+    """C one element into its buffer with an odd leading dimension (nothing
+    outside C's window changes), then the fused write-back with the bias one
+    element into its buffer (bf16 and the other layouts: test_layouts_gpu)."""
+    M, N, K = 4100, 4100, 520
+    A, B = inputs.hgemm_nt_operands(M, N, K, dist="normal")
+    bufC = torch.full((M * (N + 3) + 2,), 5.0, device=DEV, dtype=torch.float16)
+    dC = bufC[1:1 + M * (N + 3)].view(M, N + 3)[:, :N]
+    assert dg.f16_nt_path(dev(A), dev(B), dC) == "f16_mfma"
+    dg.gemm_f16_nt(dev(A), dev(B), dC)
+    torch.cuda.synchronize()
+    f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
+              oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+    full = bufC.cpu().numpy()
+    mask = np.ones(full.shape, bool)
+    idx = 1 + np.arange(M)[:, None] * (N + 3) + np.arange(N)[None, :]
+    mask[idx.ravel()] = False
+    assert np.all(full[mask] == 5.0)
+    A, B, bias, res = epi_operands(M, N, K, True, True)
+    bbuf = torch.zeros(N + 1, device=DEV, dtype=torch.float16)
+    bbuf[1:].copy_(dev(bias))
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=torch.float16)
+    assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], "silu", dev(res)) == "f16_mfma"
+    dg.gemm_f16_nt_ex(dev(A), dev(B), dC, bbuf[1:], "silu", dev(res))
+    torch.cuda.synchronize()
+    check_ex(dC.cpu().numpy(), A, B, bias, "silu", res)
+
+
 def test_f16_staged_small_integers_are_exact():
     """Small-integer operands make every partial sum exact, so the staged
     kernel (ragged M, N, K with a K tail) must equal the exact product

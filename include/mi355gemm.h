@@ -316,6 +316,9 @@ enum {
   GEMM_PATH_F16_GENERAL = 5,    /* v_mfma f16 tiles with predicated loads/stores: */
                                 /*   any shape, leading dimension and alignment   */
   GEMM_PATH_F16_MFMA = 6,       /* v_mfma f16 full tiles, 16-byte aligned rows    */
+                                /*   (large ragged products with A and B rows at  */
+                                /*   16-byte addresses and K % 8 == 0: shifted    */
+                                /*   edge tiles, C anywhere)                      */
   GEMM_PATH_F16_GEMV = 7,       /* M <= 8 or N <= 8: matrix-vector kernel that    */
                                 /*   streams the long operand once (any ld/align) */
   GEMM_PATH_F16_SPLITK = 8,     /* gemm_ex only, long K over few output tiles: K   */

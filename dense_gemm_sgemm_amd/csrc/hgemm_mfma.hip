@@ -33,12 +33,15 @@ enum TileShape { kNone, k256x256, k256x224, k128x128, k128x192 };
 // 128 x 192 -> 192 tiles, 1 round x 32768 (measured 1.19x faster than
 // 128 x 128).  A 128 x 192 tile runs alone on its CU with 4 waves: a third
 // more time per output than the 256-row tiles (tile-time 128 x 192 x 4/3).
-TileShape choose(int M, int N, int cus) {
+// RAGGED: the same over ceil(M / bm) x ceil(N / bn) tiles (the ragged form),
+// for the shapes at least one tile wide and tall.
+TileShape choose(int M, int N, int cus, bool ragged = false) {
   TileShape best = kNone;
   int64_t best_cost = 0;
   auto consider = [&](TileShape t, int bm, int bn, int slots, int64_t tile_time) {
-    if (M % bm != 0 || N % bn != 0) return;
-    const int64_t tiles = (int64_t)(M / bm) * (N / bn);
+    if (ragged ? (M < bm || N < bn) : (M % bm != 0 || N % bn != 0)) return;
+    const int64_t tiles = ragged ? (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn)
+                                 : (int64_t)(M / bm) * (N / bn);
     const int64_t cost = (tiles + slots - 1) / slots * tile_time;
     if (best == kNone || cost < best_cost) {
       best = t;
@@ -81,24 +84,30 @@ hipError_t launch_shape(const Args16& a, int cus, hipStream_t stream) {
   }
 }
 
-// Products that are not whole tiles (RAG instances): 256 x 256 or 256 x 224
-// tiles, whichever takes fewer rounds times tile width, over ceil(M / 256)
-// tile rows.
+// Products that are not whole tiles (RAG instances): the tile shape of the
+// same cost model over ceil(M / bm) x ceil(N / bn) tiles.
 template <bool EPI, int FMT>
 hipError_t launch_ragged(const Args16& a, int cus, hipStream_t stream) {
-  const int64_t tm = (a.M + 255) / 256;
-  const int64_t r256 = (tm * ((a.N + 255) / 256) + cus - 1) / cus;
-  const int64_t r224 = (tm * ((a.N + 223) / 224) + cus - 1) / cus;
-  if (r224 * 224 < r256 * 256)
-    return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, true>(a, cus, stream);
-  return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false, true>(a, cus, stream);
+  switch (choose(a.M, a.N, cus, true)) {
+    case k256x224:
+      return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, true>(a, cus,
+                                                                                      stream);
+    case k128x128:
+      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false, true>(a, 2 * cus,
+                                                                                      stream);
+    case k128x192:
+      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false, true>(a, cus,
+                                                                                      stream);
+    default:
+      return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false, true>(a, cus,
+                                                                                      stream);
+  }
 }
 
 bool f16_ragged_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb) {
   constexpr int64_t kMaxLd = int64_t(1) << 28;
-  const int64_t tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  return M >= 256 && N >= 256 && K > BK && K % 8 == 0 && aligned16(A) && aligned16(B) &&
-         lda % 8 == 0 && ldb % 8 == 0 && lda < kMaxLd && ldb < kMaxLd && tiles >= kRaggedTiles;
+  return M >= 128 && N >= 128 && K > BK && K % 8 == 0 && aligned16(A) && aligned16(B) &&
+         lda % 8 == 0 && ldb % 8 == 0 && lda < kMaxLd && ldb < kMaxLd;
 }
 
 hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {

@@ -138,11 +138,8 @@ hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipSt
 // leading dimension (below 2^23) and 2-byte alignment, no copies, no
 // workspace.
 bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb);
-// The full-tile kernels' ragged form (any M, N >= 256, K > 64 with K % 8 == 0,
-// A and B rows at 16-byte addresses, C anywhere), taken from kRaggedTiles
-// tiles of 256 x 256 (one round on 256 CUs): below that the register-staged
-// wide tiles are as fast.
-constexpr int64_t kRaggedTiles = 256;
+// The full-tile kernels' ragged form: any M, N >= 128, K > 64 with K % 8 ==
+// 0, A and B rows at 16-byte addresses, C anywhere.
 bool f16_ragged_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb);
 hipError_t launch_f16_staged(const Args16& a, bool epi, int cus, hipStream_t stream);
 // Split-K: the partial products (a.sk filled in), then the reduction.

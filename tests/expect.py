@@ -54,9 +54,8 @@ def expected_f16_path(mode, M, N, K):
 
 def ragged_fits(M, N, K):
     """The full tiles' ragged form (contiguous operands: rows of K elements):
-    M, N >= 256, K > 64 with K % 8 == 0, at least 256 tiles of 256 x 256."""
-    return (M >= 256 and N >= 256 and K > 64 and K % 8 == 0 and
-            -(-M // 256) * -(-N // 256) >= 256)
+    M, N >= 128, K > 64 with K % 8 == 0."""
+    return M >= 128 and N >= 128 and K > 64 and K % 8 == 0
 
 
 def expected_ex_path(M, N, K, op_a, op_b):

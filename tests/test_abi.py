@@ -129,15 +129,16 @@ def test_fused_call_validation_and_paths(lib, monkeypatch):
     assert f16ex(lib, 5376, 5376, 2048) == F16_MFMA
     assert f16ex(lib, 5376, 5376, 2048, bias=0, res=0, act=2) == F16_MFMA
     # bias 2-byte aligned, residual rows unaligned: the full tiles' ragged form
-    # (any alignment of C and the write-back operands) from 256 tiles of
-    # 256 x 256, the register-staged wide tiles below that (from 2^30
-    # multiply-adds)
+    # (any alignment of C and the write-back operands), from 2^30
+    # multiply-adds; rows of A or B at 2-byte addresses, K % 8 != 0, K <= 64
+    # or M or N below 128: the register-staged wide tiles
     assert f16ex(lib, 5376, 5376, 2048, bias=ALIGNED + 2) == F16_MFMA
     assert f16ex(lib, 5376, 5376, 2048, ldr=5378) == F16_MFMA
-    assert f16ex(lib, 2048, 4096, 2048, bias=ALIGNED + 2) == F16_STAGED
+    assert f16ex(lib, 2048, 4096, 2048, bias=ALIGNED + 2) == F16_MFMA
     assert f16ex(lib, 4100, 4200, 1000) == F16_MFMA                     # ragged, rows aligned
     assert f16ex(lib, 4100, 4200, 1001) == F16_STAGED                   # rows 2-byte aligned
-    assert f16ex(lib, 3000, 3000, 3000) == F16_STAGED                   # 144 tiles
+    assert f16ex(lib, 3000, 3000, 3000) == F16_MFMA
+    assert f16ex(lib, 100, 30000, 1000) == F16_STAGED                   # M < 128
     assert f16ex(lib, 256, 256, 64, bias=ALIGNED + 2) == F16_GENERAL     # too small
     assert f16ex(lib, 256, 224, 64, bias=ALIGNED + 2) == F16_GENERAL
     assert f16ex(lib, 5376, 5376, 2048, ldr=5380) == F16_MFMA
@@ -178,6 +179,7 @@ def test_path_selection(lib, monkeypatch):
     assert f16(lib, 5376, 5376, 2048, ldb=2052) == F16_STAGED
     assert f16(lib, 5376, 5376, 2048, C=ALIGNED + 8) == F16_MFMA
     assert f16(lib, 4096, 4104, 2048) == F16_MFMA and f16(lib, 6000, 6000, 64) == F16_STAGED  # K > 64
+    assert f16(lib, 1500, 1500, 4096) == F16_MFMA and f16(lib, 1500, 1500, 4100) == F16_STAGED
     assert f16(lib, 1024, 1024, 1025) == F16_STAGED and f16(lib, 1024, 1024, 1000) == F16_GENERAL
     assert f16(lib, 1000, 1000, 1000) == F16_GENERAL                    # below 2^30 multiply-adds
     assert f16(lib, 128, 128, 64, C=ALIGNED + 2) == F16_GENERAL         # too small for wide tiles

@@ -134,7 +134,8 @@ def test_layouts_fused(shape, layout, fmt, act, use_bias, use_res):
 
 
 # Large ragged products in the other layouts: the K-major operands are copied
-# transposed (rows of round8(K)) and the register-staged wide tiles run on the
+# transposed (rows of round8(K)) and the register-staged wide tiles (K % 8 !=
+# 0, or N below 128) or the full tiles' ragged form (K % 8 == 0) run on the
 # copies -- ragged M and N at several residues of 8 (1030, 1100, 1001, 1023,
 # 2049), K tails of 9, 23 and 4 elements and a slab wholly past K (777, 1111,
 # 1100), a 256 x 224 tile choice (N = 3001), and an N of 9 for a K-major B.
@@ -152,7 +153,7 @@ def test_layouts_staged_on_copies(shape, layout, fmt):
     A, B = inputs.operands16(sa, sb, fmt)
     dA, dB = to_dev(A, fmt), to_dev(B, fmt)
     dC = torch.full((M, N), float("nan"), device=DEV, dtype=dtype_of(fmt))
-    assert dg.ex_path(dA, dB, dC, op_a, op_b) == "f16_staged"
+    assert dg.ex_path(dA, dB, dC, op_a, op_b) == expected_ex_path(M, N, K, op_a, op_b)
     assert dg.ex_workspace_bytes(dA, dB, dC, op_a, op_b) > 0
     dg.gemm_ex(dA, dB, dC, op_a, op_b)
     torch.cuda.synchronize()

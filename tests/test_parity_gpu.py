@@ -716,14 +716,15 @@ def test_workload_hgemm_splitk():
 # (1002, 1003, 1005, 1006), and a slab wholly past K when the slab count is
 # rounded up to an even number (1025, 1111).  N = 3001 and 1000 exercise the
 # 256 x 224 tiles as well as the 256 x 256 ones.  Rows at 16-byte addresses (K
-# a multiple of 8 here) take the direct copies, whose tail slabs are fixed in
-# LDS: none (640, 896), 24 and 8 elements into the last slab (600, 1000), a
-# slab wholly past K (1056), and K below one slab (24: the first slab is the
-# tail).
+# a multiple of 8 here) and K > 64 take the full tiles' ragged form instead
+# when M and N are at least 128; the others with such rows take the direct
+# copies, whose tail slabs are fixed in LDS: K below one slab (24: the first
+# slab is the tail), M below 128 with 8 elements in the last slab (100 x
+# 30000 x 1000).
 STAGED_SHAPES = [(1000, 1001, 1111), (2048, 1000, 640), (1000, 2048, 640), (1024, 1024, 1025),
                  (1536, 1000, 777), (1111, 1152, 896), (1300, 1000, 1100), (1024, 1100, 1002),
                  (1100, 1024, 1003), (1024, 1024, 1005), (1050, 1030, 1006), (700, 3001, 600),
-                 (1040, 1000, 1000), (1024, 1040, 1056), (6144, 7424, 24)]
+                 (1040, 1000, 1000), (1024, 1040, 1056), (6144, 7424, 24), (100, 30000, 1000)]
 
 
 @pytest.mark.parametrize("shape", STAGED_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -794,9 +795,10 @@ def test_f16_staged_small_integers_are_exact():
 
 
 def test_f16_staged_unaligned_and_c_only():
-    """Operands one element into their buffers with odd leading dimensions;
-    then aligned operands with only C misaligned.  Nothing outside C's window
-    changes."""
+    """Operands one element into their buffers with odd leading dimensions
+    (the register-staged wide tiles); then aligned operands with only C
+    misaligned (the full tiles' ragged form, C at any 2-byte address).
+    Nothing outside C's window changes."""
     for (M, N, K, off_ab) in [(1030, 1100, 1000, 1), (1024, 1024, 1024, 0)]:
         lda, ldb = (K + 3, K + 1) if off_ab else (K, K)
         ldc = N + 5
@@ -809,7 +811,7 @@ def test_f16_staged_unaligned_and_c_only():
         dC = bufC[1:1 + M * ldc].view(M, ldc)[:, :N]
         dA.copy_(dev(A))
         dB.copy_(dev(B))
-        assert dg.f16_nt_path(dA, dB, dC) == "f16_staged"
+        assert dg.f16_nt_path(dA, dB, dC) == ("f16_staged" if off_ab else "f16_mfma")
         dg.gemm_f16_nt(dA, dB, dC)
         torch.cuda.synchronize()
         f16_check(dC.cpu().numpy(), oracle.gemm_f16_nt_exact(A, B),
@@ -823,9 +825,9 @@ def test_f16_staged_unaligned_and_c_only():
 
 @pytest.mark.parametrize("act,use_bias,use_res", EPI_CASES)
 def test_f16_staged_fused(act, use_bias, use_res):
-    """The fused write-back on the staged path: a ragged shape, then an
-    aligned shape with the bias one element into its buffer and the residual
-    rows of odd length, in place."""
+    """The fused write-back on the staged path (a ragged shape with K odd),
+    then on an aligned shape with the bias one element into its buffer and
+    the residual rows of odd length, in place (the full tiles' ragged form)."""
     M, N, K = 1000, 1001, 1111
     A, B, bias, res = epi_operands(M, N, K, use_bias, use_res)
     dA, dB = dev(A), dev(B)
@@ -845,7 +847,9 @@ def test_f16_staged_fused(act, use_bias, use_res):
     cbuf = torch.zeros(M, N + 1, device=DEV, dtype=torch.float16)
     cbuf[:, :N].copy_(dev(res))
     dC = cbuf[:, :N]
-    assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], act, dC) == "f16_staged"
+    # aligned operands: the full tiles' ragged form (bias, residual and C at
+    # any 2-byte address), the residual read in place of C
+    assert dg.f16_nt_ex_path(dev(A), dev(B), dC, bbuf[1:], act, dC) == "f16_mfma"
     dg.gemm_f16_nt_ex(dev(A), dev(B), dC, bbuf[1:], act, dC)
     torch.cuda.synchronize()
     check_ex(dC.cpu().numpy(), A, B, bias, act, res)

@@ -1,6 +1,7 @@
 """A seeded random sweep across the paths: shapes drawn so that every kernel
 family is reached (streaming, register-staged full and wide tiles, edge,
-split-K through the explicit calls, matrix-vector), with padded leading
+split-K through the explicit calls, matrix-vector, the ragged forms of the
+full and streaming tiles), with padded leading
 dimensions and, for fp32, random alpha and beta.  Products up to 2^27 multiply-adds are compared element by element
 with the oracle, larger ones on sampled outputs."""
 from __future__ import annotations
@@ -24,7 +25,7 @@ DEV = "cuda:0"
 def draw(seed):
     rng = np.random.default_rng(seed)
     kind = "f32" if seed % 2 == 0 else "f16"
-    family = rng.integers(0, 5)
+    family = rng.integers(0, 5) if seed < 48 else 5
     if family == 0:       # small and ragged
         M, N, K = (int(x) for x in rng.integers(1, 300, 3))
     elif family == 1:     # whole tiles
@@ -33,16 +34,24 @@ def draw(seed):
         M, N, K = (int(x) for x in rng.integers(900, 2600, 3))
     elif family == 3:     # few tiles, long K (split-K)
         M, N, K = int(rng.integers(1, 400)), int(rng.integers(1, 400)), int(rng.integers(2048, 9000))
-    else:                 # thin (matrix-vector for fp16)
+    elif family == 4:     # thin (matrix-vector for fp16)
         M, N, K = int(rng.integers(1, 9)), int(rng.integers(100, 5000)), int(rng.integers(1, 3000))
         if rng.integers(0, 2):
             M, N = N, M
+    else:                 # large and ragged, rows at 16-byte addresses (the ragged full tiles)
+        M, N = (int(x) for x in rng.integers(1000, 5000, 2))
+        K = 8 * int(rng.integers(9, 400))
+        if kind == "f32":
+            N -= N % 4    # fp32 B and C rows at 16-byte addresses too
+        pad = int(rng.choice([0, 8]))
+        alpha, beta = [(1.0, 0.0), (0.5, 1.0), (-1.5, 0.25)][int(rng.integers(0, 3))]
+        return kind, M, N, K, pad, alpha, beta, False
     pad = int(rng.choice([0, 0, 1, 4, 8]))
     alpha, beta = [(1.0, 0.0), (0.5, 1.0), (-1.5, 0.25)][int(rng.integers(0, 3))]
     return kind, M, N, K, pad, alpha, beta, int(family) == 3
 
 
-SEEDS = list(range(48))
+SEEDS = list(range(64))
 
 
 @pytest.mark.parametrize("seed", SEEDS)
@@ -56,8 +65,12 @@ def test_random_sweep(seed):
     if small:
         rows = cols = None
     else:
-        rows = np.concatenate([np.zeros(N, np.int64), np.full(N, M - 1), rng.integers(0, M, 4000)])
-        cols = np.concatenate([np.arange(N), np.arange(N), rng.integers(0, N, 4000)])
+        # the first and last rows and columns whole (the shifted edge tiles of
+        # the ragged forms end there), and random points
+        rows = np.concatenate([np.zeros(N, np.int64), np.full(N, M - 1), np.arange(M), np.arange(M),
+                               rng.integers(0, M, 4000)])
+        cols = np.concatenate([np.arange(N), np.arange(N), np.zeros(M, np.int64), np.full(M, N - 1),
+                               rng.integers(0, N, 4000)])
     if kind == "f32":
         A, B, C = inputs.sgemm_operands(M, N, K, with_c=True)
         bA = torch.zeros(M, K + pad, device=DEV); bA[:, :K] = torch.from_numpy(A).to(DEV)

@@ -111,6 +111,8 @@ bool f16_ragged_fits(int M, int N, int K, const void* A, int64_t lda, const void
 }
 
 hipError_t launch_f16_mfma(const Args16& a, bool epi, int cus, hipStream_t stream) {
+  if (!epi && f16_small_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc, cus))
+    return launch_f16_small(a, cus, stream);
   if (!f16_mfma_fits(a.M, a.N, a.K, a.A, a.lda, a.B, a.ldb, a.C, a.ldc) ||
       (epi && !hgemm::epi_fits(a.bias, a.res, a.ldr))) {
     if (a.fmt == kFmtBF16)

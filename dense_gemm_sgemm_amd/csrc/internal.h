@@ -138,6 +138,12 @@ hipError_t launch_transpose16(const PadCopy& first, const PadCopy* second, hipSt
 // leading dimension (below 2^23) and 2-byte alignment, no copies, no
 // workspace.
 bool f16_staged_fits(int M, int N, int K, int64_t lda, int64_t ldb);
+// Few output tiles (at most as many 64 x 64 tiles as CUs) and K a multiple of
+// 128 (no fused write-back): 32 x 32 or 16 x 16 tiles with K split across the
+// four waves of a workgroup.
+bool f16_small_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                    const void* C, int64_t ldc, int cus);
+hipError_t launch_f16_small(const Args16& a, int cus, hipStream_t stream);
 // The full-tile kernels' ragged form: any M, N >= 128, K > 64 with K % 8 ==
 // 0, A and B rows at 16-byte addresses, C anywhere.
 bool f16_ragged_fits(int M, int N, int K, const void* A, int64_t lda, const void* B, int64_t ldb);

@@ -782,6 +782,25 @@ def test_f16_ragged_full_tiles_c_unaligned_and_fused():
     check_ex(dC.cpu().numpy(), A, B, bias, "silu", res)
 
 
+# Products with at most as many 64 x 64 tiles as CUs and K a multiple of 128
+# run on the small-tile kernel that splits K across the four waves of a
+# workgroup: 32 x 32 tiles (512 x 512 x 16384 and 1024 x 512 x 1024: 256 and
+# 512 tiles), 16 x 16 tiles (256 x 256 x 8192, 512 x 256 x 4096), a short
+# last chunk (2176 = 8 x 256 + 128).  Every output against the oracle, then
+# bitwise repeats.
+SMALL16_SHAPES = [(512, 512, 16384), (256, 256, 8192), (128, 512, 2176), (512, 256, 4096),
+                  (1024, 512, 1024)]
+
+
+@pytest.mark.parametrize("shape", SMALL16_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f16_small_tiles_split_k_in_workgroup(shape, path_mode):
+    M, N, K = shape
+    A, B = inputs.hgemm_nt_operands(M, N, K)
+    got = gpu_f16(A, B, expect=expected_f16_path(path_mode, M, N, K))
+    f16_check(got, oracle.gemm_f16_nt_exact(A, B), oracle.gemm_f16_nt_exact(abs16(A), abs16(B)))
+    assert np.array_equal(gpu_f16(A, B).view(np.uint16), got.view(np.uint16))
+
+
 def test_f16_staged_small_integers_are_exact():
     """Small-integer operands make every partial sum exact, so the staged
     kernel (ragged M, N, K with a K tail) must equal the exact product

@@ -318,7 +318,8 @@ enum {
   GEMM_PATH_F16_MFMA = 6,       /* v_mfma f16 full tiles, 16-byte aligned rows    */
                                 /*   (large ragged products with A and B rows at  */
                                 /*   16-byte addresses and K % 8 == 0: shifted    */
-                                /*   edge tiles, C anywhere)                      */
+                                /*   edge tiles, C anywhere; few output tiles:    */
+                                /*   32 x 32 tiles, K split across the waves)     */
   GEMM_PATH_F16_GEMV = 7,       /* M <= 8 or N <= 8: matrix-vector kernel that    */
                                 /*   streams the long operand once (any ld/align) */
   GEMM_PATH_F16_SPLITK = 8,     /* gemm_ex only, long K over few output tiles: K   */

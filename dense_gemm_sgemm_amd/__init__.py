@@ -32,6 +32,7 @@ LIB_PATH = os.path.join(HERE, "libmi355gemm.so")
 
 # Status and activation codes, mirroring include/mi355gemm.h.
 GEMM_OK = 0
+GEMM_ERR_WORKSPACE = -7
 GEMM_ERR_SCRATCH_LIMIT = -8
 STATIC_SCRATCH_BYTES = 32 << 20
 ACTS = {"none": 0, "relu": 1, "silu": 2}
@@ -395,12 +396,22 @@ def gemm_ex(A, B, C, op_a: str = "n", op_b: str = "t", bias=None, act: str = "no
     tensors (all of one dtype).  op "n": A is [M,K], B is [K,N]; op "t": A is
     [K,M], B is [N,K].  fp32 accumulation, one rounding to the dtype.
     ``workspace``: a contiguous GPU tensor of at least ``ex_workspace_bytes``
-    bytes, or None (one is taken from torch's allocator when the call uses
-    one).  Returns C."""
+    bytes, or None (one is taken from torch's allocator only when the call
+    needs one: the library checks the workspace before it enqueues any work,
+    so a call that reads its operands in place runs without).  Returns C."""
     args = _ex_args(A, B, C, op_a, op_b, bias, act, residual)
     lib = load_library()
-    need = 0 if workspace is not None else int(lib.gemm_ex_workspace(
-        args[0], args[1], args[2], args[3], args[4], args[5], args[7], args[9]))
+    if workspace is None:
+        # split-K runs only with its workspace; other calls try without first
+        if _path_name(lib.gemm_ex_path(*args)) != "f16_splitk":
+            status = lib.gemm_ex(*args, None, 0, _stream(stream))
+            if status != GEMM_ERR_WORKSPACE:
+                _check(status)
+                return C
+        need = int(lib.gemm_ex_workspace(args[0], args[1], args[2], args[3], args[4], args[5],
+                                         args[7], args[9]))
+    else:
+        need = 0
     pw, nw, _ws = _workspace(workspace, need, C.device, stream)
     _check(lib.gemm_ex(*args, pw, nw, _stream(stream)))
     return C

@@ -96,6 +96,7 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
 // there, after any copies.
 struct Plan16 {
   int path = GEMM_PATH_NOOP;
+  int lay = 0;                  // F16_MFMA reading B [K][N] (1) or A [K][M] (2) in place
   bool copy_a = false, copy_b = false;
   bool gemv_kn = false;         // matrix-vector path with the long operand K-major
   int64_t lda = 0, ldb = 0;     // leading dimensions the A * B^T kernels see
@@ -109,7 +110,7 @@ struct Plan16 {
 // operand, whatever their layout).
 Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, int lda,
               const void* B, int ldb, const void* bias, int act, const void* res, int ldr,
-              const void* C, int ldc, bool allow_split = false) {
+              const void* C, int ldc, bool allow_split = false, bool in_place = true) {
   Plan16 pl;
   auto done = [&](int code) {
     pl.path = code;
@@ -176,10 +177,18 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
       return done(GEMM_PATH_F16_SPLITK);
     }
   }
-  // The other layouts run on transposed copies: on 5376 x 5376 x 2048 the
-  // copy and the full-tile kernel take 113-122 us, where the register-staged
-  // wide tiles reading the K-major operands in place (8 x 8 blocks
-  // transposed in registers) took 164-481 us.
+  // NN and TT on whole tiles: the full-tile kernels read the K-major operand
+  // in place through the transposing LDS reads (no copy, no workspace).
+  const int lay = cb && !ca ? 1 : ca && !cb ? 2 : 0;
+  if (in_place && lay != 0 && f16_kmajor_fits(lay, M, N, K, A, lda, B, ldb, C, ldc) &&
+      (!epi || f16_epi_fits(bias, res, ldr))) {
+    pl.lay = lay;
+    return done(GEMM_PATH_F16_MFMA);
+  }
+  // The other layouts and shapes run on transposed copies: on 5376 x 5376 x
+  // 2048 TN's copies and the full-tile kernel take 113-122 us, where the
+  // register-staged wide tiles reading the K-major operands in place (8 x 8
+  // blocks transposed in registers) took 164-481 us.
   copies(ca, cb);
   const void* a_read = ca ? kCopyAddress : A;
   const void* b_read = cb ? kCopyAddress : B;
@@ -242,7 +251,8 @@ hipError_t run16(const Plan16& pl, Args16 a, int op_a, int op_b, bool epi, int c
       a.sk = splitk_args(splitk_plan(a.M, a.N, a.K, kF16Slab, kF16Rule, 0), a.M, a.N,
                          ws + pl.bytes_a + pl.bytes_b);
       return launch_f16_splitk(a, epi, cus, s);
-    case GEMM_PATH_F16_MFMA: return launch_f16_mfma(a, epi, cus, s);
+    case GEMM_PATH_F16_MFMA:
+      return pl.lay ? launch_f16_kmajor(a, pl.lay, epi, cus, s) : launch_f16_mfma(a, epi, cus, s);
     case GEMM_PATH_F16_STAGED: return launch_f16_staged(a, epi, cus, s);
     default: return launch_f16_edge(a, epi, s);
   }
@@ -343,10 +353,12 @@ MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K, con
 
 MI355GEMM_API unsigned long long gemm_ex_workspace(int type, int op_a, int op_b, int M, int N,
                                                    int K, int lda, int ldb) {
-  // The plan's workspace does not depend on the pointers: pass aligned
-  // stand-ins and a packed C.
+  // An upper bound for any pointers: aligned stand-ins, a packed C, and the
+  // copies even where aligned NN / TT operands are read in place (those calls
+  // use none of it).
   const Plan16 pl = plan16(type, op_a, op_b, M, N, K, kCopyAddress, lda, kCopyAddress, ldb,
-                           nullptr, GEMM_ACT_NONE, nullptr, 0, kCopyAddress, N > 1 ? N : 1, true);
+                           nullptr, GEMM_ACT_NONE, nullptr, 0, kCopyAddress, N > 1 ? N : 1, true,
+                           false);
   return pl.path < 0 ? 0 : pl.workspace();
 }
 

@@ -79,6 +79,35 @@ __device__ __forceinline__ f4 mfma16(h8 a, h8 b, f4 c) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
+// One direct-to-LDS copy written out as an asm statement: lane i loads 16
+// bytes from sbase + voff (sbase wave-uniform) and they land at dst + 16 i.
+// The compiler sees no LDS write in it, so it adds none of its own waits for
+// it; the kernels that use it (those with transposing LDS reads, which the
+// compiler would otherwise make wait for every copy in flight) complete it
+// with their explicit vmcnt wait before the barrier that publishes a slab.
+// M0 (the LDS destination, read when the copy issues) is set one wait state
+// ahead and restored after, since the compiler reserves M0 and does not track
+// a change made inside an asm statement.
+__device__ __forceinline__ void copy16_asm(const char* sbase, uint32_t voff, lds_void_t* dst) {
+  // (readfirstlane returns a signed int: each half goes through uint32_t so
+  // that the low half is zero-extended, not sign-extended, into the address)
+  const uint64_t v = (uint64_t)sbase;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint64_t base = ((uint64_t)hi << 32) | lo;
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(m0v)
+      : "memory");
+}
+
 // Tile order.  The dispatcher deals consecutive workgroups round-robin to the
 // 8 XCDs (each with its own L2).  Workgroup b is remapped so that each XCD
 // gets a contiguous range of the linear tile order, and that order walks GM
@@ -158,12 +187,31 @@ __device__ __forceinline__ void static_for(F&& f) {
 // i / tiles of tile i % tiles, p.sk.per slabs from slab (i / tiles) * per --
 // and store each item's fp32 partial tile to the split-K workspace instead of
 // writing C.
+//
+// LAY 1 instances read B stored [K][N] (C = A * B) and LAY 2 instances A
+// stored [K][M] (C = A^T * B^T) in place: the page's kernel consumes the
+// operand in the layout it is stored in rather than transposing it first
+// ("从零开始的 AI Infra: 算子基础与GPU架构", section 19).  That operand's slab
+// is kept in LDS as 64 k-rows of 256 values (512 bytes: 32 chunks of 16
+// bytes), chunk c of k-row k at position c ^ tsw(k) with
+// tsw(k) = 2 (k & 3) | 8 (((k >> 3) ^ (k >> 4)) & 1), and its fragments are
+// read with gfx950's transposing LDS read (ds_read_b64_tr_b16): in each
+// group of 16 lanes, lane 4 a + b receives element b of the 8-byte reads of
+// lanes a, a + 4, a + 8 and a + 12.  Lane l (group g = l / 16, i = l % 16)
+// reads k-row 32 s + 8 g + 4 h + i / 4 at values x0 + 4 (i % 4) .. + 3 for
+// h = 0, 1, and so holds k = 32 s + 8 g .. + 7 of value x0 + i: the same k
+// bijection as the K-contiguous operand's fragments.  Among any two of the
+// four lane groups the sixteen rows' chunk pairs fall on distinct bank quads.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
-          int FMT, bool SPLIT = false, bool RAG = false>
+          int FMT, bool SPLIT = false, bool RAG = false, int LAY = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVES_M * WAVES_N))
 void hgemm_nt_kernel(TileArgs ta) {
   static_assert(!(RAG && SPLIT), "ragged tiles store C");
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
+  constexpr bool kAT = LAY == 2, kBT = LAY == 1;   // A or B stored K-major
+  static_assert(LAY == 0 || (!RAG && !SPLIT && C::kCopyWaves == 4 && (OPT & 2) == 0),
+                "K-major operands: whole tiles, four copying waves, two fragment sets");
+  static_assert((!kBT || BN == 256) && (!kAT || BM == 256), "K-major slab rows of 256 values");
   constexpr int kChunks = C::kChunks;
   const Args16& p = ta.p;
   // Two slab stages, then the epilogue staging area (16 rows of 256 bytes per
@@ -232,6 +280,18 @@ void hgemm_nt_kernel(TileArgs ta) {
   const int64_t copy_strideB = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.ldb * 2;
   const int64_t firstA = (int64_t)cwp * C::kRowsPerCopy * p.lda * 2;
   const int64_t firstB = (int64_t)cwp * C::kRowsPerCopy * p.ldb * 2;
+  // The K-major operand (LAY): copy c fills k-rows 2 c and 2 c + 1, lane l
+  // writing k-row 2 c + l / 32 at position l % 32, so it loads logical chunk
+  // (l % 32) ^ tsw(k-row).  Copy i of wave cw is c = 4 i + cw, k-row
+  // 8 i + 2 cw + l / 32: its k & 3 is 2 (cw & 1) + l / 32 and its
+  // ((k >> 3) ^ (k >> 4)) & 1 is (i ^ (i >> 1)) & 1, so two lane offsets serve
+  // every copy.
+  const int64_t ldt = kBT ? p.ldb : p.lda;
+  const int tlo = 2 * (2 * (cwp & 1) + (lane >> 5));
+  const uint32_t offT0 = (uint32_t)((lane >> 5) * ldt * 2 + 16 * ((lane & 31) ^ tlo));
+  const uint32_t offT1 = (uint32_t)((lane >> 5) * ldt * 2 + 16 * ((lane & 31) ^ (tlo | 8)));
+  const int64_t firstT = (int64_t)2 * cwp * ldt * 2;
+  const int64_t copy_strideT = (int64_t)8 * ldt * 2;
 
   // This wave's copies of one K slab: the sources of its A and B rows and
   // the slab's LDS stage, then copy instruction c (A copies first) one at a
@@ -245,24 +305,41 @@ void hgemm_nt_kernel(TileArgs ta) {
   auto slab_base = [&](int stage, int m0, int n0, int t, bool tail) __attribute__((always_inline)) {
     CopyBase cb;
     cb.l = lds + stage * C::kStageBytes;
-    cb.a = (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
-    cb.b = (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
+    cb.a = kAT ? (const char*)(p.A + (int64_t)t * BK * p.lda + m0) + firstT
+               : (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
+    cb.b = kBT ? (const char*)(p.B + (int64_t)t * BK * p.ldb + n0) + firstT
+               : (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
     cb.oa = RAG && tail ? offA_tail : offA;
     cb.ob = RAG && tail ? offB_tail : offB;
     return cb;
   };
+  // One copy (LAY: through the asm statement above, so that the compiler
+  // adds no waits before the transposing reads).
+  auto issue = [&](const char* base, uint32_t off, unsigned char* dst) __attribute__((always_inline)) {
+    if constexpr (LAY != 0)
+      copy16_asm(base, off, (lds_void_t*)dst);
+    else
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + off), (lds_void_t*)dst, 16, 0, 0);
+  };
   auto copy_one = [&](const CopyBase& cb, int c) __attribute__((always_inline)) {
     if (c < C::kPerWaveA) {
-      if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(cb.a + c * copy_strideA + cb.oa),
-                                         (lds_void_t*)(cb.l + (c * C::kCopyWaves + cw) * 1024),
-                                         16, 0, 0);
+      if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA) {
+        if constexpr (kAT)
+          issue(cb.a + c * copy_strideT, ((c ^ (c >> 1)) & 1) ? offT1 : offT0,
+                cb.l + (c * C::kCopyWaves + cw) * 1024);
+        else
+          issue(cb.a + c * copy_strideA, cb.oa, cb.l + (c * C::kCopyWaves + cw) * 1024);
+      }
     } else {
       const int i = c - C::kPerWaveA;
-      if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB)
-        __builtin_amdgcn_global_load_lds(
-            (gbl_void_t*)(cb.b + i * copy_strideB + cb.ob),
-            (lds_void_t*)(cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024), 16, 0, 0);
+      if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB) {
+        if constexpr (kBT)
+          issue(cb.b + i * copy_strideT, ((i ^ (i >> 1)) & 1) ? offT1 : offT0,
+                cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024);
+        else
+          issue(cb.b + i * copy_strideB, cb.ob,
+                cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024);
+      }
     }
   };
   // All of this wave's copies have landed in LDS, and all of its LDS reads
@@ -298,6 +375,32 @@ void hgemm_nt_kernel(TileArgs ta) {
   const int fr = slab_swz(r);
   const int a_off = (wm + r) * kChunks, b_off = (BM + wn + r) * kChunks;   // in 16-byte units
 
+  // K-major operand fragments (LAY): per-lane byte offsets of block x's
+  // first transposing read within the operand's stage area (block x covers
+  // values x0 = w0 + 16 x .. + 15 of the wave's w0 = wm or wn).
+  constexpr int kTBlocks = kBT ? C::kBlocksN : kAT ? C::kBlocksM : 1;
+  uint32_t toff[kTBlocks];
+  {
+    const int ti = lane & 15;
+    const int tsw = (2 * (ti >> 2)) | (8 * ((g ^ (g >> 1)) & 1));
+    const int w0 = kBT ? wn : wm;
+#pragma unroll
+    for (int x = 0; x < kTBlocks; ++x)
+      toff[x] = (uint32_t)((8 * g + (ti >> 2)) * 512 +
+                           16 * (((w0 >> 3) + 2 * x + ((ti & 3) >> 1)) ^ tsw) + 8 * (ti & 1));
+  }
+  // Block x of k-step s from the operand area `area` (A's or B's part of a
+  // stage): two transposing reads, k-rows 4 apart.
+  auto tread = [&](const unsigned char* area, int x, int s) __attribute__((always_inline)) {
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    typedef __attribute__((address_space(3))) const unsigned char lds_u8;
+    lds_u8* base = (lds_u8*)area + toff[x] + s * 32 * 512;
+    const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)base);
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(base + 4 * 512));
+    return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
   f4 acc[C::kBlocksM][C::kBlocksN];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -313,11 +416,18 @@ void hgemm_nt_kernel(TileArgs ta) {
   h8 fa[2][C::kBlocksM], fb[kOneB ? 1 : 2][C::kBlocksN];
   auto load_frags = [&](int set, int stage, int s) __attribute__((always_inline)) {
     const h8* st = (const h8*)(lds + stage * C::kStageBytes);
+    const unsigned char* sa = lds + stage * C::kStageBytes;
     const int pc = (4 * s + g) ^ fr;
 #pragma unroll
-    for (int i = 0; i < C::kBlocksM; ++i) fa[set][i] = st[a_off + 16 * kChunks * i + pc];
+    for (int i = 0; i < C::kBlocksM; ++i) {
+      if constexpr (kAT) fa[set][i] = tread(sa, i, s);
+      else fa[set][i] = st[a_off + 16 * kChunks * i + pc];
+    }
 #pragma unroll
-    for (int j = 0; j < C::kBlocksN; ++j) fb[kOneB ? 0 : set][j] = st[b_off + 16 * kChunks * j + pc];
+    for (int j = 0; j < C::kBlocksN; ++j) {
+      if constexpr (kBT) fb[kOneB ? 0 : set][j] = tread(sa + BM * BK * 2, j, s);
+      else fb[kOneB ? 0 : set][j] = st[b_off + 16 * kChunks * j + pc];
+    }
   };
   auto mfma_step = [&](int set) __attribute__((always_inline)) {
 #pragma unroll
@@ -330,11 +440,15 @@ void hgemm_nt_kernel(TileArgs ta) {
   // k-step (row block q / kBlocksN, column block q % kBlocksN).
   auto read_one = [&](int set, int stage, int step, int q) __attribute__((always_inline)) {
     const h8* st = (const h8*)(lds + stage * C::kStageBytes);
+    const unsigned char* sa = lds + stage * C::kStageBytes;
     const int pc = (4 * step + g) ^ fr;
-    if (q < C::kBlocksM)
-      fa[set][q] = st[a_off + 16 * kChunks * q + pc];
-    else
-      fb[set][q - C::kBlocksM] = st[b_off + 16 * kChunks * (q - C::kBlocksM) + pc];
+    if (q < C::kBlocksM) {
+      if constexpr (kAT) fa[set][q] = tread(sa, q, step);
+      else fa[set][q] = st[a_off + 16 * kChunks * q + pc];
+    } else {
+      if constexpr (kBT) fb[set][q - C::kBlocksM] = tread(sa + BM * BK * 2, q - C::kBlocksM, step);
+      else fb[set][q - C::kBlocksM] = st[b_off + 16 * kChunks * (q - C::kBlocksM) + pc];
+    }
   };
   auto mfma_one = [&](int set, int q) __attribute__((always_inline)) {
     const int i = q / C::kBlocksN, j = q % C::kBlocksN;
@@ -466,8 +580,10 @@ void hgemm_nt_kernel(TileArgs ta) {
   // next barrier.
   constexpr int kMfma = C::kBlocksM * C::kBlocksN;
   constexpr int kReads = C::kBlocksM + C::kBlocksN;
+  // LDS read instructions per k-step (a K-major block takes two)
+  constexpr int kReadInstr = kReads + (kAT ? C::kBlocksM : 0) + (kBT ? C::kBlocksN : 0);
   constexpr int kCopies = C::kPerWaveA + C::kPerWaveB;
-  static_assert(kReads <= kMfma && kCopies <= kMfma, "interleave pattern");
+  static_assert(kReadInstr <= kMfma && kCopies <= kMfma, "interleave pattern");
   const int nk = SPLIT ? p.sk.per : RAG ? (p.K + BK - 1) / BK : p.K / BK;   // slabs per work item
   // The copy target runs two slabs ahead of the compute: slab tc of the tile
   // `ahead` tiles after the current one (origins o[0..2] are refreshed once
@@ -575,11 +691,11 @@ void hgemm_nt_kernel(TileArgs ta) {
     load_frags(1, gs & 1, 1);
     mfma_step(0);
 #pragma unroll
-    for (int q = 0; q < kReads; ++q) {
+    for (int q = 0; q < kReadInstr; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReadInstr, 0);
     __builtin_amdgcn_sched_barrier(0);
     sync();
     __builtin_amdgcn_sched_barrier(0);
@@ -654,7 +770,7 @@ void hgemm_nt_kernel(TileArgs ta) {
 // each walking its tiles; otherwise one workgroup per tile.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT = 0,
           bool PERSISTENT = true, bool EPI = false, int FMT = kFmtF16, bool SPLIT = false,
-          bool RAG = false>
+          bool RAG = false, int LAY = 0>
 hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   const int64_t tiles = RAG ? (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN)
@@ -666,7 +782,8 @@ hipError_t launch(const Args16& a, int slots, hipStream_t stream) {
   void* args[] = {&ta};
   return hipLaunchKernel(
       (const void*)
-          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT, RAG>,
+          hgemm_nt_kernel<BM, BN, BK, WAVES_M, WAVES_N, GM, COPY_SEL, OPT, EPI, FMT, SPLIT, RAG,
+                          LAY>,
       dim3((unsigned)grid), dim3(C::kThreads), args, 0, stream);
 }
 

@@ -68,6 +68,8 @@ def expected_ex_path(M, N, K, op_a, op_b):
     if splitk_auto(M, N, K, 64):
         return "f16_splitk"
     large = M * N * K >= 1 << 30 and K >= 8
+    if kmajor_in_place(M, N, K, op_a, op_b):
+        return "f16_mfma"
     # NT in place, or the other layouts through 16-byte aligned transposed copies
     fast = K % 64 == 0 and ((M % 256 == 0 and (N % 256 == 0 or N % 224 == 0)) or
                             (M % 128 == 0 and (N % 128 == 0 or N % 192 == 0)))
@@ -76,3 +78,16 @@ def expected_ex_path(M, N, K, op_a, op_b):
     if large and ragged_fits(M, N, K):
         return "f16_mfma"
     return "f16_staged" if large else "f16_general"
+
+
+def kmajor_in_place(M, N, K, op_a, op_b):
+    """gemm_ex NN on whole 224 x 256 tiles and TT on whole 256 x 224 tiles
+    (K % 64 == 0, aligned operands): the full tiles read the K-major operand
+    in place, with no workspace."""
+    if K % 64 != 0 or K == 0:
+        return False
+    if (op_a, op_b) == ("n", "n"):
+        return M % 224 == 0 and N % 256 == 0
+    if (op_a, op_b) == ("t", "t"):
+        return M % 256 == 0 and N % 224 == 0
+    return False

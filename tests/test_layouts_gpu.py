@@ -257,7 +257,7 @@ def test_bf16_exact_cases_and_determinism():
 
 
 @pytest.mark.parametrize("fmt,layout", [("bf16", ("n", "t")), ("f16", ("n", "n")),
-                                        ("bf16", ("t", "n"))])
+                                        ("bf16", ("t", "n")), ("f16", ("t", "t"))])
 def test_workload_5376_layouts(fmt, layout):
     """5376 x 5376 x 2048 in bf16 and in the other layouts, on the fast
     kernel, every output against the oracle."""
@@ -314,5 +314,70 @@ def test_layouts_ragged_full_tiles(layout, fmt):
     res = r.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(r)
     got = run_ex(A, B, op_a, op_b, fmt, M, N, bias, "silu", res, expect="f16_mfma")
     ref, sab = reference(A, B, op_a, op_b, fmt, bias, "silu", res)
+    dec = oracle.half_to_double if fmt == "f16" else oracle.bf16_to_double
+    check16(got, ref, sab, fmt, np.abs(dec(bias))[None, :], np.abs(dec(res)), fused=True)
+
+
+# NN on whole 224 x 256 tiles and TT on whole 256 x 224 tiles: the full-tile
+# kernel reads the K-major operand in place (transposing LDS reads).  One
+# tile with one slab, a few tiles, and more tiles than CUs (each workgroup
+# then walks two tiles, prefetching across the tile boundary).
+KMAJOR_CASES = [(("n", "n"), 224, 256, 64), (("n", "n"), 448, 512, 192),
+                (("n", "n"), 672, 768, 320), (("n", "n"), 5376, 3072, 128),
+                (("t", "t"), 256, 224, 64), (("t", "t"), 512, 448, 192),
+                (("t", "t"), 768, 672, 320), (("t", "t"), 3072, 5376, 128)]
+
+
+def run_in_place(A, B, op_a, op_b, fmt, M, N, pad=0, bias=None, act="none", res=None):
+    """gemm_ex with an empty workspace (the call fails if it needs one); the
+    K-major operand optionally in rows padded by `pad` elements."""
+    def stored(x, kmajor):
+        if not (kmajor and pad):
+            return to_dev(x, fmt)
+        return to_dev(np.pad(x, ((0, 0), (0, pad))), fmt)[:, :x.shape[1]]
+    dA = stored(A, op_a == "t")
+    dB = stored(B, op_b == "n")
+    dbias = to_dev(bias, fmt) if bias is not None else None
+    dres = to_dev(res, fmt) if res is not None else None
+    dC = torch.full((M, N), float("nan"), device=DEV, dtype=dtype_of(fmt))
+    assert dg.ex_path(dA, dB, dC, op_a, op_b, dbias, act, dres) == "f16_mfma"
+    dg.gemm_ex(dA, dB, dC, op_a, op_b, dbias, act, dres,
+               workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    return to_host(dC, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout,M,N,K", KMAJOR_CASES,
+                         ids=lambda v: "".join(v) if isinstance(v, tuple) else str(v))
+def test_layouts_kmajor_in_place(layout, M, N, K, fmt):
+    """Every output against the oracle, with no workspace; the larger
+    shapes also with the K-major operand's rows padded by 8 elements."""
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    ref, sab = reference(A, B, op_a, op_b, fmt)
+    check16(run_in_place(A, B, op_a, op_b, fmt, M, N), ref, sab, fmt)
+    if M * N >= 448 * 512:
+        check16(run_in_place(A, B, op_a, op_b, fmt, M, N, pad=8), ref, sab, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("layout,M,N,K,act", [(("n", "n"), 448, 512, 192, "silu"),
+                                              (("t", "t"), 512, 448, 256, "relu")],
+                         ids=lambda v: "".join(v) if isinstance(v, tuple) else str(v))
+def test_layouts_kmajor_in_place_fused(layout, M, N, K, act, fmt):
+    """The fused write-back (bias, activation, residual) on the in-place
+    NN / TT kernels, against the oracle."""
+    op_a, op_b = layout
+    sa, sb = stored_shapes(M, N, K, op_a, op_b)
+    A, B = inputs.operands16(sa, sb, fmt)
+    rng = np.random.default_rng(45)
+    b = rng.normal(0, 1.5, N)
+    r = rng.normal(0, 2.0, (M, N))
+    bias = b.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(b)
+    res = r.astype(np.float16) if fmt == "f16" else inputs.bf16_bits(r)
+    got = run_in_place(A, B, op_a, op_b, fmt, M, N, bias=bias, act=act, res=res)
+    ref, sab = reference(A, B, op_a, op_b, fmt, bias, act, res)
     dec = oracle.half_to_double if fmt == "f16" else oracle.bf16_to_double
     check16(got, ref, sab, fmt, np.abs(dec(bias))[None, :], np.abs(dec(res)), fused=True)

@@ -39,6 +39,7 @@ V_NAME = "hgemv_nt_1x16384x4096"
 V_COPIES = 4
 S_NAME = "hgemm_nt_128x128x16384"
 Q_NAME = "hgemm_nt_2048x2304x768"
+N_NAME = "hgemm_nn_5376x5376x2048"
 
 
 def parse_args():
@@ -48,14 +49,15 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", choices=["both", "hgemm", "sgemm", "hgemm_ragged", "hgemm_fused",
                                        "hgemv", "hgemm_splitk", "sgemm_256", "sgemm_1024",
-                                       "sgemm_beta", "hgemm_qkv", "blas_context"],
+                                       "sgemm_beta", "hgemm_qkv", "hgemm_nn", "blas_context"],
                     default="both",
                     help="time only one product (for profiling): one of the two step products, "
                          "the ragged 5000x3001x1537 fp16 product, the 5376^2 x 2048 product "
                          "with the fused bias + SiLU + residual write-back, the 1 x 16384 x "
                          "4096 decode product, the 128 x 128 x 16384 split-K product, the "
                          "256^3 or 1024^3 SGEMM, the 4096^3 SGEMM with beta = 0.5, or the "
-                         "2048 x 2304 x 768 fused-QKV fp16 product; blas_context times "
+                         "2048 x 2304 x 768 fused-QKV fp16 product, or the step's fp16 product "
+                         "with B stored [K][N] (read in place); blas_context times "
                          "torch.matmul (hipBLASLt) instead, on the step's operands and on "
                          "4096^3 and 8192^3 fp16 A*B^T, for context only")
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -93,7 +95,7 @@ KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sge
 KERNEL_SOURCES[S_NAME] = KERNEL_SOURCES[H_NAME] + ["dense_gemm_sgemm_amd/csrc/splitk.hip"]
 KERNEL_SOURCES["sgemm_256"] = KERNEL_SOURCES["sgemm_1024"] = KERNEL_SOURCES[F_NAME]
 KERNEL_SOURCES[F_NAME + "_beta0.5"] = KERNEL_SOURCES[F_NAME]
-KERNEL_SOURCES[Q_NAME] = KERNEL_SOURCES[H_NAME]
+KERNEL_SOURCES[Q_NAME] = KERNEL_SOURCES[N_NAME] = KERNEL_SOURCES[H_NAME]
 COPY_BYTES = 1 << 30
 # Bytes written between launches for the cold-cache figure: twice the 256 MB
 # last-level cache.
@@ -233,14 +235,16 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
     small SGEMMs, the 4096^3 SGEMM with beta = 0.5, the ragged fp16 product,
     the 5376^2 x 2048 fp16 product with the fused bias + SiLU + residual
     write-back, the fused-QKV shape, the single-tile long-K product (split-K),
+    the step's fp16 product with B stored [K][N] (NN, read in place),
     the step's fp16 product from a cold cache and the decode product.  Reported
     next to the step for context; not part of ``value``."""
     res = {}
     cases = [("sgemm_256", 0.0), ("sgemm_1024", 0.0), ("sgemm_4096", 0.5),
              ("hgemm_nt_5000x3001x1537", None), ("hgemm_nt_5376x5376x2048", "fused"),
-             ("hgemm_nt_2048x2304x768", None), ("hgemm_nt_128x128x16384", None)]
+             ("hgemm_nt_2048x2304x768", None), ("hgemm_nt_128x128x16384", None),
+             (N_NAME, None)]
     for name, beta in cases:
-        w = inputs.WORKLOADS[name]
+        w = inputs.WORKLOADS[H_NAME if name == N_NAME else name]
         if beta == "fused":
             # the fused write-back C = silu(A B^T + bias) + residual
             A, B = inputs.workload_operands(name)
@@ -258,6 +262,17 @@ def other_configs(dg, inputs, torch, dev, reps: int = 20) -> dict:
             run = lambda: dg.gemm_f32(dA, dB, dC, 1.0, beta)
             path = dg.f32_path(dA, dB, dC, 1.0, beta)
             dt = "f32"
+        elif name == N_NAME:
+            # the step's product with B stored [K][N] (gemm_ex NN): read in
+            # place, with an empty workspace
+            A, B = inputs.workload_operands(H_NAME)
+            dA = torch.from_numpy(A).to(dev)
+            dB = torch.from_numpy(np.ascontiguousarray(B.T)).to(dev)
+            dC = torch.empty(w["M"], w["N"], device=dev, dtype=torch.float16)
+            no_ws = torch.empty(0, dtype=torch.uint8, device=dev)
+            run = lambda: dg.gemm_ex(dA, dB, dC, "n", "n", workspace=no_ws)
+            path = dg.ex_path(dA, dB, dC, "n", "n") + " (gemm_ex NN, no workspace)"
+            dt = "f16"
         elif name == S_NAME:
             # one output tile, long K: the explicit split-K call with a workspace
             A, B = inputs.workload_operands(name)
@@ -339,6 +354,7 @@ def shape_of(inputs, name: str):
     name carries)."""
     base = name.replace("_bias_silu_residual", "").replace("_beta0.5", "")
     base = base.replace("torch_matmul_f16_nt_", "").replace("torch_matmul_", "")
+    base = base.replace("hgemm_nn_", "")
     if base in inputs.WORKLOADS:
         return [inputs.WORKLOADS[base][k] for k in ("M", "N", "K")]
     return [int(x) for x in base.split("x")]
@@ -428,6 +444,15 @@ def main():
         assert dg.f16_nt_path(dAq, dBq, dCq) == "f16_mfma"
         parts.append((Q_NAME, "f16", "hgemm_nt_kernel", flops(qw),
                       lambda: dg.gemm_f16_nt(dAq, dBq, dCq)))
+    if args.only == "hgemm_nn":
+        An, Bn = inputs.workload_operands(H_NAME)
+        dAn = torch.from_numpy(An).to(dev)
+        dBn = torch.from_numpy(np.ascontiguousarray(Bn.T)).to(dev)   # B stored [K][N]
+        dCn = torch.empty(hw["M"], hw["N"], device=dev, dtype=torch.float16)
+        no_ws = torch.empty(0, dtype=torch.uint8, device=dev)
+        assert dg.ex_path(dAn, dBn, dCn, "n", "n") == "f16_mfma"
+        parts.append((N_NAME, "f16", "hgemm_nt_kernel", flops(hw),
+                      lambda: dg.gemm_ex(dAn, dBn, dCn, "n", "n", workspace=no_ws)))
     if args.only == "blas_context":
         # Context, never the library: the vendor GEMM on the same operands.
         # B^T is passed as a transposed view, as an A*B^T caller would.

@@ -96,7 +96,7 @@ int f32_select(int M, int N, int K, float alpha, const float* A, int lda, const 
 // there, after any copies.
 struct Plan16 {
   int path = GEMM_PATH_NOOP;
-  int lay = 0;                  // F16_MFMA reading B [K][N] (1) or A [K][M] (2) in place
+  int lay = 0;                  // F16_MFMA reading B [K][N] (1), A [K][M] (2) or both (3) in place
   bool copy_a = false, copy_b = false;
   bool gemv_kn = false;         // matrix-vector path with the long operand K-major
   int64_t lda = 0, ldb = 0;     // leading dimensions the A * B^T kernels see
@@ -177,9 +177,10 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
       return done(GEMM_PATH_F16_SPLITK);
     }
   }
-  // NN and TT on whole tiles: the full-tile kernels read the K-major operand
-  // in place through the transposing LDS reads (no copy, no workspace).
-  const int lay = cb && !ca ? 1 : ca && !cb ? 2 : 0;
+  // NN, TT and TN on whole tiles: the full-tile kernels read the K-major
+  // operands in place through the transposing LDS reads (no copy, no
+  // workspace).
+  const int lay = cb && !ca ? 1 : ca && !cb ? 2 : ca && cb ? 3 : 0;
   if (in_place && lay != 0 && f16_kmajor_fits(lay, M, N, K, A, lda, B, ldb, C, ldc) &&
       (!epi || f16_epi_fits(bias, res, ldr))) {
     pl.lay = lay;

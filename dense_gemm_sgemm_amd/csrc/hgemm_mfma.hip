@@ -145,15 +145,16 @@ hipError_t launch_f16_partials_mfma(const Args16& a, int cus, hipStream_t stream
   return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 0, true, false, kFmtF16, true>(a, 2 * cus, stream);
 }
 
-// NN (lay 1: B stored [K][N]) and TT (lay 2: A stored [K][M]) read in place
-// by the full-tile kernels: 224 x 256 tiles (waves of 112 x 64, four B blocks
-// per k-step through the transposing reads) for NN, 256 x 224 (waves of
-// 64 x 112, four A blocks) for TT, so that 5376 x 5376 still takes 504 tiles
-// in two rounds.  Whole tiles, K a multiple of 64, the fast path's alignment.
+// NN (lay 1: B stored [K][N]), TT (lay 2: A stored [K][M]) and TN (lay 3:
+// both) read in place by the full-tile kernels: 224 x 256 tiles (waves of
+// 112 x 64, four B blocks per k-step through the transposing reads) for NN,
+// 256 x 224 (waves of 64 x 112: four A blocks, and TN's seven B blocks too)
+// for TT and TN, so that 5376 x 5376 still takes 504 tiles in two rounds.
+// Whole tiles, K a multiple of 64, the fast path's alignment.
 bool f16_kmajor_fits(int lay, int M, int N, int K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, const void* C, int64_t ldc) {
   if (lay == 1) return hgemm::fits<224, 256, BK>(M, N, K, A, lda, B, ldb, C, ldc);
-  if (lay == 2) return hgemm::fits<256, 224, BK>(M, N, K, A, lda, B, ldb, C, ldc);
+  if (lay == 2 || lay == 3) return hgemm::fits<256, 224, BK>(M, N, K, A, lda, B, ldb, C, ldc);
   return false;
 }
 
@@ -162,7 +163,10 @@ hipError_t launch_kmajor(const Args16& a, int lay, int cus, hipStream_t stream) 
   if (lay == 1)
     return hgemm::launch<224, 256, BK, 2, 4, GM, 1, 0, true, EPI, FMT, false, false, 1>(a, cus,
                                                                                       stream);
-  return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, false, 2>(a, cus,
+  if (lay == 2)
+    return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, false, 2>(a, cus,
+                                                                                      stream);
+  return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, false, 3>(a, cus,
                                                                                     stream);
 }
 

@@ -188,12 +188,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 // and store each item's fp32 partial tile to the split-K workspace instead of
 // writing C.
 //
-// LAY 1 instances read B stored [K][N] (C = A * B) and LAY 2 instances A
-// stored [K][M] (C = A^T * B^T) in place: the page's kernel consumes the
-// operand in the layout it is stored in rather than transposing it first
-// ("从零开始的 AI Infra: 算子基础与GPU架构", section 19).  That operand's slab
-// is kept in LDS as 64 k-rows of 256 values (512 bytes: 32 chunks of 16
-// bytes), chunk c of k-row k at position c ^ tsw(k) with
+// LAY 1 instances read B stored [K][N] (C = A * B), LAY 2 instances A
+// stored [K][M] (C = A^T * B^T) and LAY 3 instances both (C = A^T * B) in
+// place: the page's kernel consumes the operand in the layout it is stored in
+// rather than transposing it first ("从零开始的 AI Infra: 算子基础与GPU架构",
+// section 19).  Such an operand's slab is kept in LDS as 64 k-rows of 512
+// bytes (32 chunks of 16 bytes: the tile's 256 or 224 values, then unused
+// positions), chunk c of k-row k at position c ^ tsw(k) with
 // tsw(k) = 2 (k & 3) | 8 (((k >> 3) ^ (k >> 4)) & 1), and its fragments are
 // read with gfx950's transposing LDS read (ds_read_b64_tr_b16): in each
 // group of 16 lanes, lane 4 a + b receives element b of the 8-byte reads of
@@ -208,17 +209,27 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVE
 void hgemm_nt_kernel(TileArgs ta) {
   static_assert(!(RAG && SPLIT), "ragged tiles store C");
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
-  constexpr bool kAT = LAY == 2, kBT = LAY == 1;   // A or B stored K-major
+  constexpr bool kAT = LAY == 2 || LAY == 3, kBT = LAY == 1 || LAY == 3;   // stored K-major
   static_assert(LAY == 0 || (!RAG && !SPLIT && C::kCopyWaves == 4 && (OPT & 2) == 0),
                 "K-major operands: whole tiles, four copying waves, two fragment sets");
-  static_assert((!kBT || BN == 256) && (!kAT || BM == 256), "K-major slab rows of 256 values");
+  static_assert((!kBT || (BN <= 256 && BN % 32 == 0)) && (!kAT || (BM <= 256 && BM % 32 == 0)),
+                "K-major slab rows of at most 256 values");
+  // A stage: A's area, then B's; a K-major operand takes 64 k-rows of 512
+  // bytes, copied two k-rows per copy instruction.
+  constexpr int kAreaA = kAT ? BK * 512 : BM * BK * 2;
+  constexpr int kAreaB = kBT ? BK * 512 : BN * BK * 2;
+  constexpr int kStage = kAreaA + kAreaB;
+  static_assert(kBT || kAreaA == BM * BK * 2, "K-contiguous B fragments are read past A's area");
+  constexpr int kCopiesA = kAT ? BK / 2 : C::kCopiesA, kCopiesB = kBT ? BK / 2 : C::kCopiesB;
+  constexpr int kPerWaveA = (kCopiesA + C::kCopyWaves - 1) / C::kCopyWaves;
+  constexpr int kPerWaveB = (kCopiesB + C::kCopyWaves - 1) / C::kCopyWaves;
   constexpr int kChunks = C::kChunks;
   const Args16& p = ta.p;
   // Two slab stages, then the epilogue staging area (16 rows of 256 bytes per
   // wave, see below).
   constexpr int kOutRows = 16;
   constexpr int kOutBytes = C::kWaves * kOutRows * C::kOutRowBytes;
-  constexpr int kLds = 2 * C::kStageBytes + kOutBytes;
+  constexpr int kLds = 2 * kStage + kOutBytes;
   static_assert(kLds <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
 
@@ -280,18 +291,23 @@ void hgemm_nt_kernel(TileArgs ta) {
   const int64_t copy_strideB = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.ldb * 2;
   const int64_t firstA = (int64_t)cwp * C::kRowsPerCopy * p.lda * 2;
   const int64_t firstB = (int64_t)cwp * C::kRowsPerCopy * p.ldb * 2;
-  // The K-major operand (LAY): copy c fills k-rows 2 c and 2 c + 1, lane l
+  // A K-major operand (LAY): copy c fills k-rows 2 c and 2 c + 1, lane l
   // writing k-row 2 c + l / 32 at position l % 32, so it loads logical chunk
-  // (l % 32) ^ tsw(k-row).  Copy i of wave cw is c = 4 i + cw, k-row
-  // 8 i + 2 cw + l / 32: its k & 3 is 2 (cw & 1) + l / 32 and its
-  // ((k >> 3) ^ (k >> 4)) & 1 is (i ^ (i >> 1)) & 1, so two lane offsets serve
-  // every copy.
-  const int64_t ldt = kBT ? p.ldb : p.lda;
+  // (l % 32) ^ tsw(k-row) -- the row's last chunk where that lies past the
+  // tile's values (its position is never read).  Copy i of wave cw is
+  // c = 4 i + cw, k-row 8 i + 2 cw + l / 32: its k & 3 is 2 (cw & 1) + l / 32
+  // and its ((k >> 3) ^ (k >> 4)) & 1 is (i ^ (i >> 1)) & 1, so two lane
+  // offsets per operand serve every copy.
   const int tlo = 2 * (2 * (cwp & 1) + (lane >> 5));
-  const uint32_t offT0 = (uint32_t)((lane >> 5) * ldt * 2 + 16 * ((lane & 31) ^ tlo));
-  const uint32_t offT1 = (uint32_t)((lane >> 5) * ldt * 2 + 16 * ((lane & 31) ^ (tlo | 8)));
-  const int64_t firstT = (int64_t)2 * cwp * ldt * 2;
-  const int64_t copy_strideT = (int64_t)8 * ldt * 2;
+  auto t_off = [&](int64_t ld, int width, int hi) __attribute__((always_inline)) {
+    int lc = (lane & 31) ^ (tlo | hi);
+    if (lc >= width / 8) lc = width / 8 - 1;
+    return (uint32_t)((lane >> 5) * ld * 2 + 16 * lc);
+  };
+  const uint32_t offTA0 = t_off(p.lda, BM, 0), offTA1 = t_off(p.lda, BM, 8);
+  const uint32_t offTB0 = t_off(p.ldb, BN, 0), offTB1 = t_off(p.ldb, BN, 8);
+  const int64_t firstTA = (int64_t)2 * cwp * p.lda * 2, firstTB = (int64_t)2 * cwp * p.ldb * 2;
+  const int64_t copy_strideTA = (int64_t)8 * p.lda * 2, copy_strideTB = (int64_t)8 * p.ldb * 2;
 
   // This wave's copies of one K slab: the sources of its A and B rows and
   // the slab's LDS stage, then copy instruction c (A copies first) one at a
@@ -304,10 +320,10 @@ void hgemm_nt_kernel(TileArgs ta) {
   };
   auto slab_base = [&](int stage, int m0, int n0, int t, bool tail) __attribute__((always_inline)) {
     CopyBase cb;
-    cb.l = lds + stage * C::kStageBytes;
-    cb.a = kAT ? (const char*)(p.A + (int64_t)t * BK * p.lda + m0) + firstT
+    cb.l = lds + stage * kStage;
+    cb.a = kAT ? (const char*)(p.A + (int64_t)t * BK * p.lda + m0) + firstTA
                : (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
-    cb.b = kBT ? (const char*)(p.B + (int64_t)t * BK * p.ldb + n0) + firstT
+    cb.b = kBT ? (const char*)(p.B + (int64_t)t * BK * p.ldb + n0) + firstTB
                : (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
     cb.oa = RAG && tail ? offA_tail : offA;
     cb.ob = RAG && tail ? offB_tail : offB;
@@ -322,23 +338,23 @@ void hgemm_nt_kernel(TileArgs ta) {
       __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + off), (lds_void_t*)dst, 16, 0, 0);
   };
   auto copy_one = [&](const CopyBase& cb, int c) __attribute__((always_inline)) {
-    if (c < C::kPerWaveA) {
-      if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA) {
+    if (c < kPerWaveA) {
+      if (kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < kCopiesA) {
         if constexpr (kAT)
-          issue(cb.a + c * copy_strideT, ((c ^ (c >> 1)) & 1) ? offT1 : offT0,
+          issue(cb.a + c * copy_strideTA, ((c ^ (c >> 1)) & 1) ? offTA1 : offTA0,
                 cb.l + (c * C::kCopyWaves + cw) * 1024);
         else
           issue(cb.a + c * copy_strideA, cb.oa, cb.l + (c * C::kCopyWaves + cw) * 1024);
       }
     } else {
-      const int i = c - C::kPerWaveA;
-      if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB) {
+      const int i = c - kPerWaveA;
+      if (kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < kCopiesB) {
         if constexpr (kBT)
-          issue(cb.b + i * copy_strideT, ((i ^ (i >> 1)) & 1) ? offT1 : offT0,
-                cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024);
+          issue(cb.b + i * copy_strideTB, ((i ^ (i >> 1)) & 1) ? offTB1 : offTB0,
+                cb.l + kAreaA + (i * C::kCopyWaves + cw) * 1024);
         else
           issue(cb.b + i * copy_strideB, cb.ob,
-                cb.l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024);
+                cb.l + kAreaA + (i * C::kCopyWaves + cw) * 1024);
       }
     }
   };
@@ -356,15 +372,15 @@ void hgemm_nt_kernel(TileArgs ta) {
   auto wait_zero_sync = [&](bool zero, int stage) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
     if (zero && copier && chunk_past) {
-      unsigned char* l = lds + stage * C::kStageBytes;
+      unsigned char* l = lds + stage * kStage;
 #pragma unroll
-      for (int c = 0; c < C::kPerWaveA; ++c)
-        if (C::kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < C::kCopiesA)
+      for (int c = 0; c < kPerWaveA; ++c)
+        if (kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < kCopiesA)
           *(h8*)(l + (c * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
 #pragma unroll
-      for (int i = 0; i < C::kPerWaveB; ++i)
-        if (C::kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < C::kCopiesB)
-          *(h8*)(l + BM * BK * 2 + (i * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
+      for (int i = 0; i < kPerWaveB; ++i)
+        if (kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < kCopiesB)
+          *(h8*)(l + kAreaA + (i * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     asm volatile("s_barrier" ::: "memory");
@@ -377,21 +393,24 @@ void hgemm_nt_kernel(TileArgs ta) {
 
   // K-major operand fragments (LAY): per-lane byte offsets of block x's
   // first transposing read within the operand's stage area (block x covers
-  // values x0 = w0 + 16 x .. + 15 of the wave's w0 = wm or wn).
-  constexpr int kTBlocks = kBT ? C::kBlocksN : kAT ? C::kBlocksM : 1;
-  uint32_t toff[kTBlocks];
+  // values x0 = w0 + 16 x .. + 15 of the wave's w0 = wm for A, wn for B).
+  uint32_t toffA[kAT ? C::kBlocksM : 1], toffB[kBT ? C::kBlocksN : 1];
   {
     const int ti = lane & 15;
     const int tsw = (2 * (ti >> 2)) | (8 * ((g ^ (g >> 1)) & 1));
-    const int w0 = kBT ? wn : wm;
+    auto fill = [&](uint32_t* toff, int nblocks, int w0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int x = 0; x < kTBlocks; ++x)
-      toff[x] = (uint32_t)((8 * g + (ti >> 2)) * 512 +
-                           16 * (((w0 >> 3) + 2 * x + ((ti & 3) >> 1)) ^ tsw) + 8 * (ti & 1));
+      for (int x = 0; x < nblocks; ++x)
+        toff[x] = (uint32_t)((8 * g + (ti >> 2)) * 512 +
+                             16 * (((w0 >> 3) + 2 * x + ((ti & 3) >> 1)) ^ tsw) + 8 * (ti & 1));
+    };
+    if constexpr (kAT) fill(toffA, C::kBlocksM, wm);
+    if constexpr (kBT) fill(toffB, C::kBlocksN, wn);
   }
   // Block x of k-step s from the operand area `area` (A's or B's part of a
-  // stage): two transposing reads, k-rows 4 apart.
-  auto tread = [&](const unsigned char* area, int x, int s) __attribute__((always_inline)) {
+  // stage, offsets toff): two transposing reads, k-rows 4 apart.
+  auto tread = [&](const unsigned char* area, const uint32_t* toff, int x, int s)
+                   __attribute__((always_inline)) {
     typedef short s4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s4 lds_s4;
     typedef __attribute__((address_space(3))) const unsigned char lds_u8;
@@ -415,17 +434,17 @@ void hgemm_nt_kernel(TileArgs ta) {
   constexpr bool kOneB = (OPT & 2) != 0;
   h8 fa[2][C::kBlocksM], fb[kOneB ? 1 : 2][C::kBlocksN];
   auto load_frags = [&](int set, int stage, int s) __attribute__((always_inline)) {
-    const h8* st = (const h8*)(lds + stage * C::kStageBytes);
-    const unsigned char* sa = lds + stage * C::kStageBytes;
+    const h8* st = (const h8*)(lds + stage * kStage);
+    const unsigned char* sa = lds + stage * kStage;
     const int pc = (4 * s + g) ^ fr;
 #pragma unroll
     for (int i = 0; i < C::kBlocksM; ++i) {
-      if constexpr (kAT) fa[set][i] = tread(sa, i, s);
+      if constexpr (kAT) fa[set][i] = tread(sa, toffA, i, s);
       else fa[set][i] = st[a_off + 16 * kChunks * i + pc];
     }
 #pragma unroll
     for (int j = 0; j < C::kBlocksN; ++j) {
-      if constexpr (kBT) fb[kOneB ? 0 : set][j] = tread(sa + BM * BK * 2, j, s);
+      if constexpr (kBT) fb[kOneB ? 0 : set][j] = tread(sa + kAreaA, toffB, j, s);
       else fb[kOneB ? 0 : set][j] = st[b_off + 16 * kChunks * j + pc];
     }
   };
@@ -439,14 +458,14 @@ void hgemm_nt_kernel(TileArgs ta) {
   // Fragment q of a k-step (the A blocks, then the B blocks), and MFMA q of a
   // k-step (row block q / kBlocksN, column block q % kBlocksN).
   auto read_one = [&](int set, int stage, int step, int q) __attribute__((always_inline)) {
-    const h8* st = (const h8*)(lds + stage * C::kStageBytes);
-    const unsigned char* sa = lds + stage * C::kStageBytes;
+    const h8* st = (const h8*)(lds + stage * kStage);
+    const unsigned char* sa = lds + stage * kStage;
     const int pc = (4 * step + g) ^ fr;
     if (q < C::kBlocksM) {
-      if constexpr (kAT) fa[set][q] = tread(sa, q, step);
+      if constexpr (kAT) fa[set][q] = tread(sa, toffA, q, step);
       else fa[set][q] = st[a_off + 16 * kChunks * q + pc];
     } else {
-      if constexpr (kBT) fb[set][q - C::kBlocksM] = tread(sa + BM * BK * 2, q - C::kBlocksM, step);
+      if constexpr (kBT) fb[set][q - C::kBlocksM] = tread(sa + kAreaA, toffB, q - C::kBlocksM, step);
       else fb[set][q - C::kBlocksM] = st[b_off + 16 * kChunks * (q - C::kBlocksM) + pc];
     }
   };
@@ -467,7 +486,7 @@ void hgemm_nt_kernel(TileArgs ta) {
   // covers them all, then compute act(acc + bias) + residual in fp32, the
   // activation chosen once per quad.  The accumulator is never -0 (its sum
   // starts at +0), so adding a zero for an absent operand changes nothing.
-  unsigned char* stage_out = lds + 2 * C::kStageBytes + wave * (kOutRows * C::kOutRowBytes);
+  unsigned char* stage_out = lds + 2 * kStage + wave * (kOutRows * C::kOutRowBytes);
   auto epilogue = [&](int m0, int n0, int mlo, int nlo) __attribute__((always_inline)) {
     (void)mlo;
     (void)nlo;
@@ -582,7 +601,7 @@ void hgemm_nt_kernel(TileArgs ta) {
   constexpr int kReads = C::kBlocksM + C::kBlocksN;
   // LDS read instructions per k-step (a K-major block takes two)
   constexpr int kReadInstr = kReads + (kAT ? C::kBlocksM : 0) + (kBT ? C::kBlocksN : 0);
-  constexpr int kCopies = C::kPerWaveA + C::kPerWaveB;
+  constexpr int kCopies = kPerWaveA + kPerWaveB;
   static_assert(kReadInstr <= kMfma && kCopies <= kMfma, "interleave pattern");
   const int nk = SPLIT ? p.sk.per : RAG ? (p.K + BK - 1) / BK : p.K / BK;   // slabs per work item
   // The copy target runs two slabs ahead of the compute: slab tc of the tile
@@ -646,8 +665,8 @@ void hgemm_nt_kernel(TileArgs ta) {
       constexpr int MB = C::kBlocksM, NB = C::kBlocksN;
       constexpr int kB = kMfma + MB;
       static_assert(kB + kCopies <= 2 * kMfma, "copies after the barrier");
-      const h8* cur_st = (const h8*)(lds + (gs & 1) * C::kStageBytes);
-      const h8* nxt_st = (const h8*)(lds + ((gs + 1) & 1) * C::kStageBytes);
+      const h8* cur_st = (const h8*)(lds + (gs & 1) * kStage);
+      const h8* nxt_st = (const h8*)(lds + ((gs + 1) & 1) * kStage);
       const int pc1 = (4 + g) ^ fr, pc0 = g ^ fr;
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_sched_barrier(0);

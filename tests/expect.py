@@ -81,13 +81,13 @@ def expected_ex_path(M, N, K, op_a, op_b):
 
 
 def kmajor_in_place(M, N, K, op_a, op_b):
-    """gemm_ex NN on whole 224 x 256 tiles and TT on whole 256 x 224 tiles
-    (K % 64 == 0, aligned operands): the full tiles read the K-major operand
-    in place, with no workspace."""
+    """gemm_ex NN on whole 224 x 256 tiles, TT and TN on whole 256 x 224
+    tiles (K % 64 == 0, aligned operands): the full tiles read the K-major
+    operands in place, with no workspace."""
     if K % 64 != 0 or K == 0:
         return False
     if (op_a, op_b) == ("n", "n"):
         return M % 224 == 0 and N % 256 == 0
-    if (op_a, op_b) == ("t", "t"):
+    if (op_a, op_b) in (("t", "t"), ("t", "n")):
         return M % 256 == 0 and N % 224 == 0
     return False

@@ -314,8 +314,8 @@ def test_gemm_ex_validation_and_paths(lib, monkeypatch):
 
 
 def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
-    """NN on whole 224 x 256 tiles and TT on whole 256 x 224 tiles read the
-    K-major operand in place: a call without a workspace passes the
+    """NN on whole 224 x 256 tiles, TT and TN on whole 256 x 224 tiles read
+    the K-major operands in place: a call without a workspace passes the
     workspace check and reaches the device check (no device here), where
     the copy paths stop at GEMM_ERR_WORKSPACE.  gemm_ex_workspace stays an
     upper bound for any pointers (the copies)."""
@@ -333,9 +333,13 @@ def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
     for op in ((N_, N_), (T_, T_)):
         assert call(*op, 5376, 5376, 2048) == -4
         assert ex_ws(lib, 0, *op, 5376, 5376, 2048) == 5376 * 2048 * 2
+    assert call(T_, N_, 5376, 5376, 2048) == -4                     # TN: both in place
+    assert ex_ws(lib, 0, T_, N_, 5376, 5376, 2048) == 2 * 5376 * 2048 * 2
     assert call(N_, N_, 448, 512, 64) == -4 and call(T_, T_, 512, 448, 64) == -4
+    assert call(T_, N_, 512, 448, 64) == -4
     assert call(N_, T_, 5376, 5376, 2048) == -4                     # NT: always in place
-    assert call(T_, N_, 5376, 5376, 2048) == -7                     # TN: both copied
+    assert call(T_, N_, 5376, 5376 - 224, 2048) == -4
+    assert call(T_, N_, 5376 - 224, 5376, 2048) == -7               # TN: 256-row tiles
     assert call(N_, N_, 5376, 5000, 2048) == -7                     # not whole tiles
     assert call(N_, N_, 5376, 5376, 2000) == -7                     # K % 64 != 0
     assert call(T_, T_, 5376 - 224, 5376, 2048) == -7               # TT: 256-row tiles
@@ -343,6 +347,7 @@ def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
     assert call(N_, N_, 5376, 5376, 2048, ldb=5380) == -7           # ldb % 8 != 0
     assert ex(lib, 0, N_, N_, 448, 512, 64) == F16_MFMA
     assert ex(lib, 0, T_, T_, 512, 448, 64) == F16_MFMA
+    assert ex(lib, 0, T_, N_, 512, 448, 64) == F16_MFMA
 
 
 def test_split_k_workspace_errors_need_no_device(lib):

@@ -318,14 +318,16 @@ def test_layouts_ragged_full_tiles(layout, fmt):
     check16(got, ref, sab, fmt, np.abs(dec(bias))[None, :], np.abs(dec(res)), fused=True)
 
 
-# NN on whole 224 x 256 tiles and TT on whole 256 x 224 tiles: the full-tile
-# kernel reads the K-major operand in place (transposing LDS reads).  One
+# NN on whole 224 x 256 tiles, TT and TN on whole 256 x 224 tiles: the
+# full-tile kernel reads the K-major operands in place (transposing LDS reads).  One
 # tile with one slab, a few tiles, and more tiles than CUs (each workgroup
 # then walks two tiles, prefetching across the tile boundary).
 KMAJOR_CASES = [(("n", "n"), 224, 256, 64), (("n", "n"), 448, 512, 192),
                 (("n", "n"), 672, 768, 320), (("n", "n"), 5376, 3072, 128),
                 (("t", "t"), 256, 224, 64), (("t", "t"), 512, 448, 192),
-                (("t", "t"), 768, 672, 320), (("t", "t"), 3072, 5376, 128)]
+                (("t", "t"), 768, 672, 320), (("t", "t"), 3072, 5376, 128),
+                (("t", "n"), 256, 224, 64), (("t", "n"), 512, 448, 192),
+                (("t", "n"), 768, 672, 320), (("t", "n"), 3072, 5376, 128)]
 
 
 def run_in_place(A, B, op_a, op_b, fmt, M, N, pad=0, bias=None, act="none", res=None):
@@ -364,7 +366,8 @@ def test_layouts_kmajor_in_place(layout, M, N, K, fmt):
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("layout,M,N,K,act", [(("n", "n"), 448, 512, 192, "silu"),
-                                              (("t", "t"), 512, 448, 256, "relu")],
+                                              (("t", "t"), 512, 448, 256, "relu"),
+                                              (("t", "n"), 512, 448, 128, "silu")],
                          ids=lambda v: "".join(v) if isinstance(v, tuple) else str(v))
 def test_layouts_kmajor_in_place_fused(layout, M, N, K, act, fmt):
     """The fused write-back (bias, activation, residual) on the in-place

@@ -248,9 +248,9 @@ MI355GEMM_API int gemm_f16_nt_splitk_static(int M, int N, int K,
  *
  * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  NN
  * (B stored [K][N]) with M % 224 == 0 and N % 256 == 0, and TT (A stored
- * [K][M]) with M % 256 == 0 and N % 224 == 0 -- K % 64 == 0, A, B and C
- * 16-byte aligned, lda, ldb and ldc multiples of 8 -- read the K-major operand
- * in place, with no workspace (the NT page, section 19: the kernel consumes B
+ * [K][M]) and TN (both) with M % 256 == 0 and N % 224 == 0 -- K % 64 == 0, A,
+ * B and C 16-byte aligned, lda, ldb and ldc multiples of 8 -- read the K-major
+ * operands in place, with no workspace (the NT page, section 19: the kernel consumes B
  * in its stored layout instead of transposing it first).  The other layouts
  * and shapes first copy each operand that is not K-contiguous (A for OP_T, B
  * for OP_N) into the workspace, transposed, then run the A * B^T kernels -- except on
@@ -290,8 +290,8 @@ MI355GEMM_API int gemm_ex(int type, int op_a, int op_b, int M, int N, int K,
 /* Workspace bytes gemm_ex uses for these sizes, layouts and leading
  * dimensions, split-K partial sums included (0 when none, or for arguments
  * gemm_ex rejects).  Without the split-K part gemm_ex runs unsplit and needs
- * only the rest.  The figure holds for any pointers: for NN and TT it counts
- * the transposed copy, which the calls that read the operand in place (see
+ * only the rest.  The figure holds for any pointers: for NN, TT and TN it
+ * counts the transposed copies, which the calls that read the operand in place (see
  * gemm_ex) do not use -- they accept a NULL workspace. */
 MI355GEMM_API unsigned long long gemm_ex_workspace(int type, int op_a, int op_b, int M, int N,
                                                    int K, int lda, int ldb);

@@ -384,3 +384,24 @@ def test_layouts_kmajor_in_place_fused(layout, M, N, K, act, fmt):
     ref, sab = reference(A, B, op_a, op_b, fmt, bias, act, res)
     dec = oracle.half_to_double if fmt == "f16" else oracle.bf16_to_double
     check16(got, ref, sab, fmt, np.abs(dec(bias))[None, :], np.abs(dec(res)), fused=True)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_kmajor_layouts_bitwise_equal_nt(fmt):
+    """The in-place NN, TT and TN kernels take the same k order per output as
+    the NT kernel (the same k bijection inside a k-step, the same slab
+    order), so on the same values every layout gives the NT result bit for
+    bit; the NT result is itself checked against the oracle."""
+    M = N = 1792    # whole tiles of 224 x 256 and 256 x 224
+    K = 192
+    A, Bt = inputs.operands16((M, K), (N, K), fmt)
+    ref, sab = reference(A, Bt, "n", "t", fmt)
+    nt = run_ex(A, Bt, "n", "t", fmt, M, N, expect="f16_mfma")
+    check16(nt, ref, sab, fmt)
+    stored = {"n": (np.ascontiguousarray(A), np.ascontiguousarray(Bt.T)),
+              "t": (np.ascontiguousarray(A.T), np.ascontiguousarray(Bt))}
+    for op_a, op_b in [("n", "n"), ("t", "t"), ("t", "n")]:
+        sa = stored["n"][0] if op_a == "n" else stored["t"][0]
+        sb = stored["n"][1] if op_b == "n" else stored["t"][1]
+        got = run_in_place(sa, sb, op_a, op_b, fmt, M, N)
+        assert np.array_equal(got.view(np.uint16), nt.view(np.uint16)), (op_a, op_b)

@@ -35,7 +35,7 @@ enum TileShape { kNone, k256x256, k256x224, k128x128, k128x192 };
 // more time per output than the 256-row tiles (tile-time 128 x 192 x 4/3).
 // RAGGED: the same over ceil(M / bm) x ceil(N / bn) tiles (the ragged form),
 // for the shapes at least one tile wide and tall.
-TileShape choose(int M, int N, int cus, bool ragged = false) {
+TileShape choose(int M, int N, int cus, bool ragged = false, int64_t* cost_out = nullptr) {
   TileShape best = kNone;
   int64_t best_cost = 0;
   auto consider = [&](TileShape t, int bm, int bn, int slots, int64_t tile_time) {
@@ -52,6 +52,7 @@ TileShape choose(int M, int N, int cus, bool ragged = false) {
   consider(k256x224, 256, 224, cus, 256 * 224);
   consider(k128x128, 128, 128, 2 * cus, 2 * 128 * 128 * 6 / 5);
   consider(k128x192, 128, 192, cus, 128 * 192 * 4 / 3);
+  if (cost_out) *cost_out = best_cost;
   return best;
 }
 }  // namespace
@@ -146,28 +147,78 @@ hipError_t launch_f16_partials_mfma(const Args16& a, int cus, hipStream_t stream
 }
 
 // NN (lay 1: B stored [K][N]), TT (lay 2: A stored [K][M]) and TN (lay 3:
-// both) read in place by the full-tile kernels: 224 x 256 tiles (waves of
-// 112 x 64, four B blocks per k-step through the transposing reads) for NN,
-// 256 x 224 (waves of 64 x 112: four A blocks, and TN's seven B blocks too)
-// for TT and TN, so that 5376 x 5376 still takes 504 tiles in two rounds.
-// Whole tiles, K a multiple of 64, the fast path's alignment.
+// both) read in place by the full-tile kernels (their LAY instances), on
+// whole tiles with K a multiple of 64 and the fast path's alignment.  Tile
+// shapes, by the cost model of choose(): 224 x 256 for NN (waves of
+// 112 x 64, the four B blocks per k-step through the transposing reads) or
+// 256 x 224 for TT and TN (waves of 64 x 112), so that 5376 x 5376 still
+// takes 504 tiles in two rounds; 128 x 128 (two workgroups per CU) and
+// 128 x 192 (one) as for NT.
+TileShape choose_kmajor(int lay, int M, int N, int cus, int64_t* cost_out = nullptr) {
+  TileShape best = kNone;
+  int64_t best_cost = 0;
+  auto consider = [&](TileShape t, int bm, int bn, int slots, int64_t tile_time) {
+    if (M % bm != 0 || N % bn != 0) return;
+    const int64_t tiles = (int64_t)(M / bm) * (N / bn);
+    const int64_t cost = (tiles + slots - 1) / slots * tile_time;
+    if (best == kNone || cost < best_cost) {
+      best = t;
+      best_cost = cost;
+    }
+  };
+  if (lay == 1)
+    consider(k256x224, 224, 256, cus, 224 * 256);   // NN: 224 rows x 256 columns
+  else
+    consider(k256x224, 256, 224, cus, 256 * 224);
+  consider(k128x128, 128, 128, 2 * cus, 2 * 128 * 128 * 6 / 5);
+  consider(k128x192, 128, 192, cus, 128 * 192 * 4 / 3);
+  if (cost_out) *cost_out = best_cost;
+  return best;
+}
+
+// Whether the K-major tiles take the product (whole tiles, the fast path's
+// alignment and leading dimensions) at no more cost, in the model above, than
+// the NT tiles would on transposed copies -- the copy's own time aside.  The
+// choice is made when the call is planned, before any device query, for the
+// chip's 256 CUs (the launch then picks the shape for the device's count).
+// Measured: 4096^3 NN, TT, TN, where the K-major tiles could only be
+// 128 x 128 (two rounds) against NT's 256 x 256 (one), took 139-145 us in
+// place against 119-129 us through the copies; 2048^3 28-30 against
+// 32-34 us, 2048 x 2304 x 768 16-17 against 20-22 us, 5376^2 x 2048 103-114
+// against 105-113 us.
 bool f16_kmajor_fits(int lay, int M, int N, int K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, const void* C, int64_t ldc) {
-  if (lay == 1) return hgemm::fits<224, 256, BK>(M, N, K, A, lda, B, ldb, C, ldc);
-  if (lay == 2 || lay == 3) return hgemm::fits<256, 224, BK>(M, N, K, A, lda, B, ldb, C, ldc);
-  return false;
+  constexpr int kPlanCus = 256;
+  int64_t kcost = 0, ncost = 0;
+  if (lay < 1 || lay > 3 || choose_kmajor(lay, M, N, kPlanCus, &kcost) == kNone) return false;
+  if (choose(M, N, kPlanCus, false, &ncost) != kNone && ncost < kcost) return false;
+  return hgemm::fits<64, 64, BK>(64, 64, K, A, lda, B, ldb, C, ldc);
+}
+
+template <int LAY, bool EPI, int FMT>
+hipError_t launch_kmajor_lay(const Args16& a, int cus, hipStream_t stream) {
+  switch (choose_kmajor(LAY, a.M, a.N, cus)) {
+    case k128x128:
+      return hgemm::launch<128, 128, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false, false, LAY>(
+          a, 2 * cus, stream);
+    case k128x192:
+      return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false, false, LAY>(
+          a, cus, stream);
+    default:
+      if constexpr (LAY == 1)
+        return hgemm::launch<224, 256, BK, 2, 4, GM, 1, 0, true, EPI, FMT, false, false, 1>(
+            a, cus, stream);
+      else
+        return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, false, LAY>(
+            a, cus, stream);
+  }
 }
 
 template <bool EPI, int FMT>
 hipError_t launch_kmajor(const Args16& a, int lay, int cus, hipStream_t stream) {
-  if (lay == 1)
-    return hgemm::launch<224, 256, BK, 2, 4, GM, 1, 0, true, EPI, FMT, false, false, 1>(a, cus,
-                                                                                      stream);
-  if (lay == 2)
-    return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, false, 2>(a, cus,
-                                                                                      stream);
-  return hgemm::launch<256, 224, BK, 4, 2, GM, 1, 0, true, EPI, FMT, false, false, 3>(a, cus,
-                                                                                    stream);
+  if (lay == 1) return launch_kmajor_lay<1, EPI, FMT>(a, cus, stream);
+  if (lay == 2) return launch_kmajor_lay<2, EPI, FMT>(a, cus, stream);
+  return launch_kmajor_lay<3, EPI, FMT>(a, cus, stream);
 }
 
 hipError_t launch_f16_kmajor(const Args16& a, int lay, bool epi, int cus, hipStream_t stream) {

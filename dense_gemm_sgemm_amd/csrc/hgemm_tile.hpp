@@ -193,8 +193,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 // place: the page's kernel consumes the operand in the layout it is stored in
 // rather than transposing it first ("从零开始的 AI Infra: 算子基础与GPU架构",
 // section 19).  Such an operand's slab is kept in LDS as 64 k-rows of 512
-// bytes (32 chunks of 16 bytes: the tile's 256 or 224 values, then unused
-// positions), chunk c of k-row k at position c ^ tsw(k) with
+// bytes (32 chunks of 16 bytes: the tile's 256, 224 or 192 values, then
+// unused positions; 256 bytes for a 128-value tile side), chunk c of k-row k
+// at position c ^ tsw(k) with
 // tsw(k) = 2 (k & 3) | 8 (((k >> 3) ^ (k >> 4)) & 1), and its fragments are
 // read with gfx950's transposing LDS read (ds_read_b64_tr_b16): in each
 // group of 16 lanes, lane 4 a + b receives element b of the 8-byte reads of
@@ -214,13 +215,16 @@ void hgemm_nt_kernel(TileArgs ta) {
                 "K-major operands: whole tiles, four copying waves, two fragment sets");
   static_assert((!kBT || (BN <= 256 && BN % 32 == 0)) && (!kAT || (BM <= 256 && BM % 32 == 0)),
                 "K-major slab rows of at most 256 values");
-  // A stage: A's area, then B's; a K-major operand takes 64 k-rows of 512
-  // bytes, copied two k-rows per copy instruction.
-  constexpr int kAreaA = kAT ? BK * 512 : BM * BK * 2;
-  constexpr int kAreaB = kBT ? BK * 512 : BN * BK * 2;
+  // A stage: A's area, then B's.  A K-major operand takes 64 k-rows of kTP
+  // bytes -- 256 for 128 values, else 512 (up to 256 values, padded) -- and
+  // one copy instruction fills 1024 / kTP of them.
+  constexpr int kTPA = BM <= 128 ? 256 : 512, kTPB = BN <= 128 ? 256 : 512;
+  constexpr int kAreaA = kAT ? BK * kTPA : BM * BK * 2;
+  constexpr int kAreaB = kBT ? BK * kTPB : BN * BK * 2;
   constexpr int kStage = kAreaA + kAreaB;
   static_assert(kBT || kAreaA == BM * BK * 2, "K-contiguous B fragments are read past A's area");
-  constexpr int kCopiesA = kAT ? BK / 2 : C::kCopiesA, kCopiesB = kBT ? BK / 2 : C::kCopiesB;
+  constexpr int kCopiesA = kAT ? BK * kTPA / 1024 : C::kCopiesA;
+  constexpr int kCopiesB = kBT ? BK * kTPB / 1024 : C::kCopiesB;
   constexpr int kPerWaveA = (kCopiesA + C::kCopyWaves - 1) / C::kCopyWaves;
   constexpr int kPerWaveB = (kCopiesB + C::kCopyWaves - 1) / C::kCopyWaves;
   constexpr int kChunks = C::kChunks;
@@ -291,23 +295,32 @@ void hgemm_nt_kernel(TileArgs ta) {
   const int64_t copy_strideB = (int64_t)C::kCopyWaves * C::kRowsPerCopy * p.ldb * 2;
   const int64_t firstA = (int64_t)cwp * C::kRowsPerCopy * p.lda * 2;
   const int64_t firstB = (int64_t)cwp * C::kRowsPerCopy * p.ldb * 2;
-  // A K-major operand (LAY): copy c fills k-rows 2 c and 2 c + 1, lane l
-  // writing k-row 2 c + l / 32 at position l % 32, so it loads logical chunk
-  // (l % 32) ^ tsw(k-row) -- the row's last chunk where that lies past the
-  // tile's values (its position is never read).  Copy i of wave cw is
-  // c = 4 i + cw, k-row 8 i + 2 cw + l / 32: its k & 3 is 2 (cw & 1) + l / 32
-  // and its ((k >> 3) ^ (k >> 4)) & 1 is (i ^ (i >> 1)) & 1, so two lane
-  // offsets per operand serve every copy.
-  const int tlo = 2 * (2 * (cwp & 1) + (lane >> 5));
-  auto t_off = [&](int64_t ld, int width, int hi) __attribute__((always_inline)) {
-    int lc = (lane & 31) ^ (tlo | hi);
+  // A K-major operand (LAY) with R = 1024 / kTP k-rows per copy: copy c
+  // fills k-rows R c .. R c + R - 1, lane l writing k-row R c + l / (kTP / 16)
+  // at position l % (kTP / 16), so it loads logical chunk
+  // (l % (kTP / 16)) ^ tsw(k-row) -- the row's last chunk where that lies
+  // past the tile's values (its position is never read).  Copy i of wave cw
+  // is c = 4 i + cw.  R = 2: k-row 8 i + 2 cw + l / 32, k & 3 = 2 (cw & 1) +
+  // l / 32 and ((k >> 3) ^ (k >> 4)) & 1 = (i ^ (i >> 1)) & 1.  R = 4: k-row
+  // 16 i + 4 cw + l / 16, k & 3 = l / 16 and ((k >> 3) ^ (k >> 4)) & 1 =
+  // ((cw >> 1) ^ i) & 1.  Two lane offsets per operand serve every copy.
+  auto t_off = [&](int64_t ld, int width, int pitch, int hi) __attribute__((always_inline)) {
+    const int cpr = pitch / 16;
+    const int tlo = pitch == 512 ? 2 * (2 * (cwp & 1) + (lane >> 5)) : 2 * (lane >> 4);
+    int lc = (lane % cpr) ^ (tlo | hi);
     if (lc >= width / 8) lc = width / 8 - 1;
-    return (uint32_t)((lane >> 5) * ld * 2 + 16 * lc);
+    return (uint32_t)((lane / cpr) * ld * 2 + 16 * lc);
   };
-  const uint32_t offTA0 = t_off(p.lda, BM, 0), offTA1 = t_off(p.lda, BM, 8);
-  const uint32_t offTB0 = t_off(p.ldb, BN, 0), offTB1 = t_off(p.ldb, BN, 8);
-  const int64_t firstTA = (int64_t)2 * cwp * p.lda * 2, firstTB = (int64_t)2 * cwp * p.ldb * 2;
-  const int64_t copy_strideTA = (int64_t)8 * p.lda * 2, copy_strideTB = (int64_t)8 * p.ldb * 2;
+  // whether copy i of this wave takes the offset with bit 3 set
+  auto t_hi = [&](int pitch, int i) __attribute__((always_inline)) {
+    return pitch == 512 ? ((i ^ (i >> 1)) & 1) != 0 : (((cwp >> 1) ^ i) & 1) != 0;
+  };
+  const uint32_t offTA0 = t_off(p.lda, BM, kTPA, 0), offTA1 = t_off(p.lda, BM, kTPA, 8);
+  const uint32_t offTB0 = t_off(p.ldb, BN, kTPB, 0), offTB1 = t_off(p.ldb, BN, kTPB, 8);
+  const int64_t firstTA = (int64_t)(1024 / kTPA) * cwp * p.lda * 2;
+  const int64_t firstTB = (int64_t)(1024 / kTPB) * cwp * p.ldb * 2;
+  const int64_t copy_strideTA = (int64_t)4 * (1024 / kTPA) * p.lda * 2;
+  const int64_t copy_strideTB = (int64_t)4 * (1024 / kTPB) * p.ldb * 2;
 
   // This wave's copies of one K slab: the sources of its A and B rows and
   // the slab's LDS stage, then copy instruction c (A copies first) one at a
@@ -341,7 +354,7 @@ void hgemm_nt_kernel(TileArgs ta) {
     if (c < kPerWaveA) {
       if (kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < kCopiesA) {
         if constexpr (kAT)
-          issue(cb.a + c * copy_strideTA, ((c ^ (c >> 1)) & 1) ? offTA1 : offTA0,
+          issue(cb.a + c * copy_strideTA, t_hi(kTPA, c) ? offTA1 : offTA0,
                 cb.l + (c * C::kCopyWaves + cw) * 1024);
         else
           issue(cb.a + c * copy_strideA, cb.oa, cb.l + (c * C::kCopyWaves + cw) * 1024);
@@ -350,7 +363,7 @@ void hgemm_nt_kernel(TileArgs ta) {
       const int i = c - kPerWaveA;
       if (kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < kCopiesB) {
         if constexpr (kBT)
-          issue(cb.b + i * copy_strideTB, ((i ^ (i >> 1)) & 1) ? offTB1 : offTB0,
+          issue(cb.b + i * copy_strideTB, t_hi(kTPB, i) ? offTB1 : offTB0,
                 cb.l + kAreaA + (i * C::kCopyWaves + cw) * 1024);
         else
           issue(cb.b + i * copy_strideB, cb.ob,
@@ -398,25 +411,26 @@ void hgemm_nt_kernel(TileArgs ta) {
   {
     const int ti = lane & 15;
     const int tsw = (2 * (ti >> 2)) | (8 * ((g ^ (g >> 1)) & 1));
-    auto fill = [&](uint32_t* toff, int nblocks, int w0) __attribute__((always_inline)) {
+    auto fill = [&](uint32_t* toff, int nblocks, int w0, int pitch) __attribute__((always_inline)) {
 #pragma unroll
       for (int x = 0; x < nblocks; ++x)
-        toff[x] = (uint32_t)((8 * g + (ti >> 2)) * 512 +
+        toff[x] = (uint32_t)((8 * g + (ti >> 2)) * pitch +
                              16 * (((w0 >> 3) + 2 * x + ((ti & 3) >> 1)) ^ tsw) + 8 * (ti & 1));
     };
-    if constexpr (kAT) fill(toffA, C::kBlocksM, wm);
-    if constexpr (kBT) fill(toffB, C::kBlocksN, wn);
+    if constexpr (kAT) fill(toffA, C::kBlocksM, wm, kTPA);
+    if constexpr (kBT) fill(toffB, C::kBlocksN, wn, kTPB);
   }
   // Block x of k-step s from the operand area `area` (A's or B's part of a
-  // stage, offsets toff): two transposing reads, k-rows 4 apart.
-  auto tread = [&](const unsigned char* area, const uint32_t* toff, int x, int s)
+  // stage, offsets toff, k-rows of `pitch` bytes): two transposing reads,
+  // k-rows 4 apart.
+  auto tread = [&](const unsigned char* area, const uint32_t* toff, int x, int s, int pitch)
                    __attribute__((always_inline)) {
     typedef short s4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s4 lds_s4;
     typedef __attribute__((address_space(3))) const unsigned char lds_u8;
-    lds_u8* base = (lds_u8*)area + toff[x] + s * 32 * 512;
+    lds_u8* base = (lds_u8*)area + toff[x] + s * 32 * pitch;
     const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)base);
-    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(base + 4 * 512));
+    const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(base + 4 * pitch));
     return __builtin_bit_cast(h8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
@@ -439,12 +453,12 @@ void hgemm_nt_kernel(TileArgs ta) {
     const int pc = (4 * s + g) ^ fr;
 #pragma unroll
     for (int i = 0; i < C::kBlocksM; ++i) {
-      if constexpr (kAT) fa[set][i] = tread(sa, toffA, i, s);
+      if constexpr (kAT) fa[set][i] = tread(sa, toffA, i, s, kTPA);
       else fa[set][i] = st[a_off + 16 * kChunks * i + pc];
     }
 #pragma unroll
     for (int j = 0; j < C::kBlocksN; ++j) {
-      if constexpr (kBT) fb[kOneB ? 0 : set][j] = tread(sa + kAreaA, toffB, j, s);
+      if constexpr (kBT) fb[kOneB ? 0 : set][j] = tread(sa + kAreaA, toffB, j, s, kTPB);
       else fb[kOneB ? 0 : set][j] = st[b_off + 16 * kChunks * j + pc];
     }
   };
@@ -462,10 +476,11 @@ void hgemm_nt_kernel(TileArgs ta) {
     const unsigned char* sa = lds + stage * kStage;
     const int pc = (4 * step + g) ^ fr;
     if (q < C::kBlocksM) {
-      if constexpr (kAT) fa[set][q] = tread(sa, toffA, q, step);
+      if constexpr (kAT) fa[set][q] = tread(sa, toffA, q, step, kTPA);
       else fa[set][q] = st[a_off + 16 * kChunks * q + pc];
     } else {
-      if constexpr (kBT) fb[set][q - C::kBlocksM] = tread(sa + kAreaA, toffB, q - C::kBlocksM, step);
+      if constexpr (kBT)
+        fb[set][q - C::kBlocksM] = tread(sa + kAreaA, toffB, q - C::kBlocksM, step, kTPB);
       else fb[set][q - C::kBlocksM] = st[b_off + 16 * kChunks * (q - C::kBlocksM) + pc];
     }
   };

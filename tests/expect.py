@@ -80,14 +80,33 @@ def expected_ex_path(M, N, K, op_a, op_b):
     return "f16_staged" if large else "f16_general"
 
 
+def tile_cost(shapes, M, N, cus=256):
+    """The library's tile cost model: ceil(tiles / slots) x tile-time over the
+    whole-tile shapes given as (bm, bn, slots per CU, tile-time); None if none
+    fits."""
+    best = None
+    for bm, bn, per_cu, tt in shapes:
+        if M % bm or N % bn:
+            continue
+        c = -(-(M // bm) * (N // bn) // (per_cu * cus)) * tt
+        best = c if best is None or c < best else best
+    return best
+
+
+SMALL_TILES = [(128, 128, 2, 2 * 128 * 128 * 6 // 5), (128, 192, 1, 128 * 192 * 4 // 3)]
+NT_TILES = [(256, 256, 1, 256 * 256), (256, 224, 1, 256 * 224)] + SMALL_TILES
+
+
 def kmajor_in_place(M, N, K, op_a, op_b):
-    """gemm_ex NN on whole 224 x 256 tiles, TT and TN on whole 256 x 224
-    tiles (K % 64 == 0, aligned operands): the full tiles read the K-major
-    operands in place, with no workspace."""
-    if K % 64 != 0 or K == 0:
+    """gemm_ex NN, TT and TN on whole tiles (K % 64 == 0, aligned operands):
+    224 x 256 (NN) or 256 x 224 (TT, TN), 128 x 128 or 128 x 192; the full
+    tiles read the K-major operands in place, with no workspace -- unless the
+    NT tiles on transposed copies cost less in the tile model (256 CUs)."""
+    if K % 64 != 0 or K == 0 or (op_a, op_b) == ("n", "t"):
         return False
-    if (op_a, op_b) == ("n", "n"):
-        return M % 224 == 0 and N % 256 == 0
-    if (op_a, op_b) in (("t", "t"), ("t", "n")):
-        return M % 256 == 0 and N % 224 == 0
-    return False
+    big = (224, 256, 1, 224 * 256) if (op_a, op_b) == ("n", "n") else (256, 224, 1, 256 * 224)
+    kc = tile_cost([big] + SMALL_TILES, M, N)
+    if kc is None:
+        return False
+    nc = tile_cost(NT_TILES, M, N)
+    return nc is None or kc <= nc

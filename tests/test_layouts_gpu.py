@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from dense_gemm_sgemm_amd import inputs
-from expect import expected_ex_path
+from expect import expected_ex_path, kmajor_in_place
 from tolerance import check16
 
 torch = pytest.importorskip("torch")
@@ -318,16 +318,24 @@ def test_layouts_ragged_full_tiles(layout, fmt):
     check16(got, ref, sab, fmt, np.abs(dec(bias))[None, :], np.abs(dec(res)), fused=True)
 
 
-# NN on whole 224 x 256 tiles, TT and TN on whole 256 x 224 tiles: the
-# full-tile kernel reads the K-major operands in place (transposing LDS reads).  One
+# NN on whole 224 x 256 tiles, TT and TN on whole 256 x 224 tiles, all three
+# on whole 128 x 128 or 128 x 192 tiles: the full-tile kernel reads the
+# K-major operands in place (transposing LDS reads).  One
 # tile with one slab, a few tiles, and more tiles than CUs (each workgroup
 # then walks two tiles, prefetching across the tile boundary).
 KMAJOR_CASES = [(("n", "n"), 224, 256, 64), (("n", "n"), 448, 512, 192),
-                (("n", "n"), 672, 768, 320), (("n", "n"), 5376, 3072, 128),
+                (("n", "n"), 672, 768, 320), (("n", "n"), 5376, 5376, 128),
                 (("t", "t"), 256, 224, 64), (("t", "t"), 512, 448, 192),
-                (("t", "t"), 768, 672, 320), (("t", "t"), 3072, 5376, 128),
+                (("t", "t"), 768, 672, 320), (("t", "t"), 5376, 5376, 128),
                 (("t", "n"), 256, 224, 64), (("t", "n"), 512, 448, 192),
-                (("t", "n"), 768, 672, 320), (("t", "n"), 3072, 5376, 128)]
+                (("t", "n"), 768, 672, 320), (("t", "n"), 5376, 5376, 128),
+                # 128 x 128 tiles (two workgroups per CU; 4096 x 3968: each walks
+                # two tiles) and 128 x 192 tiles (one per CU; NN on the fused-QKV
+                # shape)
+                (("n", "n"), 384, 640, 192), (("t", "t"), 640, 384, 128),
+                (("t", "n"), 384, 512, 256), (("n", "n"), 4096, 3968, 128),
+                (("t", "n"), 4096, 3968, 64), (("n", "n"), 2048, 2304, 768),
+                (("t", "t"), 256, 384, 192), (("t", "n"), 1024, 1152, 64)]
 
 
 def run_in_place(A, B, op_a, op_b, fmt, M, N, pad=0, bias=None, act="none", res=None):
@@ -356,11 +364,12 @@ def test_layouts_kmajor_in_place(layout, M, N, K, fmt):
     """Every output against the oracle, with no workspace; the larger
     shapes also with the K-major operand's rows padded by 8 elements."""
     op_a, op_b = layout
+    assert kmajor_in_place(M, N, K, op_a, op_b)
     sa, sb = stored_shapes(M, N, K, op_a, op_b)
     A, B = inputs.operands16(sa, sb, fmt)
     ref, sab = reference(A, B, op_a, op_b, fmt)
     check16(run_in_place(A, B, op_a, op_b, fmt, M, N), ref, sab, fmt)
-    if M * N >= 448 * 512:
+    if 448 * 512 <= M * N <= 4096 * 2048:
         check16(run_in_place(A, B, op_a, op_b, fmt, M, N, pad=8), ref, sab, fmt)
 
 

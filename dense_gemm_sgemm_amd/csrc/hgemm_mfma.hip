@@ -152,8 +152,8 @@ hipError_t launch_f16_partials_mfma(const Args16& a, int cus, hipStream_t stream
 // shapes, by the cost model of choose(): 224 x 256 for NN (waves of
 // 112 x 64, the four B blocks per k-step through the transposing reads) or
 // 256 x 224 for TT and TN (waves of 64 x 112), so that 5376 x 5376 still
-// takes 504 tiles in two rounds; 128 x 128 (two workgroups per CU) and
-// 128 x 192 (one) as for NT.
+// takes 504 tiles in two rounds; 256 x 256 (NN and TT), 128 x 128 (two
+// workgroups per CU) and 128 x 192 (one) as for NT.
 TileShape choose_kmajor(int lay, int M, int N, int cus, int64_t* cost_out = nullptr) {
   TileShape best = kNone;
   int64_t best_cost = 0;
@@ -166,6 +166,9 @@ TileShape choose_kmajor(int lay, int M, int N, int cus, int64_t* cost_out = null
       best_cost = cost;
     }
   };
+  // TN on 256 x 256 (both operands transposed, one B set) spills 64
+  // registers: 4096^3 took 142.5 us against 127.5 us through the copies
+  if (lay != 3) consider(k256x256, 256, 256, cus, 256 * 256);
   if (lay == 1)
     consider(k256x224, 224, 256, cus, 224 * 256);   // NN: 224 rows x 256 columns
   else
@@ -181,11 +184,11 @@ TileShape choose_kmajor(int lay, int M, int N, int cus, int64_t* cost_out = null
 // the NT tiles would on transposed copies -- the copy's own time aside.  The
 // choice is made when the call is planned, before any device query, for the
 // chip's 256 CUs (the launch then picks the shape for the device's count).
-// Measured: 4096^3 NN, TT, TN, where the K-major tiles could only be
-// 128 x 128 (two rounds) against NT's 256 x 256 (one), took 139-145 us in
-// place against 119-129 us through the copies; 2048^3 28-30 against
-// 32-34 us, 2048 x 2304 x 768 16-17 against 20-22 us, 5376^2 x 2048 103-114
-// against 105-113 us.
+// Measured: 4096^3 NN, TT, TN on 128 x 128 tiles (two rounds, against one
+// of NT's 256 x 256) took 139-145 us in place against 119-129 us through the
+// copies; with the 256 x 256 K-major tiles NN 117.0 against 118.1 us and TT
+// 113.0 against 117.8 us; 2048^3 28-30 against 31-34 us, 2048 x 2304 x 768
+// 16-17 against 20-22 us, 5376^2 x 2048 102-116 against 105-112 us.
 bool f16_kmajor_fits(int lay, int M, int N, int K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, const void* C, int64_t ldc) {
   constexpr int kPlanCus = 256;
@@ -204,6 +207,13 @@ hipError_t launch_kmajor_lay(const Args16& a, int cus, hipStream_t stream) {
     case k128x192:
       return hgemm::launch<128, 192, BK, 2, 2, GM, 0, 1, true, EPI, FMT, false, false, LAY>(
           a, cus, stream);
+    case k256x256:
+      // one set of B fragments, as for NT (OPT bit 1); never chosen for TN
+      if constexpr (LAY != 3)
+        return hgemm::launch<256, 256, BK, 4, 2, GM, 1, 2, true, EPI, FMT, false, false, LAY>(
+            a, cus, stream);
+      else
+        return hipErrorInvalidValue;
     default:
       if constexpr (LAY == 1)
         return hgemm::launch<224, 256, BK, 2, 4, GM, 1, 0, true, EPI, FMT, false, false, 1>(

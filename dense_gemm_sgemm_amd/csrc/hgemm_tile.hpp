@@ -211,8 +211,8 @@ void hgemm_nt_kernel(TileArgs ta) {
   static_assert(!(RAG && SPLIT), "ragged tiles store C");
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr bool kAT = LAY == 2 || LAY == 3, kBT = LAY == 1 || LAY == 3;   // stored K-major
-  static_assert(LAY == 0 || (!RAG && !SPLIT && C::kCopyWaves == 4 && (OPT & 2) == 0),
-                "K-major operands: whole tiles, four copying waves, two fragment sets");
+  static_assert(LAY == 0 || (!RAG && !SPLIT && C::kCopyWaves == 4),
+                "K-major operands: whole tiles, four copying waves");
   static_assert((!kBT || (BN <= 256 && BN % 32 == 0)) && (!kAT || (BM <= 256 && BM % 32 == 0)),
                 "K-major slab rows of at most 256 values");
   // A stage: A's area, then B's.  A K-major operand takes 64 k-rows of kTP
@@ -682,6 +682,8 @@ void hgemm_nt_kernel(TileArgs ta) {
       static_assert(kB + kCopies <= 2 * kMfma, "copies after the barrier");
       const h8* cur_st = (const h8*)(lds + (gs & 1) * kStage);
       const h8* nxt_st = (const h8*)(lds + ((gs + 1) & 1) * kStage);
+      const unsigned char* cur_sa = lds + (gs & 1) * kStage;
+      const unsigned char* nxt_sa = lds + ((gs + 1) & 1) * kStage;
       const int pc1 = (4 + g) ^ fr, pc0 = g ^ fr;
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_sched_barrier(0);
@@ -695,21 +697,31 @@ void hgemm_nt_kernel(TileArgs ta) {
         acc[i][j] = mfma16<FMT>(fb[0][j], fa[step][i], acc[i][j]);
         if constexpr (step == 0) {
           // step 1 of this slab: A fragment qq, B fragment j after its last use
-          if constexpr (qq < MB) fa[1][qq] = cur_st[a_off + 16 * kChunks * qq + pc1];
-          if constexpr (i == MB - 1) fb[0][j] = cur_st[b_off + 16 * kChunks * j + pc1];
+          if constexpr (qq < MB) {
+            if constexpr (kAT) fa[1][qq] = tread(cur_sa, toffA, qq, 1, kTPA);
+            else fa[1][qq] = cur_st[a_off + 16 * kChunks * qq + pc1];
+          }
+          if constexpr (i == MB - 1) {
+            if constexpr (kBT) fb[0][j] = tread(cur_sa + kAreaA, toffB, j, 1, kTPB);
+            else fb[0][j] = cur_st[b_off + 16 * kChunks * j + pc1];
+          }
         }
         if constexpr (kNext) {
           // step 0 of the next slab, after the barrier
           static_for<MB>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i2 = decltype(ic)::value;
-            if constexpr (q == (kB > kMfma + i2 ? kB : kMfma + i2))
-              fa[0][i2] = nxt_st[a_off + 16 * kChunks * i2 + pc0];
+            if constexpr (q == (kB > kMfma + i2 ? kB : kMfma + i2)) {
+              if constexpr (kAT) fa[0][i2] = tread(nxt_sa, toffA, i2, 0, kTPA);
+              else fa[0][i2] = nxt_st[a_off + 16 * kChunks * i2 + pc0];
+            }
           });
           static_for<NB>([&](auto jc) __attribute__((always_inline)) {
             constexpr int j2 = decltype(jc)::value;
             constexpr int last = kMfma + MB * j2 + MB - 1;
-            if constexpr (q == (kB > last ? kB : last))
-              fb[0][j2] = nxt_st[b_off + 16 * kChunks * j2 + pc0];
+            if constexpr (q == (kB > last ? kB : last)) {
+              if constexpr (kBT) fb[0][j2] = tread(nxt_sa + kAreaA, toffB, j2, 0, kTPB);
+              else fb[0][j2] = nxt_st[b_off + 16 * kChunks * j2 + pc0];
+            }
           });
         }
         if constexpr (kCp) {

@@ -99,13 +99,15 @@ NT_TILES = [(256, 256, 1, 256 * 256), (256, 224, 1, 256 * 224)] + SMALL_TILES
 
 def kmajor_in_place(M, N, K, op_a, op_b):
     """gemm_ex NN, TT and TN on whole tiles (K % 64 == 0, aligned operands):
-    224 x 256 (NN) or 256 x 224 (TT, TN), 128 x 128 or 128 x 192; the full
+    256 x 256 (NN, TT), 224 x 256 (NN) or 256 x 224 (TT, TN), 128 x 128 or
+    128 x 192; the full
     tiles read the K-major operands in place, with no workspace -- unless the
     NT tiles on transposed copies cost less in the tile model (256 CUs)."""
     if K % 64 != 0 or K == 0 or (op_a, op_b) == ("n", "t"):
         return False
     big = (224, 256, 1, 224 * 256) if (op_a, op_b) == ("n", "n") else (256, 224, 1, 256 * 224)
-    kc = tile_cost([big] + SMALL_TILES, M, N)
+    square = [(256, 256, 1, 256 * 256)] if (op_a, op_b) != ("t", "n") else []
+    kc = tile_cost(square + [big] + SMALL_TILES, M, N)
     if kc is None:
         return False
     nc = tile_cost(NT_TILES, M, N)

@@ -340,13 +340,16 @@ def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
     assert call(N_, T_, 5376, 5376, 2048) == -4                     # NT: always in place
     assert call(T_, N_, 5376, 5376 - 224, 2048) == -4
     assert call(T_, N_, 5376 - 224, 5376, 2048) == -7               # TN: 256-row tiles
-    # 128-row tiles in place; but 4096^2 NN, TT, TN go through the copies,
-    # where NT's 256 x 256 tiles take one round against two of 128 x 128
+    # 256 x 256 (NN, TT) and 128-row tiles in place; NN 4096 x 3584 goes
+    # through the copy, where NT's 256 x 224 tiles take fewer tile-times than
+    # NN's shapes, and so does TN 4096^2 (its K-major tiles stop at 256 x 224)
     assert call(N_, N_, 2048, 2304, 768) == -4 and call(T_, N_, 384, 512, 256) == -4
     assert call(T_, T_, 640, 384, 128) == -4
     for op in ((N_, N_), (T_, T_), (T_, N_)):
-        assert call(*op, 4096, 4096, 4096) == -7
         assert call(*op, 4096, 3968, 128) == -4
+    assert call(N_, N_, 4096, 4096, 4096) == -4 and call(T_, T_, 4096, 4096, 4096) == -4
+    assert call(T_, N_, 4096, 4096, 4096) == -7                     # TN: no 256 x 256
+    assert call(N_, N_, 4096, 3584, 128) == -7 and call(T_, T_, 4096, 3584, 128) == -4
     assert call(N_, N_, 5376, 5000, 2048) == -7                     # not whole tiles
     assert call(N_, N_, 5376, 5376, 2000) == -7                     # K % 64 != 0
     assert call(T_, T_, 5376 - 224, 5376, 2048) == -7               # TT: 256-row tiles

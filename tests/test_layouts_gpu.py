@@ -335,7 +335,9 @@ KMAJOR_CASES = [(("n", "n"), 224, 256, 64), (("n", "n"), 448, 512, 192),
                 (("n", "n"), 384, 640, 192), (("t", "t"), 640, 384, 128),
                 (("t", "n"), 384, 512, 256), (("n", "n"), 4096, 3968, 128),
                 (("t", "n"), 4096, 3968, 64), (("n", "n"), 2048, 2304, 768),
-                (("t", "t"), 256, 384, 192), (("t", "n"), 1024, 1152, 64)]
+                (("t", "t"), 256, 384, 192), (("t", "n"), 1024, 1152, 64),
+                # 256 x 256 tiles (NN and TT; one set of B fragments)
+                (("n", "n"), 4096, 4096, 64), (("t", "t"), 4096, 4096, 128)]
 
 
 def run_in_place(A, B, op_a, op_b, fmt, M, N, pad=0, bias=None, act="none", res=None):
@@ -396,13 +398,14 @@ def test_layouts_kmajor_in_place_fused(layout, M, N, K, act, fmt):
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_kmajor_layouts_bitwise_equal_nt(fmt):
+@pytest.mark.parametrize("M,N,K", [(1792, 1792, 192), (4096, 4096, 64)])
+def test_kmajor_layouts_bitwise_equal_nt(fmt, M, N, K):
     """The in-place NN, TT and TN kernels take the same k order per output as
     the NT kernel (the same k bijection inside a k-step, the same slab
     order), so on the same values every layout gives the NT result bit for
-    bit; the NT result is itself checked against the oracle."""
-    M = N = 1792    # whole tiles of 224 x 256 and 256 x 224
-    K = 192
+    bit, in place or on copies; the NT result is itself checked against the
+    oracle."""
+    # 1792: whole tiles of 224 x 256 and 256 x 224; 4096: of 256 x 256
     A, Bt = inputs.operands16((M, K), (N, K), fmt)
     ref, sab = reference(A, Bt, "n", "t", fmt)
     nt = run_ex(A, Bt, "n", "t", fmt, M, N, expect="f16_mfma")
@@ -412,5 +415,7 @@ def test_kmajor_layouts_bitwise_equal_nt(fmt):
     for op_a, op_b in [("n", "n"), ("t", "t"), ("t", "n")]:
         sa = stored["n"][0] if op_a == "n" else stored["t"][0]
         sb = stored["n"][1] if op_b == "n" else stored["t"][1]
-        got = run_in_place(sa, sb, op_a, op_b, fmt, M, N)
+        # (TN 4096^2 runs on transposed copies, with the NT kernel)
+        got = (run_in_place(sa, sb, op_a, op_b, fmt, M, N) if kmajor_in_place(M, N, K, op_a, op_b)
+               else run_ex(sa, sb, op_a, op_b, fmt, M, N))
         assert np.array_equal(got.view(np.uint16), nt.view(np.uint16)), (op_a, op_b)

@@ -248,7 +248,8 @@ MI355GEMM_API int gemm_f16_nt_splitk_static(int M, int N, int K,
  *
  * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  NN
  * (B stored [K][N]), TT (A stored [K][M]) and TN (both) on whole tiles --
- * 224 x 256 for NN or 256 x 224 for TT and TN, 128 x 128 or 128 x 192; K % 64
+ * 256 x 256 for NN and TT, 224 x 256 for NN or 256 x 224 for TT and TN,
+ * 128 x 128 or 128 x 192; K % 64
  * == 0, A, B and C 16-byte aligned, lda, ldb and ldc multiples of 8 -- read
  * the K-major operands in place, with no workspace, unless the A * B^T tiles
  * on transposed copies would take fewer rounds of the GPU (4096 x 4096, for

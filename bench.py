@@ -83,7 +83,8 @@ def parse_args():
 # only while they are unchanged.
 KERNEL_SOURCES = {
     H_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_mfma.hip",
-             "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
+             "dense_gemm_sgemm_amd/csrc/hgemm_shapes.hpp", "dense_gemm_sgemm_amd/csrc/internal.h",
+             "dense_gemm_sgemm_amd/build.py"],
     F_NAME: ["dense_gemm_sgemm_amd/csrc/sgemm_mfma.hip", "dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp",
              "dense_gemm_sgemm_amd/csrc/internal.h", "dense_gemm_sgemm_amd/build.py"],
     R_NAME: ["dense_gemm_sgemm_amd/csrc/hgemm_tile.hpp", "dense_gemm_sgemm_amd/csrc/hgemm_staged.hip",
@@ -95,7 +96,8 @@ KERNEL_SOURCES[V_NAME] = ["dense_gemm_sgemm_amd/csrc/hgemv.hip", "dense_gemm_sge
 KERNEL_SOURCES[S_NAME] = KERNEL_SOURCES[H_NAME] + ["dense_gemm_sgemm_amd/csrc/splitk.hip"]
 KERNEL_SOURCES["sgemm_256"] = KERNEL_SOURCES["sgemm_1024"] = KERNEL_SOURCES[F_NAME]
 KERNEL_SOURCES[F_NAME + "_beta0.5"] = KERNEL_SOURCES[F_NAME]
-KERNEL_SOURCES[Q_NAME] = KERNEL_SOURCES[N_NAME] = KERNEL_SOURCES[H_NAME]
+KERNEL_SOURCES[Q_NAME] = KERNEL_SOURCES[H_NAME]
+KERNEL_SOURCES[N_NAME] = KERNEL_SOURCES[H_NAME] + ["dense_gemm_sgemm_amd/csrc/hgemm_kmajor.hip"]
 COPY_BYTES = 1 << 30
 # Bytes written between launches for the cold-cache figure: twice the 256 MB
 # last-level cache.

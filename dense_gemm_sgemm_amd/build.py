@@ -38,12 +38,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build")
 
 
-# Per-source compiler flags.  The fp16 tile kernel keeps two register sets of
+# Per-source compiler flags.  The fp16 tile kernels (A * B^T and the in-place
+# layouts) keep two register sets of
 # operand fragments and 112-128 accumulator registers live in each of its
 # waves; LLVM's register-minimising scheduler spills less there than the
 # default one and measured about 1 % faster on 5376 x 5376 x 2048.
 FILE_FLAGS = {
     "hgemm_mfma.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"],
+    "hgemm_kmajor.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-minreg"],
 }
 
 

@@ -211,8 +211,10 @@ void hgemm_nt_kernel(TileArgs ta) {
   static_assert(!(RAG && SPLIT), "ragged tiles store C");
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr bool kAT = LAY == 2 || LAY == 3, kBT = LAY == 1 || LAY == 3;   // stored K-major
-  static_assert(LAY == 0 || (!RAG && !SPLIT && C::kCopyWaves == 4),
-                "K-major operands: whole tiles, four copying waves");
+  // (RAG with K-major operands: ragged M and N only -- the host requires
+  // K % 64 == 0, so no slab reaches past K)
+  static_assert(LAY == 0 || (!SPLIT && C::kCopyWaves == 4),
+                "K-major operands: four copying waves, no split-K");
   static_assert((!kBT || (BN <= 256 && BN % 32 == 0)) && (!kAT || (BM <= 256 && BM % 32 == 0)),
                 "K-major slab rows of at most 256 values");
   // A stage: A's area, then B's.  A K-major operand takes 64 k-rows of kTP

@@ -80,15 +80,17 @@ def expected_ex_path(M, N, K, op_a, op_b):
     return "f16_staged" if large else "f16_general"
 
 
-def tile_cost(shapes, M, N, cus=256):
+def tile_cost(shapes, M, N, cus=256, ragged=False):
     """The library's tile cost model: ceil(tiles / slots) x tile-time over the
-    whole-tile shapes given as (bm, bn, slots per CU, tile-time); None if none
-    fits."""
+    shapes given as (bm, bn, slots per CU, tile-time) -- whole tiles, or
+    ceil(M / bm) x ceil(N / bn) tiles at least one tile wide and tall
+    (ragged); None if none fits."""
     best = None
     for bm, bn, per_cu, tt in shapes:
-        if M % bm or N % bn:
+        if (M < bm or N < bn) if ragged else (M % bm or N % bn):
             continue
-        c = -(-(M // bm) * (N // bn) // (per_cu * cus)) * tt
+        tiles = -(-M // bm) * -(-N // bn) if ragged else (M // bm) * (N // bn)
+        c = -(-tiles // (per_cu * cus)) * tt
         best = c if best is None or c < best else best
     return best
 
@@ -97,18 +99,36 @@ SMALL_TILES = [(128, 128, 2, 2 * 128 * 128 * 6 // 5), (128, 192, 1, 128 * 192 * 
 NT_TILES = [(256, 256, 1, 256 * 256), (256, 224, 1, 256 * 224)] + SMALL_TILES
 
 
-def kmajor_in_place(M, N, K, op_a, op_b):
-    """gemm_ex NN, TT and TN on whole tiles (K % 64 == 0, aligned operands):
+def kmajor_in_place(M, N, K, op_a, op_b, c_aligned=True):
+    """gemm_ex NN, TT and TN with K % 64 == 0 (contiguous operands at 16-byte
+    addresses): tiles of
     256 x 256 (NN, TT), 224 x 256 (NN) or 256 x 224 (TT, TN), 128 x 128 or
-    128 x 192; the full
-    tiles read the K-major operands in place, with no workspace -- unless the
-    NT tiles on transposed copies cost less in the tile model (256 CUs)."""
+    128 x 192 read the K-major operands in place, with no workspace -- whole
+    tiles (C aligned), or the ragged form for products of at least 2^30
+    multiply-adds at least 128 wide and tall -- unless the NT tiles on
+    transposed copies cost less in the tile model (256 CUs)."""
     if K % 64 != 0 or K == 0 or (op_a, op_b) == ("n", "t"):
+        return False
+    # contiguous K-major operands: rows of M (A stored [K][M]) or N (B stored
+    # [K][N]) elements, at 16-byte addresses only for multiples of 8
+    if (op_a == "t" and M % 8) or (op_b == "n" and N % 8):
         return False
     big = (224, 256, 1, 224 * 256) if (op_a, op_b) == ("n", "n") else (256, 224, 1, 256 * 224)
     square = [(256, 256, 1, 256 * 256)] if (op_a, op_b) != ("t", "n") else []
-    kc = tile_cost(square + [big] + SMALL_TILES, M, N)
+    shapes = square + [big] + SMALL_TILES
+    kc = tile_cost(shapes, M, N)
+    if kc is not None:
+        if not c_aligned:
+            return False
+        nc = tile_cost(NT_TILES, M, N)
+        return nc is None or kc <= nc
+    if M * N * K < (1 << 30):
+        return False
+    kc = tile_cost(shapes, M, N, ragged=True)
     if kc is None:
         return False
     nc = tile_cost(NT_TILES, M, N)
+    if nc is not None:
+        return kc <= nc
+    nc = tile_cost(NT_TILES, M, N, ragged=True)
     return nc is None or kc <= nc

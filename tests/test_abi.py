@@ -339,7 +339,12 @@ def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
     assert call(T_, N_, 512, 448, 64) == -4
     assert call(N_, T_, 5376, 5376, 2048) == -4                     # NT: always in place
     assert call(T_, N_, 5376, 5376 - 224, 2048) == -4
-    assert call(T_, N_, 5376 - 224, 5376, 2048) == -7               # TN: 256-row tiles
+    # ragged M or N with K % 64 == 0: the K-major tiles' ragged form, in place
+    assert call(T_, N_, 5376 - 224, 5376, 2048) == -4
+    assert call(T_, T_, 5376 - 224, 5376, 2048) == -4
+    assert call(N_, N_, 5376, 5000, 2048) == -4 and call(N_, N_, 4100, 4200, 1024) == -4
+    assert call(N_, N_, 1000, 1000, 512) == -7                      # small: the copy
+    assert call(N_, N_, 4100, 100, 4096) == -7                      # not 128 wide
     # 256 x 256 (NN, TT) and 128-row tiles in place; NN 4096 x 3584 goes
     # through the copy, where NT's 256 x 224 tiles take fewer tile-times than
     # NN's shapes, and so does TN 4096^2 (its K-major tiles stop at 256 x 224)
@@ -350,9 +355,7 @@ def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
     assert call(N_, N_, 4096, 4096, 4096) == -4 and call(T_, T_, 4096, 4096, 4096) == -4
     assert call(T_, N_, 4096, 4096, 4096) == -7                     # TN: no 256 x 256
     assert call(N_, N_, 4096, 3584, 128) == -7 and call(T_, T_, 4096, 3584, 128) == -4
-    assert call(N_, N_, 5376, 5000, 2048) == -7                     # not whole tiles
     assert call(N_, N_, 5376, 5376, 2000) == -7                     # K % 64 != 0
-    assert call(T_, T_, 5376 - 224, 5376, 2048) == -7               # TT: 256-row tiles
     assert call(N_, N_, 5376, 5376, 2048, B=p(ALIGNED + 2)) == -7   # B unaligned
     assert call(N_, N_, 5376, 5376, 2048, ldb=5380) == -7           # ldb % 8 != 0
     assert ex(lib, 0, N_, N_, 448, 512, 64) == F16_MFMA

@@ -337,7 +337,12 @@ KMAJOR_CASES = [(("n", "n"), 224, 256, 64), (("n", "n"), 448, 512, 192),
                 (("t", "n"), 4096, 3968, 64), (("n", "n"), 2048, 2304, 768),
                 (("t", "t"), 256, 384, 192), (("t", "n"), 1024, 1152, 64),
                 # 256 x 256 tiles (NN and TT; one set of B fragments)
-                (("n", "n"), 4096, 4096, 64), (("t", "t"), 4096, 4096, 128)]
+                (("n", "n"), 4096, 4096, 64), (("t", "t"), 4096, 4096, 128),
+                # ragged M or N (K % 64 == 0): the K-major tiles' ragged form
+                # (the K-major operands' rows, M or N elements, at 16-byte addresses)
+                (("n", "n"), 4100, 4200, 64), (("t", "t"), 5000, 3001, 128),
+                (("t", "n"), 4104, 4112, 64), (("n", "n"), 5152, 5376, 64),
+                (("t", "n"), 1000, 1104, 1024), (("t", "t"), 1104, 1030, 1024)]
 
 
 def run_in_place(A, B, op_a, op_b, fmt, M, N, pad=0, bias=None, act="none", res=None):
@@ -371,14 +376,15 @@ def test_layouts_kmajor_in_place(layout, M, N, K, fmt):
     A, B = inputs.operands16(sa, sb, fmt)
     ref, sab = reference(A, B, op_a, op_b, fmt)
     check16(run_in_place(A, B, op_a, op_b, fmt, M, N), ref, sab, fmt)
-    if 448 * 512 <= M * N <= 4096 * 2048:
+    if 448 * 512 <= M * N <= 4096 * 2048 or (M % 64 and N % 64):
         check16(run_in_place(A, B, op_a, op_b, fmt, M, N, pad=8), ref, sab, fmt)
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
 @pytest.mark.parametrize("layout,M,N,K,act", [(("n", "n"), 448, 512, 192, "silu"),
                                               (("t", "t"), 512, 448, 256, "relu"),
-                                              (("t", "n"), 512, 448, 128, "silu")],
+                                              (("t", "n"), 512, 448, 128, "silu"),
+                                              (("n", "n"), 4100, 4200, 64, "silu")],
                          ids=lambda v: "".join(v) if isinstance(v, tuple) else str(v))
 def test_layouts_kmajor_in_place_fused(layout, M, N, K, act, fmt):
     """The fused write-back (bias, activation, residual) on the in-place

@@ -9,9 +9,9 @@ namespace mi355gemm {
 using namespace hshape;
 
 // NN (lay 1: B stored [K][N]), TT (lay 2: A stored [K][M]) and TN (lay 3:
-// both) read in place by the full-tile kernels (their LAY instances), on
-// whole tiles with K a multiple of 64 and the fast path's alignment.  Tile
-// shapes, by the cost model of choose(): 224 x 256 for NN (waves of
+// both) read in place by the full-tile kernels (their LAY instances), with K
+// a multiple of 64 and A and B rows at 16-byte addresses.  Tile shapes, by
+// the cost model of choose(): 224 x 256 for NN (waves of
 // 112 x 64, the four B blocks per k-step through the transposing reads) or
 // 256 x 224 for TT and TN (waves of 64 x 112), so that 5376 x 5376 still
 // takes 504 tiles in two rounds; 256 x 256 (NN and TT), 128 x 128 (two

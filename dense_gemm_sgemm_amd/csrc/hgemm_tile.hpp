@@ -204,6 +204,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // h = 0, 1, and so holds k = 32 s + 8 g .. + 7 of value x0 + i: the same k
 // bijection as the K-contiguous operand's fragments.  Among any two of the
 // four lane groups the sixteen rows' chunk pairs fall on distinct bank quads.
+// The copies of these instances are issued from copy16_asm (the compiler
+// would otherwise wait for every copy in flight before each transposing
+// read).  Preconditions as above (whole tiles, or RAG), with K % 64 == 0 and
+// the K-major operand's rows at 16-byte addresses.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
           int FMT, bool SPLIT = false, bool RAG = false, int LAY = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVES_M * WAVES_N))

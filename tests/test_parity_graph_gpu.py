@@ -1,7 +1,8 @@
 """HIP graph capture: the library's calls recorded with torch.cuda.graph and
 replayed.  The library allocates nothing, so capture records only its
 kernels; the calls that take a workspace (explicit split-K, gemm_ex's
-transposed copies) get one allocated before capture.  Each graph is replayed
+transposed copies) get one allocated before capture (gemm_ex's in-place
+layouts are given one too, and leave it untouched).  Each graph is replayed
 several times, with the program's own eager work and synchronisations in
 between, and every replay must equal the eager result bit for bit (the
 kernels are deterministic and the path choice is the same)."""
@@ -28,6 +29,9 @@ CASES = [
     ("f16", (1000, 1030, 1100), "f16_staged"),
     ("f16_splitk", (128, 128, 16384), "f16_mfma"),
     ("ex_nn", (500, 301, 153), "f16_general"),
+    # B stored [K][N] read in place: whole 128 x 192 tiles, and the ragged form
+    ("ex_nn", (2048, 2304, 768), "f16_mfma"),
+    ("ex_nn", (4100, 4200, 1024), "f16_mfma"),
 ]
 
 

@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 SHAPES = [("f32", (1030, 1100, 1000)), ("f32_splitk", (512, 512, 16384)),
           ("f16", (1000, 1030, 1100)), ("f16_splitk", (128, 128, 16384)),
-          ("f32", (1024, 1024, 1024)), ("ex_nn", (500, 301, 153)), ("ex_nn", (1000, 1030, 1100))]
+          ("f32", (1024, 1024, 1024)), ("ex_nn", (500, 301, 153)), ("ex_nn", (1000, 1030, 1100)),
+          ("ex_nn", (2048, 2304, 768))]   # the last read in place, no workspace
 
 
 def make(kind, M, N, K):

@@ -177,10 +177,9 @@ Plan16 plan16(int type, int op_a, int op_b, int M, int N, int K, const void* A, 
       return done(GEMM_PATH_F16_SPLITK);
     }
   }
-  // NN, TT and TN with K % 64 == 0 on whole tiles or their ragged form: the
-  // full-tile kernels read the K-major operands in place through the
-  // transposing LDS reads (no copy, no workspace), unless the A * B^T tiles on
-  // copies would cost less.
+  // NN, TT and TN on whole tiles or their ragged form: the full-tile kernels
+  // read the K-major operands in place through the transposing LDS reads (no
+  // copy, no workspace), unless the A * B^T tiles on copies would cost less.
   const int lay = cb && !ca ? 1 : ca && !cb ? 2 : ca && cb ? 3 : 0;
   if (in_place && lay != 0 && f16_kmajor_fits(lay, M, N, K, A, lda, B, ldb, C, ldc) &&
       (!epi || f16_epi_fits(bias, res, ldr))) {

@@ -9,8 +9,8 @@ namespace mi355gemm {
 using namespace hshape;
 
 // NN (lay 1: B stored [K][N]), TT (lay 2: A stored [K][M]) and TN (lay 3:
-// both) read in place by the full-tile kernels (their LAY instances), with K
-// a multiple of 64 and A and B rows at 16-byte addresses.  Tile shapes, by
+// both) read in place by the full-tile kernels (their LAY instances), with A
+// and B rows at 16-byte addresses.  Tile shapes, by
 // the cost model of choose(): 224 x 256 for NN (waves of
 // 112 x 64, the four B blocks per k-step through the transposing reads) or
 // 256 x 224 for TT and TN (waves of 64 x 112), so that 5376 x 5376 still
@@ -18,8 +18,9 @@ using namespace hshape;
 // workgroups per CU) and 128 x 192 (one) as for NT.
 //
 // RAGGED: the same over ceil(M / bm) x ceil(N / bn) tiles (the ragged form:
-// the last tile row and column shifted back to end at M and N), for shapes
-// at least one tile wide and tall; K stays a multiple of 64.
+// the last tile row and column shifted back to end at M and N, and a K tail
+// taken by a last slab copied from K - 64), for shapes at least one tile wide
+// and tall.
 namespace {
 TileShape choose_kmajor(int lay, int M, int N, int cus, bool ragged = false,
                         int64_t* cost_out = nullptr) {
@@ -64,25 +65,31 @@ bool large(int M, int N, int K) { return (int64_t)M * N * K >= (int64_t(1) << 30
 // 113.0 against 117.8 us; 2048^3 28-30 against 31-34 us, 2048 x 2304 x 768
 // 16-17 against 20-22 us, 5376^2 x 2048 102-116 against 105-112 us.
 //
-// Ragged M or N (K still a multiple of 64; C at any 2-byte address): the
+// Ragged M or N, or K not a multiple of 64 (C at any 2-byte address): the
 // ragged form of the K-major tiles, for large products at least 128 wide and
-// tall, against the NT tiles -- whole or ragged -- on the copies.
+// tall, against the NT tiles -- whole, or ragged where K % 8 == 0 -- on the
+// copies.  Its last slab is copied from K - 64 (K > 64), which keeps the
+// K-contiguous operand's chunks at 16-byte addresses only for K % 8 == 0: NN
+// and TT need that, TN (both operands K-major) takes any K.
 bool f16_kmajor_fits(int lay, int M, int N, int K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, const void* C, int64_t ldc) {
   constexpr int kPlanCus = 256;
   constexpr int64_t kMaxLd = int64_t(1) << 28;
-  if (lay < 1 || lay > 3 || K <= 0 || K % BK != 0 || !aligned16(A) || !aligned16(B) ||
-      lda % 8 != 0 || ldb % 8 != 0 || lda >= kMaxLd || ldb >= kMaxLd)
+  if (lay < 1 || lay > 3 || K <= 0 || !aligned16(A) || !aligned16(B) || lda % 8 != 0 ||
+      ldb % 8 != 0 || lda >= kMaxLd || ldb >= kMaxLd)
     return false;
+  const bool whole_k = K % BK == 0;
+  if (!whole_k && (K < BK || (lay != 3 && K % 8 != 0))) return false;
   int64_t kcost = 0, ncost = 0;
-  if (choose_kmajor(lay, M, N, kPlanCus, false, &kcost) != kNone) {
+  if (whole_k && choose_kmajor(lay, M, N, kPlanCus, false, &kcost) != kNone) {
     // whole tiles: C 16-byte aligned as well
     if (!aligned16(C) || ldc % 8 != 0) return false;
     return choose(M, N, kPlanCus, false, &ncost) == kNone || kcost <= ncost;
   }
   if (!large(M, N, K) || choose_kmajor(lay, M, N, kPlanCus, true, &kcost) == kNone) return false;
-  if (choose(M, N, kPlanCus, false, &ncost) != kNone) return kcost <= ncost;
-  return choose(M, N, kPlanCus, true, &ncost) == kNone || kcost <= ncost;
+  if (whole_k && choose(M, N, kPlanCus, false, &ncost) != kNone) return kcost <= ncost;
+  if (K % 8 == 0 && choose(M, N, kPlanCus, true, &ncost) != kNone) return kcost <= ncost;
+  return true;
 }
 
 template <int LAY, bool EPI, int FMT, bool RAG>
@@ -113,10 +120,10 @@ hipError_t launch_kmajor_lay(const Args16& a, TileShape t, int cus, hipStream_t 
   }
 }
 
-// Whole tiles where they fit, else the ragged form.
+// Whole tiles where they fit and K is a multiple of 64, else the ragged form.
 template <int LAY, bool EPI, int FMT>
 hipError_t launch_kmajor_any(const Args16& a, int cus, hipStream_t stream) {
-  const TileShape whole = choose_kmajor(LAY, a.M, a.N, cus);
+  const TileShape whole = a.K % BK == 0 ? choose_kmajor(LAY, a.M, a.N, cus) : kNone;
   if (whole != kNone) return launch_kmajor_lay<LAY, EPI, FMT, false>(a, whole, cus, stream);
   return launch_kmajor_lay<LAY, EPI, FMT, true>(a, choose_kmajor(LAY, a.M, a.N, cus, true), cus,
                                                 stream);

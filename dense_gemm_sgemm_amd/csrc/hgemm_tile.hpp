@@ -206,8 +206,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // four lane groups the sixteen rows' chunk pairs fall on distinct bank quads.
 // The copies of these instances are issued from copy16_asm (the compiler
 // would otherwise wait for every copy in flight before each transposing
-// read).  Preconditions as above (whole tiles, or RAG), with K % 64 == 0 and
-// the K-major operand's rows at 16-byte addresses.
+// read).  Preconditions as above, with the K-major operands' rows at 16-byte
+// addresses: whole tiles with K % 64 == 0, or RAG, whose last slab is copied
+// from K - 64 when K % 64 != 0 (K > 64; K % 8 == 0 if an operand is
+// K-contiguous) and has its repeated positions zeroed.
 template <int BM, int BN, int BK, int WAVES_M, int WAVES_N, int GM, int COPY_SEL, int OPT, bool EPI,
           int FMT, bool SPLIT = false, bool RAG = false, int LAY = 0>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, waves_per_simd(BM, BN, WAVES_M * WAVES_N))
@@ -215,8 +217,6 @@ void hgemm_nt_kernel(TileArgs ta) {
   static_assert(!(RAG && SPLIT), "ragged tiles store C");
   typedef Config<BM, BN, BK, WAVES_M, WAVES_N, COPY_SEL> C;
   constexpr bool kAT = LAY == 2 || LAY == 3, kBT = LAY == 1 || LAY == 3;   // stored K-major
-  // (RAG with K-major operands: ragged M and N only -- the host requires
-  // K % 64 == 0, so no slab reaches past K)
   static_assert(LAY == 0 || (!SPLIT && C::kCopyWaves == 4),
                 "K-major operands: four copying waves, no split-K");
   static_assert((!kBT || (BN <= 256 && BN % 32 == 0)) && (!kAT || (BM <= 256 && BM % 32 == 0)),
@@ -337,15 +337,19 @@ void hgemm_nt_kernel(TileArgs ta) {
     unsigned char* l;
     uint32_t oa, ob;   // this lane's offsets (RAG: the clamped ones in a tile's last slab)
   };
+  // LAY with a K tail (RAG): the last slab is copied from K - 64 .. K - 1,
+  // every row and chunk inside the matrix; its first 64 - kv positions repeat
+  // the slab before and are zeroed in LDS (wait_zero_sync), so they add 0 x 0.
   auto slab_base = [&](int stage, int m0, int n0, int t, bool tail) __attribute__((always_inline)) {
     CopyBase cb;
     cb.l = lds + stage * kStage;
-    cb.a = kAT ? (const char*)(p.A + (int64_t)t * BK * p.lda + m0) + firstTA
-               : (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * t * BK;
-    cb.b = kBT ? (const char*)(p.B + (int64_t)t * BK * p.ldb + n0) + firstTB
-               : (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * t * BK;
-    cb.oa = RAG && tail ? offA_tail : offA;
-    cb.ob = RAG && tail ? offB_tail : offB;
+    const int64_t k0 = LAY != 0 && RAG && tail ? (int64_t)p.K - BK : (int64_t)t * BK;
+    cb.a = kAT ? (const char*)(p.A + k0 * p.lda + m0) + firstTA
+               : (const char*)(p.A + (int64_t)m0 * p.lda) + firstA + 2 * k0;
+    cb.b = kBT ? (const char*)(p.B + k0 * p.ldb + n0) + firstTB
+               : (const char*)(p.B + (int64_t)n0 * p.ldb) + firstB + 2 * k0;
+    cb.oa = LAY == 0 && RAG && tail ? offA_tail : offA;
+    cb.ob = LAY == 0 && RAG && tail ? offB_tail : offB;
     return cb;
   };
   // One copy (LAY: through the asm statement above, so that the compiler
@@ -388,9 +392,31 @@ void hgemm_nt_kernel(TileArgs ta) {
   };
   // RAG: the same, and before the barrier this wave zeroes its chunks past K
   // of the slab in `stage` when that slab is the last of its tile.
+  // LAY: this wave zeroes what its copies put in the first 64 - kv
+  // positions of that slab (copied from K - 64, above): K-major k-rows below
+  // 64 - kv, and K-contiguous chunks whose first k is below it.
   auto wait_zero_sync = [&](bool zero, int stage) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
-    if (zero && copier && chunk_past) {
+    if constexpr (LAY != 0) {
+      if (zero && copier) {
+        const int ks = BK - kv;
+        unsigned char* l = lds + stage * kStage;
+        // the k-row a K-major copy c of this lane wrote (R = 1024 / pitch rows per copy)
+        auto trow = [&](int pitch, int c) __attribute__((always_inline)) {
+          return (1024 / pitch) * (c * C::kCopyWaves + cw) + lane / (pitch / 16);
+        };
+#pragma unroll
+        for (int c = 0; c < kPerWaveA; ++c)
+          if ((kCopiesA % C::kCopyWaves == 0 || c * C::kCopyWaves + cw < kCopiesA) &&
+              (kAT ? trow(kTPA, c) < ks : 8 * lane_chunk < ks))
+            *(h8*)(l + (c * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
+#pragma unroll
+        for (int i = 0; i < kPerWaveB; ++i)
+          if ((kCopiesB % C::kCopyWaves == 0 || i * C::kCopyWaves + cw < kCopiesB) &&
+              (kBT ? trow(kTPB, i) < ks : 8 * lane_chunk < ks))
+            *(h8*)(l + kAreaA + (i * C::kCopyWaves + cw) * 1024 + 16 * lane) = h8{};
+      }
+    } else if (zero && copier && chunk_past) {
       unsigned char* l = lds + stage * kStage;
 #pragma unroll
       for (int c = 0; c < kPerWaveA; ++c)

@@ -152,10 +152,11 @@ hipError_t launch_f16_staged(const Args16& a, bool epi, int cus, hipStream_t str
 // stored [K][N] (gemm_ex NN); lay 2, A stored [K][M] (gemm_ex TT); lay 3,
 // both (gemm_ex TN).  Tiles of 256 x 256 (NN, TT), 224 x 256 (NN) or
 // 256 x 224 (TT, TN), 128 x 128 or 128 x 192, where they cost no more than
-// the A * B^T tiles on transposed copies: whole tiles (C 16-byte aligned,
-// ldc % 8 == 0), or the ragged form for products of at least 2^30
-// multiply-adds at least 128 wide and tall (C anywhere); K % 64 == 0, A and
-// B 16-byte aligned, lda and ldb multiples of 8 (below 2^28).
+// the A * B^T tiles on transposed copies: whole tiles with K % 64 == 0 (C
+// 16-byte aligned, ldc % 8 == 0), or the ragged form for products of at
+// least 2^30 multiply-adds at least 128 wide and tall (C anywhere; K > 64,
+// and K % 8 == 0 unless both operands are K-major); A and B 16-byte
+// aligned, lda and ldb multiples of 8 (below 2^28).
 bool f16_kmajor_fits(int lay, int M, int N, int K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, const void* C, int64_t ldc);
 hipError_t launch_f16_kmajor(const Args16& a, int lay, bool epi, int cus, hipStream_t stream);

@@ -100,14 +100,17 @@ NT_TILES = [(256, 256, 1, 256 * 256), (256, 224, 1, 256 * 224)] + SMALL_TILES
 
 
 def kmajor_in_place(M, N, K, op_a, op_b, c_aligned=True):
-    """gemm_ex NN, TT and TN with K % 64 == 0 (contiguous operands at 16-byte
-    addresses): tiles of
-    256 x 256 (NN, TT), 224 x 256 (NN) or 256 x 224 (TT, TN), 128 x 128 or
-    128 x 192 read the K-major operands in place, with no workspace -- whole
-    tiles (C aligned), or the ragged form for products of at least 2^30
-    multiply-adds at least 128 wide and tall -- unless the NT tiles on
-    transposed copies cost less in the tile model (256 CUs)."""
-    if K % 64 != 0 or K == 0 or (op_a, op_b) == ("n", "t"):
+    """gemm_ex NN, TT and TN (contiguous operands at 16-byte addresses):
+    tiles of 256 x 256 (NN, TT), 224 x 256 (NN) or 256 x 224 (TT, TN),
+    128 x 128 or 128 x 192 read the K-major operands in place, with no
+    workspace -- whole tiles with K % 64 == 0 (C aligned), or the ragged form
+    for products of at least 2^30 multiply-adds at least 128 wide and tall
+    (K > 64; K % 8 == 0 for NN and TT) -- unless the NT tiles on transposed
+    copies cost less in the tile model (256 CUs)."""
+    if K == 0 or (op_a, op_b) == ("n", "t"):
+        return False
+    whole_k = K % 64 == 0
+    if not whole_k and (K < 64 or ((op_a, op_b) != ("t", "n") and K % 8)):
         return False
     # contiguous K-major operands: rows of M (A stored [K][M]) or N (B stored
     # [K][N]) elements, at 16-byte addresses only for multiples of 8
@@ -116,19 +119,24 @@ def kmajor_in_place(M, N, K, op_a, op_b, c_aligned=True):
     big = (224, 256, 1, 224 * 256) if (op_a, op_b) == ("n", "n") else (256, 224, 1, 256 * 224)
     square = [(256, 256, 1, 256 * 256)] if (op_a, op_b) != ("t", "n") else []
     shapes = square + [big] + SMALL_TILES
-    kc = tile_cost(shapes, M, N)
-    if kc is not None:
-        if not c_aligned:
-            return False
-        nc = tile_cost(NT_TILES, M, N)
-        return nc is None or kc <= nc
+    if whole_k:
+        kc = tile_cost(shapes, M, N)
+        if kc is not None:
+            if not c_aligned:
+                return False
+            nc = tile_cost(NT_TILES, M, N)
+            return nc is None or kc <= nc
     if M * N * K < (1 << 30):
         return False
     kc = tile_cost(shapes, M, N, ragged=True)
     if kc is None:
         return False
-    nc = tile_cost(NT_TILES, M, N)
-    if nc is not None:
-        return kc <= nc
-    nc = tile_cost(NT_TILES, M, N, ragged=True)
-    return nc is None or kc <= nc
+    if whole_k:
+        nc = tile_cost(NT_TILES, M, N)
+        if nc is not None:
+            return kc <= nc
+    if K % 8 == 0:
+        nc = tile_cost(NT_TILES, M, N, ragged=True)
+        if nc is not None:
+            return kc <= nc
+    return True

@@ -355,7 +355,12 @@ def test_gemm_ex_kmajor_in_place_needs_no_workspace(lib, monkeypatch):
     assert call(N_, N_, 4096, 4096, 4096) == -4 and call(T_, T_, 4096, 4096, 4096) == -4
     assert call(T_, N_, 4096, 4096, 4096) == -7                     # TN: no 256 x 256
     assert call(N_, N_, 4096, 3584, 128) == -7 and call(T_, T_, 4096, 3584, 128) == -4
-    assert call(N_, N_, 5376, 5376, 2000) == -7                     # K % 64 != 0
+    # K % 64 != 0: the ragged form's last slab copied from K - 64; NN and TT
+    # need K % 8 == 0 (their K-contiguous operand), TN takes any K > 64
+    assert call(N_, N_, 5376, 5376, 2000) == -4 and call(T_, T_, 4096, 4096, 1000) == -4
+    assert call(T_, N_, 5376, 5376, 2001) == -4 and call(T_, N_, 4104, 4112, 1537) == -4
+    assert call(N_, N_, 5376, 5376, 2001) == -7                     # A rows unaligned
+    assert call(T_, N_, 2048, 2048, 40) == -7                       # small, K < 64
     assert call(N_, N_, 5376, 5376, 2048, B=p(ALIGNED + 2)) == -7   # B unaligned
     assert call(N_, N_, 5376, 5376, 2048, ldb=5380) == -7           # ldb % 8 != 0
     assert ex(lib, 0, N_, N_, 448, 512, 64) == F16_MFMA

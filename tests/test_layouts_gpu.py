@@ -342,7 +342,12 @@ KMAJOR_CASES = [(("n", "n"), 224, 256, 64), (("n", "n"), 448, 512, 192),
                 # (the K-major operands' rows, M or N elements, at 16-byte addresses)
                 (("n", "n"), 4100, 4200, 64), (("t", "t"), 5000, 3001, 128),
                 (("t", "n"), 4104, 4112, 64), (("n", "n"), 5152, 5376, 64),
-                (("t", "n"), 1000, 1104, 1024), (("t", "t"), 1104, 1030, 1024)]
+                (("t", "n"), 1000, 1104, 1024), (("t", "t"), 1104, 1030, 1024),
+                # K not a multiple of 64: the ragged form's last slab copied
+                # from K - 64, its repeated positions zeroed (TN: any K)
+                (("n", "n"), 4100, 4200, 1000), (("t", "t"), 5000, 3001, 1000),
+                (("t", "n"), 1000, 1104, 1001), (("n", "n"), 4096, 4096, 72),
+                (("t", "n"), 4096, 4096, 100)]
 
 
 def run_in_place(A, B, op_a, op_b, fmt, M, N, pad=0, bias=None, act="none", res=None):
@@ -384,7 +389,8 @@ def test_layouts_kmajor_in_place(layout, M, N, K, fmt):
 @pytest.mark.parametrize("layout,M,N,K,act", [(("n", "n"), 448, 512, 192, "silu"),
                                               (("t", "t"), 512, 448, 256, "relu"),
                                               (("t", "n"), 512, 448, 128, "silu"),
-                                              (("n", "n"), 4100, 4200, 64, "silu")],
+                                              (("n", "n"), 4100, 4200, 64, "silu"),
+                                              (("t", "t"), 4104, 4200, 1000, "relu")],
                          ids=lambda v: "".join(v) if isinstance(v, tuple) else str(v))
 def test_layouts_kmajor_in_place_fused(layout, M, N, K, act, fmt):
     """The fused write-back (bias, activation, residual) on the in-place

@@ -247,14 +247,15 @@ MI355GEMM_API int gemm_f16_nt_splitk_static(int M, int N, int K,
  *          GEMM_ACT_NONE and residual NULL give the plain product).
  *
  * (GEMM_TYPE_F16, GEMM_OP_N, GEMM_OP_T) is exactly gemm_f16_nt_ex.  NN
- * (B stored [K][N]), TT (A stored [K][M]) and TN (both) with K % 64 == 0,
- * A and B 16-byte aligned and lda, ldb multiples of 8 read the K-major
- * operands in place, with no workspace: on whole tiles (256 x 256 for NN and
- * TT, 224 x 256 for NN or 256 x 224 for TT and TN, 128 x 128 or 128 x 192;
- * C 16-byte aligned, ldc a multiple of 8), or, for products of at least 2^30
- * multiply-adds at least 128 wide and tall, on their ragged form (C anywhere)
- * -- unless the A * B^T tiles on transposed copies would take fewer rounds of
- * the GPU (NN 4096 x 3584, for one) (the NT page, section 19: the kernel consumes B
+ * (B stored [K][N]), TT (A stored [K][M]) and TN (both) with A and B
+ * 16-byte aligned and lda, ldb multiples of 8 read the K-major operands in
+ * place, with no workspace: on whole tiles with K % 64 == 0 (256 x 256 for NN
+ * and TT, 224 x 256 for NN or 256 x 224 for TT and TN, 128 x 128 or
+ * 128 x 192; C 16-byte aligned, ldc a multiple of 8), or, for products of at
+ * least 2^30 multiply-adds at least 128 wide and tall with K > 64 (and
+ * K % 8 == 0 for NN and TT), on their ragged form (C anywhere) -- unless the
+ * A * B^T tiles on transposed copies would take fewer rounds of the GPU (NN
+ * 4096 x 3584, for one) (the NT page, section 19: the kernel consumes B
  * in its stored layout instead of transposing it first).  The other layouts
  * and shapes first copy each operand that is not K-contiguous (A for OP_T, B
  * for OP_N) into the workspace, transposed, then run the A * B^T kernels -- except on

@@ -30,6 +30,9 @@ TileShape choose_kmajor(int lay, int M, int N, int cus, bool ragged = false,
     if (ragged ? (M < bm || N < bn) : (M % bm != 0 || N % bn != 0)) return;
     const int64_t tiles = ragged ? (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn)
                                  : (int64_t)(M / bm) * (N / bn);
+    // 128 x 128 tiles that do not outnumber the CUs each get a CU to
+    // themselves: about 0.8 of a 128 x 192 tile-time (see the model above)
+    if (t == k128x128 && tiles <= cus) tile_time = 128 * 128 * 8 / 5;
     const int64_t cost = (tiles + slots - 1) / slots * tile_time;
     if (best == kNone || cost < best_cost) {
       best = t;

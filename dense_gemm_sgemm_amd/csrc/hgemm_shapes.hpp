@@ -36,6 +36,11 @@ enum TileShape { kNone, k256x256, k256x224, k128x128, k128x192 };
 // 128 x 192 -> 192 tiles, 1 round x 32768 (measured 1.19x faster than
 // 128 x 128).  A 128 x 192 tile runs alone on its CU with 4 waves: a third
 // more time per output than the 256-row tiles (tile-time 128 x 192 x 4/3).
+// 128 x 128 tiles that do not outnumber the CUs run one per CU, each with a
+// CU to itself: tile-time 128 x 128 x 8/5, about 0.8 of a 128 x 192 tile
+// (measured: 1536 x 2304 x 2048 24.7 against 27.6 us on 144 tiles of
+// 128 x 192; 1536^2 x 4096 40.8 against 46.9 us; 1024 x 3072 x 2048 23.7
+// against 26.6 us).
 // RAGGED: the same over ceil(M / bm) x ceil(N / bn) tiles (the ragged form),
 // for the shapes at least one tile wide and tall.
 inline TileShape choose(int M, int N, int cus, bool ragged = false, int64_t* cost_out = nullptr) {
@@ -45,6 +50,9 @@ inline TileShape choose(int M, int N, int cus, bool ragged = false, int64_t* cos
     if (ragged ? (M < bm || N < bn) : (M % bm != 0 || N % bn != 0)) return;
     const int64_t tiles = ragged ? (int64_t)((M + bm - 1) / bm) * ((N + bn - 1) / bn)
                                  : (int64_t)(M / bm) * (N / bn);
+    // 128 x 128 tiles that do not outnumber the CUs each get a CU to
+    // themselves: about 0.8 of a 128 x 192 tile-time (see the model above)
+    if (t == k128x128 && tiles <= cus) tile_time = 128 * 128 * 8 / 5;
     const int64_t cost = (tiles + slots - 1) / slots * tile_time;
     if (best == kNone || cost < best_cost) {
       best = t;

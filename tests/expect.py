@@ -90,6 +90,8 @@ def tile_cost(shapes, M, N, cus=256, ragged=False):
         if (M < bm or N < bn) if ragged else (M % bm or N % bn):
             continue
         tiles = -(-M // bm) * -(-N // bn) if ragged else (M // bm) * (N // bn)
+        if (bm, bn) == (128, 128) and tiles <= cus:
+            tt = 128 * 128 * 8 // 5    # one tile per CU
         c = -(-tiles // (per_cu * cus)) * tt
         best = c if best is None or c < best else best
     return best

@@ -893,16 +893,21 @@ bool f32_stream_fits(int M, int N, int K, const void* A, int64_t lda, const void
          ldb < kStreamMaxLd;
 }
 
-// The small-tile kernel: whole tiles, K a multiple of 64, and at most a
-// quarter as many 64 x 64 tiles as CUs (it then runs at least four times as
-// many workgroups as the 64 x 64 kernels would); 16 x 16 tiles when even
-// 32 x 32 tiles would leave CUs idle.  Long K included: 512 x 512 x 16384 in
-// 144 us against 272 us on the 64 x 64 streaming tiles (256 x 256 x 16384:
-// 66 against 271 us; even at K = 4096).
+// The small-tile kernel: whole tiles, K a multiple of 64, and at most half
+// as many 64 x 64 tiles as CUs (it then runs at least twice as many
+// workgroups as the 64 x 64 kernels would, on every CU); 16 x 16 tiles when
+// even 32 x 32 tiles would leave CUs idle.  Long K included: 512 x 512 x 16384
+// in 144 us against 272 us on the 64 x 64 streaming tiles (256 x 256 x 16384:
+// 66 against 271 us; even at K = 4096).  Between a quarter and half as many
+// 64 x 64 tiles as CUs, against the 64 x 64 streaming tiles (same box):
+// 512 x 1024 x 2048 30.2 against 38.4 us, 640^2 x 4096 54.7 against 71.0 us,
+// 512 x 1024 x 8192 104.4 against 137.5 us, 768 x 512 x 1024 16.3 against
+// 21.4 us; with as many tiles as CUs the streaming tiles stay ahead (1024^3:
+// 22.9 against 31.2 us).
 static bool f32_small32_fits(int M, int N, int K, const void* A, int64_t lda, const void* B,
                              int64_t ldb, const void* C, int64_t ldc, int cus) {
   const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 63) / 64);
-  return M % 32 == 0 && N % 32 == 0 && K % 64 == 0 && 4 * tiles64 <= cus &&
+  return M % 32 == 0 && N % 32 == 0 && K % 64 == 0 && 2 * tiles64 <= cus &&
          aligned16(A) && aligned16(B) && aligned16(C) && lda % 4 == 0 && ldb % 4 == 0 &&
          ldc % 4 == 0;
 }

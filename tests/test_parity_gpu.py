@@ -1021,18 +1021,20 @@ def test_f32_stream64_alpha_beta_padded_and_exact():
     assert np.array_equal(gpu_f32(Ai, Bi, expect="f32_mfma").astype(np.float64), oracle.gemm_f32(Ai, Bi))
 
 
-# Products with at most a quarter as many 64 x 64 tiles as CUs (K a multiple
-# of 64) run on the small-tile kernel whose four waves split each K chunk of
-# up to 256 four ways, with 16 x 16 tiles while 32 x 32 ones would leave CUs
+# Products with at most half as many 64 x 64 tiles as CUs (K a multiple of
+# 64) run on the small-tile kernel whose four waves split each K chunk of up
+# to 256 four ways, with 16 x 16 tiles while 32 x 32 ones would leave CUs
 # idle: one chunk (256^3, 64^3), a short last chunk (320 = 256 + 64, 192,
 # 1088), sixteen chunks (512 x 512 x 4096), long K (256 x 256 x 16384, 512 x
 # 256 x 8192), a wide strip; the 32 x 32 tiles at 512 x 512 x 4096 and
-# 256 x 1024 x 320 (256 tiles each), the 16 x 16 ones at the others.  Element by element against the oracle;
-# the smallest of these shapes also appear in the stream64 list above, which
-# the small-tile kernel now takes.
+# 256 x 1024 x 320 (256 tiles each) and between a quarter and half as many
+# 64 x 64 tiles as CUs (512 x 1024 x 2048, 768 x 512 x 1088: 128 and 96
+# tiles of 64 x 64), the 16 x 16 ones at the others.  Element by element
+# against the oracle; the smallest of these shapes also appear in the
+# stream64 list above, which the small-tile kernel now takes.
 SMALL32_SHAPES = [(256, 256, 256), (64, 64, 64), (128, 512, 320), (512, 512, 4096),
                   (64, 1024, 192), (256, 128, 1088), (256, 1024, 320), (256, 256, 16384),
-                  (512, 256, 8192)]
+                  (512, 256, 8192), (512, 1024, 2048), (768, 512, 1088)]
 
 
 @pytest.mark.parametrize("shape", SMALL32_SHAPES, ids=lambda s: "x".join(map(str, s)))
